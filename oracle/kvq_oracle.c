@@ -1,0 +1,415 @@
+/*
+ * kvq_oracle.c -- CPU oracle for the 8-bit paged KV cache and its decode-step attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load this file's library.  The product path (the HIP library) never calls it, shares no
+ * code, header, table or constant with it, and must fail loudly when its own extension is missing.
+ *
+ * It is deliberately plain and slow: scalar loops, fp64 arithmetic, one function per step of the
+ * method, each step taken from its definition.  Sources, by page title and section:
+ *
+ *   [TGI-FP8] "Accelerating Inference with FP8 KV Cache" (text-generation-inference docs)
+ *       section "FP8 Formats: E4M3 and E5M2": the OCP E4M3 layout (1 sign, 4 biased-exponent,
+ *       3 mantissa bits) and E5M2 layout (1 sign, 5 biased-exponent, 2 mantissa bits); a
+ *       per-tensor FP32 scaling factor stored alongside the quantized tensor.
+ *       section "FP8 E4M3 KV Cache": the scale defaults to 1.0 when none is given.
+ *       opening section: the cache is stored as FP8 while the attention arithmetic runs at higher
+ *       precision (FP16 there; fp64 here, since this is the reference).
+ *   [LMD-1463] "[Feature] TurboMind support W8A8 or FP8 KV Cache" (lmdeploy issue thread):
+ *       the online INT8 KV cache variant.  The thread gives no formula; the reading used here is
+ *       symmetric INT8 with one fp32 scale per (token, head): s = amax/127, q = rne(x/s) clamped to
+ *       [-127, 127].
+ *   [QQQ-2] "[QST] Scale factors and benchmarks" (QQQ issue thread): the serving stack the
+ *       8-bit cache lives in is paged ("armed with paged attention"): fixed-size token blocks
+ *       reached through a per-sequence block table.
+ *
+ * Readings where the pages are silent:
+ *   - Exponent biases and special values follow the OCP definitions the page names: E4M3 has bias 7,
+ *     no infinities and NaN only at S.1111.111 (largest finite 448); E5M2 has bias 15 with IEEE-style
+ *     infinities (exponent 31, mantissa 0) and NaNs (exponent 31, mantissa != 0).
+ *   - Encode direction: code = enc(fl32(x / kv_scale)); decode: value = dec(code) * kv_scale.
+ *   - The quotient is one correctly rounded fp32 division; the 8-bit rounding is round-to-nearest,
+ *     ties to the code with an even mantissa LSB; finite overflow and +-inf saturate to +-max;
+ *     NaN encodes as sign | 0x7F; signed zero and subnormals are kept.
+ *   - Cache layout (both formats and INT8): K codes [num_blocks][Hkv][16 tokens][128 dims];
+ *     V codes [num_blocks][Hkv][128 dims][16 tokens]; INT8 scales [num_blocks][Hkv][16 tokens].
+ *   - context_lens are post-append lengths; context_lens[b] == 0 gives an all-zero output row.
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *
+ * Build (see oracle/build.py): gcc -O2 -std=c11 -ffp-contract=off (no -ffast-math); x86-64 SSE
+ * arithmetic, so `float` operations are IEEE binary32 with round-to-nearest-even and the default
+ * FE_TONEAREST mode makes nearbyint() round half to even.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KVQO_E4M3 1
+#define KVQO_E5M2 2
+#define KVQO_INT8 3
+
+#define KVQO_BLOCK 16
+#define KVQO_DIM 128
+
+/* ------------------------------------------------------------------------------------------ */
+/* IEEE binary16 -> double, from the format's definition: 1 sign bit, 5 exponent bits with bias 15,
+ * 10 fraction bits; exponent 0 is subnormal (f * 2^-24), exponent 31 is inf / NaN.  Exact.      */
+double kvqo_fp16_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* FP8 format parameters [TGI-FP8 "FP8 Formats: E4M3 and E5M2"] with the OCP bias reading.      */
+typedef struct {
+    int ebits, mbits, bias;
+    double max_finite;   /* E4M3 448, E5M2 57344 */
+    double min_normal;   /* 2^(1-bias) */
+} kvqo_fp8_fmt;
+
+static int kvqo_get_fmt(int fmt, kvqo_fp8_fmt *out)
+{
+    if (fmt == KVQO_E4M3) {
+        out->ebits = 4; out->mbits = 3; out->bias = 7;
+        /* largest exponent field 15 with mantissa 110b: 2^(15-7) * (1 + 6/8) = 448 (111b is NaN) */
+        out->max_finite = ldexp(1.0 + 6.0 / 8.0, 15 - 7);
+    } else if (fmt == KVQO_E5M2) {
+        out->ebits = 5; out->mbits = 2; out->bias = 15;
+        /* largest finite exponent field 30 (31 is inf/NaN) with mantissa 11b: 2^15 * 1.75 = 57344 */
+        out->max_finite = ldexp(1.0 + 3.0 / 4.0, 30 - 15);
+    } else {
+        return -1;
+    }
+    out->min_normal = ldexp(1.0, 1 - out->bias);
+    return 0;
+}
+
+/* Decode one FP8 code to its exact value.  Normal: (-1)^s 2^(e-bias) (1 + m/2^mbits);
+ * subnormal (e == 0): (-1)^s 2^(1-bias) (m/2^mbits); E4M3 S.1111.111 is NaN; E5M2 exponent 31 is
+ * inf (m == 0) or NaN.  Returns NAN for an unknown format.                                      */
+double kvqo_fp8_decode(int fmt, uint8_t code)
+{
+    kvqo_fp8_fmt F;
+    if (kvqo_get_fmt(fmt, &F) != 0)
+        return NAN;
+    int sign = code >> 7;
+    int e = (code >> F.mbits) & ((1 << F.ebits) - 1);
+    int m = code & ((1 << F.mbits) - 1);
+    double v;
+    if (fmt == KVQO_E4M3 && e == 15 && m == 7)
+        v = NAN;
+    else if (fmt == KVQO_E5M2 && e == 31)
+        v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0)
+        v = ldexp((double)m, 1 - F.bias - F.mbits);
+    else
+        v = ldexp((double)((1 << F.mbits) + m), e - F.bias - F.mbits);
+    return sign ? -v : v;
+}
+
+/* Encode an fp32 value y (already divided by the scale) to FP8: saturating, round to nearest,
+ * ties to even mantissa LSB.  The magnitude is clamped to max_finite first; every value that would
+ * round above max_finite lies above it, and values in (max, rounding threshold] round to max anyway,
+ * so clamping first is the same as rounding and then saturating.                                  */
+uint8_t kvqo_fp8_encode(int fmt, float y)
+{
+    kvqo_fp8_fmt F;
+    if (kvqo_get_fmt(fmt, &F) != 0)
+        return 0;
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)y);
+    if (a > F.max_finite)
+        a = F.max_finite;                       /* saturation, also for +-inf */
+    if (a >= F.min_normal) {
+        int k;
+        (void)frexp(a, &k);                     /* a = f * 2^k with f in [0.5, 1) */
+        int e = k - 1;                          /* a = 2^e * (1 + frac) */
+        double M = nearbyint((ldexp(a, -e) - 1.0) * (double)(1 << F.mbits));
+        if (M == (double)(1 << F.mbits)) {      /* mantissa rounded up into the next binade */
+            e += 1;
+            M = 0.0;
+        }
+        return (uint8_t)(sign | ((e + F.bias) << F.mbits) | (int)M);
+    }
+    /* subnormal range: multiples of the step 2^(1-bias-mbits); M == 2^mbits is the min-normal code,
+     * whose bit pattern is exactly (1 << mbits), so the same expression covers it */
+    double M = nearbyint(ldexp(a, F.bias - 1 + F.mbits));
+    return (uint8_t)(sign | (int)M);
+}
+
+/* One element of the FP8 append: y = fl32(fl32(x) / kv_scale), then encode. */
+uint8_t kvqo_fp8_quantize(int fmt, uint16_t x_fp16, float kv_scale)
+{
+    float x = (float)kvqo_fp16_to_double(x_fp16); /* exact: every binary16 value is a binary32 */
+    float y = x / kv_scale;                        /* one IEEE binary32 division */
+    return kvqo_fp8_encode(fmt, y);
+}
+
+/* Online INT8 encode of one (token, head) row of n values: a = max |x| (exact), s = fl32(a/127),
+ * q = clamp(rne(fl32(x/s)), -127, 127); a zero row gives s = 0 and q = 0.                        */
+void kvqo_int8_quantize_row(const uint16_t *x, int n, int8_t *q, float *s_out)
+{
+    float amax = 0.0f;
+    for (int d = 0; d < n; ++d) {
+        float v = fabsf((float)kvqo_fp16_to_double(x[d]));
+        if (v > amax)
+            amax = v;
+    }
+    if (amax == 0.0f) {
+        for (int d = 0; d < n; ++d)
+            q[d] = 0;
+        *s_out = 0.0f;
+        return;
+    }
+    float s = amax / 127.0f;
+    for (int d = 0; d < n; ++d) {
+        float y = (float)kvqo_fp16_to_double(x[d]) / s;
+        double r = nearbyint((double)y);
+        if (r > 127.0)
+            r = 127.0;
+        if (r < -127.0)
+            r = -127.0;
+        q[d] = (int8_t)r;
+    }
+    *s_out = s;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Paged layout offsets (see the header comment).                                               */
+static size_t k_off(int Hkv, int blk, int g, int t, int d)
+{
+    return (((size_t)blk * Hkv + g) * KVQO_BLOCK + t) * KVQO_DIM + d;
+}
+static size_t v_off(int Hkv, int blk, int g, int t, int d)
+{
+    return (((size_t)blk * Hkv + g) * KVQO_DIM + d) * KVQO_BLOCK + t;
+}
+static size_t s_off(int Hkv, int blk, int g, int t)
+{
+    return ((size_t)blk * Hkv + g) * KVQO_BLOCK + t;
+}
+
+/* Append new K/V rows into the paged cache (all arrays in host memory).
+ *   k_new, v_new : fp16 bits [T][Hkv][128]
+ *   cu_new_lens  : [B+1] row offsets per sequence, or NULL for exactly one row per sequence
+ *   context_lens : post-append lengths; sequence b's j-th new row goes to position
+ *                  context_lens[b] - n_b + j, i.e. block block_tables[b][p/16], slot p%16.
+ * Returns 0, or -1 for an unknown dtype / a position outside the block table.                   */
+int kvqo_append(int dtype, int Hkv, uint8_t *k_cache, uint8_t *v_cache, float *k_scale,
+                float *v_scale, float kv_scale, const uint16_t *k_new, const uint16_t *v_new,
+                const int32_t *cu_new_lens, const int32_t *block_tables, int max_blocks_per_seq,
+                const int32_t *context_lens, int batch)
+{
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8)
+        return -1;
+    int8_t qk[KVQO_DIM], qv[KVQO_DIM];
+    for (int b = 0; b < batch; ++b) {
+        int row0 = cu_new_lens ? cu_new_lens[b] : b;
+        int n_b = cu_new_lens ? cu_new_lens[b + 1] - cu_new_lens[b] : 1;
+        for (int j = 0; j < n_b; ++j) {
+            int p = context_lens[b] - n_b + j;
+            if (p < 0 || p / KVQO_BLOCK >= max_blocks_per_seq)
+                return -1;
+            int blk = block_tables[(size_t)b * max_blocks_per_seq + p / KVQO_BLOCK];
+            int t = p % KVQO_BLOCK;
+            for (int g = 0; g < Hkv; ++g) {
+                const uint16_t *xk = k_new + ((size_t)(row0 + j) * Hkv + g) * KVQO_DIM;
+                const uint16_t *xv = v_new + ((size_t)(row0 + j) * Hkv + g) * KVQO_DIM;
+                if (dtype == KVQO_INT8) {
+                    float sk, sv;
+                    kvqo_int8_quantize_row(xk, KVQO_DIM, qk, &sk);
+                    kvqo_int8_quantize_row(xv, KVQO_DIM, qv, &sv);
+                    for (int d = 0; d < KVQO_DIM; ++d) {
+                        k_cache[k_off(Hkv, blk, g, t, d)] = (uint8_t)qk[d];
+                        v_cache[v_off(Hkv, blk, g, t, d)] = (uint8_t)qv[d];
+                    }
+                    k_scale[s_off(Hkv, blk, g, t)] = sk;
+                    v_scale[s_off(Hkv, blk, g, t)] = sv;
+                } else {
+                    for (int d = 0; d < KVQO_DIM; ++d) {
+                        k_cache[k_off(Hkv, blk, g, t, d)] = kvqo_fp8_quantize(dtype, xk[d], kv_scale);
+                        v_cache[v_off(Hkv, blk, g, t, d)] = kvqo_fp8_quantize(dtype, xv[d], kv_scale);
+                    }
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* Exact dequantized value of one cached element, in fp64: FP8 dec(c) * kv_scale, INT8 q * s.
+ * Both products are exact in fp64 (at most 4 + 24 or 8 + 24 significant bits).                  */
+static double dq_k(int dtype, int Hkv, const uint8_t *kc, const float *ks, float kv_scale, int blk,
+                   int g, int t, int d)
+{
+    uint8_t c = kc[k_off(Hkv, blk, g, t, d)];
+    if (dtype == KVQO_INT8)
+        return (double)(int8_t)c * (double)ks[s_off(Hkv, blk, g, t)];
+    return kvqo_fp8_decode(dtype, c) * (double)kv_scale;
+}
+static double dq_v(int dtype, int Hkv, const uint8_t *vc, const float *vs, float kv_scale, int blk,
+                   int g, int t, int d)
+{
+    uint8_t c = vc[v_off(Hkv, blk, g, t, d)];
+    if (dtype == KVQO_INT8)
+        return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, t)];
+    return kvqo_fp8_decode(dtype, c) * (double)kv_scale;
+}
+
+/* Dequantize the cache into dense fp32 [B][Hkv][max_context_len][128] for K and V:
+ * out = fl32(exact dequantized value) -- one rounding.  Slots t >= context_lens[b] are untouched. */
+int kvqo_dequant(int dtype, int Hkv, const uint8_t *k_cache, const uint8_t *v_cache,
+                 const float *k_scale, const float *v_scale, float kv_scale,
+                 const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                 int batch, int max_context_len, float *k_out, float *v_out)
+{
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8)
+        return -1;
+    for (int b = 0; b < batch; ++b) {
+        int n = context_lens[b];
+        if (n > max_context_len)
+            return -1;
+        for (int g = 0; g < Hkv; ++g)
+            for (int t = 0; t < n; ++t) {
+                int blk = block_tables[(size_t)b * max_blocks_per_seq + t / KVQO_BLOCK];
+                for (int d = 0; d < KVQO_DIM; ++d) {
+                    size_t o = (((size_t)b * Hkv + g) * max_context_len + t) * KVQO_DIM + d;
+                    k_out[o] = (float)dq_k(dtype, Hkv, k_cache, k_scale, kv_scale, blk, g, t % KVQO_BLOCK, d);
+                    v_out[o] = (float)dq_v(dtype, Hkv, v_cache, v_scale, kv_scale, blk, g, t % KVQO_BLOCK, d);
+                }
+            }
+    }
+    return 0;
+}
+
+/* Decode-step attention of one query head h of sequence b over the paged cache, in fp64:
+ *   g = h / (Hq/Hkv), n = context_lens[b];
+ *   z_t = sm_scale * sum_d q[b][h][d] * k^[t][d]      for t < n;
+ *   out[d] = sum_t exp(z_t - max z) v^[t][d] / sum_t exp(z_t - max z).
+ * q is fp16 bits [B][Hq][128]; out is 128 doubles.  n == 0 gives zeros.  Returns 0 or -1.      */
+int kvqo_decode_attn_head(int dtype, int Hkv, int Hq, const uint8_t *k_cache, const uint8_t *v_cache,
+                          const float *k_scale, const float *v_scale, float kv_scale,
+                          const uint16_t *q, float sm_scale, const int32_t *block_tables,
+                          int max_blocks_per_seq, const int32_t *context_lens, int b, int h,
+                          double *out)
+{
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8)
+        return -1;
+    if (Hkv <= 0 || Hq % Hkv != 0)
+        return -1;
+    int G = Hq / Hkv;
+    int g = h / G;
+    int n = context_lens[b];
+    for (int d = 0; d < KVQO_DIM; ++d)
+        out[d] = 0.0;
+    if (n <= 0)
+        return 0;
+    double qd[KVQO_DIM];
+    for (int d = 0; d < KVQO_DIM; ++d)
+        qd[d] = kvqo_fp16_to_double(q[((size_t)b * Hq + h) * KVQO_DIM + d]);
+    double *z = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!z)
+        return -1;
+    double zmax = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        int blk = block_tables[(size_t)b * max_blocks_per_seq + t / KVQO_BLOCK];
+        double acc = 0.0;
+        for (int d = 0; d < KVQO_DIM; ++d)
+            acc += qd[d] * dq_k(dtype, Hkv, k_cache, k_scale, kv_scale, blk, g, t % KVQO_BLOCK, d);
+        z[t] = (double)sm_scale * acc;
+        if (z[t] > zmax)
+            zmax = z[t];
+    }
+    double denom = 0.0;
+    for (int t = 0; t < n; ++t) {
+        double w = exp(z[t] - zmax);
+        int blk = block_tables[(size_t)b * max_blocks_per_seq + t / KVQO_BLOCK];
+        denom += w;
+        for (int d = 0; d < KVQO_DIM; ++d)
+            out[d] += w * dq_v(dtype, Hkv, v_cache, v_scale, kv_scale, blk, g, t % KVQO_BLOCK, d);
+    }
+    for (int d = 0; d < KVQO_DIM; ++d)
+        out[d] /= denom;
+    free(z);
+    return 0;
+}
+
+/* The same attention over dense, unquantized fp16 K/V rows of one (sequence, KV head):
+ * k, v are fp16 bits [n][128]; q is fp16 bits [128].  Used only to report how far the quantized
+ * cache moves the result; it is not a gate.                                                     */
+int kvqo_attn_fp16_dense(const uint16_t *q, const uint16_t *k, const uint16_t *v, int n,
+                         float sm_scale, double *out)
+{
+    for (int d = 0; d < KVQO_DIM; ++d)
+        out[d] = 0.0;
+    if (n <= 0)
+        return 0;
+    double *z = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!z)
+        return -1;
+    double zmax = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+        double acc = 0.0;
+        for (int d = 0; d < KVQO_DIM; ++d)
+            acc += kvqo_fp16_to_double(q[d]) * kvqo_fp16_to_double(k[(size_t)t * KVQO_DIM + d]);
+        z[t] = (double)sm_scale * acc;
+        if (z[t] > zmax)
+            zmax = z[t];
+    }
+    double denom = 0.0;
+    for (int t = 0; t < n; ++t) {
+        double w = exp(z[t] - zmax);
+        denom += w;
+        for (int d = 0; d < KVQO_DIM; ++d)
+            out[d] += w * kvqo_fp16_to_double(v[(size_t)t * KVQO_DIM + d]);
+    }
+    for (int d = 0; d < KVQO_DIM; ++d)
+        out[d] /= denom;
+    free(z);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Array forms of the element functions above (plain loops), so the tests can sweep inputs.      */
+void kvqo_fp8_decode_array(int fmt, const uint8_t *codes, int n, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = kvqo_fp8_decode(fmt, codes[i]);
+}
+
+void kvqo_fp8_encode_array(int fmt, const float *y, int n, uint8_t *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = kvqo_fp8_encode(fmt, y[i]);
+}
+
+void kvqo_fp8_quantize_array(int fmt, const uint16_t *x, int n, float kv_scale, uint8_t *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = kvqo_fp8_quantize(fmt, x[i], kv_scale);
+}
+
+void kvqo_fp16_to_double_array(const uint16_t *x, int n, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = kvqo_fp16_to_double(x[i]);
+}
+
+void kvqo_int8_quantize_rows(const uint16_t *x, int rows, int n, int8_t *q, float *s)
+{
+    for (int r = 0; r < rows; ++r)
+        kvqo_int8_quantize_row(x + (size_t)r * n, n, q + (size_t)r * n, s + r);
+}

@@ -1,0 +1,121 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case copies the oracle's C source, plants one mistake (a wrong bias, a dropped term, a
+transposed layout, a wrong index, a rounding mode), builds it with gcc into a temporary directory
+and runs a set of the pins against it; at least one pin must fail.  Everything here runs on the
+CPU; the shipped oracle is never modified.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import build as obuild
+
+import test_oracle_attention as TA
+import test_oracle_codec as TC
+import test_oracle_int8 as TI
+
+MUTATIONS = {
+    "decode-exponent-off-by-one": (
+        "v = ldexp((double)((1 << F.mbits) + m), e - F.bias - F.mbits);",
+        "v = ldexp((double)((1 << F.mbits) + m), e - F.bias - F.mbits + 1);"),
+    "encode-round-half-up": (
+        "double M = nearbyint((ldexp(a, -e) - 1.0) * (double)(1 << F.mbits));",
+        "double M = floor(0.5 + (ldexp(a, -e) - 1.0) * (double)(1 << F.mbits));"),
+    "encode-no-saturation": (
+        "        a = F.max_finite;                       /* saturation, also for +-inf */",
+        "        a = a;"),
+    "encode-subnormal-step": (
+        "double M = nearbyint(ldexp(a, F.bias - 1 + F.mbits));",
+        "double M = nearbyint(ldexp(a, F.bias + F.mbits));"),
+    "encode-drops-sign": (
+        "uint8_t sign = signbit(y) ? 0x80 : 0x00;",
+        "uint8_t sign = 0x00;"),
+    "e4m3-nan-code-finite": (
+        "if (fmt == KVQO_E4M3 && e == 15 && m == 7)",
+        "if (fmt == KVQO_E4M3 && e == 16)"),
+    "fp16-exponent-bias": (
+        "v = ldexp((double)(1024 + f), e - 25);",
+        "v = ldexp((double)(1024 + f), e - 24);"),
+    "int8-scale-128": (
+        "float s = amax / 127.0f;",
+        "float s = amax / 128.0f;"),
+    "int8-v-uses-k-scale": (
+        "return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, t)];",
+        "return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, 0)];"),
+    "attn-drops-sm-scale": (
+        "z[t] = (double)sm_scale * acc;\n        if (z[t] > zmax)\n            zmax = z[t];\n    }\n    double denom = 0.0;\n    for (int t = 0; t < n; ++t) {\n        double w = exp(z[t] - zmax);\n        int blk",
+        "z[t] = acc;\n        if (z[t] > zmax)\n            zmax = z[t];\n    }\n    double denom = 0.0;\n    for (int t = 0; t < n; ++t) {\n        double w = exp(z[t] - zmax);\n        int blk"),
+    "attn-gqa-index": (
+        "int g = h / G;",
+        "int g = h % Hkv;"),
+    "attn-denominator": (
+        "        out[d] /= denom;\n    free(z);\n    return 0;\n}\n\n/* The same attention",
+        "        out[d] /= (denom + 1.0);\n    free(z);\n    return 0;\n}\n\n/* The same attention"),
+    "v-layout-token-major": (
+        "return (((size_t)blk * Hkv + g) * KVQO_DIM + d) * KVQO_BLOCK + t;",
+        "return (((size_t)blk * Hkv + g) * KVQO_BLOCK + t) * KVQO_DIM + d;"),
+    "append-position-reversed": (
+        "int p = context_lens[b] - n_b + j;",
+        "int p = context_lens[b] - 1 - j;"),
+}
+
+
+def _pins():
+    w = None
+
+    def widths():
+        nonlocal w
+        if w is None:
+            import json
+            here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fp8_formats.json")
+            with open(here) as f:
+                g = json.load(f)
+            w = ({TC.E4M3: g["formats"]["E4M3"], TC.E5M2: g["formats"]["E5M2"]}, g)
+        return w
+
+    o = oracle
+    return [
+        lambda: TC.test_decode_table_matches_bit_layout(o, widths(), TC.E4M3),
+        lambda: TC.test_decode_table_matches_bit_layout(o, widths(), TC.E5M2),
+        lambda: TC.test_fp16_to_double_matches_numpy(o),
+        lambda: TC.test_encoder_exhaustive_fp16_bruteforce(o, widths(), TC.E4M3, 3.0),
+        lambda: TC.test_encoder_exhaustive_fp16_bruteforce(o, widths(), TC.E5M2, 2.0 ** -7),
+        lambda: TC.test_encoder_direct_fp32_edges(o, widths(), TC.E4M3),
+        lambda: TC.test_encoder_direct_fp32_edges(o, widths(), TC.E5M2),
+        lambda: TI.test_int8_matches_numpy_rint(o, True),
+        lambda: TI.test_int8_zero_row_and_ties(o),
+        lambda: TA.test_append_layout_and_poison(o, TA.INT8),
+        lambda: TA.test_dequant_matches_independent_decode(o, TA.INT8),
+        lambda: TA.test_attention_matches_torch_sdpa_float64(o, TA.E4M3, 8, 2),
+        lambda: TA.test_attention_matches_torch_sdpa_float64(o, TA.INT8, 2, 2),
+    ]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found once in the oracle"
+    mut = tmp_path / "kvq_oracle_mut.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.run(["gcc", *obuild.CFLAGS, "-w", str(mut), "-o", str(lib), "-lm"], check=True)
+    saved = oracle._lib
+    oracle._lib = oracle.load(str(lib))
+    failed = []
+    try:
+        for i, pin in enumerate(_pins()):
+            try:
+                with np.errstate(all="ignore"):
+                    pin()
+            except AssertionError:
+                failed.append(i)
+                break
+    finally:
+        oracle._lib = saved
+    assert failed, f"no pin caught the planted mistake {name!r}"
