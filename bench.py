@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the 8-bit paged KV cache on one MI355X.
+
+A step is one decode step of one attention layer: kvq_append of one new token per sequence, then
+kvq_paged_decode_attn (split-K partition kernel + merge kernel).  Inputs are seeded synthetic
+tensors already resident in HBM.  The timed loop walks over `--layers` copies of the layer's cache
+so consecutive steps read different memory (the 256 MB last-level cache cannot serve a step from
+the previous one).
+
+Prints one JSON line: achieved HBM GB/s of the whole step (algorithmic bytes / step time), with
+tokens/s, the roofline of the dominant kernel (the attention partition kernel, timed with HIP
+events on its own stream) and the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8-KV paged decode attention: achieved HBM GB/s (% of peak), tokens/s"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+DEFAULT_WORKLOAD = "llama2-7b-mha-e4m3"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "quantized_kv_cache_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, digest: str):
+    """HBM bytes per launch of the partition kernel from the committed rocprofv3 --pmc summary,
+    only if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"pmc_attn_partition_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_digest") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, threads: int, budget_s: float, scale: float):
+    """The oracle as it stands (C, fp64): append + attention for a prefix of the batch, timed on
+    this host; reported in the metric's unit (algorithmic GB/s of the sample)."""
+    import numpy as np
+
+    import oracle
+    from quantized_kv_cache_03_amd import workloads as W
+
+    ctx_all = W.context_lens(w)
+    ch = W.outlier_channels(w)
+    # a bounded sample: the first sequences of the batch, all their heads
+    nseq = 0
+    est = 0.0
+    per_tok_head_s = 2.5e-6  # rough single-thread cost of one (token, head) of append+attention
+    while nseq < len(ctx_all):
+        est += ctx_all[nseq] * w.num_q_heads * per_tok_head_s / max(1, threads)
+        nseq += 1
+        if est > budget_s:
+            break
+    seqs = list(range(nseq))
+    ctx = ctx_all[seqs].astype(np.int32)
+    sub = w.scaled(name=w.name + "-cpu-sample", batch=len(seqs), context=("list", ctx.tolist()))
+    bt, nb = W.block_tables(sub, ctx)
+    rows = [W.kv_rows(w, b, int(ctx[i]), ch) for i, b in enumerate(seqs)]
+    k = np.concatenate([r[0] for r in rows])
+    v = np.concatenate([r[1] for r in rows])
+    cu = np.zeros(len(seqs) + 1, np.int32)
+    cu[1:] = np.cumsum(ctx)
+    q = W.query(w)[seqs]
+    dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8}[w.dtype]
+    cache = oracle.Cache(dt, nb, w.num_kv_heads, scale)
+    t0 = time.perf_counter()
+    oracle.append(cache, k, v, bt, ctx, cu)  # the prefill of the sample's rows (single-threaded)
+    t1 = time.perf_counter()
+    # the timed step: the append of one token per sequence + attention over the whole sample
+    last = cu[1:] - 1
+    oracle.append(cache, k[last], v[last], bt, ctx)
+    oracle.decode_attn(cache, q, bt, ctx, threads=threads)
+    t2 = time.perf_counter()
+    per_tok = 2 * 128 + (8 if w.dtype == "int8" else 0)
+    bytes_ = (int(ctx.sum()) * w.num_kv_heads * per_tok + 2 * len(seqs) * w.num_q_heads * 128 * 2
+              + 4 * int(((ctx + 15) // 16).sum()) + 4 * len(seqs))
+    step_s = t2 - t1
+    return {"value": bytes_ / step_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(seqs)} of {len(ctx_all)} sequences (sum ctx {int(ctx.sum())}), "
+                      f"all {w.num_q_heads} heads: one append + fp64 attention, "
+                      f"{step_s:.2f} s; prefill of the sample not timed ({t1 - t0:.1f} s)",
+            "tokens_per_s": len(seqs) / step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--layers", type=int, default=4, help="cache copies the steps rotate over")
+    ap.add_argument("--partition", type=int, default=None, help="override the split-K partition size")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode kernels run on a single MI355X and this build "
+              "has no multi-GPU path (see the design notes on how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_kv_cache_03_amd import harness, kvq, workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = W.WORKLOADS[args.workload]
+    if args.partition is not None:
+        w = w.scaled(name=w.name, partition_size=args.partition)
+    log(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype} "
+        f"partition={w.partition_size}")
+    t0 = time.time()
+    case = harness.DeviceCase(w, verbose=False)
+    log(f"[bench] cache filled in {time.time() - t0:.1f} s: {case.num_blocks} blocks, "
+        f"sum ctx {int(case.ctx.sum())}")
+    # layer copies: same codes, distinct memory
+    layers = [case.cache]
+    for _ in range(args.layers - 1):
+        c = case.cache
+        layers.append(kvq.PagedKVCache(c.dtype, c.k_cache.clone(), c.v_cache.clone(),
+                                       None if c.k_scale is None else c.k_scale.clone(),
+                                       None if c.v_scale is None else c.v_scale.clone(), c.kv_scale))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        case.cache = layers[i % len(layers)]
+        case.step(stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    kvq.timing_begin(args.steps)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    main_ms, main_n, merge_ms, merge_n = kvq.timing_end()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    step_bytes = case.algorithmic_bytes()
+    attn_bytes = case.attention_bytes()
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    main_avg_ms = main_ms / max(1, main_n)
+    merge_avg_ms = merge_ms / max(1, merge_n) if merge_n else 0.0
+    achieved = attn_bytes / (main_avg_ms * 1e-3) / 1e9
+    digest = kernel_source_digest()
+    traffic = load_traffic(w.name, digest)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        threads = max(1, min(threads, 16))
+        log(f"[bench] cpu baseline: oracle on {threads} threads")
+        cpu = cpu_baseline(w, threads, args.cpu_budget_s, case.kv_scale)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": 128,
+            "block_size": 16,
+            "context": list(w.context),
+            "sum_context": int(case.ctx.sum()),
+            "block_table": w.table,
+            "kv_cache_dtype": w.dtype,
+            "kv_scale": case.kv_scale,
+            "partition_size": w.partition_size,
+            "layers_rotated": args.layers,
+        },
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "kv_tokens_per_s": round(int(case.ctx.sum()) / (ms_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "wall_s_timed_region": round(wall, 4),
+        "kernels_ms": {"attn_partition_avg": round(main_avg_ms, 5),
+                       "attn_merge_avg": round(merge_avg_ms, 5)},
+        "roofline": {
+            "kernel": f"attn_partition_valu<{w.dtype}>",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": attn_bytes,
+            "kernel_source_digest": digest,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

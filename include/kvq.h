@@ -1,0 +1,164 @@
+/*
+ * kvq.h -- C ABI of the 8-bit paged KV cache for AMD MI355X (gfx950).
+ *
+ * One decode step of one attention layer over a paged KV cache whose K and V are stored as 8-bit
+ * codes and dequantized on read, the arithmetic running in fp16/fp32:
+ *
+ *   "Accelerating Inference with FP8 KV Cache" (text-generation-inference docs):
+ *     opening section    -- K/V are stored as FP8, computation runs at FP16;
+ *     "FP8 Formats: E4M3 and E5M2" -- the OCP E4M3 (1/4/3 bits) and E5M2 (1/5/2 bits) layouts and a
+ *                           per-tensor FP32 scaling factor;
+ *     "FP8 E4M3 KV Cache" -- the scale defaults to 1.0; the names fp8 / fp8_e5m2.
+ *   "[Feature] TurboMind support W8A8 or FP8 KV Cache" (lmdeploy issue thread):
+ *     the online INT8 KV cache, read here as symmetric INT8 with one fp32 scale per (token, head).
+ *   "[QST] Scale factors and benchmarks" (QQQ issue thread):
+ *     the cache lives in a paged-attention serving stack: fixed-size blocks of tokens reached
+ *     through a per-sequence block table.
+ *
+ * Numerics (bit-exact contract of the cache bytes):
+ *   FP8 code   = enc(fl32(fl32(x) / kv_scale)), x the fp16 input: one correctly rounded fp32
+ *                division, then round to nearest with ties to the even code, finite overflow and
+ *                +-inf saturating to +-max (E4M3 448, E5M2 57344), NaN -> sign|0x7F, signed zero
+ *                and subnormals kept.  Decode: value = dec(code) * kv_scale.
+ *   INT8 codes = per (token, KV head) row of 128 values: s = fl32(amax / 127),
+ *                q = clamp(rne(fl32(x / s)), -127, 127); an all-zero row gives s = 0, q = 0.
+ *                Decode: value = q * s.  Inputs are assumed finite.
+ *
+ * Memory layout (all device memory, caller-owned, dense, no padding):
+ *   K codes  uint8 [num_blocks][num_kv_heads][16 tokens][128 dims]   (token-major tile, 2 KiB)
+ *   V codes  uint8 [num_blocks][num_kv_heads][128 dims][16 tokens]   (dim-major tile, 2 KiB)
+ *   INT8 scales  float [num_blocks][num_kv_heads][16 tokens], one array for K and one for V
+ *   block_tables int32 [batch][max_blocks_per_seq]: logical block i of sequence b is physical block
+ *                block_tables[b][i]; entries past a sequence's last block are never read.
+ *   context_lens int32 [batch]: the number of tokens of each sequence after the append.
+ *   q, out       fp16 [batch][num_q_heads][128];  query head h reads KV head h / (Hq / Hkv).
+ *
+ * Conventions:
+ *   - head_dim must be 128 and block_size 16; Hq must be a multiple of Hkv with Hq / Hkv <= 16.
+ *   - Every call validates its host-side arguments, enqueues its kernels on `stream` (a
+ *     hipStream_t; NULL is the legacy default stream) and returns without synchronizing.
+ *   - The library allocates no device memory; the split-K workspace is passed in by the caller.
+ *   - Return value: KVQ_OK (0) or a negative KVQ_ERR_*; kvq_last_error() then gives a message
+ *     (per calling thread).  No call aborts or throws.
+ *   - Device-side contract, not checked (violations are undefined behaviour): block ids are in
+ *     [0, num_blocks); 0 <= context_lens[b] <= min(max_context_len, 16 * max_blocks_per_seq);
+ *     every pointer addresses memory of the documented size on the current device.
+ *   - Functions hold no state across calls (apart from the optional kernel-timing hook) and may be
+ *     called concurrently on different streams for disjoint outputs.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_FP8_E4M3 = 1, /* OCP E4M3 with per-tensor fp32 kv_scale ("fp8", "fp8_e4m3")        */
+    KVQ_FP8_E5M2 = 2, /* OCP E5M2 with per-tensor fp32 kv_scale, usually 1.0 ("fp8_e5m2")  */
+    KVQ_INT8 = 3      /* symmetric INT8, one fp32 scale per (token, KV head) ("int8")      */
+} kvq_dtype;
+
+enum {
+    KVQ_OK = 0,
+    KVQ_ERR_ARG = -1,       /* NULL pointer, negative size, non-finite scale, ...          */
+    KVQ_ERR_DTYPE = -2,     /* unknown kvq_dtype                                            */
+    KVQ_ERR_SHAPE = -3,     /* unsupported head_dim / block_size / head grouping            */
+    KVQ_ERR_WORKSPACE = -4, /* split-K workspace missing or too small                       */
+    KVQ_ERR_HIP = -5        /* the HIP runtime reported an error at launch                  */
+};
+
+#define KVQ_HEAD_DIM 128
+#define KVQ_BLOCK_SIZE 16
+#define KVQ_MAX_GROUP 16
+
+/* Cache descriptor: a host struct read at call time; the pointers are device pointers. */
+typedef struct {
+    kvq_dtype dtype;
+    int32_t num_blocks;
+    int32_t block_size;   /* must be 16 */
+    int32_t num_kv_heads;
+    int32_t head_dim;     /* must be 128 */
+    uint8_t *k_cache;     /* K codes, layout above */
+    uint8_t *v_cache;     /* V codes, layout above */
+    float *k_scale;       /* INT8 only: [num_blocks][Hkv][16]; NULL for FP8 */
+    float *v_scale;       /* INT8 only: [num_blocks][Hkv][16]; NULL for FP8 */
+    float kv_scale;       /* FP8 only: per-tensor scale shared by K and V, finite and > 0;
+                             1.0 is the default ("FP8 E4M3 KV Cache" section) */
+} kvq_cache;
+
+/* Quantize new K/V rows and write them into their paged slots ("FP8 Formats: E4M3 and E5M2";
+ * the online INT8 cache of the lmdeploy thread).
+ *   k_new, v_new : fp16 [num_new_rows][Hkv][128], device.
+ *   cu_new_lens  : int32 [batch + 1] device row offsets (sequence b owns rows cu[b] .. cu[b+1]-1),
+ *                  or NULL for exactly one new row per sequence (then num_new_rows == batch).
+ *   The j-th of sequence b's n_b new rows goes to position p = context_lens[b] - n_b + j, i.e.
+ *   block block_tables[b][p / 16], slot p % 16.  No other byte of the cache is written.
+ *   With cu_new_lens, num_new_rows must equal cu[batch] (the caller's host-side copy). */
+int kvq_append(const kvq_cache *cache, const void *k_new, const void *v_new,
+               const int32_t *cu_new_lens, int32_t num_new_rows, const int32_t *block_tables,
+               int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t batch,
+               void *stream);
+
+/* Bytes of split-K workspace kvq_paged_decode_attn needs for these sizes (0 when one pass
+ * suffices).  partition_size 0 means a single pass over each whole context. */
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* Decode-step attention over the paged 8-bit cache (the opening section of "Accelerating
+ * Inference with FP8 KV Cache": stored as FP8, computed at higher precision):
+ *   out[b][h] = sum_t softmax_t(sm_scale * q[b][h] . k^[t]) v^[t] over t < context_lens[b],
+ *   with k^, v^ the dequantized rows of KV head h / (Hq / Hkv).  context_lens[b] == 0 gives zeros.
+ *   sm_scale       : finite; 1/sqrt(128) is the usual value.
+ *   max_context_len: host-side upper bound of context_lens (sizes the grid without a device read).
+ *   partition_size : 0 for one pass per sequence, else a multiple of 16 (flash-decoding split-K:
+ *                    each partition writes fp32 (max, sum, unnormalized output) partials into
+ *                    `workspace`, and a second kernel merges them).  For a fixed partition size the
+ *                    result is bitwise deterministic.
+ *   workspace      : device memory of at least kvq_decode_workspace_size(...) bytes (may be NULL
+ *                    when that size is 0); its contents need no initialization. */
+int kvq_paged_decode_attn(const kvq_cache *cache, const void *q, void *out, int32_t num_q_heads,
+                          float sm_scale, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                          const int32_t *context_lens, int32_t batch, int32_t max_context_len,
+                          int32_t partition_size, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Dequantize the cache into dense fp32 [batch][Hkv][max_context_len][128] arrays for K and V:
+ * each element is fl32(dec(code) * kv_scale) (FP8) or fl32(q * s) (INT8), one rounding.  Slots
+ * t >= context_lens[b] are left untouched.  For inspection and tests; not on the decode path. */
+int kvq_dequant(const kvq_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *context_lens, int32_t batch, int32_t max_context_len, float *k_out,
+                float *v_out, void *stream);
+
+/* "fp8" | "fp8_e4m3" -> KVQ_FP8_E4M3, "fp8_e5m2" -> KVQ_FP8_E5M2, "int8" -> KVQ_INT8
+ * (the --kv-cache-dtype names of "Accelerating Inference with FP8 KV Cache").
+ * Returns KVQ_OK or KVQ_ERR_DTYPE (out untouched). */
+int kvq_dtype_from_string(const char *s, kvq_dtype *out);
+
+/* Static text of a status code. */
+const char *kvq_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+/* Kernel-timing hook for benchmarks: after kvq_timing_begin(capacity), each kvq_paged_decode_attn
+ * call records a HIP event pair around its main (partition) kernel and another around its merge
+ * kernel, on the call's stream, for up to `capacity` calls.  kvq_timing_end() waits for the
+ * events, returns the summed milliseconds and counts, and releases them.  Events are created in
+ * kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a time.
+ * Returns KVQ_OK or KVQ_ERR_ARG / KVQ_ERR_HIP. */
+int kvq_timing_begin(int32_t capacity);
+int kvq_timing_end(double *main_ms_total, int32_t *main_count, double *merge_ms_total,
+                   int32_t *merge_count);
+
+/* Library version, "major.minor.patch". */
+const char *kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

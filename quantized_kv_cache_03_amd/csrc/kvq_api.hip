@@ -1,0 +1,308 @@
+// kvq_api.hip -- the extern "C" surface declared in include/kvq.h: argument validation, split-K
+// planning, launches on the caller's stream, error reporting and the kernel-timing hook.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return KVQ_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(KVQ_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+int check_cache(const kvq_cache* c) {
+    if (!c) return fail(KVQ_ERR_ARG, "cache descriptor is NULL");
+    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8)
+        return fail(KVQ_ERR_DTYPE, "unknown kv cache dtype %d", (int)c->dtype);
+    if (c->head_dim != KVQ_HEAD_DIM)
+        return fail(KVQ_ERR_SHAPE, "head_dim %d is not supported (must be %d)", c->head_dim, KVQ_HEAD_DIM);
+    if (c->block_size != KVQ_BLOCK_SIZE)
+        return fail(KVQ_ERR_SHAPE, "block_size %d is not supported (must be %d)", c->block_size,
+                    KVQ_BLOCK_SIZE);
+    if (c->num_kv_heads <= 0) return fail(KVQ_ERR_SHAPE, "num_kv_heads %d must be positive", c->num_kv_heads);
+    if (c->num_blocks <= 0) return fail(KVQ_ERR_SHAPE, "num_blocks %d must be positive", c->num_blocks);
+    if (!c->k_cache || !c->v_cache) return fail(KVQ_ERR_ARG, "k_cache / v_cache pointer is NULL");
+    if (c->dtype == KVQ_INT8) {
+        if (!c->k_scale || !c->v_scale)
+            return fail(KVQ_ERR_ARG, "INT8 cache needs k_scale and v_scale arrays");
+    } else {
+        if (!(isfinite(c->kv_scale) && c->kv_scale > 0.0f))
+            return fail(KVQ_ERR_ARG, "kv_scale %g must be finite and positive", (double)c->kv_scale);
+    }
+    return KVQ_OK;
+}
+
+int check_common(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                 int32_t batch) {
+    if (batch < 0) return fail(KVQ_ERR_ARG, "batch %d is negative", batch);
+    if (batch == 0) return KVQ_OK;
+    if (!block_tables || !context_lens) return fail(KVQ_ERR_ARG, "block_tables / context_lens is NULL");
+    if (max_blocks_per_seq <= 0)
+        return fail(KVQ_ERR_ARG, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
+    return KVQ_OK;
+}
+
+// Split-K plan: partitions in the grid and tokens per partition.
+struct Plan {
+    int32_t P;
+    int32_t PS;
+};
+
+Plan plan(int32_t max_context_len, int32_t partition_size) {
+    Plan p;
+    if (partition_size <= 0) {
+        const int32_t whole = ((max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE) * KVQ_BLOCK_SIZE;
+        p.PS = whole > 0 ? whole : KVQ_BLOCK_SIZE;
+        p.P = 1;
+    } else {
+        p.PS = partition_size;
+        p.P = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+    }
+    return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// kernel-timing hook state
+struct Timing {
+    bool active = false;
+    int32_t capacity = 0;
+    int32_t used = 0;
+    std::vector<hipEvent_t> ev;  // 4 per call: main begin/end, merge begin/end
+    std::vector<int> has_merge;
+};
+Timing g_timing;
+
+void timing_release() {
+    for (hipEvent_t e : g_timing.ev)
+        if (e) (void)hipEventDestroy(e);
+    g_timing.ev.clear();
+    g_timing.has_merge.clear();
+    g_timing.active = false;
+    g_timing.capacity = g_timing.used = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_version(void) { return "0.1.0"; }
+
+const char* kvq_last_error(void) { return g_err; }
+
+const char* kvq_status_string(int status) {
+    switch (status) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_ARG: return "invalid argument";
+        case KVQ_ERR_DTYPE: return "unknown kv cache dtype";
+        case KVQ_ERR_SHAPE: return "unsupported shape";
+        case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int kvq_dtype_from_string(const char* s, kvq_dtype* out) {
+    if (!s || !out) return fail(KVQ_ERR_ARG, "NULL argument");
+    if (!strcmp(s, "fp8") || !strcmp(s, "fp8_e4m3")) *out = KVQ_FP8_E4M3;
+    else if (!strcmp(s, "fp8_e5m2")) *out = KVQ_FP8_E5M2;
+    else if (!strcmp(s, "int8")) *out = KVQ_INT8;
+    else return fail(KVQ_ERR_DTYPE, "unknown kv cache dtype name '%s'", s);
+    return ok();
+}
+
+int kvq_append(const kvq_cache* cache, const void* k_new, const void* v_new,
+               const int32_t* cu_new_lens, int32_t num_new_rows, const int32_t* block_tables,
+               int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch, void* stream) {
+    int st = check_cache(cache);
+    if (st) return st;
+    st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
+    if (st) return st;
+    if (num_new_rows < 0) return fail(KVQ_ERR_ARG, "num_new_rows %d is negative", num_new_rows);
+    if (!cu_new_lens && num_new_rows != batch)
+        return fail(KVQ_ERR_ARG, "without cu_new_lens, num_new_rows (%d) must equal batch (%d)",
+                    num_new_rows, batch);
+    if (batch == 0 || num_new_rows == 0) return ok();
+    if (!k_new || !v_new) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
+    if ((size_t)num_new_rows * (size_t)cache->num_kv_heads > 0x7FFFFFFFull)
+        return fail(KVQ_ERR_SHAPE, "too many new rows");
+    hipError_t e = kvq::launch_append(*cache, static_cast<const uint16_t*>(k_new),
+                                      static_cast<const uint16_t*>(v_new), cu_new_lens, num_new_rows,
+                                      block_tables, max_blocks_per_seq, context_lens, batch,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kvq_append");
+    return ok();
+}
+
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+    if (batch <= 0 || num_q_heads <= 0 || head_dim != KVQ_HEAD_DIM || max_context_len < 0) return 0;
+    const Plan p = plan(max_context_len, partition_size);
+    if (p.P <= 1) return 0;
+    const size_t rows = (size_t)batch * (size_t)num_q_heads * (size_t)p.P;
+    return align256(rows * KVQ_HEAD_DIM * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int32_t num_q_heads,
+                          float sm_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    int st = check_cache(cache);
+    if (st) return st;
+    st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
+    if (st) return st;
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+        return fail(KVQ_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    num_q_heads, cache->num_kv_heads);
+    if (num_q_heads / cache->num_kv_heads > KVQ_MAX_GROUP)
+        return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
+                    num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
+    if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
+    if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
+    if (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0)
+        return fail(KVQ_ERR_ARG, "partition_size %d must be 0 or a positive multiple of %d",
+                    partition_size, KVQ_BLOCK_SIZE);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
+        return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",
+                    max_context_len, max_blocks_per_seq, KVQ_BLOCK_SIZE);
+    if (batch == 0) return ok();
+    if (!q || !out) return fail(KVQ_ERR_ARG, "q / out is NULL");
+    if (batch > 65535 || num_q_heads > 65535)
+        return fail(KVQ_ERR_SHAPE, "batch and num_q_heads must be at most 65535");
+
+    const Plan p = plan(max_context_len, partition_size);
+    const size_t need = kvq_decode_workspace_size(batch, num_q_heads, KVQ_HEAD_DIM, max_context_len,
+                                                  partition_size);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(KVQ_ERR_WORKSPACE, "split-K workspace of %zu bytes needed, %zu given%s", need,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+
+    kvq::DecodeArgs a;
+    a.cache = cache;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.num_q_heads = num_q_heads;
+    a.sm_scale = sm_scale;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.batch = batch;
+    a.num_partitions = p.P;
+    a.partition_size = p.PS;
+    a.part_o = a.part_m = a.part_l = nullptr;
+    if (need > 0) {
+        const size_t rows = (size_t)batch * (size_t)num_q_heads * (size_t)p.P;
+        char* w = static_cast<char*>(workspace);
+        a.part_o = reinterpret_cast<float*>(w);
+        a.part_m = reinterpret_cast<float*>(w + align256(rows * KVQ_HEAD_DIM * sizeof(float)));
+        a.part_l = reinterpret_cast<float*>(w + align256(rows * KVQ_HEAD_DIM * sizeof(float)) +
+                                            align256(rows * sizeof(float)));
+    }
+
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    int slot = -1;
+    if (g_timing.active && g_timing.used < g_timing.capacity) {
+        slot = g_timing.used++;
+        for (int i = 0; i < 4; ++i) ev[i] = g_timing.ev[4 * slot + i];
+        g_timing.has_merge[slot] = p.P > 1;
+    }
+    hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), ev[0], ev[1], ev[2], ev[3]);
+    if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode_attn");
+    return ok();
+}
+
+int kvq_dequant(const kvq_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, int32_t batch, int32_t max_context_len, float* k_out,
+                float* v_out, void* stream) {
+    int st = check_cache(cache);
+    if (st) return st;
+    st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
+    if (st) return st;
+    if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
+        return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table", max_context_len);
+    if (batch == 0 || max_context_len == 0) return ok();
+    if (!k_out || !v_out) return fail(KVQ_ERR_ARG, "k_out / v_out is NULL");
+    if (batch > 65535 || cache->num_kv_heads > 65535)
+        return fail(KVQ_ERR_SHAPE, "batch and num_kv_heads must be at most 65535");
+    hipError_t e = kvq::launch_dequant(*cache, block_tables, max_blocks_per_seq, context_lens, batch,
+                                       max_context_len, k_out, v_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kvq_dequant");
+    return ok();
+}
+
+int kvq_timing_begin(int32_t capacity) {
+    if (capacity <= 0 || capacity > (1 << 20)) return fail(KVQ_ERR_ARG, "capacity %d out of range", capacity);
+    timing_release();
+    g_timing.ev.assign((size_t)capacity * 4, nullptr);
+    g_timing.has_merge.assign((size_t)capacity, 0);
+    for (auto& e : g_timing.ev) {
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            timing_release();
+            return hip_fail(r, "kvq_timing_begin");
+        }
+    }
+    g_timing.capacity = capacity;
+    g_timing.used = 0;
+    g_timing.active = true;
+    return ok();
+}
+
+int kvq_timing_end(double* main_ms_total, int32_t* main_count, double* merge_ms_total,
+                   int32_t* merge_count) {
+    if (!g_timing.active) return fail(KVQ_ERR_ARG, "no timing session is active");
+    double mt = 0.0, gt = 0.0;
+    int32_t mc = 0, gc = 0;
+    for (int s = 0; s < g_timing.used; ++s) {
+        float ms = 0.0f;
+        hipError_t r = hipEventSynchronize(g_timing.ev[4 * s + 1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[4 * s], g_timing.ev[4 * s + 1]);
+        if (r != hipSuccess) {
+            timing_release();
+            return hip_fail(r, "kvq_timing_end");
+        }
+        mt += ms;
+        ++mc;
+        if (g_timing.has_merge[s]) {
+            r = hipEventSynchronize(g_timing.ev[4 * s + 3]);
+            if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[4 * s + 2], g_timing.ev[4 * s + 3]);
+            if (r != hipSuccess) {
+                timing_release();
+                return hip_fail(r, "kvq_timing_end");
+            }
+            gt += ms;
+            ++gc;
+        }
+    }
+    if (main_ms_total) *main_ms_total = mt;
+    if (main_count) *main_count = mc;
+    if (merge_ms_total) *merge_ms_total = gt;
+    if (merge_count) *merge_count = gc;
+    timing_release();
+    return ok();
+}
+
+}  // extern "C"

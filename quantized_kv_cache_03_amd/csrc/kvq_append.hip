@@ -1,0 +1,129 @@
+// kvq_append.hip -- quantize new K/V rows into their paged slots.
+//
+// FP8: code = enc(fl32(x / kv_scale)) per element ("Accelerating Inference with FP8 KV Cache",
+// section "FP8 Formats: E4M3 and E5M2": E4M3/E5M2 with a per-tensor FP32 scale).
+// INT8: one fp32 scale per (token, KV head) row, s = fl32(amax / 127), q = clamp(rne(x / s))
+// (the online INT8 cache of "[Feature] TurboMind support W8A8 or FP8 KV Cache").
+//
+// One wave per (new row, KV head): lane l owns dims 2l and 2l+1 of the K row and the V row.
+// The append moves one token per sequence per decode step, so its cost is negligible next to the
+// attention read; it is written for exactness, not speed: a correctly rounded fp32 division
+// (hipcc's default), integer rounding on the binary32 pattern, no contraction.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+
+// Sequence of a row from the row offsets: the last b with cu[b] <= row (empty sequences are
+// skipped because their successor has the same offset).
+__device__ __forceinline__ int seq_of_row(const int32_t* cu, int batch, int row) {
+    int lo = 0, hi = batch;  // invariant: cu[lo] <= row < cu[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= row) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ float fp16_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+template <int DT>
+__global__ __launch_bounds__(64) void append_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
+    float* __restrict__ vs, float kv_scale, const uint32_t* __restrict__ k_new,
+    const uint32_t* __restrict__ v_new, const int32_t* __restrict__ cu, int32_t batch,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks, const int32_t* __restrict__ ctx,
+    int32_t Hkv) {
+    const int row = blockIdx.x;
+    const int g = blockIdx.y;
+    const int lane = threadIdx.x;
+
+    int b, n_b, j;
+    if (cu == nullptr) {
+        b = row; n_b = 1; j = 0;
+    } else {
+        b = seq_of_row(cu, batch, row);
+        n_b = cu[b + 1] - cu[b];
+        j = row - cu[b];
+    }
+    const int p = ctx[b] - n_b + j;
+    if (p < 0 || p / kBlock >= max_blocks) return;  // outside the documented contract: write nothing
+    const int blk = block_tables[(size_t)b * max_blocks + p / kBlock];
+    const int t = p % kBlock;
+    const size_t tile = ((size_t)blk * Hkv + g) * kTileBytes;
+
+    // two fp16 values per lane, K and V
+    const size_t src = ((size_t)row * Hkv + g) * (kDim / 2) + lane;
+    const uint32_t kw = k_new[src];
+    const uint32_t vw = v_new[src];
+    const float k0 = fp16_bits_to_float(kw & 0xFFFFu), k1 = fp16_bits_to_float(kw >> 16);
+    const float v0 = fp16_bits_to_float(vw & 0xFFFFu), v1 = fp16_bits_to_float(vw >> 16);
+
+    uint32_t kc0, kc1, vc0, vc1;
+    if constexpr (DT == KVQ_INT8) {
+        const float ka = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
+        const float va = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+        const float sk = ka / 127.0f;
+        const float sv = va / 127.0f;
+        auto q8 = [](float x, float s) -> uint32_t {
+            if (s == 0.0f) return 0u;
+            const float r = fminf(fmaxf(__builtin_rintf(x / s), -127.0f), 127.0f);
+            return (uint32_t)(int32_t)r & 0xFFu;
+        };
+        kc0 = q8(k0, ka == 0.0f ? 0.0f : sk);
+        kc1 = q8(k1, ka == 0.0f ? 0.0f : sk);
+        vc0 = q8(v0, va == 0.0f ? 0.0f : sv);
+        vc1 = q8(v1, va == 0.0f ? 0.0f : sv);
+        if (lane == 0) {
+            const size_t so = ((size_t)blk * Hkv + g) * kBlock + t;
+            ks[so] = (ka == 0.0f) ? 0.0f : sk;
+            vs[so] = (va == 0.0f) ? 0.0f : sv;
+        }
+    } else {
+        kc0 = encode_fp8<DT>(k0 / kv_scale);
+        kc1 = encode_fp8<DT>(k1 / kv_scale);
+        vc0 = encode_fp8<DT>(v0 / kv_scale);
+        vc1 = encode_fp8<DT>(v1 / kv_scale);
+    }
+    // K tile is token-major [16][128]: the two codes are adjacent
+    *reinterpret_cast<uint16_t*>(kc + tile + (size_t)t * kDim + 2 * lane) =
+        (uint16_t)(kc0 | (kc1 << 8));
+    // V tile is dim-major [128][16]: the two codes sit 16 bytes apart
+    vc[tile + (size_t)(2 * lane) * kBlock + t] = (uint8_t)vc0;
+    vc[tile + (size_t)(2 * lane + 1) * kBlock + t] = (uint8_t)vc1;
+}
+
+hipError_t launch_append(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* cu_new_lens, int32_t num_rows, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                         hipStream_t stream) {
+    if (num_rows == 0 || batch == 0) return hipSuccess;
+    const dim3 grid((unsigned)num_rows, (unsigned)c.num_kv_heads);
+    const auto* kw = reinterpret_cast<const uint32_t*>(k_new);
+    const auto* vw = reinterpret_cast<const uint32_t*>(v_new);
+    switch (c.dtype) {
+        case KVQ_FP8_E4M3:
+            append_kernel<KVQ_FP8_E4M3><<<grid, 64, 0, stream>>>(
+                c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.kv_scale, kw, vw, cu_new_lens, batch,
+                block_tables, max_blocks_per_seq, context_lens, c.num_kv_heads);
+            break;
+        case KVQ_FP8_E5M2:
+            append_kernel<KVQ_FP8_E5M2><<<grid, 64, 0, stream>>>(
+                c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.kv_scale, kw, vw, cu_new_lens, batch,
+                block_tables, max_blocks_per_seq, context_lens, c.num_kv_heads);
+            break;
+        default:
+            append_kernel<KVQ_INT8><<<grid, 64, 0, stream>>>(
+                c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.kv_scale, kw, vw, cu_new_lens, batch,
+                block_tables, max_blocks_per_seq, context_lens, c.num_kv_heads);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,143 @@
+// kvq_device.h -- device-side helpers of the HIP path (gfx950 only).
+//
+// FP8 / INT8 encode and decode written from the formats' definitions ("Accelerating Inference with
+// FP8 KV Cache", section "FP8 Formats: E4M3 and E5M2": OCP E4M3 = 1/4/3 bits, E5M2 = 1/5/2 bits;
+// the online INT8 cache of "[Feature] TurboMind support W8A8 or FP8 KV Cache"), plus wave-level
+// reductions.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDim = KVQ_HEAD_DIM;     // 128
+constexpr int kBlock = KVQ_BLOCK_SIZE; // 16
+constexpr int kTileBytes = kDim * kBlock;  // 2048 bytes per (block, KV head) tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------------------------------------
+// encode (append path).  y is the fp32 quotient x / kv_scale.
+//
+// Normal range: round the binary32 significand to M mantissa bits, ties to even, directly on the
+// bit pattern -- adding (half ulp - 1) plus the kept LSB and truncating rounds half to even, and a
+// carry out of the mantissa moves into the exponent field as it should.  The binary32 exponent
+// field (bias 127) is then rebased to the FP8 bias.  Subnormal range: the code is the number of
+// steps 2^(1-bias-M), rounded to nearest even; the value 2^M steps is the smallest normal code,
+// whose bit pattern is exactly 2^M.  Magnitudes at or above the largest finite value saturate:
+// every such value either rounds to it or overflows, and overflow saturates.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_fp8(float y) {
+    constexpr int M = (FMT == KVQ_FP8_E4M3) ? 3 : 2;
+    constexpr int BIAS = (FMT == KVQ_FP8_E4M3) ? 7 : 15;
+    constexpr uint32_t MAX_BITS = (FMT == KVQ_FP8_E4M3) ? 0x43E00000u   // 448
+                                                        : 0x47600000u;  // 57344
+    constexpr uint32_t MAX_CODE = (FMT == KVQ_FP8_E4M3) ? 0x7Eu : 0x7Bu;
+    constexpr uint32_t MIN_NORMAL_BITS = (uint32_t)(127 + 1 - BIAS) << 23;  // 2^(1-bias)
+    constexpr int SH = 23 - M;
+
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+    if (a >= MAX_BITS) return sign | MAX_CODE;         // saturation (covers +-inf)
+    if (a >= MIN_NORMAL_BITS) {
+        const uint32_t r = a + ((1u << (SH - 1)) - 1u) + ((a >> SH) & 1u);
+        return sign | ((r >> SH) - ((uint32_t)(127 - BIAS) << M));
+    }
+    // exact power-of-two scaling, then round half to even (v_rndne_f32)
+    const float steps = __uint_as_float(a) * (float)(1u << (BIAS - 1 + M));
+    return sign | (uint32_t)__builtin_rintf(steps);
+}
+
+// ------------------------------------------------------------------------------------------------
+// decode to exact fp16 pairs.  `w` holds four codes (byte i = code i); `SEL` picks bytes
+// (2*SEL, 2*SEL+1), returned as (lo, hi) halves.
+
+// E4M3 -> fp16 with the gfx950 converter (unit scale): every E4M3 value, subnormals included, is
+// a normal binary16 number, so the conversion is exact.
+template <int SEL>
+__device__ __forceinline__ half2_t e4m3x2_to_f16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL != 0);
+}
+
+// E5M2 -> fp16 by placement: E5M2 is binary16 with its low 8 fraction bits dropped (same sign,
+// exponent width and bias), so the code becomes the high byte of the half.
+template <int SEL>
+__device__ __forceinline__ half2_t e5m2x2_to_f16(uint32_t w) {
+    constexpr uint32_t sel = (SEL == 0) ? 0x010C000Cu : 0x030C020Cu;
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, sel));
+}
+
+// INT8 -> fp16: put each signed byte in the low byte of a half with high byte 0x64 and its sign
+// bit flipped, which is the binary16 number 1024 + (q + 128); subtracting 1152 leaves q exactly
+// (all integers below 2048 are exact in binary16).
+template <int SEL>
+__device__ __forceinline__ half2_t int8x2_to_f16(uint32_t w) {
+    constexpr uint32_t sel = (SEL == 0) ? 0x0C010C00u : 0x0C030C02u;
+    const uint32_t x = __builtin_amdgcn_perm(0u, w, sel) ^ 0x64806480u;
+    return __builtin_bit_cast(half2_t, x) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+}
+
+template <int DT, int SEL>
+__device__ __forceinline__ half2_t codes_to_f16(uint32_t w) {
+    if constexpr (DT == KVQ_FP8_E4M3) return e4m3x2_to_f16<SEL>(w);
+    else if constexpr (DT == KVQ_FP8_E5M2) return e5m2x2_to_f16<SEL>(w);
+    else return int8x2_to_f16<SEL>(w);
+}
+
+__device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
+    return __builtin_amdgcn_fdot2(a, b, c, false);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    half2_t h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// ------------------------------------------------------------------------------------------------
+// cross-lane helpers (wave64)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, true));
+}
+// sum over each aligned group of 8 lanes: xor 1, xor 2 (quad permutes), then the mirrored half-row
+__device__ __forceinline__ float sum8(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    return v;
+}
+// reductions across the eight groups of 8 lanes (lanes l, l^8, l^16, ..., l^56)
+__device__ __forceinline__ float max_across8(float v) {
+    v = fmaxf(v, dpp<0x128>(v));  // row_ror:8 == xor 8 within a 16-lane row
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float sum_across8(float v) {
+    v += dpp<0x128>(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    return max_across8(v);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace kvq

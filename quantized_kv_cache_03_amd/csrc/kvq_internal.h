@@ -1,0 +1,43 @@
+// kvq_internal.h -- host-side launchers shared between the ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Launch parameters of the decode-attention kernels, resolved by the ABI layer.
+struct DecodeArgs {
+    const kvq_cache* cache;
+    const uint16_t* q;        // fp16 bits [B][Hq][128]
+    uint16_t* out;            // fp16 bits [B][Hq][128]
+    int32_t num_q_heads;
+    float sm_scale;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* context_lens;
+    int32_t batch;
+    int32_t num_partitions;   // grid extent over partitions (>= 1)
+    int32_t partition_size;   // tokens per partition; covers the whole context when num_partitions == 1
+    float* part_o;            // [B][Hq][P][128] (NULL when num_partitions == 1)
+    float* part_m;            // [B][Hq][P]
+    float* part_l;            // [B][Hq][P]
+};
+
+hipError_t launch_append(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* cu_new_lens, int32_t num_rows, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                         hipStream_t stream);
+
+hipError_t launch_dequant(const kvq_cache& c, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                          float* k_out, float* v_out, hipStream_t stream);
+
+// Partition kernel, then (when num_partitions > 1) the merge kernel.  The optional events are
+// recorded around each of the two launches (kernel-timing hook).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
+                         hipEvent_t main_end, hipEvent_t merge_begin, hipEvent_t merge_end);
+
+}  // namespace kvq

@@ -1,0 +1,226 @@
+"""Python binding of ``libkvq.so`` (the C ABI in ``include/kvq.h``): argument marshalling only.
+
+Torch supplies device memory and the current HIP stream; every step of the decode path runs in
+the library's HIP kernels.  Importing this module loads the library and raises ``ImportError``
+if it is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+FP8_E4M3, FP8_E5M2, INT8 = 1, 2, 3
+HEAD_DIM = 128
+BLOCK_SIZE = 16
+DTYPE_NAMES = {"fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3, "fp8_e5m2": FP8_E5M2, "int8": INT8}
+
+OK, ERR_ARG, ERR_DTYPE, ERR_SHAPE, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+                      f"g.build()' or python quantized_kv_cache_03_amd/build.py)")
+
+
+class KvqCache(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int),
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p),
+        ("v_cache", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("kv_scale", ctypes.c_float),
+    ]
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+lib = ctypes.CDLL(LIB_PATH)
+lib.kvq_append.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _vp]
+lib.kvq_append.restype = ctypes.c_int
+lib.kvq_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+lib.kvq_decode_workspace_size.restype = _sz
+lib.kvq_paged_decode_attn.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _i32, _f32, _vp, _i32,
+                                      _vp, _i32, _i32, _i32, _vp, _sz, _vp]
+lib.kvq_paged_decode_attn.restype = ctypes.c_int
+lib.kvq_dequant.argtypes = [ctypes.POINTER(KvqCache), _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]
+lib.kvq_dequant.restype = ctypes.c_int
+lib.kvq_dtype_from_string.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]
+lib.kvq_dtype_from_string.restype = ctypes.c_int
+lib.kvq_status_string.argtypes = [ctypes.c_int]
+lib.kvq_status_string.restype = ctypes.c_char_p
+lib.kvq_last_error.argtypes = []
+lib.kvq_last_error.restype = ctypes.c_char_p
+lib.kvq_timing_begin.argtypes = [_i32]
+lib.kvq_timing_begin.restype = ctypes.c_int
+lib.kvq_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32),
+                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
+lib.kvq_timing_end.restype = ctypes.c_int
+lib.kvq_version.argtypes = []
+lib.kvq_version.restype = ctypes.c_char_p
+
+EXPORTS = ["kvq_append", "kvq_decode_workspace_size", "kvq_paged_decode_attn", "kvq_dequant",
+           "kvq_dtype_from_string", "kvq_status_string", "kvq_last_error", "kvq_timing_begin",
+           "kvq_timing_end", "kvq_version"]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.kvq_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib.kvq_status_string(status).decode()} ({status}): {msg}")
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise KvqError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors passed to the library must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dtype_from_string(name: str) -> int:
+    out = ctypes.c_int(0)
+    _check(lib.kvq_dtype_from_string(name.encode(), ctypes.byref(out)), "kvq_dtype_from_string")
+    return out.value
+
+
+@dataclass
+class PagedKVCache:
+    """Device tensors of one layer's paged cache (layouts as in kvq.h)."""
+    dtype: int
+    k_cache: torch.Tensor           # uint8 [num_blocks][Hkv][16][128]
+    v_cache: torch.Tensor           # uint8 [num_blocks][Hkv][128][16]
+    k_scale: torch.Tensor | None    # float32 [num_blocks][Hkv][16] (INT8)
+    v_scale: torch.Tensor | None
+    kv_scale: float = 1.0
+
+    @property
+    def num_blocks(self) -> int:
+        return self.k_cache.shape[0]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_cache.shape[1]
+
+    @staticmethod
+    def allocate(dtype, num_blocks: int, num_kv_heads: int, kv_scale: float = 1.0,
+                 device="cuda", poison: bool = True) -> "PagedKVCache":
+        if isinstance(dtype, str):
+            dtype = dtype_from_string(dtype)
+        fill = 0x7F if poison else 0
+        k = torch.full((num_blocks, num_kv_heads, BLOCK_SIZE, HEAD_DIM), fill, dtype=torch.uint8, device=device)
+        v = torch.full((num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE), fill, dtype=torch.uint8, device=device)
+        ks = vs = None
+        if dtype == INT8:
+            ks = torch.full((num_blocks, num_kv_heads, BLOCK_SIZE), float("nan") if poison else 0.0,
+                            dtype=torch.float32, device=device)
+            vs = torch.full_like(ks, float("nan") if poison else 0.0)
+        return PagedKVCache(dtype, k, v, ks, vs, float(kv_scale))
+
+    def descriptor(self) -> KvqCache:
+        return KvqCache(self.dtype, self.k_cache.shape[0], BLOCK_SIZE, self.k_cache.shape[1], HEAD_DIM,
+                        self.k_cache.data_ptr(), self.v_cache.data_ptr(),
+                        self.k_scale.data_ptr() if self.k_scale is not None else None,
+                        self.v_scale.data_ptr() if self.v_scale is not None else None,
+                        float(self.kv_scale))
+
+
+def append(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, cu_new_lens: torch.Tensor | None = None,
+           num_new_rows: int | None = None, stream=None) -> None:
+    """kvq_append: fp16 rows [T][Hkv][128] -> their paged slots (post-append context_lens)."""
+    assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    batch = context_lens.shape[0]
+    T = k_new.shape[0] if num_new_rows is None else num_new_rows
+    if cu_new_lens is not None:
+        assert cu_new_lens.dtype == torch.int32
+    d = cache.descriptor()
+    _check(lib.kvq_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(cu_new_lens), T,
+                          _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), batch,
+                          _stream(stream)), "kvq_append")
+
+
+def workspace_size(batch: int, num_q_heads: int, max_context_len: int, partition_size: int) -> int:
+    return int(lib.kvq_decode_workspace_size(batch, num_q_heads, HEAD_DIM, max_context_len, partition_size))
+
+
+def alloc_workspace(batch, num_q_heads, max_context_len, partition_size, device="cuda"):
+    n = workspace_size(batch, num_q_heads, max_context_len, partition_size)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, max_context_len: int, sm_scale: float | None = None,
+                      partition_size: int = 512, workspace: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_paged_decode_attn: q fp16 [B][Hq][128] -> out fp16 [B][Hq][128]."""
+    assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
+    B, Hq, _ = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_size(B, Hq, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = cache.descriptor()
+    _check(lib.kvq_paged_decode_attn(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
+                                     _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+                                     int(max_context_len), int(partition_size), _ptr(workspace),
+                                     ws_bytes, _stream(stream)), "kvq_paged_decode_attn")
+    return out
+
+
+def dequant(cache: PagedKVCache, block_tables: torch.Tensor, context_lens: torch.Tensor,
+            max_context_len: int, k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None,
+            stream=None):
+    """kvq_dequant -> (k, v) fp32 [B][Hkv][max_context_len][128] (slots past a context untouched)."""
+    B = context_lens.shape[0]
+    shape = (B, cache.num_kv_heads, max_context_len, HEAD_DIM)
+    dev = cache.k_cache.device
+    if k_out is None:
+        k_out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+    if v_out is None:
+        v_out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+    d = cache.descriptor()
+    _check(lib.kvq_dequant(ctypes.byref(d), _ptr(block_tables), block_tables.shape[1],
+                           _ptr(context_lens), B, int(max_context_len), _ptr(k_out), _ptr(v_out),
+                           _stream(stream)), "kvq_dequant")
+    return k_out, v_out
+
+
+def timing_begin(capacity: int) -> None:
+    _check(lib.kvq_timing_begin(capacity), "kvq_timing_begin")
+
+
+def timing_end():
+    """-> (main_ms_total, main_count, merge_ms_total, merge_count)."""
+    mt, gt = ctypes.c_double(0), ctypes.c_double(0)
+    mc, gc = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.kvq_timing_end(ctypes.byref(mt), ctypes.byref(mc), ctypes.byref(gt), ctypes.byref(gc)),
+           "kvq_timing_end")
+    return mt.value, mc.value, gt.value, gc.value
+
+
+def version() -> str:
+    return lib.kvq_version().decode()

@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU parity tests: oracle twins of device cases and the attention gate."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from quantized_kv_cache_03_amd import workloads as W
+
+DT = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8}
+
+# Attention gate: |gpu - oracle| <= ATOL + RTOL * |oracle| element by element, on the same codes.
+ATOL = 1e-3
+RTOL = 1e-2
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+class OracleTwin:
+    """The oracle's own cache for a subset of a device case's sequences, built from the same fp16
+    rows with the oracle's encoder (blocks renumbered compactly; attention does not depend on the
+    block numbering, and the tests check that separately)."""
+
+    def __init__(self, case, seqs):
+        self.seqs = list(seqs)
+        ctx = case.ctx[self.seqs]
+        nblk = (ctx + 15) // 16
+        self.bt = np.full((len(self.seqs), max(1, int(nblk.max()))), -1, np.int32)
+        self.gpu_blocks = []
+        nb = 0
+        for i, b in enumerate(self.seqs):
+            n = int(nblk[i])
+            self.bt[i, :n] = np.arange(nb, nb + n)
+            self.gpu_blocks.extend(int(x) for x in case.bt[b, :n])
+            nb += n
+        self.ctx = ctx.astype(np.int32)
+        self.cache = oracle.Cache(DT[case.w.dtype], nb, case.w.num_kv_heads, case.kv_scale)
+        rows = [case.rows_of(b) for b in self.seqs]
+        k = np.concatenate([r[0] for r in rows])
+        v = np.concatenate([r[1] for r in rows])
+        cu = np.zeros(len(self.seqs) + 1, np.int32)
+        cu[1:] = np.cumsum(self.ctx)
+        oracle.append(self.cache, k, v, self.bt, self.ctx, cu)
+        self.q = case.q[self.seqs]
+
+    def attention(self, heads=None, threads=8):
+        return oracle.decode_attn(self.cache, self.q, self.bt, self.ctx, heads=heads, threads=threads)
+
+
+def device_blocks(case, blocks):
+    """Copy the given physical blocks of the device cache to host (K, V and INT8 scales)."""
+    import torch
+    idx = torch.tensor(blocks, dtype=torch.long, device=case.cache.k_cache.device)
+    k = case.cache.k_cache.index_select(0, idx).cpu().numpy()
+    v = case.cache.v_cache.index_select(0, idx).cpu().numpy()
+    ks = vs = None
+    if case.cache.k_scale is not None:
+        ks = case.cache.k_scale.index_select(0, idx).cpu().numpy()
+        vs = case.cache.v_scale.index_select(0, idx).cpu().numpy()
+    return k, v, ks, vs
+
+
+def assert_cache_bytes_equal(case, twin, tag=""):
+    k, v, ks, vs = device_blocks(case, twin.gpu_blocks)
+    ok = twin.cache
+    np.testing.assert_array_equal(k.reshape(ok.k.shape), ok.k, err_msg=f"K codes {tag}")
+    np.testing.assert_array_equal(v.reshape(ok.v.shape), ok.v, err_msg=f"V codes {tag}")
+    if ks is not None:
+        np.testing.assert_array_equal(ks.reshape(ok.ks.shape).view(np.uint32),
+                                      ok.ks.view(np.uint32), err_msg=f"K scales {tag}")
+        np.testing.assert_array_equal(vs.reshape(ok.vs.shape).view(np.uint32),
+                                      ok.vs.view(np.uint32), err_msg=f"V scales {tag}")
+
+
+def attn_stats(gpu: np.ndarray, ref: np.ndarray):
+    g = gpu.astype(np.float64)
+    d = np.abs(g - ref)
+    rel = d / np.maximum(np.abs(ref), 1e-30)
+    return {"max_abs": float(d.max(initial=0)), "max_rel_where_ref_ge_0.1":
+            float(rel[np.abs(ref) >= 0.1].max(initial=0)),
+            "worst_ratio": float((d / (ATOL + RTOL * np.abs(ref))).max(initial=0))}
+
+
+def assert_attn_close(gpu: np.ndarray, ref: np.ndarray, tag=""):
+    g = gpu.astype(np.float64)
+    assert not np.isnan(g).any(), f"NaN in GPU attention output {tag}"
+    bad = np.abs(g - ref) > ATOL + RTOL * np.abs(ref)
+    st = attn_stats(gpu, ref)
+    assert not bad.any(), f"attention outside the gate {tag}: {int(bad.sum())} elements, {st}"
+    return st

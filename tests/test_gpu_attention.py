@@ -1,0 +1,114 @@
+"""GPU parity of the decode step (kvq_append + kvq_paged_decode_attn) against the oracle.
+
+Scaled-down copies of the five workloads keep the oracle within seconds while still spanning
+several tiles, several partitions and ragged tails; every (sequence, head) output is compared.
+The cache bytes written by the library are compared bit for bit with the oracle's encoding of
+the same rows, and attention is gated on |gpu - oracle| <= 1e-3 + 1e-2 |oracle| elementwise.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import OracleTwin, assert_attn_close, assert_cache_bytes_equal, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from quantized_kv_cache_03_amd import harness
+    return harness
+
+
+def _scaled(name, ctx, **kw):
+    from quantized_kv_cache_03_amd import workloads as W
+    base = W.WORKLOADS[name]
+    return base.scaled(name=f"{name}-scaled", seed=100 + base.seed, batch=len(ctx),
+                       context=("list", list(ctx)), **kw)
+
+
+CASES = [
+    ("tiny-e4m3", [512, 1, 37], {}),
+    ("llama2-7b-mha-e4m3", [512, 700, 1037, 33, 2048], {"num_q_heads": 4, "num_kv_heads": 4}),
+    ("llama3-8b-gqa-e5m2", [1200, 16, 513], {"num_q_heads": 8, "num_kv_heads": 2}),
+    ("llama2-13b-mha-int8", [2, 600, 1500, 17], {"num_q_heads": 3, "num_kv_heads": 3}),
+    ("llama3-70b-gqa-e4m3-32k", [3000, 1], {"num_q_heads": 16, "num_kv_heads": 2}),
+]
+
+
+@pytest.mark.parametrize("name,ctx,kw", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("partition", [0, 16, 64, 512])
+def test_decode_step_scaled(H, name, ctx, kw, partition):
+    w = _scaled(name, ctx, partition_size=partition, **kw)
+    say(f"[decode step] {w.name} ctx={ctx} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"dtype={w.dtype} partition={partition}")
+    case = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2)
+    out = case.step().cpu().numpy()
+    twin = OracleTwin(case, range(case.B))
+    assert_cache_bytes_equal(case, twin, w.name)
+    ref = twin.attention()
+    st = assert_attn_close(out, ref, w.name)
+    say(f"    ok {st}")
+
+
+def test_split_partition_sizes_agree(H):
+    """Split-K at several partition sizes and one pass agree within the gate; one partition size
+    is bitwise reproducible run to run."""
+    w = _scaled("llama2-7b-mha-e4m3", [4096, 100, 2500], num_q_heads=2, num_kv_heads=2)
+    say("[partition sizes]")
+    case = H.DeviceCase(w, keep_host_rows=True)
+    case.append_step()
+    outs = {ps: case.attention(partition_size=ps).clone().cpu().numpy() for ps in (0, 16, 256, 512, 4096)}
+    ref = OracleTwin(case, range(case.B)).attention()
+    for ps, o in outs.items():
+        assert_attn_close(o, ref, f"partition {ps}")
+    again = case.attention(partition_size=512).cpu().numpy()
+    np.testing.assert_array_equal(again.view(np.uint16), outs[512].view(np.uint16))
+
+
+def test_shuffled_table_is_bitwise_invariant(H):
+    """The same rows behind a sequential or a shuffled block table give bitwise equal outputs."""
+    outs = []
+    for table in ("sequential", "shuffled"):
+        w = _scaled("llama2-7b-mha-e4m3", [900, 1500, 31], num_q_heads=4, num_kv_heads=4, table=table)
+        case = H.DeviceCase(w)
+        outs.append(case.step().cpu().numpy())
+    np.testing.assert_array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+
+
+def test_zero_length_and_single_token(H):
+    import torch
+    from quantized_kv_cache_03_amd import kvq
+    say("[zero length / single token]")
+    w = _scaled("tiny-e4m3", [1, 40, 16], num_q_heads=4, num_kv_heads=4)
+    case = H.DeviceCase(w, keep_host_rows=True)
+    out = case.step().cpu().numpy()
+    twin = OracleTwin(case, range(case.B))
+    assert_attn_close(out, twin.attention())
+    # a sequence of length 0 yields zeros, others unaffected
+    ctx0 = case.ctx_d.clone()
+    ctx0[1] = 0
+    o2 = kvq.paged_decode_attn(case.cache, case.q_d, case.bt_d, ctx0, case.max_ctx, partition_size=16)
+    o2 = o2.cpu().numpy()
+    assert np.all(o2[1] == 0)
+    np.testing.assert_array_equal(o2[0].view(np.uint16), out[0].view(np.uint16))
+    # one token: the output is that token's dequantized value row (rounded to fp16)
+    _, vo = kvq.dequant(case.cache, case.bt_d, case.ctx_d, case.max_ctx)
+    vrow = vo[0, :, 0, :].cpu().numpy()
+    np.testing.assert_array_equal(out[0], vrow.astype(np.float16))
+    torch.cuda.synchronize()
+
+
+def test_empty_batch_is_a_no_op(H):
+    import torch
+    from quantized_kv_cache_03_amd import kvq
+    c = kvq.PagedKVCache.allocate("fp8_e4m3", 2, 2)
+    bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    ctx = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    q = torch.zeros((0, 2, 128), dtype=torch.float16, device="cuda")
+    out = kvq.paged_decode_attn(c, q, bt, ctx, 0, partition_size=512)
+    assert out.shape == (0, 2, 128)
+    kvq.append(c, q, q, bt, ctx)
+    torch.cuda.synchronize()

@@ -1,0 +1,45 @@
+"""The five workloads at full size, in the launch configuration the benchmark times.
+
+Each case fills the whole cache through kvq_append, runs one decode step (append one token per
+sequence, then split-K attention with the workload's partition size) and checks sampled
+sequences against the oracle: every cache byte of those sequences bit for bit, and every output
+element of every head of those sequences within the gate.  The rest of the batch is checked for
+properties that hold at any size: no NaN, and the step is bitwise reproducible.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import OracleTwin, assert_attn_close, assert_cache_bytes_equal, say
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["tiny-e4m3", "llama2-7b-mha-e4m3", "llama3-8b-gqa-e5m2", "llama2-13b-mha-int8",
+         "llama3-70b-gqa-e4m3-32k"]
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_decode_step(name):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from quantized_kv_cache_03_amd import harness, workloads as W
+    w = W.WORKLOADS[name]
+    say(f"[full size] {name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype} "
+        f"partition={w.partition_size}")
+    case = harness.DeviceCase(w, verbose=True)
+    say(f"  cache filled: {case.num_blocks} blocks, sum ctx {int(case.ctx.sum())}, kv_scale {case.kv_scale!r}")
+    out1 = case.step().clone()
+    out2 = case.step().clone()
+    torch.cuda.synchronize()
+    o1 = out1.cpu().numpy()
+    assert not np.isnan(o1.astype(np.float32)).any()
+    np.testing.assert_array_equal(o1.view(np.uint16), out2.cpu().numpy().view(np.uint16))
+    seqs = sorted({0, case.B - 1, int(np.argmax(case.ctx))})
+    say(f"  oracle on sequences {seqs} (ctx {case.ctx[seqs].tolist()})")
+    twin = OracleTwin(case, seqs)
+    assert_cache_bytes_equal(case, twin, name)
+    ref = twin.attention(threads=16)
+    st = assert_attn_close(o1[seqs], ref, name)
+    say(f"  ok {st}")
+    del case
+    torch.cuda.empty_cache()
