@@ -12,14 +12,14 @@
 // base 2 with log2(e) folded into the logit scale.
 //
 // Work decomposition (one wave per work item, no LDS):
-//   grid (partition, query head, sequence); a wave streams its partition in chunks of TW tiles of
+//   grid (query head, partition, sequence); a wave streams its partition in chunks of TW tiles of
 //   16 tokens, issuing every K and V load of a chunk before using any, and keeps a running max /
 //   sum / accumulator across chunks.
-//   K tile (token-major 16 x 128 B): lane l holds 16 dims of token l/8 (and of token 8 + l/8),
+//   K tile (token-major 16 x 128 B): lane l holds 16 dims of tokens 2 (l/8) and 2 (l/8) + 1,
 //     dots them with its slice of q (v_dot2_f32_f16), and 8-lane DPP sums finish each logit.
 //   V tile (dim-major 128 x 16 B): lane l holds the 16 tokens of dims l and 64 + l, so each lane
 //     accumulates whole output elements; the 16 weights of a tile reach every lane as packed fp16
-//     (hi, lo) pairs read with v_readlane.
+//     (hi, lo) pairs through a 64-byte LDS broadcast.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -75,18 +75,6 @@ __device__ __forceinline__ void split_f16x2(float wa, float wb, uint32_t& hi, ui
     lo = pack_f16x2(wa - (float)ha, wb - (float)hb);
 }
 
-// pairs (w_2i, w_2i+1) of a tile's 16 weights from lanes 8j, which hold (w_j, w_{8+j})
-__device__ __forceinline__ void gather_pairs(uint32_t mine, uint32_t* pw) {
-    uint32_t r[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = __builtin_amdgcn_readlane(mine, 8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        pw[j] = (r[2 * j] & 0xFFFFu) | (r[2 * j + 1] << 16);          // tokens 2j, 2j+1
-        pw[4 + j] = (r[2 * j] >> 16) | (r[2 * j + 1] & 0xFFFF0000u);  // tokens 8+2j, 9+2j
-    }
-}
-
 struct KernelParams {
     const uint8_t* kc;
     const uint8_t* vc;
@@ -109,11 +97,121 @@ struct KernelParams {
 };
 
 // ------------------------------------------------------------------------------------------------
-// Partition kernel, one wave per (partition, query head, sequence).
-template <int DT, int TW>
+// Merge of the np partials of one (sequence, query head), by one wave:
+//   M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Partials are read in partition order, so the result is bitwise deterministic.
+__device__ __forceinline__ void merge_partials(const KernelParams& a, int b, int h, int np, int lane) {
+    const size_t prow0 = ((size_t)b * a.Hq + h) * a.P;
+    float M = kNegInf;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[prow0 + p]);
+    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int p = 0; p < np; ++p) {
+        const float w = __builtin_amdgcn_exp2f(a.part_m[prow0 + p] - M);
+        L += w * a.part_l[prow0 + p];
+        const float2 op = reinterpret_cast<const float2*>(a.part_o + (prow0 + p) * kDim)[lane];
+        o0 += w * op.x;
+        o1 += w * op.y;
+    }
+    const float inv = a.v_scale / L;
+    const size_t orow = ((size_t)b * a.Hq + h) * kDim;
+    half2_t r = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
+    reinterpret_cast<half2_t*>(a.out + orow)[lane] = r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// One chunk of TW tiles of the partition kernel.  Lane l belongs to group j = l / 8; the group holds
+// tokens 2j and 2j+1 of every tile (K rows read at 256 j + 16 (l % 8) and 128 further), so after the
+// 8-lane sums it owns the weight pair (w_2j, w_2j+1) -- exactly the pairing of adjacent tokens in a
+// V row.  Group leaders publish their (hi, lo) weight pairs in LDS and every lane reads all eight
+// back with broadcast loads.  MASKED handles a chunk that reaches past the partition end (its logits
+// past the end become -inf; the caller has already zeroed the V codes of the partial tile).
+template <int DT, int TW, bool MASKED>
+__device__ __forceinline__ void chunk_step(const KernelParams& a, const uint4 (&ka)[TW],
+                                           const uint4 (&kb)[TW], const uint4 (&va)[TW],
+                                           const uint4 (&vb)[TW],
+                                           const int (&blks)[TW], int tile0, int nvalid, int t_end,
+                                           const half2_t (&qv)[8], int g, int lane, uint32_t* lds,
+                                           float& m_run, float& l_lane, float& acc0, float& acc1) {
+    const int j = lane >> 3;
+    float za[TW], zb[TW];
+    float cmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const float sa = sum8(dot16<DT>(ka[i], qv));
+        const float sb = sum8(dot16<DT>(kb[i], qv));
+        float fa = a.qk_scale, fb = a.qk_scale;
+        if constexpr (DT == KVQ_INT8) {
+            if (!MASKED || i < nvalid) {
+                const float2 s2 = *reinterpret_cast<const float2*>(
+                    a.ks + ((size_t)blks[i] * a.Hkv + g) * kBlock + 2 * j);
+                fa *= s2.x;
+                fb *= s2.y;
+            }
+        }
+        za[i] = sa * fa;
+        zb[i] = sb * fb;
+        if constexpr (MASKED) {
+            const int pos = (tile0 + i) * kBlock + 2 * j;
+            za[i] = (i < nvalid && pos < t_end) ? za[i] : kNegInf;
+            zb[i] = (i < nvalid && pos + 1 < t_end) ? zb[i] : kNegInf;
+        }
+        cmax = fmaxf(cmax, fmaxf(za[i], zb[i]));
+    }
+    cmax = max_across8(cmax);  // a chunk always holds at least one valid token
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    acc0 *= alpha;
+    acc1 *= alpha;
+    l_lane *= alpha;
+
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const float pa = __builtin_amdgcn_exp2f(za[i] - m_new);
+        const float pb = __builtin_amdgcn_exp2f(zb[i] - m_new);
+        l_lane += pa + pb;
+        float wa = pa, wb = pb;
+        if constexpr (DT == KVQ_INT8) {
+            if (!MASKED || i < nvalid) {
+                const float2 s2 = *reinterpret_cast<const float2*>(
+                    a.vs + ((size_t)blks[i] * a.Hkv + g) * kBlock + 2 * j);
+                // masked slots may hold NaN scales: keep their weight exactly 0
+                wa = (pa > 0.0f) ? pa * s2.x : 0.0f;
+                wb = (pb > 0.0f) ? pb * s2.y : 0.0f;
+            }
+        }
+        uint32_t hi, lo;
+        split_f16x2(wa, wb, hi, lo);
+        if ((lane & 7) == 0) {
+            lds[i * 16 + j] = hi;
+            lds[i * 16 + 8 + j] = lo;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const uint4* l4 = reinterpret_cast<const uint4*>(lds + i * 16);
+        const uint4 h0 = l4[0], h1 = l4[1], w0 = l4[2], w1 = l4[3];
+        const uint32_t whi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t wlo[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        acc0 = pv16<DT>(va[i], whi, wlo, acc0);
+        acc1 = pv16<DT>(vb[i], whi, wlo, acc1);
+        // keep the next tile's weight reads from being hoisted: they would pin 16 more VGPRs per tile
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ------------------------------------------------------------------------------------------------
+// Partition kernel, one wave per (query head, partition, sequence).  The head is the fastest grid
+// dimension: workgroups are handed to the eight XCDs round-robin by linear id, so consecutive ids
+// must carry equal work -- all heads of one (partition, sequence) do, while consecutive partitions
+// of one sequence do not (its last partitions are ragged or empty).
+template <int DT, int TW, bool PIPE>
 __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
-    const int p = blockIdx.x;
-    const int h = blockIdx.y;
+    __shared__ uint32_t lds[TW * 16];
+    const int h = blockIdx.x;
+    const int p = blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
     const int G = a.Hq / a.Hkv;
@@ -148,10 +246,11 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
     const size_t head_off = (size_t)g * kTileBytes;
     const size_t blk_stride = (size_t)a.Hkv * kTileBytes;
-    const int tok_in_tile = lane >> 3;  // 0..7, the K row this lane reads (and 8 + it)
+    const uint32_t k_off = 256u * ((uint32_t)lane >> 3) + 16u * ((uint32_t)lane & 7u);  // token 2 (lane/8)
+    const uint32_t v_off = 16u * (uint32_t)lane;
 
     float m_run = kNegInf;  // running max of the base-2 logits (wave-uniform)
-    float l_lane = 0.0f;    // running sum of weights of this lane's two tokens per tile
+    float l_lane = 0.0f;    // running sum of the weights of this lane's group
     float acc0 = 0.0f, acc1 = 0.0f;  // unnormalized output, dims lane and 64 + lane
 
     for (int tb = tile_begin; tb < tile_end; tb += 64) {
@@ -159,89 +258,69 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
         const int nt_grp = min(64, tile_end - tb);
         const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
 
-        for (int c0 = 0; c0 < nt_grp; c0 += TW) {
-            uint4 ka[TW], kb[TW], va[TW], vb[TW];
-            int blks[TW];
+        auto load_chunk = [&](int c, uint4 (&ka)[TW], uint4 (&kb)[TW], uint4 (&va)[TW],
+                              uint4 (&vb)[TW], int (&blks)[TW]) {
 #pragma unroll
             for (int i = 0; i < TW; ++i) {
-                if (c0 + i < nt_grp) {
-                    blks[i] = __builtin_amdgcn_readlane(blk_lane, c0 + i);
-                    const uint8_t* kt = a.kc + (size_t)blks[i] * blk_stride + head_off;
-                    const uint8_t* vt = a.vc + (size_t)blks[i] * blk_stride + head_off;
-                    ka[i] = ldg16(kt + 16 * lane);
-                    kb[i] = ldg16(kt + 1024 + 16 * lane);
-                    va[i] = ldg16(vt + 16 * lane);
-                    vb[i] = ldg16(vt + 1024 + 16 * lane);
-                } else {
-                    blks[i] = 0;
-                    ka[i] = kb[i] = va[i] = vb[i] = make_uint4(0u, 0u, 0u, 0u);
+                blks[i] = __builtin_amdgcn_readlane(blk_lane, c * TW + i);
+                const uint8_t* kt = a.kc + (size_t)blks[i] * blk_stride + head_off;
+                const uint8_t* vt = a.vc + (size_t)blks[i] * blk_stride + head_off;
+                ka[i] = ldg16(kt + k_off);
+                kb[i] = ldg16(kt + k_off + 128u);
+                va[i] = ldg16(vt + v_off);
+                vb[i] = ldg16(vt + 1024u + v_off);
+            }
+        };
+        // whole chunks: TW tiles, all inside the partition
+        const int full_tiles = min(nt_grp, (t_end - tb * kBlock) / kBlock);
+        const int nfull = full_tiles / TW;
+        if constexpr (PIPE) {
+            // two register buffers: the next chunk's loads are in flight while this one computes
+            uint4 ka0[TW], kb0[TW], va0[TW], vb0[TW], ka1[TW], kb1[TW], va1[TW], vb1[TW];
+            int bl0[TW], bl1[TW];
+            if (nfull > 0) load_chunk(0, ka0, kb0, va0, vb0, bl0);
+            for (int c = 0; c < nfull; c += 2) {
+                if (c + 1 < nfull) load_chunk(c + 1, ka1, kb1, va1, vb1, bl1);
+                chunk_step<DT, TW, false>(a, ka0, kb0, va0, vb0, bl0, tb + c * TW, TW, t_end, qv, g,
+                                          lane, lds, m_run, l_lane, acc0, acc1);
+                if (c + 1 < nfull) {
+                    if (c + 2 < nfull) load_chunk(c + 2, ka0, kb0, va0, vb0, bl0);
+                    chunk_step<DT, TW, false>(a, ka1, kb1, va1, vb1, bl1, tb + (c + 1) * TW, TW,
+                                              t_end, qv, g, lane, lds, m_run, l_lane, acc0, acc1);
                 }
             }
-            // logits of the chunk (base 2); lanes of group j hold tokens j and 8 + j of each tile
-            float za[TW], zb[TW];
-            float cmax = kNegInf;
-#pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                const float sa = sum8(dot16<DT>(ka[i], qv));
-                const float sb = sum8(dot16<DT>(kb[i], qv));
-                const int tile = tb + c0 + i;
-                const int pa = tile * kBlock + tok_in_tile;
-                const int pb = pa + 8;
-                float fa = a.qk_scale, fb = a.qk_scale;
-                if constexpr (DT == KVQ_INT8) {
-                    if (c0 + i < nt_grp) {
-                        const float* st = a.ks + ((size_t)blks[i] * a.Hkv + g) * kBlock;
-                        fa *= st[tok_in_tile];
-                        fb *= st[tok_in_tile + 8];
-                    }
-                }
-                const bool in_a = (c0 + i < nt_grp) && pa < t_end;
-                const bool in_b = (c0 + i < nt_grp) && pb < t_end;
-                za[i] = in_a ? sa * fa : kNegInf;
-                zb[i] = in_b ? sb * fb : kNegInf;
-                cmax = fmaxf(cmax, fmaxf(za[i], zb[i]));
+        } else {
+            for (int c = 0; c < nfull; ++c) {
+                uint4 ka[TW], kb[TW], va[TW], vb[TW];
+                int blks[TW];
+                load_chunk(c, ka, kb, va, vb, blks);
+                chunk_step<DT, TW, false>(a, ka, kb, va, vb, blks, tb + c * TW, TW, t_end, qv, g,
+                                          lane, lds, m_run, l_lane, acc0, acc1);
             }
-            cmax = max_across8(cmax);  // every chunk holds at least one valid token
-            const float m_new = fmaxf(m_run, cmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            acc0 *= alpha;
-            acc1 *= alpha;
-            l_lane *= alpha;
-
-#pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                const float pa = __builtin_amdgcn_exp2f(za[i] - m_new);
-                const float pb = __builtin_amdgcn_exp2f(zb[i] - m_new);
-                l_lane += pa + pb;
-                float wa = pa, wb = pb;
-                if constexpr (DT == KVQ_INT8) {
-                    if (c0 + i < nt_grp) {
-                        const float* st = a.vs + ((size_t)blks[i] * a.Hkv + g) * kBlock;
-                        const float sa = st[tok_in_tile], sb = st[tok_in_tile + 8];
-                        wa = (pa > 0.0f) ? pa * sa : 0.0f;   // masked slots may hold NaN scales
-                        wb = (pb > 0.0f) ? pb * sb : 0.0f;
-                    }
-                }
-                // lane 8j holds (w_j, w_{8+j}); gather the 16 weights as pairs (w_2i, w_2i+1)
-                uint32_t mine_hi, mine_lo, whi[8], wlo[8];
-                split_f16x2(wa, wb, mine_hi, mine_lo);
-                gather_pairs(mine_hi, whi);
-                gather_pairs(mine_lo, wlo);
-                uint4 v0 = va[i], v1 = vb[i];
-                const int tile = tb + c0 + i;
-                const int valid = t_end - tile * kBlock;  // tokens of this tile inside the partition
-                if (valid < kBlock) {
-                    // slots past the end may hold any code, NaN included: zero them (weight 0 alone
-                    // would still give 0 * NaN)
-                    v0.x = keep_bytes(v0.x, valid); v0.y = keep_bytes(v0.y, valid - 4);
-                    v0.z = keep_bytes(v0.z, valid - 8); v0.w = keep_bytes(v0.w, valid - 12);
-                    v1.x = keep_bytes(v1.x, valid); v1.y = keep_bytes(v1.y, valid - 4);
-                    v1.z = keep_bytes(v1.z, valid - 8); v1.w = keep_bytes(v1.w, valid - 12);
-                }
-                acc0 = pv16<DT>(v0, whi, wlo, acc0);
-                acc1 = pv16<DT>(v1, whi, wlo, acc1);
+        }
+        int c0 = nfull * TW;
+        // the rest one tile at a time, the last one possibly partial
+        for (; c0 < nt_grp; ++c0) {
+            uint4 ka[1], kb[1], va[1], vb[1];
+            int blks[1];
+            blks[0] = __builtin_amdgcn_readlane(blk_lane, c0);
+            const uint8_t* kt = (a.kc + (size_t)blks[0] * blk_stride + head_off);
+            const uint8_t* vt = (a.vc + (size_t)blks[0] * blk_stride + head_off);
+            ka[0] = ldg16(kt + k_off);
+            kb[0] = ldg16(kt + k_off + 128u);
+            va[0] = ldg16(vt + v_off);
+            vb[0] = ldg16(vt + 1024u + v_off);
+            const int valid = t_end - (tb + c0) * kBlock;
+            if (valid < kBlock) {
+                // slots past the end may hold any code, NaN included: zero them, since a zero
+                // weight alone would still give 0 * NaN
+                va[0].x = keep_bytes(va[0].x, valid); va[0].y = keep_bytes(va[0].y, valid - 4);
+                va[0].z = keep_bytes(va[0].z, valid - 8); va[0].w = keep_bytes(va[0].w, valid - 12);
+                vb[0].x = keep_bytes(vb[0].x, valid); vb[0].y = keep_bytes(vb[0].y, valid - 4);
+                vb[0].z = keep_bytes(vb[0].z, valid - 8); vb[0].w = keep_bytes(vb[0].w, valid - 12);
             }
+            chunk_step<DT, 1, true>(a, ka, kb, va, vb, blks, tb + c0, 1, t_end, qv, g, lane, lds,
+                                    m_run, l_lane, acc0, acc1);
         }
     }
     // each token's weight was added by all 8 lanes of its group: count group leaders only
@@ -265,38 +344,20 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     }
 }
 
-// ------------------------------------------------------------------------------------------------
-// Merge kernel, one wave per (query head, sequence) whose context spans several partitions:
-//   M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// Partials are read in partition order, so the result is bitwise deterministic.
+// Separate merge kernel, one wave per (query head, sequence) whose context spans several partitions.
 __global__ __launch_bounds__(64) void attn_merge(KernelParams a) {
     const int h = blockIdx.x;
     const int b = blockIdx.y;
-    const int lane = threadIdx.x;
     const int n = a.ctx[b];
     const int np = min((n + a.PS - 1) / a.PS, a.P);
     if (np <= 1) return;  // written directly by the partition kernel
-    const size_t prow0 = ((size_t)b * a.Hq + h) * a.P;
-    float M = kNegInf;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[prow0 + p]);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int p = 0; p < np; ++p) {
-        const float w = __builtin_amdgcn_exp2f(a.part_m[prow0 + p] - M);
-        L += w * a.part_l[prow0 + p];
-        const float2 op = reinterpret_cast<const float2*>(a.part_o + (prow0 + p) * kDim)[lane];
-        o0 += w * op.x;
-        o1 += w * op.y;
-    }
-    const float inv = a.v_scale / L;
-    const size_t orow = ((size_t)b * a.Hq + h) * kDim;
-    half2_t r = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
-    reinterpret_cast<half2_t*>(a.out + orow)[lane] = r;
+    merge_partials(a, b, h, np, threadIdx.x);
 }
 
 // ------------------------------------------------------------------------------------------------
 template <int DT>
 static void launch_partition(const KernelParams& kp, dim3 grid, hipStream_t stream) {
-    attn_partition_valu<DT, 4><<<grid, 64, 0, stream>>>(kp);
+    attn_partition_valu<DT, 4, false><<<grid, 64, 0, stream>>>(kp);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
@@ -324,7 +385,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.qk_scale = a.sm_scale * kLog2e * (fp8 ? c.kv_scale : 1.0f);
     kp.v_scale = fp8 ? c.kv_scale : 1.0f;
 
-    const dim3 grid((unsigned)a.num_partitions, (unsigned)a.num_q_heads, (unsigned)a.batch);
+    const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_partitions, (unsigned)a.batch);
     if (main_begin) (void)hipEventRecord(main_begin, stream);
     switch (c.dtype) {
         case KVQ_FP8_E4M3: launch_partition<KVQ_FP8_E4M3>(kp, grid, stream); break;
