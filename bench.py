@@ -163,14 +163,13 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    main_ms, main_n, merge_ms, merge_n = kvq.timing_end()
+    main_ms, main_n = kvq.timing_end()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     step_bytes = case.algorithmic_bytes()
     attn_bytes = case.attention_bytes()
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     main_avg_ms = main_ms / max(1, main_n)
-    merge_avg_ms = merge_ms / max(1, merge_n) if merge_n else 0.0
     achieved = attn_bytes / (main_avg_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
     traffic = load_traffic(w.name, digest)
@@ -215,8 +214,7 @@ def main():
         "kv_tokens_per_s": round(int(case.ctx.sum()) / (ms_step * 1e-3), 1),
         "step_bytes": step_bytes,
         "wall_s_timed_region": round(wall, 4),
-        "kernels_ms": {"attn_partition_avg": round(main_avg_ms, 5),
-                       "attn_merge_avg": round(merge_avg_ms, 5)},
+        "kernels_ms": {"attn_partition_avg": round(main_avg_ms, 5)},
         "roofline": {
             "kernel": f"attn_partition_valu<{w.dtype}>",
             "bound": "hbm",

@@ -126,6 +126,19 @@ int kvq_paged_decode_attn(const kvq_cache *cache, const void *q, void *out, int3
                           int32_t partition_size, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/* One whole decode step: kvq_append of one new row per sequence (cu_new_lens == NULL) followed by
+ * kvq_paged_decode_attn, fused so that the append costs no launch of its own.  The cache bytes
+ * written and the output are bitwise identical to those two calls made in sequence with the same
+ * arguments.  k_new, v_new: fp16 [batch][Hkv][128], the token at position context_lens[b] - 1 of
+ * each sequence (context_lens are post-append lengths and must be >= 1; a sequence with
+ * context_lens[b] == 0 appends nothing and gets zeros).  Other arguments as for
+ * kvq_paged_decode_attn. */
+int kvq_decode_step(const kvq_cache *cache, const void *k_new, const void *v_new, const void *q,
+                    void *out, int32_t num_q_heads, float sm_scale, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t batch,
+                    int32_t max_context_len, int32_t partition_size, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
 /* Dequantize the cache into dense fp32 [batch][Hkv][max_context_len][128] arrays for K and V:
  * each element is fl32(dec(code) * kv_scale) (FP8) or fl32(q * s) (INT8), one rounding.  Slots
  * t >= context_lens[b] are left untouched.  For inspection and tests; not on the decode path. */
@@ -145,14 +158,13 @@ const char *kvq_status_string(int status);
 const char *kvq_last_error(void);
 
 /* Kernel-timing hook for benchmarks: after kvq_timing_begin(capacity), each kvq_paged_decode_attn
- * call records a HIP event pair around its main (partition) kernel and another around its merge
- * kernel, on the call's stream, for up to `capacity` calls.  kvq_timing_end() waits for the
- * events, returns the summed milliseconds and counts, and releases them.  Events are created in
- * kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a time.
- * Returns KVQ_OK or KVQ_ERR_ARG / KVQ_ERR_HIP. */
+ * or kvq_decode_step call records a HIP event pair around its main (partition) kernel, on the
+ * call's stream, for up to `capacity` calls.  kvq_timing_end() waits for the events, returns the
+ * summed milliseconds and the number of timed launches, and releases the events.  Events are
+ * created in kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a
+ * time.  Returns KVQ_OK or KVQ_ERR_ARG / KVQ_ERR_HIP. */
 int kvq_timing_begin(int32_t capacity);
-int kvq_timing_end(double *main_ms_total, int32_t *main_count, double *merge_ms_total,
-                   int32_t *merge_count);
+int kvq_timing_end(double *main_ms_total, int32_t *main_count);
 
 /* Library version, "major.minor.patch". */
 const char *kvq_version(void);

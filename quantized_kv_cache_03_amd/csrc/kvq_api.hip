@@ -89,8 +89,7 @@ struct Timing {
     bool active = false;
     int32_t capacity = 0;
     int32_t used = 0;
-    std::vector<hipEvent_t> ev;  // 4 per call: main begin/end, merge begin/end
-    std::vector<int> has_merge;
+    std::vector<hipEvent_t> ev;  // 2 per call: before and after the partition kernel
 };
 Timing g_timing;
 
@@ -98,7 +97,6 @@ void timing_release() {
     for (hipEvent_t e : g_timing.ev)
         if (e) (void)hipEventDestroy(e);
     g_timing.ev.clear();
-    g_timing.has_merge.clear();
     g_timing.active = false;
     g_timing.capacity = g_timing.used = 0;
 }
@@ -164,11 +162,16 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t hea
     return align256(rows * KVQ_HEAD_DIM * sizeof(float)) + 2 * align256(rows * sizeof(float));
 }
 
-int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int32_t num_q_heads,
-                          float sm_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* context_lens, int32_t batch, int32_t max_context_len,
-                          int32_t partition_size, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of kvq_paged_decode_attn and kvq_decode_step (k_new / v_new set for the latter).
+int decode_common(const char* where, const kvq_cache* cache, const void* k_new, const void* v_new,
+                  const void* q, void* out, int32_t num_q_heads, float sm_scale,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_cache(cache);
     if (st) return st;
     st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
@@ -189,10 +192,12 @@ int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int3
                     max_context_len, max_blocks_per_seq, KVQ_BLOCK_SIZE);
     if (batch == 0) return ok();
     if (!q || !out) return fail(KVQ_ERR_ARG, "q / out is NULL");
+    if ((k_new == nullptr) != (v_new == nullptr)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
     if (batch > 65535 || num_q_heads > 65535)
         return fail(KVQ_ERR_SHAPE, "batch and num_q_heads must be at most 65535");
 
     const Plan p = plan(max_context_len, partition_size);
+    if (p.P > 65535) return fail(KVQ_ERR_SHAPE, "%d partitions exceed the grid limit 65535", p.P);
     const size_t need = kvq_decode_workspace_size(batch, num_q_heads, KVQ_HEAD_DIM, max_context_len,
                                                   partition_size);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -212,6 +217,8 @@ int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int3
     a.num_partitions = p.P;
     a.partition_size = p.PS;
     a.part_o = a.part_m = a.part_l = nullptr;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
     if (need > 0) {
         const size_t rows = (size_t)batch * (size_t)num_q_heads * (size_t)p.P;
         char* w = static_cast<char*>(workspace);
@@ -221,16 +228,40 @@ int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int3
                                             align256(rows * sizeof(float)));
     }
 
-    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
-    int slot = -1;
+    hipEvent_t ev[2] = {nullptr, nullptr};
     if (g_timing.active && g_timing.used < g_timing.capacity) {
-        slot = g_timing.used++;
-        for (int i = 0; i < 4; ++i) ev[i] = g_timing.ev[4 * slot + i];
-        g_timing.has_merge[slot] = p.P > 1;
+        const int slot = g_timing.used++;
+        ev[0] = g_timing.ev[2 * slot];
+        ev[1] = g_timing.ev[2 * slot + 1];
     }
-    hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), ev[0], ev[1], ev[2], ev[3]);
-    if (e != hipSuccess) return hip_fail(e, "kvq_paged_decode_attn");
+    hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), ev[0], ev[1]);
+    if (e != hipSuccess) return hip_fail(e, where);
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int32_t num_q_heads,
+                          float sm_scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                          int32_t partition_size, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return decode_common("kvq_paged_decode_attn", cache, nullptr, nullptr, q, out, num_q_heads,
+                         sm_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                         max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+int kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                    void* out, int32_t num_q_heads, float sm_scale, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                    int32_t max_context_len, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (batch > 0 && (!k_new || !v_new)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
+    return decode_common("kvq_decode_step", cache, k_new, v_new, q, out, num_q_heads, sm_scale,
+                         block_tables, max_blocks_per_seq, context_lens, batch, max_context_len,
+                         partition_size, workspace, workspace_bytes, stream);
 }
 
 int kvq_dequant(const kvq_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -256,8 +287,7 @@ int kvq_dequant(const kvq_cache* cache, const int32_t* block_tables, int32_t max
 int kvq_timing_begin(int32_t capacity) {
     if (capacity <= 0 || capacity > (1 << 20)) return fail(KVQ_ERR_ARG, "capacity %d out of range", capacity);
     timing_release();
-    g_timing.ev.assign((size_t)capacity * 4, nullptr);
-    g_timing.has_merge.assign((size_t)capacity, 0);
+    g_timing.ev.assign((size_t)capacity * 2, nullptr);
     for (auto& e : g_timing.ev) {
         hipError_t r = hipEventCreate(&e);
         if (r != hipSuccess) {
@@ -271,36 +301,23 @@ int kvq_timing_begin(int32_t capacity) {
     return ok();
 }
 
-int kvq_timing_end(double* main_ms_total, int32_t* main_count, double* merge_ms_total,
-                   int32_t* merge_count) {
+int kvq_timing_end(double* main_ms_total, int32_t* main_count) {
     if (!g_timing.active) return fail(KVQ_ERR_ARG, "no timing session is active");
-    double mt = 0.0, gt = 0.0;
-    int32_t mc = 0, gc = 0;
+    double mt = 0.0;
+    int32_t mc = 0;
     for (int s = 0; s < g_timing.used; ++s) {
         float ms = 0.0f;
-        hipError_t r = hipEventSynchronize(g_timing.ev[4 * s + 1]);
-        if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[4 * s], g_timing.ev[4 * s + 1]);
+        hipError_t r = hipEventSynchronize(g_timing.ev[2 * s + 1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[2 * s], g_timing.ev[2 * s + 1]);
         if (r != hipSuccess) {
             timing_release();
             return hip_fail(r, "kvq_timing_end");
         }
         mt += ms;
         ++mc;
-        if (g_timing.has_merge[s]) {
-            r = hipEventSynchronize(g_timing.ev[4 * s + 3]);
-            if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.ev[4 * s + 2], g_timing.ev[4 * s + 3]);
-            if (r != hipSuccess) {
-                timing_release();
-                return hip_fail(r, "kvq_timing_end");
-            }
-            gt += ms;
-            ++gc;
-        }
     }
     if (main_ms_total) *main_ms_total = mt;
     if (main_count) *main_count = mc;
-    if (merge_ms_total) *merge_ms_total = gt;
-    if (merge_count) *merge_count = gc;
     timing_release();
     return ok();
 }

@@ -28,10 +28,6 @@ __device__ __forceinline__ int seq_of_row(const int32_t* cu, int batch, int row)
     return lo;
 }
 
-__device__ __forceinline__ float fp16_bits_to_float(uint32_t bits16) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
-}
-
 template <int DT>
 __global__ __launch_bounds__(64) void append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks,
@@ -61,28 +57,23 @@ __global__ __launch_bounds__(64) void append_kernel(
     const size_t src = ((size_t)row * Hkv + g) * (kDim / 2) + lane;
     const uint32_t kw = k_new[src];
     const uint32_t vw = v_new[src];
-    const float k0 = fp16_bits_to_float(kw & 0xFFFFu), k1 = fp16_bits_to_float(kw >> 16);
-    const float v0 = fp16_bits_to_float(vw & 0xFFFFu), v1 = fp16_bits_to_float(vw >> 16);
+    const float k0 = half_bits_to_float(kw & 0xFFFFu), k1 = half_bits_to_float(kw >> 16);
+    const float v0 = half_bits_to_float(vw & 0xFFFFu), v1 = half_bits_to_float(vw >> 16);
 
     uint32_t kc0, kc1, vc0, vc1;
     if constexpr (DT == KVQ_INT8) {
         const float ka = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
         const float va = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-        const float sk = ka / 127.0f;
+        const float sk = ka / 127.0f;  // 0 for an all-zero row
         const float sv = va / 127.0f;
-        auto q8 = [](float x, float s) -> uint32_t {
-            if (s == 0.0f) return 0u;
-            const float r = fminf(fmaxf(__builtin_rintf(x / s), -127.0f), 127.0f);
-            return (uint32_t)(int32_t)r & 0xFFu;
-        };
-        kc0 = q8(k0, ka == 0.0f ? 0.0f : sk);
-        kc1 = q8(k1, ka == 0.0f ? 0.0f : sk);
-        vc0 = q8(v0, va == 0.0f ? 0.0f : sv);
-        vc1 = q8(v1, va == 0.0f ? 0.0f : sv);
+        kc0 = encode_int8(k0, sk);
+        kc1 = encode_int8(k1, sk);
+        vc0 = encode_int8(v0, sv);
+        vc1 = encode_int8(v1, sv);
         if (lane == 0) {
             const size_t so = ((size_t)blk * Hkv + g) * kBlock + t;
-            ks[so] = (ka == 0.0f) ? 0.0f : sk;
-            vs[so] = (va == 0.0f) ? 0.0f : sv;
+            ks[so] = sk;
+            vs[so] = sv;
         }
     } else {
         kc0 = encode_fp8<DT>(k0 / kv_scale);

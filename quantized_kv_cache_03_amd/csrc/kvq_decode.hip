@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int nbytes) {
 }
 
 template <int DT>
-__device__ __forceinline__ float dot16(const uint4& k, const half2_t* q8) {
+__device__ __forceinline__ float dot16(const u32x4& k, const half2_t* q8) {
     float s = 0.0f;
     s = dot2(codes_to_f16<DT, 0>(k.x), q8[0], s);
     s = dot2(codes_to_f16<DT, 1>(k.x), q8[1], s);
@@ -60,7 +60,7 @@ __device__ __forceinline__ float pv_pair(uint32_t codes4, const uint32_t* hi, co
     return acc;
 }
 template <int DT>
-__device__ __forceinline__ float pv16(const uint4& v, const uint32_t* hi, const uint32_t* lo, float acc) {
+__device__ __forceinline__ float pv16(const u32x4& v, const uint32_t* hi, const uint32_t* lo, float acc) {
     acc = pv_pair<DT>(v.x, hi + 0, lo + 0, acc);
     acc = pv_pair<DT>(v.y, hi + 2, lo + 2, acc);
     acc = pv_pair<DT>(v.z, hi + 4, lo + 4, acc);
@@ -94,6 +94,9 @@ struct KernelParams {
     int32_t PS;         // tokens per partition
     float qk_scale;     // sm_scale * log2(e) (* kv_scale for FP8)
     float v_scale;      // kv_scale for FP8, 1 for INT8
+    float kv_scale;     // per-tensor scale of the FP8 encoder (fused append)
+    const uint16_t* k_new;  // fused append: fp16 [B][Hkv][128] new rows (else NULL)
+    const uint16_t* v_new;
 };
 
 // ------------------------------------------------------------------------------------------------
@@ -102,15 +105,24 @@ struct KernelParams {
 // Partials are read in partition order, so the result is bitwise deterministic.
 __device__ __forceinline__ void merge_partials(const KernelParams& a, int b, int h, int np, int lane) {
     const size_t prow0 = ((size_t)b * a.Hq + h) * a.P;
+    // the statistics of up to 64 partitions at a time, one per lane
     float M = kNegInf;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[prow0 + p]);
+    for (int p0 = 0; p0 < np; p0 += 64)
+        M = fmaxf(M, (p0 + lane < np) ? a.part_m[prow0 + p0 + lane] : kNegInf);
+    M = wave_max(M);
     float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int p = 0; p < np; ++p) {
-        const float w = __builtin_amdgcn_exp2f(a.part_m[prow0 + p] - M);
-        L += w * a.part_l[prow0 + p];
-        const float2 op = reinterpret_cast<const float2*>(a.part_o + (prow0 + p) * kDim)[lane];
-        o0 += w * op.x;
-        o1 += w * op.y;
+    for (int p0 = 0; p0 < np; p0 += 64) {
+        const int cnt = min(64, np - p0);
+        const float w_lane = (lane < cnt) ? __builtin_amdgcn_exp2f(a.part_m[prow0 + p0 + lane] - M) : 0.0f;
+        const float wl_lane = (lane < cnt) ? w_lane * a.part_l[prow0 + p0 + lane] : 0.0f;
+        L += wave_sum(wl_lane);
+        for (int i = 0; i < cnt; ++i) {
+            const float w = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), i));
+            const float2 op = reinterpret_cast<const float2*>(a.part_o + (prow0 + p0 + i) * kDim)[lane];
+            o0 += w * op.x;
+            o1 += w * op.y;
+        }
     }
     const float inv = a.v_scale / L;
     const size_t orow = ((size_t)b * a.Hq + h) * kDim;
@@ -119,41 +131,108 @@ __device__ __forceinline__ void merge_partials(const KernelParams& a, int b, int
 }
 
 // ------------------------------------------------------------------------------------------------
+// The codes (and INT8 scales) one lane holds for one tile of 16 tokens.
+//   ka / kb : 16 K codes of tokens 2j and 2j+1 (j = lane / 8), dims 16 (lane % 8) .. +15
+//   va / vb : the 16 tokens' V codes of dims lane and 64 + lane
+//   ks / vs : INT8 scales of tokens 2j and 2j+1
+struct Tile {
+    u32x4 ka, kb, va, vb;
+    float2 ks, vs;
+};
+
+// The token a fused decode step appends, quantized by every wave that reads its tile.
+struct NewToken {
+    int tile;    // tile index inside the sequence; -1 when this wave does not read it
+    int slot;    // position inside the tile
+    u32x4 k;     // this lane's 16 K codes (dims 16 (lane % 8) .. +15)
+    uint32_t v0, v1;  // V codes of dims lane and 64 + lane
+    float ks, vs;     // INT8 scales
+};
+
+template <int DT>
+__device__ __forceinline__ void load_tile(const KernelParams& a, Tile& t, int blk, int g,
+                                          uint32_t k_off, uint32_t v_off, int j) {
+    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+    const uint8_t* kt = a.kc + tile;
+    const uint8_t* vt = a.vc + tile;
+    t.ka = ldg16(kt + k_off);
+    t.kb = ldg16(kt + k_off + 128u);
+    t.va = ldg16(vt + v_off);
+    t.vb = ldg16(vt + 1024u + v_off);
+    if constexpr (DT == KVQ_INT8) {
+        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 2 * j;
+        t.ks = *reinterpret_cast<const float2*>(a.ks + so);
+        t.vs = *reinterpret_cast<const float2*>(a.vs + so);
+    }
+}
+
+__device__ __forceinline__ u32x4 set_byte(u32x4 v, int slot, uint32_t code) {
+    const int sh = 8 * (slot & 3);
+    const uint32_t m = ~(0xFFu << sh), c = code << sh;
+    switch (slot >> 2) {  // wave-uniform
+        case 0: v.x = (v.x & m) | c; break;
+        case 1: v.y = (v.y & m) | c; break;
+        case 2: v.z = (v.z & m) | c; break;
+        default: v.w = (v.w & m) | c; break;
+    }
+    return v;
+}
+
+// Replace the new token's slot in the registers of its tile by the freshly computed codes.
+template <int DT>
+__device__ __forceinline__ void patch_tile(Tile& t, const NewToken& nt, int j) {
+    if (j == (nt.slot >> 1)) {
+        if (nt.slot & 1) {
+            t.kb = nt.k;
+            if constexpr (DT == KVQ_INT8) { t.ks.y = nt.ks; t.vs.y = nt.vs; }
+        } else {
+            t.ka = nt.k;
+            if constexpr (DT == KVQ_INT8) { t.ks.x = nt.ks; t.vs.x = nt.vs; }
+        }
+    }
+    t.va = set_byte(t.va, nt.slot, nt.v0);
+    t.vb = set_byte(t.vb, nt.slot, nt.v1);
+}
+
+// Zero the V codes of the slots at and past `valid` (they may hold any code, NaN included, and a
+// zero weight alone would still give 0 * NaN).
+__device__ __forceinline__ void zero_tail(Tile& t, int valid) {
+    t.va.x = keep_bytes(t.va.x, valid); t.va.y = keep_bytes(t.va.y, valid - 4);
+    t.va.z = keep_bytes(t.va.z, valid - 8); t.va.w = keep_bytes(t.va.w, valid - 12);
+    t.vb.x = keep_bytes(t.vb.x, valid); t.vb.y = keep_bytes(t.vb.y, valid - 4);
+    t.vb.z = keep_bytes(t.vb.z, valid - 8); t.vb.w = keep_bytes(t.vb.w, valid - 12);
+}
+
+// ------------------------------------------------------------------------------------------------
 // One chunk of TW tiles of the partition kernel.  Lane l belongs to group j = l / 8; the group holds
-// tokens 2j and 2j+1 of every tile (K rows read at 256 j + 16 (l % 8) and 128 further), so after the
-// 8-lane sums it owns the weight pair (w_2j, w_2j+1) -- exactly the pairing of adjacent tokens in a
-// V row.  Group leaders publish their (hi, lo) weight pairs in LDS and every lane reads all eight
-// back with broadcast loads.  MASKED handles a chunk that reaches past the partition end (its logits
-// past the end become -inf; the caller has already zeroed the V codes of the partial tile).
+// tokens 2j and 2j+1 of every tile, so after the 8-lane sums it owns the weight pair (w_2j, w_2j+1)
+// -- exactly the pairing of adjacent tokens in a V row.  Group leaders publish their (hi, lo)
+// weight pairs in LDS and every lane reads all eight back with broadcast loads.  MASKED handles a
+// chunk that reaches past the partition end (logits past the end become -inf; the caller has
+// already zeroed the V codes of the partial tile).
 template <int DT, int TW, bool MASKED>
-__device__ __forceinline__ void chunk_step(const KernelParams& a, const uint4 (&ka)[TW],
-                                           const uint4 (&kb)[TW], const uint4 (&va)[TW],
-                                           const uint4 (&vb)[TW],
-                                           const int (&blks)[TW], int tile0, int nvalid, int t_end,
-                                           const half2_t (&qv)[8], int g, int lane, uint32_t* lds,
-                                           float& m_run, float& l_lane, float& acc0, float& acc1) {
+__device__ __forceinline__ void chunk_step(const KernelParams& a, const Tile (&t)[TW], int tile0,
+                                           int t_end, const half2_t (&qv)[8], int lane,
+                                           uint32_t* lds, float& m_run, float& l_lane, float& acc0,
+                                           float& acc1) {
     const int j = lane >> 3;
     float za[TW], zb[TW];
     float cmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const float sa = sum8(dot16<DT>(ka[i], qv));
-        const float sb = sum8(dot16<DT>(kb[i], qv));
+        const float sa = sum8(dot16<DT>(t[i].ka, qv));
+        const float sb = sum8(dot16<DT>(t[i].kb, qv));
         float fa = a.qk_scale, fb = a.qk_scale;
         if constexpr (DT == KVQ_INT8) {
-            if (!MASKED || i < nvalid) {
-                const float2 s2 = *reinterpret_cast<const float2*>(
-                    a.ks + ((size_t)blks[i] * a.Hkv + g) * kBlock + 2 * j);
-                fa *= s2.x;
-                fb *= s2.y;
-            }
+            fa *= t[i].ks.x;
+            fb *= t[i].ks.y;
         }
         za[i] = sa * fa;
         zb[i] = sb * fb;
         if constexpr (MASKED) {
             const int pos = (tile0 + i) * kBlock + 2 * j;
-            za[i] = (i < nvalid && pos < t_end) ? za[i] : kNegInf;
-            zb[i] = (i < nvalid && pos + 1 < t_end) ? zb[i] : kNegInf;
+            za[i] = (pos < t_end) ? za[i] : kNegInf;
+            zb[i] = (pos + 1 < t_end) ? zb[i] : kNegInf;
         }
         cmax = fmaxf(cmax, fmaxf(za[i], zb[i]));
     }
@@ -172,13 +251,9 @@ __device__ __forceinline__ void chunk_step(const KernelParams& a, const uint4 (&
         l_lane += pa + pb;
         float wa = pa, wb = pb;
         if constexpr (DT == KVQ_INT8) {
-            if (!MASKED || i < nvalid) {
-                const float2 s2 = *reinterpret_cast<const float2*>(
-                    a.vs + ((size_t)blks[i] * a.Hkv + g) * kBlock + 2 * j);
-                // masked slots may hold NaN scales: keep their weight exactly 0
-                wa = (pa > 0.0f) ? pa * s2.x : 0.0f;
-                wb = (pb > 0.0f) ? pb * s2.y : 0.0f;
-            }
+            // masked slots may hold NaN scales: keep their weight exactly 0
+            wa = (pa > 0.0f) ? pa * t[i].vs.x : 0.0f;
+            wb = (pb > 0.0f) ? pb * t[i].vs.y : 0.0f;
         }
         uint32_t hi, lo;
         split_f16x2(wa, wb, hi, lo);
@@ -190,16 +265,80 @@ __device__ __forceinline__ void chunk_step(const KernelParams& a, const uint4 (&
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const uint4* l4 = reinterpret_cast<const uint4*>(lds + i * 16);
-        const uint4 h0 = l4[0], h1 = l4[1], w0 = l4[2], w1 = l4[3];
+        const u32x4* l4 = reinterpret_cast<const u32x4*>(lds + i * 16);
+        const u32x4 h0 = l4[0], h1 = l4[1], w0 = l4[2], w1 = l4[3];
         const uint32_t whi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
         const uint32_t wlo[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        acc0 = pv16<DT>(va[i], whi, wlo, acc0);
-        acc1 = pv16<DT>(vb[i], whi, wlo, acc1);
+        acc0 = pv16<DT>(t[i].va, whi, wlo, acc0);
+        acc1 = pv16<DT>(t[i].vb, whi, wlo, acc1);
         // keep the next tile's weight reads from being hoisted: they would pin 16 more VGPRs per tile
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// Quantize the appended token of sequence b for KV head g in the lane layout of a Tile; the wave
+// designated as writer also stores it into the cache.  Bit-identical to the append kernel.
+template <int DT>
+__device__ __forceinline__ NewToken new_token(const KernelParams& a, int b, int g, int n,
+                                              bool writer, int lane, const int32_t* bt) {
+    NewToken nt;
+    nt.tile = (n - 1) / kBlock;
+    nt.slot = (n - 1) % kBlock;
+    const size_t row = ((size_t)b * a.Hkv + g) * kDim;
+    const u32x4 kr0 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7));
+    const u32x4 kr1 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7) + 8);
+    const uint32_t kw[8] = {kr0.x, kr0.y, kr0.z, kr0.w, kr1.x, kr1.y, kr1.z, kr1.w};
+    float kx[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        kx[2 * i] = half_bits_to_float(kw[i] & 0xFFFFu);
+        kx[2 * i + 1] = half_bits_to_float(kw[i] >> 16);
+    }
+    const float vx0 = half_bits_to_float(a.v_new[row + lane]);
+    const float vx1 = half_bits_to_float(a.v_new[row + 64 + lane]);
+    uint32_t kc[16];
+    if constexpr (DT == KVQ_INT8) {
+        float km = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) km = fmaxf(km, fabsf(kx[i]));
+        const float ka = wave_max(km);  // lanes l, l+8, .. hold the same 16 dims: max is unaffected
+        const float va = wave_max(fmaxf(fabsf(vx0), fabsf(vx1)));
+        nt.ks = ka / 127.0f;
+        nt.vs = va / 127.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kc[i] = encode_int8(kx[i], nt.ks);
+        nt.v0 = encode_int8(vx0, nt.vs);
+        nt.v1 = encode_int8(vx1, nt.vs);
+    } else {
+        const float s = a.kv_scale;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kc[i] = encode_fp8<DT>(kx[i] / s);
+        nt.v0 = encode_fp8<DT>(vx0 / s);
+        nt.v1 = encode_fp8<DT>(vx1 / s);
+        nt.ks = nt.vs = 0.0f;
+    }
+    nt.k.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
+    nt.k.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
+    nt.k.z = kc[8] | (kc[9] << 8) | (kc[10] << 16) | (kc[11] << 24);
+    nt.k.w = kc[12] | (kc[13] << 8) | (kc[14] << 16) | (kc[15] << 24);
+    if (writer) {
+        const int blk = bt[nt.tile];
+        const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+        uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
+        uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
+        if (lane < 8) *reinterpret_cast<u32x4*>(kt + nt.slot * kDim + 16 * lane) = nt.k;
+        vt[(size_t)lane * kBlock + nt.slot] = (uint8_t)nt.v0;
+        vt[(size_t)(64 + lane) * kBlock + nt.slot] = (uint8_t)nt.v1;
+        if constexpr (DT == KVQ_INT8) {
+            if (lane == 0) {
+                const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + nt.slot;
+                const_cast<float*>(a.ks)[so] = nt.ks;
+                const_cast<float*>(a.vs)[so] = nt.vs;
+            }
+        }
+    }
+    return nt;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -207,7 +346,10 @@ __device__ __forceinline__ void chunk_step(const KernelParams& a, const uint4 (&
 // dimension: workgroups are handed to the eight XCDs round-robin by linear id, so consecutive ids
 // must carry equal work -- all heads of one (partition, sequence) do, while consecutive partitions
 // of one sequence do not (its last partitions are ragged or empty).
-template <int DT, int TW, bool PIPE>
+// APPEND: the decode step's new token (one per sequence, at position context_lens[b] - 1) is
+// quantized here by the waves of the last partition and written to the cache by the wave of the
+// group's first query head.
+template <int DT, int TW, bool APPEND>
 __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     __shared__ uint32_t lds[TW * 16];
     const int h = blockIdx.x;
@@ -216,6 +358,7 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     const int lane = threadIdx.x;
     const int G = a.Hq / a.Hkv;
     const int g = h / G;
+    const int j = lane >> 3;
 
     const int n = a.ctx[b];
     const int np = (n + a.PS - 1) / a.PS;  // partitions this sequence uses
@@ -232,20 +375,23 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     const int t_end = min(n, t_begin + a.PS);
     const int tile_begin = t_begin / kBlock;
     const int tile_end = (t_end + kBlock - 1) / kBlock;
+    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+
+    NewToken nt{-1, 0, u32x4{0u, 0u, 0u, 0u}, 0u, 0u, 0.0f, 0.0f};
+    if constexpr (APPEND) {
+        if (p == np - 1) nt = new_token<DT>(a, b, g, n, h % G == 0, lane, bt);
+    }
 
     // q slice of this lane's K dims: 16 (lane % 8) .. +15
     half2_t qv[8];
     {
-        const uint4* qp = reinterpret_cast<const uint4*>(a.q + orow + (lane & 7) * 16);
-        const uint4 q0 = qp[0], q1 = qp[1];
+        const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + orow + (lane & 7) * 16);
+        const u32x4 q0 = qp[0], q1 = qp[1];
         const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) qv[i] = __builtin_bit_cast(half2_t, qw[i]);
     }
 
-    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
-    const size_t head_off = (size_t)g * kTileBytes;
-    const size_t blk_stride = (size_t)a.Hkv * kTileBytes;
     const uint32_t k_off = 256u * ((uint32_t)lane >> 3) + 16u * ((uint32_t)lane & 7u);  // token 2 (lane/8)
     const uint32_t v_off = 16u * (uint32_t)lane;
 
@@ -258,69 +404,31 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
         const int nt_grp = min(64, tile_end - tb);
         const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
 
-        auto load_chunk = [&](int c, uint4 (&ka)[TW], uint4 (&kb)[TW], uint4 (&va)[TW],
-                              uint4 (&vb)[TW], int (&blks)[TW]) {
-#pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                blks[i] = __builtin_amdgcn_readlane(blk_lane, c * TW + i);
-                const uint8_t* kt = a.kc + (size_t)blks[i] * blk_stride + head_off;
-                const uint8_t* vt = a.vc + (size_t)blks[i] * blk_stride + head_off;
-                ka[i] = ldg16(kt + k_off);
-                kb[i] = ldg16(kt + k_off + 128u);
-                va[i] = ldg16(vt + v_off);
-                vb[i] = ldg16(vt + 1024u + v_off);
-            }
-        };
-        // whole chunks: TW tiles, all inside the partition
-        const int full_tiles = min(nt_grp, (t_end - tb * kBlock) / kBlock);
+        // whole chunks: TW tiles, all inside the partition.  The sequence's last tile (which holds
+        // the token a fused step appends) is always left to the single-tile loop below, with or
+        // without the fused append, so that both give bitwise the same arithmetic.
+        int full_tiles = min(nt_grp, (t_end - tb * kBlock) / kBlock);
+        if (p == np - 1) full_tiles = min(full_tiles, (n - 1) / kBlock - tb);
         const int nfull = full_tiles / TW;
-        if constexpr (PIPE) {
-            // two register buffers: the next chunk's loads are in flight while this one computes
-            uint4 ka0[TW], kb0[TW], va0[TW], vb0[TW], ka1[TW], kb1[TW], va1[TW], vb1[TW];
-            int bl0[TW], bl1[TW];
-            if (nfull > 0) load_chunk(0, ka0, kb0, va0, vb0, bl0);
-            for (int c = 0; c < nfull; c += 2) {
-                if (c + 1 < nfull) load_chunk(c + 1, ka1, kb1, va1, vb1, bl1);
-                chunk_step<DT, TW, false>(a, ka0, kb0, va0, vb0, bl0, tb + c * TW, TW, t_end, qv, g,
-                                          lane, lds, m_run, l_lane, acc0, acc1);
-                if (c + 1 < nfull) {
-                    if (c + 2 < nfull) load_chunk(c + 2, ka0, kb0, va0, vb0, bl0);
-                    chunk_step<DT, TW, false>(a, ka1, kb1, va1, vb1, bl1, tb + (c + 1) * TW, TW,
-                                              t_end, qv, g, lane, lds, m_run, l_lane, acc0, acc1);
-                }
-            }
-        } else {
-            for (int c = 0; c < nfull; ++c) {
-                uint4 ka[TW], kb[TW], va[TW], vb[TW];
-                int blks[TW];
-                load_chunk(c, ka, kb, va, vb, blks);
-                chunk_step<DT, TW, false>(a, ka, kb, va, vb, blks, tb + c * TW, TW, t_end, qv, g,
-                                          lane, lds, m_run, l_lane, acc0, acc1);
-            }
+        for (int c = 0; c < nfull; ++c) {
+            Tile t[TW];
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+                load_tile<DT>(a, t[i], __builtin_amdgcn_readlane(blk_lane, c * TW + i), g, k_off,
+                              v_off, j);
+            chunk_step<DT, TW, false>(a, t, tb + c * TW, t_end, qv, lane, lds, m_run, l_lane, acc0,
+                                      acc1);
         }
-        int c0 = nfull * TW;
-        // the rest one tile at a time, the last one possibly partial
-        for (; c0 < nt_grp; ++c0) {
-            uint4 ka[1], kb[1], va[1], vb[1];
-            int blks[1];
-            blks[0] = __builtin_amdgcn_readlane(blk_lane, c0);
-            const uint8_t* kt = (a.kc + (size_t)blks[0] * blk_stride + head_off);
-            const uint8_t* vt = (a.vc + (size_t)blks[0] * blk_stride + head_off);
-            ka[0] = ldg16(kt + k_off);
-            kb[0] = ldg16(kt + k_off + 128u);
-            va[0] = ldg16(vt + v_off);
-            vb[0] = ldg16(vt + 1024u + v_off);
-            const int valid = t_end - (tb + c0) * kBlock;
-            if (valid < kBlock) {
-                // slots past the end may hold any code, NaN included: zero them, since a zero
-                // weight alone would still give 0 * NaN
-                va[0].x = keep_bytes(va[0].x, valid); va[0].y = keep_bytes(va[0].y, valid - 4);
-                va[0].z = keep_bytes(va[0].z, valid - 8); va[0].w = keep_bytes(va[0].w, valid - 12);
-                vb[0].x = keep_bytes(vb[0].x, valid); vb[0].y = keep_bytes(vb[0].y, valid - 4);
-                vb[0].z = keep_bytes(vb[0].z, valid - 8); vb[0].w = keep_bytes(vb[0].w, valid - 12);
+        // the rest one tile at a time: the last one possibly partial, or holding the new token
+        for (int c0 = nfull * TW; c0 < nt_grp; ++c0) {
+            Tile t[1];
+            load_tile<DT>(a, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, k_off, v_off, j);
+            if constexpr (APPEND) {
+                if (tb + c0 == nt.tile) patch_tile<DT>(t[0], nt, j);
             }
-            chunk_step<DT, 1, true>(a, ka, kb, va, vb, blks, tb + c0, 1, t_end, qv, g, lane, lds,
-                                    m_run, l_lane, acc0, acc1);
+            const int valid = t_end - (tb + c0) * kBlock;
+            if (valid < kBlock) zero_tail(t[0], valid);
+            chunk_step<DT, 1, true>(a, t, tb + c0, t_end, qv, lane, lds, m_run, l_lane, acc0, acc1);
         }
     }
     // each token's weight was added by all 8 lanes of its group: count group leaders only
@@ -357,11 +465,14 @@ __global__ __launch_bounds__(64) void attn_merge(KernelParams a) {
 // ------------------------------------------------------------------------------------------------
 template <int DT>
 static void launch_partition(const KernelParams& kp, dim3 grid, hipStream_t stream) {
-    attn_partition_valu<DT, 4, false><<<grid, 64, 0, stream>>>(kp);
+    if (kp.k_new)
+        attn_partition_valu<DT, 4, true><<<grid, 64, 0, stream>>>(kp);
+    else
+        attn_partition_valu<DT, 4, false><<<grid, 64, 0, stream>>>(kp);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
-                         hipEvent_t main_end, hipEvent_t merge_begin, hipEvent_t merge_end) {
+                         hipEvent_t main_end) {
     const kvq_cache& c = *a.cache;
     if (a.batch == 0) return hipSuccess;
     KernelParams kp;
@@ -384,6 +495,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     const bool fp8 = c.dtype != KVQ_INT8;
     kp.qk_scale = a.sm_scale * kLog2e * (fp8 ? c.kv_scale : 1.0f);
     kp.v_scale = fp8 ? c.kv_scale : 1.0f;
+    kp.kv_scale = c.kv_scale;
+    kp.k_new = a.k_new;
+    kp.v_new = a.v_new;
 
     const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_partitions, (unsigned)a.batch);
     if (main_begin) (void)hipEventRecord(main_begin, stream);
@@ -396,9 +510,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.num_partitions > 1) {
-        if (merge_begin) (void)hipEventRecord(merge_begin, stream);
         attn_merge<<<dim3((unsigned)a.num_q_heads, (unsigned)a.batch), 64, 0, stream>>>(kp);
-        if (merge_end) (void)hipEventRecord(merge_end, stream);
         e = hipGetLastError();
     }
     return e;

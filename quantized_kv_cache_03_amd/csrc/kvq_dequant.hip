@@ -35,7 +35,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(
         const int tok = half * 8 + (lane >> 3);
         const int pos = tile_idx * kBlock + tok;
         const int d0 = (lane & 7) * 16;
-        const uint4 w = ldg16(kc + tile + (size_t)tok * kDim + d0);
+        const u32x4 w = ldg16(kc + tile + (size_t)tok * kDim + d0);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
         const float s = (DT == KVQ_INT8) ? ks[sbase + tok] : kv_scale;
         if (pos < n) {
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const int d = half * 64 + lane;
-        const uint4 w = ldg16(vc + tile + (size_t)d * kBlock);
+        const u32x4 w = ldg16(vc + tile + (size_t)d * kBlock);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -17,6 +17,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 codes, byte i = code i
 
 constexpr int kDim = KVQ_HEAD_DIM;     // 128
 constexpr int kBlock = KVQ_BLOCK_SIZE; // 16
@@ -35,6 +36,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // every such value either rounds to it or overflows, and overflow saturates.
 template <int FMT>
 __device__ __forceinline__ uint32_t encode_fp8(float y) {
+#pragma clang fp contract(off)
     constexpr int M = (FMT == KVQ_FP8_E4M3) ? 3 : 2;
     constexpr int BIAS = (FMT == KVQ_FP8_E4M3) ? 7 : 15;
     constexpr uint32_t MAX_BITS = (FMT == KVQ_FP8_E4M3) ? 0x43E00000u   // 448
@@ -55,6 +57,19 @@ __device__ __forceinline__ uint32_t encode_fp8(float y) {
     // exact power-of-two scaling, then round half to even (v_rndne_f32)
     const float steps = __uint_as_float(a) * (float)(1u << (BIAS - 1 + M));
     return sign | (uint32_t)__builtin_rintf(steps);
+}
+
+// INT8 code of x for a row scale s (s = fl32(amax / 127) > 0): clamp(rne(fl32(x / s)), -127, 127),
+// as a byte; a zero row (s == 0) gives 0.
+__device__ __forceinline__ uint32_t encode_int8(float x, float s) {
+#pragma clang fp contract(off)
+    if (s == 0.0f) return 0u;
+    const float r = fminf(fmaxf(__builtin_rintf(x / s), -127.0f), 127.0f);
+    return (uint32_t)(int32_t)r & 0xFFu;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -129,6 +144,13 @@ __device__ __forceinline__ float sum_across8(float v) {
     v += __shfl_xor(v, 32);
     return v;
 }
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    v = sum_across8(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+}
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp<0xB1>(v));
     v = fmaxf(v, dpp<0x4E>(v));
@@ -136,8 +158,8 @@ __device__ __forceinline__ float wave_max(float v) {
     return max_across8(v);
 }
 
-__device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
-    return *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ u32x4 ldg16(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
 }
 
 }  // namespace kvq

@@ -24,6 +24,8 @@ struct DecodeArgs {
     float* part_o;            // [B][Hq][P][128] (NULL when num_partitions == 1)
     float* part_m;            // [B][Hq][P]
     float* part_l;            // [B][Hq][P]
+    const uint16_t* k_new;    // fused decode step: fp16 [B][Hkv][128] rows to append, else NULL
+    const uint16_t* v_new;
 };
 
 hipError_t launch_append(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
@@ -35,9 +37,10 @@ hipError_t launch_dequant(const kvq_cache& c, const int32_t* block_tables, int32
                           const int32_t* context_lens, int32_t batch, int32_t max_context_len,
                           float* k_out, float* v_out, hipStream_t stream);
 
-// Partition kernel, then (when num_partitions > 1) the merge kernel.  The optional events are
-// recorded around each of the two launches (kernel-timing hook).
+// Partition kernel (with the append of the decode step when k_new is set), then, when
+// num_partitions > 1, the merge kernel.  The optional events are recorded around the partition
+// kernel (kernel-timing hook).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
-                         hipEvent_t main_end, hipEvent_t merge_begin, hipEvent_t merge_end);
+                         hipEvent_t main_end);
 
 }  // namespace kvq

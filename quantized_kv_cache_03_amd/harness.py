@@ -1,9 +1,10 @@
 """Device-side set-up of a synthetic decode workload through the library's own entry points.
 
 Allocates one layer's paged cache on the GPU, fills it with kvq_append (a prefill over every
-sequence's rows), and prepares the decode step: one new token per sequence (the last row of each
-sequence, re-appended to the slot it already occupies, so repeated steps are idempotent) followed
-by kvq_paged_decode_attn.  Host arrays come from ``workloads``; nothing here computes the method.
+sequence's rows, optionally all but the last), and prepares the decode step: one new token per
+sequence (the last row of each sequence, written to its slot; repeated steps rewrite the same bytes,
+so they are idempotent) followed by the attention, as one kvq_decode_step call or as kvq_append then
+kvq_paged_decode_attn.  Host arrays come from ``workloads``; nothing here computes the method.
 """
 from __future__ import annotations
 
@@ -19,7 +20,10 @@ _CHUNK_ROWS = 1 << 20
 
 class DeviceCase:
     def __init__(self, w: W.Workload, device: str = "cuda", spare_blocks: int = 0,
-                 keep_host_rows: bool = False, poison: bool = True, verbose: bool = False):
+                 keep_host_rows: bool = False, poison: bool = True, verbose: bool = False,
+                 prefill_last: bool = True):
+        """prefill_last=False leaves each sequence's last slot unwritten (poisoned), so the first
+        decode step is the only writer of the appended token."""
         self.w = w
         self.device = device
         self.ctx = W.context_lens(w)
@@ -45,7 +49,7 @@ class DeviceCase:
         self.q = W.query(w)
         self.q_d = torch.from_numpy(self.q).to(device)
         self.out_d = torch.empty_like(self.q_d)
-        self._prefill(k, v, verbose)
+        self._prefill(k, v, verbose, 0 if prefill_last else 1)
         # the decode step's new rows: the last row of each sequence
         last_k = np.empty((self.B, w.num_kv_heads, W.HEAD_DIM), np.float16)
         last_v = np.empty_like(last_k)
@@ -65,8 +69,11 @@ class DeviceCase:
             self.B, w.num_q_heads, self.max_ctx, self.partition_size, device=device)
         torch.cuda.synchronize()
 
-    def _prefill(self, k, v, verbose):
+    def _prefill(self, k, v, verbose, skip: int):
+        """Append every sequence's rows but the last `skip` ones, in chunks of sequences."""
         w, ctx = self.w, self.ctx
+        pre = np.maximum(ctx - skip, 0).astype(np.int32)
+        pre_d = torch.from_numpy(pre).to(self.device)
         b0 = 0
         while b0 < self.B:
             b1, rows = b0, 0
@@ -75,17 +82,19 @@ class DeviceCase:
                 b1 += 1
             if k is not None:
                 cu_all = np.concatenate([[0], np.cumsum(ctx)])
-                kc, vc = k[cu_all[b0]:cu_all[b1]], v[cu_all[b0]:cu_all[b1]]
+                kc = np.concatenate([k[cu_all[b]:cu_all[b] + pre[b]] for b in range(b0, b1)])
+                vc = np.concatenate([v[cu_all[b]:cu_all[b] + pre[b]] for b in range(b0, b1)])
             else:
                 parts = [W.kv_rows(w, b, int(ctx[b]), self.channels) for b in range(b0, b1)]
-                kc = np.concatenate([p[0] for p in parts])
-                vc = np.concatenate([p[1] for p in parts])
+                kc = np.concatenate([p[0][:pre[b0 + i]] for i, p in enumerate(parts)])
+                vc = np.concatenate([p[1][:pre[b0 + i]] for i, p in enumerate(parts)])
             cu = np.zeros(b1 - b0 + 1, np.int32)
-            cu[1:] = np.cumsum(ctx[b0:b1])
-            kd = torch.from_numpy(np.ascontiguousarray(kc)).to(self.device)
-            vd = torch.from_numpy(np.ascontiguousarray(vc)).to(self.device)
-            K.append(self.cache, kd, vd, self.bt_d[b0:b1].contiguous(), self.ctx_d[b0:b1].contiguous(),
-                     cu_new_lens=torch.from_numpy(cu).to(self.device), num_new_rows=int(cu[-1]))
+            cu[1:] = np.cumsum(pre[b0:b1])
+            if int(cu[-1]) > 0:
+                kd = torch.from_numpy(np.ascontiguousarray(kc)).to(self.device)
+                vd = torch.from_numpy(np.ascontiguousarray(vc)).to(self.device)
+                K.append(self.cache, kd, vd, self.bt_d[b0:b1].contiguous(), pre_d[b0:b1].contiguous(),
+                         cu_new_lens=torch.from_numpy(cu).to(self.device), num_new_rows=int(cu[-1]))
             if verbose:
                 print(f"  prefill sequences {b0}..{b1 - 1} ({rows} rows)", flush=True)
             b0 = b1
@@ -102,9 +111,15 @@ class DeviceCase:
                                    partition_size=ps, workspace=ws,
                                    out=self.out_d if out is None else out, stream=stream)
 
-    def step(self, stream=None):
-        self.append_step(stream)
-        return self.attention(stream=stream)
+    def step(self, stream=None, fused: bool = True):
+        """One decode step: append one token per sequence, then attention (one fused call, or
+        kvq_append followed by kvq_paged_decode_attn)."""
+        if not fused:
+            self.append_step(stream)
+            return self.attention(stream=stream)
+        return K.decode_step(self.cache, self.step_k_d, self.step_v_d, self.q_d, self.bt_d, self.ctx_d,
+                             self.max_ctx, partition_size=self.partition_size,
+                             workspace=self.workspace, out=self.out_d, stream=stream)
 
     # host views of the sequences' own rows (regenerated from the seeds)
     def rows_of(self, b: int):

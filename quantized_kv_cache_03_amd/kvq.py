@@ -50,6 +50,9 @@ lib.kvq_decode_workspace_size.restype = _sz
 lib.kvq_paged_decode_attn.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _i32, _f32, _vp, _i32,
                                       _vp, _i32, _i32, _i32, _vp, _sz, _vp]
 lib.kvq_paged_decode_attn.restype = ctypes.c_int
+lib.kvq_decode_step.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32,
+                                _vp, _i32, _i32, _i32, _vp, _sz, _vp]
+lib.kvq_decode_step.restype = ctypes.c_int
 lib.kvq_dequant.argtypes = [ctypes.POINTER(KvqCache), _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 lib.kvq_dequant.restype = ctypes.c_int
 lib.kvq_dtype_from_string.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]
@@ -60,13 +63,13 @@ lib.kvq_last_error.argtypes = []
 lib.kvq_last_error.restype = ctypes.c_char_p
 lib.kvq_timing_begin.argtypes = [_i32]
 lib.kvq_timing_begin.restype = ctypes.c_int
-lib.kvq_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32),
-                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
+lib.kvq_timing_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i32)]
 lib.kvq_timing_end.restype = ctypes.c_int
 lib.kvq_version.argtypes = []
 lib.kvq_version.restype = ctypes.c_char_p
 
-EXPORTS = ["kvq_append", "kvq_decode_workspace_size", "kvq_paged_decode_attn", "kvq_dequant",
+EXPORTS = ["kvq_append", "kvq_decode_workspace_size", "kvq_paged_decode_attn", "kvq_decode_step",
+           "kvq_dequant",
            "kvq_dtype_from_string", "kvq_status_string", "kvq_last_error", "kvq_timing_begin",
            "kvq_timing_end", "kvq_version"]
 
@@ -191,6 +194,32 @@ def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.
     return out
 
 
+def decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                sm_scale: float | None = None, partition_size: int = 512,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """kvq_decode_step: append one row per sequence (fp16 [B][Hkv][128]) and attend, fused."""
+    assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
+    assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
+    B, Hq, _ = q.shape
+    assert k_new.shape == (B, cache.num_kv_heads, HEAD_DIM) and v_new.shape == k_new.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty_like(q)
+    need = workspace_size(B, Hq, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = cache.descriptor()
+    _check(lib.kvq_decode_step(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), Hq,
+                               float(sm_scale), _ptr(block_tables), block_tables.shape[1],
+                               _ptr(context_lens), B, int(max_context_len), int(partition_size),
+                               _ptr(workspace), ws_bytes, _stream(stream)), "kvq_decode_step")
+    return out
+
+
 def dequant(cache: PagedKVCache, block_tables: torch.Tensor, context_lens: torch.Tensor,
             max_context_len: int, k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None,
             stream=None):
@@ -214,12 +243,11 @@ def timing_begin(capacity: int) -> None:
 
 
 def timing_end():
-    """-> (main_ms_total, main_count, merge_ms_total, merge_count)."""
-    mt, gt = ctypes.c_double(0), ctypes.c_double(0)
-    mc, gc = ctypes.c_int32(0), ctypes.c_int32(0)
-    _check(lib.kvq_timing_end(ctypes.byref(mt), ctypes.byref(mc), ctypes.byref(gt), ctypes.byref(gc)),
-           "kvq_timing_end")
-    return mt.value, mc.value, gt.value, gc.value
+    """-> (summed milliseconds of the timed partition kernels, number of timed launches)."""
+    mt = ctypes.c_double(0)
+    mc = ctypes.c_int32(0)
+    _check(lib.kvq_timing_end(ctypes.byref(mt), ctypes.byref(mc)), "kvq_timing_end")
+    return mt.value, mc.value
 
 
 def version() -> str:

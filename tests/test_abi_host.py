@@ -136,4 +136,19 @@ def test_dequant_argument_errors(K):
 
 
 def test_timing_end_without_begin(K):
-    assert K.lib.kvq_timing_end(None, None, None, None) == K.ERR_ARG
+    assert K.lib.kvq_timing_end(None, None) == K.ERR_ARG
+
+
+def test_decode_step_argument_errors(K):
+    c = _cache(K)
+    L = K.lib
+    args = dict(Hq=2, sm=0.1, bt=0x10, mb=4, ctx=0x20, B=1, L=64, ps=0)
+    # missing new rows
+    assert L.kvq_decode_step(ctypes.byref(c), None, 0x60, 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1, 64, 0,
+                             None, 0, None) == K.ERR_ARG
+    # the shared validation applies
+    assert L.kvq_decode_step(ctypes.byref(c), 0x50, 0x60, 0x30, 0x40, 3, 0.1, 0x10, 4, 0x20, 1, 64, 0,
+                             None, 0, None) == K.ERR_SHAPE
+    assert L.kvq_decode_step(ctypes.byref(c), 0x50, 0x60, 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1, 64, 16,
+                             None, 0, None) == K.ERR_WORKSPACE
+    del args

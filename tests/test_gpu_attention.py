@@ -1,4 +1,5 @@
-"""GPU parity of the decode step (kvq_append + kvq_paged_decode_attn) against the oracle.
+"""GPU parity of the decode step against the oracle: kvq_append + kvq_paged_decode_attn, and the
+fused kvq_decode_step.
 
 Scaled-down copies of the five workloads keep the oracle within seconds while still spanning
 several tiles, several partitions and ragged tails; every (sequence, head) output is compared.
@@ -44,8 +45,8 @@ def test_decode_step_scaled(H, name, ctx, kw, partition):
     w = _scaled(name, ctx, partition_size=partition, **kw)
     say(f"[decode step] {w.name} ctx={ctx} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"dtype={w.dtype} partition={partition}")
-    case = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2)
-    out = case.step().cpu().numpy()
+    case = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2, prefill_last=False)
+    out = case.step(fused=False).cpu().numpy()  # kvq_append, then kvq_paged_decode_attn
     twin = OracleTwin(case, range(case.B))
     assert_cache_bytes_equal(case, twin, w.name)
     ref = twin.attention()
@@ -112,3 +113,22 @@ def test_empty_batch_is_a_no_op(H):
     assert out.shape == (0, 2, 128)
     kvq.append(c, q, q, bt, ctx)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,ctx,kw", CASES, ids=[c[0] for c in CASES])
+def test_fused_step_appends_and_matches_separate_calls(H, name, ctx, kw):
+    """kvq_decode_step on a cache whose last slots were never written: its cache bytes equal the
+    oracle's full append, its output passes the gate, and both equal, bit for bit, kvq_append
+    followed by kvq_paged_decode_attn on an identically prepared cache."""
+    w = _scaled(name, ctx, partition_size=64, **kw)
+    say(f"[fused step] {w.name} ctx={ctx} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype}")
+    fused = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2, prefill_last=False)
+    sep = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2, prefill_last=False)
+    out_f = fused.step(fused=True).cpu().numpy()
+    out_s = sep.step(fused=False).cpu().numpy()
+    twin = OracleTwin(fused, range(fused.B))
+    assert_cache_bytes_equal(fused, twin, "fused " + w.name)
+    assert_cache_bytes_equal(sep, twin, "separate " + w.name)
+    np.testing.assert_array_equal(out_f.view(np.uint16), out_s.view(np.uint16))
+    st = assert_attn_close(out_f, twin.attention(), w.name)
+    say(f"    ok {st}")

@@ -1,7 +1,8 @@
 """The five workloads at full size, in the launch configuration the benchmark times.
 
-Each case fills the whole cache through kvq_append, runs one decode step (append one token per
-sequence, then split-K attention with the workload's partition size) and checks sampled
+Each case fills the cache through kvq_append with all but each sequence's last token, runs one
+fused decode step (kvq_decode_step: append that token, then split-K attention with the workload's
+partition size, as the benchmark times it) and checks sampled
 sequences against the oracle: every cache byte of those sequences bit for bit, and every output
 element of every head of those sequences within the gate.  The rest of the batch is checked for
 properties that hold at any size: no NaN, and the step is bitwise reproducible.
@@ -26,7 +27,7 @@ def test_full_size_decode_step(name):
     w = W.WORKLOADS[name]
     say(f"[full size] {name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype} "
         f"partition={w.partition_size}")
-    case = harness.DeviceCase(w, verbose=True)
+    case = harness.DeviceCase(w, verbose=True, prefill_last=False)  # the step writes the last token
     say(f"  cache filled: {case.num_blocks} blocks, sum ctx {int(case.ctx.sum())}, kv_scale {case.kv_scale!r}")
     out1 = case.step().clone()
     out2 = case.step().clone()
