@@ -36,10 +36,17 @@ CASES = [
     ("llama3-8b-gqa-e5m2", [1200, 16, 513], {"num_q_heads": 8, "num_kv_heads": 2}),
     ("llama2-13b-mha-int8", [2, 600, 1500, 17], {"num_q_heads": 3, "num_kv_heads": 3}),
     ("llama3-70b-gqa-e4m3-32k", [3000, 1], {"num_q_heads": 16, "num_kv_heads": 2}),
+    # more head groupings: 3 (INT8 with outliers), 16 (the largest), 2
+    ("llama2-13b-mha-int8", [700, 33], {"num_q_heads": 6, "num_kv_heads": 2}),
+    ("tiny-e4m3", [300, 2], {"num_q_heads": 16, "num_kv_heads": 1}),
+    ("llama3-8b-gqa-e5m2", [100, 517], {"num_q_heads": 4, "num_kv_heads": 2}),
 ]
 
 
-@pytest.mark.parametrize("name,ctx,kw", CASES, ids=[c[0] for c in CASES])
+IDS = [f"{c[0]}-G{c[2].get('num_q_heads', 0) // max(1, c[2].get('num_kv_heads', 1))}" for c in CASES]
+
+
+@pytest.mark.parametrize("name,ctx,kw", CASES, ids=IDS)
 @pytest.mark.parametrize("partition", [0, 16, 64, 512])
 def test_decode_step_scaled(H, name, ctx, kw, partition):
     w = _scaled(name, ctx, partition_size=partition, **kw)
@@ -115,7 +122,7 @@ def test_empty_batch_is_a_no_op(H):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name,ctx,kw", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("name,ctx,kw", CASES, ids=IDS)
 def test_fused_step_appends_and_matches_separate_calls(H, name, ctx, kw):
     """kvq_decode_step on a cache whose last slots were never written: its cache bytes equal the
     oracle's full append, its output passes the gate, and both equal, bit for bit, kvq_append
