@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="override the split-K partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before warmup, run one plain device-to-device copy of this many MiB (a known "
+                         "amount of HBM traffic, used to calibrate memory counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,6 +147,15 @@ def main():
                                        None if c.k_scale is None else c.k_scale.clone(),
                                        None if c.v_scale is None else c.v_scale.clone(), c.kv_scale))
     stream = torch.cuda.current_stream()
+    if args.calibration_copy_mib > 0:
+        nbytes = args.calibration_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {nbytes} bytes read and {nbytes} bytes written")
+        del src, dst
 
     def step(i):
         case.cache = layers[i % len(layers)]
