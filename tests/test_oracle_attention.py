@@ -184,3 +184,20 @@ def test_attention_paging_invariance_and_zero_length(oracle_mod):
         res.append(oracle_mod.decode_attn(cache, q, bt, c))
     np.testing.assert_array_equal(res[0], res[1])
     assert np.all(res[0][0] == 0.0)  # context length 0 gives zeros
+
+
+def test_dense_fp16_attention_matches_torch_sdpa(oracle_mod):
+    """The unquantized reference (used only to report how far quantization moves the output)
+    against torch's float64 scaled_dot_product_attention on the same fp16 rows."""
+    r = np.random.default_rng(21)
+    for n in (1, 2, 17, 300):
+        q = r.standard_normal(128).astype(np.float16)
+        k = r.standard_normal((n, 128)).astype(np.float16)
+        v = r.standard_normal((n, 128)).astype(np.float16)
+        sm = float(np.float32(1.0 / np.sqrt(128.0)))
+        got = oracle_mod.attn_fp16_dense(q, k, v, sm)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q.astype(np.float64))[None, None, :],
+            torch.from_numpy(k.astype(np.float64))[None], torch.from_numpy(v.astype(np.float64))[None],
+            scale=sm)[0, 0]
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
