@@ -161,8 +161,11 @@ __device__ __forceinline__ void load_tile(const KernelParams& a, Tile& t, int bl
     t.vb = ldg16(vt + 1024u + v_off);
     if constexpr (DT == KVQ_INT8) {
         const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 2 * j;
-        t.ks = *reinterpret_cast<const float2*>(a.ks + so);
-        t.vs = *reinterpret_cast<const float2*>(a.vs + so);
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 ks2 = ldg_nt(reinterpret_cast<const f32x2*>(a.ks + so));
+        const f32x2 vs2 = ldg_nt(reinterpret_cast<const f32x2*>(a.vs + so));
+        t.ks = make_float2(ks2.x, ks2.y);
+        t.vs = make_float2(vs2.x, vs2.y);
     }
 }
 
@@ -546,11 +549,11 @@ __global__ __launch_bounds__(64) void attn_partition_mfma(KernelParams a) {
                     kb[i] = ldg16(kt + k_off + 64u);
 #pragma unroll
                     for (int r = 0; r < 8; ++r)
-                        vd[i][r] = *reinterpret_cast<const uint32_t*>(vt + v_off + (uint32_t)r * 256u);
+                        vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
                     if constexpr (DT == KVQ_INT8) {
                         const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
-                        ks4[i] = *reinterpret_cast<const float4_t*>(a.ks + so);
-                        vs4[i] = *reinterpret_cast<const float4_t*>(a.vs + so);
+                        ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+                        vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
                     }
                 } else {
                     ka[i] = kb[i] = u32x4{0u, 0u, 0u, 0u};

@@ -158,8 +158,17 @@ __device__ __forceinline__ float wave_max(float v) {
     return max_across8(v);
 }
 
+// Cache codes are read exactly once per step: load them with the non-temporal (streaming) hint,
+// which keeps them from displacing reusable lines and measurably raises the achieved HBM bandwidth.
 __device__ __forceinline__ u32x4 ldg16(const uint8_t* p) {
-    return *reinterpret_cast<const u32x4*>(p);
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ uint32_t ldg4(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const T* p) {
+    return __builtin_nontemporal_load(p);
 }
 
 }  // namespace kvq
