@@ -1,15 +1,16 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the 8-bit paged KV cache on one MI355X.
 
-A step is one decode step of one attention layer: kvq_append of one new token per sequence, then
-kvq_paged_decode_attn (split-K partition kernel + merge kernel).  Inputs are seeded synthetic
-tensors already resident in HBM.  The timed loop walks over `--layers` copies of the layer's cache
-so consecutive steps read different memory (the 256 MB last-level cache cannot serve a step from
-the previous one).
+A step is one decode step of one attention layer: the append of one new token per sequence and
+paged attention over the whole cache, through kvq_decode_step (append fused into the split-K
+partition kernel, then the merge kernel; `--separate-calls` times kvq_append +
+kvq_paged_decode_attn instead).  Inputs are seeded synthetic tensors already resident in HBM.  The
+timed loop walks over `--layers` copies of the layer's cache so consecutive steps read different
+memory (the 256 MB last-level cache cannot serve a step from the previous one).
 
 Prints one JSON line: achieved HBM GB/s of the whole step (algorithmic bytes / step time), with
 tokens/s, the roofline of the dominant kernel (the attention partition kernel, timed with HIP
-events on its own stream) and the CPU oracle timed on this host as a baseline.
+events on its own stream in a second pass) and the CPU oracle timed on this host as a baseline.
 """
 from __future__ import annotations
 
@@ -114,6 +115,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None, help="override the split-K partition size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time kvq_append + kvq_paged_decode_attn instead of the fused kvq_decode_step")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known "
                          "amount of HBM traffic, used to calibrate memory counters)")
@@ -159,13 +162,13 @@ def main():
 
     def step(i):
         case.cache = layers[i % len(layers)]
-        case.step(stream=stream)
+        case.step(stream=stream, fused=not args.separate_calls)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    kvq.timing_begin(args.steps)
+    # Region 1: the step throughput, with nothing between the launches.
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
@@ -175,9 +178,16 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    main_ms, main_n = kvq.timing_end()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+    # Region 2: the same steps again with a HIP event pair around every partition-kernel launch,
+    # on the stream it is launched on.  The events put gaps between launches, so this region
+    # gives the kernel's own duration and not the step time.
+    kvq.timing_begin(args.steps)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    main_ms, main_n = kvq.timing_end()
     step_bytes = case.algorithmic_bytes()
     attn_bytes = case.attention_bytes()
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
@@ -220,12 +230,15 @@ def main():
             "kv_scale": case.kv_scale,
             "partition_size": w.partition_size,
             "layers_rotated": args.layers,
+            "entry_points": ("kvq_append+kvq_paged_decode_attn" if args.separate_calls
+                             else "kvq_decode_step"),
         },
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
         "kv_tokens_per_s": round(int(case.ctx.sum()) / (ms_step * 1e-3), 1),
         "step_bytes": step_bytes,
         "wall_s_timed_region": round(wall, 4),
+        "kernel_timing": "partition kernel timed with HIP events in a second pass over the same steps",
         "kernels_ms": {"attn_partition_avg": round(main_avg_ms, 5)},
         "roofline": {
             "kernel": f"attn_partition_valu<{w.dtype}>",

@@ -280,26 +280,38 @@ __device__ __forceinline__ void chunk_step(const KernelParams& a, const Tile (&t
     __builtin_amdgcn_wave_barrier();
 }
 
-// Quantize the appended token of sequence b for KV head g in the lane layout of a Tile; the wave
-// designated as writer also stores it into the cache.  Bit-identical to the append kernel.
+// The appended row's fp16 values in the lane layout of a Tile: 16 K dims 16 (lane % 8) .. +15,
+// and V dims lane and 64 + lane.  Loaded when the wave starts, quantized when it reaches the tile.
+struct NewRow {
+    u32x4 k0, k1;
+    uint32_t v0, v1;
+};
+
+__device__ __forceinline__ NewRow load_new_row(const KernelParams& a, int b, int g, int lane) {
+    const size_t row = ((size_t)b * a.Hkv + g) * kDim;
+    NewRow r;
+    r.k0 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7));
+    r.k1 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7) + 8);
+    r.v0 = a.v_new[row + lane];
+    r.v1 = a.v_new[row + 64 + lane];
+    return r;
+}
+
+// Quantize the appended token in the lane layout of a Tile.  Bit-identical to the append kernel.
 template <int DT>
-__device__ __forceinline__ NewToken new_token(const KernelParams& a, int b, int g, int n,
-                                              bool writer, int lane, const int32_t* bt) {
+__device__ __forceinline__ NewToken new_token(const KernelParams& a, const NewRow& raw, int n) {
     NewToken nt;
     nt.tile = (n - 1) / kBlock;
     nt.slot = (n - 1) % kBlock;
-    const size_t row = ((size_t)b * a.Hkv + g) * kDim;
-    const u32x4 kr0 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7));
-    const u32x4 kr1 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7) + 8);
-    const uint32_t kw[8] = {kr0.x, kr0.y, kr0.z, kr0.w, kr1.x, kr1.y, kr1.z, kr1.w};
+    const uint32_t kw[8] = {raw.k0.x, raw.k0.y, raw.k0.z, raw.k0.w, raw.k1.x, raw.k1.y, raw.k1.z, raw.k1.w};
     float kx[16];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         kx[2 * i] = half_bits_to_float(kw[i] & 0xFFFFu);
         kx[2 * i + 1] = half_bits_to_float(kw[i] >> 16);
     }
-    const float vx0 = half_bits_to_float(a.v_new[row + lane]);
-    const float vx1 = half_bits_to_float(a.v_new[row + 64 + lane]);
+    const float vx0 = half_bits_to_float(raw.v0);
+    const float vx1 = half_bits_to_float(raw.v1);
     uint32_t kc[16];
     if constexpr (DT == KVQ_INT8) {
         float km = 0.0f;
@@ -325,23 +337,32 @@ __device__ __forceinline__ NewToken new_token(const KernelParams& a, int b, int 
     nt.k.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
     nt.k.z = kc[8] | (kc[9] << 8) | (kc[10] << 16) | (kc[11] << 24);
     nt.k.w = kc[12] | (kc[13] << 8) | (kc[14] << 16) | (kc[15] << 24);
-    if (writer) {
-        const int blk = bt[nt.tile];
-        const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
-        uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
-        uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
-        if (lane < 8) *reinterpret_cast<u32x4*>(kt + nt.slot * kDim + 16 * lane) = nt.k;
-        vt[(size_t)lane * kBlock + nt.slot] = (uint8_t)nt.v0;
-        vt[(size_t)(64 + lane) * kBlock + nt.slot] = (uint8_t)nt.v1;
-        if constexpr (DT == KVQ_INT8) {
-            if (lane == 0) {
-                const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + nt.slot;
-                const_cast<float*>(a.ks)[so] = nt.ks;
-                const_cast<float*>(a.vs)[so] = nt.vs;
-            }
+    return nt;
+}
+
+// Store the appended token: its K row (128 contiguous codes, written by lanes 0..7) and its V
+// codes.  A V tile row holds one dim's 16 tokens, so the token's V codes are one byte in each of
+// 128 rows; instead of 128 scattered byte stores (partial-line writes), each lane rewrites its two
+// whole 16-byte rows as loaded with the new code patched in -- the other 15 bytes of each row are
+// written back unchanged.  Only valid when this wave is the only reader and writer of the tile
+// (the MHA kernel: one wave per (query head = KV head, partition, sequence)).
+template <int DT>
+__device__ __forceinline__ void store_new_token(const KernelParams& a, const NewToken& nt,
+                                                const Tile& patched, int blk, int g, int lane,
+                                                uint32_t v_off) {
+    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+    uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
+    uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
+    if (lane < 8) __builtin_nontemporal_store(nt.k, reinterpret_cast<u32x4*>(kt + nt.slot * kDim + 16 * lane));
+    __builtin_nontemporal_store(patched.va, reinterpret_cast<u32x4*>(vt + v_off));
+    __builtin_nontemporal_store(patched.vb, reinterpret_cast<u32x4*>(vt + 1024u + v_off));
+    if constexpr (DT == KVQ_INT8) {
+        if (lane == 0) {
+            const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + nt.slot;
+            const_cast<float*>(a.ks)[so] = nt.ks;
+            const_cast<float*>(a.vs)[so] = nt.vs;
         }
     }
-    return nt;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -350,8 +371,8 @@ __device__ __forceinline__ NewToken new_token(const KernelParams& a, int b, int 
 // must carry equal work -- all heads of one (partition, sequence) do, while consecutive partitions
 // of one sequence do not (its last partitions are ragged or empty).
 // APPEND: the decode step's new token (one per sequence, at position context_lens[b] - 1) is
-// quantized here by the waves of the last partition and written to the cache by the wave of the
-// group's first query head.
+// quantized here by the wave of the last partition, patched into its registers and stored.  Used
+// only with one query head per KV head (grouped heads take the append kernel first).
 template <int DT, int TW, bool APPEND>
 __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     __shared__ uint32_t lds[TW * 16];
@@ -380,9 +401,14 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     const int tile_end = (t_end + kBlock - 1) / kBlock;
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
-    NewToken nt{-1, 0, u32x4{0u, 0u, 0u, 0u}, 0u, 0u, 0.0f, 0.0f};
+    // fused append: the new row's loads are issued now, its encode waits for its tile (the last)
+    NewRow raw{u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, 0u, 0u};
+    int tile_new = -1;
     if constexpr (APPEND) {
-        if (p == np - 1) nt = new_token<DT>(a, b, g, n, h % G == 0, lane, bt);
+        if (p == np - 1) {
+            raw = load_new_row(a, b, g, lane);
+            tile_new = (n - 1) / kBlock;
+        }
     }
 
     // q slice of this lane's K dims: 16 (lane % 8) .. +15
@@ -427,7 +453,12 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
             Tile t[1];
             load_tile<DT>(a, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, k_off, v_off, j);
             if constexpr (APPEND) {
-                if (tb + c0 == nt.tile) patch_tile<DT>(t[0], nt, j);
+                if (tb + c0 == tile_new) {
+                    const NewToken nt = new_token<DT>(a, raw, n);
+                    patch_tile<DT>(t[0], nt, j);
+                    store_new_token<DT>(a, nt, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, lane,
+                                        v_off);
+                }
             }
             const int valid = t_end - (tb + c0) * kBlock;
             if (valid < kBlock) zero_tail(t[0], valid);
