@@ -25,7 +25,8 @@
  *                Decode: value = q * s.  Inputs are assumed finite.
  *
  * Memory layout (all device memory, caller-owned, dense, no padding):
- *   K codes  uint8 [num_blocks][num_kv_heads][16 tokens][128 dims]   (token-major tile, 2 KiB)
+ *   K codes  uint8 [num_blocks][num_kv_heads][8][16 tokens][16 dims] (2 KiB tile of eight 256-byte
+ *            chunks: dim d of token t is byte (d / 16) * 256 + t * 16 + d % 16 of the tile)
  *   V codes  uint8 [num_blocks][num_kv_heads][128 dims][16 tokens]   (dim-major tile, 2 KiB)
  *   INT8 scales  float [num_blocks][num_kv_heads][16 tokens], one array for K and one for V
  *   block_tables int32 [batch][max_blocks_per_seq]: logical block i of sequence b is physical block

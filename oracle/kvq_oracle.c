@@ -31,7 +31,8 @@
  *   - The quotient is one correctly rounded fp32 division; the 8-bit rounding is round-to-nearest,
  *     ties to the code with an even mantissa LSB; finite overflow and +-inf saturate to +-max;
  *     NaN encodes as sign | 0x7F; signed zero and subnormals are kept.
- *   - Cache layout (both formats and INT8): K codes [num_blocks][Hkv][16 tokens][128 dims];
+ *   - Cache layout (both formats and INT8): K codes [num_blocks][Hkv][8][16 tokens][16 dims], i.e.
+ *     dim d of token t sits at byte (d / 16) * 256 + t * 16 + d % 16 of its 2048-byte tile;
  *     V codes [num_blocks][Hkv][128 dims][16 tokens]; INT8 scales [num_blocks][Hkv][16 tokens].
  *   - context_lens are post-append lengths; context_lens[b] == 0 gives an all-zero output row.
  *   - Query head h reads KV head h / (Hq / Hkv).
@@ -191,7 +192,9 @@ void kvqo_int8_quantize_row(const uint16_t *x, int n, int8_t *q, float *s_out)
 /* Paged layout offsets (see the header comment).                                               */
 static size_t k_off(int Hkv, int blk, int g, int t, int d)
 {
-    return (((size_t)blk * Hkv + g) * KVQO_BLOCK + t) * KVQO_DIM + d;
+    /* [blk][g][d / 16][t][d % 16]: the tile is eight 256-byte chunks of 16 dims x 16 tokens */
+    size_t tile = ((size_t)blk * Hkv + g) * KVQO_BLOCK * KVQO_DIM;
+    return tile + (size_t)(d / 16) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)(d % 16);
 }
 static size_t v_off(int Hkv, int blk, int g, int t, int d)
 {

@@ -81,9 +81,8 @@ __global__ __launch_bounds__(64) void append_kernel(
         vc0 = encode_fp8<DT>(v0 / kv_scale);
         vc1 = encode_fp8<DT>(v1 / kv_scale);
     }
-    // K tile is token-major [16][128]: the two codes are adjacent
-    *reinterpret_cast<uint16_t*>(kc + tile + (size_t)t * kDim + 2 * lane) =
-        (uint16_t)(kc0 | (kc1 << 8));
+    // K tile is chunked [8][16 tokens][16 dims]: dims 2l and 2l+1 are adjacent in one chunk
+    *reinterpret_cast<uint16_t*>(kc + tile + k_byte(t, 2 * lane)) = (uint16_t)(kc0 | (kc1 << 8));
     // V tile is dim-major [128][16]: the two codes sit 16 bytes apart
     vc[tile + (size_t)(2 * lane) * kBlock + t] = (uint8_t)vc0;
     vc[tile + (size_t)(2 * lane + 1) * kBlock + t] = (uint8_t)vc1;

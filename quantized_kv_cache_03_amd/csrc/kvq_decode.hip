@@ -15,8 +15,9 @@
 //   grid (query head, partition, sequence); a wave streams its partition in chunks of TW tiles of
 //   16 tokens, issuing every K and V load of a chunk before using any, and keeps a running max /
 //   sum / accumulator across chunks.
-//   K tile (token-major 16 x 128 B): lane l holds 16 dims of tokens 2 (l/8) and 2 (l/8) + 1,
-//     dots them with its slice of q (v_dot2_f32_f16), and 8-lane DPP sums finish each logit.
+//   K tile (eight 256-byte chunks of 16 dims x 16 tokens): lane l holds 32 dims of token l/4 --
+//     chunks l%4 and l%4 + 4, one whole 1 KiB half of the tile per load instruction -- dots them
+//     with its slice of q (v_dot2_f32_f16), and two quad DPP sums finish each logit.
 //   V tile (dim-major 128 x 16 B): lane l holds the 16 tokens of dims l and 64 + l, so each lane
 //     accumulates whole output elements; the 16 weights of a tile reach every lane as packed fp16
 //     (hi, lo) pairs through a 64-byte LDS broadcast.
@@ -131,41 +132,31 @@ __device__ __forceinline__ void merge_partials(const KernelParams& a, int b, int
 }
 
 // ------------------------------------------------------------------------------------------------
-// The codes (and INT8 scales) one lane holds for one tile of 16 tokens.
-//   ka / kb : 16 K codes of tokens 2j and 2j+1 (j = lane / 8), dims 16 (lane % 8) .. +15
-//   va / vb : the 16 tokens' V codes of dims lane and 64 + lane
-//   ks / vs : INT8 scales of tokens 2j and 2j+1
+// The codes (and INT8 scales) one lane holds for one tile of 16 tokens.  Lane l is the (token
+// tk = l / 4, chunk c = l % 4) piece of the K tile; the two K loads of a tile each read one whole
+// 1 KiB half of it.
+//   ka / kb : K codes of token tk, dims 16 c .. +15 (chunk c) and 64 + 16 c .. +15 (chunk c + 4)
+//   va / vb : the 16 tokens' V codes of dims l and 64 + l
+//   ks / vs : INT8 scales of token tk
 struct Tile {
     u32x4 ka, kb, va, vb;
-    float2 ks, vs;
-};
-
-// The token a fused decode step appends, quantized by every wave that reads its tile.
-struct NewToken {
-    int tile;    // tile index inside the sequence; -1 when this wave does not read it
-    int slot;    // position inside the tile
-    u32x4 k;     // this lane's 16 K codes (dims 16 (lane % 8) .. +15)
-    uint32_t v0, v1;  // V codes of dims lane and 64 + lane
-    float ks, vs;     // INT8 scales
+    float ks, vs;
 };
 
 template <int DT>
 __device__ __forceinline__ void load_tile(const KernelParams& a, Tile& t, int blk, int g,
-                                          uint32_t k_off, uint32_t v_off, int j) {
+                                          uint32_t k_off, uint32_t v_off, int tk) {
     const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
     const uint8_t* kt = a.kc + tile;
     const uint8_t* vt = a.vc + tile;
     t.ka = ldg16(kt + k_off);
-    t.kb = ldg16(kt + k_off + 128u);
+    t.kb = ldg16(kt + 1024u + k_off);
     t.va = ldg16(vt + v_off);
     t.vb = ldg16(vt + 1024u + v_off);
     if constexpr (DT == KVQ_INT8) {
-        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 2 * j;
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 ks2 = ldg_nt(reinterpret_cast<const f32x2*>(a.ks + so));
-        const f32x2 vs2 = ldg_nt(reinterpret_cast<const f32x2*>(a.vs + so));
-        t.ks = make_float2(ks2.x, ks2.y);
-        t.vs = make_float2(vs2.x, vs2.y);
+        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + tk;
+        t.ks = ldg_nt(a.ks + so);
+        t.vs = ldg_nt(a.vs + so);
     }
 }
 
@@ -181,22 +172,6 @@ __device__ __forceinline__ u32x4 set_byte(u32x4 v, int slot, uint32_t code) {
     return v;
 }
 
-// Replace the new token's slot in the registers of its tile by the freshly computed codes.
-template <int DT>
-__device__ __forceinline__ void patch_tile(Tile& t, const NewToken& nt, int j) {
-    if (j == (nt.slot >> 1)) {
-        if (nt.slot & 1) {
-            t.kb = nt.k;
-            if constexpr (DT == KVQ_INT8) { t.ks.y = nt.ks; t.vs.y = nt.vs; }
-        } else {
-            t.ka = nt.k;
-            if constexpr (DT == KVQ_INT8) { t.ks.x = nt.ks; t.vs.x = nt.vs; }
-        }
-    }
-    t.va = set_byte(t.va, nt.slot, nt.v0);
-    t.vb = set_byte(t.vb, nt.slot, nt.v1);
-}
-
 // Zero the V codes of the slots at and past `valid` (they may hold any code, NaN included, and a
 // zero weight alone would still give 0 * NaN).
 __device__ __forceinline__ void zero_tail(Tile& t, int valid) {
@@ -207,39 +182,31 @@ __device__ __forceinline__ void zero_tail(Tile& t, int valid) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// One chunk of TW tiles of the partition kernel.  Lane l belongs to group j = l / 8; the group holds
-// tokens 2j and 2j+1 of every tile, so after the 8-lane sums it owns the weight pair (w_2j, w_2j+1)
-// -- exactly the pairing of adjacent tokens in a V row.  Group leaders publish their (hi, lo)
-// weight pairs in LDS and every lane reads all eight back with broadcast loads.  MASKED handles a
-// chunk that reaches past the partition end (logits past the end become -inf; the caller has
-// already zeroed the V codes of the partial tile).
+// One chunk of TW tiles of the partition kernel.  Each lane dots its 32 K dims with the matching q
+// slice; the four lanes of a quad (one token) then hold identical logits after two DPP sums.  The
+// odd token of a pair takes its even neighbour's weight with a row shift, and one lane per pair
+// publishes the packed (hi, lo) fp16 pairs in LDS -- the pairing of adjacent tokens in a V row --
+// which every lane reads back with broadcast loads.  MASKED handles a chunk that reaches past the
+// partition end (logits past the end become -inf; the caller has already zeroed the V codes of the
+// partial tile).
 template <int DT, int TW, bool MASKED>
 __device__ __forceinline__ void chunk_step(const KernelParams& a, const Tile (&t)[TW], int tile0,
-                                           int t_end, const half2_t (&qv)[8], int lane,
+                                           int t_end, const half2_t (&qv)[16], int lane,
                                            uint32_t* lds, float& m_run, float& l_lane, float& acc0,
                                            float& acc1) {
-    const int j = lane >> 3;
-    float za[TW], zb[TW];
+    const int tk = lane >> 2;
+    float z[TW];
     float cmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const float sa = sum8(dot16<DT>(t[i].ka, qv));
-        const float sb = sum8(dot16<DT>(t[i].kb, qv));
-        float fa = a.qk_scale, fb = a.qk_scale;
-        if constexpr (DT == KVQ_INT8) {
-            fa *= t[i].ks.x;
-            fb *= t[i].ks.y;
-        }
-        za[i] = sa * fa;
-        zb[i] = sb * fb;
-        if constexpr (MASKED) {
-            const int pos = (tile0 + i) * kBlock + 2 * j;
-            za[i] = (pos < t_end) ? za[i] : kNegInf;
-            zb[i] = (pos + 1 < t_end) ? zb[i] : kNegInf;
-        }
-        cmax = fmaxf(cmax, fmaxf(za[i], zb[i]));
+        const float s = sum4(dot16<DT>(t[i].ka, qv) + dot16<DT>(t[i].kb, qv + 8));
+        float f = a.qk_scale;
+        if constexpr (DT == KVQ_INT8) f *= t[i].ks;
+        z[i] = s * f;
+        if constexpr (MASKED) z[i] = ((tile0 + i) * kBlock + tk < t_end) ? z[i] : kNegInf;
+        cmax = fmaxf(cmax, z[i]);
     }
-    cmax = max_across8(cmax);  // a chunk always holds at least one valid token
+    cmax = max_across_quads(cmax);  // a chunk always holds at least one valid token
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
@@ -249,20 +216,17 @@ __device__ __forceinline__ void chunk_step(const KernelParams& a, const Tile (&t
 
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const float pa = __builtin_amdgcn_exp2f(za[i] - m_new);
-        const float pb = __builtin_amdgcn_exp2f(zb[i] - m_new);
-        l_lane += pa + pb;
-        float wa = pa, wb = pb;
-        if constexpr (DT == KVQ_INT8) {
-            // masked slots may hold NaN scales: keep their weight exactly 0
-            wa = (pa > 0.0f) ? pa * t[i].vs.x : 0.0f;
-            wb = (pb > 0.0f) ? pb * t[i].vs.y : 0.0f;
-        }
-        uint32_t hi, lo;
-        split_f16x2(wa, wb, hi, lo);
-        if ((lane & 7) == 0) {
-            lds[i * 16 + j] = hi;
-            lds[i * 16 + 8 + j] = lo;
+        const float pw = __builtin_amdgcn_exp2f(z[i] - m_new);
+        l_lane += pw;
+        float w = pw;
+        // masked slots may hold NaN scales: keep their weight exactly 0
+        if constexpr (DT == KVQ_INT8) w = (pw > 0.0f) ? pw * t[i].vs : 0.0f;
+        const float w_even = dpp<0x114>(w);  // row_shr:4: the weight of token tk - 1
+        if ((lane & 7) == 4) {               // odd token of pair lane / 8, chunk 0
+            uint32_t hi, lo;
+            split_f16x2(w_even, w, hi, lo);
+            lds[i * 16 + (lane >> 3)] = hi;
+            lds[i * 16 + 8 + (lane >> 3)] = lo;
         }
     }
     __builtin_amdgcn_wave_barrier();
@@ -280,80 +244,93 @@ __device__ __forceinline__ void chunk_step(const KernelParams& a, const Tile (&t
     __builtin_amdgcn_wave_barrier();
 }
 
-// The appended row's fp16 values in the lane layout of a Tile: 16 K dims 16 (lane % 8) .. +15,
-// and V dims lane and 64 + lane.  Loaded when the wave starts, quantized when it reaches the tile.
+// The appended row's fp16 values: K dims 2l and 2l+1 (as the append kernel holds them) and V dims
+// l and 64 + l (as a Tile holds them).  Loaded when the wave starts, quantized at its tile.
 struct NewRow {
-    u32x4 k0, k1;
+    uint32_t k2;
     uint32_t v0, v1;
 };
 
 __device__ __forceinline__ NewRow load_new_row(const KernelParams& a, int b, int g, int lane) {
     const size_t row = ((size_t)b * a.Hkv + g) * kDim;
     NewRow r;
-    r.k0 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7));
-    r.k1 = *reinterpret_cast<const u32x4*>(a.k_new + row + 16 * (lane & 7) + 8);
+    r.k2 = reinterpret_cast<const uint32_t*>(a.k_new + row)[lane];
     r.v0 = a.v_new[row + lane];
     r.v1 = a.v_new[row + 64 + lane];
     return r;
 }
 
-// Quantize the appended token in the lane layout of a Tile.  Bit-identical to the append kernel.
+// The appended token's codes: K in LDS as the token's row of 128 codes (16 bytes per chunk), V in
+// the lane layout of a Tile.  The same per-element arithmetic as the append kernel, bit for bit.
+struct NewToken {
+    int slot;          // position inside the tile
+    uint32_t v0, v1;   // V codes of dims lane and 64 + lane
+    float ks, vs;      // INT8 scales
+};
+
 template <int DT>
-__device__ __forceinline__ NewToken new_token(const KernelParams& a, const NewRow& raw, int n) {
+__device__ __forceinline__ NewToken new_token(const KernelParams& a, const NewRow& raw, int n,
+                                              int lane, uint16_t* lds_k) {
     NewToken nt;
-    nt.tile = (n - 1) / kBlock;
     nt.slot = (n - 1) % kBlock;
-    const uint32_t kw[8] = {raw.k0.x, raw.k0.y, raw.k0.z, raw.k0.w, raw.k1.x, raw.k1.y, raw.k1.z, raw.k1.w};
-    float kx[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        kx[2 * i] = half_bits_to_float(kw[i] & 0xFFFFu);
-        kx[2 * i + 1] = half_bits_to_float(kw[i] >> 16);
-    }
+    const float k0 = half_bits_to_float(raw.k2 & 0xFFFFu), k1 = half_bits_to_float(raw.k2 >> 16);
     const float vx0 = half_bits_to_float(raw.v0);
     const float vx1 = half_bits_to_float(raw.v1);
-    uint32_t kc[16];
+    uint32_t kc0, kc1;
     if constexpr (DT == KVQ_INT8) {
-        float km = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) km = fmaxf(km, fabsf(kx[i]));
-        const float ka = wave_max(km);  // lanes l, l+8, .. hold the same 16 dims: max is unaffected
+        const float ka = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
         const float va = wave_max(fmaxf(fabsf(vx0), fabsf(vx1)));
         nt.ks = ka / 127.0f;
         nt.vs = va / 127.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) kc[i] = encode_int8(kx[i], nt.ks);
+        kc0 = encode_int8(k0, nt.ks);
+        kc1 = encode_int8(k1, nt.ks);
         nt.v0 = encode_int8(vx0, nt.vs);
         nt.v1 = encode_int8(vx1, nt.vs);
     } else {
         const float s = a.kv_scale;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) kc[i] = encode_fp8<DT>(kx[i] / s);
+        kc0 = encode_fp8<DT>(k0 / s);
+        kc1 = encode_fp8<DT>(k1 / s);
         nt.v0 = encode_fp8<DT>(vx0 / s);
         nt.v1 = encode_fp8<DT>(vx1 / s);
         nt.ks = nt.vs = 0.0f;
     }
-    nt.k.x = kc[0] | (kc[1] << 8) | (kc[2] << 16) | (kc[3] << 24);
-    nt.k.y = kc[4] | (kc[5] << 8) | (kc[6] << 16) | (kc[7] << 24);
-    nt.k.z = kc[8] | (kc[9] << 8) | (kc[10] << 16) | (kc[11] << 24);
-    nt.k.w = kc[12] | (kc[13] << 8) | (kc[14] << 16) | (kc[15] << 24);
+    lds_k[lane] = (uint16_t)(kc0 | (kc1 << 8));  // codes of dims 2 lane, 2 lane + 1
+    __builtin_amdgcn_wave_barrier();
     return nt;
 }
 
-// Store the appended token: its K row (128 contiguous codes, written by lanes 0..7) and its V
-// codes.  A V tile row holds one dim's 16 tokens, so the token's V codes are one byte in each of
-// 128 rows; instead of 128 scattered byte stores (partial-line writes), each lane rewrites its two
-// whole 16-byte rows as loaded with the new code patched in -- the other 15 bytes of each row are
-// written back unchanged.  Only valid when this wave is the only reader and writer of the tile
-// (the MHA kernel: one wave per (query head = KV head, partition, sequence)).
+// Replace the new token's slot in the registers of its tile by the freshly computed codes.
+template <int DT>
+__device__ __forceinline__ void patch_tile(Tile& t, const NewToken& nt, const uint16_t* lds_k,
+                                           int lane) {
+    if ((lane >> 2) == nt.slot) {
+        const u32x4* rowk = reinterpret_cast<const u32x4*>(lds_k);
+        t.ka = rowk[lane & 3];
+        t.kb = rowk[4 + (lane & 3)];
+        if constexpr (DT == KVQ_INT8) { t.ks = nt.ks; t.vs = nt.vs; }
+    }
+    t.va = set_byte(t.va, nt.slot, nt.v0);
+    t.vb = set_byte(t.vb, nt.slot, nt.v1);
+}
+
+// Store the appended token: its K codes (16 bytes in each of the eight chunks, from LDS, written
+// by lanes 0..7) and its V codes.  A V tile row holds one dim's 16 tokens, so the token's V codes
+// are one byte in each of 128 rows; instead of 128 scattered byte stores (partial-line writes),
+// each lane rewrites its two whole 16-byte rows as loaded with the new code patched in -- the
+// other 15 bytes of each row are written back unchanged.  Only valid when this wave is the only
+// reader and writer of the tile (the MHA kernel: one wave per (query head = KV head, partition,
+// sequence)).
 template <int DT>
 __device__ __forceinline__ void store_new_token(const KernelParams& a, const NewToken& nt,
-                                                const Tile& patched, int blk, int g, int lane,
-                                                uint32_t v_off) {
+                                                const Tile& patched, const uint16_t* lds_k, int blk,
+                                                int g, int lane, uint32_t v_off) {
     const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
     uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
     uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
-    if (lane < 8) __builtin_nontemporal_store(nt.k, reinterpret_cast<u32x4*>(kt + nt.slot * kDim + 16 * lane));
+    if (lane < 8) {
+        const u32x4 kchunk = reinterpret_cast<const u32x4*>(lds_k)[lane];
+        __builtin_nontemporal_store(kchunk, reinterpret_cast<u32x4*>(kt + k_byte(nt.slot, kChunk * lane)));
+    }
     __builtin_nontemporal_store(patched.va, reinterpret_cast<u32x4*>(vt + v_off));
     __builtin_nontemporal_store(patched.vb, reinterpret_cast<u32x4*>(vt + 1024u + v_off));
     if constexpr (DT == KVQ_INT8) {
@@ -374,15 +351,17 @@ __device__ __forceinline__ void store_new_token(const KernelParams& a, const New
 // quantized here by the wave of the last partition, patched into its registers and stored.  Used
 // only with one query head per KV head (grouped heads take the append kernel first).
 template <int DT, int TW, bool APPEND>
-__global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((DT == KVQ_INT8 && APPEND) ? 4 : 5, 8))) void attn_partition_valu(
+    KernelParams a) {
     __shared__ uint32_t lds[TW * 16];
+    __shared__ u32x4 lds_knew[APPEND ? 8 : 1];
     const int h = blockIdx.x;
     const int p = blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
     const int G = a.Hq / a.Hkv;
     const int g = h / G;
-    const int j = lane >> 3;
+    const int tk = lane >> 2;
 
     const int n = a.ctx[b];
     const int np = (n + a.PS - 1) / a.PS;  // partitions this sequence uses
@@ -402,7 +381,7 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
     // fused append: the new row's loads are issued now, its encode waits for its tile (the last)
-    NewRow raw{u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, 0u, 0u};
+    NewRow raw{0u, 0u, 0u};
     int tile_new = -1;
     if constexpr (APPEND) {
         if (p == np - 1) {
@@ -411,21 +390,22 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
         }
     }
 
-    // q slice of this lane's K dims: 16 (lane % 8) .. +15
-    half2_t qv[8];
+    // q slice of this lane's K dims: 16 c .. +15 and 64 + 16 c .. +15 (c = lane % 4)
+    half2_t qv[16];
     {
-        const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + orow + (lane & 7) * 16);
-        const u32x4 q0 = qp[0], q1 = qp[1];
-        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + orow + (lane & 3) * kChunk);
+        const u32x4 q0 = qp[0], q1 = qp[1], q2 = qp[8], q3 = qp[9];
+        const uint32_t qw[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                                 q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qv[i] = __builtin_bit_cast(half2_t, qw[i]);
+        for (int i = 0; i < 16; ++i) qv[i] = __builtin_bit_cast(half2_t, qw[i]);
     }
 
-    const uint32_t k_off = 256u * ((uint32_t)lane >> 3) + 16u * ((uint32_t)lane & 7u);  // token 2 (lane/8)
+    const uint32_t k_off = (uint32_t)kChunkBytes * ((uint32_t)lane & 3u) + (uint32_t)kChunk * (uint32_t)tk;
     const uint32_t v_off = 16u * (uint32_t)lane;
 
     float m_run = kNegInf;  // running max of the base-2 logits (wave-uniform)
-    float l_lane = 0.0f;    // running sum of the weights of this lane's group
+    float l_lane = 0.0f;    // running sum of the weights of this lane's token
     float acc0 = 0.0f, acc1 = 0.0f;  // unnormalized output, dims lane and 64 + lane
 
     for (int tb = tile_begin; tb < tile_end; tb += 64) {
@@ -444,20 +424,21 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
 #pragma unroll
             for (int i = 0; i < TW; ++i)
                 load_tile<DT>(a, t[i], __builtin_amdgcn_readlane(blk_lane, c * TW + i), g, k_off,
-                              v_off, j);
+                              v_off, tk);
             chunk_step<DT, TW, false>(a, t, tb + c * TW, t_end, qv, lane, lds, m_run, l_lane, acc0,
                                       acc1);
         }
         // the rest one tile at a time: the last one possibly partial, or holding the new token
         for (int c0 = nfull * TW; c0 < nt_grp; ++c0) {
             Tile t[1];
-            load_tile<DT>(a, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, k_off, v_off, j);
+            load_tile<DT>(a, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, k_off, v_off, tk);
             if constexpr (APPEND) {
                 if (tb + c0 == tile_new) {
-                    const NewToken nt = new_token<DT>(a, raw, n);
-                    patch_tile<DT>(t[0], nt, j);
-                    store_new_token<DT>(a, nt, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, lane,
-                                        v_off);
+                    uint16_t* lds_k = reinterpret_cast<uint16_t*>(lds_knew);
+                    const NewToken nt = new_token<DT>(a, raw, n, lane, lds_k);
+                    patch_tile<DT>(t[0], nt, lds_k, lane);
+                    store_new_token<DT>(a, nt, t[0], lds_k, __builtin_amdgcn_readlane(blk_lane, c0),
+                                        g, lane, v_off);
                 }
             }
             const int valid = t_end - (tb + c0) * kBlock;
@@ -465,11 +446,8 @@ __global__ __launch_bounds__(64) void attn_partition_valu(KernelParams a) {
             chunk_step<DT, 1, true>(a, t, tb + c0, t_end, qv, lane, lds, m_run, l_lane, acc0, acc1);
         }
     }
-    // each token's weight was added by all 8 lanes of its group: count group leaders only
-    // (lanes 0, 8, .., 56 end with the total; broadcast it from lane 0)
-    const float l_lead = sum_across8((lane & 7) == 0 ? l_lane : 0.0f);
-    const float l_sum =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l_lead), 0));
+    // each token's weight was added by the four lanes of its quad: count one lane per quad
+    const float l_sum = wave_sum((lane & 3) == 0 ? l_lane : 0.0f);
 
     if (np == 1) {
         const float inv = a.v_scale / l_sum;
@@ -512,7 +490,8 @@ __device__ __forceinline__ half8_v codes8(uint32_t w0, uint32_t w1) {
 }
 
 template <int DT, int TW>
-__global__ __launch_bounds__(64) void attn_partition_mfma(KernelParams a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void attn_partition_mfma(
+    KernelParams a) {
     static_assert(TW % 2 == 0, "tiles are paired for the PV products");
     const int g = blockIdx.x;
     const int p = blockIdx.y;
@@ -559,7 +538,7 @@ __global__ __launch_bounds__(64) void attn_partition_mfma(KernelParams a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const uint32_t k_off = (uint32_t)col * kDim + 16u * (uint32_t)q4;  // token col, dims 16 q4 (+64)
+    const uint32_t k_off = 16u * (uint32_t)lane;  // chunk q4 (+4): token col, dims 16 q4 (+64)
     const uint32_t v_off = (uint32_t)col * kBlock + 4u * (uint32_t)q4;  // dim col (+16 r), tokens 4 q4
 
     for (int tb = tile_begin; tb < tile_end; tb += 64) {
@@ -577,7 +556,7 @@ __global__ __launch_bounds__(64) void attn_partition_mfma(KernelParams a) {
                     const uint8_t* kt = a.kc + tile;
                     const uint8_t* vt = a.vc + tile;
                     ka[i] = ldg16(kt + k_off);
-                    kb[i] = ldg16(kt + k_off + 64u);
+                    kb[i] = ldg16(kt + k_off + 1024u);
 #pragma unroll
                     for (int r = 0; r < 8; ++r)
                         vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);

@@ -28,14 +28,14 @@ __global__ __launch_bounds__(64) void dequant_kernel(
     const size_t sbase = ((size_t)blk * Hkv + g) * kBlock;
     const size_t obase = ((size_t)b * Hkv + g) * (size_t)max_ctx * kDim;
 
-    // K: token-major tile; lane l reads 16 codes of token (l / 8) (+8 in the second half), dims
-    // 16 (l % 8) .. +15.
+    // K: chunked tile; in each 1 KiB half lane l reads the 16 codes of token l % 16 in chunk
+    // 4 half + l / 16 (dims 16 (4 half + l / 16) .. +15).
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-        const int tok = half * 8 + (lane >> 3);
+        const int tok = lane & 15;
         const int pos = tile_idx * kBlock + tok;
-        const int d0 = (lane & 7) * 16;
-        const u32x4 w = ldg16(kc + tile + (size_t)tok * kDim + d0);
+        const int d0 = (half * 4 + (lane >> 4)) * kChunk;
+        const u32x4 w = ldg16(kc + tile + k_byte(tok, d0));
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
         const float s = (DT == KVQ_INT8) ? ks[sbase + tok] : kv_scale;
         if (pos < n) {

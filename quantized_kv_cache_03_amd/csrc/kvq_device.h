@@ -22,6 +22,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 codes, byte i
 constexpr int kDim = KVQ_HEAD_DIM;     // 128
 constexpr int kBlock = KVQ_BLOCK_SIZE; // 16
 constexpr int kTileBytes = kDim * kBlock;  // 2048 bytes per (block, KV head) tile
+// K tile: eight 256-byte chunks, chunk c holding dims 16c .. 16c+15 of the 16 tokens (16 B per
+// token).  Any 1 KiB half of the tile is four whole chunks, so a wave's 16-byte-per-lane load of
+// one half reads whole 128-byte lines whatever lane owns which (chunk, token) piece.
+constexpr int kChunk = 16;
+constexpr int kChunkBytes = kChunk * kBlock;  // 256
+__device__ __forceinline__ uint32_t k_byte(int t, int d) {
+    return (uint32_t)(d / kChunk) * kChunkBytes + (uint32_t)t * kChunk + (uint32_t)(d % kChunk);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------------------------------------
@@ -124,11 +132,19 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                                                  0xF, 0xF, true));
 }
-// sum over each aligned group of 8 lanes: xor 1, xor 2 (quad permutes), then the mirrored half-row
-__device__ __forceinline__ float sum8(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
+// sum over each quad (xor 1, then xor 2).  Floating-point addition is commutative, so the four
+// lanes of a quad end with bitwise the same sum.
+__device__ __forceinline__ float sum4(float v) {
+    v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+    return v;
+}
+// max over the 16 quads (the four quads of a 16-lane row by rotation, then across rows)
+__device__ __forceinline__ float max_across_quads(float v) {
+    v = fmaxf(v, dpp<0x124>(v));  // row_ror:4
+    v = fmaxf(v, dpp<0x128>(v));  // row_ror:8
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
     return v;
 }
 // reductions across the eight groups of 8 lanes (lanes l, l^8, l^16, ..., l^56)

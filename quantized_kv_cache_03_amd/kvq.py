@@ -109,7 +109,7 @@ def dtype_from_string(name: str) -> int:
 class PagedKVCache:
     """Device tensors of one layer's paged cache (layouts as in kvq.h)."""
     dtype: int
-    k_cache: torch.Tensor           # uint8 [num_blocks][Hkv][16][128]
+    k_cache: torch.Tensor           # uint8 [num_blocks][Hkv][8][16][16]: 16-dim chunks x 16 tokens
     v_cache: torch.Tensor           # uint8 [num_blocks][Hkv][128][16]
     k_scale: torch.Tensor | None    # float32 [num_blocks][Hkv][16] (INT8)
     v_scale: torch.Tensor | None
@@ -129,7 +129,8 @@ class PagedKVCache:
         if isinstance(dtype, str):
             dtype = dtype_from_string(dtype)
         fill = 0x7F if poison else 0
-        k = torch.full((num_blocks, num_kv_heads, BLOCK_SIZE, HEAD_DIM), fill, dtype=torch.uint8, device=device)
+        k = torch.full((num_blocks, num_kv_heads, HEAD_DIM // 16, BLOCK_SIZE, 16), fill, dtype=torch.uint8,
+                       device=device)
         v = torch.full((num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE), fill, dtype=torch.uint8, device=device)
         ks = vs = None
         if dtype == INT8:

@@ -46,8 +46,8 @@ def test_dequant_every_code(K, dtype):
     ek, ev = oracle.dequant(oc, bt, ctx, L)
 
     dc = K.PagedKVCache.allocate(dtype, nb, Hkv, scale)
-    dc.k_cache.copy_(torch.from_numpy(kcodes).view(nb, Hkv, 16, 128))
-    dc.v_cache.copy_(torch.from_numpy(vcodes).view(nb, Hkv, 128, 16))
+    dc.k_cache.copy_(torch.from_numpy(kcodes).view(dc.k_cache.shape))
+    dc.v_cache.copy_(torch.from_numpy(vcodes).view(dc.v_cache.shape))
     if ks is not None:
         dc.k_scale.copy_(torch.from_numpy(ks))
         dc.v_scale.copy_(torch.from_numpy(vs))

@@ -19,6 +19,12 @@ TORCH_DT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
 DT_NAME = {E4M3: "fp8_e4m3", E5M2: "fp8_e5m2", INT8: "int8"}
 
 
+def k_token_rows(k, num_blocks, Hkv):
+    """K codes as [block][head][token][dim] from the chunked tile layout: 8 chunks of 16 dims, each
+    chunk 16 tokens x 16 bytes (dim d of token t at byte (d // 16) * 256 + t * 16 + d % 16)."""
+    return k.reshape(num_blocks, Hkv, 8, 16, 16).transpose(0, 1, 3, 2, 4).reshape(num_blocks, Hkv, 16, 128)
+
+
 def _setup(oracle_mod, dtype, ctx, Hq=4, Hkv=2, table="sequential", scale_rule="amax/448",
            seed=11, outliers=0):
     w = W.Workload("pin", seed, len(ctx), Hq, Hkv, DT_NAME[dtype], ("list", list(ctx)), table=table,
@@ -56,7 +62,7 @@ def test_append_layout_and_poison(oracle_mod, dtype):
         for p in range(n):
             blk = bt[b, p // 16]
             used.add((blk, p % 16))
-    kc = cache.k.reshape(cache.num_blocks, cache.Hkv, 16, 128)
+    kc = k_token_rows(cache.k, cache.num_blocks, cache.Hkv)
     vc = cache.v.reshape(cache.num_blocks, cache.Hkv, 128, 16)
     for blk in range(cache.num_blocks):
         for t in range(16):
@@ -91,7 +97,7 @@ def test_append_one_token_per_sequence(oracle_mod):
     cache = oracle_mod.Cache(E4M3, nb, 2, 1.0)
     rows = np.random.default_rng(0).standard_normal((3, 2, 128)).astype(np.float16)
     oracle_mod.append(cache, rows, rows, bt, ctx)
-    kc = cache.k.reshape(nb, 2, 16, 128)
+    kc = k_token_rows(cache.k, nb, 2)
     written = np.argwhere(np.any(kc != 0x7F, axis=(1, 3)))
     expect = sorted((int(bt[b, (n - 1) // 16]), int((n - 1) % 16)) for b, n in enumerate(ctx))
     assert sorted(map(tuple, written.tolist())) == expect

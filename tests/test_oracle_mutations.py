@@ -55,6 +55,9 @@ MUTATIONS = {
     "attn-denominator": (
         "        out[d] /= denom;\n    free(z);\n    return 0;\n}\n\n/* The same attention",
         "        out[d] /= (denom + 1.0);\n    free(z);\n    return 0;\n}\n\n/* The same attention"),
+    "k-layout-token-major": (
+        "return tile + (size_t)(d / 16) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)(d % 16);",
+        "return tile + (size_t)t * KVQO_DIM + (size_t)d;"),
     "v-layout-token-major": (
         "return (((size_t)blk * Hkv + g) * KVQO_DIM + d) * KVQO_BLOCK + t;",
         "return (((size_t)blk * Hkv + g) * KVQO_BLOCK + t) * KVQO_DIM + d;"),
