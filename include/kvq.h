@@ -104,9 +104,12 @@ int kvq_append(const kvq_cache *cache, const void *k_new, const void *v_new,
                int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t batch,
                void *stream);
 
-/* Bytes of split-K workspace kvq_paged_decode_attn needs for these sizes (0 when one pass
- * suffices).  partition_size 0 means a single pass over each whole context. */
-size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+/* partition_size value selecting the balanced split (see kvq_paged_decode_attn). */
+#define KVQ_PARTITION_BALANCED (-1)
+
+/* Bytes of split-K workspace kvq_paged_decode_attn needs for these sizes and partition_size
+ * (0 when none is needed; also 0 for arguments the attention call would reject). */
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size);
 
 /* Decode-step attention over the paged 8-bit cache (the opening section of "Accelerating
@@ -115,10 +118,16 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t hea
  *   with k^, v^ the dequantized rows of KV head h / (Hq / Hkv).  context_lens[b] == 0 gives zeros.
  *   sm_scale       : finite; 1/sqrt(128) is the usual value.
  *   max_context_len: host-side upper bound of context_lens (sizes the grid without a device read).
- *   partition_size : 0 for one pass per sequence, else a multiple of 16 (flash-decoding split-K:
- *                    each partition writes fp32 (max, sum, unnormalized output) partials into
- *                    `workspace`, and a second kernel merges them).  For a fixed partition size the
- *                    result is bitwise deterministic.
+ *   partition_size : how the work is split (flash-decoding split-K: each piece writes fp32 (max,
+ *                    sum, unnormalized output) partials into `workspace`, and a second kernel merges
+ *                    them with the log-sum-exp rule):
+ *                      0                      one pass per sequence, no workspace;
+ *                      a positive multiple of 16: fixed partitions of that many tokens;
+ *                      KVQ_PARTITION_BALANCED the tiles of all sequences, laid end to end, are cut
+ *                                             into equal shares, about 2048 waves in all, whatever
+ *                                             the mix of context lengths (a share may hold the end
+ *                                             of one sequence and the start of the next).
+ *                    For given arguments the result is bitwise deterministic.
  *   workspace      : device memory of at least kvq_decode_workspace_size(...) bytes (may be NULL
  *                    when that size is 0); its contents need no initialization. */
 int kvq_paged_decode_attn(const kvq_cache *cache, const void *q, void *out, int32_t num_q_heads,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "kvq.h"
@@ -63,26 +64,53 @@ int check_common(const int32_t* block_tables, int32_t max_blocks_per_seq, const 
     return KVQ_OK;
 }
 
-// Split-K plan: partitions in the grid and tokens per partition.
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Work split of the decode attention.  Fixed partitions: P partitions of PS tokens (P == 1: one
+// pass, no workspace).  Balanced split: NW waves per head row (query heads for MHA, KV heads for
+// grouped heads), about kBalancedWaves waves in all -- two per SIMD of the 1024 on the chip, enough
+// to keep HBM busy while each wave streams a long, equal share.  A wave gets at least kMinTiles
+// tiles (the device caps the waves it uses by the same rule on the actual tile count).
+constexpr int64_t kBalancedWaves = 2048;
+constexpr int64_t kMinTiles = 8;
+
 struct Plan {
-    int32_t P;
-    int32_t PS;
+    int32_t P = 1;
+    int32_t PS = KVQ_BLOCK_SIZE;
+    int32_t NW = 0;          // balanced split: waves per head row (0 for fixed partitions)
+    size_t rows = 0;         // partial rows in the workspace
+    size_t plan_bytes = 0;   // balanced split: int32 [batch + 2]
 };
 
-Plan plan(int32_t max_context_len, int32_t partition_size) {
+Plan plan(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_context_len, int32_t partition_size) {
     Plan p;
-    if (partition_size <= 0) {
+    if (partition_size == KVQ_PARTITION_BALANCED) {
+        const int64_t hw = Hq == Hkv ? Hq : Hkv;
+        const int64_t max_tiles = (int64_t)batch * ((max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE);
+        int64_t nw = (kBalancedWaves + hw - 1) / hw;
+        nw = std::min(nw, std::max<int64_t>(1, (max_tiles + kMinTiles - 1) / kMinTiles));
+        nw = std::min<int64_t>(nw, 65535);
+        p.NW = (int32_t)nw;
+        p.rows = (size_t)Hq * (size_t)(nw + batch);
+        p.plan_bytes = (size_t)(batch + 2) * sizeof(int32_t);
+    } else if (partition_size == 0) {
         const int32_t whole = ((max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE) * KVQ_BLOCK_SIZE;
         p.PS = whole > 0 ? whole : KVQ_BLOCK_SIZE;
-        p.P = 1;
     } else {
         p.PS = partition_size;
         p.P = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+        if (p.P > 1) p.rows = (size_t)batch * (size_t)Hq * (size_t)p.P;
     }
     return p;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Workspace layout: [plan][part_o rows x 128 f32][part_m rows f32][part_l rows f32], each 256-byte
+// aligned.
+size_t plan_workspace_bytes(const Plan& p) {
+    if (p.rows == 0 && p.plan_bytes == 0) return 0;
+    return align256(p.plan_bytes) + align256(p.rows * KVQ_HEAD_DIM * sizeof(float)) +
+           2 * align256(p.rows * sizeof(float));
+}
 
 // kernel-timing hook state
 struct Timing {
@@ -153,13 +181,14 @@ int kvq_append(const kvq_cache* cache, const void* k_new, const void* v_new,
     return ok();
 }
 
-size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size) {
-    if (batch <= 0 || num_q_heads <= 0 || head_dim != KVQ_HEAD_DIM || max_context_len < 0) return 0;
-    const Plan p = plan(max_context_len, partition_size);
-    if (p.P <= 1) return 0;
-    const size_t rows = (size_t)batch * (size_t)num_q_heads * (size_t)p.P;
-    return align256(rows * KVQ_HEAD_DIM * sizeof(float)) + 2 * align256(rows * sizeof(float));
+    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        max_context_len < 0)
+        return 0;
+    if (partition_size != KVQ_PARTITION_BALANCED && (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE))
+        return 0;
+    return plan_workspace_bytes(plan(batch, num_q_heads, num_kv_heads, max_context_len, partition_size));
 }
 
 }  // extern "C"
@@ -184,8 +213,10 @@ int decode_common(const char* where, const kvq_cache* cache, const void* k_new, 
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
     if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
-    if (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0)
-        return fail(KVQ_ERR_ARG, "partition_size %d must be 0 or a positive multiple of %d",
+    if (partition_size != KVQ_PARTITION_BALANCED &&
+        (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0))
+        return fail(KVQ_ERR_ARG,
+                    "partition_size %d must be KVQ_PARTITION_BALANCED (-1), 0 or a positive multiple of %d",
                     partition_size, KVQ_BLOCK_SIZE);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
         return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",
@@ -196,10 +227,9 @@ int decode_common(const char* where, const kvq_cache* cache, const void* k_new, 
     if (batch > 65535 || num_q_heads > 65535)
         return fail(KVQ_ERR_SHAPE, "batch and num_q_heads must be at most 65535");
 
-    const Plan p = plan(max_context_len, partition_size);
+    const Plan p = plan(batch, num_q_heads, cache->num_kv_heads, max_context_len, partition_size);
     if (p.P > 65535) return fail(KVQ_ERR_SHAPE, "%d partitions exceed the grid limit 65535", p.P);
-    const size_t need = kvq_decode_workspace_size(batch, num_q_heads, KVQ_HEAD_DIM, max_context_len,
-                                                  partition_size);
+    const size_t need = plan_workspace_bytes(p);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVQ_ERR_WORKSPACE, "split-K workspace of %zu bytes needed, %zu given%s", need,
                     workspace_bytes, workspace ? "" : " (NULL)");
@@ -216,16 +246,20 @@ int decode_common(const char* where, const kvq_cache* cache, const void* k_new, 
     a.batch = batch;
     a.num_partitions = p.P;
     a.partition_size = p.PS;
+    a.balanced_waves = p.NW;
+    a.plan = nullptr;
     a.part_o = a.part_m = a.part_l = nullptr;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
     if (need > 0) {
-        const size_t rows = (size_t)batch * (size_t)num_q_heads * (size_t)p.P;
         char* w = static_cast<char*>(workspace);
+        if (p.plan_bytes) a.plan = reinterpret_cast<int32_t*>(w);
+        w += align256(p.plan_bytes);
         a.part_o = reinterpret_cast<float*>(w);
-        a.part_m = reinterpret_cast<float*>(w + align256(rows * KVQ_HEAD_DIM * sizeof(float)));
-        a.part_l = reinterpret_cast<float*>(w + align256(rows * KVQ_HEAD_DIM * sizeof(float)) +
-                                            align256(rows * sizeof(float)));
+        w += align256(p.rows * KVQ_HEAD_DIM * sizeof(float));
+        a.part_m = reinterpret_cast<float*>(w);
+        w += align256(p.rows * sizeof(float));
+        a.part_l = reinterpret_cast<float*>(w);
     }
 
     hipEvent_t ev[2] = {nullptr, nullptr};

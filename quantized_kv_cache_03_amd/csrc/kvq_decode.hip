@@ -83,16 +83,20 @@ struct KernelParams {
     const float* vs;
     const uint16_t* q;
     uint16_t* out;
-    float* part_o;
-    float* part_m;
-    float* part_l;
+    float* part_o;      // partial rows [R][128]: unnormalized outputs
+    float* part_m;      // [R] running max (base-2 logits)
+    float* part_l;      // [R] sum of weights
+    int32_t* plan;      // balanced split: [B + 2] = tiles before each sequence, total tiles, waves used
     const int32_t* block_tables;
     const int32_t* ctx;
     int32_t max_blocks;
+    int32_t B;
     int32_t Hq;
     int32_t Hkv;
-    int32_t P;          // partitions in the grid
-    int32_t PS;         // tokens per partition
+    int32_t P;          // fixed partitions: partitions in the grid; partial row (b Hq + h) P + p
+    int32_t PS;         // fixed partitions: tokens per partition
+    int32_t NW;         // balanced split: waves per head row in the grid (0 for fixed partitions)
+    int32_t S;          // balanced split: partial rows per query head (NW + B); row h S + w + b
     float qk_scale;     // sm_scale * log2(e) (* kv_scale for FP8)
     float v_scale;      // kv_scale for FP8, 1 for INT8
     float kv_scale;     // per-tensor scale of the FP8 encoder (fused append)
@@ -100,35 +104,109 @@ struct KernelParams {
     const uint16_t* v_new;
 };
 
+__device__ __forceinline__ int tiles_of(int n) { return n > 0 ? (n + kBlock - 1) / kBlock : 0; }
+
 // ------------------------------------------------------------------------------------------------
-// Merge of the np partials of one (sequence, query head), by one wave:
+// Balanced split.  Per head row, the tiles of all sequences are laid end to end (T in total) and
+// wave w of the row takes tiles [floor(w T / nw), floor((w + 1) T / nw)): every wave streams the
+// same amount whatever the mix of context lengths, and a wave's share may hold the end of one
+// sequence and the start of the next.  Each piece of one sequence ("segment") yields one partial,
+// or the final output when the wave holds the whole sequence.  nw <= NW caps the waves so each
+// gets at least kMinTiles tiles.
+constexpr int kMinTiles = 8;
+
+__device__ __forceinline__ int balanced_waves(int T, int NW) {
+    return T == 0 ? 1 : min(NW, (T + kMinTiles - 1) / kMinTiles);
+}
+// the wave whose share holds flattened tile c
+__device__ __forceinline__ int wave_of_tile(int c, int T, int nw) {
+    return (int)(((int64_t)(c + 1) * nw + T - 1) / T) - 1;
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+__device__ __forceinline__ int readlane_i(int v, int i) { return __builtin_amdgcn_readlane(v, i); }
+
+// Calls seg(b, n, nt, lo, hi) for each segment (tiles [lo, hi) of sequence b, which has n tokens
+// in nt tiles) of wave w's share, in sequence order.  The writer wave also stores the plan that
+// the merge kernel reads.
+template <typename F>
+__device__ __forceinline__ void for_each_segment(const KernelParams& a, int w, bool writer, int lane,
+                                                 F&& seg) {
+    int T = 0;
+    for (int base = 0; base < a.B; base += 64) {
+        const int idx = base + lane;
+        const int nt = tiles_of(idx < a.B ? a.ctx[idx] : 0);
+        const int incl = wave_incl_scan(nt, lane);
+        if (writer && idx < a.B) a.plan[idx] = T + incl - nt;
+        T += readlane_i(incl, 63);
+    }
+    const int nw = balanced_waves(T, a.NW);
+    if (writer && lane == 0) {
+        a.plan[a.B] = T;
+        a.plan[a.B + 1] = nw;
+    }
+    if (w >= nw) return;
+    const int s1 = (int)((int64_t)(w + 1) * T / nw);
+    int cur = (int)((int64_t)w * T / nw);
+    int running = 0;  // tiles before the current 64-sequence chunk
+    for (int base = 0; base < a.B && cur < s1; base += 64) {
+        const int idx = base + lane;
+        // only the inclusive prefix stays in a register across the segments
+        const int incl = running + wave_incl_scan(tiles_of(idx < a.B ? a.ctx[idx] : 0), lane);
+        const int chunk_end = readlane_i(incl, 63);
+        while (cur < s1 && cur < chunk_end) {
+            // the first sequence of the chunk whose tiles reach past cur (it has tiles)
+            const int b = base + (int)__builtin_ctzll(__ballot(incl > cur));
+            const int n = a.ctx[b];
+            const int ntb = tiles_of(n);
+            const int c0 = readlane_i(incl, b - base) - ntb;
+            const int hi = min(ntb, s1 - c0);
+            seg(b, n, ntb, cur - c0, hi);
+            cur = c0 + hi;
+        }
+        running = chunk_end;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Merge of the np partials in rows r0 .. r0 + np - 1 of one (sequence, query head), by one wave:
 //   M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// Partials are read in partition order, so the result is bitwise deterministic.
-__device__ __forceinline__ void merge_partials(const KernelParams& a, int b, int h, int np, int lane) {
-    const size_t prow0 = ((size_t)b * a.Hq + h) * a.P;
-    // the statistics of up to 64 partitions at a time, one per lane
+// Lane l sums dims 4 (l % 32) .. +3 over the partials of parity l / 32 (two partial rows per load
+// instruction, four loads in flight), and the two halves are added at the end.  The order of the
+// sums is fixed, so the result is bitwise deterministic.
+__device__ __forceinline__ void merge_rows(const KernelParams& a, int64_t r0, int np, size_t orow,
+                                           int lane) {
     float M = kNegInf;
     for (int p0 = 0; p0 < np; p0 += 64)
-        M = fmaxf(M, (p0 + lane < np) ? a.part_m[prow0 + p0 + lane] : kNegInf);
+        M = fmaxf(M, (p0 + lane < np) ? a.part_m[r0 + p0 + lane] : kNegInf);
     M = wave_max(M);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int p0 = 0; p0 < np; p0 += 64) {
-        const int cnt = min(64, np - p0);
-        const float w_lane = (lane < cnt) ? __builtin_amdgcn_exp2f(a.part_m[prow0 + p0 + lane] - M) : 0.0f;
-        const float wl_lane = (lane < cnt) ? w_lane * a.part_l[prow0 + p0 + lane] : 0.0f;
-        L += wave_sum(wl_lane);
-        for (int i = 0; i < cnt; ++i) {
-            const float w = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), i));
-            const float2 op = reinterpret_cast<const float2*>(a.part_o + (prow0 + p0 + i) * kDim)[lane];
-            o0 += w * op.x;
-            o1 += w * op.y;
-        }
+    const int d4 = (lane & 31) * 4;
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float L = 0.0f;
+#pragma unroll 4
+    for (int p = lane >> 5; p < np; p += 2) {
+        const float w = __builtin_amdgcn_exp2f(a.part_m[r0 + p] - M);
+        L += w * a.part_l[r0 + p];
+        const float4_t o = *reinterpret_cast<const float4_t*>(a.part_o + (r0 + p) * kDim + d4);
+        acc += w * o;
     }
-    const float inv = a.v_scale / L;
-    const size_t orow = ((size_t)b * a.Hq + h) * kDim;
-    half2_t r = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
-    reinterpret_cast<half2_t*>(a.out + orow)[lane] = r;
+    L += __shfl_xor(L, 32);
+    acc.x += __shfl_xor(acc.x, 32);
+    acc.y += __shfl_xor(acc.y, 32);
+    acc.z += __shfl_xor(acc.z, 32);
+    acc.w += __shfl_xor(acc.w, 32);
+    if (lane < 32) {
+        const float inv = a.v_scale / L;
+        const half4_t r = {(_Float16)(acc.x * inv), (_Float16)(acc.y * inv), (_Float16)(acc.z * inv),
+                           (_Float16)(acc.w * inv)};
+        *reinterpret_cast<half4_t*>(a.out + orow + d4) = r;
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -343,50 +421,30 @@ __device__ __forceinline__ void store_new_token(const KernelParams& a, const New
 }
 
 // ------------------------------------------------------------------------------------------------
-// Partition kernel, one wave per (query head, partition, sequence).  The head is the fastest grid
-// dimension: workgroups are handed to the eight XCDs round-robin by linear id, so consecutive ids
-// must carry equal work -- all heads of one (partition, sequence) do, while consecutive partitions
-// of one sequence do not (its last partitions are ragged or empty).
+// MHA partition kernel: one wave per (query head, share of the work).  The work of one segment --
+// tiles [lo, hi) of sequence b (n tokens, nt tiles) -- ends with the final output when the segment
+// is the whole sequence, else with a partial in row h * rmul + radd.
 // APPEND: the decode step's new token (one per sequence, at position context_lens[b] - 1) is
-// quantized here by the wave of the last partition, patched into its registers and stored.  Used
-// only with one query head per KV head (grouped heads take the append kernel first).
+// quantized by the wave whose segment holds the sequence's last tile, patched into its registers
+// and stored.  Used only with one query head per KV head (grouped heads take the append kernel
+// first).
 template <int DT, int TW, bool APPEND>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((DT == KVQ_INT8 && APPEND) ? 4 : 5, 8))) void attn_partition_valu(
-    KernelParams a) {
-    __shared__ uint32_t lds[TW * 16];
-    __shared__ u32x4 lds_knew[APPEND ? 8 : 1];
-    const int h = blockIdx.x;
-    const int p = blockIdx.y;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x;
-    const int G = a.Hq / a.Hkv;
-    const int g = h / G;
+__device__ __forceinline__ void mha_segment(const KernelParams& a, int b, int h, int g, int n, int nt,
+                                            int lo, int hi, int64_t rmul, int64_t radd, int lane,
+                                            uint32_t* lds, u32x4* lds_knew) {
     const int tk = lane >> 2;
-
-    const int n = a.ctx[b];
-    const int np = (n + a.PS - 1) / a.PS;  // partitions this sequence uses
     const size_t orow = ((size_t)b * a.Hq + h) * kDim;
-    if (n <= 0) {
-        if (p == 0) {
-            a.out[orow + lane] = 0;
-            a.out[orow + 64 + lane] = 0;
-        }
-        return;
-    }
-    if (p >= np) return;
-    const int t_begin = p * a.PS;
-    const int t_end = min(n, t_begin + a.PS);
-    const int tile_begin = t_begin / kBlock;
-    const int tile_end = (t_end + kBlock - 1) / kBlock;
+    const bool has_last = hi == nt;
+    const int t_end = min(n, hi * kBlock);
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
     // fused append: the new row's loads are issued now, its encode waits for its tile (the last)
     NewRow raw{0u, 0u, 0u};
     int tile_new = -1;
     if constexpr (APPEND) {
-        if (p == np - 1) {
+        if (has_last) {
             raw = load_new_row(a, b, g, lane);
-            tile_new = (n - 1) / kBlock;
+            tile_new = nt - 1;
         }
     }
 
@@ -408,16 +466,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((DT == KVQ_I
     float l_lane = 0.0f;    // running sum of the weights of this lane's token
     float acc0 = 0.0f, acc1 = 0.0f;  // unnormalized output, dims lane and 64 + lane
 
-    for (int tb = tile_begin; tb < tile_end; tb += 64) {
+    for (int tb = lo; tb < hi; tb += 64) {
         // block ids of up to 64 tiles, one per lane
-        const int nt_grp = min(64, tile_end - tb);
+        const int nt_grp = min(64, hi - tb);
         const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
 
-        // whole chunks: TW tiles, all inside the partition.  The sequence's last tile (which holds
+        // whole chunks: TW tiles, all inside the segment.  The sequence's last tile (which holds
         // the token a fused step appends) is always left to the single-tile loop below, with or
         // without the fused append, so that both give bitwise the same arithmetic.
         int full_tiles = min(nt_grp, (t_end - tb * kBlock) / kBlock);
-        if (p == np - 1) full_tiles = min(full_tiles, (n - 1) / kBlock - tb);
+        if (has_last) full_tiles = min(full_tiles, nt - 1 - tb);
         const int nfull = full_tiles / TW;
         for (int c = 0; c < nfull; ++c) {
             Tile t[TW];
@@ -435,9 +493,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((DT == KVQ_I
             if constexpr (APPEND) {
                 if (tb + c0 == tile_new) {
                     uint16_t* lds_k = reinterpret_cast<uint16_t*>(lds_knew);
-                    const NewToken nt = new_token<DT>(a, raw, n, lane, lds_k);
-                    patch_tile<DT>(t[0], nt, lds_k, lane);
-                    store_new_token<DT>(a, nt, t[0], lds_k, __builtin_amdgcn_readlane(blk_lane, c0),
+                    const NewToken ntok = new_token<DT>(a, raw, n, lane, lds_k);
+                    patch_tile<DT>(t[0], ntok, lds_k, lane);
+                    store_new_token<DT>(a, ntok, t[0], lds_k, __builtin_amdgcn_readlane(blk_lane, c0),
                                         g, lane, v_off);
                 }
             }
@@ -449,18 +507,58 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((DT == KVQ_I
     // each token's weight was added by the four lanes of its quad: count one lane per quad
     const float l_sum = wave_sum((lane & 3) == 0 ? l_lane : 0.0f);
 
-    if (np == 1) {
+    if (lo == 0 && has_last) {
         const float inv = a.v_scale / l_sum;
         a.out[orow + lane] = __builtin_bit_cast(uint16_t, (_Float16)(acc0 * inv));
         a.out[orow + 64 + lane] = __builtin_bit_cast(uint16_t, (_Float16)(acc1 * inv));
     } else {
-        const size_t prow = ((size_t)b * a.Hq + h) * a.P + p;
+        const int64_t prow = h * rmul + radd;
         a.part_o[prow * kDim + lane] = acc0;
         a.part_o[prow * kDim + 64 + lane] = acc1;
         if (lane == 0) {
             a.part_m[prow] = m_run;
             a.part_l[prow] = l_sum;
         }
+    }
+}
+
+// BAL: grid (query head, wave of the balanced split).  Otherwise grid (query head, partition,
+// sequence) with fixed partitions of PS tokens.  The balanced split runs about two waves per SIMD,
+// so its register budget is that of two waves; fixed partitions can have many more waves than fit
+// and are held to the occupancy the plain loop reaches (5, 4 for INT8 with the append).  The head is the fastest grid dimension:
+// workgroups are handed to the eight XCDs round-robin by linear id, so consecutive ids should
+// carry equal work -- all heads of one (partition or share, sequence) do.
+template <int DT, int TW, bool APPEND, bool BAL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((DT == KVQ_INT8 && APPEND) ? 4 : 5), 8))) void attn_partition_valu(
+    KernelParams a) {
+    __shared__ uint32_t lds[TW * 16];
+    __shared__ u32x4 lds_knew[APPEND ? 8 : 1];
+    const int lane = threadIdx.x;
+    const int h = blockIdx.x;
+    const int g = h / (a.Hq / a.Hkv);
+    if constexpr (BAL) {
+        const int w = blockIdx.y;
+        for_each_segment(a, w, h == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
+            mha_segment<DT, TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, lds_knew);
+        });
+    } else {
+        const int p = blockIdx.y;
+        const int b = blockIdx.z;
+        const int n = a.ctx[b];
+        if (n <= 0) {
+            if (p == 0) {
+                const size_t orow = ((size_t)b * a.Hq + h) * kDim;
+                a.out[orow + lane] = 0;
+                a.out[orow + 64 + lane] = 0;
+            }
+            return;
+        }
+        const int nt = tiles_of(n);
+        const int lo = p * (a.PS / kBlock);
+        if (lo >= nt) return;
+        const int hi = min(nt, lo + a.PS / kBlock);
+        mha_segment<DT, TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane,
+                                    lds, lds_knew);
     }
 }
 
@@ -490,35 +588,16 @@ __device__ __forceinline__ half8_v codes8(uint32_t w0, uint32_t w1) {
 }
 
 template <int DT, int TW>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void attn_partition_mfma(
-    KernelParams a) {
+__device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g, int n, int nt, int lo,
+                                            int hi, int64_t rmul, int64_t radd, int lane) {
     static_assert(TW % 2 == 0, "tiles are paired for the PV products");
-    const int g = blockIdx.x;
-    const int p = blockIdx.y;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x;
     const int col = lane & 15;  // query head within the group (B / C column), or A row
     const int q4 = lane >> 4;   // MFMA k-group / C row group
     const int G = a.Hq / a.Hkv;
     const int h = g * G + col;  // this lane's query head (valid when col < G)
-
-    const int n = a.ctx[b];
-    const int np = (n + a.PS - 1) / a.PS;
-    if (n <= 0) {
-        if (p == 0) {
-            for (int jh = 0; jh < G; ++jh) {
-                const size_t orow = ((size_t)b * a.Hq + g * G + jh) * kDim;
-                a.out[orow + lane] = 0;
-                a.out[orow + 64 + lane] = 0;
-            }
-        }
-        return;
-    }
-    if (p >= np) return;
-    const int t_begin = p * a.PS;
-    const int t_end = min(n, t_begin + a.PS);
-    const int tile_begin = t_begin / kBlock;
-    const int tile_end = (t_end + kBlock - 1) / kBlock;
+    const int t_end = min(n, hi * kBlock);
+    const int tile_begin = lo;
+    const int tile_end = hi;
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
     // Q^T operands: MFMA m covers dims 64 (m/2) + 16 q4 + 8 (m%2) .. +7 in k-slots 8 q4 .. +7
@@ -641,52 +720,112 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     float l_sum = l_lane + __shfl_xor(l_lane, 16);
     l_sum += __shfl_xor(l_sum, 32);
 
-    if (col >= G) return;
-    if (np == 1) {
-        const float inv = a.v_scale / l_sum;
-        uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * kDim;
+    if (col < G) {
+        if (lo == 0 && hi == nt) {
+            const float inv = a.v_scale / l_sum;
+            uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * kDim;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const half4_t o = {(_Float16)(acc[r][0] * inv), (_Float16)(acc[r][1] * inv),
-                               (_Float16)(acc[r][2] * inv), (_Float16)(acc[r][3] * inv)};
-            *reinterpret_cast<half4_t*>(orow + 16 * r + 4 * q4) = o;
-        }
-    } else {
-        const size_t prow = ((size_t)b * a.Hq + h) * a.P + p;
+            for (int r = 0; r < 8; ++r) {
+                const half4_t o = {(_Float16)(acc[r][0] * inv), (_Float16)(acc[r][1] * inv),
+                                   (_Float16)(acc[r][2] * inv), (_Float16)(acc[r][3] * inv)};
+                *reinterpret_cast<half4_t*>(orow + 16 * r + 4 * q4) = o;
+            }
+        } else {
+            const int64_t prow = h * rmul + radd;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            *reinterpret_cast<float4_t*>(a.part_o + prow * kDim + 16 * r + 4 * q4) = acc[r];
-        if (q4 == 0) {
-            a.part_m[prow] = m_run;
-            a.part_l[prow] = l_sum;
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<float4_t*>(a.part_o + prow * kDim + 16 * r + 4 * q4) = acc[r];
+            if (q4 == 0) {
+                a.part_m[prow] = m_run;
+                a.part_l[prow] = l_sum;
+            }
         }
     }
 }
 
-// Separate merge kernel, one wave per (query head, sequence) whose context spans several partitions.
+// BAL: grid (KV head, wave of the balanced split), else (KV head, partition, sequence).
+template <int DT, int TW, bool BAL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 4, 8))) void attn_partition_mfma(
+    KernelParams a) {
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    if constexpr (BAL) {
+        const int w = blockIdx.y;
+        for_each_segment(a, w, g == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
+            gqa_segment<DT, TW>(a, b, g, n, nt, lo, hi, a.S, w + b, lane);
+        });
+    } else {
+        const int p = blockIdx.y;
+        const int b = blockIdx.z;
+        const int G = a.Hq / a.Hkv;
+        const int n = a.ctx[b];
+        if (n <= 0) {
+            if (p == 0) {
+                for (int jh = 0; jh < G; ++jh) {
+                    const size_t orow = ((size_t)b * a.Hq + g * G + jh) * kDim;
+                    a.out[orow + lane] = 0;
+                    a.out[orow + 64 + lane] = 0;
+                }
+            }
+            return;
+        }
+        const int nt = tiles_of(n);
+        const int lo = p * (a.PS / kBlock);
+        if (lo >= nt) return;
+        const int hi = min(nt, lo + a.PS / kBlock);
+        gqa_segment<DT, TW>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane);
+    }
+}
+
+// Merge kernel, one wave per (query head, sequence): combines the partials of a sequence whose work
+// was split; with the balanced split it also writes the zeros of empty sequences.
 __global__ __launch_bounds__(64) void attn_merge(KernelParams a) {
     const int h = blockIdx.x;
     const int b = blockIdx.y;
+    const int lane = threadIdx.x;
     const int n = a.ctx[b];
-    const int np = min((n + a.PS - 1) / a.PS, a.P);
-    if (np <= 1) return;  // written directly by the partition kernel
-    merge_partials(a, b, h, np, threadIdx.x);
+    const size_t orow = ((size_t)b * a.Hq + h) * kDim;
+    if (a.NW > 0) {
+        const int nt = tiles_of(n);
+        if (nt == 0) {
+            a.out[orow + lane] = 0;
+            a.out[orow + 64 + lane] = 0;
+            return;
+        }
+        const int T = a.plan[a.B], nw = a.plan[a.B + 1];
+        const int c0 = a.plan[b];
+        const int wlo = wave_of_tile(c0, T, nw), whi = wave_of_tile(c0 + nt - 1, T, nw);
+        if (wlo == whi) return;  // one wave held the whole sequence and wrote the output
+        merge_rows(a, (int64_t)h * a.S + wlo + b, whi - wlo + 1, orow, lane);
+    } else {
+        const int np = min((n + a.PS - 1) / a.PS, a.P);
+        if (np <= 1) return;  // written directly by the partition kernel
+        merge_rows(a, ((int64_t)b * a.Hq + h) * a.P, np, orow, lane);
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
-template <int DT>
-static void launch_partition(const KernelParams& kp, int batch, hipStream_t stream) {
+template <int DT, bool BAL>
+static void launch_partition(const KernelParams& kp, hipStream_t stream) {
+    const int hw = kp.Hq == kp.Hkv ? kp.Hq : kp.Hkv;  // waves per column of the grid
+    const dim3 grid = BAL ? dim3((unsigned)hw, (unsigned)kp.NW) : dim3((unsigned)hw, (unsigned)kp.P, (unsigned)kp.B);
     if (kp.Hq == kp.Hkv) {
-        const dim3 grid((unsigned)kp.Hq, (unsigned)kp.P, (unsigned)batch);
         if (kp.k_new)
-            attn_partition_valu<DT, 4, true><<<grid, 64, 0, stream>>>(kp);
+            attn_partition_valu<DT, 4, true, BAL><<<grid, 64, 0, stream>>>(kp);
         else
-            attn_partition_valu<DT, 4, false><<<grid, 64, 0, stream>>>(kp);
+            attn_partition_valu<DT, 4, false, BAL><<<grid, 64, 0, stream>>>(kp);
     } else {
         // grouped query heads: one wave per KV head; the KV head is the fastest grid dimension
-        const dim3 grid((unsigned)kp.Hkv, (unsigned)kp.P, (unsigned)batch);
-        attn_partition_mfma<DT, 2><<<grid, 64, 0, stream>>>(kp);
+        attn_partition_mfma<DT, 2, BAL><<<grid, 64, 0, stream>>>(kp);
     }
+}
+
+template <int DT>
+static void launch_partition(const KernelParams& kp, hipStream_t stream) {
+    if (kp.NW > 0)
+        launch_partition<DT, true>(kp, stream);
+    else
+        launch_partition<DT, false>(kp, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
@@ -703,13 +842,17 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.part_o = a.part_o;
     kp.part_m = a.part_m;
     kp.part_l = a.part_l;
+    kp.plan = a.plan;
     kp.block_tables = a.block_tables;
     kp.ctx = a.context_lens;
     kp.max_blocks = a.max_blocks_per_seq;
+    kp.B = a.batch;
     kp.Hq = a.num_q_heads;
     kp.Hkv = c.num_kv_heads;
     kp.P = a.num_partitions;
     kp.PS = a.partition_size;
+    kp.NW = a.balanced_waves;
+    kp.S = a.balanced_waves + a.batch;
     const bool fp8 = c.dtype != KVQ_INT8;
     kp.qk_scale = a.sm_scale * kLog2e * (fp8 ? c.kv_scale : 1.0f);
     kp.v_scale = fp8 ? c.kv_scale : 1.0f;
@@ -726,14 +869,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     }
     if (main_begin) (void)hipEventRecord(main_begin, stream);
     switch (c.dtype) {
-        case KVQ_FP8_E4M3: launch_partition<KVQ_FP8_E4M3>(kp, a.batch, stream); break;
-        case KVQ_FP8_E5M2: launch_partition<KVQ_FP8_E5M2>(kp, a.batch, stream); break;
-        default: launch_partition<KVQ_INT8>(kp, a.batch, stream); break;
+        case KVQ_FP8_E4M3: launch_partition<KVQ_FP8_E4M3>(kp, stream); break;
+        case KVQ_FP8_E5M2: launch_partition<KVQ_FP8_E5M2>(kp, stream); break;
+        default: launch_partition<KVQ_INT8>(kp, stream); break;
     }
     if (main_end) (void)hipEventRecord(main_end, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.num_partitions > 1) {
+    if (kp.NW > 0 || kp.P > 1) {
         attn_merge<<<dim3((unsigned)a.num_q_heads, (unsigned)a.batch), 64, 0, stream>>>(kp);
         e = hipGetLastError();
     }

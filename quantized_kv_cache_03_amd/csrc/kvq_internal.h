@@ -19,11 +19,14 @@ struct DecodeArgs {
     int32_t max_blocks_per_seq;
     const int32_t* context_lens;
     int32_t batch;
-    int32_t num_partitions;   // grid extent over partitions (>= 1)
-    int32_t partition_size;   // tokens per partition; covers the whole context when num_partitions == 1
-    float* part_o;            // [B][Hq][P][128] (NULL when num_partitions == 1)
-    float* part_m;            // [B][Hq][P]
-    float* part_l;            // [B][Hq][P]
+    int32_t num_partitions;   // fixed partitions: grid extent over partitions (>= 1)
+    int32_t partition_size;   // fixed partitions: tokens per partition (the whole context when
+                              // num_partitions == 1)
+    int32_t balanced_waves;   // balanced split: waves per head row (NW); 0 for fixed partitions
+    int32_t* plan;            // balanced split: int32 [B + 2]
+    float* part_o;            // partial rows: fixed [B][Hq][P][128], balanced [Hq][NW + B][128]
+    float* part_m;            // one float per partial row
+    float* part_l;            // one float per partial row
     const uint16_t* k_new;    // fused decode step: fp16 [B][Hkv][128] rows to append, else NULL
     const uint16_t* v_new;
 };
@@ -37,8 +40,8 @@ hipError_t launch_dequant(const kvq_cache& c, const int32_t* block_tables, int32
                           const int32_t* context_lens, int32_t batch, int32_t max_context_len,
                           float* k_out, float* v_out, hipStream_t stream);
 
-// Partition kernel (with the append of the decode step when k_new is set), then, when
-// num_partitions > 1, the merge kernel.  The optional events are recorded around the partition
+// Partition kernel (with the append of the decode step when k_new is set), then, with the balanced
+// split or num_partitions > 1, the merge kernel.  The optional events are recorded around the partition
 // kernel (kernel-timing hook).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
                          hipEvent_t main_end);

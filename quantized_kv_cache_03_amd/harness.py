@@ -51,22 +51,25 @@ class DeviceCase:
         self.out_d = torch.empty_like(self.q_d)
         self._prefill(k, v, verbose, 0 if prefill_last else 1)
         # the decode step's new rows: the last row of each sequence
-        last_k = np.empty((self.B, w.num_kv_heads, W.HEAD_DIM), np.float16)
-        last_v = np.empty_like(last_k)
+        # (an empty sequence appends nothing: its row stays zero)
+        last_k = np.zeros((self.B, w.num_kv_heads, W.HEAD_DIM), np.float16)
+        last_v = np.zeros_like(last_k)
+        has = self.ctx > 0
         if k is not None:
             cu = np.concatenate([[0], np.cumsum(self.ctx)])
-            last_k[:] = k[cu[1:] - 1]
-            last_v[:] = v[cu[1:] - 1]
+            last_k[has] = k[cu[1:][has] - 1]
+            last_v[has] = v[cu[1:][has] - 1]
         else:
             for b, n in enumerate(self.ctx):
-                kb, vb = W.kv_rows(w, b, int(n), self.channels)
-                last_k[b], last_v[b] = kb[-1], vb[-1]
+                if n > 0:
+                    kb, vb = W.kv_rows(w, b, int(n), self.channels)
+                    last_k[b], last_v[b] = kb[-1], vb[-1]
         self.step_k_host, self.step_v_host = last_k, last_v
         self.step_k_d = torch.from_numpy(last_k).to(device)
         self.step_v_d = torch.from_numpy(last_v).to(device)
         self.partition_size = w.partition_size
         self.workspace, self.workspace_bytes = K.alloc_workspace(
-            self.B, w.num_q_heads, self.max_ctx, self.partition_size, device=device)
+            self.B, w.num_q_heads, w.num_kv_heads, self.max_ctx, self.partition_size, device=device)
         torch.cuda.synchronize()
 
     def _prefill(self, k, v, verbose, skip: int):

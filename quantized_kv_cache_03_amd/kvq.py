@@ -163,18 +163,23 @@ def append(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, block_
                           _stream(stream)), "kvq_append")
 
 
-def workspace_size(batch: int, num_q_heads: int, max_context_len: int, partition_size: int) -> int:
-    return int(lib.kvq_decode_workspace_size(batch, num_q_heads, HEAD_DIM, max_context_len, partition_size))
+PARTITION_BALANCED = -1  # KVQ_PARTITION_BALANCED
 
 
-def alloc_workspace(batch, num_q_heads, max_context_len, partition_size, device="cuda"):
-    n = workspace_size(batch, num_q_heads, max_context_len, partition_size)
+def workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_context_len: int,
+                   partition_size: int) -> int:
+    return int(lib.kvq_decode_workspace_size(batch, num_q_heads, num_kv_heads, max_context_len,
+                                             partition_size))
+
+
+def alloc_workspace(batch, num_q_heads, num_kv_heads, max_context_len, partition_size, device="cuda"):
+    n = workspace_size(batch, num_q_heads, num_kv_heads, max_context_len, partition_size)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
 
 
 def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.Tensor,
                       context_lens: torch.Tensor, max_context_len: int, sm_scale: float | None = None,
-                      partition_size: int = 512, workspace: torch.Tensor | None = None,
+                      partition_size: int = PARTITION_BALANCED, workspace: torch.Tensor | None = None,
                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """kvq_paged_decode_attn: q fp16 [B][Hq][128] -> out fp16 [B][Hq][128]."""
     assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
@@ -183,7 +188,7 @@ def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty_like(q)
-    need = workspace_size(B, Hq, max_context_len, partition_size)
+    need = workspace_size(B, Hq, cache.num_kv_heads, max_context_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -197,7 +202,7 @@ def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.
 
 def decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
                 block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                sm_scale: float | None = None, partition_size: int = 512,
+                sm_scale: float | None = None, partition_size: int = PARTITION_BALANCED,
                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 stream=None) -> torch.Tensor:
     """kvq_decode_step: append one row per sequence (fp16 [B][Hkv][128]) and attend, fused."""
@@ -209,7 +214,7 @@ def decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty_like(q)
-    need = workspace_size(B, Hq, max_context_len, partition_size)
+    need = workspace_size(B, Hq, cache.num_kv_heads, max_context_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -43,7 +43,7 @@ class Workload:
     scale_rule: str = "one"     # "amax/448" | "one"
     outliers: int = 0
     outlier_gain: float = 20.0
-    partition_size: int = 512
+    partition_size: int = -1  # the balanced split (KVQ_PARTITION_BALANCED)
 
     @property
     def group(self) -> int:
@@ -56,7 +56,7 @@ class Workload:
 
 WORKLOADS = {
     "tiny-e4m3": Workload("tiny-e4m3", 1, 1, 8, 8, "fp8_e4m3", ("fixed", 512),
-                          scale_rule="amax/448", partition_size=0),
+                          scale_rule="amax/448"),
     "llama2-7b-mha-e4m3": Workload("llama2-7b-mha-e4m3", 2, 32, 32, 32, "fp8_e4m3",
                                    ("uniform", 512, 4096), table="shuffled",
                                    scale_rule="amax/448"),
@@ -166,4 +166,6 @@ def kv_scale(w: Workload, k: np.ndarray | None = None, v: np.ndarray | None = No
         for b, n in enumerate(ctx):
             kb, vb = kv_rows(w, b, int(n), ch)
             amax = max(amax, float(np.abs(kb).max(initial=0)), float(np.abs(vb).max(initial=0)))
+    if amax == 0.0:  # no values at all (every sequence empty): the default scale
+        return 1.0
     return float(np.float32(amax) / np.float32(448.0))

@@ -106,12 +106,31 @@ def test_attention_argument_errors(K, name, ckw, akw, status):
 
 
 def test_workspace_size(K):
-    assert K.workspace_size(32, 32, 4096, 0) == 0
-    assert K.workspace_size(32, 32, 512, 512) == 0
-    n = K.workspace_size(32, 32, 4096, 512)
+    assert K.workspace_size(32, 32, 32, 4096, 0) == 0
+    assert K.workspace_size(32, 32, 32, 512, 512) == 0
+    n = K.workspace_size(32, 32, 32, 4096, 512)
     rows = 32 * 32 * 8
     assert n >= rows * 130 * 4
-    assert K.lib.kvq_decode_workspace_size(1, 1, 64, 100, 16) == 0  # unsupported head_dim
+    assert K.lib.kvq_decode_workspace_size(1, 3, 2, 100, 16) == 0    # Hq not a multiple of Hkv
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 100, 24) == 0    # not a multiple of 16
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 100, -2) == 0    # negative, not the balanced value
+
+
+def test_workspace_size_balanced(K):
+    """Balanced split: a plan of batch + 2 int32 plus partial rows for every query head, one per
+    wave of its row and one per sequence (a wave's share starts at most one new partial per
+    sequence boundary).  The waves per row target about 2048 waves in all, at least 8 tiles each."""
+    B = K.PARTITION_BALANCED
+    # MHA: 32 heads -> 64 waves per head row; rows = Hq * (64 + batch)
+    n = K.workspace_size(32, 32, 32, 4096, B)
+    assert n >= 32 * (64 + 32) * 130 * 4 + (32 + 2) * 4
+    # grouped heads: 8 KV heads -> 256 waves per row; rows use the query heads
+    n8 = K.workspace_size(16, 64, 8, 32768, B)
+    assert n8 >= 64 * (256 + 16) * 130 * 4
+    # a tiny problem caps the waves at ceil(tiles / 8): one sequence of 40 tokens -> 3 tiles, 1 wave
+    small = K.workspace_size(1, 8, 8, 40, B)
+    assert 0 < small < 8 * (2 + 1) * 130 * 4 + 1024
+    assert K.workspace_size(0, 8, 8, 40, B) == 0
 
 
 def test_append_argument_errors(K):

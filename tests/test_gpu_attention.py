@@ -47,7 +47,7 @@ IDS = [f"{c[0]}-G{c[2].get('num_q_heads', 0) // max(1, c[2].get('num_kv_heads', 
 
 
 @pytest.mark.parametrize("name,ctx,kw", CASES, ids=IDS)
-@pytest.mark.parametrize("partition", [0, 16, 64, 512])
+@pytest.mark.parametrize("partition", [-1, 0, 16, 64, 512])
 def test_decode_step_scaled(H, name, ctx, kw, partition):
     w = _scaled(name, ctx, partition_size=partition, **kw)
     say(f"[decode step] {w.name} ctx={ctx} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
@@ -68,7 +68,7 @@ def test_split_partition_sizes_agree(H):
     say("[partition sizes]")
     case = H.DeviceCase(w, keep_host_rows=True)
     case.append_step()
-    outs = {ps: case.attention(partition_size=ps).clone().cpu().numpy() for ps in (0, 16, 256, 512, 4096)}
+    outs = {ps: case.attention(partition_size=ps).clone().cpu().numpy() for ps in (-1, 0, 16, 256, 512, 4096)}
     ref = OracleTwin(case, range(case.B)).attention()
     for ps, o in outs.items():
         assert_attn_close(o, ref, f"partition {ps}")
@@ -123,11 +123,12 @@ def test_empty_batch_is_a_no_op(H):
 
 
 @pytest.mark.parametrize("name,ctx,kw", CASES, ids=IDS)
-def test_fused_step_appends_and_matches_separate_calls(H, name, ctx, kw):
+@pytest.mark.parametrize("partition", [-1, 64])
+def test_fused_step_appends_and_matches_separate_calls(H, name, ctx, kw, partition):
     """kvq_decode_step on a cache whose last slots were never written: its cache bytes equal the
     oracle's full append, its output passes the gate, and both equal, bit for bit, kvq_append
     followed by kvq_paged_decode_attn on an identically prepared cache."""
-    w = _scaled(name, ctx, partition_size=64, **kw)
+    w = _scaled(name, ctx, partition_size=partition, **kw)
     say(f"[fused step] {w.name} ctx={ctx} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype}")
     fused = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2, prefill_last=False)
     sep = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2, prefill_last=False)
@@ -139,3 +140,36 @@ def test_fused_step_appends_and_matches_separate_calls(H, name, ctx, kw):
     np.testing.assert_array_equal(out_f.view(np.uint16), out_s.view(np.uint16))
     st = assert_attn_close(out_f, twin.attention(), w.name)
     say(f"    ok {st}")
+
+
+BALANCED_CASES = [
+    # many short sequences: a wave's share spans several of them; more than 64 sequences (the
+    # per-wave scan takes several chunks); empty sequences anywhere, the first included
+    ("llama2-7b-mha-e4m3", [0, 3, 17, 1, 0, 40, 2, 300] * 12, {"num_q_heads": 2, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-e5m2", [5, 0, 1, 33, 16, 700, 15, 0, 64] * 9, {"num_q_heads": 8, "num_kv_heads": 2}),
+    ("llama2-13b-mha-int8", [1, 2, 3, 0, 129, 48] * 13, {"num_q_heads": 2, "num_kv_heads": 2}),
+    # one long sequence split over every wave of its row, plus one of length 1
+    ("llama3-70b-gqa-e4m3-32k", [9000, 1], {"num_q_heads": 8, "num_kv_heads": 1}),
+    ("llama2-7b-mha-e4m3", [6000], {"num_q_heads": 1, "num_kv_heads": 1}),
+    # all sequences empty
+    ("tiny-e4m3", [0, 0, 0], {"num_q_heads": 2, "num_kv_heads": 2}),
+]
+
+
+@pytest.mark.parametrize("name,ctx,kw", BALANCED_CASES,
+                         ids=[f"{c[0]}-B{len(c[1])}-{i}" for i, c in enumerate(BALANCED_CASES)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_balanced_split_edge_cases(H, name, ctx, kw, fused):
+    """Balanced split over ragged batches: every (sequence, head) against the oracle, empty
+    sequences give zeros, and the cache bytes of the step's append are the oracle's."""
+    w = _scaled(name, ctx, partition_size=-1, **kw)
+    say(f"[balanced] {w.name} B={len(ctx)} Hq={w.num_q_heads} Hkv={w.num_kv_heads} fused={fused}")
+    case = H.DeviceCase(w, keep_host_rows=True, spare_blocks=2, prefill_last=False)
+    out = case.step(fused=fused).cpu().numpy()
+    twin = OracleTwin(case, range(case.B))
+    assert_cache_bytes_equal(case, twin, w.name)
+    empty = np.asarray(ctx) == 0
+    assert np.all(out[empty] == 0)
+    if (~empty).any():
+        st = assert_attn_close(out[~empty], twin.attention()[~empty], w.name)
+        say(f"    ok {st}")
