@@ -2,9 +2,9 @@
 """Decode-step benchmark of the 8-bit paged KV cache on one MI355X.
 
 A step is one decode step of one attention layer: the append of one new token per sequence and
-paged attention over the whole cache, through kvq_decode_step (append fused into the split-K
-partition kernel, then the merge kernel; `--separate-calls` times kvq_append +
-kvq_paged_decode_attn instead).  Inputs are seeded synthetic tensors already resident in HBM.  The
+paged attention over the whole cache, through kvq_decode_step (append fused into the partition
+kernel, then the merge kernel; `--separate-calls` times kvq_append + kvq_paged_decode_attn
+instead).  Inputs are seeded synthetic tensors already resident in HBM.  The
 timed loop walks over `--layers` copies of the layer's cache so consecutive steps read different
 memory (the 256 MB last-level cache cannot serve a step from the previous one).
 
@@ -33,10 +33,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+def partition_kernel(w) -> tuple[str, str]:
+    """(kernel name, source file) of the partition kernel that serves the workload."""
+    if w.num_q_heads == w.num_kv_heads:
+        return f"attn_partition_valu<{w.dtype}>", "kvq_attn_mha.hip"
+    return f"attn_partition_mfma<{w.dtype}>", "kvq_attn_gqa.hip"
+
+
+def kernel_source_digest(w) -> str:
+    """Digest of the partition kernel's sources (its file and the headers it includes)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_device.h"):
+    for f in (partition_kernel(w)[1], "kvq_attn.h", "kvq_device.h"):
         with open(os.path.join(ROOT, "quantized_kv_cache_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -193,7 +201,7 @@ def main():
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     main_avg_ms = main_ms / max(1, main_n)
     achieved = attn_bytes / (main_avg_ms * 1e-3) / 1e9
-    digest = kernel_source_digest()
+    digest = kernel_source_digest(w)
     traffic = load_traffic(w.name, digest)
 
     cpu = None
@@ -241,7 +249,7 @@ def main():
         "kernel_timing": "partition kernel timed with HIP events in a second pass over the same steps",
         "kernels_ms": {"attn_partition_avg": round(main_avg_ms, 5)},
         "roofline": {
-            "kernel": f"attn_partition_valu<{w.dtype}>",
+            "kernel": partition_kernel(w)[0],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,

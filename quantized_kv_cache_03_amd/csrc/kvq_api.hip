@@ -71,7 +71,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // grouped heads), about kBalancedWaves waves in all -- two per SIMD of the 1024 on the chip, enough
 // to keep HBM busy while each wave streams a long, equal share.  A wave gets at least kMinTiles
 // tiles (the device caps the waves it uses by the same rule on the actual tile count).
-constexpr int64_t kBalancedWaves = 2048;
+#ifndef KVQ_BALANCED_WAVES
+#define KVQ_BALANCED_WAVES 2048
+#endif
+constexpr int64_t kBalancedWaves = KVQ_BALANCED_WAVES;
 constexpr int64_t kMinTiles = 8;
 
 struct Plan {

@@ -1,0 +1,332 @@
+// kvq_attn_gqa.hip -- decode attention for grouped query heads (the MFMA kernel).
+#include "kvq_attn.h"
+
+namespace kvq {
+
+// Grouped-query kernel: one wave per (KV head, share of the work) serves the G <= 16 query heads
+// that share the KV head, so each K/V code is read and decoded once for all of them, and the two
+// products run on the matrix cores (v_mfma_f32_16x16x32_f16, query heads padded to 16 columns):
+//   S^T = K Q^T   per tile: A = K rows (lane: token lane%16, 8 of its dims), B = Q^T (lane: head
+//                 lane%16, the same 8 dims), C = 16 tokens x 16 heads (lane: head lane%16, tokens
+//                 4 (lane/16) .. +3).  The 128 dims are 4 MFMAs of 32; any fixed assignment of dims
+//                 to MFMA k-slots works as long as K and Q agree.
+//   O^T += V^T P^T per pair of tiles and 16-dim row block: A = V^T (lane: dim, tokens 4 (lane/16)
+//                 .. +3 of both tiles, read as one dword per tile from the dim-major V rows),
+//                 B = P^T in exactly the layout the S^T accumulator left it (lane: head, the same
+//                 tokens), so no transposition is needed.  P is split into fp16 hi + lo parts.
+// The online softmax keeps one running max per head (all lanes of a column agree).
+typedef _Float16 half8_v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ half8_v join8(half2_t a, half2_t b, half2_t c, half2_t d) {
+    return half8_v{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+template <int DT>
+__device__ __forceinline__ half8_v codes8(uint32_t w0, uint32_t w1) {
+    return join8(codes_to_f16<DT, 0>(w0), codes_to_f16<DT, 1>(w0), codes_to_f16<DT, 0>(w1),
+                 codes_to_f16<DT, 1>(w1));
+}
+
+// Replace the appended token's slot in the MFMA operand registers of its tile by the codes in LDS
+// (K: lane (token, k-group) takes chunks q4 and q4 + 4 of the token; V: the lanes of k-group
+// slot / 4 hold the slot's byte in each of their dwords) and store the token: its eight K chunks
+// from LDS, the whole V tile from the patched registers (each store instruction writes 256
+// contiguous bytes; the other tokens' bytes are written back unchanged -- this wave is the only
+// reader and writer of the tile), and the INT8 scales.
+template <int DT>
+__device__ __forceinline__ void gqa_patch_and_store(const KernelParams& a, const NewToken& nt,
+                                                    const u32x4* lds_k, const uint8_t* lds_v, int blk,
+                                                    int g, int lane, uint32_t v_off, u32x4& ka,
+                                                    u32x4& kb, uint32_t (&vd)[8], float4_t& ks4,
+                                                    float4_t& vs4) {
+    const int col = lane & 15, q4 = lane >> 4;
+    if (col == nt.slot) {
+        ka = lds_k[q4];
+        kb = lds_k[4 + q4];
+    }
+    if (q4 == (nt.slot >> 2)) {
+        const int sh = 8 * (nt.slot & 3);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            vd[r] = (vd[r] & ~(0xFFu << sh)) | ((uint32_t)lds_v[16 * r + col] << sh);
+        if constexpr (DT == KVQ_INT8) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (t == (nt.slot & 3)) {
+                    ks4[t] = nt.ks;
+                    vs4[t] = nt.vs;
+                }
+        }
+    }
+    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+    uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
+    uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
+    if (lane < 8)
+        __builtin_nontemporal_store(lds_k[lane], reinterpret_cast<u32x4*>(kt + k_byte(nt.slot, kChunk * lane)));
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        __builtin_nontemporal_store(vd[r], reinterpret_cast<uint32_t*>(vt + v_off + (uint32_t)r * 256u));
+    if constexpr (DT == KVQ_INT8) {
+        if (lane == 0) {
+            const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + nt.slot;
+            const_cast<float*>(a.ks)[so] = nt.ks;
+            const_cast<float*>(a.vs)[so] = nt.vs;
+        }
+    }
+}
+
+// APPEND: the decode step's new token is quantized by the wave whose segment holds the sequence's
+// last tile, patched into its registers and stored (one wave per (KV head, tile) reads it, so the
+// wave is the tile's only reader and writer).
+template <int DT, int TW, bool APPEND>
+__device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g, int n, int nt, int lo,
+                                            int hi, int64_t rmul, int64_t radd, int lane,
+                                            u32x4* lds_knew, uint8_t* lds_vnew) {
+    static_assert(TW % 2 == 0, "tiles are paired for the PV products");
+    const int col = lane & 15;  // query head within the group (B / C column), or A row
+    const int q4 = lane >> 4;   // MFMA k-group / C row group
+    const int G = a.Hq / a.Hkv;
+    const int h = g * G + col;  // this lane's query head (valid when col < G)
+    const int t_end = min(n, hi * kBlock);
+    const int tile_begin = lo;
+    const int tile_end = hi;
+    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+
+    // fused append: the new row's loads are issued now, its encode waits for its tile (the last)
+    NewRow raw{0u, 0u, 0u};
+    int tile_new = -1;
+    if constexpr (APPEND) {
+        if (hi == nt) {
+            raw = load_new_row(a, b, g, lane);
+            tile_new = nt - 1;
+        }
+    }
+
+    // Q^T operands: MFMA m covers dims 64 (m/2) + 16 q4 + 8 (m%2) .. +7 in k-slots 8 q4 .. +7
+    half8_v qB[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qB[m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
+    if (col < G) {
+        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h) * kDim;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            qB[m] = *reinterpret_cast<const half8_v*>(qrow + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
+    }
+
+    float m_run = kNegInf;  // running max of this lane's head (base-2 logits)
+    float l_lane = 0.0f;    // sum of this lane's weights (tokens 4 q4 .. +3 of every tile)
+    float4_t acc[8];        // O^T row blocks: dims 16 r + 4 q4 .. +3 of head col
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const uint32_t k_off = 16u * (uint32_t)lane;  // chunk q4 (+4): token col, dims 16 q4 (+64)
+    const uint32_t v_off = (uint32_t)col * kBlock + 4u * (uint32_t)q4;  // dim col (+16 r), tokens 4 q4
+
+    for (int tb = tile_begin; tb < tile_end; tb += 64) {
+        const int nt_grp = min(64, tile_end - tb);
+        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        for (int c0 = 0; c0 < nt_grp; c0 += TW) {
+            u32x4 ka[TW], kb[TW];
+            uint32_t vd[TW][8];
+            float4_t ks4[TW], vs4[TW];
+#pragma unroll
+            for (int i = 0; i < TW; ++i) {
+                if (c0 + i < nt_grp) {
+                    const int blk = __builtin_amdgcn_readlane(blk_lane, c0 + i);
+                    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+                    const uint8_t* kt = a.kc + tile;
+                    const uint8_t* vt = a.vc + tile;
+                    ka[i] = ldg16(kt + k_off);
+                    kb[i] = ldg16(kt + k_off + 1024u);
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
+                    if constexpr (DT == KVQ_INT8) {
+                        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
+                        ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+                        vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
+                    }
+                } else {
+                    ka[i] = kb[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) vd[i][r] = 0u;
+                    ks4[i] = vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+            }
+            if constexpr (APPEND) {
+                const int inew = tile_new - (tb + c0);  // wave-uniform
+                if (inew >= 0 && inew < TW) {
+                    const NewToken ntok = new_token<DT>(a, raw, n, lane, reinterpret_cast<uint16_t*>(lds_knew));
+                    lds_vnew[lane] = (uint8_t)ntok.v0;
+                    lds_vnew[64 + lane] = (uint8_t)ntok.v1;
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int i = 0; i < TW; ++i)
+                        if (i == inew)
+                            gqa_patch_and_store<DT>(a, ntok, lds_knew, lds_vnew,
+                                                    __builtin_amdgcn_readlane(blk_lane, c0 + i), g, lane,
+                                                    v_off, ka[i], kb[i], vd[i], ks4[i], vs4[i]);
+                }
+            }
+            // logits S^T: lane holds tokens 4 q4 .. +3 of each tile for head col
+            float z[TW][4];
+            float cmax = kNegInf;
+#pragma unroll
+            for (int i = 0; i < TW; ++i) {
+                float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].x, ka[i].y), qB[0], sacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].z, ka[i].w), qB[1], sacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].x, kb[i].y), qB[2], sacc, 0, 0, 0);
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].z, kb[i].w), qB[3], sacc, 0, 0, 0);
+                const int pos0 = (tb + c0 + i) * kBlock + 4 * q4;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    float f = a.qk_scale;
+                    if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
+                    z[i][t] = (pos0 + t < t_end) ? sacc[t] * f : kNegInf;
+                    cmax = fmaxf(cmax, z[i][t]);
+                }
+            }
+            // max over the head's tokens: the four row groups of the column
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+            const float m_new = fmaxf(m_run, cmax);  // finite: every chunk holds a valid token
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_lane *= alpha;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+
+#pragma unroll
+            for (int i = 0; i < TW; i += 2) {
+                // weights of the tile pair (i, i+1), hi and lo fp16 parts, in the B layout
+                half8_v whi, wlo;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float pw = __builtin_amdgcn_exp2f(z[i + u][t] - m_new);
+                        l_lane += pw;
+                        float w = pw;
+                        if constexpr (DT == KVQ_INT8) w = (pw > 0.0f) ? pw * vs4[i + u][t] : 0.0f;
+                        const _Float16 hi = (_Float16)w;
+                        whi[4 * u + t] = hi;
+                        wlo[4 * u + t] = (_Float16)(w - (float)hi);
+                    }
+                }
+                // V codes of the slots past the end are zeroed (they may hold NaN codes)
+                uint32_t v0[8], v1[8];
+                const int valid0 = t_end - (tb + c0 + i) * kBlock - 4 * q4;
+                const int valid1 = valid0 - kBlock;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    v0[r] = keep_bytes(vd[i][r], valid0);
+                    v1[r] = keep_bytes(vd[i + 1][r], valid1);
+                }
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const half8_v va8 = join8(codes_to_f16<DT, 0>(v0[r]), codes_to_f16<DT, 1>(v0[r]),
+                                              codes_to_f16<DT, 0>(v1[r]), codes_to_f16<DT, 1>(v1[r]));
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi, acc[r], 0, 0, 0);
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, wlo, acc[r], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // sum of the head's weights over the four row groups
+    float l_sum = l_lane + __shfl_xor(l_lane, 16);
+    l_sum += __shfl_xor(l_sum, 32);
+
+    if (col < G) {
+        if (lo == 0 && hi == nt) {
+            const float inv = a.v_scale / l_sum;
+            uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * kDim;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const half4_t o = {(_Float16)(acc[r][0] * inv), (_Float16)(acc[r][1] * inv),
+                                   (_Float16)(acc[r][2] * inv), (_Float16)(acc[r][3] * inv)};
+                *reinterpret_cast<half4_t*>(orow + 16 * r + 4 * q4) = o;
+            }
+        } else {
+            const int64_t prow = h * rmul + radd;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<float4_t*>(a.part_o + prow * kDim + 16 * r + 4 * q4) = acc[r];
+            if (q4 == 0) {
+                a.part_m[prow] = m_run;
+                a.part_l[prow] = l_sum;
+            }
+        }
+    }
+}
+
+// BAL: grid (KV head, wave of the balanced split), else (KV head, partition, sequence).
+template <int DT, int TW, bool APPEND, bool BAL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((DT == KVQ_INT8 && APPEND) ? 3 : 4), 8))) void attn_partition_mfma(
+    KernelParams a) {
+    __shared__ u32x4 lds_knew[APPEND ? 8 : 1];
+    __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    if constexpr (BAL) {
+        const int w = blockIdx.y;
+        for_each_segment(a, w, g == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
+            gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, lds_knew, lds_vnew);
+        });
+    } else {
+        const int p = blockIdx.y;
+        const int b = blockIdx.z;
+        const int G = a.Hq / a.Hkv;
+        const int n = a.ctx[b];
+        if (n <= 0) {
+            if (p == 0) {
+                for (int jh = 0; jh < G; ++jh) {
+                    const size_t orow = ((size_t)b * a.Hq + g * G + jh) * kDim;
+                    a.out[orow + lane] = 0;
+                    a.out[orow + 64 + lane] = 0;
+                }
+            }
+            return;
+        }
+        const int nt = tiles_of(n);
+        const int lo = p * (a.PS / kBlock);
+        if (lo >= nt) return;
+        const int hi = min(nt, lo + a.PS / kBlock);
+        gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane,
+                                    lds_knew, lds_vnew);
+    }
+}
+
+// Tiles per chunk (even: tiles are paired for the PV products).
+#ifndef KVQ_GQA_TILES
+#define KVQ_GQA_TILES 2
+#endif
+
+template <int DT, bool BAL>
+static void launch_gqa(const KernelParams& kp, hipStream_t stream) {
+    // one wave per KV head; the KV head is the fastest grid dimension
+    const dim3 grid = BAL ? dim3((unsigned)kp.Hkv, (unsigned)kp.NW)
+                          : dim3((unsigned)kp.Hkv, (unsigned)kp.P, (unsigned)kp.B);
+    if (kp.k_new)
+        attn_partition_mfma<DT, KVQ_GQA_TILES, true, BAL><<<grid, 64, 0, stream>>>(kp);
+    else
+        attn_partition_mfma<DT, KVQ_GQA_TILES, false, BAL><<<grid, 64, 0, stream>>>(kp);
+}
+
+template <int DT>
+static void launch_gqa(const KernelParams& kp, hipStream_t stream) {
+    if (kp.NW > 0)
+        launch_gqa<DT, true>(kp, stream);
+    else
+        launch_gqa<DT, false>(kp, stream);
+}
+
+void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream) {
+    switch (dtype) {
+        case KVQ_FP8_E4M3: launch_gqa<KVQ_FP8_E4M3>(kp, stream); break;
+        case KVQ_FP8_E5M2: launch_gqa<KVQ_FP8_E5M2>(kp, stream); break;
+        default: launch_gqa<KVQ_INT8>(kp, stream); break;
+    }
+}
+
+}  // namespace kvq
