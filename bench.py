@@ -188,9 +188,9 @@ def main():
     wall = time.perf_counter() - wall0
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
-    # Region 2: the same steps again with a HIP event pair around every partition-kernel launch,
-    # on the stream it is launched on.  The events put gaps between launches, so this region
-    # gives the kernel's own duration and not the step time.
+    # Region 2: the same steps again with a HIP event pair in every partition-kernel dispatch (the
+    # library's timing hook launches it through hipExtLaunchKernel), on the stream it is launched
+    # on.  This region gives the kernel's own duration; the step time comes from region 1 alone.
     kvq.timing_begin(args.steps)
     for i in range(args.steps):
         step(i)

@@ -168,8 +168,8 @@ const char *kvq_status_string(int status);
 const char *kvq_last_error(void);
 
 /* Kernel-timing hook for benchmarks: after kvq_timing_begin(capacity), each kvq_paged_decode_attn
- * or kvq_decode_step call records a HIP event pair around its main (partition) kernel, on the
- * call's stream, for up to `capacity` calls.  kvq_timing_end() waits for the events, returns the
+ * or kvq_decode_step call times its main (partition) kernel with a HIP event pair recorded in that
+ * kernel's own dispatch (hipExtLaunchKernel), on the call's stream, for up to `capacity` calls.  kvq_timing_end() waits for the events, returns the
  * summed milliseconds and the number of timed launches, and releases the events.  Events are
  * created in kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a
  * time.  Returns KVQ_OK or KVQ_ERR_ARG / KVQ_ERR_HIP. */

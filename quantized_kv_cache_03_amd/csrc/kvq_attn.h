@@ -10,6 +10,8 @@
 // base 2 with log2(e) folded into the logit scale.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -188,8 +190,21 @@ __device__ __forceinline__ NewToken new_token(const KernelParams& a, const NewRo
 }
 
 // ------------------------------------------------------------------------------------------------
-// Partition-kernel launchers, one translation unit each.  dtype is a kvq_dtype.
-void launch_partition_mha(const KernelParams& kp, int dtype, hipStream_t stream);
-void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream);
+// Partition-kernel launchers, one translation unit each.  dtype is a kvq_dtype.  With start / stop
+// events (kernel-timing hook) the kernel is launched through hipExtLaunchKernel, which records the
+// events in the kernel's own dispatch: they time the kernel alone, as a profiler's trace does.
+void launch_partition_mha(const KernelParams& kp, int dtype, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop);
+void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop);
+
+template <typename K>
+inline void launch_timed(K kernel, dim3 grid, const KernelParams& kp, hipStream_t stream,
+                         hipEvent_t start, hipEvent_t stop) {
+    if (start)
+        hipExtLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, start, stop, 0, kp);
+    else
+        kernel<<<grid, 64, 0, stream>>>(kp);
+}
 
 }  // namespace kvq

@@ -303,29 +303,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
 #endif
 
 template <int DT, bool BAL>
-static void launch_gqa(const KernelParams& kp, hipStream_t stream) {
+static void launch_gqa(const KernelParams& kp, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     // one wave per KV head; the KV head is the fastest grid dimension
     const dim3 grid = BAL ? dim3((unsigned)kp.Hkv, (unsigned)kp.NW)
                           : dim3((unsigned)kp.Hkv, (unsigned)kp.P, (unsigned)kp.B);
     if (kp.k_new)
-        attn_partition_mfma<DT, KVQ_GQA_TILES, true, BAL><<<grid, 64, 0, stream>>>(kp);
+        launch_timed(attn_partition_mfma<DT, KVQ_GQA_TILES, true, BAL>, grid, kp, stream, t0, t1);
     else
-        attn_partition_mfma<DT, KVQ_GQA_TILES, false, BAL><<<grid, 64, 0, stream>>>(kp);
+        launch_timed(attn_partition_mfma<DT, KVQ_GQA_TILES, false, BAL>, grid, kp, stream, t0, t1);
 }
 
 template <int DT>
-static void launch_gqa(const KernelParams& kp, hipStream_t stream) {
+static void launch_gqa(const KernelParams& kp, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (kp.NW > 0)
-        launch_gqa<DT, true>(kp, stream);
+        launch_gqa<DT, true>(kp, stream, t0, t1);
     else
-        launch_gqa<DT, false>(kp, stream);
+        launch_gqa<DT, false>(kp, stream, t0, t1);
 }
 
-void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream) {
+void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
     switch (dtype) {
-        case KVQ_FP8_E4M3: launch_gqa<KVQ_FP8_E4M3>(kp, stream); break;
-        case KVQ_FP8_E5M2: launch_gqa<KVQ_FP8_E5M2>(kp, stream); break;
-        default: launch_gqa<KVQ_INT8>(kp, stream); break;
+        case KVQ_FP8_E4M3: launch_gqa<KVQ_FP8_E4M3>(kp, stream, start, stop); break;
+        case KVQ_FP8_E5M2: launch_gqa<KVQ_FP8_E5M2>(kp, stream, start, stop); break;
+        default: launch_gqa<KVQ_INT8>(kp, stream, start, stop); break;
     }
 }
 

@@ -106,12 +106,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.k_new = a.k_new;
     kp.v_new = a.v_new;
 
-    if (main_begin) (void)hipEventRecord(main_begin, stream);
     if (kp.Hq == kp.Hkv)
-        launch_partition_mha(kp, c.dtype, stream);
+        launch_partition_mha(kp, c.dtype, stream, main_begin, main_end);
     else
-        launch_partition_gqa(kp, c.dtype, stream);
-    if (main_end) (void)hipEventRecord(main_end, stream);
+        launch_partition_gqa(kp, c.dtype, stream, main_begin, main_end);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (kp.NW > 0 || kp.P > 1) {

@@ -41,8 +41,8 @@ hipError_t launch_dequant(const kvq_cache& c, const int32_t* block_tables, int32
                           float* k_out, float* v_out, hipStream_t stream);
 
 // Partition kernel (with the append of the decode step when k_new is set), then, with the balanced
-// split or num_partitions > 1, the merge kernel.  The optional events are recorded around the partition
-// kernel (kernel-timing hook).
+// split or num_partitions > 1, the merge kernel.  The optional events time the partition kernel's
+// own dispatch (kernel-timing hook).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
                          hipEvent_t main_end);
 
