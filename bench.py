@@ -11,6 +11,8 @@ memory (the 256 MB last-level cache cannot serve a step from the previous one).
 Prints one JSON line: achieved HBM GB/s of the whole step (algorithmic bytes / step time), with
 tokens/s, the roofline of the dominant kernel (the attention partition kernel, timed with HIP
 events on its own stream in a second pass) and the CPU oracle timed on this host as a baseline.
+Besides: the spread of the per-step time over ten blocks of the timed steps, the attention alone
+(kvq_paged_decode_attn without the append), and the step on one cache every time (no rotation).
 """
 from __future__ import annotations
 
@@ -63,6 +65,17 @@ def load_traffic(workload: str, digest: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, threads: int, budget_s: float, scale: float):
     """The oracle as it stands (C, fp64): append + attention for a prefix of the batch, timed on
     this host; reported in the metric's unit (algorithmic GB/s of the sample)."""
@@ -107,6 +120,7 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
               + 4 * int(((ctx + 15) // 16).sum()) + 4 * len(seqs))
     step_s = t2 - t1
     return {"value": bytes_ / step_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {len(seqs)} of {len(ctx_all)} sequences (sum ctx {int(ctx.sum())}), "
                       f"all {w.num_q_heads} heads: one append + fp64 attention, "
                       f"{step_s:.2f} s; prefill of the sample not timed ({t1 - t0:.1f} s)",
@@ -136,6 +150,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from quantized_kv_cache_03_amd import harness, kvq, workloads as W
@@ -176,17 +191,27 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Region 1: the step throughput, with nothing between the launches.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    def timed(fn, n: int, blocks: int = 1):
+        """Run fn(i) for i < n with an event at each of `blocks` block boundaries only (no event
+        between the launches inside a block); -> (total ms, per-step ms of each block)."""
+        bounds = [n * k // blocks for k in range(blocks + 1)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in bounds]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for k in range(blocks):
+            for i in range(bounds[k], bounds[k + 1]):
+                fn(i)
+            evs[k + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [evs[k].elapsed_time(evs[k + 1]) / max(1, bounds[k + 1] - bounds[k]) for k in range(blocks)
+               if bounds[k + 1] > bounds[k]]
+        return evs[0].elapsed_time(evs[-1]), per
+
+    # Region 1: the step throughput, with nothing between the launches but ten block boundaries
+    # (for the spread of the per-step time across blocks).
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_total, block_ms = timed(step, args.steps, blocks=min(10, args.steps))
     wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     # Region 2: the same steps again with a HIP event pair in every partition-kernel dispatch (the
     # library's timing hook launches it through hipExtLaunchKernel), on the stream it is launched
@@ -196,6 +221,17 @@ def main():
         step(i)
     torch.cuda.synchronize()
     main_ms, main_n = kvq.timing_end()
+
+    # Region 3: attention alone (kvq_paged_decode_attn, no append), over the rotated caches.
+    def attend(i):
+        case.cache = layers[i % len(layers)]
+        case.attention(stream=stream)
+    attn_ms = timed(attend, args.steps)[0] / args.steps
+    # Region 4: the step on one cache every time (the last-level cache keeps what it can).
+    def step_same(i):
+        case.cache = layers[0]
+        case.step(stream=stream, fused=not args.separate_calls)
+    same_ms = timed(step_same, args.steps)[0] / args.steps
     step_bytes = case.algorithmic_bytes()
     attn_bytes = case.attention_bytes()
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
@@ -248,6 +284,12 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "kernel_timing": "partition kernel timed with HIP events in a second pass over the same steps",
         "kernels_ms": {"attn_partition_avg": round(main_avg_ms, 5)},
+        "step_ms_blocks": {"blocks": len(block_ms), "p10": round(float(np.percentile(block_ms, 10)), 5),
+                           "median": round(float(np.median(block_ms)), 5),
+                           "p90": round(float(np.percentile(block_ms, 90)), 5)},
+        "attention_only": {"ms": round(attn_ms, 5),
+                           "gbs": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 2)},
+        "step_ms_same_cache": round(same_ms, 5),
         "roofline": {
             "kernel": partition_kernel(w)[0],
             "bound": "hbm",
