@@ -127,6 +127,102 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
             "tokens_per_s": len(seqs) / step_s}
 
 
+PREFILL_METRIC = "prefill attention over the 8-bit paged cache: achieved TFLOP/s (% of fp16 MFMA peak)"
+PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+
+
+def run_prefill(args, w):
+    """Prefill (causal) attention over whole prompts (or the last --prefill-rows tokens of each):
+    kvq_paged_prefill_attn after the prompt's bulk append.  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from quantized_kv_cache_03_amd import harness, kvq
+
+    w = w.scaled(name=w.name + f"-prefill{args.prefill_ctx}", batch=args.prefill_batch,
+                 context=("fixed", args.prefill_ctx))
+    case = harness.DeviceCase(w, keep_host_rows=not args.no_cpu_baseline)
+    n = int(case.ctx[0])
+    m = min(n, args.prefill_rows or n)
+    nq = [m] * case.B
+    cu_q = np.arange(case.B + 1, dtype=np.int32) * m
+    q = np.random.default_rng([w.seed, 9]).standard_normal((int(cu_q[-1]), w.num_q_heads, 128),
+                                                          dtype=np.float32).astype(np.float16)
+    q_d, cu_d = torch.from_numpy(q).cuda(), torch.from_numpy(cu_q).cuda()
+    out = torch.empty_like(q_d)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        kvq.paged_prefill_attn(case.cache, q_d, cu_d, case.bt_d, case.ctx_d, case.max_ctx, m, out=out,
+                               stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kvq.timing_begin(args.steps)
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    kms, kn = kvq.timing_end()
+    kms /= max(1, kn)
+    # algorithmic flops: QK^T and PV, 2 * 2 * 128 per (row, head, visible token); visible tokens of
+    # row j of a sequence of n tokens with m query rows: n - m + j + 1
+    visible = case.B * (m * (n - m) + m * (m + 1) // 2)
+    flops = 4 * 128 * w.num_q_heads * visible
+    per_tok = 2 * 128 + (8 if w.dtype == "int8" else 0)
+    code_bytes = case.B * n * w.num_kv_heads * per_tok
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        # the oracle as it stands (fp64) on 8 evenly spaced query rows, all heads
+        import oracle
+        threads = max(1, min(len(os.sched_getaffinity(0)), 16))
+        dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8}[w.dtype]
+        oc = oracle.Cache(dt, case.num_blocks, w.num_kv_heads, case.kv_scale)
+        oracle.append(oc, case.k_host, case.v_host, case.bt, case.ctx, case.cu)
+        T = int(cu_q[-1])
+        rows = sorted(set(np.linspace(0, T - 1, 8).astype(int).tolist()))
+        t0 = time.perf_counter()
+        ref = oracle.prefill_attn(oc, q, case.bt, case.ctx, cu_q, rows=rows, threads=threads)
+        sec = time.perf_counter() - t0
+        fl = sum(4 * 128 * w.num_q_heads * (n - m + (r % m) + 1) for r in rows)
+        cpu = {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(),
+               "sample": f"{len(rows)} of {T} query rows, all {w.num_q_heads} heads, fp64 ({sec:.2f} s)"}
+        g = out.cpu().numpy()[rows].astype(np.float64)
+        err = np.abs(g - ref[rows])
+        parity = {"rows": len(rows), "max_abs": float(err.max()),
+                  "within_gate": bool((err <= 1e-3 + 1e-2 * np.abs(ref[rows])).all())}
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": 128, "block_size": 16,
+                   "context": n, "query_rows_per_sequence": m, "kv_cache_dtype": w.dtype,
+                   "entry_points": "kvq_paged_prefill_attn"},
+        "flops": flops,
+        "kv_code_bytes": code_bytes,
+        "roofline": {"kernel": f"attn_prefill_mfma<{w.dtype}>", "bound": "mfma",
+                     "achieved": round(flops / (kms * 1e-3) / 1e12, 2), "peak": PEAK_MFMA_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (kms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms": round(kms, 5)},
+        "parity_sampled_rows": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +235,12 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--separate-calls", action="store_true",
                     help="time kvq_append + kvq_paged_decode_attn instead of the fused kvq_decode_step")
+    ap.add_argument("--prefill", action="store_true",
+                    help="measure prefill attention (kvq_paged_prefill_attn) instead of the decode step")
+    ap.add_argument("--prefill-ctx", type=int, default=4096, help="prompt length (prefill mode)")
+    ap.add_argument("--prefill-batch", type=int, default=4, help="prompts (prefill mode)")
+    ap.add_argument("--prefill-rows", type=int, default=0,
+                    help="query rows per prompt, its last tokens (0: the whole prompt)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before warmup, run one plain device-to-device copy of this many MiB (a known "
                          "amount of HBM traffic, used to calibrate memory counters)")
@@ -157,6 +259,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = W.WORKLOADS[args.workload]
+    if args.prefill:
+        run_prefill(args, w)
+        return
     if args.partition is not None:
         w = w.scaled(name=w.name, partition_size=args.partition)
     log(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype} "

@@ -149,6 +149,25 @@ int kvq_decode_step(const kvq_cache *cache, const void *k_new, const void *v_new
                     int32_t max_context_len, int32_t partition_size, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Prefill / chunked-prefill attention over the paged 8-bit cache (the same formats and arithmetic
+ * as kvq_paged_decode_attn: stored as FP8 or INT8, computed at higher precision):
+ *   sequence b brings n_b = cu_q_lens[b+1] - cu_q_lens[b] query rows, the last n_b of its
+ *   context_lens[b] tokens, whose K/V rows are already in the cache (kvq_append with the same
+ *   cu_new_lens).  Row j sits at position p = context_lens[b] - n_b + j and attends to the cache
+ *   tokens at positions 0 .. p (causal):
+ *     out[cu_q_lens[b] + j][h] = sum_{t <= p} softmax_t(sm_scale * q . k^[t]) v^[t].
+ *   Decode is the case n_b = 1; a whole prompt is n_b = context_lens[b].
+ *   q, out      : fp16 [num_q_rows][num_q_heads][128], device; num_q_rows = cu_q_lens[batch].
+ *   cu_q_lens   : int32 [batch + 1] device row offsets.
+ *   max_q_len   : host-side upper bound of n_b (sizes the grid), at most max_context_len.
+ *   Device-side contract: n_b <= context_lens[b] (rows of a sequence breaking it get zeros),
+ *   n_b <= max_q_len.  No workspace; the result is bitwise deterministic. */
+int kvq_paged_prefill_attn(const kvq_cache *cache, const void *q, void *out, int32_t num_q_heads,
+                           float sm_scale, const int32_t *cu_q_lens, int32_t num_q_rows,
+                           int32_t max_q_len, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                           const int32_t *context_lens, int32_t batch, int32_t max_context_len,
+                           void *stream);
+
 /* Dequantize the cache into dense fp32 [batch][Hkv][max_context_len][128] arrays for K and V:
  * each element is fl32(dec(code) * kv_scale) (FP8) or fl32(q * s) (INT8), one rounding.  Slots
  * t >= context_lens[b] are left untouched.  For inspection and tests; not on the decode path. */
@@ -167,12 +186,13 @@ const char *kvq_status_string(int status);
 /* Message of the last failed call on this thread ("" if none). */
 const char *kvq_last_error(void);
 
-/* Kernel-timing hook for benchmarks: after kvq_timing_begin(capacity), each kvq_paged_decode_attn
- * or kvq_decode_step call times its main (partition) kernel with a HIP event pair recorded in that
- * kernel's own dispatch (hipExtLaunchKernel), on the call's stream, for up to `capacity` calls.  kvq_timing_end() waits for the events, returns the
- * summed milliseconds and the number of timed launches, and releases the events.  Events are
- * created in kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a
- * time.  Returns KVQ_OK or KVQ_ERR_ARG / KVQ_ERR_HIP. */
+/* Kernel-timing hook for benchmarks: after kvq_timing_begin(capacity), each kvq_paged_decode_attn,
+ * kvq_decode_step or kvq_paged_prefill_attn call times its main (attention) kernel with a HIP event
+ * pair recorded in that kernel's own dispatch (hipExtLaunchKernel), on the call's stream, for up to
+ * `capacity` calls.  kvq_timing_end() waits for the events, returns the summed milliseconds and the
+ * number of timed launches, and releases the events.  Events are created in kvq_timing_begin,
+ * outside any timed region.  Not thread-safe: one timing session at a time.  Returns KVQ_OK or
+ * KVQ_ERR_ARG / KVQ_ERR_HIP. */
 int kvq_timing_begin(int32_t capacity);
 int kvq_timing_end(double *main_ms_total, int32_t *main_count);
 

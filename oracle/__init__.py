@@ -241,6 +241,32 @@ def decode_attn(cache: Cache, q, block_tables, context_lens, sm_scale: float | N
     return out
 
 
+def prefill_attn(cache: Cache, q, block_tables, context_lens, cu_q_lens, sm_scale: float | None = None,
+                 rows=None, threads: int = 1) -> np.ndarray:
+    """fp64 prefill (causal) attention.  q: fp16 [T][Hq][128], sequence b's rows cu_q_lens[b] ..
+    cu_q_lens[b+1]-1 being the last n_b of its context_lens[b] tokens; row j of b attends to the
+    tokens at positions 0 .. context_lens[b] - n_b + j.  That is decode attention over the row's
+    visible prefix, so each row is one decode_attn row with its own length and b's block table.
+    Returns [T][Hq][128] float64 (rows not in ``rows``, a list of row indices, are left NaN)."""
+    q = np.asarray(q)
+    T, Hq, _ = q.shape
+    cu = np.asarray(cu_q_lens, np.int64)
+    ctx = np.asarray(context_lens, np.int64)
+    bt = np.asarray(block_tables, np.int32)
+    seq = np.searchsorted(cu, np.arange(T), side="right") - 1   # sequence of each row
+    pos = ctx[seq] - (cu[seq + 1] - cu[seq]) + (np.arange(T) - cu[seq])
+    assert np.all(pos >= 0), "a sequence has more query rows than tokens"
+    if rows is None:
+        rows = range(T)
+    rows = list(rows)
+    out = np.full((T, Hq, DIM), np.nan, np.float64)
+    if rows:
+        sub = decode_attn(cache, q[rows], bt[seq[rows]], (pos[rows] + 1).astype(np.int32),
+                          sm_scale=sm_scale, threads=threads)
+        out[rows] = sub
+    return out
+
+
 def attn_fp16_dense(q_row, k_rows, v_rows, sm_scale: float | None = None) -> np.ndarray:
     """fp64 attention of one fp16 query row [128] over unquantized fp16 rows [n][128]."""
     qb = _fp16_bits(q_row)

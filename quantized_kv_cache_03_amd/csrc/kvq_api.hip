@@ -301,6 +301,62 @@ int kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new
                          partition_size, workspace, workspace_bytes, stream);
 }
 
+int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int32_t num_q_heads,
+                           float sm_scale, const int32_t* cu_q_lens, int32_t num_q_rows,
+                           int32_t max_q_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                           void* stream) {
+    int st = check_cache(cache);
+    if (st) return st;
+    st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
+    if (st) return st;
+    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
+        return fail(KVQ_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    num_q_heads, cache->num_kv_heads);
+    if (num_q_heads / cache->num_kv_heads > KVQ_MAX_GROUP)
+        return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
+                    num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
+    if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
+    if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
+        return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",
+                    max_context_len, max_blocks_per_seq, KVQ_BLOCK_SIZE);
+    if (num_q_rows < 0 || max_q_len < 0)
+        return fail(KVQ_ERR_ARG, "num_q_rows %d / max_q_len %d is negative", num_q_rows, max_q_len);
+    if (max_q_len > max_context_len)
+        return fail(KVQ_ERR_ARG, "max_q_len %d exceeds max_context_len %d (query rows are cache tokens)",
+                    max_q_len, max_context_len);
+    if (batch == 0 || num_q_rows == 0 || max_q_len == 0) return ok();
+    if (!q || !out || !cu_q_lens) return fail(KVQ_ERR_ARG, "q / out / cu_q_lens is NULL");
+    if (batch > 65535) return fail(KVQ_ERR_SHAPE, "batch must be at most 65535");
+    const int32_t G = num_q_heads / cache->num_kv_heads;
+    if ((int64_t)(max_q_len + 16 / G - 1) / (16 / G) > 65535)
+        return fail(KVQ_ERR_SHAPE, "max_q_len %d needs more than 65535 row tiles", max_q_len);
+
+    kvq::PrefillArgs a;
+    a.cache = cache;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.num_q_heads = num_q_heads;
+    a.sm_scale = sm_scale;
+    a.cu_q_lens = cu_q_lens;
+    a.num_q_rows = num_q_rows;
+    a.max_q_len = max_q_len;
+    a.block_tables = block_tables;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.context_lens = context_lens;
+    a.batch = batch;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (g_timing.active && g_timing.used < g_timing.capacity) {
+        const int slot = g_timing.used++;
+        ev[0] = g_timing.ev[2 * slot];
+        ev[1] = g_timing.ev[2 * slot + 1];
+    }
+    hipError_t e = kvq::launch_prefill(a, static_cast<hipStream_t>(stream), ev[0], ev[1]);
+    if (e != hipSuccess) return hip_fail(e, "kvq_paged_prefill_attn");
+    return ok();
+}
+
 int kvq_dequant(const kvq_cache* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, int32_t batch, int32_t max_context_len, float* k_out,
                 float* v_out, void* stream) {

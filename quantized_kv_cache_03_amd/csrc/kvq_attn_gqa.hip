@@ -1,5 +1,6 @@
 // kvq_attn_gqa.hip -- decode attention for grouped query heads (the MFMA kernel).
 #include "kvq_attn.h"
+#include "kvq_mfma.h"
 
 namespace kvq {
 
@@ -15,17 +16,6 @@ namespace kvq {
 //                 B = P^T in exactly the layout the S^T accumulator left it (lane: head, the same
 //                 tokens), so no transposition is needed.  P is split into fp16 hi + lo parts.
 // The online softmax keeps one running max per head (all lanes of a column agree).
-typedef _Float16 half8_v __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ half8_v join8(half2_t a, half2_t b, half2_t c, half2_t d) {
-    return half8_v{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
-template <int DT>
-__device__ __forceinline__ half8_v codes8(uint32_t w0, uint32_t w1) {
-    return join8(codes_to_f16<DT, 0>(w0), codes_to_f16<DT, 1>(w0), codes_to_f16<DT, 0>(w1),
-                 codes_to_f16<DT, 1>(w1));
-}
 
 // Replace the appended token's slot in the MFMA operand registers of its tile by the codes in LDS
 // (K: lane (token, k-group) takes chunks q4 and q4 + 4 of the token; V: the lanes of k-group

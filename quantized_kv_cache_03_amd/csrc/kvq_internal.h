@@ -31,6 +31,22 @@ struct DecodeArgs {
     const uint16_t* v_new;
 };
 
+// Launch parameters of the prefill attention, resolved by the ABI layer.
+struct PrefillArgs {
+    const kvq_cache* cache;
+    const uint16_t* q;        // fp16 bits [num_q_rows][Hq][128]
+    uint16_t* out;            // fp16 bits [num_q_rows][Hq][128]
+    int32_t num_q_heads;
+    float sm_scale;
+    const int32_t* cu_q_lens; // [B + 1]
+    int32_t num_q_rows;
+    int32_t max_q_len;
+    const int32_t* block_tables;
+    int32_t max_blocks_per_seq;
+    const int32_t* context_lens;
+    int32_t batch;
+};
+
 hipError_t launch_append(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* cu_new_lens, int32_t num_rows, const int32_t* block_tables,
                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
@@ -45,5 +61,8 @@ hipError_t launch_dequant(const kvq_cache& c, const int32_t* block_tables, int32
 // own dispatch (kernel-timing hook).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t main_begin,
                          hipEvent_t main_end);
+
+// Prefill attention kernel; the optional events time its own dispatch (kernel-timing hook).
+hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace kvq

@@ -53,6 +53,9 @@ lib.kvq_paged_decode_attn.restype = ctypes.c_int
 lib.kvq_decode_step.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32,
                                 _vp, _i32, _i32, _i32, _vp, _sz, _vp]
 lib.kvq_decode_step.restype = ctypes.c_int
+lib.kvq_paged_prefill_attn.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _i32, _f32, _vp, _i32, _i32,
+                                       _vp, _i32, _vp, _i32, _i32, _vp]
+lib.kvq_paged_prefill_attn.restype = ctypes.c_int
 lib.kvq_dequant.argtypes = [ctypes.POINTER(KvqCache), _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 lib.kvq_dequant.restype = ctypes.c_int
 lib.kvq_dtype_from_string.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]
@@ -69,7 +72,7 @@ lib.kvq_version.argtypes = []
 lib.kvq_version.restype = ctypes.c_char_p
 
 EXPORTS = ["kvq_append", "kvq_decode_workspace_size", "kvq_paged_decode_attn", "kvq_decode_step",
-           "kvq_dequant",
+           "kvq_paged_prefill_attn", "kvq_dequant",
            "kvq_dtype_from_string", "kvq_status_string", "kvq_last_error", "kvq_timing_begin",
            "kvq_timing_end", "kvq_version"]
 
@@ -223,6 +226,27 @@ def decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q
                                float(sm_scale), _ptr(block_tables), block_tables.shape[1],
                                _ptr(context_lens), B, int(max_context_len), int(partition_size),
                                _ptr(workspace), ws_bytes, _stream(stream)), "kvq_decode_step")
+    return out
+
+
+def paged_prefill_attn(cache: PagedKVCache, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                       max_q_len: int, sm_scale: float | None = None, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """kvq_paged_prefill_attn: q fp16 [T][Hq][128] (rows of sequence b at cu_q_lens[b] ..
+    cu_q_lens[b+1]-1, the last rows of its context) -> out fp16 [T][Hq][128], causal."""
+    assert q.dtype == torch.float16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM
+    T, Hq, _ = q.shape
+    B = context_lens.shape[0]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty_like(q)
+    d = cache.descriptor()
+    _check(lib.kvq_paged_prefill_attn(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
+                                      _ptr(cu_q_lens), T, int(max_q_len), _ptr(block_tables),
+                                      block_tables.shape[1], _ptr(context_lens), B,
+                                      int(max_context_len), _stream(stream)), "kvq_paged_prefill_attn")
     return out
 
 

@@ -1,0 +1,132 @@
+"""GPU parity of kvq_paged_prefill_attn (prefill / chunked-prefill attention, causal) against the
+oracle: every (row, head) of scaled-down batches, and sampled rows of full-size prompts.
+
+The cache holds every token of each sequence (the bulk append); sequence b's query rows are its
+last n_b tokens.  Gate: |gpu - oracle| <= 1e-3 + 1e-2 |oracle| elementwise, as for decode.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import OracleTwin, assert_attn_close, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from quantized_kv_cache_03_amd import harness
+    return harness
+
+
+def _case(H, name, ctx, kw, seed=0):
+    from quantized_kv_cache_03_amd import workloads as W
+    base = W.WORKLOADS[name]
+    w = base.scaled(name=f"{name}-prefill", seed=200 + base.seed + seed, batch=len(ctx),
+                    context=("list", list(ctx)), **kw)
+    return w, H.DeviceCase(w, keep_host_rows=True, spare_blocks=1)
+
+
+def _rows(case, nq, seed):
+    import torch
+    cu_q = np.zeros(len(nq) + 1, np.int32)
+    cu_q[1:] = np.cumsum(nq)
+    q = np.random.default_rng(seed).standard_normal((int(cu_q[-1]), case.w.num_q_heads, 128),
+                                                    dtype=np.float32).astype(np.float16)
+    return q, cu_q, torch.from_numpy(q).cuda(), torch.from_numpy(cu_q).cuda()
+
+
+def _run(K, case, q_d, cu_d, nq):
+    return K.paged_prefill_attn(case.cache, q_d, cu_d, case.bt_d, case.ctx_d, case.max_ctx,
+                                max(nq) if len(nq) else 0).cpu().numpy()
+
+
+CASES = [
+    # (workload, context lengths, query rows per sequence, head config)
+    ("llama2-7b-mha-e4m3", [40, 300, 129, 17, 64], [40, 33, 1, 17, 0], {"num_q_heads": 2, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-e5m2", [300, 77, 16], [70, 77, 5], {"num_q_heads": 8, "num_kv_heads": 2}),
+    ("llama2-13b-mha-int8", [90, 200, 3], [90, 31, 3], {"num_q_heads": 3, "num_kv_heads": 3}),
+    ("llama3-70b-gqa-e4m3-32k", [500, 33], [37, 33], {"num_q_heads": 16, "num_kv_heads": 2}),
+    ("llama2-13b-mha-int8", [260, 45], [100, 45], {"num_q_heads": 6, "num_kv_heads": 2}),   # G = 3
+    ("tiny-e4m3", [150, 2], [150, 2], {"num_q_heads": 16, "num_kv_heads": 1}),             # G = 16
+    ("llama3-8b-gqa-e5m2", [64, 129], [64, 50], {"num_q_heads": 4, "num_kv_heads": 2}),    # G = 2
+]
+
+
+@pytest.mark.parametrize("name,ctx,nq,kw", CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_prefill_scaled(H, name, ctx, nq, kw):
+    from quantized_kv_cache_03_amd import kvq as K
+    w, case = _case(H, name, ctx, kw)
+    say(f"[prefill] {w.name} ctx={ctx} nq={nq} Hq={w.num_q_heads} Hkv={w.num_kv_heads} {w.dtype}")
+    q, cu_q, q_d, cu_d = _rows(case, nq, seed=7)
+    out = _run(K, case, q_d, cu_d, nq)
+    twin = OracleTwin(case, range(case.B))
+    import oracle
+    ref = oracle.prefill_attn(twin.cache, q, twin.bt, twin.ctx, cu_q, threads=8)
+    st = assert_attn_close(out, ref, w.name)
+    say(f"    ok {st}")
+    # bitwise repeatable
+    again = _run(K, case, q_d, cu_d, nq)
+    np.testing.assert_array_equal(again.view(np.uint16), out.view(np.uint16))
+
+
+def test_prefill_one_row_per_sequence_is_decode(H):
+    """With one query row per sequence (the last token) prefill computes decode attention: both
+    pass the gate against the same oracle rows."""
+    from quantized_kv_cache_03_amd import kvq as K
+    import oracle
+    w, case = _case(H, "llama3-8b-gqa-e5m2", [700, 16, 1, 333], {"num_q_heads": 8, "num_kv_heads": 2})
+    say("[prefill one row]")
+    nq = [1] * case.B
+    q_d = case.q_d
+    import torch
+    cu_d = torch.arange(case.B + 1, dtype=torch.int32, device="cuda")
+    out = _run(K, case, q_d, cu_d, nq)
+    dec = case.attention().cpu().numpy()
+    twin = OracleTwin(case, range(case.B))
+    ref = twin.attention()
+    assert_attn_close(out, ref, "prefill n=1")
+    assert_attn_close(dec, ref, "decode")
+
+
+def test_prefill_rows_beyond_context_get_zeros(H):
+    """A sequence with more query rows than tokens is outside the contract: its rows are zeros and
+    the other sequences are unaffected."""
+    from quantized_kv_cache_03_amd import kvq as K
+    import oracle
+    import torch
+    w, case = _case(H, "llama2-7b-mha-e4m3", [20, 50], {"num_q_heads": 2, "num_kv_heads": 2})
+    say("[prefill beyond context]")
+    nq = [30, 50]                       # 30 > 20
+    q, cu_q, q_d, cu_d = _rows(case, nq, seed=3)
+    out = _run(K, case, q_d, cu_d, nq)
+    assert np.all(out[:30] == 0)
+    twin = OracleTwin(case, [1])
+    ref = oracle.prefill_attn(twin.cache, q[30:], twin.bt, twin.ctx, np.array([0, 50], np.int32))
+    assert_attn_close(out[30:], ref, "second sequence")
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,kw,ctx,nq", [
+    ("llama2-7b-mha-e4m3", {}, [4096, 2500], [4096, 1200]),
+    ("llama3-70b-gqa-e4m3-32k", {}, [8192], [2048]),
+])
+def test_prefill_full_size_sampled_rows(H, name, kw, ctx, nq):
+    """Prompts at model size (all heads of the workload's layer); sampled rows against the oracle,
+    every row finite."""
+    from quantized_kv_cache_03_amd import kvq as K
+    import oracle
+    w, case = _case(H, name, ctx, kw)
+    say(f"[prefill full size] {w.name} ctx={ctx} nq={nq}")
+    q, cu_q, q_d, cu_d = _rows(case, nq, seed=11)
+    out = _run(K, case, q_d, cu_d, nq)
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(1)
+    rows = sorted(set([0, int(cu_q[1]) - 1, int(cu_q[-1]) - 1] +
+                      rng.integers(0, int(cu_q[-1]), 5).tolist()))
+    twin = OracleTwin(case, range(case.B))
+    ref = oracle.prefill_attn(twin.cache, q, twin.bt, twin.ctx, cu_q, rows=rows, threads=16)
+    st = assert_attn_close(out[rows], ref[rows], w.name)
+    say(f"    ok {st}")

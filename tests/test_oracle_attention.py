@@ -207,3 +207,56 @@ def test_dense_fp16_attention_matches_torch_sdpa(oracle_mod):
             torch.from_numpy(k.astype(np.float64))[None], torch.from_numpy(v.astype(np.float64))[None],
             scale=sm)[0, 0]
         np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def _prefill_rows(ctx, nq, Hq, seed):
+    """Query rows of a chunked prefill: sequence b's last nq[b] tokens, fp16 [sum nq][Hq][128]."""
+    cu_q = np.zeros(len(ctx) + 1, np.int32)
+    cu_q[1:] = np.cumsum(nq)
+    q = np.random.default_rng(seed).standard_normal((int(cu_q[-1]), Hq, 128)).astype(np.float16)
+    return q, cu_q
+
+
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8])
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
+def test_prefill_matches_torch_causal_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
+    """Chunked prefill rows against torch float64 attention with an explicit causal mask (query row
+    j of a chunk of n rows at position ctx - n + j sees keys 0 .. ctx - n + j), on tensors decoded
+    independently of the oracle."""
+    ctx = [1, 17, 40, 33]
+    nq = [1, 17, 9, 16]  # a one-token prompt, a whole prompt, chunks over a prefix
+    w, ctx, bt, k, v, cu, s, cache, _ = _setup(oracle_mod, dtype, ctx, Hq=Hq, Hkv=Hkv, table="shuffled",
+                                               outliers=2 if dtype == INT8 else 0)
+    q, cu_q = _prefill_rows(ctx, nq, Hq, seed=5)
+    sm = float(np.float32(1.0 / np.sqrt(128.0)))
+    out = oracle_mod.prefill_attn(cache, q, bt, ctx, cu_q, sm)
+    G = Hq // Hkv
+    for b, n in enumerate(ctx):
+        kd = torch.from_numpy(_independent_dequant(dtype, k[cu[b]:cu[b + 1]], s))
+        vd = torch.from_numpy(_independent_dequant(dtype, v[cu[b]:cu[b + 1]], s))
+        kk = kd.permute(1, 0, 2).repeat_interleave(G, dim=0)      # [Hq][n][D]
+        vv = vd.permute(1, 0, 2).repeat_interleave(G, dim=0)
+        rows = q[cu_q[b]:cu_q[b + 1]].astype(np.float64)          # [m][Hq][D]
+        qq = torch.from_numpy(rows).permute(1, 0, 2)              # [Hq][m][D]
+        m = rows.shape[0]
+        qpos = np.arange(n - m, n)[:, None]
+        allowed = torch.from_numpy(np.arange(n)[None, :] <= qpos)  # [m][n]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=allowed, scale=sm)
+        np.testing.assert_allclose(out[cu_q[b]:cu_q[b + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_closed_forms_and_decode_case(oracle_mod):
+    """A prompt's first row (position 0) returns the dequantized V row of token 0 for every head;
+    one query row per sequence is decode attention, bit for bit."""
+    ctx = [5, 20, 1]
+    w, ctx, bt, k, v, cu, s, cache, qd = _setup(oracle_mod, E4M3, ctx, Hq=4, Hkv=2)
+    q, cu_q = _prefill_rows(ctx, ctx, 4, seed=6)   # whole prompts
+    out = oracle_mod.prefill_attn(cache, q, bt, ctx, cu_q)
+    for b in range(len(ctx)):
+        v0 = _independent_dequant(E4M3, v[cu[b]:cu[b] + 1], s)[0]   # [Hkv][D]
+        np.testing.assert_allclose(out[cu_q[b]], np.repeat(v0, 2, axis=0), rtol=1e-15, atol=0)
+    one = np.arange(len(ctx) + 1, dtype=np.int32)
+    dec = oracle_mod.decode_attn(cache, qd, bt, ctx)
+    pre = oracle_mod.prefill_attn(cache, qd, bt, ctx, one)
+    np.testing.assert_array_equal(pre, dec)
