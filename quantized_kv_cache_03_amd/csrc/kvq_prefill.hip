@@ -37,14 +37,16 @@ struct PrefillParams {
     int32_t Hq;
     int32_t Hkv;
     int32_t G;              // query heads per KV head
-    int32_t R;              // query rows per wave (16 / G)
-    int32_t row_tiles;      // grid extent over row tiles
+    int32_t R;              // query rows per column block (16 / G)
+    int32_t row_tiles;      // grid extent over row tiles (NB R rows each)
     float qk_scale;         // sm_scale * log2(e) (* kv_scale for FP8)
     float v_scale;          // kv_scale for FP8, 1 for INT8
 };
 
-template <int DT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void attn_prefill_mfma(
+// NB column blocks of 16 per wave (NB R consecutive rows): the K and V^T operands of a tile are
+// decoded once and feed the MFMAs of every block, which is what keeps the VALU from limiting.
+template <int DT, int NB>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 : (NB > 1 ? 2 : (DT == KVQ_INT8 ? 3 : 4)), 8))) void attn_prefill_mfma(
     PrefillParams a) {
     constexpr int TW = 2;  // tiles per chunk, paired for the PV products
     const int g = blockIdx.x;
@@ -52,162 +54,272 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int rt = a.row_tiles - 1 - (int)blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int col = lane & 15;  // column: (row jr, head hg) of the tile
+    const int col = lane & 15;  // column of each block: (row jr, head hg)
     const int q4 = lane >> 4;   // MFMA k-group / C row group
 
     const int r0 = a.cu_q[b];
     const int nq = a.cu_q[b + 1] - r0;
-    const int j0 = rt * a.R;
+    const int j0 = rt * (NB * a.R);
     if (j0 >= nq) return;
     const int n = a.ctx[b];
-    const int rows = min(a.R, nq - j0);
     const int jr = col / a.G, hg = col % a.G;
-    const bool live = jr < rows;                    // the column holds a real (row, head)
-    const size_t orow = ((size_t)(r0 + j0 + jr) * a.Hq + (size_t)g * a.G + hg) * kDim;
-    if (n < nq) {  // more query rows than tokens: outside the contract; the rows get zeros
-        if (live) {
+    bool live[NB];        // the column of block nb holds a real (row, head)
+    size_t orow[NB];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                *reinterpret_cast<half4_t*>(a.out + orow + 16 * r + 4 * q4) = half4_t{0, 0, 0, 0};
-        }
+    for (int nb = 0; nb < NB; ++nb) {
+        const int j = j0 + nb * a.R + jr;
+        live[nb] = jr < a.R && j < nq;
+        orow[nb] = ((size_t)(r0 + j) * a.Hq + (size_t)g * a.G + hg) * kDim;
+    }
+    if (n < nq) {  // more query rows than tokens: outside the contract; the rows get zeros
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            if (live[nb]) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    *reinterpret_cast<half4_t*>(a.out + orow[nb] + 16 * r + 4 * q4) = half4_t{0, 0, 0, 0};
+            }
         return;
     }
-    const int pos = n - nq + j0 + (live ? jr : 0);  // last visible position of the column
-    const int t_end = n - nq + j0 + rows;           // tokens the wave reads: up to its last row
+    const int pos_min = n - nq + j0;                 // the wave's first row: every column sees 0..pos_min
+    const int t_end = n - nq + min(nq, j0 + NB * a.R);  // tokens the wave reads: up to its last row
     const int tile_end = (t_end + kBlock - 1) / kBlock;
+    int pos[NB];  // last visible position of each block's column (padding columns: pos_min)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pos[nb] = live[nb] ? n - nq + j0 + nb * a.R + jr : pos_min;
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
     // Q^T operands: MFMA m covers dims 64 (m/2) + 16 q4 + 8 (m%2) .. +7 in k-slots 8 q4 .. +7
-    half8_v qB[4];
+    half8_v qB[NB][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) qB[m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
-    if (live) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            qB[m] = *reinterpret_cast<const half8_v*>(a.q + orow + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
+        for (int m = 0; m < 4; ++m) qB[nb][m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
+        if (live[nb]) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                qB[nb][m] = *reinterpret_cast<const half8_v*>(a.q + orow[nb] + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
+        }
     }
 
-    float m_run = kNegInf;  // running max of this lane's column (base-2 logits)
-    float l_lane = 0.0f;    // sum of this lane's weights (tokens 4 q4 .. +3 of every tile)
-    float4_t acc[8];        // O^T row blocks: dims 16 r + 4 q4 .. +3 of column col
+    float m_run[NB], l_lane[NB];  // per block: running max (base-2 logits) and this lane's weights
+    float4_t acc[NB][8];          // O^T row blocks: dims 16 r + 4 q4 .. +3 of the block's column
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = kNegInf;
+        l_lane[nb] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[nb][r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     const uint32_t k_off = 16u * (uint32_t)lane;  // chunk q4 (+4): token col, dims 16 q4 (+64)
     const uint32_t v_off = (uint32_t)col * kBlock + 4u * (uint32_t)q4;  // dim col (+16 r), tokens 4 q4
 
-    for (int tb = 0; tb < tile_end; tb += 64) {
-        const int nt_grp = min(64, tile_end - tb);
-        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
-        for (int c0 = 0; c0 < nt_grp; c0 += TW) {
-            u32x4 ka[TW], kb[TW];
-            uint32_t vd[TW][8];
-            float4_t ks4[TW], vs4[TW];
+    // Block ids in groups of 64 tiles, one per lane: ids_cur for group grp, ids_nxt for grp + 1 (loaded
+    // a group ahead, so a prefetch never waits for the table).
+    auto load_ids = [&](int group) {
+        const int t = group * 64 + lane;
+        return t < tile_end ? bt[t] : 0;
+    };
+    int grp = 0;
+    int ids_cur = load_ids(0), ids_nxt = load_ids(1);
+    // Codes of a chunk (two tiles); tiles at or past tile_end are zeros.
+    struct Chunk {
+        u32x4 ka[TW], kb[TW];
+        uint32_t vd[TW][8];
+        float4_t ks4[TW], vs4[TW];
+    };
+    auto load_chunk = [&](Chunk& ch, int t0) {
 #pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                if (c0 + i < nt_grp) {
-                    const int blk = __builtin_amdgcn_readlane(blk_lane, c0 + i);
-                    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
-                    const uint8_t* kt = a.kc + tile;
-                    const uint8_t* vt = a.vc + tile;
-                    ka[i] = ldg16(kt + k_off);
-                    kb[i] = ldg16(kt + k_off + 1024u);
+        for (int i = 0; i < TW; ++i) {
+            const int t = t0 + i;
+            if (t < tile_end) {
+                const int blk = (t >> 6) == grp ? __builtin_amdgcn_readlane(ids_cur, t & 63)
+                                                : __builtin_amdgcn_readlane(ids_nxt, t & 63);
+                const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+                const uint8_t* kt = a.kc + tile;
+                const uint8_t* vt = a.vc + tile;
+                ch.ka[i] = ldg16(kt + k_off);
+                ch.kb[i] = ldg16(kt + k_off + 1024u);
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
-                    if constexpr (DT == KVQ_INT8) {
-                        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
-                        ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
-                        vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-                    }
-                } else {
-                    ka[i] = kb[i] = u32x4{0u, 0u, 0u, 0u};
+                for (int r = 0; r < 8; ++r) ch.vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
+                if constexpr (DT == KVQ_INT8) {
+                    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
+                    ch.ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+                    ch.vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
+                }
+            } else {
+                ch.ka[i] = u32x4{0u, 0u, 0u, 0u};
+                ch.kb[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) vd[i][r] = 0u;
-                    ks4[i] = vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int r = 0; r < 8; ++r) ch.vd[i][r] = 0u;
+                if constexpr (DT == KVQ_INT8) {
+                    ch.ks4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    ch.vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 }
             }
-            // logits S^T: lane holds tokens 4 q4 .. +3 of each tile for column col; a token past
-            // the column's own position is masked
-            float z[TW][4];
-            float cmax = kNegInf;
-#pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].x, ka[i].y), qB[0], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].z, ka[i].w), qB[1], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].x, kb[i].y), qB[2], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].z, kb[i].w), qB[3], sacc, 0, 0, 0);
-                const int tok0 = (tb + c0 + i) * kBlock + 4 * q4;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    float f = a.qk_scale;
-                    if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
-                    z[i][t] = (tok0 + t <= pos) ? sacc[t] * f : kNegInf;
-                    cmax = fmaxf(cmax, z[i][t]);
-                }
-            }
-            // max over the column's tokens: the four row groups of the column.  Every column sees
-            // token 0, which the first chunk holds, so the running max is finite from then on.
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-            const float m_new = fmaxf(m_run, cmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_lane *= alpha;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+        }
+    };
 
+    // the next prefetch reads tile t: keep its group in the two id registers
+    auto ids_for = [&](int t) {
+        if ((t >> 6) > grp + 1) {
+            ++grp;
+            ids_cur = ids_nxt;
+            ids_nxt = load_ids(grp + 1);
+        }
+    };
+
+    auto compute_chunk = [&](Chunk& ch, int t0) {
+        {
+            const int tok_base = t0 * kBlock;  // first token of the chunk
+            u32x4 (&ka)[TW] = ch.ka;
+            u32x4 (&kb)[TW] = ch.kb;
+            uint32_t (&vd)[TW][8] = ch.vd;
+            float4_t (&ks4)[TW] = ch.ks4;
+            float4_t (&vs4)[TW] = ch.vs4;
+            // logits S^T for every block from the K operands decoded once
+            float z[NB][TW][4];
+            const bool all_visible = tok_base + TW * kBlock - 1 <= pos_min;  // wave-uniform
 #pragma unroll
-            for (int i = 0; i < TW; i += 2) {
-                // weights of the tile pair (i, i+1), hi and lo fp16 parts, in the B layout
-                half8_v whi, wlo;
+            for (int i = 0; i < TW; ++i) {
+                const half8_v k0 = codes8<DT>(ka[i].x, ka[i].y), k1 = codes8<DT>(ka[i].z, ka[i].w);
+                const half8_v k2 = codes8<DT>(kb[i].x, kb[i].y), k3 = codes8<DT>(kb[i].z, kb[i].w);
+                const int tok0 = tok_base + i * kBlock + 4 * q4;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qB[nb][0], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qB[nb][1], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k2, qB[nb][2], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k3, qB[nb][3], sacc, 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        float f = a.qk_scale;
+                        if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
+                        z[nb][i][t] = sacc[t] * f;
+                        // a token past the column's own position is masked
+                        if (!all_visible && tok0 + t > pos[nb]) z[nb][i][t] = kNegInf;
+                    }
+                }
+            }
+            // per block: max over the column's tokens (the four row groups of the column).  Every
+            // column sees token 0, which the first chunk holds, so the running max is finite from
+            // then on.
+            float m_new[NB];
+            bool moved = false;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                float cmax = kNegInf;
+#pragma unroll
+                for (int i = 0; i < TW; ++i)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) cmax = fmaxf(cmax, z[nb][i][t]);
+                cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+                cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+                m_new[nb] = fmaxf(m_run[nb], cmax);
+                moved |= m_new[nb] > m_run[nb];
+            }
+            if (__builtin_amdgcn_ballot_w64(moved)) {  // rescale only when some running max moved
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new[nb]);
+                    l_lane[nb] *= alpha;
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) acc[nb][r] *= alpha;
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) m_run[nb] = m_new[nb];
+
+            // weights of the tile pair, hi and lo fp16 parts, in the B layout, per block
+            half8_v whi[NB], wlo[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const float pw = __builtin_amdgcn_exp2f(z[i + u][t] - m_new);
-                        l_lane += pw;
+                        const float pw = __builtin_amdgcn_exp2f(z[nb][u][t] - m_new[nb]);
+                        l_lane[nb] += pw;
                         float w = pw;
-                        if constexpr (DT == KVQ_INT8) w = (pw > 0.0f) ? pw * vs4[i + u][t] : 0.0f;
+                        if constexpr (DT == KVQ_INT8) w = (pw > 0.0f) ? pw * vs4[u][t] : 0.0f;
                         const _Float16 hi = (_Float16)w;
-                        whi[4 * u + t] = hi;
-                        wlo[4 * u + t] = (_Float16)(w - (float)hi);
+                        whi[nb][4 * u + t] = hi;
+                        wlo[nb][4 * u + t] = (_Float16)(w - (float)hi);
                     }
                 }
-                // V codes of the slots at and past t_end are zeroed (past the context they may hold
-                // NaN codes; a zero weight alone would still give 0 * NaN)
-                uint32_t v0[8], v1[8];
-                const int valid0 = t_end - (tb + c0 + i) * kBlock - 4 * q4;
-                const int valid1 = valid0 - kBlock;
+            }
+            // V codes of the slots at and past t_end are zeroed (past the context they may hold NaN
+            // codes; a zero weight alone would still give 0 * NaN); chunks inside it need nothing
+            if (tok_base + TW * kBlock > t_end) {
+                const int valid0 = t_end - tok_base - 4 * q4;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    v0[r] = keep_bytes(vd[i][r], valid0);
-                    v1[r] = keep_bytes(vd[i + 1][r], valid1);
+                    vd[0][r] = keep_bytes(vd[0][r], valid0);
+                    vd[1][r] = keep_bytes(vd[1][r], valid0 - kBlock);
                 }
+            }
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const half8_v va8 = join8(codes_to_f16<DT, 0>(v0[r]), codes_to_f16<DT, 1>(v0[r]),
-                                              codes_to_f16<DT, 0>(v1[r]), codes_to_f16<DT, 1>(v1[r]));
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi, acc[r], 0, 0, 0);
-                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, wlo, acc[r], 0, 0, 0);
+            for (int r = 0; r < 8; ++r) {
+                const half8_v va8 = join8(codes_to_f16<DT, 0>(vd[0][r]), codes_to_f16<DT, 1>(vd[0][r]),
+                                          codes_to_f16<DT, 0>(vd[1][r]), codes_to_f16<DT, 1>(vd[1][r]));
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi[nb], acc[nb][r], 0, 0, 0);
+                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, wlo[nb], acc[nb][r], 0, 0, 0);
                 }
             }
         }
-    }
-    // sum of the column's weights over the four row groups
-    float l_sum = l_lane + __shfl_xor(l_lane, 16);
-    l_sum += __shfl_xor(l_sum, 32);
+    };
 
-    if (live) {
-        const float inv = a.v_scale / l_sum;
+    if constexpr (DT == KVQ_INT8) {
+        // the per-token scales do not fit in registers twice: one chunk at a time
+        Chunk A;
+        for (int t0 = 0; t0 < tile_end; t0 += TW) {
+            load_chunk(A, t0);
+            ids_for(t0 + TW);
+            compute_chunk(A, t0);
+        }
+    } else {
+        // Software pipeline, unrolled by two so the buffers swap roles without a register copy:
+        // the loads of the next chunk are in flight while the current one is computed.
+        Chunk A, B;
+        load_chunk(A, 0);
+        for (int t0 = 0; t0 < tile_end; t0 += 2 * TW) {
+            if (t0 + TW < tile_end) {
+                load_chunk(B, t0 + TW);
+                ids_for(t0 + 2 * TW);
+            }
+            compute_chunk(A, t0);
+            if (t0 + TW >= tile_end) break;
+            if (t0 + 2 * TW < tile_end) {
+                load_chunk(A, t0 + 2 * TW);
+                ids_for(t0 + 3 * TW);
+            }
+            compute_chunk(B, t0 + TW);
+        }
+    }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const half4_t o = {(_Float16)(acc[r][0] * inv), (_Float16)(acc[r][1] * inv),
-                               (_Float16)(acc[r][2] * inv), (_Float16)(acc[r][3] * inv)};
-            *reinterpret_cast<half4_t*>(a.out + orow + 16 * r + 4 * q4) = o;
+    for (int nb = 0; nb < NB; ++nb) {
+        // sum of the column's weights over the four row groups
+        float l_sum = l_lane[nb] + __shfl_xor(l_lane[nb], 16);
+        l_sum += __shfl_xor(l_sum, 32);
+        if (live[nb]) {
+            const float inv = a.v_scale / l_sum;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const half4_t o = {(_Float16)(acc[nb][r][0] * inv), (_Float16)(acc[nb][r][1] * inv),
+                                   (_Float16)(acc[nb][r][2] * inv), (_Float16)(acc[nb][r][3] * inv)};
+                *reinterpret_cast<half4_t*>(a.out + orow[nb] + 16 * r + 4 * q4) = o;
+            }
         }
     }
 }
+
+#ifndef KVQ_PREFILL_BLOCKS
+#define KVQ_PREFILL_BLOCKS 2
+#endif
 
 hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const kvq_cache& c = *p.cache;
@@ -227,7 +339,8 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
     a.Hkv = c.num_kv_heads;
     a.G = p.num_q_heads / c.num_kv_heads;
     a.R = 16 / a.G;
-    a.row_tiles = (p.max_q_len + a.R - 1) / a.R;
+    const int rows_per_wave = KVQ_PREFILL_BLOCKS * a.R;
+    a.row_tiles = (p.max_q_len + rows_per_wave - 1) / rows_per_wave;
     const bool fp8 = c.dtype != KVQ_INT8;
     a.qk_scale = p.sm_scale * kLog2e * (fp8 ? c.kv_scale : 1.0f);
     a.v_scale = fp8 ? c.kv_scale : 1.0f;
@@ -239,9 +352,9 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
             hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a);
     };
     switch (c.dtype) {
-        case KVQ_FP8_E4M3: go(attn_prefill_mfma<KVQ_FP8_E4M3>); break;
-        case KVQ_FP8_E5M2: go(attn_prefill_mfma<KVQ_FP8_E5M2>); break;
-        default: go(attn_prefill_mfma<KVQ_INT8>); break;
+        case KVQ_FP8_E4M3: go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS>); break;
+        case KVQ_FP8_E5M2: go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS>); break;
+        default: go(attn_prefill_mfma<KVQ_INT8, KVQ_PREFILL_BLOCKS>); break;
     }
     return hipGetLastError();
 }
