@@ -19,16 +19,11 @@ namespace kvq {
 
 // Replace the appended token's slot in the MFMA operand registers of its tile by the codes in LDS
 // (K: lane (token, k-group) takes chunks q4 and q4 + 4 of the token; V: the lanes of k-group
-// slot / 4 hold the slot's byte in each of their dwords) and store the token: its eight K chunks
-// from LDS, the whole V tile from the patched registers (each store instruction writes 256
-// contiguous bytes; the other tokens' bytes are written back unchanged -- this wave is the only
-// reader and writer of the tile), and the INT8 scales.
+// slot / 4 hold the slot's byte in each of their dwords).
 template <int DT>
-__device__ __forceinline__ void gqa_patch_and_store(const KernelParams& a, const NewToken& nt,
-                                                    const u32x4* lds_k, const uint8_t* lds_v, int blk,
-                                                    int g, int lane, uint32_t v_off, u32x4& ka,
-                                                    u32x4& kb, uint32_t (&vd)[8], float4_t& ks4,
-                                                    float4_t& vs4) {
+__device__ __forceinline__ void gqa_patch(const NewToken& nt, const u32x4* lds_k, const uint8_t* lds_v,
+                                          int lane, u32x4& ka, u32x4& kb, uint32_t (&vd)[8],
+                                          float4_t& ks4, float4_t& vs4) {
     const int col = lane & 15, q4 = lane >> 4;
     if (col == nt.slot) {
         ka = lds_k[q4];
@@ -48,30 +43,52 @@ __device__ __forceinline__ void gqa_patch_and_store(const KernelParams& a, const
                 }
         }
     }
-    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+}
+
+// The appended token's stores, held back until the wave has read all its tiles (stored between
+// tiles, into the tile just streamed, they stall the wave's later waits for loads: a CDNA wave
+// counts vector loads and stores in one counter).  The K codes wait in LDS, this lane's patched V
+// dwords in registers.
+struct PendingAppendG {
+    int blk;          // physical block of the token's tile; -1 when nothing is pending (wave-uniform)
+    int slot;         // position inside the tile
+    uint32_t vd[8];   // this lane's V dwords (dims col + 16 r, tokens 4 q4 .. +3), patched
+    float ks, vs;     // INT8 scales
+};
+
+// Store a pending token: its eight K chunks from LDS (lanes 0..7), the whole V tile from the patched
+// registers (each store instruction writes 256 contiguous bytes; the other tokens' bytes are
+// written back unchanged -- this wave is the only reader and writer of the tile), and the INT8
+// scales.
+template <int DT>
+__device__ __forceinline__ void flush_append_g(const KernelParams& a, PendingAppendG& pa,
+                                               const u32x4* lds_k, int g, int lane, uint32_t v_off) {
+    if (pa.blk < 0) return;
+    const size_t tile = ((size_t)pa.blk * a.Hkv + g) * kTileBytes;
     uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
     uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
     if (lane < 8)
-        __builtin_nontemporal_store(lds_k[lane], reinterpret_cast<u32x4*>(kt + k_byte(nt.slot, kChunk * lane)));
+        __builtin_nontemporal_store(lds_k[lane], reinterpret_cast<u32x4*>(kt + k_byte(pa.slot, kChunk * lane)));
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-        __builtin_nontemporal_store(vd[r], reinterpret_cast<uint32_t*>(vt + v_off + (uint32_t)r * 256u));
+        __builtin_nontemporal_store(pa.vd[r], reinterpret_cast<uint32_t*>(vt + v_off + (uint32_t)r * 256u));
     if constexpr (DT == KVQ_INT8) {
         if (lane == 0) {
-            const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + nt.slot;
-            const_cast<float*>(a.ks)[so] = nt.ks;
-            const_cast<float*>(a.vs)[so] = nt.vs;
+            const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
+            const_cast<float*>(a.ks)[so] = pa.ks;
+            const_cast<float*>(a.vs)[so] = pa.vs;
         }
     }
+    pa.blk = -1;
 }
 
 // APPEND: the decode step's new token is quantized by the wave whose segment holds the sequence's
-// last tile, patched into its registers and stored (one wave per (KV head, tile) reads it, so the
-// wave is the tile's only reader and writer).
+// last tile and patched into its registers; its stores are left pending until the wave's end (one
+// wave per (KV head, tile) reads it, so the wave is the tile's only reader and writer).
 template <int DT, int TW, bool APPEND>
 __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g, int n, int nt, int lo,
                                             int hi, int64_t rmul, int64_t radd, int lane,
-                                            u32x4* lds_knew, uint8_t* lds_vnew) {
+                                            u32x4* lds_knew, uint8_t* lds_vnew, PendingAppendG& pend) {
     static_assert(TW % 2 == 0, "tiles are paired for the PV products");
     const int col = lane & 15;  // query head within the group (B / C column), or A row
     const int q4 = lane >> 4;   // MFMA k-group / C row group
@@ -146,16 +163,23 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
             if constexpr (APPEND) {
                 const int inew = tile_new - (tb + c0);  // wave-uniform
                 if (inew >= 0 && inew < TW) {
+                    flush_append_g<DT>(a, pend, lds_knew, g, lane, v_off);  // an earlier token, if any
                     const NewToken ntok = new_token<DT>(a, raw, n, lane, reinterpret_cast<uint16_t*>(lds_knew));
                     lds_vnew[lane] = (uint8_t)ntok.v0;
                     lds_vnew[64 + lane] = (uint8_t)ntok.v1;
                     __builtin_amdgcn_wave_barrier();
 #pragma unroll
                     for (int i = 0; i < TW; ++i)
-                        if (i == inew)
-                            gqa_patch_and_store<DT>(a, ntok, lds_knew, lds_vnew,
-                                                    __builtin_amdgcn_readlane(blk_lane, c0 + i), g, lane,
-                                                    v_off, ka[i], kb[i], vd[i], ks4[i], vs4[i]);
+                        if (i == inew) {
+                            gqa_patch<DT>(ntok, lds_knew, lds_vnew, lane, ka[i], kb[i], vd[i], ks4[i],
+                                          vs4[i]);
+                            pend.blk = __builtin_amdgcn_readlane(blk_lane, c0 + i);
+                            pend.slot = ntok.slot;
+#pragma unroll
+                            for (int r = 0; r < 8; ++r) pend.vd[r] = vd[i][r];
+                            pend.ks = ntok.ks;
+                            pend.vs = ntok.vs;
+                        }
                 }
             }
             // logits S^T: lane holds tokens 4 q4 .. +3 of each tile for head col
@@ -258,11 +282,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
     __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
     const int lane = threadIdx.x;
     const int g = blockIdx.x;
+    // V offset of this lane: dim col (+16 r), tokens 4 q4 (as in gqa_segment)
+    const uint32_t v_off = (uint32_t)(lane & 15) * kBlock + 4u * (uint32_t)(lane >> 4);
+    PendingAppendG pend{-1, 0, {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u}, 0.0f, 0.0f};
     if constexpr (BAL) {
         const int w = blockIdx.y;
         for_each_segment(a, w, g == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
-            gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, lds_knew, lds_vnew);
+            gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, lds_knew, lds_vnew, pend);
         });
+        if constexpr (APPEND) flush_append_g<DT>(a, pend, lds_knew, g, lane, v_off);
     } else {
         const int p = blockIdx.y;
         const int b = blockIdx.z;
@@ -283,7 +311,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
         if (lo >= nt) return;
         const int hi = min(nt, lo + a.PS / kBlock);
         gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane,
-                                    lds_knew, lds_vnew);
+                                    lds_knew, lds_vnew, pend);
+        if constexpr (APPEND) flush_append_g<DT>(a, pend, lds_knew, g, lane, v_off);
     }
 }
 

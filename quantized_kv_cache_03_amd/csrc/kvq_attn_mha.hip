@@ -171,33 +171,46 @@ __device__ __forceinline__ void patch_tile(Tile& t, const NewToken& nt, const ui
     t.vb = set_byte(t.vb, nt.slot, nt.v1);
 }
 
-// Store the appended token: its K codes (16 bytes in each of the eight chunks, from LDS, written
-// by lanes 0..7) and its V codes.  A V tile row holds one dim's 16 tokens, so the token's V codes
-// are one byte in each of 128 rows; instead of 128 scattered byte stores (partial-line writes),
-// each lane rewrites its two whole 16-byte rows as loaded with the new code patched in -- the
-// other 15 bytes of each row are written back unchanged.  Only valid when this wave is the only
-// reader and writer of the tile (the MHA kernel: one wave per (query head = KV head, partition,
-// sequence)).
+// The appended token's stores, held back until the wave has read all its tiles.  Stored between
+// tiles, into the tile the wave has just streamed, they cost ~6 us per step on the Llama-2-7B batch
+// (a CDNA wave counts its vector loads and stores in one counter, so later waits for tile loads
+// also wait for the stores); held to the wave's end they cost ~1.5 us.  (Holding back the partial
+// rows likewise measured no gain, so those are written when ready.)  The K codes wait in LDS, this
+// lane's two patched V rows in registers.
+struct PendingAppend {
+    int blk;       // physical block of the token's tile; -1 when nothing is pending (wave-uniform)
+    int slot;      // position inside the tile
+    u32x4 va, vb;  // this lane's two V rows (dims lane and 64 + lane) with the new code patched in
+    float ks, vs;  // INT8 scales
+};
+
+// Store a pending token: its K codes (16 bytes in each of the eight chunks, from LDS, written by
+// lanes 0..7) and its V codes.  A V tile row holds one dim's 16 tokens, so the token's V codes are
+// one byte in each of 128 rows; each lane rewrites its two whole 16-byte rows as loaded with the
+// new code patched in -- the other 15 bytes of each row are written back unchanged.  Only valid
+// because this wave is the only reader and writer of the tile (one wave per query head = KV head
+// and tile).
 template <int DT>
-__device__ __forceinline__ void store_new_token(const KernelParams& a, const NewToken& nt,
-                                                const Tile& patched, const uint16_t* lds_k, int blk,
-                                                int g, int lane, uint32_t v_off) {
-    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+__device__ __forceinline__ void flush_append(const KernelParams& a, PendingAppend& pa,
+                                             const uint16_t* lds_k, int g, int lane) {
+    if (pa.blk < 0) return;
+    const size_t tile = ((size_t)pa.blk * a.Hkv + g) * kTileBytes;
     uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
     uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
     if (lane < 8) {
         const u32x4 kchunk = reinterpret_cast<const u32x4*>(lds_k)[lane];
-        __builtin_nontemporal_store(kchunk, reinterpret_cast<u32x4*>(kt + k_byte(nt.slot, kChunk * lane)));
+        __builtin_nontemporal_store(kchunk, reinterpret_cast<u32x4*>(kt + k_byte(pa.slot, kChunk * lane)));
     }
-    __builtin_nontemporal_store(patched.va, reinterpret_cast<u32x4*>(vt + v_off));
-    __builtin_nontemporal_store(patched.vb, reinterpret_cast<u32x4*>(vt + 1024u + v_off));
+    __builtin_nontemporal_store(pa.va, reinterpret_cast<u32x4*>(vt + 16u * (uint32_t)lane));
+    __builtin_nontemporal_store(pa.vb, reinterpret_cast<u32x4*>(vt + 1024u + 16u * (uint32_t)lane));
     if constexpr (DT == KVQ_INT8) {
         if (lane == 0) {
-            const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + nt.slot;
-            const_cast<float*>(a.ks)[so] = nt.ks;
-            const_cast<float*>(a.vs)[so] = nt.vs;
+            const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
+            const_cast<float*>(a.ks)[so] = pa.ks;
+            const_cast<float*>(a.vs)[so] = pa.vs;
         }
     }
+    pa.blk = -1;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -205,13 +218,12 @@ __device__ __forceinline__ void store_new_token(const KernelParams& a, const New
 // tiles [lo, hi) of sequence b (n tokens, nt tiles) -- ends with the final output when the segment
 // is the whole sequence, else with a partial in row h * rmul + radd.
 // APPEND: the decode step's new token (one per sequence, at position context_lens[b] - 1) is
-// quantized by the wave whose segment holds the sequence's last tile, patched into its registers
-// and stored.  Used only with one query head per KV head (grouped heads take the append kernel
-// first).
+// quantized by the wave whose segment holds the sequence's last tile and patched into its
+// registers; its stores are left pending (flush_append) until the wave has no loads left.
 template <int DT, int TW, bool APPEND>
 __device__ __forceinline__ void mha_segment(const KernelParams& a, int b, int h, int g, int n, int nt,
                                             int lo, int hi, int64_t rmul, int64_t radd, int lane,
-                                            uint32_t* lds, u32x4* lds_knew) {
+                                            uint32_t* lds, u32x4* lds_knew, PendingAppend& pend) {
     const int tk = lane >> 2;
     const size_t orow = ((size_t)b * a.Hq + h) * kDim;
     const bool has_last = hi == nt;
@@ -273,10 +285,11 @@ __device__ __forceinline__ void mha_segment(const KernelParams& a, int b, int h,
             if constexpr (APPEND) {
                 if (tb + c0 == tile_new) {
                     uint16_t* lds_k = reinterpret_cast<uint16_t*>(lds_knew);
+                    flush_append<DT>(a, pend, lds_k, g, lane);  // an earlier sequence's token, if any
                     const NewToken ntok = new_token<DT>(a, raw, n, lane, lds_k);
                     patch_tile<DT>(t[0], ntok, lds_k, lane);
-                    store_new_token<DT>(a, ntok, t[0], lds_k, __builtin_amdgcn_readlane(blk_lane, c0),
-                                        g, lane, v_off);
+                    pend = PendingAppend{__builtin_amdgcn_readlane(blk_lane, c0), ntok.slot, t[0].va,
+                                         t[0].vb, ntok.ks, ntok.vs};
                 }
             }
             const int valid = t_end - (tb + c0) * kBlock;
@@ -305,22 +318,24 @@ __device__ __forceinline__ void mha_segment(const KernelParams& a, int b, int h,
 // BAL: grid (query head, wave of the balanced split).  Otherwise grid (query head, partition,
 // sequence) with fixed partitions of PS tokens.  The balanced split runs about two waves per SIMD,
 // so its register budget is that of two waves; fixed partitions can have many more waves than fit
-// and are held to the occupancy the plain loop reaches (5, 4 for INT8 with the append).  The head is the fastest grid dimension:
-// workgroups are handed to the eight XCDs round-robin by linear id, so consecutive ids should
-// carry equal work -- all heads of one (partition or share, sequence) do.
+// and are held to the occupancy the plain loop reaches (5; 4 with the append).  The head
+// is the fastest grid dimension: workgroups are handed to the eight XCDs round-robin by linear id,
+// so consecutive ids should carry equal work -- all heads of one (partition or share, sequence) do.
 template <int DT, int TW, bool APPEND, bool BAL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((DT == KVQ_INT8 && APPEND) ? 4 : 5), 8))) void attn_partition_valu(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : (APPEND ? 4 : 5), 8))) void attn_partition_valu(
     KernelParams a) {
     __shared__ uint32_t lds[TW * 16];
     __shared__ u32x4 lds_knew[APPEND ? 8 : 1];
     const int lane = threadIdx.x;
     const int h = blockIdx.x;
     const int g = h / (a.Hq / a.Hkv);
+    PendingAppend pend{-1, 0, u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}, 0.0f, 0.0f};
     if constexpr (BAL) {
         const int w = blockIdx.y;
         for_each_segment(a, w, h == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
-            mha_segment<DT, TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, lds_knew);
+            mha_segment<DT, TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, lds_knew, pend);
         });
+        if constexpr (APPEND) flush_append<DT>(a, pend, reinterpret_cast<const uint16_t*>(lds_knew), g, lane);
     } else {
         const int p = blockIdx.y;
         const int b = blockIdx.z;
@@ -338,7 +353,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
         if (lo >= nt) return;
         const int hi = min(nt, lo + a.PS / kBlock);
         mha_segment<DT, TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane,
-                                    lds, lds_knew);
+                                    lds, lds_knew, pend);
+        if constexpr (APPEND) flush_append<DT>(a, pend, reinterpret_cast<const uint16_t*>(lds_knew), g, lane);
     }
 }
 
