@@ -9,6 +9,9 @@ step is written from its definition in fp64:
 
 * FP8 E4M3 / E5M2 codes: "Accelerating Inference with FP8 KV Cache", section "FP8 Formats: E4M3
   and E5M2" (bit layouts, per-tensor FP32 scale) and section "FP8 E4M3 KV Cache" (default scale 1.0).
+* FP8 E4M3FNUZ codes: the same page, sections "Current Hardware Support" (AMD's FP8E4M3FNUZ) and
+  "Checkpoint structure for KV scales" (float8_e4m3fnuz): bias 8, no infinities, no negative zero,
+  NaN at 0x80.
 * Online INT8 codes: "[Feature] TurboMind support W8A8 or FP8 KV Cache" (the online INT8 KV cache);
   read as symmetric INT8 with one fp32 scale per (token, head).
 * Paged cache: "[QST] Scale factors and benchmarks" (paged attention in the serving stack).
@@ -24,7 +27,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-E4M3, E5M2, INT8 = 1, 2, 3
+E4M3, E5M2, INT8, E4M3FNUZ = 1, 2, 3, 4
 BLOCK = 16
 DIM = 128
 

@@ -27,6 +27,12 @@
  *   - Exponent biases and special values follow the OCP definitions the page names: E4M3 has bias 7,
  *     no infinities and NaN only at S.1111.111 (largest finite 448); E5M2 has bias 15 with IEEE-style
  *     infinities (exponent 31, mantissa 0) and NaNs (exponent 31, mantissa != 0).
+ *   - E4M3FNUZ, the FP8 flavour the page lists for AMD GPUs ("Current Hardware Support") and as a
+ *     kv_cache_torch_dtype ("Checkpoint structure for KV scales"): the same 1/4/3 layout read as the
+ *     "finite, NaN-as-unsigned-zero" format -- bias 8, no infinities, no negative zero, and the one
+ *     NaN at 0x80 (the code -0 would have); the largest finite value is S.1111.111 = 240.  Every
+ *     other code means half of what the same bits mean in E4M3.  A NaN encodes as 0x80 and a value
+ *     that rounds to zero as 0x00, whatever its sign.
  *   - Encode direction: code = enc(fl32(x / kv_scale)); decode: value = dec(code) * kv_scale.
  *   - The quotient is one correctly rounded fp32 division; the 8-bit rounding is round-to-nearest,
  *     ties to the code with an even mantissa LSB; finite overflow and +-inf saturate to +-max;
@@ -49,6 +55,7 @@
 #define KVQO_E4M3 1
 #define KVQO_E5M2 2
 #define KVQO_INT8 3
+#define KVQO_E4M3FNUZ 4
 
 #define KVQO_BLOCK 16
 #define KVQO_DIM 128
@@ -75,7 +82,7 @@ double kvqo_fp16_to_double(uint16_t h)
 /* FP8 format parameters [TGI-FP8 "FP8 Formats: E4M3 and E5M2"] with the OCP bias reading.      */
 typedef struct {
     int ebits, mbits, bias;
-    double max_finite;   /* E4M3 448, E5M2 57344 */
+    double max_finite;   /* E4M3 448, E5M2 57344, E4M3FNUZ 240 */
     double min_normal;   /* 2^(1-bias) */
 } kvqo_fp8_fmt;
 
@@ -85,6 +92,10 @@ static int kvqo_get_fmt(int fmt, kvqo_fp8_fmt *out)
         out->ebits = 4; out->mbits = 3; out->bias = 7;
         /* largest exponent field 15 with mantissa 110b: 2^(15-7) * (1 + 6/8) = 448 (111b is NaN) */
         out->max_finite = ldexp(1.0 + 6.0 / 8.0, 15 - 7);
+    } else if (fmt == KVQO_E4M3FNUZ) {
+        out->ebits = 4; out->mbits = 3; out->bias = 8;
+        /* every exponent field is finite: 2^(15-8) * (1 + 7/8) = 240 */
+        out->max_finite = ldexp(1.0 + 7.0 / 8.0, 15 - 8);
     } else if (fmt == KVQO_E5M2) {
         out->ebits = 5; out->mbits = 2; out->bias = 15;
         /* largest finite exponent field 30 (31 is inf/NaN) with mantissa 11b: 2^15 * 1.75 = 57344 */
@@ -98,7 +109,8 @@ static int kvqo_get_fmt(int fmt, kvqo_fp8_fmt *out)
 
 /* Decode one FP8 code to its exact value.  Normal: (-1)^s 2^(e-bias) (1 + m/2^mbits);
  * subnormal (e == 0): (-1)^s 2^(1-bias) (m/2^mbits); E4M3 S.1111.111 is NaN; E5M2 exponent 31 is
- * inf (m == 0) or NaN.  Returns NAN for an unknown format.                                      */
+ * inf (m == 0) or NaN; E4M3FNUZ 0x80 (sign set, all else zero) is NaN.  Returns NAN for an unknown
+ * format.                                                                                       */
 double kvqo_fp8_decode(int fmt, uint8_t code)
 {
     kvqo_fp8_fmt F;
@@ -110,6 +122,8 @@ double kvqo_fp8_decode(int fmt, uint8_t code)
     double v;
     if (fmt == KVQO_E4M3 && e == 15 && m == 7)
         v = NAN;
+    else if (fmt == KVQO_E4M3FNUZ && code == 0x80)
+        v = NAN;
     else if (fmt == KVQO_E5M2 && e == 31)
         v = (m == 0) ? INFINITY : NAN;
     else if (e == 0)
@@ -119,19 +133,13 @@ double kvqo_fp8_decode(int fmt, uint8_t code)
     return sign ? -v : v;
 }
 
-/* Encode an fp32 value y (already divided by the scale) to FP8: saturating, round to nearest,
- * ties to even mantissa LSB.  The magnitude is clamped to max_finite first; every value that would
- * round above max_finite lies above it, and values in (max, rounding threshold] round to max anyway,
- * so clamping first is the same as rounding and then saturating.                                  */
-uint8_t kvqo_fp8_encode(int fmt, float y)
+/* The magnitude bits (the code without its sign) of a >= 0 in format F: saturating, round to
+ * nearest, ties to even mantissa LSB.  The magnitude is clamped to max_finite first; every value
+ * that would round above max_finite lies above it, and values in (max, rounding threshold] round to
+ * max anyway, so clamping first is the same as rounding and then saturating.                    */
+static uint8_t kvqo_fp8_encode_magnitude(const kvqo_fp8_fmt *Fp, double a)
 {
-    kvqo_fp8_fmt F;
-    if (kvqo_get_fmt(fmt, &F) != 0)
-        return 0;
-    uint8_t sign = signbit(y) ? 0x80 : 0x00;
-    if (isnan(y))
-        return (uint8_t)(sign | 0x7F);
-    double a = fabs((double)y);
+    kvqo_fp8_fmt F = *Fp;
     if (a > F.max_finite)
         a = F.max_finite;                       /* saturation, also for +-inf */
     if (a >= F.min_normal) {
@@ -143,12 +151,29 @@ uint8_t kvqo_fp8_encode(int fmt, float y)
             e += 1;
             M = 0.0;
         }
-        return (uint8_t)(sign | ((e + F.bias) << F.mbits) | (int)M);
+        return (uint8_t)(((e + F.bias) << F.mbits) | (int)M);
     }
     /* subnormal range: multiples of the step 2^(1-bias-mbits); M == 2^mbits is the min-normal code,
      * whose bit pattern is exactly (1 << mbits), so the same expression covers it */
     double M = nearbyint(ldexp(a, F.bias - 1 + F.mbits));
-    return (uint8_t)(sign | (int)M);
+    return (uint8_t)(int)M;
+}
+
+/* Encode an fp32 value y (already divided by the scale) to FP8: the sign bit, then the magnitude
+ * as above.  NaN encodes as sign | 0x7F (E4M3, E5M2); E4M3FNUZ has one NaN code (0x80) and no
+ * negative zero.                                                                                 */
+uint8_t kvqo_fp8_encode(int fmt, float y)
+{
+    kvqo_fp8_fmt F;
+    if (kvqo_get_fmt(fmt, &F) != 0)
+        return 0;
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y))
+        return (uint8_t)(fmt == KVQO_E4M3FNUZ ? 0x80 : (sign | 0x7F));
+    uint8_t mag = kvqo_fp8_encode_magnitude(&F, fabs((double)y));
+    if (fmt == KVQO_E4M3FNUZ && mag == 0)
+        return 0x00;                            /* unsigned zero */
+    return (uint8_t)(sign | mag);
 }
 
 /* One element of the FP8 append: y = fl32(fl32(x) / kv_scale), then encode. */
@@ -216,7 +241,7 @@ int kvqo_append(int dtype, int Hkv, uint8_t *k_cache, uint8_t *v_cache, float *k
                 const int32_t *cu_new_lens, const int32_t *block_tables, int max_blocks_per_seq,
                 const int32_t *context_lens, int batch)
 {
-    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8)
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ)
         return -1;
     int8_t qk[KVQO_DIM], qv[KVQO_DIM];
     for (int b = 0; b < batch; ++b) {
@@ -279,7 +304,7 @@ int kvqo_dequant(int dtype, int Hkv, const uint8_t *k_cache, const uint8_t *v_ca
                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
                  int batch, int max_context_len, float *k_out, float *v_out)
 {
-    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8)
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ)
         return -1;
     for (int b = 0; b < batch; ++b) {
         int n = context_lens[b];
@@ -309,7 +334,7 @@ int kvqo_decode_attn_head(int dtype, int Hkv, int Hq, const uint8_t *k_cache, co
                           int max_blocks_per_seq, const int32_t *context_lens, int b, int h,
                           double *out)
 {
-    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8)
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ)
         return -1;
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;

@@ -16,8 +16,9 @@ Generation recipe (every stream is ``numpy.random.default_rng([seed, stream, ...
   stream (4, b) : sequence b's K rows then V rows ~ N(0,1) float32, outlier channels multiplied by
              ``outlier_gain`` in float32, then rounded to float16.  The last row of each sequence is
              the token appended by the decode step.
-The per-tensor scale of the E4M3 workloads is the synthetic calibration ``fl32(amax) / 448``,
-with amax over every K and V value of the layer (a stand-in for the offline calibration tools).
+The per-tensor scale of the E4M3 workloads is the synthetic calibration ``fl32(amax) / 448``
+(``/ 240`` for E4M3FNUZ, whose largest finite value is 240), with amax over every K and V value of
+the layer (a stand-in for the offline calibration tools).
 """
 from __future__ import annotations
 
@@ -37,10 +38,10 @@ class Workload:
     batch: int
     num_q_heads: int
     num_kv_heads: int
-    dtype: str                  # "fp8_e4m3" | "fp8_e5m2" | "int8"
+    dtype: str                  # "fp8_e4m3" | "fp8_e5m2" | "int8" | "fp8_e4m3fnuz"
     context: tuple              # ("fixed", n) | ("uniform", lo, hi) | ("lognormal", median, sigma, cap)
     table: str = "sequential"   # "sequential" | "shuffled"
-    scale_rule: str = "one"     # "amax/448" | "one"
+    scale_rule: str = "one"     # "amax/448" | "amax/240" | "one"
     outliers: int = 0
     outlier_gain: float = 20.0
     partition_size: int = -1  # the balanced split (KVQ_PARTITION_BALANCED)
@@ -66,6 +67,12 @@ WORKLOADS = {
                                     ("lognormal", 2048, 1.0, 16384), outliers=4),
     "llama3-70b-gqa-e4m3-32k": Workload("llama3-70b-gqa-e4m3-32k", 5, 16, 64, 8, "fp8_e4m3",
                                         ("fixed", 32768), scale_rule="amax/448"),
+    # the AMD E4M3 flavour (FNUZ) on the Llama-2-7B and Llama-3-70B shapes
+    "llama2-7b-mha-e4m3fnuz": Workload("llama2-7b-mha-e4m3fnuz", 2, 32, 32, 32, "fp8_e4m3fnuz",
+                                       ("uniform", 512, 4096), table="shuffled",
+                                       scale_rule="amax/240"),
+    "llama3-70b-gqa-e4m3fnuz-32k": Workload("llama3-70b-gqa-e4m3fnuz-32k", 5, 16, 64, 8,
+                                            "fp8_e4m3fnuz", ("fixed", 32768), scale_rule="amax/240"),
 }
 ORDER = list(WORKLOADS)
 
@@ -152,11 +159,13 @@ def all_kv_rows(w: Workload, ctx: np.ndarray):
 
 def kv_scale(w: Workload, k: np.ndarray | None = None, v: np.ndarray | None = None,
              ctx: np.ndarray | None = None) -> float:
-    """Per-tensor scale: 1.0, or fl32(amax over K and V) / 448 (synthetic calibration)."""
+    """Per-tensor scale: 1.0, or fl32(amax over K and V) / 448 or / 240 (synthetic calibration to
+    the largest finite E4M3 or E4M3FNUZ value)."""
     if w.scale_rule == "one" or w.dtype == "int8":
         return 1.0
-    if w.scale_rule != "amax/448":
+    if w.scale_rule not in ("amax/448", "amax/240"):
         raise ValueError(w.scale_rule)
+    top = np.float32(448.0) if w.scale_rule == "amax/448" else np.float32(240.0)
     if k is not None and v is not None:
         amax = max(float(np.abs(k).max(initial=0)), float(np.abs(v).max(initial=0)))
     else:
@@ -168,4 +177,4 @@ def kv_scale(w: Workload, k: np.ndarray | None = None, v: np.ndarray | None = No
             amax = max(amax, float(np.abs(kb).max(initial=0)), float(np.abs(vb).max(initial=0)))
     if amax == 0.0:  # no values at all (every sequence empty): the default scale
         return 1.0
-    return float(np.float32(amax) / np.float32(448.0))
+    return float(np.float32(amax) / top)

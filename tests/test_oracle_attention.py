@@ -14,9 +14,10 @@ import torch
 
 from quantized_kv_cache_03_amd import workloads as W
 
-E4M3, E5M2, INT8 = 1, 2, 3
-TORCH_DT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
-DT_NAME = {E4M3: "fp8_e4m3", E5M2: "fp8_e5m2", INT8: "int8"}
+E4M3, E5M2, INT8, E4M3FNUZ = 1, 2, 3, 4
+TORCH_DT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2, E4M3FNUZ: torch.float8_e4m3fnuz}
+DT_NAME = {E4M3: "fp8_e4m3", E5M2: "fp8_e5m2", INT8: "int8", E4M3FNUZ: "fp8_e4m3fnuz"}
+SCALE_RULE = {E4M3: "amax/448", E4M3FNUZ: "amax/240"}
 
 
 def k_token_rows(k, num_blocks, Hkv):
@@ -25,10 +26,9 @@ def k_token_rows(k, num_blocks, Hkv):
     return k.reshape(num_blocks, Hkv, 8, 16, 16).transpose(0, 1, 3, 2, 4).reshape(num_blocks, Hkv, 16, 128)
 
 
-def _setup(oracle_mod, dtype, ctx, Hq=4, Hkv=2, table="sequential", scale_rule="amax/448",
-           seed=11, outliers=0):
+def _setup(oracle_mod, dtype, ctx, Hq=4, Hkv=2, table="sequential", seed=11, outliers=0):
     w = W.Workload("pin", seed, len(ctx), Hq, Hkv, DT_NAME[dtype], ("list", list(ctx)), table=table,
-                   scale_rule=scale_rule if dtype == E4M3 else "one", outliers=outliers)
+                   scale_rule=SCALE_RULE.get(dtype, "one"), outliers=outliers)
     ctx = W.context_lens(w)
     bt, nb = W.block_tables(w, ctx, spare_blocks=3)
     k, v, cu = W.all_kv_rows(w, ctx)
@@ -49,11 +49,11 @@ def _independent_dequant(dtype, rows, s):
             qq = np.where(sc[..., None] > 0, np.clip(np.rint(xf / sc[..., None]), -127, 127), 0)
         return qq.astype(np.float64) * sc[..., None].astype(np.float64)
     y = torch.from_numpy(rows.astype(np.float32)) / torch.tensor(np.float32(s))
-    codes = y.to(TORCH_DT[dtype])  # no overflow on these inputs (|y| <= 448 by the scale rule)
+    codes = y.to(TORCH_DT[dtype])  # no overflow on these inputs (|y| <= max by the scale rule)
     return codes.to(torch.float64).numpy() * np.float64(np.float32(s))
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
 def test_append_layout_and_poison(oracle_mod, dtype):
     ctx = [1, 15, 16, 17, 40]
     w, ctx, bt, k, v, cu, s, cache, q = _setup(oracle_mod, dtype, ctx, table="shuffled")
@@ -103,7 +103,7 @@ def test_append_one_token_per_sequence(oracle_mod):
     assert sorted(map(tuple, written.tolist())) == expect
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
 def test_dequant_matches_independent_decode(oracle_mod, dtype):
     ctx = [3, 16, 29]
     w, ctx, bt, k, v, cu, s, cache, q = _setup(oracle_mod, dtype, ctx, table="shuffled", outliers=2)
@@ -117,7 +117,7 @@ def test_dequant_matches_independent_decode(oracle_mod, dtype):
         assert np.all(np.isnan(ko[b, :, n:, :]))  # slots past the context are untouched
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2), (16, 2)])
 def test_attention_matches_torch_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
     ctx = [1, 2, 15, 16, 17, 33, 70]
@@ -136,7 +136,7 @@ def test_attention_matches_torch_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
         np.testing.assert_allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("dtype", [E4M3, INT8])
+@pytest.mark.parametrize("dtype", [E4M3, INT8, E4M3FNUZ])
 def test_attention_closed_forms(oracle_mod, dtype):
     ctx = [1, 2, 40]
     w, ctx, bt, k, v, cu, s, cache, q = _setup(oracle_mod, dtype, ctx, Hq=2, Hkv=2)
@@ -217,7 +217,7 @@ def _prefill_rows(ctx, nq, Hq, seed):
     return q, cu_q
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
 def test_prefill_matches_torch_causal_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
     """Chunked prefill rows against torch float64 attention with an explicit causal mask (query row

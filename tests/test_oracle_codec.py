@@ -4,6 +4,8 @@ Nothing here re-types the oracle's formulas.  The decode tables are checked agai
 from the bit-field widths printed on "Accelerating Inference with FP8 KV Cache", section "FP8
 Formats: E4M3 and E5M2" (tests/golden/fp8_formats.json) with exact rationals, (ii) torch's CPU
 float8 dtypes, and (iii) the textbook identity that an E5M2 code is the top byte of an IEEE binary16.
+E4M3FNUZ (the AMD flavour the page lists under "Current Hardware Support") is pinned the same way
+(its torch dtype is float8_e4m3fnuz) and by its relation to the already pinned E4M3 table.
 The encoder is checked by brute force: for every one of the 65,536 fp16 inputs and several scales,
 the nearest finite code over all 256 codes (ties to the even code), against torch's cast where the
 cast does not overflow, and by the round trip enc(dec(c)) == c.
@@ -16,28 +18,34 @@ import numpy as np
 import pytest
 import torch
 
-E4M3, E5M2 = 1, 2
-FMT_NAME = {E4M3: "E4M3", E5M2: "E5M2"}
-TORCH_DT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+E4M3, E5M2, E4M3FNUZ = 1, 2, 4
+FMT_NAME = {E4M3: "E4M3", E5M2: "E5M2", E4M3FNUZ: "E4M3FNUZ"}
+TORCH_DT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2, E4M3FNUZ: torch.float8_e4m3fnuz}
+FMTS = [E4M3, E5M2, E4M3FNUZ]
+NAN_CODE = {E4M3: 0x7F, E5M2: 0x7F, E4M3FNUZ: 0x80}  # the code a NaN encodes to (sign aside)
 
 
 @pytest.fixture(scope="module")
 def widths(golden_dir):
     with open(os.path.join(golden_dir, "fp8_formats.json")) as f:
         g = json.load(f)
-    return {E4M3: g["formats"]["E4M3"], E5M2: g["formats"]["E5M2"]}, g
+    return {E4M3: g["formats"]["E4M3"], E5M2: g["formats"]["E5M2"],
+            E4M3FNUZ: g["formats"]["E4M3FNUZ"]}, g
 
 
 def closed_form_value(code: int, w: dict, fmt: int):
     """Exact value (Fraction) or 'nan' / 'inf' / '-inf' from the page's field widths and the OCP
     reading: bias 2^(E-1)-1; E4M3 has no infinities and S.1111.111 is NaN; E5M2's all-ones
-    exponent is inf (mantissa 0) or NaN."""
+    exponent is inf (mantissa 0) or NaN.  FNUZ reading: bias 2^(E-1), no infinities, and the
+    negative-zero pattern is the only NaN."""
     eb, mb = w["exponent_bits"], w["mantissa_bits"]
     assert w["sign_bits"] + eb + mb == 8
-    bias = 2 ** (eb - 1) - 1
+    bias = 2 ** (eb - 1) - 1 if fmt != E4M3FNUZ else 2 ** (eb - 1)
     s = code >> (eb + mb)
     e = (code >> mb) & (2 ** eb - 1)
     m = code & (2 ** mb - 1)
+    if fmt == E4M3FNUZ and code == 0x80:
+        return "nan"
     if fmt == E4M3 and e == 2 ** eb - 1 and m == 2 ** mb - 1:
         return "nan"
     if fmt == E5M2 and e == 2 ** eb - 1:
@@ -49,7 +57,7 @@ def closed_form_value(code: int, w: dict, fmt: int):
     return -v if s else v
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_decode_table_matches_bit_layout(oracle_mod, widths, fmt):
     w = widths[0][fmt]
     table = oracle_mod.fp8_decode_table(fmt)
@@ -61,12 +69,13 @@ def test_decode_table_matches_bit_layout(oracle_mod, widths, fmt):
         elif exp in ("inf", "-inf"):
             assert np.isinf(got) and (got > 0) == (exp == "inf"), hex(c)
         else:
+            assert np.isfinite(got), (FMT_NAME[fmt], hex(c), got, exp)
             assert Fraction(float(got)) == exp, (FMT_NAME[fmt], hex(c), got, exp)
             if exp == 0:  # signed zero survives
                 assert np.signbit(got) == bool(c & 0x80)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_decode_table_matches_torch(oracle_mod, fmt):
     codes = torch.arange(256, dtype=torch.uint8)
     ref = codes.view(TORCH_DT[fmt]).to(torch.float64).numpy()
@@ -88,6 +97,22 @@ def test_e5m2_is_fp16_top_byte(oracle_mod):
     np.testing.assert_array_equal(got[ok], ref[ok])
 
 
+def test_fnuz_is_half_of_e4m3(oracle_mod):
+    """The two E4M3 flavours share the 1/4/3 layout and differ by one in the bias, so every code
+    other than the special ones (FN's NaNs 0x7F / 0xFF, FNUZ's NaN 0x80) means exactly half in
+    FNUZ of what it means in FN; FNUZ's 0x7F / 0xFF are finite, +-240: the same mantissa one binade
+    above 0x77 / 0xF7."""
+    fn = oracle_mod.fp8_decode_table(E4M3)
+    fz = oracle_mod.fp8_decode_table(E4M3FNUZ)
+    special = {0x7F, 0xFF, 0x80}
+    for c in range(256):
+        if c in special:
+            continue
+        assert fz[c] == fn[c] / 2, hex(c)
+    assert fz[0x7F] == 240.0 and fz[0xFF] == -240.0 and np.isnan(fz[0x80])
+    assert fz[0x7F] == 2 * fz[0x77] and fz[0xFF] == 2 * fz[0xF7]
+
+
 def test_spot_values(oracle_mod):
     t4 = oracle_mod.fp8_decode_table(E4M3)
     t5 = oracle_mod.fp8_decode_table(E5M2)
@@ -96,6 +121,10 @@ def test_spot_values(oracle_mod):
     assert np.isfinite(t4).sum() == 254  # no infinities, two NaNs
     assert t5[0x3C] == 1.0 and t5[0x7B] == 57344.0 and t5[0x04] == 2.0 ** -14 and t5[0x01] == 2.0 ** -16
     assert t5[0x7C] == np.inf and t5[0xFC] == -np.inf and np.isnan(t5[0x7D])
+    tz = oracle_mod.fp8_decode_table(E4M3FNUZ)
+    assert tz[0x40] == 1.0 and tz[0x7F] == 240.0 and tz[0x08] == 2.0 ** -7 and tz[0x01] == 2.0 ** -10
+    assert tz[0x00] == 0.0 and not np.signbit(tz[0x00]) and np.isnan(tz[0x80])
+    assert np.isfinite(tz).sum() == 255 and not np.signbit(tz[np.isfinite(tz) & (tz == 0)]).any()
 
 
 def test_fp16_to_double_matches_numpy(oracle_mod):
@@ -123,8 +152,9 @@ def _finite_positive_codes(fmt, widths):
 
 def brute_force_encode(fmt, y: np.ndarray, widths) -> np.ndarray:
     """Nearest finite code to each fp32 value y over all codes, ties to the even code (even mantissa
-    LSB); NaN -> sign | 0x7F; +-inf -> +-max (saturation).  Distances are taken in binary64 and
-    every row where that shows a tie is settled again in exact rational arithmetic."""
+    LSB); NaN -> sign | 0x7F (FNUZ: 0x80); +-inf -> +-max (saturation); FNUZ zero is unsigned.
+    Distances are taken in binary64 and every row where that shows a tie is settled again in exact
+    rational arithmetic."""
     codes, vals = _finite_positive_codes(fmt, widths)
     y = np.asarray(y, np.float32)
     sign = np.signbit(y).astype(np.int64) << 7
@@ -151,7 +181,12 @@ def brute_force_encode(fmt, y: np.ndarray, widths) -> np.ndarray:
         pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
         out[ii] = codes[pick]
     out[inf] = codes[np.argmax(vals)]
-    out[nan] = 0x7F
+    if fmt == E4M3FNUZ:
+        sign = np.where(out == 0, 0, sign)  # no negative zero
+        out[nan] = 0x80
+        sign[nan] = 0
+    else:
+        out[nan] = 0x7F
     return (out | sign).astype(np.uint8)
 
 
@@ -166,7 +201,7 @@ def _config1_scale():
 SCALES = [1.0, "tiny", 2.0 ** -7, 3.0, float(np.float32(1.0 / 3.0))]
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("scale", SCALES)
 def test_encoder_exhaustive_fp16_bruteforce(oracle_mod, widths, fmt, scale):
     s = np.float32(_config1_scale() if scale == "tiny" else scale)
@@ -180,7 +215,7 @@ def test_encoder_exhaustive_fp16_bruteforce(oracle_mod, widths, fmt, scale):
                            for i in bad[:8]]
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_encoder_direct_fp32_edges(oracle_mod, widths, fmt):
     """fp32 values next to every rounding midpoint, subnormal boundary and the saturation
     threshold, plus signed zeros, fp32 subnormals, inf and NaN."""
@@ -198,11 +233,11 @@ def test_encoder_direct_fp32_edges(oracle_mod, widths, fmt):
     assert bad.size == 0, [(float(y[i]), hex(got[i]), hex(exp[i])) for i in bad[:8]]
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_encoder_matches_torch_cast_without_overflow(oracle_mod, fmt):
     """torch's CPU cast rounds to nearest even but does not saturate, so compare only where
-    |y| stays below the overflow threshold (E4M3 464, E5M2 61440) and y is not NaN."""
-    thr = 464.0 if fmt == E4M3 else 61440.0
+    |y| stays below the overflow threshold (E4M3 464, E5M2 61440, E4M3FNUZ 248) and y is not NaN."""
+    thr = {E4M3: 464.0, E5M2: 61440.0, E4M3FNUZ: 248.0}[fmt]
     x = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
     for s in [1.0, 2.0 ** -7, 3.0, float(np.float32(0.1))]:
         y = x.astype(np.float32) / np.float32(s)
@@ -212,7 +247,7 @@ def test_encoder_matches_torch_cast_without_overflow(oracle_mod, fmt):
         np.testing.assert_array_equal(got, ref)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_encode_decode_roundtrip(oracle_mod, fmt):
     """Every FP8 value is exact in fp16, so enc(dec(c)) == c at scale 1 for every non-NaN code."""
     table = oracle_mod.fp8_decode_table(fmt)
@@ -238,7 +273,7 @@ def test_e5m2_unit_scale_closed_form(oracle_mod):
     np.testing.assert_array_equal(got, exp)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_default_scale_is_one(oracle_mod, golden_dir, fmt):
     """The page's default scale is 1.0: quantizing with it equals quantizing the raw value."""
     with open(os.path.join(golden_dir, "fp8_formats.json")) as f:

@@ -61,6 +61,18 @@ MUTATIONS = {
     "v-layout-token-major": (
         "return (((size_t)blk * Hkv + g) * KVQO_DIM + d) * KVQO_BLOCK + t;",
         "return (((size_t)blk * Hkv + g) * KVQO_BLOCK + t) * KVQO_DIM + d;"),
+    "fnuz-bias-7": (
+        "out->ebits = 4; out->mbits = 3; out->bias = 8;",
+        "out->ebits = 4; out->mbits = 3; out->bias = 7;"),
+    "fnuz-keeps-negative-zero": (
+        "    if (fmt == KVQO_E4M3FNUZ && mag == 0)\n        return 0x00;",
+        "    if (fmt == KVQO_E4M3FNUZ && mag == 0 && !sign)\n        return 0x00;"),
+    "fnuz-nan-as-fn": (
+        "return (uint8_t)(fmt == KVQO_E4M3FNUZ ? 0x80 : (sign | 0x7F));",
+        "return (uint8_t)(sign | 0x7F);"),
+    "fnuz-top-code-nan": (
+        "    else if (fmt == KVQO_E4M3FNUZ && code == 0x80)\n        v = NAN;",
+        "    else if (fmt == KVQO_E4M3FNUZ && (code & 0x7F) == 0x7F)\n        v = NAN;"),
     "append-position-reversed": (
         "int p = context_lens[b] - n_b + j;",
         "int p = context_lens[b] - 1 - j;"),
@@ -77,7 +89,8 @@ def _pins():
             here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fp8_formats.json")
             with open(here) as f:
                 g = json.load(f)
-            w = ({TC.E4M3: g["formats"]["E4M3"], TC.E5M2: g["formats"]["E5M2"]}, g)
+            w = ({TC.E4M3: g["formats"]["E4M3"], TC.E5M2: g["formats"]["E5M2"],
+                  TC.E4M3FNUZ: g["formats"]["E4M3FNUZ"]}, g)
         return w
 
     o = oracle
@@ -89,6 +102,8 @@ def _pins():
         lambda: TC.test_encoder_exhaustive_fp16_bruteforce(o, widths(), TC.E5M2, 2.0 ** -7),
         lambda: TC.test_encoder_direct_fp32_edges(o, widths(), TC.E4M3),
         lambda: TC.test_encoder_direct_fp32_edges(o, widths(), TC.E5M2),
+        lambda: TC.test_decode_table_matches_bit_layout(o, widths(), TC.E4M3FNUZ),
+        lambda: TC.test_encoder_direct_fp32_edges(o, widths(), TC.E4M3FNUZ),
         lambda: TI.test_int8_matches_numpy_rint(o, True),
         lambda: TI.test_int8_zero_row_and_ties(o),
         lambda: TA.test_append_layout_and_poison(o, TA.INT8),
