@@ -105,7 +105,8 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
     cu = np.zeros(len(seqs) + 1, np.int32)
     cu[1:] = np.cumsum(ctx)
     q = W.query(w)[seqs]
-    dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8}[w.dtype]
+    dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
+          "fp8_e4m3fnuz": oracle.E4M3FNUZ}[w.dtype]
     cache = oracle.Cache(dt, nb, w.num_kv_heads, scale)
     t0 = time.perf_counter()
     oracle.append(cache, k, v, bt, ctx, cu)  # the prefill of the sample's rows (single-threaded)
@@ -184,7 +185,8 @@ def run_prefill(args, w):
         # the oracle as it stands (fp64) on 8 evenly spaced query rows, all heads
         import oracle
         threads = max(1, min(len(os.sched_getaffinity(0)), 16))
-        dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8}[w.dtype]
+        dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
+          "fp8_e4m3fnuz": oracle.E4M3FNUZ}[w.dtype]
         oc = oracle.Cache(dt, case.num_blocks, w.num_kv_heads, case.kv_scale)
         oracle.append(oc, case.k_host, case.v_host, case.bt, case.ctx, case.cu)
         T = int(cu_q[-1])

@@ -9,6 +9,9 @@
  *     "FP8 Formats: E4M3 and E5M2" -- the OCP E4M3 (1/4/3 bits) and E5M2 (1/5/2 bits) layouts and a
  *                           per-tensor FP32 scaling factor;
  *     "FP8 E4M3 KV Cache" -- the scale defaults to 1.0; the names fp8 / fp8_e5m2.
+ *     "Current Hardware Support", "Checkpoint structure for KV scales" -- AMD's FP8E4M3FNUZ flavour
+ *                           (torch dtype float8_e4m3fnuz), read as the 1/4/3 layout with bias 8,
+ *                           no infinities, no negative zero and one NaN code, 0x80.
  *   "[Feature] TurboMind support W8A8 or FP8 KV Cache" (lmdeploy issue thread):
  *     the online INT8 KV cache, read here as symmetric INT8 with one fp32 scale per (token, head).
  *   "[QST] Scale factors and benchmarks" (QQQ issue thread):
@@ -18,8 +21,10 @@
  * Numerics (bit-exact contract of the cache bytes):
  *   FP8 code   = enc(fl32(fl32(x) / kv_scale)), x the fp16 input: one correctly rounded fp32
  *                division, then round to nearest with ties to the even code, finite overflow and
- *                +-inf saturating to +-max (E4M3 448, E5M2 57344), NaN -> sign|0x7F, signed zero
- *                and subnormals kept.  Decode: value = dec(code) * kv_scale.
+ *                +-inf saturating to +-max (E4M3 448, E5M2 57344, E4M3FNUZ 240), NaN -> sign|0x7F
+ *                (E4M3FNUZ: 0x80), signed zero (E4M3FNUZ: unsigned zero) and subnormals kept.
+ *                Decode: value = dec(code) * kv_scale.  The attention calls take a cache without
+ *                E4M3FNUZ NaN codes (only a NaN input writes one); kvq_dequant decodes them as NaN.
  *   INT8 codes = per (token, KV head) row of 128 values: s = fl32(amax / 127),
  *                q = clamp(rne(fl32(x / s)), -127, 127); an all-zero row gives s = 0, q = 0.
  *                Decode: value = q * s.  Inputs are assumed finite.
@@ -60,7 +65,8 @@ extern "C" {
 typedef enum {
     KVQ_FP8_E4M3 = 1, /* OCP E4M3 with per-tensor fp32 kv_scale ("fp8", "fp8_e4m3")        */
     KVQ_FP8_E5M2 = 2, /* OCP E5M2 with per-tensor fp32 kv_scale, usually 1.0 ("fp8_e5m2")  */
-    KVQ_INT8 = 3      /* symmetric INT8, one fp32 scale per (token, KV head) ("int8")      */
+    KVQ_INT8 = 3,     /* symmetric INT8, one fp32 scale per (token, KV head) ("int8")      */
+    KVQ_FP8_E4M3FNUZ = 4 /* AMD's E4M3FNUZ with per-tensor fp32 kv_scale ("fp8_e4m3fnuz")  */
 } kvq_dtype;
 
 enum {
@@ -175,8 +181,9 @@ int kvq_dequant(const kvq_cache *cache, const int32_t *block_tables, int32_t max
                 const int32_t *context_lens, int32_t batch, int32_t max_context_len, float *k_out,
                 float *v_out, void *stream);
 
-/* "fp8" | "fp8_e4m3" -> KVQ_FP8_E4M3, "fp8_e5m2" -> KVQ_FP8_E5M2, "int8" -> KVQ_INT8
- * (the --kv-cache-dtype names of "Accelerating Inference with FP8 KV Cache").
+/* "fp8" | "fp8_e4m3" -> KVQ_FP8_E4M3, "fp8_e5m2" -> KVQ_FP8_E5M2, "int8" -> KVQ_INT8,
+ * "fp8_e4m3fnuz" -> KVQ_FP8_E4M3FNUZ (the --kv-cache-dtype names and the float8_e4m3fnuz
+ * kv_cache_torch_dtype of "Accelerating Inference with FP8 KV Cache").
  * Returns KVQ_OK or KVQ_ERR_DTYPE (out untouched). */
 int kvq_dtype_from_string(const char *s, kvq_dtype *out);
 

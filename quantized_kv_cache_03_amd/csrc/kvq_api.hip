@@ -34,7 +34,8 @@ int hip_fail(hipError_t e, const char* where) {
 
 int check_cache(const kvq_cache* c) {
     if (!c) return fail(KVQ_ERR_ARG, "cache descriptor is NULL");
-    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8)
+    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8 &&
+        c->dtype != KVQ_FP8_E4M3FNUZ)
         return fail(KVQ_ERR_DTYPE, "unknown kv cache dtype %d", (int)c->dtype);
     if (c->head_dim != KVQ_HEAD_DIM)
         return fail(KVQ_ERR_SHAPE, "head_dim %d is not supported (must be %d)", c->head_dim, KVQ_HEAD_DIM);
@@ -157,6 +158,7 @@ int kvq_dtype_from_string(const char* s, kvq_dtype* out) {
     if (!strcmp(s, "fp8") || !strcmp(s, "fp8_e4m3")) *out = KVQ_FP8_E4M3;
     else if (!strcmp(s, "fp8_e5m2")) *out = KVQ_FP8_E5M2;
     else if (!strcmp(s, "int8")) *out = KVQ_INT8;
+    else if (!strcmp(s, "fp8_e4m3fnuz")) *out = KVQ_FP8_E4M3FNUZ;
     else return fail(KVQ_ERR_DTYPE, "unknown kv cache dtype name '%s'", s);
     return ok();
 }

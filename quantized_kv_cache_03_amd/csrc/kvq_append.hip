@@ -1,7 +1,8 @@
 // kvq_append.hip -- quantize new K/V rows into their paged slots.
 //
 // FP8: code = enc(fl32(x / kv_scale)) per element ("Accelerating Inference with FP8 KV Cache",
-// section "FP8 Formats: E4M3 and E5M2": E4M3/E5M2 with a per-tensor FP32 scale).
+// section "FP8 Formats: E4M3 and E5M2": E4M3/E5M2 with a per-tensor FP32 scale; section "Current
+// Hardware Support": AMD's E4M3FNUZ).
 // INT8: one fp32 scale per (token, KV head) row, s = fl32(amax / 127), q = clamp(rne(x / s))
 // (the online INT8 cache of "[Feature] TurboMind support W8A8 or FP8 KV Cache").
 //
@@ -104,6 +105,11 @@ hipError_t launch_append(const kvq_cache& c, const uint16_t* k_new, const uint16
             break;
         case KVQ_FP8_E5M2:
             append_kernel<KVQ_FP8_E5M2><<<grid, 64, 0, stream>>>(
+                c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.kv_scale, kw, vw, cu_new_lens, batch,
+                block_tables, max_blocks_per_seq, context_lens, c.num_kv_heads);
+            break;
+        case KVQ_FP8_E4M3FNUZ:
+            append_kernel<KVQ_FP8_E4M3FNUZ><<<grid, 64, 0, stream>>>(
                 c.k_cache, c.v_cache, c.k_scale, c.v_scale, c.kv_scale, kw, vw, cu_new_lens, batch,
                 block_tables, max_blocks_per_seq, context_lens, c.num_kv_heads);
             break;

@@ -57,8 +57,8 @@ struct KernelParams {
     int32_t PS;         // fixed partitions: tokens per partition
     int32_t NW;         // balanced split: waves per head row in the grid (0 for fixed partitions)
     int32_t S;          // balanced split: partial rows per query head (NW + B); row h S + w + b
-    float qk_scale;     // sm_scale * log2(e) (* kv_scale for FP8)
-    float v_scale;      // kv_scale for FP8, 1 for INT8
+    float qk_scale;     // sm_scale * log2(e) (* kv_scale * code_unit for FP8)
+    float v_scale;      // kv_scale * code_unit for FP8, 1 for INT8
     float kv_scale;     // per-tensor scale of the FP8 encoder (fused append)
     const uint16_t* k_new;  // fused append: fp16 [B][Hkv][128] new rows (else NULL)
     const uint16_t* v_new;

@@ -386,6 +386,7 @@ void launch_partition_mha(const KernelParams& kp, int dtype, hipStream_t stream,
     switch (dtype) {
         case KVQ_FP8_E4M3: launch_mha<KVQ_FP8_E4M3>(kp, stream, start, stop); break;
         case KVQ_FP8_E5M2: launch_mha<KVQ_FP8_E5M2>(kp, stream, start, stop); break;
+        case KVQ_FP8_E4M3FNUZ: launch_mha<KVQ_FP8_E4M3FNUZ>(kp, stream, start, stop); break;
         default: launch_mha<KVQ_INT8>(kp, stream, start, stop); break;
     }
 }

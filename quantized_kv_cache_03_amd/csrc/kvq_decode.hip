@@ -100,8 +100,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.NW = a.balanced_waves;
     kp.S = a.balanced_waves + a.batch;
     const bool fp8 = c.dtype != KVQ_INT8;
-    kp.qk_scale = a.sm_scale * kLog2e * (fp8 ? c.kv_scale : 1.0f);
-    kp.v_scale = fp8 ? c.kv_scale : 1.0f;
+    // the decoders give code values divided by code_unit (a power of two): fold it into the scales
+    const float unit_scale = fp8 ? c.kv_scale * code_unit(c.dtype) : 1.0f;
+    kp.qk_scale = a.sm_scale * kLog2e * unit_scale;
+    kp.v_scale = unit_scale;
     kp.kv_scale = c.kv_scale;
     kp.k_new = a.k_new;
     kp.v_new = a.v_new;

@@ -10,6 +10,18 @@
 
 namespace kvq {
 
+// The exact value of a code from the decoder's fp16 result f (code = the low byte of `code`): the
+// decoders' unit is folded back in (a power of two, exact), and E4M3FNUZ's NaN code, which the
+// attention kernels' decoder does not single out, becomes NaN.
+template <int DT>
+__device__ __forceinline__ float code_value(float f, uint32_t code) {
+    if constexpr (DT == KVQ_FP8_E4M3FNUZ) {
+        if ((code & 0xFFu) == 0x80u) return __builtin_nanf("");
+        return f * code_unit(DT);
+    }
+    return f;
+}
+
 // One wave per (tile of 16 tokens, KV head, sequence).
 template <int DT>
 __global__ __launch_bounds__(64) void dequant_kernel(
@@ -44,10 +56,9 @@ __global__ __launch_bounds__(64) void dequant_kernel(
             for (int i = 0; i < 4; ++i) {
                 const half2_t lo = codes_to_f16<DT, 0>(ws[i]);
                 const half2_t hi = codes_to_f16<DT, 1>(ws[i]);
-                o[4 * i + 0] = (float)lo.x * s;
-                o[4 * i + 1] = (float)lo.y * s;
-                o[4 * i + 2] = (float)hi.x * s;
-                o[4 * i + 3] = (float)hi.y * s;
+                const float vals[4] = {(float)lo.x, (float)lo.y, (float)hi.x, (float)hi.y};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) o[4 * i + k] = code_value<DT>(vals[k], ws[i] >> (8 * k)) * s;
             }
         }
     }
@@ -68,7 +79,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(
                 const int pos = tile_idx * kBlock + tok;
                 if (pos < n) {
                     const float s = (DT == KVQ_INT8) ? vs[sbase + tok] : kv_scale;
-                    v_out[obase + (size_t)pos * kDim + d] = vals[k] * s;
+                    v_out[obase + (size_t)pos * kDim + d] = code_value<DT>(vals[k], ws[i] >> (8 * k)) * s;
                 }
             }
         }
@@ -89,6 +100,7 @@ hipError_t launch_dequant(const kvq_cache& c, const int32_t* block_tables, int32
     switch (c.dtype) {
         case KVQ_FP8_E4M3: KVQ_DQ(KVQ_FP8_E4M3); break;
         case KVQ_FP8_E5M2: KVQ_DQ(KVQ_FP8_E5M2); break;
+        case KVQ_FP8_E4M3FNUZ: KVQ_DQ(KVQ_FP8_E4M3FNUZ); break;
         default: KVQ_DQ(KVQ_INT8); break;
     }
 #undef KVQ_DQ

@@ -2,8 +2,9 @@
 //
 // FP8 / INT8 encode and decode written from the formats' definitions ("Accelerating Inference with
 // FP8 KV Cache", section "FP8 Formats: E4M3 and E5M2": OCP E4M3 = 1/4/3 bits, E5M2 = 1/5/2 bits;
-// the online INT8 cache of "[Feature] TurboMind support W8A8 or FP8 KV Cache"), plus wave-level
-// reductions.  Nothing here is shared with the CPU oracle.
+// section "Current Hardware Support": AMD's E4M3FNUZ, the 1/4/3 layout with bias 8, no infinities,
+// no negative zero and its one NaN at 0x80; the online INT8 cache of "[Feature] TurboMind support
+// W8A8 or FP8 KV Cache"), plus wave-level reductions.  Nothing here is shared with the CPU oracle.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,21 +43,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 // steps 2^(1-bias-M), rounded to nearest even; the value 2^M steps is the smallest normal code,
 // whose bit pattern is exactly 2^M.  Magnitudes at or above the largest finite value saturate:
 // every such value either rounds to it or overflows, and overflow saturates.
+// E4M3FNUZ differs only in its constants and special codes: NaN is 0x80 and a magnitude that
+// rounds to zero is the unsigned zero 0x00.
 template <int FMT>
 __device__ __forceinline__ uint32_t encode_fp8(float y) {
 #pragma clang fp contract(off)
-    constexpr int M = (FMT == KVQ_FP8_E4M3) ? 3 : 2;
-    constexpr int BIAS = (FMT == KVQ_FP8_E4M3) ? 7 : 15;
-    constexpr uint32_t MAX_BITS = (FMT == KVQ_FP8_E4M3) ? 0x43E00000u   // 448
-                                                        : 0x47600000u;  // 57344
-    constexpr uint32_t MAX_CODE = (FMT == KVQ_FP8_E4M3) ? 0x7Eu : 0x7Bu;
+    constexpr bool FNUZ = FMT == KVQ_FP8_E4M3FNUZ;
+    constexpr int M = (FMT == KVQ_FP8_E5M2) ? 2 : 3;
+    constexpr int BIAS = (FMT == KVQ_FP8_E5M2) ? 15 : (FNUZ ? 8 : 7);
+    constexpr uint32_t MAX_BITS = (FMT == KVQ_FP8_E4M3) ? 0x43E00000u     // 448
+                                  : (FNUZ ? 0x43700000u                   // 240
+                                          : 0x47600000u);                 // 57344
+    constexpr uint32_t MAX_CODE = (FMT == KVQ_FP8_E4M3) ? 0x7Eu : (FNUZ ? 0x7Fu : 0x7Bu);
     constexpr uint32_t MIN_NORMAL_BITS = (uint32_t)(127 + 1 - BIAS) << 23;  // 2^(1-bias)
     constexpr int SH = 23 - M;
 
     const uint32_t u = __float_as_uint(y);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t a = u & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+    if (a > 0x7F800000u) return FNUZ ? 0x80u : (sign | 0x7Fu);  // NaN
     if (a >= MAX_BITS) return sign | MAX_CODE;         // saturation (covers +-inf)
     if (a >= MIN_NORMAL_BITS) {
         const uint32_t r = a + ((1u << (SH - 1)) - 1u) + ((a >> SH) & 1u);
@@ -64,7 +69,9 @@ __device__ __forceinline__ uint32_t encode_fp8(float y) {
     }
     // exact power-of-two scaling, then round half to even (v_rndne_f32)
     const float steps = __uint_as_float(a) * (float)(1u << (BIAS - 1 + M));
-    return sign | (uint32_t)__builtin_rintf(steps);
+    const uint32_t mag = (uint32_t)__builtin_rintf(steps);
+    if constexpr (FNUZ) return mag == 0u ? 0u : (sign | mag);
+    return sign | mag;
 }
 
 // INT8 code of x for a row scale s (s = fl32(amax / 127) > 0): clamp(rne(fl32(x / s)), -127, 127),
@@ -99,6 +106,22 @@ __device__ __forceinline__ half2_t e5m2x2_to_f16(uint32_t w) {
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0u, w, sel));
 }
 
+// E4M3FNUZ -> fp16 at 2^-7 of the value.  The code's exponent and mantissa fields s.eeee.mmm go to
+// the fp16 fields s.0eeee.mmm0000000; with fp16's bias 15 against the code's 8 that is the value
+// times 2^-7 exactly, the subnormal codes (e = 0, m * 2^-10) included as fp16 subnormals m * 2^-17.
+// The callers fold the 2^7 into their scales (code_unit).  The NaN code 0x80 comes out as -0: the
+// attention kernels take a cache without NaN codes (only a NaN input writes one); kvq_dequant
+// restores the NaN itself.
+template <int SEL>
+__device__ __forceinline__ half2_t e4m3fnuz_x2_to_f16(uint32_t w) {
+    typedef short short2_t __attribute__((ext_vector_type(2)));
+    constexpr uint32_t sel = (SEL == 0) ? 0x010C000Cu : 0x030C020Cu;  // codes to the halves' high bytes
+    const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
+    // one arithmetic shift per half leaves s.s.eeee.mmm0000000; clear the second sign bit
+    const short2_t sh = __builtin_bit_cast(short2_t, x) >> (short2_t){1, 1};
+    return __builtin_bit_cast(half2_t, __builtin_bit_cast(uint32_t, sh) & 0xBF80BF80u);
+}
+
 // INT8 -> fp16: put each signed byte in the low byte of a half with high byte 0x64 and its sign
 // bit flipped, which is the binary16 number 1024 + (q + 128); subtracting 1152 leaves q exactly
 // (all integers below 2048 are exact in binary16).
@@ -109,11 +132,18 @@ __device__ __forceinline__ half2_t int8x2_to_f16(uint32_t w) {
     return __builtin_bit_cast(half2_t, x) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
 }
 
+// Codes (2*SEL, 2*SEL+1) of w as fp16; each code's value is the result times code_unit(DT).
 template <int DT, int SEL>
 __device__ __forceinline__ half2_t codes_to_f16(uint32_t w) {
     if constexpr (DT == KVQ_FP8_E4M3) return e4m3x2_to_f16<SEL>(w);
     else if constexpr (DT == KVQ_FP8_E5M2) return e5m2x2_to_f16<SEL>(w);
+    else if constexpr (DT == KVQ_FP8_E4M3FNUZ) return e4m3fnuz_x2_to_f16<SEL>(w);
     else return int8x2_to_f16<SEL>(w);
+}
+
+// The factor between codes_to_f16's result and the code's value: 2^7 for E4M3FNUZ, else 1.
+__host__ __device__ constexpr float code_unit(int dtype) {
+    return dtype == KVQ_FP8_E4M3FNUZ ? 128.0f : 1.0f;
 }
 
 __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {

@@ -39,8 +39,8 @@ struct PrefillParams {
     int32_t G;              // query heads per KV head
     int32_t R;              // query rows per column block (16 / G)
     int32_t row_tiles;      // grid extent over row tiles (NB R rows each)
-    float qk_scale;         // sm_scale * log2(e) (* kv_scale for FP8)
-    float v_scale;          // kv_scale for FP8, 1 for INT8
+    float qk_scale;         // sm_scale * log2(e) (* kv_scale * code_unit for FP8)
+    float v_scale;          // kv_scale * code_unit for FP8, 1 for INT8
 };
 
 // NB column blocks of 16 per wave (NB R consecutive rows): the K and V^T operands of a tile are
@@ -342,8 +342,10 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
     const int rows_per_wave = KVQ_PREFILL_BLOCKS * a.R;
     a.row_tiles = (p.max_q_len + rows_per_wave - 1) / rows_per_wave;
     const bool fp8 = c.dtype != KVQ_INT8;
-    a.qk_scale = p.sm_scale * kLog2e * (fp8 ? c.kv_scale : 1.0f);
-    a.v_scale = fp8 ? c.kv_scale : 1.0f;
+    // the decoders give code values divided by code_unit (a power of two): fold it into the scales
+    const float unit_scale = fp8 ? c.kv_scale * code_unit(c.dtype) : 1.0f;
+    a.qk_scale = p.sm_scale * kLog2e * unit_scale;
+    a.v_scale = unit_scale;
     const dim3 grid((unsigned)a.Hkv, (unsigned)a.row_tiles, (unsigned)p.batch);
     auto go = [&](auto kernel) {
         if (start)
@@ -354,6 +356,7 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
     switch (c.dtype) {
         case KVQ_FP8_E4M3: go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS>); break;
         case KVQ_FP8_E5M2: go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS>); break;
+        case KVQ_FP8_E4M3FNUZ: go(attn_prefill_mfma<KVQ_FP8_E4M3FNUZ, KVQ_PREFILL_BLOCKS>); break;
         default: go(attn_prefill_mfma<KVQ_INT8, KVQ_PREFILL_BLOCKS>); break;
     }
     return hipGetLastError();

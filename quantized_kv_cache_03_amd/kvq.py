@@ -13,10 +13,11 @@ from dataclasses import dataclass
 
 import torch
 
-FP8_E4M3, FP8_E5M2, INT8 = 1, 2, 3
+FP8_E4M3, FP8_E5M2, INT8, FP8_E4M3FNUZ = 1, 2, 3, 4
 HEAD_DIM = 128
 BLOCK_SIZE = 16
-DTYPE_NAMES = {"fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3, "fp8_e5m2": FP8_E5M2, "int8": INT8}
+DTYPE_NAMES = {"fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3, "fp8_e5m2": FP8_E5M2, "int8": INT8,
+               "fp8_e4m3fnuz": FP8_E4M3FNUZ}
 
 OK, ERR_ARG, ERR_DTYPE, ERR_SHAPE, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 

@@ -54,9 +54,11 @@ def test_dtype_names(K):
     assert K.dtype_from_string("fp8_e4m3") == K.FP8_E4M3
     assert K.dtype_from_string("fp8_e5m2") == K.FP8_E5M2
     assert K.dtype_from_string("int8") == K.INT8
-    with pytest.raises(K.KvqError) as e:
-        K.dtype_from_string("fp8_e4m3fnuz")
-    assert e.value.status == K.ERR_DTYPE
+    assert K.dtype_from_string("fp8_e4m3fnuz") == K.FP8_E4M3FNUZ
+    for bad in ("fp8_e4m3fn", "e4m3", "FP8", ""):
+        with pytest.raises(K.KvqError) as e:
+            K.dtype_from_string(bad)
+        assert e.value.status == K.ERR_DTYPE
 
 
 def _cache(K, **kw):

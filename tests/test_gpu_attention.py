@@ -40,6 +40,9 @@ CASES = [
     ("llama2-13b-mha-int8", [700, 33], {"num_q_heads": 6, "num_kv_heads": 2}),
     ("tiny-e4m3", [300, 2], {"num_q_heads": 16, "num_kv_heads": 1}),
     ("llama3-8b-gqa-e5m2", [100, 517], {"num_q_heads": 4, "num_kv_heads": 2}),
+    # the E4M3FNUZ mode, on both kernels
+    ("llama2-7b-mha-e4m3fnuz", [900, 33, 1600], {"num_q_heads": 4, "num_kv_heads": 4}),
+    ("llama3-70b-gqa-e4m3fnuz-32k", [2100, 7], {"num_q_heads": 16, "num_kv_heads": 2}),
 ]
 
 

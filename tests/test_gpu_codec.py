@@ -8,7 +8,8 @@ from gpu_common import say
 
 pytestmark = pytest.mark.gpu
 
-FMT = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8}
+FMT = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
+       "fp8_e4m3fnuz": oracle.E4M3FNUZ}
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +21,7 @@ def K():
     return kvq
 
 
-@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2", "int8"])
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2", "int8", "fp8_e4m3fnuz"])
 def test_dequant_every_code(K, dtype):
     import torch
     say(f"[dequant every code] {dtype}")
@@ -60,7 +61,7 @@ def test_dequant_every_code(K, dtype):
                                       err_msg=f"{name} values (bitwise, signed zero included)")
 
 
-@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2"])
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2", "fp8_e4m3fnuz"])
 @pytest.mark.parametrize("scale", [1.0, "tiny", 2.0 ** -7, 3.0, float(np.float32(1.0 / 3.0))])
 def test_append_every_fp16_input(K, dtype, scale):
     """One 512-token sequence of one KV head holds exactly the 65,536 fp16 bit patterns (K in

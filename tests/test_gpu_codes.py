@@ -1,0 +1,88 @@
+"""GPU parity of attention on caches written code by code (not through the encoder).
+
+Every format's smallest-magnitude codes are drawn on purpose: the subnormal and lowest normal
+binades, with a per-tensor scale that lifts them to values of order one, so that a decoder or a
+product that flushed subnormal inputs to zero, or mis-scaled the lowest binade, moves the output by
+far more than the gate.  E5M2's subnormals decode to binary16 subnormals, and the E4M3FNUZ decoder
+produces binary16 subnormals for its own; E4M3's decode to binary16 normals.  INT8 takes codes
+over the whole [-127, 127] range with random per-token scales.  Decode (balanced split and fixed
+partitions) and prefill both run on the same cache, for one query head per KV head and for groups
+of 4 and 8, against the oracle on the same codes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_common import DT, assert_attn_close, say
+
+pytestmark = pytest.mark.gpu
+
+# codes of the two lowest binades (exponent field 0 or 1), both signs, and the scale that maps
+# them to [1/8, 2): E4M3 bias 7 (values m 2^-9 and 2^-6 (1 + m/8)), E5M2 bias 15 (m 2^-16 and
+# 2^-14 (1 + m/4)), E4M3FNUZ bias 8 (m 2^-10 and 2^-7 (1 + m/8)); FNUZ's 0x80 is its NaN.
+LOW = {
+    "fp8_e4m3": ([c | s for s in (0, 0x80) for c in range(0x00, 0x10)], 2.0 ** 6),
+    "fp8_e5m2": ([c | s for s in (0, 0x80) for c in range(0x00, 0x08)], 2.0 ** 14),
+    "fp8_e4m3fnuz": ([c | s for s in (0, 0x80) for c in range(0x00, 0x10) if (c | s) != 0x80], 2.0 ** 7),
+}
+
+
+def _codes(dtype, shape, r):
+    if dtype == "int8":
+        return r.integers(-127, 128, size=shape).astype(np.int8).view(np.uint8)
+    pool = np.array(LOW[dtype][0], np.uint8)
+    return pool[r.integers(0, len(pool), size=shape)]
+
+
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2", "fp8_e4m3fnuz", "int8"])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 2)])
+def test_attention_on_low_binade_codes(dtype, Hq, Hkv):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from quantized_kv_cache_03_amd import kvq as K
+    say(f"[low-binade codes] {dtype} Hq={Hq} Hkv={Hkv}")
+    r = np.random.default_rng([17, Hq, Hkv, len(dtype)])
+    ctx = np.array([700, 1, 16, 129, 1500], np.int32)
+    nblk = (ctx + 15) // 16
+    nb = int(nblk.sum()) + 1
+    bt = np.full((len(ctx), int(nblk.max())), -1, np.int32)
+    ids = r.permutation(nb)
+    o = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = ids[o:o + n]
+        o += int(n)
+    kcodes = _codes(dtype, (nb, Hkv, 16 * 128), r)
+    vcodes = _codes(dtype, (nb, Hkv, 16 * 128), r)
+    ks = vs = None
+    scale = 1.0
+    if dtype == "int8":
+        ks = r.uniform(2.0 ** -9, 2.0 ** -6, (nb, Hkv, 16)).astype(np.float32)
+        vs = r.uniform(2.0 ** -9, 2.0 ** -6, (nb, Hkv, 16)).astype(np.float32)
+    else:
+        scale = LOW[dtype][1]
+    oc = oracle.Cache(DT[dtype], nb, Hkv, scale, kcodes, vcodes, ks, vs)
+    dc = K.PagedKVCache.allocate(dtype, nb, Hkv, scale)
+    dc.k_cache.copy_(torch.from_numpy(kcodes).view(dc.k_cache.shape))
+    dc.v_cache.copy_(torch.from_numpy(vcodes).view(dc.v_cache.shape))
+    if ks is not None:
+        dc.k_scale.copy_(torch.from_numpy(ks))
+        dc.v_scale.copy_(torch.from_numpy(vs))
+    q = r.standard_normal((len(ctx), Hq, 128), dtype=np.float32).astype(np.float16)
+    bt_d, ctx_d, q_d = torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), torch.from_numpy(q).cuda()
+    L = int(ctx.max())
+    ref = oracle.decode_attn(oc, q, bt, ctx, threads=8)
+    for ps in (K.PARTITION_BALANCED, 0, 64):
+        out = K.paged_decode_attn(dc, q_d, bt_d, ctx_d, L, partition_size=ps).cpu().numpy()
+        st = assert_attn_close(out, ref, f"{dtype} decode partition {ps}")
+        say(f"    decode partition {ps}: {st}")
+    # prefill: the last nq tokens of each sequence as query rows
+    nq = np.minimum(ctx, np.array([40, 1, 16, 17, 33], np.int32))
+    cu_q = np.zeros(len(ctx) + 1, np.int32)
+    cu_q[1:] = np.cumsum(nq)
+    qp = r.standard_normal((int(cu_q[-1]), Hq, 128), dtype=np.float32).astype(np.float16)
+    outp = K.paged_prefill_attn(dc, torch.from_numpy(qp).cuda(), torch.from_numpy(cu_q).cuda(), bt_d,
+                                ctx_d, L, int(nq.max())).cpu().numpy()
+    refp = oracle.prefill_attn(oc, qp, bt, ctx, cu_q, threads=8)
+    st = assert_attn_close(outp, refp, f"{dtype} prefill")
+    say(f"    prefill: {st}")

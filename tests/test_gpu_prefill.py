@@ -52,6 +52,8 @@ CASES = [
     ("llama2-13b-mha-int8", [260, 45], [100, 45], {"num_q_heads": 6, "num_kv_heads": 2}),   # G = 3
     ("tiny-e4m3", [150, 2], [150, 2], {"num_q_heads": 16, "num_kv_heads": 1}),             # G = 16
     ("llama3-8b-gqa-e5m2", [64, 129], [64, 50], {"num_q_heads": 4, "num_kv_heads": 2}),    # G = 2
+    ("llama2-7b-mha-e4m3fnuz", [200, 37], [70, 37], {"num_q_heads": 2, "num_kv_heads": 2}),
+    ("llama3-70b-gqa-e4m3fnuz-32k", [260, 16], [100, 16], {"num_q_heads": 16, "num_kv_heads": 2}),
 ]
 
 
