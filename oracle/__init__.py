@@ -14,10 +14,13 @@ step is written from its definition in fp64:
   NaN at 0x80.
 * Online INT8 codes: "[Feature] TurboMind support W8A8 or FP8 KV Cache" (the online INT8 KV cache);
   read as symmetric INT8 with one fp32 scale per (token, head).
+* Online INT4 codes: the same thread names INT4 next to INT8; read as asymmetric 4-bit codes with
+  one fp32 (scale, zero point) pair per (token, head), two codes per byte.
 * Paged cache: "[QST] Scale factors and benchmarks" (paged attention in the serving stack).
 
-Layouts are those the C file documents: K codes ``[num_blocks][Hkv][16][128]``, V codes
-``[num_blocks][Hkv][128][16]``, INT8 scales ``[num_blocks][Hkv][16]``.
+Layouts are those the C file documents: K codes ``[num_blocks][Hkv][8][16][16]`` (16-dim chunks),
+V codes ``[num_blocks][Hkv][128][16]``, INT8 scales ``[num_blocks][Hkv][16]``; INT4 tiles are half
+the size (two codes per byte) and its (scale, zero point) pairs are ``[num_blocks][Hkv][16][2]``.
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-E4M3, E5M2, INT8, E4M3FNUZ = 1, 2, 3, 4
+E4M3, E5M2, INT8, E4M3FNUZ, INT4 = 1, 2, 3, 4, 5
 BLOCK = 16
 DIM = 128
 
@@ -71,6 +74,7 @@ def load(path: str):
     L.kvqo_fp8_quantize_array.argtypes = [_c_int, _u16p, _c_int, _c_float, _u8p]
     L.kvqo_fp16_to_double_array.argtypes = [_u16p, _c_int, _f64p]
     L.kvqo_int8_quantize_rows.argtypes = [_u16p, _c_int, _c_int, _i8p, _f32p]
+    L.kvqo_int4_quantize_rows.argtypes = [_u16p, _c_int, _c_int, _u8p, _f32p, _f32p]
     L.kvqo_append.argtypes = [_c_int, _c_int, _u8p, _u8p, _f32p, _f32p, _c_float, _u16p, _u16p,
                               _i32p, _i32p, _c_int, _i32p, _c_int]
     L.kvqo_append.restype = _c_int
@@ -151,6 +155,24 @@ def int8_quantize_rows(x_fp16) -> tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
+def int4_quantize_rows(x_fp16) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Rows of the last axis -> (uint8 codes 0..15, fp32 scales, fp32 zero points)."""
+    bits = _fp16_bits(x_fp16)
+    n = bits.shape[-1]
+    rows = bits.size // n
+    q = np.empty(bits.shape, np.uint8)
+    s = np.empty(bits.shape[:-1], np.float32)
+    z = np.empty(bits.shape[:-1], np.float32)
+    lib().kvqo_int4_quantize_rows(_ptr(bits.reshape(-1), _u16p), rows, n, _ptr(q.reshape(-1), _u8p),
+                                  _ptr(s.reshape(-1), _f32p), _ptr(z.reshape(-1), _f32p))
+    return q, s, z
+
+
+def tile_bytes(dtype: int) -> int:
+    """Bytes of one (block, KV head) tile of K (or of V) codes."""
+    return BLOCK * DIM // 2 if dtype == INT4 else BLOCK * DIM
+
+
 # ---------------------------------------------------------------------------------------------
 # paged cache
 class Cache:
@@ -162,12 +184,12 @@ class Cache:
         self.num_blocks = num_blocks
         self.Hkv = num_kv_heads
         self.kv_scale = float(np.float32(kv_scale))
-        shape = (num_blocks, num_kv_heads, BLOCK * DIM)
+        shape = (num_blocks, num_kv_heads, tile_bytes(dtype))
         fill = 0x7F if poison else 0
         self.k = np.full(shape, fill, np.uint8) if k_codes is None else np.ascontiguousarray(k_codes, np.uint8).reshape(shape)
         self.v = np.full(shape, fill, np.uint8) if v_codes is None else np.ascontiguousarray(v_codes, np.uint8).reshape(shape)
-        if dtype == INT8:
-            sshape = (num_blocks, num_kv_heads, BLOCK)
+        if dtype in (INT8, INT4):
+            sshape = (num_blocks, num_kv_heads, BLOCK) + ((2,) if dtype == INT4 else ())
             self.ks = np.full(sshape, np.nan, np.float32) if k_scale is None else np.ascontiguousarray(k_scale, np.float32).reshape(sshape)
             self.vs = np.full(sshape, np.nan, np.float32) if v_scale is None else np.ascontiguousarray(v_scale, np.float32).reshape(sshape)
         else:

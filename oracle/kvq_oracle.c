@@ -19,6 +19,11 @@
  *       the online INT8 KV cache variant.  The thread gives no formula; the reading used here is
  *       symmetric INT8 with one fp32 scale per (token, head): s = amax/127, q = rne(x/s) clamped to
  *       [-127, 127].
+ *       The same thread names INT4 next to INT8 for the online KV cache.  The reading used here
+ *       for INT4 is asymmetric, one (scale, zero point) pair of fp32 per (token, head): the 16 levels
+ *       zp + q * s, q = 0..15, span the row from its minimum zp = min x to its maximum,
+ *       s = fl32(fl32(max x - min x) / 15), q = rne(fl32(fl32(x - zp) / s)) clamped to [0, 15]; a
+ *       constant row gives s = 0 and q = 0 (its value is zp).  [QQQ-2] cites kv4 caches (QServe).
  *   [QQQ-2] "[QST] Scale factors and benchmarks" (QQQ issue thread): the serving stack the
  *       8-bit cache lives in is paged ("armed with paged attention"): fixed-size token blocks
  *       reached through a per-sequence block table.
@@ -40,6 +45,11 @@
  *   - Cache layout (both formats and INT8): K codes [num_blocks][Hkv][8][16 tokens][16 dims], i.e.
  *     dim d of token t sits at byte (d / 16) * 256 + t * 16 + d % 16 of its 2048-byte tile;
  *     V codes [num_blocks][Hkv][128 dims][16 tokens]; INT8 scales [num_blocks][Hkv][16 tokens].
+ *   - INT4 layout (two 4-bit codes per byte, the even one in the low nibble): K [num_blocks][Hkv]
+ *     [4][16 tokens][16 bytes], dim d of token t in byte (d / 32) * 256 + t * 16 + (d % 32) / 2
+ *     of its 1024-byte tile, nibble d % 2; V [num_blocks][Hkv][128 dims][8 bytes], token t of dim
+ *     d in byte d * 8 + t / 2, nibble t % 2; (scale, zero point) pairs [num_blocks][Hkv][16][2] for
+ *     K and for V.
  *   - context_lens are post-append lengths; context_lens[b] == 0 gives an all-zero output row.
  *   - Query head h reads KV head h / (Hq / Hkv).
  *
@@ -56,6 +66,7 @@
 #define KVQO_E5M2 2
 #define KVQO_INT8 3
 #define KVQO_E4M3FNUZ 4
+#define KVQO_INT4 5
 
 #define KVQO_BLOCK 16
 #define KVQO_DIM 128
@@ -213,6 +224,40 @@ void kvqo_int8_quantize_row(const uint16_t *x, int n, int8_t *q, float *s_out)
     *s_out = s;
 }
 
+/* Online INT4 encode of one (token, head) row of n values (reading in the header): zp = min x,
+ * s = fl32(fl32(max x - zp) / 15), q = clamp(rne(fl32(fl32(x - zp) / s)), 0, 15); a constant row
+ * gives s = 0 and q = 0.  Inputs are assumed finite.                                            */
+void kvqo_int4_quantize_row(const uint16_t *x, int n, uint8_t *q, float *s_out, float *zp_out)
+{
+    float mn = INFINITY, mx = -INFINITY;
+    for (int d = 0; d < n; ++d) {
+        float v = (float)kvqo_fp16_to_double(x[d]);
+        if (v < mn)
+            mn = v;
+        if (v > mx)
+            mx = v;
+    }
+    float range = mx - mn;          /* one binary32 subtraction */
+    float s = range / 15.0f;        /* one binary32 division */
+    *zp_out = mn;
+    if (s == 0.0f) {
+        for (int d = 0; d < n; ++d)
+            q[d] = 0;
+        *s_out = 0.0f;
+        return;
+    }
+    for (int d = 0; d < n; ++d) {
+        float y = ((float)kvqo_fp16_to_double(x[d]) - mn) / s;
+        double r = nearbyint((double)y);
+        if (r > 15.0)
+            r = 15.0;
+        if (r < 0.0)
+            r = 0.0;
+        q[d] = (uint8_t)r;
+    }
+    *s_out = s;
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* Paged layout offsets (see the header comment).                                               */
 static size_t k_off(int Hkv, int blk, int g, int t, int d)
@@ -229,6 +274,25 @@ static size_t s_off(int Hkv, int blk, int g, int t)
 {
     return ((size_t)blk * Hkv + g) * KVQO_BLOCK + t;
 }
+/* INT4: byte offsets; the code is nibble (d % 2) of the K byte and nibble (t % 2) of the V byte */
+static size_t k_off4(int Hkv, int blk, int g, int t, int d)
+{
+    size_t tile = ((size_t)blk * Hkv + g) * (KVQO_BLOCK * KVQO_DIM / 2);
+    return tile + (size_t)(d / 32) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)((d % 32) / 2);
+}
+static size_t v_off4(int Hkv, int blk, int g, int t, int d)
+{
+    size_t tile = ((size_t)blk * Hkv + g) * (KVQO_BLOCK * KVQO_DIM / 2);
+    return tile + (size_t)d * (KVQO_BLOCK / 2) + (size_t)(t / 2);
+}
+static uint8_t get_nibble(const uint8_t *a, size_t off, int hi)
+{
+    return hi ? (uint8_t)(a[off] >> 4) : (uint8_t)(a[off] & 0x0F);
+}
+static void put_nibble(uint8_t *a, size_t off, int hi, uint8_t q)
+{
+    a[off] = hi ? (uint8_t)((a[off] & 0x0F) | (q << 4)) : (uint8_t)((a[off] & 0xF0) | q);
+}
 
 /* Append new K/V rows into the paged cache (all arrays in host memory).
  *   k_new, v_new : fp16 bits [T][Hkv][128]
@@ -241,9 +305,11 @@ int kvqo_append(int dtype, int Hkv, uint8_t *k_cache, uint8_t *v_cache, float *k
                 const int32_t *cu_new_lens, const int32_t *block_tables, int max_blocks_per_seq,
                 const int32_t *context_lens, int batch)
 {
-    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ)
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ &&
+        dtype != KVQO_INT4)
         return -1;
     int8_t qk[KVQO_DIM], qv[KVQO_DIM];
+    uint8_t uk[KVQO_DIM], uv[KVQO_DIM];
     for (int b = 0; b < batch; ++b) {
         int row0 = cu_new_lens ? cu_new_lens[b] : b;
         int n_b = cu_new_lens ? cu_new_lens[b + 1] - cu_new_lens[b] : 1;
@@ -256,7 +322,19 @@ int kvqo_append(int dtype, int Hkv, uint8_t *k_cache, uint8_t *v_cache, float *k
             for (int g = 0; g < Hkv; ++g) {
                 const uint16_t *xk = k_new + ((size_t)(row0 + j) * Hkv + g) * KVQO_DIM;
                 const uint16_t *xv = v_new + ((size_t)(row0 + j) * Hkv + g) * KVQO_DIM;
-                if (dtype == KVQO_INT8) {
+                if (dtype == KVQO_INT4) {
+                    float sk, zk, sv, zv;
+                    kvqo_int4_quantize_row(xk, KVQO_DIM, uk, &sk, &zk);
+                    kvqo_int4_quantize_row(xv, KVQO_DIM, uv, &sv, &zv);
+                    for (int d = 0; d < KVQO_DIM; ++d) {
+                        put_nibble(k_cache, k_off4(Hkv, blk, g, t, d), d % 2, uk[d]);
+                        put_nibble(v_cache, v_off4(Hkv, blk, g, t, d), t % 2, uv[d]);
+                    }
+                    k_scale[2 * s_off(Hkv, blk, g, t)] = sk;
+                    k_scale[2 * s_off(Hkv, blk, g, t) + 1] = zk;
+                    v_scale[2 * s_off(Hkv, blk, g, t)] = sv;
+                    v_scale[2 * s_off(Hkv, blk, g, t) + 1] = zv;
+                } else if (dtype == KVQO_INT8) {
                     float sk, sv;
                     kvqo_int8_quantize_row(xk, KVQO_DIM, qk, &sk);
                     kvqo_int8_quantize_row(xv, KVQO_DIM, qv, &sv);
@@ -278,11 +356,20 @@ int kvqo_append(int dtype, int Hkv, uint8_t *k_cache, uint8_t *v_cache, float *k
     return 0;
 }
 
-/* Exact dequantized value of one cached element, in fp64: FP8 dec(c) * kv_scale, INT8 q * s.
- * Both products are exact in fp64 (at most 4 + 24 or 8 + 24 significant bits).                  */
+/* Exact dequantized value of one cached element, in fp64: FP8 dec(c) * kv_scale, INT8 q * s,
+ * INT4 q * s + zp.  All are exact in fp64.  The products have at most 4 + 24 or 8 + 24 significant
+ * bits.  For INT4, zp is a binary16 value (the row's minimum) and s is at least 1/30 of a binary16
+ * step at the row's extremes (max > min are both binary16), so the bits of q * s + zp span at most
+ * about 41 places.                                                                             */
+static double dq4(const uint8_t *codes, size_t off, int hi, const float *sz, size_t so)
+{
+    return (double)get_nibble(codes, off, hi) * (double)sz[2 * so] + (double)sz[2 * so + 1];
+}
 static double dq_k(int dtype, int Hkv, const uint8_t *kc, const float *ks, float kv_scale, int blk,
                    int g, int t, int d)
 {
+    if (dtype == KVQO_INT4)
+        return dq4(kc, k_off4(Hkv, blk, g, t, d), d % 2, ks, s_off(Hkv, blk, g, t));
     uint8_t c = kc[k_off(Hkv, blk, g, t, d)];
     if (dtype == KVQO_INT8)
         return (double)(int8_t)c * (double)ks[s_off(Hkv, blk, g, t)];
@@ -291,6 +378,8 @@ static double dq_k(int dtype, int Hkv, const uint8_t *kc, const float *ks, float
 static double dq_v(int dtype, int Hkv, const uint8_t *vc, const float *vs, float kv_scale, int blk,
                    int g, int t, int d)
 {
+    if (dtype == KVQO_INT4)
+        return dq4(vc, v_off4(Hkv, blk, g, t, d), t % 2, vs, s_off(Hkv, blk, g, t));
     uint8_t c = vc[v_off(Hkv, blk, g, t, d)];
     if (dtype == KVQO_INT8)
         return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, t)];
@@ -304,7 +393,8 @@ int kvqo_dequant(int dtype, int Hkv, const uint8_t *k_cache, const uint8_t *v_ca
                  const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
                  int batch, int max_context_len, float *k_out, float *v_out)
 {
-    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ)
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ &&
+        dtype != KVQO_INT4)
         return -1;
     for (int b = 0; b < batch; ++b) {
         int n = context_lens[b];
@@ -334,7 +424,8 @@ int kvqo_decode_attn_head(int dtype, int Hkv, int Hq, const uint8_t *k_cache, co
                           int max_blocks_per_seq, const int32_t *context_lens, int b, int h,
                           double *out)
 {
-    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ)
+    if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ &&
+        dtype != KVQO_INT4)
         return -1;
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -1;
@@ -440,4 +531,10 @@ void kvqo_int8_quantize_rows(const uint16_t *x, int rows, int n, int8_t *q, floa
 {
     for (int r = 0; r < rows; ++r)
         kvqo_int8_quantize_row(x + (size_t)r * n, n, q + (size_t)r * n, s + r);
+}
+
+void kvqo_int4_quantize_rows(const uint16_t *x, int rows, int n, uint8_t *q, float *s, float *zp)
+{
+    for (int r = 0; r < rows; ++r)
+        kvqo_int4_quantize_row(x + (size_t)r * n, n, q + (size_t)r * n, s + r, zp + r);
 }

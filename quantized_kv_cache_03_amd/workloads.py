@@ -38,7 +38,7 @@ class Workload:
     batch: int
     num_q_heads: int
     num_kv_heads: int
-    dtype: str                  # "fp8_e4m3" | "fp8_e5m2" | "int8" | "fp8_e4m3fnuz"
+    dtype: str                  # "fp8_e4m3" | "fp8_e5m2" | "int8" | "fp8_e4m3fnuz" | "int4"
     context: tuple              # ("fixed", n) | ("uniform", lo, hi) | ("lognormal", median, sigma, cap)
     table: str = "sequential"   # "sequential" | "shuffled"
     scale_rule: str = "one"     # "amax/448" | "amax/240" | "one"
@@ -73,6 +73,11 @@ WORKLOADS = {
                                        scale_rule="amax/240"),
     "llama3-70b-gqa-e4m3fnuz-32k": Workload("llama3-70b-gqa-e4m3fnuz-32k", 5, 16, 64, 8,
                                             "fp8_e4m3fnuz", ("fixed", 32768), scale_rule="amax/240"),
+    # online INT4 (asymmetric, per (token, head) scale and zero point) on the Llama-2-7B and
+    # Llama-3-8B shapes
+    "llama2-7b-mha-int4": Workload("llama2-7b-mha-int4", 2, 32, 32, 32, "int4",
+                                   ("uniform", 512, 4096), table="shuffled"),
+    "llama3-8b-gqa-int4": Workload("llama3-8b-gqa-int4", 3, 64, 32, 8, "int4", ("fixed", 8192)),
 }
 ORDER = list(WORKLOADS)
 
@@ -161,7 +166,7 @@ def kv_scale(w: Workload, k: np.ndarray | None = None, v: np.ndarray | None = No
              ctx: np.ndarray | None = None) -> float:
     """Per-tensor scale: 1.0, or fl32(amax over K and V) / 448 or / 240 (synthetic calibration to
     the largest finite E4M3 or E4M3FNUZ value)."""
-    if w.scale_rule == "one" or w.dtype == "int8":
+    if w.scale_rule == "one" or w.dtype in ("int8", "int4"):
         return 1.0
     if w.scale_rule not in ("amax/448", "amax/240"):
         raise ValueError(w.scale_rule)

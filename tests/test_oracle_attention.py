@@ -14,9 +14,9 @@ import torch
 
 from quantized_kv_cache_03_amd import workloads as W
 
-E4M3, E5M2, INT8, E4M3FNUZ = 1, 2, 3, 4
+E4M3, E5M2, INT8, E4M3FNUZ, INT4 = 1, 2, 3, 4, 5
 TORCH_DT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2, E4M3FNUZ: torch.float8_e4m3fnuz}
-DT_NAME = {E4M3: "fp8_e4m3", E5M2: "fp8_e5m2", INT8: "int8", E4M3FNUZ: "fp8_e4m3fnuz"}
+DT_NAME = {E4M3: "fp8_e4m3", E5M2: "fp8_e5m2", INT8: "int8", E4M3FNUZ: "fp8_e4m3fnuz", INT4: "int4"}
 SCALE_RULE = {E4M3: "amax/448", E4M3FNUZ: "amax/240"}
 
 
@@ -41,6 +41,13 @@ def _setup(oracle_mod, dtype, ctx, Hq=4, Hkv=2, table="sequential", seed=11, out
 
 def _independent_dequant(dtype, rows, s):
     """rows fp16 [n][Hkv][128] -> exact dequantized float64 via torch casts / numpy rint."""
+    if dtype == INT4:
+        xf = rows.astype(np.float32)
+        mn = xf.min(axis=-1, keepdims=True)
+        sc = (xf.max(axis=-1, keepdims=True) - mn) / np.float32(15)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            qq = np.where(sc > 0, np.clip(np.rint((xf - mn) / sc), 0, 15), 0)
+        return qq.astype(np.float64) * sc.astype(np.float64) + mn.astype(np.float64)
     if dtype == INT8:
         xf = rows.astype(np.float32)
         amax = np.abs(xf).max(axis=-1)
@@ -103,7 +110,7 @@ def test_append_one_token_per_sequence(oracle_mod):
     assert sorted(map(tuple, written.tolist())) == expect
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ, INT4])
 def test_dequant_matches_independent_decode(oracle_mod, dtype):
     ctx = [3, 16, 29]
     w, ctx, bt, k, v, cu, s, cache, q = _setup(oracle_mod, dtype, ctx, table="shuffled", outliers=2)
@@ -117,7 +124,7 @@ def test_dequant_matches_independent_decode(oracle_mod, dtype):
         assert np.all(np.isnan(ko[b, :, n:, :]))  # slots past the context are untouched
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ, INT4])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2), (16, 2)])
 def test_attention_matches_torch_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
     ctx = [1, 2, 15, 16, 17, 33, 70]
@@ -136,7 +143,7 @@ def test_attention_matches_torch_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
         np.testing.assert_allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("dtype", [E4M3, INT8, E4M3FNUZ])
+@pytest.mark.parametrize("dtype", [E4M3, INT8, E4M3FNUZ, INT4])
 def test_attention_closed_forms(oracle_mod, dtype):
     ctx = [1, 2, 40]
     w, ctx, bt, k, v, cu, s, cache, q = _setup(oracle_mod, dtype, ctx, Hq=2, Hkv=2)
@@ -217,7 +224,7 @@ def _prefill_rows(ctx, nq, Hq, seed):
     return q, cu_q
 
 
-@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ])
+@pytest.mark.parametrize("dtype", [E4M3, E5M2, INT8, E4M3FNUZ, INT4])
 @pytest.mark.parametrize("Hq,Hkv", [(2, 2), (8, 2)])
 def test_prefill_matches_torch_causal_sdpa_float64(oracle_mod, dtype, Hq, Hkv):
     """Chunked prefill rows against torch float64 attention with an explicit causal mask (query row

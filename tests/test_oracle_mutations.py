@@ -16,6 +16,7 @@ from oracle import build as obuild
 
 import test_oracle_attention as TA
 import test_oracle_codec as TC
+import test_oracle_int4 as T4
 import test_oracle_int8 as TI
 
 MUTATIONS = {
@@ -73,6 +74,21 @@ MUTATIONS = {
     "fnuz-top-code-nan": (
         "    else if (fmt == KVQO_E4M3FNUZ && code == 0x80)\n        v = NAN;",
         "    else if (fmt == KVQO_E4M3FNUZ && (code & 0x7F) == 0x7F)\n        v = NAN;"),
+    "int4-divide-16": (
+        "float s = range / 15.0f;",
+        "float s = range / 16.0f;"),
+    "int4-zero-point-max": (
+        "*zp_out = mn;",
+        "*zp_out = mx;"),
+    "int4-k-nibble-offset": (
+        "return tile + (size_t)(d / 32) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)((d % 32) / 2);",
+        "return tile + (size_t)(d / 32) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)((d % 32) % 16);"),
+    "int4-v-token-major": (
+        "return tile + (size_t)d * (KVQO_BLOCK / 2) + (size_t)(t / 2);",
+        "return tile + (size_t)t * (KVQO_DIM / 2) + (size_t)(d / 2);"),
+    "int4-dequant-drops-zero-point": (
+        "return (double)get_nibble(codes, off, hi) * (double)sz[2 * so] + (double)sz[2 * so + 1];",
+        "return (double)get_nibble(codes, off, hi) * (double)sz[2 * so];"),
     "append-position-reversed": (
         "int p = context_lens[b] - n_b + j;",
         "int p = context_lens[b] - 1 - j;"),
@@ -110,6 +126,9 @@ def _pins():
         lambda: TA.test_dequant_matches_independent_decode(o, TA.INT8),
         lambda: TA.test_attention_matches_torch_sdpa_float64(o, TA.E4M3, 8, 2),
         lambda: TA.test_attention_matches_torch_sdpa_float64(o, TA.INT8, 2, 2),
+        lambda: T4.test_int4_matches_numpy(o, "normal"),
+        lambda: T4.test_int4_append_layout_and_poison(o),
+        lambda: TA.test_dequant_matches_independent_decode(o, TA.INT4),
     ]
 
 
