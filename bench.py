@@ -106,7 +106,7 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
     cu[1:] = np.cumsum(ctx)
     q = W.query(w)[seqs]
     dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
-          "fp8_e4m3fnuz": oracle.E4M3FNUZ}[w.dtype]
+          "fp8_e4m3fnuz": oracle.E4M3FNUZ, "int4": oracle.INT4}[w.dtype]
     cache = oracle.Cache(dt, nb, w.num_kv_heads, scale)
     t0 = time.perf_counter()
     oracle.append(cache, k, v, bt, ctx, cu)  # the prefill of the sample's rows (single-threaded)
@@ -122,7 +122,8 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
         if time.perf_counter() - t1 >= budget_s:
             break
     t2 = time.perf_counter()
-    per_tok = 2 * 128 + (8 if w.dtype == "int8" else 0)
+    from quantized_kv_cache_03_amd.harness import kv_bytes_per_token
+    per_tok = kv_bytes_per_token(w.dtype)
     bytes_ = (int(ctx.sum()) * w.num_kv_heads * per_tok + 2 * len(seqs) * w.num_q_heads * 128 * 2
               + 4 * int(((ctx + 15) // 16).sum()) + 4 * len(seqs))
     step_s = (t2 - t1) / reps
@@ -193,7 +194,7 @@ def run_prefill(args, w):
         import oracle
         threads = max(1, min(len(os.sched_getaffinity(0)), 16))
         dt = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
-          "fp8_e4m3fnuz": oracle.E4M3FNUZ}[w.dtype]
+          "fp8_e4m3fnuz": oracle.E4M3FNUZ, "int4": oracle.INT4}[w.dtype]
         oc = oracle.Cache(dt, case.num_blocks, w.num_kv_heads, case.kv_scale)
         oracle.append(oc, case.k_host, case.v_host, case.bt, case.ctx, case.cu)
         T = int(cu_q[-1])

@@ -13,7 +13,9 @@
  *                           (torch dtype float8_e4m3fnuz), read as the 1/4/3 layout with bias 8,
  *                           no infinities, no negative zero and one NaN code, 0x80.
  *   "[Feature] TurboMind support W8A8 or FP8 KV Cache" (lmdeploy issue thread):
- *     the online INT8 KV cache, read here as symmetric INT8 with one fp32 scale per (token, head).
+ *     the online INT8 KV cache, read here as symmetric INT8 with one fp32 scale per (token, head);
+ *     INT4, named beside it, read as asymmetric 4-bit codes with an fp32 (scale, zero point) pair
+ *     per (token, head).
  *   "[QST] Scale factors and benchmarks" (QQQ issue thread):
  *     the cache lives in a paged-attention serving stack: fixed-size blocks of tokens reached
  *     through a per-sequence block table.
@@ -28,12 +30,21 @@
  *   INT8 codes = per (token, KV head) row of 128 values: s = fl32(amax / 127),
  *                q = clamp(rne(fl32(x / s)), -127, 127); an all-zero row gives s = 0, q = 0.
  *                Decode: value = q * s.  Inputs are assumed finite.
+ *   INT4 codes = per (token, KV head) row: zp = min x, s = fl32(fl32(max x - zp) / 15),
+ *                q = clamp(rne(fl32(fl32(x - zp) / s)), 0, 15); a constant row gives s = 0, q = 0.
+ *                Decode: value = q * s + zp.  Inputs are assumed finite.
  *
  * Memory layout (all device memory, caller-owned, dense, no padding):
  *   K codes  uint8 [num_blocks][num_kv_heads][8][16 tokens][16 dims] (2 KiB tile of eight 256-byte
  *            chunks: dim d of token t is byte (d / 16) * 256 + t * 16 + d % 16 of the tile)
  *   V codes  uint8 [num_blocks][num_kv_heads][128 dims][16 tokens]   (dim-major tile, 2 KiB)
  *   INT8 scales  float [num_blocks][num_kv_heads][16 tokens], one array for K and one for V
+ *   INT4 (two codes per byte, the even element in the low nibble; tiles of 1 KiB):
+ *     K codes  uint8 [num_blocks][num_kv_heads][4][16 tokens][16 bytes]: dim d of token t is in
+ *              byte (d / 32) * 256 + t * 16 + (d % 32) / 2 of the tile, nibble d % 2
+ *     V codes  uint8 [num_blocks][num_kv_heads][128 dims][8 bytes]: token t of dim d is in byte
+ *              d * 8 + t / 2, nibble t % 2
+ *     scales   float [num_blocks][num_kv_heads][16 tokens][2] = (scale, zero point), for K and V
  *   block_tables int32 [batch][max_blocks_per_seq]: logical block i of sequence b is physical block
  *                block_tables[b][i]; entries past a sequence's last block are never read.
  *   context_lens int32 [batch]: the number of tokens of each sequence after the append.
@@ -66,7 +77,9 @@ typedef enum {
     KVQ_FP8_E4M3 = 1, /* OCP E4M3 with per-tensor fp32 kv_scale ("fp8", "fp8_e4m3")        */
     KVQ_FP8_E5M2 = 2, /* OCP E5M2 with per-tensor fp32 kv_scale, usually 1.0 ("fp8_e5m2")  */
     KVQ_INT8 = 3,     /* symmetric INT8, one fp32 scale per (token, KV head) ("int8")      */
-    KVQ_FP8_E4M3FNUZ = 4 /* AMD's E4M3FNUZ with per-tensor fp32 kv_scale ("fp8_e4m3fnuz")  */
+    KVQ_FP8_E4M3FNUZ = 4, /* AMD's E4M3FNUZ with per-tensor fp32 kv_scale ("fp8_e4m3fnuz") */
+    KVQ_INT4 = 5      /* asymmetric 4-bit codes, fp32 (scale, zero point) per (token, KV head)
+                         ("int4"); two codes per byte                                        */
 } kvq_dtype;
 
 enum {
@@ -91,8 +104,8 @@ typedef struct {
     int32_t head_dim;     /* must be 128 */
     uint8_t *k_cache;     /* K codes, layout above */
     uint8_t *v_cache;     /* V codes, layout above */
-    float *k_scale;       /* INT8 only: [num_blocks][Hkv][16]; NULL for FP8 */
-    float *v_scale;       /* INT8 only: [num_blocks][Hkv][16]; NULL for FP8 */
+    float *k_scale;       /* INT8: [num_blocks][Hkv][16]; INT4: [num_blocks][Hkv][16][2]; NULL for FP8 */
+    float *v_scale;       /* INT8: [num_blocks][Hkv][16]; INT4: [num_blocks][Hkv][16][2]; NULL for FP8 */
     float kv_scale;       /* FP8 only: per-tensor scale shared by K and V, finite and > 0;
                              1.0 is the default ("FP8 E4M3 KV Cache" section) */
 } kvq_cache;
@@ -175,15 +188,16 @@ int kvq_paged_prefill_attn(const kvq_cache *cache, const void *q, void *out, int
                            void *stream);
 
 /* Dequantize the cache into dense fp32 [batch][Hkv][max_context_len][128] arrays for K and V:
- * each element is fl32(dec(code) * kv_scale) (FP8) or fl32(q * s) (INT8), one rounding.  Slots
- * t >= context_lens[b] are left untouched.  For inspection and tests; not on the decode path. */
+ * each element is fl32(dec(code) * kv_scale) (FP8), fl32(q * s) (INT8) or fl32(q * s + zp)
+ * (INT4), one rounding.  Slots t >= context_lens[b] are left untouched.  For inspection and tests;
+ * not on the decode path. */
 int kvq_dequant(const kvq_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
                 const int32_t *context_lens, int32_t batch, int32_t max_context_len, float *k_out,
                 float *v_out, void *stream);
 
 /* "fp8" | "fp8_e4m3" -> KVQ_FP8_E4M3, "fp8_e5m2" -> KVQ_FP8_E5M2, "int8" -> KVQ_INT8,
- * "fp8_e4m3fnuz" -> KVQ_FP8_E4M3FNUZ (the --kv-cache-dtype names and the float8_e4m3fnuz
- * kv_cache_torch_dtype of "Accelerating Inference with FP8 KV Cache").
+ * "int4" -> KVQ_INT4, "fp8_e4m3fnuz" -> KVQ_FP8_E4M3FNUZ (the --kv-cache-dtype names and the
+ * float8_e4m3fnuz kv_cache_torch_dtype of "Accelerating Inference with FP8 KV Cache").
  * Returns KVQ_OK or KVQ_ERR_DTYPE (out untouched). */
 int kvq_dtype_from_string(const char *s, kvq_dtype *out);
 

@@ -35,7 +35,7 @@ int hip_fail(hipError_t e, const char* where) {
 int check_cache(const kvq_cache* c) {
     if (!c) return fail(KVQ_ERR_ARG, "cache descriptor is NULL");
     if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8 &&
-        c->dtype != KVQ_FP8_E4M3FNUZ)
+        c->dtype != KVQ_FP8_E4M3FNUZ && c->dtype != KVQ_INT4)
         return fail(KVQ_ERR_DTYPE, "unknown kv cache dtype %d", (int)c->dtype);
     if (c->head_dim != KVQ_HEAD_DIM)
         return fail(KVQ_ERR_SHAPE, "head_dim %d is not supported (must be %d)", c->head_dim, KVQ_HEAD_DIM);
@@ -45,9 +45,10 @@ int check_cache(const kvq_cache* c) {
     if (c->num_kv_heads <= 0) return fail(KVQ_ERR_SHAPE, "num_kv_heads %d must be positive", c->num_kv_heads);
     if (c->num_blocks <= 0) return fail(KVQ_ERR_SHAPE, "num_blocks %d must be positive", c->num_blocks);
     if (!c->k_cache || !c->v_cache) return fail(KVQ_ERR_ARG, "k_cache / v_cache pointer is NULL");
-    if (c->dtype == KVQ_INT8) {
+    if (c->dtype == KVQ_INT8 || c->dtype == KVQ_INT4) {
         if (!c->k_scale || !c->v_scale)
-            return fail(KVQ_ERR_ARG, "INT8 cache needs k_scale and v_scale arrays");
+            return fail(KVQ_ERR_ARG, "%s cache needs k_scale and v_scale arrays",
+                        c->dtype == KVQ_INT8 ? "INT8" : "INT4");
     } else {
         if (!(isfinite(c->kv_scale) && c->kv_scale > 0.0f))
             return fail(KVQ_ERR_ARG, "kv_scale %g must be finite and positive", (double)c->kv_scale);
@@ -159,6 +160,7 @@ int kvq_dtype_from_string(const char* s, kvq_dtype* out) {
     else if (!strcmp(s, "fp8_e5m2")) *out = KVQ_FP8_E5M2;
     else if (!strcmp(s, "int8")) *out = KVQ_INT8;
     else if (!strcmp(s, "fp8_e4m3fnuz")) *out = KVQ_FP8_E4M3FNUZ;
+    else if (!strcmp(s, "int4")) *out = KVQ_INT4;
     else return fail(KVQ_ERR_DTYPE, "unknown kv cache dtype name '%s'", s);
     return ok();
 }
@@ -217,6 +219,8 @@ int decode_common(const char* where, const kvq_cache* cache, const void* k_new, 
         return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
+    if (cache->dtype == KVQ_INT4 && num_q_heads != cache->num_kv_heads)
+        return fail(KVQ_ERR_DTYPE, "INT4 decode attention is built for one query head per KV head only");
     if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
     if (partition_size != KVQ_PARTITION_BALANCED &&
         (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0))
@@ -319,6 +323,8 @@ int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int
         return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
+    if (cache->dtype == KVQ_INT4)
+        return fail(KVQ_ERR_DTYPE, "prefill attention over an INT4 cache is not built");
     if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
         return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",

@@ -1,0 +1,373 @@
+// kvq_attn_mha4.hip -- decode attention over the INT4 cache, one query head per KV head (VALU).
+//
+// The online INT4 cache ("[Feature] TurboMind support W8A8 or FP8 KV Cache" names INT4 beside the
+// online INT8 cache): asymmetric 4-bit codes with an fp32 (scale s, zero point zp) pair per
+// (token, KV head), two codes per byte, 1 KiB tiles of 16 tokens.  With k^ = s_t c + zp_t the
+// logits and the output factor as
+//     z_t   = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d)
+//     out_d = (sum_t p_t s_t c_td + sum_t p_t zp_t) / sum_t p_t,
+// so the codes enter the dot products as exact small integers and the scales stay per token.
+//
+// One wave per (query head, share of the work), the structure of the 8-bit kernel
+// (kvq_attn_mha.hip): chunks of TW tiles with every load issued before any use, a running max /
+// sum / accumulator per wave.
+//   K tile (four 256-byte chunks of 32 dims x 16 tokens): lane l holds the 32 dims of chunk l % 4
+//     of token l / 4 -- one 16-byte load per lane reads the whole tile -- and two quad DPP sums
+//     finish each logit.
+//   V tile (dim-major, 8 bytes per dim): lane l holds the 16 tokens of dims 2l and 2l + 1 (16
+//     contiguous bytes), so each lane accumulates two whole output elements; the tile's 16 weights
+//     p_t s_t reach every lane as packed fp16 (hi, lo) pairs through LDS.
+// A dword of codes decodes to the pairs (i, i + 4) of its eight nibbles (int4x8_to_f16): the query
+// slice is paired the same way for K, and the weights are published in that order for V.
+#include "kvq_attn.h"
+#include "kvq_int4.h"
+
+namespace kvq {
+
+namespace {
+
+// The codes and scales one lane holds for one tile.
+//   k  : K codes of token l / 4, dims 32 (l % 4) .. +31
+//   v  : V codes of dims 2l (dwords x, y: tokens 0-7, 8-15) and 2l + 1 (dwords z, w)
+//   ks : (scale, zero point) of the K row of token l / 4; vs: of its V row
+struct Tile4 {
+    u32x4 k, v;
+    f32x2 ks, vs;
+};
+
+__device__ __forceinline__ void load_tile4(const KernelParams& a, Tile4& t, int blk, int g,
+                                           uint32_t k_off, uint32_t v_off, int tk) {
+    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes4;
+    t.k = ldg16(a.kc + tile + k_off);
+    t.v = ldg16(a.vc + tile + v_off);
+    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + tk;
+    t.ks = ldg_nt(reinterpret_cast<const f32x2*>(a.ks) + so);
+    t.vs = ldg_nt(reinterpret_cast<const f32x2*>(a.vs) + so);
+}
+
+// q . c over this lane's 32 dims; qv[4 j + i] pairs dims (8 j + i, 8 j + i + 4) of the chunk.
+__device__ __forceinline__ float dot32_int4(const u32x4& k, const half2_t (&qv)[16]) {
+    const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        half2_t h[4];
+        int4x8_to_f16(w[j], h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = dot2(h[i], qv[4 * j + i], s);
+    }
+    return s;
+}
+
+// acc += sum over the 8 tokens of one dword of a V row (tokens 8 half .. +7) of w_t c_t, with the
+// weights as fp16 (hi, lo) pairs for the tokens (8 half + i, 8 half + i + 4).
+__device__ __forceinline__ float pv8_int4(uint32_t codes8, const uint32_t* hi, const uint32_t* lo,
+                                          float acc) {
+    half2_t h[4];
+    int4x8_to_f16(codes8, h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = dot2(h[i], __builtin_bit_cast(half2_t, hi[i]), acc);
+        acc = dot2(h[i], __builtin_bit_cast(half2_t, lo[i]), acc);
+    }
+    return acc;
+}
+
+// One chunk of TW tiles.  The quad of token tk ends with identical logits; lane 4 tk publishes the
+// token's weight w = p s_v as fp16 hi and lo halves at its place in the pairing (token t goes to
+// half (t % 8) / 4 of pair 4 (t / 8) + t % 4), and adds p zp_v to the lane's zero-point sum.
+// MASKED handles a chunk reaching past the segment end (logits there become -inf, weights 0).
+template <int TW, bool MASKED>
+__device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (&t)[TW], int tile0,
+                                            int t_end, const half2_t (&qv)[16], float qsum, int lane,
+                                            uint16_t* lds, float& m_run, float& l_lane, float& z_lane,
+                                            float& acc0, float& acc1) {
+    const int tk = lane >> 2;
+    float z[TW];
+    float cmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const float s = sum4(dot32_int4(t[i].k, qv));
+        z[i] = a.qk_scale * (s * t[i].ks.x + t[i].ks.y * qsum);
+        if constexpr (MASKED) z[i] = ((tile0 + i) * kBlock + tk < t_end) ? z[i] : kNegInf;
+        cmax = fmaxf(cmax, z[i]);
+    }
+    cmax = max_across_quads(cmax);  // a chunk always holds at least one valid token
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    acc0 *= alpha;
+    acc1 *= alpha;
+    l_lane *= alpha;
+    z_lane *= alpha;
+
+    const int slot = 2 * (4 * (tk >> 3) + (tk & 3)) + ((tk >> 2) & 1);  // half index of token tk
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const float pw = __builtin_amdgcn_exp2f(z[i] - m_new);
+        l_lane += pw;
+        // masked slots may hold NaN scales: keep their weight exactly 0
+        const bool live = pw > 0.0f;
+        const float w = live ? pw * t[i].vs.x : 0.0f;
+        z_lane += live ? pw * t[i].vs.y : 0.0f;
+        if ((lane & 3) == 0) {
+            const _Float16 h = (_Float16)w;
+            lds[i * 32 + slot] = __builtin_bit_cast(uint16_t, h);
+            lds[i * 32 + 16 + slot] = __builtin_bit_cast(uint16_t, (_Float16)(w - (float)h));
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+        const u32x4* l4 = reinterpret_cast<const u32x4*>(lds + i * 32);
+        const u32x4 h0 = l4[0], h1 = l4[1], w0 = l4[2], w1 = l4[3];
+        const uint32_t whi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+        const uint32_t wlo[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        acc0 = pv8_int4(t[i].v.x, whi, wlo, acc0);
+        acc0 = pv8_int4(t[i].v.y, whi + 4, wlo + 4, acc0);
+        acc1 = pv8_int4(t[i].v.z, whi, wlo, acc1);
+        acc1 = pv8_int4(t[i].v.w, whi + 4, wlo + 4, acc1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The appended token of a fused decode step, encoded with the append kernel's arithmetic: lane l
+// holds K dims 2l, 2l + 1 and V dims 2l, 2l + 1 of the new row.  The token's 64 K bytes go to LDS
+// in chunk order (byte l = dims 2l, 2l + 1); its V codes stay in the lane, which owns those dims.
+struct NewToken4 {
+    int slot;
+    uint32_t v0, v1;  // V codes of dims 2l and 2l + 1
+    f32x2 ks, vs;    // (scale, zero point) of the K and V rows
+};
+
+__device__ __forceinline__ NewToken4 new_token4(const KernelParams& a, int b, int g, int n, int lane,
+                                                uint8_t* lds_k) {
+#pragma clang fp contract(off)
+    NewToken4 nt;
+    nt.slot = (n - 1) % kBlock;
+    const size_t row = ((size_t)b * a.Hkv + g) * (kDim / 2);
+    const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k_new)[row + lane];
+    const uint32_t vw = reinterpret_cast<const uint32_t*>(a.v_new)[row + lane];
+    const float k0 = half_bits_to_float(kw & 0xFFFFu), k1 = half_bits_to_float(kw >> 16);
+    const float v0 = half_bits_to_float(vw & 0xFFFFu), v1 = half_bits_to_float(vw >> 16);
+    const float kz = wave_min(fminf(k0, k1)), vz = wave_min(fminf(v0, v1));
+    const float ksc = (wave_max(fmaxf(k0, k1)) - kz) / 15.0f;
+    const float vsc = (wave_max(fmaxf(v0, v1)) - vz) / 15.0f;
+    lds_k[lane] = (uint8_t)(encode_int4(k0, kz, ksc) | (encode_int4(k1, kz, ksc) << 4));
+    nt.v0 = encode_int4(v0, vz, vsc);
+    nt.v1 = encode_int4(v1, vz, vsc);
+    nt.ks = f32x2{ksc, kz};
+    nt.vs = f32x2{vsc, vz};
+    __builtin_amdgcn_wave_barrier();
+    return nt;
+}
+
+__device__ __forceinline__ uint32_t set_nibble(uint32_t w, int i, uint32_t q) {
+    const int sh = 4 * i;
+    return (w & ~(0xFu << sh)) | (q << sh);
+}
+
+// Replace the new token's codes and scales in the registers of its tile.
+__device__ __forceinline__ void patch_tile4(Tile4& t, const NewToken4& nt, const uint8_t* lds_k,
+                                            int lane) {
+    if ((lane >> 2) == nt.slot) {
+        t.k = reinterpret_cast<const u32x4*>(lds_k)[lane & 3];
+        t.ks = nt.ks;
+        t.vs = nt.vs;
+    }
+    const int i = nt.slot & 7;
+    if (nt.slot < 8) {  // wave-uniform
+        t.v.x = set_nibble(t.v.x, i, nt.v0);
+        t.v.z = set_nibble(t.v.z, i, nt.v1);
+    } else {
+        t.v.y = set_nibble(t.v.y, i, nt.v0);
+        t.v.w = set_nibble(t.v.w, i, nt.v1);
+    }
+}
+
+// The appended token's stores, held back until the wave has read all its tiles (as in the 8-bit
+// kernel): its K bytes wait in LDS, this lane's patched V rows in registers.
+struct PendingAppend4 {
+    int blk;       // -1 when nothing is pending (wave-uniform)
+    int slot;
+    u32x4 v;       // this lane's V rows (dims 2l, 2l + 1), patched
+    f32x2 ks, vs;
+};
+
+// Store a pending token: 16 K bytes in each of the four chunks (lanes 0..3, from LDS), the whole V
+// tile (each lane rewrites its two 8-byte rows with the new nibble in place; the other tokens'
+// nibbles are written back unchanged -- this wave is the tile's only reader and writer), and the
+// (scale, zero point) pairs.
+__device__ __forceinline__ void flush_append4(const KernelParams& a, PendingAppend4& pa,
+                                              const uint8_t* lds_k, int g, int lane) {
+    if (pa.blk < 0) return;
+    const size_t tile = ((size_t)pa.blk * a.Hkv + g) * kTileBytes4;
+    uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
+    uint8_t* vt = const_cast<uint8_t*>(a.vc) + tile;
+    if (lane < 4)
+        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(lds_k)[lane],
+                                    reinterpret_cast<u32x4*>(kt + k_byte4(pa.slot, 32 * lane)));
+    __builtin_nontemporal_store(pa.v, reinterpret_cast<u32x4*>(vt + v_byte4(0, 2 * lane)));
+    if (lane == 0) {
+        const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
+        reinterpret_cast<f32x2*>(const_cast<float*>(a.ks))[so] = pa.ks;
+        reinterpret_cast<f32x2*>(const_cast<float*>(a.vs))[so] = pa.vs;
+    }
+    pa.blk = -1;
+}
+
+// The work of one segment -- tiles [lo, hi) of sequence b (n tokens, nt tiles) -- as in the 8-bit
+// kernel: the final output when the segment is the whole sequence, else a partial in row
+// h * rmul + radd (the unnormalized output there already includes the zero-point term).
+template <int TW, bool APPEND>
+__device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h, int g, int n, int nt,
+                                             int lo, int hi, int64_t rmul, int64_t radd, int lane,
+                                             uint16_t* lds, uint8_t* lds_knew, PendingAppend4& pend) {
+    const int tk = lane >> 2;
+    const size_t orow = ((size_t)b * a.Hq + h) * kDim;
+    const bool has_last = hi == nt;
+    const int t_end = min(n, hi * kBlock);
+    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+    const int tile_new = (APPEND && has_last) ? nt - 1 : -1;
+
+    // q slice of chunk c = lane % 4 (dims 32 c .. +31), paired (8 j + i, 8 j + i + 4), and the sum
+    // of all 128 q elements
+    half2_t qv[16];
+    float qsum;
+    {
+        const u32x4* qp = reinterpret_cast<const u32x4*>(a.q + orow + (lane & 3) * 32);
+        const u32x4 q4[4] = {qp[0], qp[1], qp[2], qp[3]};
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w[4] = {q4[j].x, q4[j].y, q4[j].z, q4[j].w};  // dims 8 j .. 8 j + 7
+            const half2_t e0 = __builtin_bit_cast(half2_t, w[0]), e1 = __builtin_bit_cast(half2_t, w[1]);
+            const half2_t e2 = __builtin_bit_cast(half2_t, w[2]), e3 = __builtin_bit_cast(half2_t, w[3]);
+            qv[4 * j + 0] = half2_t{e0.x, e2.x};
+            qv[4 * j + 1] = half2_t{e0.y, e2.y};
+            qv[4 * j + 2] = half2_t{e1.x, e3.x};
+            qv[4 * j + 3] = half2_t{e1.y, e3.y};
+            part += ((float)e0.x + (float)e0.y) + ((float)e1.x + (float)e1.y) +
+                    ((float)e2.x + (float)e2.y) + ((float)e3.x + (float)e3.y);
+        }
+        qsum = sum4(part);
+    }
+
+    const uint32_t k_off = 256u * ((uint32_t)lane & 3u) + 16u * (uint32_t)tk;
+    const uint32_t v_off = 16u * (uint32_t)lane;
+
+    float m_run = kNegInf;
+    float l_lane = 0.0f, z_lane = 0.0f;
+    float acc0 = 0.0f, acc1 = 0.0f;  // dims 2l and 2l + 1
+
+    for (int tb = lo; tb < hi; tb += 64) {
+        const int nt_grp = min(64, hi - tb);
+        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        int full_tiles = min(nt_grp, (t_end - tb * kBlock) / kBlock);
+        if (has_last) full_tiles = min(full_tiles, nt - 1 - tb);
+        const int nfull = full_tiles / TW;
+        for (int c = 0; c < nfull; ++c) {
+            Tile4 t[TW];
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+                load_tile4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c * TW + i), g, k_off, v_off, tk);
+            chunk_step4<TW, false>(a, t, tb + c * TW, t_end, qv, qsum, lane, lds, m_run, l_lane, z_lane,
+                                   acc0, acc1);
+        }
+        for (int c0 = nfull * TW; c0 < nt_grp; ++c0) {
+            Tile4 t[1];
+            load_tile4(a, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, k_off, v_off, tk);
+            if constexpr (APPEND) {
+                if (tb + c0 == tile_new) {
+                    flush_append4(a, pend, lds_knew, g, lane);  // an earlier sequence's token, if any
+                    const NewToken4 ntok = new_token4(a, b, g, n, lane, lds_knew);
+                    patch_tile4(t[0], ntok, lds_knew, lane);
+                    pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0), ntok.slot, t[0].v,
+                                          ntok.ks, ntok.vs};
+                }
+            }
+            chunk_step4<1, true>(a, t, tb + c0, t_end, qv, qsum, lane, lds, m_run, l_lane, z_lane, acc0,
+                                 acc1);
+        }
+    }
+    const float l_sum = wave_sum((lane & 3) == 0 ? l_lane : 0.0f);
+    const float z_sum = wave_sum((lane & 3) == 0 ? z_lane : 0.0f);
+    acc0 += z_sum;
+    acc1 += z_sum;
+
+    if (lo == 0 && has_last) {
+        const float inv = a.v_scale / l_sum;
+        const half2_t r = {(_Float16)(acc0 * inv), (_Float16)(acc1 * inv)};
+        *reinterpret_cast<half2_t*>(a.out + orow + 2 * lane) = r;
+    } else {
+        const int64_t prow = h * rmul + radd;
+        *reinterpret_cast<float2*>(a.part_o + prow * kDim + 2 * lane) = make_float2(acc0, acc1);
+        if (lane == 0) {
+            a.part_m[prow] = m_run;
+            a.part_l[prow] = l_sum;
+        }
+    }
+}
+
+// BAL: grid (query head, wave of the balanced split); otherwise (query head, partition, sequence)
+// with fixed partitions, as in the 8-bit kernel; three waves per SIMD there keep the eight-tile
+// chunks in registers.
+template <int TW, bool APPEND, bool BAL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 3, 8))) void attn_partition_valu4(
+    KernelParams a) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[TW * 32];
+    __shared__ u32x4 lds_knew[APPEND ? 4 : 1];
+    const int lane = threadIdx.x;
+    const int h = blockIdx.x;
+    const int g = h / (a.Hq / a.Hkv);
+    uint8_t* knew = reinterpret_cast<uint8_t*>(lds_knew);
+    PendingAppend4 pend{-1, 0, u32x4{0u, 0u, 0u, 0u}, f32x2{0.0f, 0.0f}, f32x2{0.0f, 0.0f}};
+    if constexpr (BAL) {
+        const int w = blockIdx.y;
+        for_each_segment(a, w, h == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
+            mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, knew, pend);
+        });
+        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+    } else {
+        const int p = blockIdx.y;
+        const int b = blockIdx.z;
+        const int n = a.ctx[b];
+        if (n <= 0) {
+            if (p == 0) *reinterpret_cast<uint32_t*>(a.out + ((size_t)b * a.Hq + h) * kDim + 2 * lane) = 0u;
+            return;
+        }
+        const int nt = tiles_of(n);
+        const int lo = p * (a.PS / kBlock);
+        if (lo >= nt) return;
+        const int hi = min(nt, lo + a.PS / kBlock);
+        mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane, lds,
+                                 knew, pend);
+        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+    }
+}
+
+#ifndef KVQ_MHA4_TILES
+#define KVQ_MHA4_TILES 8
+#endif
+
+template <bool BAL>
+void launch_mha4(const KernelParams& kp, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+    const dim3 grid = BAL ? dim3((unsigned)kp.Hq, (unsigned)kp.NW)
+                          : dim3((unsigned)kp.Hq, (unsigned)kp.P, (unsigned)kp.B);
+    if (kp.k_new)
+        launch_timed(attn_partition_valu4<KVQ_MHA4_TILES, true, BAL>, grid, kp, stream, t0, t1);
+    else
+        launch_timed(attn_partition_valu4<KVQ_MHA4_TILES, false, BAL>, grid, kp, stream, t0, t1);
+}
+
+}  // namespace
+
+void launch_partition_mha4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (kp.NW > 0)
+        launch_mha4<true>(kp, stream, start, stop);
+    else
+        launch_mha4<false>(kp, stream, start, stop);
+}
+
+}  // namespace kvq

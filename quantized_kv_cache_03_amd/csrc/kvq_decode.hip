@@ -8,6 +8,7 @@
 // second kernel merges the partials with the log-sum-exp rule (flash-decoding split-K).  A fused
 // decode step appends the new token inside the partition kernel (see the two kernel files).
 #include "kvq_attn.h"
+#include "kvq_int4.h"
 
 namespace kvq {
 
@@ -99,7 +100,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.PS = a.partition_size;
     kp.NW = a.balanced_waves;
     kp.S = a.balanced_waves + a.batch;
-    const bool fp8 = c.dtype != KVQ_INT8;
+    const bool fp8 = is_fp8(c.dtype);
     // the decoders give code values divided by code_unit (a power of two): fold it into the scales
     const float unit_scale = fp8 ? c.kv_scale * code_unit(c.dtype) : 1.0f;
     kp.qk_scale = a.sm_scale * kLog2e * unit_scale;
@@ -108,7 +109,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.k_new = a.k_new;
     kp.v_new = a.v_new;
 
-    if (kp.Hq == kp.Hkv)
+    if (c.dtype == KVQ_INT4)
+        launch_partition_mha4(kp, stream, main_begin, main_end);
+    else if (kp.Hq == kp.Hkv)
         launch_partition_mha(kp, c.dtype, stream, main_begin, main_end);
     else
         launch_partition_gqa(kp, c.dtype, stream, main_begin, main_end);

@@ -1,0 +1,61 @@
+// kvq_int4.h -- device helpers of the INT4 cache: the row encoder, the nibble decoder and the tile
+// geometry.
+//
+// The online INT4 KV cache ("[Feature] TurboMind support W8A8 or FP8 KV Cache" names INT4 beside
+// the online INT8 cache), read as asymmetric 4-bit codes with one fp32 (scale, zero point) pair per
+// (token, KV head): zp = min x, s = fl32(fl32(max x - zp) / 15),
+// q = clamp(rne(fl32(fl32(x - zp) / s)), 0, 15), value q s + zp; two codes per byte.  Nothing here
+// is shared with the CPU oracle.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));  // a (scale, zero point) pair
+
+// INT4 code of x for a row with zero point zp (its minimum) and scale s = fl32(range / 15) > 0:
+// clamp(rne(fl32(fl32(x - zp) / s)), 0, 15); a constant row (s == 0) gives 0.
+__device__ __forceinline__ uint32_t encode_int4(float x, float zp, float s) {
+#pragma clang fp contract(off)
+    if (s == 0.0f) return 0u;
+    const float r = fminf(fmaxf(__builtin_rintf((x - zp) / s), 0.0f), 15.0f);
+    return (uint32_t)r;
+}
+
+// The eight 4-bit codes of w (nibble i = code i) as exact small integers in fp16, in the pairs
+// (i, i + 4): a nibble placed in the low bits of a half with high byte 0x64 is the binary16 number
+// 1024 + n, and subtracting 1024 is exact.  Callers pair their other operand the same way.
+__device__ __forceinline__ void int4x8_to_f16(uint32_t w, half2_t (&h)[4]) {
+    const half2_t off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    h[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | 0x64006400u) + off;
+    h[1] = __builtin_bit_cast(half2_t, ((w >> 4) & 0x000F000Fu) | 0x64006400u) + off;
+    h[2] = __builtin_bit_cast(half2_t, ((w >> 8) & 0x000F000Fu) | 0x64006400u) + off;
+    h[3] = __builtin_bit_cast(half2_t, ((w >> 12) & 0x000F000Fu) | 0x64006400u) + off;
+}
+
+// Tile geometry (1 KiB per tile): the K byte of dim d of token t (its low nibble holds the even
+// dim), and the V byte of token t of dim d (its low nibble holds the even token).
+constexpr int kTileBytes4 = kTileBytes / 2;
+__device__ __forceinline__ uint32_t k_byte4(int t, int d) {
+    return (uint32_t)(d / 32) * 256u + (uint32_t)t * 16u + (uint32_t)((d % 32) / 2);
+}
+__device__ __forceinline__ uint32_t v_byte4(int t, int d) {
+    return (uint32_t)d * 8u + (uint32_t)(t / 2);
+}
+
+__device__ __forceinline__ float wave_min(float v) {
+    v = fminf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = fminf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = fminf(v, dpp<0x141>(v));  // row_half_mirror
+    v = fminf(v, dpp<0x128>(v));  // row_ror:8
+    v = fminf(v, __shfl_xor(v, 16));
+    v = fminf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Partition kernel of the INT4 cache for one query head per KV head (kvq_attn_mha4.hip).
+struct KernelParams;
+void launch_partition_mha4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+}  // namespace kvq

@@ -8,6 +8,11 @@
 
 namespace kvq {
 
+// The formats with one per-tensor scale (the FP8 flavours); INT8 and INT4 scale per token.
+constexpr bool is_fp8(int dtype) {
+    return dtype == KVQ_FP8_E4M3 || dtype == KVQ_FP8_E5M2 || dtype == KVQ_FP8_E4M3FNUZ;
+}
+
 // Launch parameters of the decode-attention kernels, resolved by the ABI layer.
 struct DecodeArgs {
     const kvq_cache* cache;

@@ -341,7 +341,7 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
     a.R = 16 / a.G;
     const int rows_per_wave = KVQ_PREFILL_BLOCKS * a.R;
     a.row_tiles = (p.max_q_len + rows_per_wave - 1) / rows_per_wave;
-    const bool fp8 = c.dtype != KVQ_INT8;
+    const bool fp8 = is_fp8(c.dtype);
     // the decoders give code values divided by code_unit (a power of two): fold it into the scales
     const float unit_scale = fp8 ? c.kv_scale * code_unit(c.dtype) : 1.0f;
     a.qk_scale = p.sm_scale * kLog2e * unit_scale;

@@ -18,6 +18,12 @@ from . import workloads as W
 _CHUNK_ROWS = 1 << 20
 
 
+def kv_bytes_per_token(dtype: str) -> int:
+    """Bytes one (token, KV head) occupies in the cache: K and V codes plus their per-token scale
+    (INT8) or (scale, zero point) pair (INT4)."""
+    return {"int8": 2 * W.HEAD_DIM + 8, "int4": W.HEAD_DIM + 16}.get(dtype, 2 * W.HEAD_DIM)
+
+
 class DeviceCase:
     def __init__(self, w: W.Workload, device: str = "cuda", spare_blocks: int = 0,
                  keep_host_rows: bool = False, poison: bool = True, verbose: bool = False,
@@ -134,18 +140,18 @@ class DeviceCase:
         """Bytes the decode step must move at least once (see the measurement notes)."""
         w = self.w
         sctx = int(self.ctx.sum())
-        per_tok = 2 * W.HEAD_DIM + (8 if w.dtype == "int8" else 0)
+        per_tok = kv_bytes_per_token(w.dtype)
         kv = sctx * w.num_kv_heads * per_tok
         qo = 2 * self.B * w.num_q_heads * W.HEAD_DIM * 2
         table = 4 * int(((self.ctx + 15) // 16).sum()) + 4 * self.B
-        append = self.B * w.num_kv_heads * (2 * W.HEAD_DIM * 2 + 2 * W.HEAD_DIM +
-                                             (8 if w.dtype == "int8" else 0))
+        # append: the fp16 K and V rows in, their codes and scales out
+        append = self.B * w.num_kv_heads * (2 * W.HEAD_DIM * 2 + per_tok)
         return kv + qo + table + append
 
     def attention_bytes(self) -> int:
         """Algorithmic bytes of the attention alone (codes, scales, table, q in, out)."""
         w = self.w
         sctx = int(self.ctx.sum())
-        per_tok = 2 * W.HEAD_DIM + (8 if w.dtype == "int8" else 0)
+        per_tok = kv_bytes_per_token(w.dtype)
         return (sctx * w.num_kv_heads * per_tok + 2 * self.B * w.num_q_heads * W.HEAD_DIM * 2
                 + 4 * int(((self.ctx + 15) // 16).sum()) + 4 * self.B)

@@ -13,11 +13,11 @@ from dataclasses import dataclass
 
 import torch
 
-FP8_E4M3, FP8_E5M2, INT8, FP8_E4M3FNUZ = 1, 2, 3, 4
+FP8_E4M3, FP8_E5M2, INT8, FP8_E4M3FNUZ, INT4 = 1, 2, 3, 4, 5
 HEAD_DIM = 128
 BLOCK_SIZE = 16
 DTYPE_NAMES = {"fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3, "fp8_e5m2": FP8_E5M2, "int8": INT8,
-               "fp8_e4m3fnuz": FP8_E4M3FNUZ}
+               "fp8_e4m3fnuz": FP8_E4M3FNUZ, "int4": INT4}
 
 OK, ERR_ARG, ERR_DTYPE, ERR_SHAPE, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 
@@ -114,8 +114,9 @@ class PagedKVCache:
     """Device tensors of one layer's paged cache (layouts as in kvq.h)."""
     dtype: int
     k_cache: torch.Tensor           # uint8 [num_blocks][Hkv][8][16][16]: 16-dim chunks x 16 tokens
-    v_cache: torch.Tensor           # uint8 [num_blocks][Hkv][128][16]
-    k_scale: torch.Tensor | None    # float32 [num_blocks][Hkv][16] (INT8)
+                                    # (INT4: [num_blocks][Hkv][4][16][16], 32-dim chunks)
+    v_cache: torch.Tensor           # uint8 [num_blocks][Hkv][128][16] (INT4: [..][128][8])
+    k_scale: torch.Tensor | None    # float32 [num_blocks][Hkv][16] (INT8), [..][16][2] (INT4)
     v_scale: torch.Tensor | None
     kv_scale: float = 1.0
 
@@ -133,13 +134,15 @@ class PagedKVCache:
         if isinstance(dtype, str):
             dtype = dtype_from_string(dtype)
         fill = 0x7F if poison else 0
-        k = torch.full((num_blocks, num_kv_heads, HEAD_DIM // 16, BLOCK_SIZE, 16), fill, dtype=torch.uint8,
+        per = 2 if dtype == INT4 else 1  # codes per byte
+        k = torch.full((num_blocks, num_kv_heads, HEAD_DIM // (16 * per), BLOCK_SIZE, 16), fill,
+                       dtype=torch.uint8, device=device)
+        v = torch.full((num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE // per), fill, dtype=torch.uint8,
                        device=device)
-        v = torch.full((num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE), fill, dtype=torch.uint8, device=device)
         ks = vs = None
-        if dtype == INT8:
-            ks = torch.full((num_blocks, num_kv_heads, BLOCK_SIZE), float("nan") if poison else 0.0,
-                            dtype=torch.float32, device=device)
+        if dtype in (INT8, INT4):
+            shape = (num_blocks, num_kv_heads, BLOCK_SIZE) + ((2,) if dtype == INT4 else ())
+            ks = torch.full(shape, float("nan") if poison else 0.0, dtype=torch.float32, device=device)
             vs = torch.full_like(ks, float("nan") if poison else 0.0)
         return PagedKVCache(dtype, k, v, ks, vs, float(kv_scale))
 

@@ -7,7 +7,7 @@ import oracle
 from quantized_kv_cache_03_amd import workloads as W
 
 DT = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
-      "fp8_e4m3fnuz": oracle.E4M3FNUZ}
+      "fp8_e4m3fnuz": oracle.E4M3FNUZ, "int4": oracle.INT4}
 
 # Attention gate: |gpu - oracle| <= ATOL + RTOL * |oracle| element by element, on the same codes.
 ATOL = 1e-3

@@ -43,6 +43,8 @@ CASES = [
     # the E4M3FNUZ mode, on both kernels
     ("llama2-7b-mha-e4m3fnuz", [900, 33, 1600], {"num_q_heads": 4, "num_kv_heads": 4}),
     ("llama3-70b-gqa-e4m3fnuz-32k", [2100, 7], {"num_q_heads": 16, "num_kv_heads": 2}),
+    # the INT4 mode (one query head per KV head)
+    ("llama2-7b-mha-int4", [900, 33, 1600, 1, 17], {"num_q_heads": 4, "num_kv_heads": 4}),
 ]
 
 
@@ -156,6 +158,9 @@ BALANCED_CASES = [
     ("llama2-7b-mha-e4m3", [6000], {"num_q_heads": 1, "num_kv_heads": 1}),
     # all sequences empty
     ("tiny-e4m3", [0, 0, 0], {"num_q_heads": 2, "num_kv_heads": 2}),
+    # INT4: ragged, empty and long sequences
+    ("llama2-7b-mha-int4", [0, 3, 17, 1, 0, 40, 2, 300] * 12, {"num_q_heads": 2, "num_kv_heads": 2}),
+    ("llama2-7b-mha-int4", [7000, 1], {"num_q_heads": 1, "num_kv_heads": 1}),
 ]
 
 

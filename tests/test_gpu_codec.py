@@ -9,7 +9,7 @@ from gpu_common import say
 pytestmark = pytest.mark.gpu
 
 FMT = {"fp8_e4m3": oracle.E4M3, "fp8_e5m2": oracle.E5M2, "int8": oracle.INT8,
-       "fp8_e4m3fnuz": oracle.E4M3FNUZ}
+       "fp8_e4m3fnuz": oracle.E4M3FNUZ, "int4": oracle.INT4}
 
 
 @pytest.fixture(scope="module")
@@ -138,3 +138,78 @@ def test_append_one_row_per_sequence_leaves_other_slots(K):
         np.testing.assert_array_equal(dc.v_cache.cpu().numpy().reshape(oc.v.shape), oc.v)
         if dtype == "int8":
             np.testing.assert_array_equal(dc.k_scale.cpu().numpy().view(np.uint32), oc.ks.view(np.uint32))
+
+
+def test_dequant_int4_every_code(K):
+    """Every 4-bit code in both nibbles of K and V bytes, with random (scale, zero point) pairs,
+    through kvq_dequant: fl32(q s + zp), bit for bit."""
+    import torch
+    say("[dequant every code] int4")
+    r = np.random.default_rng(6)
+    Hkv, nb = 2, 3
+    kcodes = np.empty((nb, Hkv, 1024), np.uint8)
+    vcodes = np.empty_like(kcodes)
+    for blk in range(nb):
+        for g in range(Hkv):
+            kcodes[blk, g] = np.tile(np.arange(256, dtype=np.uint8), 4)
+            vcodes[blk, g] = r.permutation(kcodes[blk, g])
+    ks = np.stack([r.uniform(1e-3, 2.0, (nb, Hkv, 16)), r.uniform(-50, 50, (nb, Hkv, 16))], -1).astype(np.float32)
+    vs = np.stack([r.uniform(1e-3, 2.0, (nb, Hkv, 16)), r.uniform(-50, 50, (nb, Hkv, 16))], -1).astype(np.float32)
+    ks[0, 0, 3] = (0.0, 1.5)  # a constant row: s = 0
+    oc = oracle.Cache(oracle.INT4, nb, Hkv, 1.0, kcodes, vcodes, ks, vs)
+    bt = np.array([[2, 0, 1]], np.int32)
+    ctx = np.array([45], np.int32)
+    L = 48
+    ek, ev = oracle.dequant(oc, bt, ctx, L)
+    dc = K.PagedKVCache.allocate("int4", nb, Hkv)
+    dc.k_cache.copy_(torch.from_numpy(kcodes).view(dc.k_cache.shape))
+    dc.v_cache.copy_(torch.from_numpy(vcodes).view(dc.v_cache.shape))
+    dc.k_scale.copy_(torch.from_numpy(ks))
+    dc.v_scale.copy_(torch.from_numpy(vs))
+    gk, gv = K.dequant(dc, torch.from_numpy(bt).cuda(), torch.from_numpy(ctx).cuda(), L)
+    gk, gv = gk.cpu().numpy(), gv.cpu().numpy()
+    for name, g, e in (("K", gk, ek), ("V", gv, ev)):
+        okm = ~np.isnan(e)
+        assert okm[0, :, :45].all()
+        np.testing.assert_array_equal(g[okm].view(np.uint32), e[okm].view(np.uint32), err_msg=name)
+
+
+def test_append_int4_rows(K):
+    """Ragged bulk append of INT4 rows, including constant rows, exact ties, fp16 subnormals and
+    rows far from zero, and neighbouring tokens of one V byte written by different waves of the
+    same launch: codes and (scale, zero point) pairs bit for bit."""
+    import torch
+    say("[append int4 rows]")
+    r = np.random.default_rng(10)
+    n, Hkv = 77, 3
+    x = r.standard_normal((n, Hkv, 128), dtype=np.float32)
+    x[:, :, :4] *= 20
+    x[5] = 0.0                                   # constant (zero) rows
+    x[6, 0, :] = 3.0                             # a constant non-zero row
+    x[8, 1, :] = 0.0
+    x[8, 1, 0] = 15.0                            # s = 1: exact ties below
+    x[8, 1, 1:7] = [0.5, 1.5, 2.5, 3.5, 13.5, 14.5]
+    x[7, 1, :] = -1e-7                           # fp16 subnormals
+    x[9] = x[9] * np.float32(2.0) + np.float32(250.0)   # far from zero
+    xk = x.astype(np.float16)
+    xv = (-x[::-1]).astype(np.float16).copy()
+    ctx = np.array([30, 47], np.int32)
+    bt = np.array([[4, 1, -1], [0, 3, 2]], np.int32)
+    cu = np.array([0, 30, 77], np.int32)
+    oc = oracle.Cache(oracle.INT4, 6, Hkv)
+    oracle.append(oc, xk, xv, bt, ctx, cu)
+    dc = K.PagedKVCache.allocate("int4", 6, Hkv)
+    K.append(dc, torch.from_numpy(xk).cuda(), torch.from_numpy(xv).cuda(), torch.from_numpy(bt).cuda(),
+             torch.from_numpy(ctx).cuda(), cu_new_lens=torch.from_numpy(cu).cuda(), num_new_rows=77)
+    np.testing.assert_array_equal(dc.k_cache.cpu().numpy().reshape(oc.k.shape), oc.k)
+    np.testing.assert_array_equal(dc.v_cache.cpu().numpy().reshape(oc.v.shape), oc.v)
+    np.testing.assert_array_equal(dc.k_scale.cpu().numpy().view(np.uint32), oc.ks.view(np.uint32))
+    np.testing.assert_array_equal(dc.v_scale.cpu().numpy().view(np.uint32), oc.vs.view(np.uint32))
+    # one more row per sequence (odd and even slots): only that token's nibbles change
+    rows = r.standard_normal((2, Hkv, 128)).astype(np.float16)
+    ctx2 = np.array([31, 48], np.int32)
+    oracle.append(oc, rows, rows[::-1].copy(), bt, ctx2)
+    K.append(dc, torch.from_numpy(rows).cuda(), torch.from_numpy(rows[::-1].copy()).cuda(),
+             torch.from_numpy(bt).cuda(), torch.from_numpy(ctx2).cuda())
+    np.testing.assert_array_equal(dc.k_cache.cpu().numpy().reshape(oc.k.shape), oc.k)
+    np.testing.assert_array_equal(dc.v_cache.cpu().numpy().reshape(oc.v.shape), oc.v)

@@ -5,7 +5,8 @@ binades, with a per-tensor scale that lifts them to values of order one, so that
 product that flushed subnormal inputs to zero, or mis-scaled the lowest binade, moves the output by
 far more than the gate.  E5M2's subnormals decode to binary16 subnormals, and the E4M3FNUZ decoder
 produces binary16 subnormals for its own; E4M3's decode to binary16 normals.  INT8 takes codes
-over the whole [-127, 127] range with random per-token scales.  Decode (balanced split and fixed
+over the whole [-127, 127] range with random per-token scales, INT4 every nibble with random
+(scale, zero point) pairs.  Decode (balanced split and fixed
 partitions) and prefill both run on the same cache, for one query head per KV head and for groups
 of 4 and 8, against the oracle on the same codes.
 """
@@ -30,12 +31,14 @@ LOW = {
 def _codes(dtype, shape, r):
     if dtype == "int8":
         return r.integers(-127, 128, size=shape).astype(np.int8).view(np.uint8)
+    if dtype == "int4":
+        return r.integers(0, 256, size=shape[:-1] + (shape[-1] // 2,)).astype(np.uint8)
     pool = np.array(LOW[dtype][0], np.uint8)
     return pool[r.integers(0, len(pool), size=shape)]
 
 
-@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2", "fp8_e4m3fnuz", "int8"])
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("dtype,Hq,Hkv", [(d, hq, hk) for d in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3fnuz", "int8")
+                                           for hq, hk in ((4, 4), (8, 2), (16, 2))] + [("int4", 4, 4)])
 def test_attention_on_low_binade_codes(dtype, Hq, Hkv):
     import torch
     if not torch.cuda.is_available():
@@ -59,6 +62,9 @@ def test_attention_on_low_binade_codes(dtype, Hq, Hkv):
     if dtype == "int8":
         ks = r.uniform(2.0 ** -9, 2.0 ** -6, (nb, Hkv, 16)).astype(np.float32)
         vs = r.uniform(2.0 ** -9, 2.0 ** -6, (nb, Hkv, 16)).astype(np.float32)
+    elif dtype == "int4":  # (scale, zero point): values zp .. zp + 15 s, of order one
+        ks = np.stack([r.uniform(0.02, 0.15, (nb, Hkv, 16)), r.uniform(-2, 1, (nb, Hkv, 16))], -1).astype(np.float32)
+        vs = np.stack([r.uniform(0.02, 0.15, (nb, Hkv, 16)), r.uniform(-2, 1, (nb, Hkv, 16))], -1).astype(np.float32)
     else:
         scale = LOW[dtype][1]
     oc = oracle.Cache(DT[dtype], nb, Hkv, scale, kcodes, vcodes, ks, vs)
@@ -76,6 +82,8 @@ def test_attention_on_low_binade_codes(dtype, Hq, Hkv):
         out = K.paged_decode_attn(dc, q_d, bt_d, ctx_d, L, partition_size=ps).cpu().numpy()
         st = assert_attn_close(out, ref, f"{dtype} decode partition {ps}")
         say(f"    decode partition {ps}: {st}")
+    if dtype == "int4":
+        return  # prefill over the INT4 cache is not built
     # prefill: the last nq tokens of each sequence as query rows
     nq = np.minimum(ctx, np.array([40, 1, 16, 17, 33], np.int32))
     cu_q = np.zeros(len(ctx) + 1, np.int32)

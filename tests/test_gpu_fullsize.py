@@ -1,4 +1,4 @@
-"""The five decode workloads (and the two E4M3FNUZ variants) at full size, in the launch
+"""The five decode workloads (and the E4M3FNUZ and INT4 variants) at full size, in the launch
 configuration the benchmark times.
 
 Each case fills the cache through kvq_append with all but each sequence's last token, runs one
@@ -16,7 +16,8 @@ from gpu_common import OracleTwin, assert_attn_close, assert_cache_bytes_equal, 
 pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny-e4m3", "llama2-7b-mha-e4m3", "llama3-8b-gqa-e5m2", "llama2-13b-mha-int8",
-         "llama3-70b-gqa-e4m3-32k", "llama2-7b-mha-e4m3fnuz", "llama3-70b-gqa-e4m3fnuz-32k"]
+         "llama3-70b-gqa-e4m3-32k", "llama2-7b-mha-e4m3fnuz", "llama3-70b-gqa-e4m3fnuz-32k",
+         "llama2-7b-mha-int4"]
 
 
 @pytest.mark.parametrize("name", NAMES)
