@@ -6,7 +6,8 @@
 // logits and the output factor as
 //     z_t   = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d)
 //     out_d = (sum_t p_t s_t c_td + sum_t p_t zp_t) / sum_t p_t,
-// so the codes enter the dot products as exact small integers and the scales stay per token.
+// so the codes enter the dot products exactly (as fp16 subnormals, int4x8_to_f16) and the scales
+// stay per token.
 //
 // One wave per (query head, share of the work), the structure of the 8-bit kernel
 // (kvq_attn_mha.hip): chunks of TW tiles with every load issued before any use, a running max /
@@ -45,32 +46,46 @@ __device__ __forceinline__ void load_tile4(const KernelParams& a, Tile4& t, int 
     t.vs = ldg_nt(reinterpret_cast<const f32x2*>(a.vs) + so);
 }
 
-// q . c over this lane's 32 dims; qv[4 j + i] pairs dims (8 j + i, 8 j + i + 4) of the chunk.
+// q . c over this lane's 32 dims, in units of 2^-24; qv[4 j + i] pairs dims (8 j + i, 8 j + i + 4)
+// of the chunk.  The even and odd nibble pairs (2^-24 and 2^-20 units) are summed apart.
 __device__ __forceinline__ float dot32_int4(const u32x4& k, const half2_t (&qv)[16]) {
     const uint32_t w[4] = {k.x, k.y, k.z, k.w};
-    float s = 0.0f;
+    float se = 0.0f, so = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         half2_t h[4];
         int4x8_to_f16(w[j], h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = dot2(h[i], qv[4 * j + i], s);
+        se = dot2(h[0], qv[4 * j + 0], se);
+        so = dot2(h[1], qv[4 * j + 1], so);
+        se = dot2(h[2], qv[4 * j + 2], se);
+        so = dot2(h[3], qv[4 * j + 3], so);
     }
-    return s;
+    return se + so * (kInt4Odd / kInt4Even);
 }
+
+// Accumulators of one output dim: the even and odd nibble pairs apart (2^-24 and 2^-20 units).
+struct Acc4 {
+    float e, o;
+};
 
 // acc += sum over the 8 tokens of one dword of a V row (tokens 8 half .. +7) of w_t c_t, with the
 // weights as fp16 (hi, lo) pairs for the tokens (8 half + i, 8 half + i + 4).
-__device__ __forceinline__ float pv8_int4(uint32_t codes8, const uint32_t* hi, const uint32_t* lo,
-                                          float acc) {
+__device__ __forceinline__ void pv8_int4(uint32_t codes8, const uint32_t* hi, const uint32_t* lo,
+                                         Acc4& acc) {
     half2_t h[4];
     int4x8_to_f16(codes8, h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc = dot2(h[i], __builtin_bit_cast(half2_t, hi[i]), acc);
-        acc = dot2(h[i], __builtin_bit_cast(half2_t, lo[i]), acc);
+    for (int i = 0; i < 4; i += 2) {
+        acc.e = dot2(h[i], __builtin_bit_cast(half2_t, hi[i]), acc.e);
+        acc.e = dot2(h[i], __builtin_bit_cast(half2_t, lo[i]), acc.e);
+        acc.o = dot2(h[i + 1], __builtin_bit_cast(half2_t, hi[i + 1]), acc.o);
+        acc.o = dot2(h[i + 1], __builtin_bit_cast(half2_t, lo[i + 1]), acc.o);
     }
-    return acc;
+}
+
+// An accumulator's value in code units.
+__device__ __forceinline__ float acc_value(const Acc4& a) {
+    return a.e * kInt4Even + a.o * kInt4Odd;
 }
 
 // One chunk of TW tiles.  The quad of token tk ends with identical logits; lane 4 tk publishes the
@@ -81,14 +96,14 @@ template <int TW, bool MASKED>
 __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (&t)[TW], int tile0,
                                             int t_end, const half2_t (&qv)[16], float qsum, int lane,
                                             uint16_t* lds, float& m_run, float& l_lane, float& z_lane,
-                                            float& acc0, float& acc1) {
+                                            Acc4& acc0, Acc4& acc1) {
     const int tk = lane >> 2;
     float z[TW];
     float cmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const float s = sum4(dot32_int4(t[i].k, qv));
-        z[i] = a.qk_scale * (s * t[i].ks.x + t[i].ks.y * qsum);
+        const float s = sum4(dot32_int4(t[i].k, qv));  // q . c in units of 2^-24
+        z[i] = a.qk_scale * (s * (t[i].ks.x * kInt4Even) + t[i].ks.y * qsum);
         if constexpr (MASKED) z[i] = ((tile0 + i) * kBlock + tk < t_end) ? z[i] : kNegInf;
         cmax = fmaxf(cmax, z[i]);
     }
@@ -96,8 +111,10 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    acc0 *= alpha;
-    acc1 *= alpha;
+    acc0.e *= alpha;
+    acc0.o *= alpha;
+    acc1.e *= alpha;
+    acc1.o *= alpha;
     l_lane *= alpha;
     z_lane *= alpha;
 
@@ -123,10 +140,10 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
         const u32x4 h0 = l4[0], h1 = l4[1], w0 = l4[2], w1 = l4[3];
         const uint32_t whi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
         const uint32_t wlo[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        acc0 = pv8_int4(t[i].v.x, whi, wlo, acc0);
-        acc0 = pv8_int4(t[i].v.y, whi + 4, wlo + 4, acc0);
-        acc1 = pv8_int4(t[i].v.z, whi, wlo, acc1);
-        acc1 = pv8_int4(t[i].v.w, whi + 4, wlo + 4, acc1);
+        pv8_int4(t[i].v.x, whi, wlo, acc0);
+        pv8_int4(t[i].v.y, whi + 4, wlo + 4, acc0);
+        pv8_int4(t[i].v.z, whi, wlo, acc1);
+        pv8_int4(t[i].v.w, whi + 4, wlo + 4, acc1);
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_wave_barrier();
@@ -259,7 +276,7 @@ __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h
 
     float m_run = kNegInf;
     float l_lane = 0.0f, z_lane = 0.0f;
-    float acc0 = 0.0f, acc1 = 0.0f;  // dims 2l and 2l + 1
+    Acc4 acc0{0.0f, 0.0f}, acc1{0.0f, 0.0f};  // dims 2l and 2l + 1
 
     for (int tb = lo; tb < hi; tb += 64) {
         const int nt_grp = min(64, hi - tb);
@@ -293,16 +310,15 @@ __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h
     }
     const float l_sum = wave_sum((lane & 3) == 0 ? l_lane : 0.0f);
     const float z_sum = wave_sum((lane & 3) == 0 ? z_lane : 0.0f);
-    acc0 += z_sum;
-    acc1 += z_sum;
+    const float o0 = acc_value(acc0) + z_sum, o1 = acc_value(acc1) + z_sum;
 
     if (lo == 0 && has_last) {
         const float inv = a.v_scale / l_sum;
-        const half2_t r = {(_Float16)(acc0 * inv), (_Float16)(acc1 * inv)};
+        const half2_t r = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
         *reinterpret_cast<half2_t*>(a.out + orow + 2 * lane) = r;
     } else {
         const int64_t prow = h * rmul + radd;
-        *reinterpret_cast<float2*>(a.part_o + prow * kDim + 2 * lane) = make_float2(acc0, acc1);
+        *reinterpret_cast<float2*>(a.part_o + prow * kDim + 2 * lane) = make_float2(o0, o1);
         if (lane == 0) {
             a.part_m[prow] = m_run;
             a.part_l[prow] = l_sum;

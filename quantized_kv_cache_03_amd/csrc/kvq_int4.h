@@ -23,15 +23,22 @@ __device__ __forceinline__ uint32_t encode_int4(float x, float zp, float s) {
     return (uint32_t)r;
 }
 
-// The eight 4-bit codes of w (nibble i = code i) as exact small integers in fp16, in the pairs
-// (i, i + 4): a nibble placed in the low bits of a half with high byte 0x64 is the binary16 number
-// 1024 + n, and subtracting 1024 is exact.  Callers pair their other operand the same way.
+// The eight 4-bit codes of w (nibble i = code i) as exact binary16 subnormals, in the pairs
+// (i, i + 4): a half whose bits are a nibble n alone is n * 2^-24, and one holding n << 4 is
+// n * 2^-20, so masking alone decodes --
+//   h[0] = nibbles (0, 4) * 2^-24,  h[1] = nibbles (1, 5) * 2^-20,
+//   h[2] = nibbles (2, 6) * 2^-24,  h[3] = nibbles (3, 7) * 2^-20.
+// Callers pair their other operand the same way, accumulate the 2^-24 and the 2^-20 pairs apart
+// and fold the powers of two back in (kInt4Even, kInt4Odd).  Products with an fp16 operand are
+// exact in fp32 (the dot-product and matrix instructions keep fp16 subnormals).
+constexpr float kInt4Even = 16777216.0f;  // 2^24
+constexpr float kInt4Odd = 1048576.0f;    // 2^20
 __device__ __forceinline__ void int4x8_to_f16(uint32_t w, half2_t (&h)[4]) {
-    const half2_t off = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    h[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | 0x64006400u) + off;
-    h[1] = __builtin_bit_cast(half2_t, ((w >> 4) & 0x000F000Fu) | 0x64006400u) + off;
-    h[2] = __builtin_bit_cast(half2_t, ((w >> 8) & 0x000F000Fu) | 0x64006400u) + off;
-    h[3] = __builtin_bit_cast(half2_t, ((w >> 12) & 0x000F000Fu) | 0x64006400u) + off;
+    const uint32_t w8 = w >> 8;
+    h[0] = __builtin_bit_cast(half2_t, w & 0x000F000Fu);
+    h[1] = __builtin_bit_cast(half2_t, w & 0x00F000F0u);
+    h[2] = __builtin_bit_cast(half2_t, w8 & 0x000F000Fu);
+    h[3] = __builtin_bit_cast(half2_t, w8 & 0x00F000F0u);
 }
 
 // Tile geometry (1 KiB per tile): the K byte of dim d of token t (its low nibble holds the even
