@@ -42,8 +42,9 @@
  *   INT4 (two codes per byte, the even element in the low nibble; tiles of 1 KiB):
  *     K codes  uint8 [num_blocks][num_kv_heads][4][16 tokens][16 bytes]: dim d of token t is in
  *              byte (d / 32) * 256 + t * 16 + (d % 32) / 2 of the tile, nibble d % 2
- *     V codes  uint8 [num_blocks][num_kv_heads][128 dims][8 bytes]: token t of dim d is in byte
- *              d * 8 + t / 2, nibble t % 2
+ *     V codes  uint8 [num_blocks][num_kv_heads][4][16][8][2 bytes]: token t of dim d is in byte
+ *              (t / 4) * 256 + (d % 16) * 16 + (d / 16) * 2 + (t % 4) / 2, nibble t % 2 (a 16-bit
+ *              unit holds four consecutive tokens of one dim)
  *     scales   float [num_blocks][num_kv_heads][16 tokens][2] = (scale, zero point), for K and V
  *   block_tables int32 [batch][max_blocks_per_seq]: logical block i of sequence b is physical block
  *                block_tables[b][i]; entries past a sequence's last block are never read.

@@ -47,9 +47,10 @@
  *     V codes [num_blocks][Hkv][128 dims][16 tokens]; INT8 scales [num_blocks][Hkv][16 tokens].
  *   - INT4 layout (two 4-bit codes per byte, the even one in the low nibble): K [num_blocks][Hkv]
  *     [4][16 tokens][16 bytes], dim d of token t in byte (d / 32) * 256 + t * 16 + (d % 32) / 2
- *     of its 1024-byte tile, nibble d % 2; V [num_blocks][Hkv][128 dims][8 bytes], token t of dim
- *     d in byte d * 8 + t / 2, nibble t % 2; (scale, zero point) pairs [num_blocks][Hkv][16][2] for
- *     K and for V.
+ *     of its 1024-byte tile, nibble d % 2; V [num_blocks][Hkv][4 token quads][16][8][2 bytes],
+ *     token t of dim d in byte (t / 4) * 256 + (d % 16) * 16 + (d / 16) * 2 + (t % 4) / 2, nibble
+ *     t % 2 (each 16-bit unit holds four consecutive tokens of one dim); (scale, zero point) pairs
+ *     [num_blocks][Hkv][16][2] for K and for V.
  *   - context_lens are post-append lengths; context_lens[b] == 0 gives an all-zero output row.
  *   - Query head h reads KV head h / (Hq / Hkv).
  *
@@ -283,7 +284,7 @@ static size_t k_off4(int Hkv, int blk, int g, int t, int d)
 static size_t v_off4(int Hkv, int blk, int g, int t, int d)
 {
     size_t tile = ((size_t)blk * Hkv + g) * (KVQO_BLOCK * KVQO_DIM / 2);
-    return tile + (size_t)d * (KVQO_BLOCK / 2) + (size_t)(t / 2);
+    return tile + (size_t)(t / 4) * 256 + (size_t)(d % 16) * 16 + (size_t)(d / 16) * 2 + (size_t)((t % 4) / 2);
 }
 static uint8_t get_nibble(const uint8_t *a, size_t off, int hi)
 {

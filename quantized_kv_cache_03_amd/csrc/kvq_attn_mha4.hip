@@ -15,11 +15,14 @@
 //   K tile (four 256-byte chunks of 32 dims x 16 tokens): lane l holds the 32 dims of chunk l % 4
 //     of token l / 4 -- one 16-byte load per lane reads the whole tile -- and two quad DPP sums
 //     finish each logit.
-//   V tile (dim-major, 8 bytes per dim): lane l holds the 16 tokens of dims 2l and 2l + 1 (16
-//     contiguous bytes), so each lane accumulates two whole output elements; the tile's 16 weights
-//     p_t s_t reach every lane as packed fp16 (hi, lo) pairs through LDS.
-// A dword of codes decodes to the pairs (i, i + 4) of its eight nibbles (int4x8_to_f16): the query
-// slice is paired the same way for K, and the weights are published in that order for V.
+//   V tile (four 256-byte token-quad blocks): lane l holds tokens 4 (l / 16) .. +3 of the eight
+//     dims l % 16 + 16 r (16 contiguous bytes; one load per lane again reads the whole tile) and
+//     accumulates those dims over its quad's tokens; the four quads' sums are added once per
+//     segment.  The weights p_t s_t of a quad reach its lanes as packed fp16 (hi, lo) pairs
+//     through LDS.
+// K dwords decode to the pairs (i, i + 4) of their eight nibbles (int4x8_to_f16) and the query
+// slice is paired the same way; V units decode to the token pairs (0, 2) and (1, 3) of a quad
+// (int4_unit_to_f16) and the weights are published in that order.
 #include "kvq_attn.h"
 #include "kvq_int4.h"
 
@@ -29,7 +32,8 @@ namespace {
 
 // The codes and scales one lane holds for one tile.
 //   k  : K codes of token l / 4, dims 32 (l % 4) .. +31
-//   v  : V codes of dims 2l (dwords x, y: tokens 0-7, 8-15) and 2l + 1 (dwords z, w)
+//   v  : V codes of tokens 4 (l / 16) .. +3 of dims l % 16 + 16 r: unit r in bits 16 (r % 2) .. +15
+//        of dword r / 2
 //   ks : (scale, zero point) of the K row of token l / 4; vs: of its V row
 struct Tile4 {
     u32x4 k, v;
@@ -63,24 +67,23 @@ __device__ __forceinline__ float dot32_int4(const u32x4& k, const half2_t (&qv)[
     return se + so * (kInt4Odd / kInt4Even);
 }
 
-// Accumulators of one output dim: the even and odd nibble pairs apart (2^-24 and 2^-20 units).
+// Accumulators of one output dim: the even and odd token pairs apart (2^-24 and 2^-20 units).
 struct Acc4 {
     float e, o;
 };
 
-// acc += sum over the 8 tokens of one dword of a V row (tokens 8 half .. +7) of w_t c_t, with the
-// weights as fp16 (hi, lo) pairs for the tokens (8 half + i, 8 half + i + 4).
-__device__ __forceinline__ void pv8_int4(uint32_t codes8, const uint32_t* hi, const uint32_t* lo,
-                                         Acc4& acc) {
-    half2_t h[4];
-    int4x8_to_f16(codes8, h);
-#pragma unroll
-    for (int i = 0; i < 4; i += 2) {
-        acc.e = dot2(h[i], __builtin_bit_cast(half2_t, hi[i]), acc.e);
-        acc.e = dot2(h[i], __builtin_bit_cast(half2_t, lo[i]), acc.e);
-        acc.o = dot2(h[i + 1], __builtin_bit_cast(half2_t, hi[i + 1]), acc.o);
-        acc.o = dot2(h[i + 1], __builtin_bit_cast(half2_t, lo[i + 1]), acc.o);
-    }
+// acc += sum over the quad's four tokens of w_t c_t for one 16-bit V unit, with the weights as
+// fp16 pairs: wq = (hi(t0, t2), hi(t1, t3), lo(t0, t2), lo(t1, t3)).
+// (The components are passed as plain words: a bit cast of a vector component such as wq.y reads
+// component x with this toolchain.)
+template <int SEL>
+__device__ __forceinline__ void pv_unit_int4(uint32_t w, const uint32_t (&wq)[4], Acc4& acc) {
+    half2_t e, o;
+    int4_unit_to_f16<SEL>(w, e, o);
+    acc.e = dot2(e, __builtin_bit_cast(half2_t, wq[0]), acc.e);
+    acc.e = dot2(e, __builtin_bit_cast(half2_t, wq[2]), acc.e);
+    acc.o = dot2(o, __builtin_bit_cast(half2_t, wq[1]), acc.o);
+    acc.o = dot2(o, __builtin_bit_cast(half2_t, wq[3]), acc.o);
 }
 
 // An accumulator's value in code units.
@@ -88,15 +91,15 @@ __device__ __forceinline__ float acc_value(const Acc4& a) {
     return a.e * kInt4Even + a.o * kInt4Odd;
 }
 
-// One chunk of TW tiles.  The quad of token tk ends with identical logits; lane 4 tk publishes the
-// token's weight w = p s_v as fp16 hi and lo halves at its place in the pairing (token t goes to
-// half (t % 8) / 4 of pair 4 (t / 8) + t % 4), and adds p zp_v to the lane's zero-point sum.
+// One chunk of TW tiles.  The four lanes of token tk (the K layout) end with identical logits; lane
+// 4 tk publishes the token's weight w = p s_v as fp16 hi and lo halves in its quad's 16 bytes of
+// LDS, in the order the V units pair the tokens, and adds p zp_v to the lane's zero-point sum.
 // MASKED handles a chunk reaching past the segment end (logits there become -inf, weights 0).
 template <int TW, bool MASKED>
 __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (&t)[TW], int tile0,
                                             int t_end, const half2_t (&qv)[16], float qsum, int lane,
                                             uint16_t* lds, float& m_run, float& l_lane, float& z_lane,
-                                            Acc4& acc0, Acc4& acc1) {
+                                            Acc4 (&acc)[8]) {
     const int tk = lane >> 2;
     float z[TW];
     float cmax = kNegInf;
@@ -111,14 +114,16 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    acc0.e *= alpha;
-    acc0.o *= alpha;
-    acc1.e *= alpha;
-    acc1.o *= alpha;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        acc[r].e *= alpha;
+        acc[r].o *= alpha;
+    }
     l_lane *= alpha;
     z_lane *= alpha;
 
-    const int slot = 2 * (4 * (tk >> 3) + (tk & 3)) + ((tk >> 2) & 1);  // half index of token tk
+    // half index of token tk: quad tk / 4, then (t0, t2, t1, t3) for hi and again for lo
+    const int slot = 8 * (tk >> 2) + (((tk & 1) << 1) | ((tk >> 1) & 1));
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
         const float pw = __builtin_amdgcn_exp2f(z[i] - m_new);
@@ -130,20 +135,26 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
         if ((lane & 3) == 0) {
             const _Float16 h = (_Float16)w;
             lds[i * 32 + slot] = __builtin_bit_cast(uint16_t, h);
-            lds[i * 32 + 16 + slot] = __builtin_bit_cast(uint16_t, (_Float16)(w - (float)h));
+            lds[i * 32 + 4 + slot] = __builtin_bit_cast(uint16_t, (_Float16)(w - (float)h));
         }
     }
     __builtin_amdgcn_wave_barrier();
+    const int quad = lane >> 4;
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const u32x4* l4 = reinterpret_cast<const u32x4*>(lds + i * 32);
-        const u32x4 h0 = l4[0], h1 = l4[1], w0 = l4[2], w1 = l4[3];
-        const uint32_t whi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-        const uint32_t wlo[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        pv8_int4(t[i].v.x, whi, wlo, acc0);
-        pv8_int4(t[i].v.y, whi + 4, wlo + 4, acc0);
-        pv8_int4(t[i].v.z, whi, wlo, acc1);
-        pv8_int4(t[i].v.w, whi + 4, wlo + 4, acc1);
+        // the halves were stored as 16-bit values: read them back through memcpy, not a vector
+        // pointer of another type
+        u32x4 wv;
+        __builtin_memcpy(&wv, lds + i * 32 + 8 * quad, sizeof(wv));
+        const uint32_t wq[4] = {wv.x, wv.y, wv.z, wv.w};
+        pv_unit_int4<0>(t[i].v.x, wq, acc[0]);
+        pv_unit_int4<1>(t[i].v.x, wq, acc[1]);
+        pv_unit_int4<0>(t[i].v.y, wq, acc[2]);
+        pv_unit_int4<1>(t[i].v.y, wq, acc[3]);
+        pv_unit_int4<0>(t[i].v.z, wq, acc[4]);
+        pv_unit_int4<1>(t[i].v.z, wq, acc[5]);
+        pv_unit_int4<0>(t[i].v.w, wq, acc[6]);
+        pv_unit_int4<1>(t[i].v.w, wq, acc[7]);
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_wave_barrier();
@@ -151,15 +162,14 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
 
 // The appended token of a fused decode step, encoded with the append kernel's arithmetic: lane l
 // holds K dims 2l, 2l + 1 and V dims 2l, 2l + 1 of the new row.  The token's 64 K bytes go to LDS
-// in chunk order (byte l = dims 2l, 2l + 1); its V codes stay in the lane, which owns those dims.
+// in chunk order (byte l = dims 2l, 2l + 1), its 128 V codes to LDS by dim.
 struct NewToken4 {
     int slot;
-    uint32_t v0, v1;  // V codes of dims 2l and 2l + 1
-    f32x2 ks, vs;    // (scale, zero point) of the K and V rows
+    f32x2 ks, vs;     // (scale, zero point) of the K and V rows
 };
 
 __device__ __forceinline__ NewToken4 new_token4(const KernelParams& a, int b, int g, int n, int lane,
-                                                uint8_t* lds_k) {
+                                                uint8_t* lds_k, uint8_t* lds_v) {
 #pragma clang fp contract(off)
     NewToken4 nt;
     nt.slot = (n - 1) % kBlock;
@@ -172,8 +182,8 @@ __device__ __forceinline__ NewToken4 new_token4(const KernelParams& a, int b, in
     const float ksc = (wave_max(fmaxf(k0, k1)) - kz) / 15.0f;
     const float vsc = (wave_max(fmaxf(v0, v1)) - vz) / 15.0f;
     lds_k[lane] = (uint8_t)(encode_int4(k0, kz, ksc) | (encode_int4(k1, kz, ksc) << 4));
-    nt.v0 = encode_int4(v0, vz, vsc);
-    nt.v1 = encode_int4(v1, vz, vsc);
+    lds_v[2 * lane] = (uint8_t)encode_int4(v0, vz, vsc);
+    lds_v[2 * lane + 1] = (uint8_t)encode_int4(v1, vz, vsc);
     nt.ks = f32x2{ksc, kz};
     nt.vs = f32x2{vsc, vz};
     __builtin_amdgcn_wave_barrier();
@@ -185,21 +195,22 @@ __device__ __forceinline__ uint32_t set_nibble(uint32_t w, int i, uint32_t q) {
     return (w & ~(0xFu << sh)) | (q << sh);
 }
 
-// Replace the new token's codes and scales in the registers of its tile.
+// Replace the new token's codes and scales in the registers of its tile: K in the four lanes of
+// the token, V in the 16 lanes of its quad (token slot % 4 of each of their eight units).
 __device__ __forceinline__ void patch_tile4(Tile4& t, const NewToken4& nt, const uint8_t* lds_k,
-                                            int lane) {
+                                            const uint8_t* lds_v, int lane) {
     if ((lane >> 2) == nt.slot) {
         t.k = reinterpret_cast<const u32x4*>(lds_k)[lane & 3];
         t.ks = nt.ks;
         t.vs = nt.vs;
     }
-    const int i = nt.slot & 7;
-    if (nt.slot < 8) {  // wave-uniform
-        t.v.x = set_nibble(t.v.x, i, nt.v0);
-        t.v.z = set_nibble(t.v.z, i, nt.v1);
-    } else {
-        t.v.y = set_nibble(t.v.y, i, nt.v0);
-        t.v.w = set_nibble(t.v.w, i, nt.v1);
+    if ((lane >> 4) == (nt.slot >> 2)) {
+        const int dlo = lane & 15, i = nt.slot & 3;
+        uint32_t w[4] = {t.v.x, t.v.y, t.v.z, t.v.w};
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            w[r / 2] = set_nibble(w[r / 2], 4 * (r % 2) + i, lds_v[dlo + 16 * r]);
+        t.v = u32x4{w[0], w[1], w[2], w[3]};
     }
 }
 
@@ -208,14 +219,14 @@ __device__ __forceinline__ void patch_tile4(Tile4& t, const NewToken4& nt, const
 struct PendingAppend4 {
     int blk;       // -1 when nothing is pending (wave-uniform)
     int slot;
-    u32x4 v;       // this lane's V rows (dims 2l, 2l + 1), patched
+    u32x4 v;       // this lane's V codes (its quad's units), patched
     f32x2 ks, vs;
 };
 
-// Store a pending token: 16 K bytes in each of the four chunks (lanes 0..3, from LDS), the whole V
-// tile (each lane rewrites its two 8-byte rows with the new nibble in place; the other tokens'
-// nibbles are written back unchanged -- this wave is the tile's only reader and writer), and the
-// (scale, zero point) pairs.
+// Store a pending token: 16 K bytes in each of the four chunks (lanes 0..3, from LDS), the token's
+// quad block of the V tile (its 16 lanes rewrite their 16 bytes with the new nibbles in place; the
+// other tokens' nibbles are written back unchanged -- this wave is the tile's only reader and
+// writer), and the (scale, zero point) pairs.
 __device__ __forceinline__ void flush_append4(const KernelParams& a, PendingAppend4& pa,
                                               const uint8_t* lds_k, int g, int lane) {
     if (pa.blk < 0) return;
@@ -225,7 +236,8 @@ __device__ __forceinline__ void flush_append4(const KernelParams& a, PendingAppe
     if (lane < 4)
         __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(lds_k)[lane],
                                     reinterpret_cast<u32x4*>(kt + k_byte4(pa.slot, 32 * lane)));
-    __builtin_nontemporal_store(pa.v, reinterpret_cast<u32x4*>(vt + v_byte4(0, 2 * lane)));
+    if ((lane >> 4) == (pa.slot >> 2))
+        __builtin_nontemporal_store(pa.v, reinterpret_cast<u32x4*>(vt + v_byte4(pa.slot & ~3, lane & 15)));
     if (lane == 0) {
         const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
         reinterpret_cast<f32x2*>(const_cast<float*>(a.ks))[so] = pa.ks;
@@ -240,7 +252,8 @@ __device__ __forceinline__ void flush_append4(const KernelParams& a, PendingAppe
 template <int TW, bool APPEND>
 __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h, int g, int n, int nt,
                                              int lo, int hi, int64_t rmul, int64_t radd, int lane,
-                                             uint16_t* lds, uint8_t* lds_knew, PendingAppend4& pend) {
+                                             uint16_t* lds, uint8_t* lds_knew, uint8_t* lds_vnew,
+                                             PendingAppend4& pend) {
     const int tk = lane >> 2;
     const size_t orow = ((size_t)b * a.Hq + h) * kDim;
     const bool has_last = hi == nt;
@@ -272,11 +285,13 @@ __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h
     }
 
     const uint32_t k_off = 256u * ((uint32_t)lane & 3u) + 16u * (uint32_t)tk;
-    const uint32_t v_off = 16u * (uint32_t)lane;
+    const uint32_t v_off = 256u * ((uint32_t)lane >> 4) + 16u * ((uint32_t)lane & 15u);
 
     float m_run = kNegInf;
     float l_lane = 0.0f, z_lane = 0.0f;
-    Acc4 acc0{0.0f, 0.0f}, acc1{0.0f, 0.0f};  // dims 2l and 2l + 1
+    Acc4 acc[8];  // dims lane % 16 + 16 r, over this lane's token quad
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = Acc4{0.0f, 0.0f};
 
     for (int tb = lo; tb < hi; tb += 64) {
         const int nt_grp = min(64, hi - tb);
@@ -290,7 +305,7 @@ __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h
             for (int i = 0; i < TW; ++i)
                 load_tile4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c * TW + i), g, k_off, v_off, tk);
             chunk_step4<TW, false>(a, t, tb + c * TW, t_end, qv, qsum, lane, lds, m_run, l_lane, z_lane,
-                                   acc0, acc1);
+                                   acc);
         }
         for (int c0 = nfull * TW; c0 < nt_grp; ++c0) {
             Tile4 t[1];
@@ -298,27 +313,38 @@ __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h
             if constexpr (APPEND) {
                 if (tb + c0 == tile_new) {
                     flush_append4(a, pend, lds_knew, g, lane);  // an earlier sequence's token, if any
-                    const NewToken4 ntok = new_token4(a, b, g, n, lane, lds_knew);
-                    patch_tile4(t[0], ntok, lds_knew, lane);
+                    const NewToken4 ntok = new_token4(a, b, g, n, lane, lds_knew, lds_vnew);
+                    patch_tile4(t[0], ntok, lds_knew, lds_vnew, lane);
                     pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0), ntok.slot, t[0].v,
                                           ntok.ks, ntok.vs};
                 }
             }
-            chunk_step4<1, true>(a, t, tb + c0, t_end, qv, qsum, lane, lds, m_run, l_lane, z_lane, acc0,
-                                 acc1);
+            chunk_step4<1, true>(a, t, tb + c0, t_end, qv, qsum, lane, lds, m_run, l_lane, z_lane, acc);
         }
     }
     const float l_sum = wave_sum((lane & 3) == 0 ? l_lane : 0.0f);
     const float z_sum = wave_sum((lane & 3) == 0 ? z_lane : 0.0f);
-    const float o0 = acc_value(acc0) + z_sum, o1 = acc_value(acc1) + z_sum;
+    // the four quads' sums of each dim (lanes l, l ^ 16, l ^ 32, l ^ 48); lane (dlo, quad) keeps
+    // dims dlo + 16 (2 quad) and dlo + 16 (2 quad + 1)
+    const int quad = lane >> 4, dlo = lane & 15;
+    float o[2];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        float v = acc_value(acc[r]);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if ((r >> 1) == quad) o[r & 1] = v + z_sum;
+    }
+    const int d0 = dlo + 32 * quad;  // and d0 + 16
 
     if (lo == 0 && has_last) {
         const float inv = a.v_scale / l_sum;
-        const half2_t r = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
-        *reinterpret_cast<half2_t*>(a.out + orow + 2 * lane) = r;
+        a.out[orow + d0] = __builtin_bit_cast(uint16_t, (_Float16)(o[0] * inv));
+        a.out[orow + d0 + 16] = __builtin_bit_cast(uint16_t, (_Float16)(o[1] * inv));
     } else {
         const int64_t prow = h * rmul + radd;
-        *reinterpret_cast<float2*>(a.part_o + prow * kDim + 2 * lane) = make_float2(o0, o1);
+        a.part_o[prow * kDim + d0] = o[0];
+        a.part_o[prow * kDim + d0 + 16] = o[1];
         if (lane == 0) {
             a.part_m[prow] = m_run;
             a.part_l[prow] = l_sum;
@@ -334,6 +360,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 3,
     KernelParams a) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[TW * 32];
     __shared__ u32x4 lds_knew[APPEND ? 4 : 1];
+    __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
     const int lane = threadIdx.x;
     const int h = blockIdx.x;
     const int g = h / (a.Hq / a.Hkv);
@@ -342,7 +369,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 3,
     if constexpr (BAL) {
         const int w = blockIdx.y;
         for_each_segment(a, w, h == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
-            mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, knew, pend);
+            mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, knew, lds_vnew, pend);
         });
         if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
     } else {
@@ -358,7 +385,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 3,
         if (lo >= nt) return;
         const int hi = min(nt, lo + a.PS / kBlock);
         mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane, lds,
-                                 knew, pend);
+                                 knew, lds_vnew, pend);
         if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
     }
 }

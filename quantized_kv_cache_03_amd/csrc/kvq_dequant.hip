@@ -122,18 +122,20 @@ __global__ __launch_bounds__(64) void dequant_kernel4(
                 o[i] = __builtin_fmaf((float)((ws[i / 8] >> (4 * (i % 8))) & 0xFu), sz.x, sz.y);
         }
     }
-    // V: lane l reads the 16 tokens of dims 2l and 2l + 1 (two 8-byte rows)
+    // V: lane l reads tokens 4 (l / 16) .. +3 of the dims l % 16 + 16 r, r = 0..7 (unit r is bits
+    // 16 (r % 2) .. +15 of dword r / 2)
     {
-        const u32x4 w = ldg16(vc + tile + v_byte4(0, 2 * lane));
+        const int quad = lane >> 4, dlo = lane & 15;
+        const u32x4 w = ldg16(vc + tile + v_byte4(4 * quad, dlo));
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            const int d = 2 * lane + i / 16, tok = i % 16;
+            const int r = i / 4, d = dlo + 16 * r, tok = 4 * quad + i % 4;
             const int pos = tile_idx * kBlock + tok;
             if (pos < n) {
                 const f32x2 sz = vsz[tok];
                 v_out[obase + (size_t)pos * kDim + d] =
-                    __builtin_fmaf((float)((ws[i / 8] >> (4 * (i % 8))) & 0xFu), sz.x, sz.y);
+                    __builtin_fmaf((float)((ws[r / 2] >> (16 * (r % 2) + 4 * (i % 4))) & 0xFu), sz.x, sz.y);
             }
         }
     }

@@ -41,14 +41,31 @@ __device__ __forceinline__ void int4x8_to_f16(uint32_t w, half2_t (&h)[4]) {
     h[3] = __builtin_bit_cast(half2_t, w8 & 0x00F000F0u);
 }
 
-// Tile geometry (1 KiB per tile): the K byte of dim d of token t (its low nibble holds the even
-// dim), and the V byte of token t of dim d (its low nibble holds the even token).
+// Tile geometry (1 KiB per tile).
+//   K: four 256-byte chunks of 32 dims x 16 tokens; the byte of dim d of token t holds dims
+//      d & ~1 (low nibble) and d | 1.
+//   V: four 256-byte blocks, one per quad of tokens; in block t / 4, the 16 bytes at (d % 16) * 16
+//      hold the dims d % 16 + 16 r (r = 0..7) as 16-bit units of the quad's four tokens (bytes
+//      2r and 2r + 1: tokens 0, 1 and 2, 3 of the quad, the even one in the low nibble).  One
+//      16-byte load per lane reads a whole tile whether a lane is a (token quad, dim) piece of the
+//      MFMA operands or of the VALU kernel.
 constexpr int kTileBytes4 = kTileBytes / 2;
 __device__ __forceinline__ uint32_t k_byte4(int t, int d) {
     return (uint32_t)(d / 32) * 256u + (uint32_t)t * 16u + (uint32_t)((d % 32) / 2);
 }
 __device__ __forceinline__ uint32_t v_byte4(int t, int d) {
-    return (uint32_t)d * 8u + (uint32_t)(t / 2);
+    return (uint32_t)(t / 4) * 256u + (uint32_t)(d % 16) * 16u + (uint32_t)(d / 16) * 2u +
+           (uint32_t)((t % 4) / 2);
+}
+
+// The 16-bit unit of a V dword (SEL 0: bits 0-15, 1: bits 16-31: four tokens of one dim) as two
+// binary16 pairs (see int4x8_to_f16): e = tokens (0, 2) * 2^-24, o = tokens (1, 3) * 2^-20.
+template <int SEL>
+__device__ __forceinline__ void int4_unit_to_f16(uint32_t w, half2_t& e, half2_t& o) {
+    constexpr uint32_t sel = (SEL == 0) ? 0x0C010C00u : 0x0C030C02u;  // its bytes to the halves' low bytes
+    const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
+    e = __builtin_bit_cast(half2_t, x & 0x000F000Fu);
+    o = __builtin_bit_cast(half2_t, x & 0x00F000F0u);
 }
 
 __device__ __forceinline__ float wave_min(float v) {

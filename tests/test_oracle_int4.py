@@ -98,11 +98,13 @@ def unpack_k(codes, nb, Hkv):
 
 
 def unpack_v(codes, nb, Hkv):
-    """INT4 V codes as [block][head][token][dim]: byte d * 8 + t // 2, low nibble for even t."""
-    v = codes.reshape(nb, Hkv, 128, 8)
-    out = np.empty((nb, Hkv, 128, 16), np.uint8)
-    out[..., 0::2], out[..., 1::2] = v & 0x0F, v >> 4
-    return out.transpose(0, 1, 3, 2)
+    """INT4 V codes as [block][head][token][dim] from the documented layout: byte
+    (t // 4) * 256 + (d % 16) * 16 + (d // 16) * 2 + (t % 4) // 2, low nibble for even t."""
+    v = codes.reshape(nb, Hkv, 4, 16, 8, 2)          # [quad][d % 16][d // 16][byte of the quad]
+    nib = np.empty((nb, Hkv, 4, 16, 8, 4), np.uint8)  # [..][token within the quad]
+    nib[..., 0::2], nib[..., 1::2] = v & 0x0F, v >> 4
+    # -> [token = 4 quad + i][dim = 16 (d // 16) + d % 16]
+    return nib.transpose(0, 1, 2, 5, 4, 3).reshape(nb, Hkv, 16, 128)
 
 
 def test_int4_append_layout_and_poison(oracle_mod):

@@ -84,8 +84,11 @@ MUTATIONS = {
         "return tile + (size_t)(d / 32) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)((d % 32) / 2);",
         "return tile + (size_t)(d / 32) * (16 * KVQO_BLOCK) + (size_t)t * 16 + (size_t)((d % 32) % 16);"),
     "int4-v-token-major": (
-        "return tile + (size_t)d * (KVQO_BLOCK / 2) + (size_t)(t / 2);",
+        "return tile + (size_t)(t / 4) * 256 + (size_t)(d % 16) * 16 + (size_t)(d / 16) * 2 + (size_t)((t % 4) / 2);",
         "return tile + (size_t)t * (KVQO_DIM / 2) + (size_t)(d / 2);"),
+    "int4-v-dim-blocks-swapped": (
+        "return tile + (size_t)(t / 4) * 256 + (size_t)(d % 16) * 16 + (size_t)(d / 16) * 2 + (size_t)((t % 4) / 2);",
+        "return tile + (size_t)(t / 4) * 256 + (size_t)(d / 8) * 16 + (size_t)(d % 8) * 2 + (size_t)((t % 4) / 2);"),
     "int4-dequant-drops-zero-point": (
         "return (double)get_nibble(codes, off, hi) * (double)sz[2 * so] + (double)sz[2 * so + 1];",
         "return (double)get_nibble(codes, off, hi) * (double)sz[2 * so];"),
