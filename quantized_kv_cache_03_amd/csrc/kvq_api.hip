@@ -219,8 +219,6 @@ int decode_common(const char* where, const kvq_cache* cache, const void* k_new, 
         return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
-    if (cache->dtype == KVQ_INT4 && num_q_heads != cache->num_kv_heads)
-        return fail(KVQ_ERR_DTYPE, "INT4 decode attention is built for one query head per KV head only");
     if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
     if (partition_size != KVQ_PARTITION_BALANCED &&
         (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0))

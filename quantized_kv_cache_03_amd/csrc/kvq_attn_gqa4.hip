@@ -1,0 +1,361 @@
+// kvq_attn_gqa4.hip -- decode attention over the INT4 cache for grouped query heads (MFMA).
+//
+// The INT4 cache (asymmetric 4-bit codes, an fp32 (scale, zero point) pair per (token, KV head);
+// the online INT4 cache named beside INT8 in "[Feature] TurboMind support W8A8 or FP8 KV Cache"):
+//     z_t   = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d)
+//     out_d = (sum_t p_t s_t c_td + sum_t p_t zp_t) / sum_t p_t.
+// One wave per (KV head, share of the work) serves the G <= 16 query heads of the group, as the
+// 8-bit grouped kernel (kvq_attn_gqa.hip) does, with both products on v_mfma_f32_16x16x32_f16
+// (query heads padded to 16 columns).  Codes decode to exact binary16 subnormals by masking
+// (int4x8_to_f16 / int4_unit_to_f16): the even nibble pairs are worth 2^-24 per unit, the odd ones
+// 2^-20, so every operand holds only one of the two kinds and each product keeps two accumulators.
+//   S^T = K Q^T per tile: A = K (lane: token l % 16, the 32 dims of chunk l / 16 -- one 16-byte
+//       load per lane reads the tile), B = Q^T (lane: head l % 16, the same dims); two MFMAs for
+//       the even nibble pairs of the chunk's dims, two for the odd ones.  C: lane (head l % 16,
+//       tokens 4 (l / 16) .. +3).
+//   O^T += V^T P^T per chunk of four tiles and 16-dim row block: A = V^T (lane: dim l % 16 + 16 r,
+//       tokens 0 and 2 -- or 1 and 3 -- of quad l / 16 of each of the four tiles, straight from the
+//       lane's 16-byte V load), B = P^T with the weights the S^T accumulator left in the lane
+//       (tokens 4 (l / 16) .. +3 of each tile), split into fp16 hi + lo parts.
+#include "kvq_attn4.h"
+#include "kvq_mfma.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kTiles4 = 4;  // tiles per chunk: the P^T operand spans four tiles
+
+// This lane's share of one tile.
+struct TileG4 {
+    u32x4 k, v;      // K: token l % 16, chunk l / 16; V: quad l / 16, dims l % 16 + 16 r
+    float4_t ks, kz;  // K (scale, zero point) of tokens 4 (l / 16) .. +3
+    float4_t vs, vz;  // V (scale, zero point) of the same tokens
+};
+
+__device__ __forceinline__ void load_tile_g4(const KernelParams& a, TileG4& t, int blk, int g,
+                                             uint32_t off, int q4) {
+    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes4;
+    t.k = ldg16(a.kc + tile + off);
+    t.v = ldg16(a.vc + tile + off);
+    // (scale, zero point) pairs of four tokens: two 16-byte loads each for K and V
+    const size_t so = (((size_t)blk * a.Hkv + g) * kBlock + 4 * q4) * 2;
+    const float4_t k0 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+    const float4_t k1 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so + 4));
+    const float4_t v0 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
+    const float4_t v1 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so + 4));
+    t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
+    t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
+    t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};
+    t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
+}
+
+__device__ __forceinline__ void zero_tile_g4(TileG4& t) {
+    t.k = t.v = u32x4{0u, 0u, 0u, 0u};
+    t.ks = t.kz = t.vs = t.vz = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+__device__ __forceinline__ half8_v join4(half2_t a, half2_t b, half2_t c, half2_t d) {
+    return join8(a, b, c, d);
+}
+
+// The K operands of one tile: (even, odd) nibble pairs of dwords (0, 1) and (2, 3).
+__device__ __forceinline__ void k_operands(const u32x4& k, half8_v (&e)[2], half8_v (&o)[2]) {
+    const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    half2_t h0[4], h1[4], h2[4], h3[4];
+    int4x8_to_f16(w[0], h0);
+    int4x8_to_f16(w[1], h1);
+    int4x8_to_f16(w[2], h2);
+    int4x8_to_f16(w[3], h3);
+    e[0] = join4(h0[0], h0[2], h1[0], h1[2]);
+    o[0] = join4(h0[1], h0[3], h1[1], h1[3]);
+    e[1] = join4(h2[0], h2[2], h3[0], h3[2]);
+    o[1] = join4(h2[1], h2[3], h3[1], h3[3]);
+}
+
+// The dims of the K operands' k-slots, relative to the chunk's first dim: nibble pairs (i, i + 4)
+// of two dwords, the even pairs (i = 0, 2) or the odd ones (i = 1, 3).
+__device__ __forceinline__ int k_slot_dim(int dw0, int odd, int slot) {
+    const int dw = dw0 + slot / 4;               // dword of the slot
+    const int pair = (slot % 4) / 2;             // first or second pair of the dword's kind
+    const int i = 2 * pair + odd;                // nibble pair (i, i + 4)
+    return 8 * dw + i + 4 * (slot % 2);
+}
+
+// One chunk of kTiles4 tiles (tiles past the segment's end are zero, their tokens masked).
+template <bool APPEND>
+__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTiles4], int tile0, int t_end,
+                                         const half8_v (&qe)[2], const half8_v (&qo)[2], float qsum,
+                                         int q4, float& m_run, float& l_lane, float& z_lane,
+                                         float4_t (&acc_e)[8], float4_t (&acc_o)[8]) {
+    float z[kTiles4][4];
+    float cmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kTiles4; ++i) {
+        half8_v e[2], o[2];
+        k_operands(t[i].k, e, o);
+        float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};
+        se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[0], qe[0], se, 0, 0, 0);
+        so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[0], qo[0], so, 0, 0, 0);
+        se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[1], qe[1], se, 0, 0, 0);
+        so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[1], qo[1], so, 0, 0, 0);
+        const int pos0 = (tile0 + i) * kBlock + 4 * q4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float s = se[u] + so[u] * (kInt4Odd / kInt4Even);  // q . c in 2^-24 units
+            const float zz = a.qk_scale * (s * (t[i].ks[u] * kInt4Even) + t[i].kz[u] * qsum);
+            z[i][u] = (pos0 + u < t_end) ? zz : kNegInf;
+            cmax = fmaxf(cmax, z[i][u]);
+        }
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);  // finite: every chunk holds a valid token
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_lane *= alpha;
+    z_lane *= alpha;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        acc_e[r] *= alpha;
+        acc_o[r] *= alpha;
+    }
+    // P^T operands: the even tokens (0, 2) and the odd tokens (1, 3) of this lane's quad of each
+    // tile, as fp16 hi and lo parts of w = p s_v
+    half8_v we_hi, we_lo, wo_hi, wo_lo;
+#pragma unroll
+    for (int i = 0; i < kTiles4; ++i) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_new);
+            l_lane += pw;
+            const bool live = pw > 0.0f;  // masked slots may hold NaN scales
+            const float w = live ? pw * t[i].vs[u] : 0.0f;
+            z_lane += live ? pw * t[i].vz[u] : 0.0f;
+            const _Float16 hi = (_Float16)w;
+            const _Float16 lo = (_Float16)(w - (float)hi);
+            const int k = 2 * i + (u >> 1);  // slot: tile i, token u of the pair (0, 2) or (1, 3)
+            if (u & 1) {
+                wo_hi[k] = hi;
+                wo_lo[k] = lo;
+            } else {
+                we_hi[k] = hi;
+                we_lo[k] = lo;
+            }
+        }
+    }
+    // O^T += V^T P^T, row block r = dims 16 r .. +15
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        half2_t ve[kTiles4], vo[kTiles4];
+#pragma unroll
+        for (int i = 0; i < kTiles4; ++i) {
+            const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
+            if (r & 1)
+                int4_unit_to_f16<1>(w[r / 2], ve[i], vo[i]);
+            else
+                int4_unit_to_f16<0>(w[r / 2], ve[i], vo[i]);
+        }
+        const half8_v ae = join4(ve[0], ve[1], ve[2], ve[3]);
+        const half8_v ao = join4(vo[0], vo[1], vo[2], vo[3]);
+        acc_e[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc_e[r], 0, 0, 0);
+        acc_e[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc_e[r], 0, 0, 0);
+        acc_o[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc_o[r], 0, 0, 0);
+        acc_o[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc_o[r], 0, 0, 0);
+    }
+}
+
+// Replace the new token's codes and scales in the registers of its tile: K in the four lanes whose
+// operand row is the token, V and the scale pairs in the 16 lanes of its quad.
+__device__ __forceinline__ void patch_tile_g4(TileG4& t, const NewToken4& nt, const uint8_t* lds_k,
+                                              const uint8_t* lds_v, int lane) {
+    const int col = lane & 15, q4 = lane >> 4;
+    if (col == nt.slot) t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
+    patch_v_quad(t.v, nt.slot, lds_v, lane);
+    if (q4 == (nt.slot >> 2)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)  // (a constant element index keeps the vectors in registers)
+            if (u == (nt.slot & 3)) {
+                t.ks[u] = nt.ks.x;
+                t.kz[u] = nt.ks.y;
+                t.vs[u] = nt.vs.x;
+                t.vz[u] = nt.vs.y;
+            }
+    }
+}
+
+// The work of one segment -- tiles [lo, hi) of sequence b (n tokens, nt tiles): the final output
+// when the segment is the whole sequence, else a partial in row h * rmul + radd.
+template <bool APPEND>
+__device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g, int n, int nt, int lo,
+                                             int hi, int64_t rmul, int64_t radd, int lane,
+                                             uint8_t* lds_knew, uint8_t* lds_vnew, PendingAppend4& pend) {
+    const int col = lane & 15;  // query head within the group (B / C column), or A row
+    const int q4 = lane >> 4;   // k-group / C row group
+    const int G = a.Hq / a.Hkv;
+    const int h = g * G + col;  // this lane's query head (valid when col < G)
+    const int t_end = min(n, hi * kBlock);
+    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+    const int tile_new = (APPEND && hi == nt) ? nt - 1 : -1;
+
+    // Q^T operands over chunk q4's dims in the K operands' slot order, and sum(q) of the head
+    half8_v qe[2], qo[2];
+    float qsum = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) qe[m] = qo[m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
+    if (col < G) {
+        const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h) * kDim + 32 * q4;
+        uint16_t qv[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(qrow)[j];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                qv[8 * j + 2 * k] = (uint16_t)(ww[k] & 0xFFFFu);
+                qv[8 * j + 2 * k + 1] = (uint16_t)(ww[k] >> 16);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < 32; ++d) qsum += (float)__builtin_bit_cast(_Float16, qv[d]);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                qe[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 0, s)]);
+                qo[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 1, s)]);
+            }
+    }
+    qsum += __shfl_xor(qsum, 16);
+    qsum += __shfl_xor(qsum, 32);
+
+    float m_run = kNegInf;
+    float l_lane = 0.0f, z_lane = 0.0f;
+    float4_t acc_e[8], acc_o[8];  // O^T row blocks: dims 16 r + 4 q4 .. +3 of head col
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc_e[r] = acc_o[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const uint32_t off = 256u * (uint32_t)q4 + 16u * (uint32_t)col;
+
+    for (int tb = lo; tb < hi; tb += 64) {
+        const int nt_grp = min(64, hi - tb);
+        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        for (int c0 = 0; c0 < nt_grp; c0 += kTiles4) {
+            TileG4 t[kTiles4];
+#pragma unroll
+            for (int i = 0; i < kTiles4; ++i) {
+                if (c0 + i < nt_grp)
+                    load_tile_g4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                else
+                    zero_tile_g4(t[i]);
+            }
+            if constexpr (APPEND) {
+                const int inew = tile_new - (tb + c0);  // wave-uniform
+                if (inew >= 0 && inew < kTiles4) {
+                    flush_append4(a, pend, lds_knew, g, lane);  // an earlier sequence's token, if any
+                    const NewToken4 ntok = new_token4(a, b, g, n, lane, lds_knew, lds_vnew);
+#pragma unroll
+                    for (int i = 0; i < kTiles4; ++i)
+                        if (i == inew) {
+                            patch_tile_g4(t[i], ntok, lds_knew, lds_vnew, lane);
+                            pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0 + i), ntok.slot,
+                                                  t[i].v, ntok.ks, ntok.vs};
+                        }
+                }
+            }
+            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, qsum, q4, m_run, l_lane, z_lane, acc_e, acc_o);
+        }
+    }
+    // the head's weight sum and zero-point sum over the four row groups
+    float l_sum = l_lane + __shfl_xor(l_lane, 16);
+    l_sum += __shfl_xor(l_sum, 32);
+    float z_sum = z_lane + __shfl_xor(z_lane, 16);
+    z_sum += __shfl_xor(z_sum, 32);
+
+    if (col < G) {
+        float4_t o[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) o[r] = acc_e[r] * kInt4Even + acc_o[r] * kInt4Odd + z_sum;
+        if (lo == 0 && hi == nt) {
+            const float inv = a.v_scale / l_sum;
+            uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * kDim;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const half4_t v = {(_Float16)(o[r][0] * inv), (_Float16)(o[r][1] * inv),
+                                   (_Float16)(o[r][2] * inv), (_Float16)(o[r][3] * inv)};
+                *reinterpret_cast<half4_t*>(orow + 16 * r + 4 * q4) = v;
+            }
+        } else {
+            const int64_t prow = h * rmul + radd;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<float4_t*>(a.part_o + prow * kDim + 16 * r + 4 * q4) = o[r];
+            if (q4 == 0) {
+                a.part_m[prow] = m_run;
+                a.part_l[prow] = l_sum;
+            }
+        }
+    }
+}
+
+// BAL: grid (KV head, wave of the balanced split), else (KV head, partition, sequence).
+template <bool APPEND, bool BAL>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_partition_mfma4(
+    KernelParams a) {
+    __shared__ u32x4 lds_knew[APPEND ? 4 : 1];
+    __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
+    const int lane = threadIdx.x;
+    const int g = blockIdx.x;
+    uint8_t* knew = reinterpret_cast<uint8_t*>(lds_knew);
+    PendingAppend4 pend{-1, 0, u32x4{0u, 0u, 0u, 0u}, f32x2{0.0f, 0.0f}, f32x2{0.0f, 0.0f}};
+    if constexpr (BAL) {
+        const int w = blockIdx.y;
+        for_each_segment(a, w, g == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
+            gqa4_segment<APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, knew, lds_vnew, pend);
+        });
+        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+    } else {
+        const int p = blockIdx.y;
+        const int b = blockIdx.z;
+        const int G = a.Hq / a.Hkv;
+        const int n = a.ctx[b];
+        if (n <= 0) {
+            if (p == 0) {
+                for (int jh = 0; jh < G; ++jh) {
+                    const size_t orow = ((size_t)b * a.Hq + g * G + jh) * kDim;
+                    a.out[orow + lane] = 0;
+                    a.out[orow + 64 + lane] = 0;
+                }
+            }
+            return;
+        }
+        const int nt = tiles_of(n);
+        const int lo = p * (a.PS / kBlock);
+        if (lo >= nt) return;
+        const int hi = min(nt, lo + a.PS / kBlock);
+        gqa4_segment<APPEND>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane, knew, lds_vnew,
+                             pend);
+        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+    }
+}
+
+template <bool BAL>
+void launch_gqa4(const KernelParams& kp, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+    const dim3 grid = BAL ? dim3((unsigned)kp.Hkv, (unsigned)kp.NW)
+                          : dim3((unsigned)kp.Hkv, (unsigned)kp.P, (unsigned)kp.B);
+    if (kp.k_new)
+        launch_timed(attn_partition_mfma4<true, BAL>, grid, kp, stream, t0, t1);
+    else
+        launch_timed(attn_partition_mfma4<false, BAL>, grid, kp, stream, t0, t1);
+}
+
+}  // namespace
+
+void launch_partition_gqa4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    if (kp.NW > 0)
+        launch_gqa4<true>(kp, stream, start, stop);
+    else
+        launch_gqa4<false>(kp, stream, start, stop);
+}
+
+}  // namespace kvq

@@ -109,8 +109,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.k_new = a.k_new;
     kp.v_new = a.v_new;
 
-    if (c.dtype == KVQ_INT4)
+    if (c.dtype == KVQ_INT4 && kp.Hq == kp.Hkv)
         launch_partition_mha4(kp, stream, main_begin, main_end);
+    else if (c.dtype == KVQ_INT4)
+        launch_partition_gqa4(kp, stream, main_begin, main_end);
     else if (kp.Hq == kp.Hkv)
         launch_partition_mha(kp, c.dtype, stream, main_begin, main_end);
     else

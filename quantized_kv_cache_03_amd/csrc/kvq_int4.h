@@ -78,8 +78,10 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 
-// Partition kernel of the INT4 cache for one query head per KV head (kvq_attn_mha4.hip).
+// Partition kernels of the INT4 cache: one query head per KV head (kvq_attn_mha4.hip) and grouped
+// query heads (kvq_attn_gqa4.hip).
 struct KernelParams;
 void launch_partition_mha4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+void launch_partition_gqa4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace kvq

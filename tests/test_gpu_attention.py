@@ -43,8 +43,11 @@ CASES = [
     # the E4M3FNUZ mode, on both kernels
     ("llama2-7b-mha-e4m3fnuz", [900, 33, 1600], {"num_q_heads": 4, "num_kv_heads": 4}),
     ("llama3-70b-gqa-e4m3fnuz-32k", [2100, 7], {"num_q_heads": 16, "num_kv_heads": 2}),
-    # the INT4 mode (one query head per KV head)
+    # the INT4 mode, one query head per KV head and grouped heads (G = 4, 3, 16)
     ("llama2-7b-mha-int4", [900, 33, 1600, 1, 17], {"num_q_heads": 4, "num_kv_heads": 4}),
+    ("llama3-8b-gqa-int4", [1200, 16, 513, 70], {"num_q_heads": 8, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-int4", [300, 2, 47], {"num_q_heads": 6, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-int4", [700, 1], {"num_q_heads": 16, "num_kv_heads": 1}),
 ]
 
 
@@ -161,6 +164,8 @@ BALANCED_CASES = [
     # INT4: ragged, empty and long sequences
     ("llama2-7b-mha-int4", [0, 3, 17, 1, 0, 40, 2, 300] * 12, {"num_q_heads": 2, "num_kv_heads": 2}),
     ("llama2-7b-mha-int4", [7000, 1], {"num_q_heads": 1, "num_kv_heads": 1}),
+    ("llama3-8b-gqa-int4", [5, 0, 1, 33, 16, 700, 15, 0, 64] * 9, {"num_q_heads": 8, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-int4", [9000, 1], {"num_q_heads": 8, "num_kv_heads": 1}),
 ]
 
 

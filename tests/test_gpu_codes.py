@@ -38,7 +38,8 @@ def _codes(dtype, shape, r):
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv", [(d, hq, hk) for d in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3fnuz", "int8")
-                                           for hq, hk in ((4, 4), (8, 2), (16, 2))] + [("int4", 4, 4)])
+                                           for hq, hk in ((4, 4), (8, 2), (16, 2))] +
+                         [("int4", 4, 4), ("int4", 8, 2), ("int4", 16, 2)])
 def test_attention_on_low_binade_codes(dtype, Hq, Hkv):
     import torch
     if not torch.cuda.is_available():

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny-e4m3", "llama2-7b-mha-e4m3", "llama3-8b-gqa-e5m2", "llama2-13b-mha-int8",
          "llama3-70b-gqa-e4m3-32k", "llama2-7b-mha-e4m3fnuz", "llama3-70b-gqa-e4m3fnuz-32k",
-         "llama2-7b-mha-int4"]
+         "llama2-7b-mha-int4", "llama3-8b-gqa-int4"]
 
 
 @pytest.mark.parametrize("name", NAMES)
