@@ -37,16 +37,26 @@ def log(*a):
 
 def partition_kernel(w) -> tuple[str, str]:
     """(kernel name, source file) of the partition kernel that serves the workload."""
-    if w.num_q_heads == w.num_kv_heads:
+    mha = w.num_q_heads == w.num_kv_heads
+    if w.dtype == "int4":
+        return (("attn_partition_valu4", "kvq_attn_mha4.hip") if mha
+                else ("attn_partition_mfma4", "kvq_attn_gqa4.hip"))
+    if mha:
         return f"attn_partition_valu<{w.dtype}>", "kvq_attn_mha.hip"
     return f"attn_partition_mfma<{w.dtype}>", "kvq_attn_gqa.hip"
+
+
+def kernel_source_files(w) -> tuple:
+    """The partition kernel's file and the headers it includes."""
+    extra = ("kvq_int4.h", "kvq_attn4.h") if w.dtype == "int4" else ()
+    return (partition_kernel(w)[1], "kvq_attn.h", "kvq_device.h") + extra
 
 
 def kernel_source_digest(w) -> str:
     """Digest of the partition kernel's sources (its file and the headers it includes)."""
     import hashlib
     h = hashlib.sha256()
-    for f in (partition_kernel(w)[1], "kvq_attn.h", "kvq_device.h"):
+    for f in kernel_source_files(w):
         with open(os.path.join(ROOT, "quantized_kv_cache_03_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
