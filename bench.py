@@ -195,7 +195,7 @@ def run_prefill(args, w):
     # row j of a sequence of n tokens with m query rows: n - m + j + 1
     visible = case.B * (m * (n - m) + m * (m + 1) // 2)
     flops = 4 * 128 * w.num_q_heads * visible
-    per_tok = 2 * 128 + (8 if w.dtype == "int8" else 0)
+    per_tok = harness.kv_bytes_per_token(w.dtype)
     code_bytes = case.B * n * w.num_kv_heads * per_tok
     cpu = None
     parity = None
@@ -233,7 +233,8 @@ def run_prefill(args, w):
                    "entry_points": "kvq_paged_prefill_attn"},
         "flops": flops,
         "kv_code_bytes": code_bytes,
-        "roofline": {"kernel": f"attn_prefill_mfma<{w.dtype}>", "bound": "mfma",
+        "roofline": {"kernel": ("attn_prefill_mfma4" if w.dtype == "int4" else f"attn_prefill_mfma<{w.dtype}>"),
+                     "bound": "mfma",
                      "achieved": round(flops / (kms * 1e-3) / 1e12, 2), "peak": PEAK_MFMA_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (kms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
                      "traffic": None, "kernel_ms": round(kms, 5)},

@@ -321,8 +321,6 @@ int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int
         return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
-    if (cache->dtype == KVQ_INT4)
-        return fail(KVQ_ERR_DTYPE, "prefill attention over an INT4 cache is not built");
     if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
         return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",

@@ -41,6 +41,15 @@ __device__ __forceinline__ void int4x8_to_f16(uint32_t w, half2_t (&h)[4]) {
     h[3] = __builtin_bit_cast(half2_t, w8 & 0x00F000F0u);
 }
 
+// The same decode with every pair in 2^-24 units (the odd nibbles shifted down first): two more
+// shifts per dword, and every product can share one accumulator.
+__device__ __forceinline__ void int4x8_to_f16_unit(uint32_t w, half2_t (&h)[4]) {
+    h[0] = __builtin_bit_cast(half2_t, w & 0x000F000Fu);
+    h[1] = __builtin_bit_cast(half2_t, (w >> 4) & 0x000F000Fu);
+    h[2] = __builtin_bit_cast(half2_t, (w >> 8) & 0x000F000Fu);
+    h[3] = __builtin_bit_cast(half2_t, (w >> 12) & 0x000F000Fu);
+}
+
 // Tile geometry (1 KiB per tile).
 //   K: four 256-byte chunks of 32 dims x 16 tokens; the byte of dim d of token t holds dims
 //      d & ~1 (low nibble) and d | 1.
@@ -78,10 +87,23 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 
+// The 16-bit unit of a V dword as int4_unit_to_f16 gives it, with both pairs in 2^-24 units.
+template <int SEL>
+__device__ __forceinline__ void int4_unit_to_f16_unit(uint32_t w, half2_t& e, half2_t& o) {
+    constexpr uint32_t sel = (SEL == 0) ? 0x0C010C00u : 0x0C030C02u;
+    const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
+    e = __builtin_bit_cast(half2_t, x & 0x000F000Fu);
+    o = __builtin_bit_cast(half2_t, (x >> 4) & 0x000F000Fu);
+}
+
 // Partition kernels of the INT4 cache: one query head per KV head (kvq_attn_mha4.hip) and grouped
 // query heads (kvq_attn_gqa4.hip).
 struct KernelParams;
 void launch_partition_mha4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 void launch_partition_gqa4(const KernelParams& kp, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+// Prefill attention over the INT4 cache (kvq_prefill4.hip).
+struct PrefillArgs;
+hipError_t launch_prefill4(const PrefillArgs& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 }  // namespace kvq

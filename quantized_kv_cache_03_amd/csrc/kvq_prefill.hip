@@ -19,6 +19,7 @@
 // of its last row.  The tiles of a head stay in its XCD's L2 for the other row tiles of the head
 // (the KV head is the fastest grid dimension, and workgroup ids go round-robin to the 8 XCDs).
 #include "kvq_attn.h"
+#include "kvq_int4.h"
 #include "kvq_mfma.h"
 
 namespace kvq {
@@ -323,6 +324,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
 
 hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     const kvq_cache& c = *p.cache;
+    if (c.dtype == KVQ_INT4) return launch_prefill4(p, stream, start, stop);
     if (p.batch == 0 || p.max_q_len == 0 || p.num_q_rows == 0) return hipSuccess;
     PrefillParams a;
     a.kc = c.k_cache;

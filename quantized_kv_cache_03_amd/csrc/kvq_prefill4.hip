@@ -1,0 +1,282 @@
+// kvq_prefill4.hip -- prefill / chunked-prefill attention over the INT4 cache.
+//
+// The same causal attention as kvq_prefill.hip (sequence b's n_b query rows are its last n_b
+// tokens; row j at position p = context_lens[b] - n_b + j sees the tokens 0 .. p) over the INT4
+// cache (asymmetric 4-bit codes, an fp32 (scale, zero point) pair per (token, KV head)), with the
+// logits and the output factored as in the INT4 decode kernels:
+//     z_t = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d),  out = (sum_t p_t s_t c_t + sum_t p_t zp_t) / sum_t p_t.
+// One wave per (KV head, tile of 16 / G query rows, sequence) on v_mfma_f32_16x16x32_f16; the 16
+// columns are (query row, query head) pairs as in the 8-bit prefill kernel, and the operands are
+// those of the grouped INT4 decode kernel (kvq_attn_gqa4.hip): one 16-byte load per lane for each
+// of the K and V tiles, P^T left in the lanes by the S^T accumulator, chunks of four tiles.  Every
+// decoded code is in 2^-24 units (odd nibbles shifted down), so each product keeps one accumulator.
+#include "kvq_attn4.h"
+#include "kvq_mfma.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kTilesP4 = 4;  // tiles per chunk: the P^T operand spans four tiles
+
+struct Prefill4Params {
+    const uint8_t* kc;
+    const uint8_t* vc;
+    const float* ks;          // (scale, zero point) pairs [num_blocks][Hkv][16][2]
+    const float* vs;
+    const uint16_t* q;        // fp16 [num_q_rows][Hq][128]
+    uint16_t* out;            // fp16 [num_q_rows][Hq][128]
+    const int32_t* block_tables;
+    const int32_t* ctx;       // post-append lengths
+    const int32_t* cu_q;      // [B + 1] query row offsets
+    int32_t max_blocks;
+    int32_t Hq;
+    int32_t Hkv;
+    int32_t G;                // query heads per KV head
+    int32_t R;                // query rows per wave (16 / G)
+    int32_t row_tiles;        // grid extent over row tiles
+    float qk_scale;           // sm_scale * log2(e)
+};
+
+// This lane's share of one tile (as in the grouped INT4 decode kernel).
+struct TileP4 {
+    u32x4 k, v;       // K: token l % 16, chunk l / 16; V: quad l / 16, dims l % 16 + 16 r
+    float4_t ks, kz;  // K (scale, zero point) of tokens 4 (l / 16) .. +3
+    float4_t vs, vz;  // V (scale, zero point) of the same tokens
+};
+
+__device__ __forceinline__ void load_tile_p4(const Prefill4Params& a, TileP4& t, int blk, int g,
+                                             uint32_t off, int q4) {
+    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes4;
+    t.k = ldg16(a.kc + tile + off);
+    t.v = ldg16(a.vc + tile + off);
+    const size_t so = (((size_t)blk * a.Hkv + g) * kBlock + 4 * q4) * 2;
+    const float4_t k0 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+    const float4_t k1 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so + 4));
+    const float4_t v0 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
+    const float4_t v1 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so + 4));
+    t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
+    t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
+    t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};
+    t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
+}
+
+// The K operands of one tile in the k-slot order of kslot_dim: the four MFMAs take the (0, 4),
+// (2, 6) nibble pairs and then the (1, 5), (3, 7) pairs of dwords (0, 1) and of dwords (2, 3).
+__device__ __forceinline__ void k_operands_p4(const u32x4& k, half8_v (&op)[4]) {
+    const uint32_t w[4] = {k.x, k.y, k.z, k.w};
+    half2_t h[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) int4x8_to_f16_unit(w[j], h[j]);
+    op[0] = join8(h[0][0], h[0][2], h[1][0], h[1][2]);
+    op[1] = join8(h[0][1], h[0][3], h[1][1], h[1][3]);
+    op[2] = join8(h[2][0], h[2][2], h[3][0], h[3][2]);
+    op[3] = join8(h[2][1], h[2][3], h[3][1], h[3][3]);
+}
+
+// Chunk-relative dim of k-slot `slot` of K operand m (see k_operands_p4).
+__device__ __forceinline__ int kslot_dim(int m, int slot) {
+    const int dw = 2 * (m / 2) + slot / 4;
+    const int i = 2 * ((slot % 4) / 2) + (m % 2);  // nibble pair (i, i + 4)
+    return 8 * dw + i + 4 * (slot % 2);
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_prefill_mfma4(
+    Prefill4Params a) {
+    const int g = blockIdx.x;
+    const int rt = a.row_tiles - 1 - (int)blockIdx.y;  // later rows read more tiles: run them first
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int col = lane & 15;  // column: (row jr, head hg)
+    const int q4 = lane >> 4;   // MFMA k-group / C row group
+
+    const int r0 = a.cu_q[b];
+    const int nq = a.cu_q[b + 1] - r0;
+    const int j0 = rt * a.R;
+    if (j0 >= nq) return;
+    const int n = a.ctx[b];
+    const int jr = col / a.G, hg = col % a.G;
+    const int j = j0 + jr;
+    const bool live = jr < a.R && j < nq;  // the column holds a real (row, head)
+    const size_t orow = ((size_t)(r0 + j) * a.Hq + (size_t)g * a.G + hg) * kDim;
+    if (n < nq) {  // more query rows than tokens: outside the contract; the rows get zeros
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<half4_t*>(a.out + orow + 16 * r + 4 * q4) = half4_t{0, 0, 0, 0};
+        }
+        return;
+    }
+    const int pos_min = n - nq + j0;                   // every column sees tokens 0 .. pos_min
+    const int t_end = n - nq + min(nq, j0 + a.R);      // tokens the wave reads
+    const int tile_end = (t_end + kBlock - 1) / kBlock;
+    const int pos = live ? n - nq + j : pos_min;       // the column's last visible token
+    const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
+
+    // Q^T operands of the column over chunk q4's dims, and the sum of its 128 q elements
+    half8_v qB[4];
+    float qsum = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qB[m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
+    if (live) {
+        const uint16_t* qrow = a.q + orow + 32 * q4;
+        uint16_t qv[32];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 w = reinterpret_cast<const u32x4*>(qrow)[c];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                qv[8 * c + 2 * k] = (uint16_t)(ww[k] & 0xFFFFu);
+                qv[8 * c + 2 * k + 1] = (uint16_t)(ww[k] >> 16);
+            }
+        }
+#pragma unroll
+        for (int d = 0; d < 32; ++d) qsum += (float)__builtin_bit_cast(_Float16, qv[d]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qB[m][s] = __builtin_bit_cast(_Float16, qv[kslot_dim(m, s)]);
+    }
+    qsum += __shfl_xor(qsum, 16);
+    qsum += __shfl_xor(qsum, 32);
+
+    float m_run = kNegInf, l_lane = 0.0f, z_lane = 0.0f;
+    float4_t acc[8];  // O^T row blocks in 2^-24 units: dims 16 r + 4 q4 .. +3 of the column
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t off = 256u * (uint32_t)q4 + 16u * (uint32_t)col;
+    const float qk24 = a.qk_scale * kInt4Even;
+
+    for (int tb = 0; tb < tile_end; tb += 64) {
+        const int nt_grp = min(64, tile_end - tb);
+        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        for (int c0 = 0; c0 < nt_grp; c0 += kTilesP4) {
+            TileP4 t[kTilesP4];
+#pragma unroll
+            for (int i = 0; i < kTilesP4; ++i) {
+                if (c0 + i < nt_grp) {
+                    load_tile_p4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                } else {
+                    t[i].k = t[i].v = u32x4{0u, 0u, 0u, 0u};
+                    t[i].ks = t[i].kz = t[i].vs = t[i].vz = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+            }
+            const int tok_base = (tb + c0) * kBlock;
+            const bool all_visible = tok_base + kTilesP4 * kBlock - 1 <= pos_min;  // wave-uniform
+            float z[kTilesP4][4];
+            float cmax = kNegInf;
+#pragma unroll
+            for (int i = 0; i < kTilesP4; ++i) {
+                half8_v kop[4];
+                k_operands_p4(t[i].k, kop);
+                float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[m], qB[m], s, 0, 0, 0);
+                const int tok0 = tok_base + i * kBlock + 4 * q4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float zz = qk24 * (s[u] * t[i].ks[u]) + a.qk_scale * (t[i].kz[u] * qsum);
+                    z[i][u] = (all_visible || tok0 + u <= pos) ? zz : kNegInf;
+                    cmax = fmaxf(cmax, z[i][u]);
+                }
+            }
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+            const float m_new = fmaxf(m_run, cmax);  // finite: the first chunk holds token 0
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_lane *= alpha;
+            z_lane *= alpha;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+            // P^T operands: tokens (0, 2) and (1, 3) of this lane's quad of each tile, w = p s_v
+            half8_v we_hi, we_lo, wo_hi, wo_lo;
+#pragma unroll
+            for (int i = 0; i < kTilesP4; ++i) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_new);
+                    l_lane += pw;
+                    const bool on = pw > 0.0f;  // masked slots may hold NaN scales
+                    const float w = on ? pw * t[i].vs[u] : 0.0f;
+                    z_lane += on ? pw * t[i].vz[u] : 0.0f;
+                    const _Float16 hi = (_Float16)w;
+                    const _Float16 lo = (_Float16)(w - (float)hi);
+                    const int k = 2 * i + (u >> 1);
+                    if (u & 1) {
+                        wo_hi[k] = hi;
+                        wo_lo[k] = lo;
+                    } else {
+                        we_hi[k] = hi;
+                        we_lo[k] = lo;
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                half2_t ve[kTilesP4], vo[kTilesP4];
+#pragma unroll
+                for (int i = 0; i < kTilesP4; ++i) {
+                    const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
+                    if (r & 1)
+                        int4_unit_to_f16_unit<1>(w[r / 2], ve[i], vo[i]);
+                    else
+                        int4_unit_to_f16_unit<0>(w[r / 2], ve[i], vo[i]);
+                }
+                const half8_v ae = join8(ve[0], ve[1], ve[2], ve[3]);
+                const half8_v ao = join8(vo[0], vo[1], vo[2], vo[3]);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc[r], 0, 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc[r], 0, 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc[r], 0, 0, 0);
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc[r], 0, 0, 0);
+            }
+        }
+    }
+    float l_sum = l_lane + __shfl_xor(l_lane, 16);
+    l_sum += __shfl_xor(l_sum, 32);
+    float z_sum = z_lane + __shfl_xor(z_lane, 16);
+    z_sum += __shfl_xor(z_sum, 32);
+    if (live) {
+        const float inv = 1.0f / l_sum;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float4_t o = acc[r] * kInt4Even + z_sum;
+            const half4_t v = {(_Float16)(o[0] * inv), (_Float16)(o[1] * inv), (_Float16)(o[2] * inv),
+                               (_Float16)(o[3] * inv)};
+            *reinterpret_cast<half4_t*>(a.out + orow + 16 * r + 4 * q4) = v;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill4(const PrefillArgs& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    const kvq_cache& c = *p.cache;
+    if (p.batch == 0 || p.max_q_len == 0 || p.num_q_rows == 0) return hipSuccess;
+    Prefill4Params a;
+    a.kc = c.k_cache;
+    a.vc = c.v_cache;
+    a.ks = c.k_scale;
+    a.vs = c.v_scale;
+    a.q = p.q;
+    a.out = p.out;
+    a.block_tables = p.block_tables;
+    a.ctx = p.context_lens;
+    a.cu_q = p.cu_q_lens;
+    a.max_blocks = p.max_blocks_per_seq;
+    a.Hq = p.num_q_heads;
+    a.Hkv = c.num_kv_heads;
+    a.G = p.num_q_heads / c.num_kv_heads;
+    a.R = 16 / a.G;
+    a.row_tiles = (p.max_q_len + a.R - 1) / a.R;
+    a.qk_scale = p.sm_scale * kLog2e;
+    const dim3 grid((unsigned)a.Hkv, (unsigned)a.row_tiles, (unsigned)p.batch);
+    if (start)
+        hipExtLaunchKernelGGL(attn_prefill_mfma4, grid, dim3(64), 0, stream, start, stop, 0, a);
+    else
+        hipLaunchKernelGGL(attn_prefill_mfma4, grid, dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -83,8 +83,6 @@ def test_attention_on_low_binade_codes(dtype, Hq, Hkv):
         out = K.paged_decode_attn(dc, q_d, bt_d, ctx_d, L, partition_size=ps).cpu().numpy()
         st = assert_attn_close(out, ref, f"{dtype} decode partition {ps}")
         say(f"    decode partition {ps}: {st}")
-    if dtype == "int4":
-        return  # prefill over the INT4 cache is not built
     # prefill: the last nq tokens of each sequence as query rows
     nq = np.minimum(ctx, np.array([40, 1, 16, 17, 33], np.int32))
     cu_q = np.zeros(len(ctx) + 1, np.int32)

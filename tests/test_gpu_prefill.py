@@ -54,6 +54,11 @@ CASES = [
     ("llama3-8b-gqa-e5m2", [64, 129], [64, 50], {"num_q_heads": 4, "num_kv_heads": 2}),    # G = 2
     ("llama2-7b-mha-e4m3fnuz", [200, 37], [70, 37], {"num_q_heads": 2, "num_kv_heads": 2}),
     ("llama3-70b-gqa-e4m3fnuz-32k", [260, 16], [100, 16], {"num_q_heads": 16, "num_kv_heads": 2}),
+    # INT4: G = 1, 4, 3, 16
+    ("llama2-7b-mha-int4", [40, 300, 129, 17, 64], [40, 33, 1, 17, 0], {"num_q_heads": 2, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-int4", [300, 77, 16], [70, 77, 5], {"num_q_heads": 8, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-int4", [260, 45], [100, 45], {"num_q_heads": 6, "num_kv_heads": 2}),
+    ("llama3-8b-gqa-int4", [150, 2], [150, 2], {"num_q_heads": 16, "num_kv_heads": 1}),
 ]
 
 
@@ -114,6 +119,7 @@ def test_prefill_rows_beyond_context_get_zeros(H):
 @pytest.mark.parametrize("name,kw,ctx,nq", [
     ("llama2-7b-mha-e4m3", {}, [4096, 2500], [4096, 1200]),
     ("llama3-70b-gqa-e4m3-32k", {}, [8192], [2048]),
+    ("llama3-8b-gqa-int4", {}, [4096, 1500], [4096, 700]),
 ])
 def test_prefill_full_size_sampled_rows(H, name, kw, ctx, nq):
     """Prompts at model size (all heads of the workload's layer); sampled rows against the oracle,
