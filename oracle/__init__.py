@@ -85,6 +85,10 @@ def load(path: str):
                                         _c_float, _u16p, _c_float, _i32p, _c_int, _i32p,
                                         _c_int, _c_int, _f64p]
     L.kvqo_decode_attn_head.restype = _c_int
+    L.kvqo_decode_attn_head_fp8q.argtypes = L.kvqo_decode_attn_head.argtypes
+    L.kvqo_decode_attn_head_fp8q.restype = _c_int
+    L.kvqo_quantize_q_fp8_rows.argtypes = [_u16p, _c_int, _u8p, _f32p]
+    L.kvqo_quantize_q_fp8_rows.restype = None
     L.kvqo_attn_fp16_dense.argtypes = [_u16p, _u16p, _u16p, _c_int, _c_float, _f64p]
     L.kvqo_attn_fp16_dense.restype = _c_int
     return L
@@ -168,6 +172,18 @@ def int4_quantize_rows(x_fp16) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     return q, s, z
 
 
+def quantize_q_fp8_rows(q_fp16) -> tuple[np.ndarray, np.ndarray]:
+    """Query rows of 128 (last axis) -> (E4M3 codes, fp32 per-row scales) of the FP8-math path."""
+    bits = _fp16_bits(q_fp16)
+    assert bits.shape[-1] == DIM
+    rows = bits.size // DIM
+    c = np.empty(bits.shape, np.uint8)
+    s = np.empty(bits.shape[:-1], np.float32)
+    lib().kvqo_quantize_q_fp8_rows(_ptr(bits.reshape(-1), _u16p), rows, _ptr(c.reshape(-1), _u8p),
+                                   _ptr(s.reshape(-1), _f32p))
+    return c, s
+
+
 def tile_bytes(dtype: int) -> int:
     """Bytes of one (block, KV head) tile of K (or of V) codes."""
     return BLOCK * DIM // 2 if dtype == INT4 else BLOCK * DIM
@@ -231,9 +247,10 @@ def dequant(cache: Cache, block_tables, context_lens, max_context_len: int,
 
 
 def decode_attn(cache: Cache, q, block_tables, context_lens, sm_scale: float | None = None,
-                heads=None, threads: int = 1) -> np.ndarray:
+                heads=None, threads: int = 1, fp8_math: bool = False) -> np.ndarray:
     """fp64 decode attention.  q: fp16 [B][Hq][128].  Returns [B][Hq][128] float64 (rows not in
-    ``heads``, a list of (b, h) pairs, are left NaN)."""
+    ``heads``, a list of (b, h) pairs, are left NaN).  fp8_math=True first replaces each query row
+    by its E4M3 quantization (quantize_q_fp8_rows), dequantized exactly."""
     qb = _fp16_bits(q)
     B, Hq, D = qb.shape
     assert D == DIM
@@ -245,14 +262,15 @@ def decode_attn(cache: Cache, q, block_tables, context_lens, sm_scale: float | N
     if heads is None:
         heads = [(b, h) for b in range(B) for h in range(Hq)]
     L = lib()
+    fn = L.kvqo_decode_attn_head_fp8q if fp8_math else L.kvqo_decode_attn_head
     cargs = cache.args()
     qp, btp, ctxp = _ptr(qb, _u16p), _ptr(bt, _i32p), _ptr(ctx, _i32p)
 
     def one(bh):
         b, h = bh
         row = np.empty(DIM, np.float64)
-        rc = L.kvqo_decode_attn_head(cargs[0], cargs[1], Hq, *cargs[2:], qp, float(sm_scale), btp,
-                                     bt.shape[1], ctxp, b, h, _ptr(row, _f64p))
+        rc = fn(cargs[0], cargs[1], Hq, *cargs[2:], qp, float(sm_scale), btp,
+                bt.shape[1], ctxp, b, h, _ptr(row, _f64p))
         if rc != 0:
             raise ValueError("oracle attention rejected its arguments")
         out[b, h] = row
@@ -267,7 +285,7 @@ def decode_attn(cache: Cache, q, block_tables, context_lens, sm_scale: float | N
 
 
 def prefill_attn(cache: Cache, q, block_tables, context_lens, cu_q_lens, sm_scale: float | None = None,
-                 rows=None, threads: int = 1) -> np.ndarray:
+                 rows=None, threads: int = 1, fp8_math: bool = False) -> np.ndarray:
     """fp64 prefill (causal) attention.  q: fp16 [T][Hq][128], sequence b's rows cu_q_lens[b] ..
     cu_q_lens[b+1]-1 being the last n_b of its context_lens[b] tokens; row j of b attends to the
     tokens at positions 0 .. context_lens[b] - n_b + j.  That is decode attention over the row's
@@ -287,7 +305,7 @@ def prefill_attn(cache: Cache, q, block_tables, context_lens, cu_q_lens, sm_scal
     out = np.full((T, Hq, DIM), np.nan, np.float64)
     if rows:
         sub = decode_attn(cache, q[rows], bt[seq[rows]], (pos[rows] + 1).astype(np.int32),
-                          sm_scale=sm_scale, threads=threads)
+                          sm_scale=sm_scale, threads=threads, fp8_math=fp8_math)
         out[rows] = sub
     return out
 

@@ -414,16 +414,72 @@ int kvqo_dequant(int dtype, int Hkv, const uint8_t *k_cache, const uint8_t *v_ca
     return 0;
 }
 
+/* FP8 math (the "FP8 attention" the lmdeploy thread points to, for the QK^T product): one query
+ * row of 128 fp16 values quantized to OCP E4M3 with a dynamic scale of its own,
+ *   s_q = fl32(max_d |q_d| / 448),  c_d = enc_E4M3(fl32(q_d / s_q))   (s_q = 1 for a zero row),
+ * so that the row's dequantized values are dec(c_d) * s_q.  Inputs are assumed finite.          */
+void kvqo_quantize_q_fp8_row(const uint16_t *q, uint8_t *codes, float *s_out)
+{
+    float amax = 0.0f;
+    for (int d = 0; d < KVQO_DIM; ++d) {
+        float v = fabsf((float)kvqo_fp16_to_double(q[d]));
+        if (v > amax)
+            amax = v;
+    }
+    float s = amax > 0.0f ? amax / 448.0f : 1.0f;   /* one binary32 division */
+    for (int d = 0; d < KVQO_DIM; ++d)
+        codes[d] = kvqo_fp8_encode(KVQO_E4M3, (float)kvqo_fp16_to_double(q[d]) / s);
+    *s_out = s;
+}
+
 /* Decode-step attention of one query head h of sequence b over the paged cache, in fp64:
  *   g = h / (Hq/Hkv), n = context_lens[b];
- *   z_t = sm_scale * sum_d q[b][h][d] * k^[t][d]      for t < n;
+ *   z_t = sm_scale * sum_d q[d] * k^[t][d]      for t < n;
  *   out[d] = sum_t exp(z_t - max z) v^[t][d] / sum_t exp(z_t - max z).
- * q is fp16 bits [B][Hq][128]; out is 128 doubles.  n == 0 gives zeros.  Returns 0 or -1.      */
+ * q is the row's 128 exact values; out is 128 doubles.  n == 0 gives zeros.  Returns 0 or -1.   */
+static int decode_attn_row(int dtype, int Hkv, int Hq, const uint8_t *k_cache, const uint8_t *v_cache,
+                           const float *k_scale, const float *v_scale, float kv_scale,
+                           const double *qd, float sm_scale, const int32_t *block_tables,
+                           int max_blocks_per_seq, const int32_t *context_lens, int b, int h,
+                           double *out);
+
+/* The same attention for the fp16 query q[b][h] (fp16 bits [B][Hq][128]).                      */
 int kvqo_decode_attn_head(int dtype, int Hkv, int Hq, const uint8_t *k_cache, const uint8_t *v_cache,
                           const float *k_scale, const float *v_scale, float kv_scale,
                           const uint16_t *q, float sm_scale, const int32_t *block_tables,
                           int max_blocks_per_seq, const int32_t *context_lens, int b, int h,
                           double *out)
+{
+    double qd[KVQO_DIM];
+    for (int d = 0; d < KVQO_DIM; ++d)
+        qd[d] = kvqo_fp16_to_double(q[((size_t)b * Hq + h) * KVQO_DIM + d]);
+    return decode_attn_row(dtype, Hkv, Hq, k_cache, v_cache, k_scale, v_scale, kv_scale, qd, sm_scale,
+                           block_tables, max_blocks_per_seq, context_lens, b, h, out);
+}
+
+/* The same attention with the query quantized to E4M3 first (FP8 math): q[b][h] is replaced by its
+ * exact dequantized values dec(c_d) * s_q (kvqo_quantize_q_fp8_row).                          */
+int kvqo_decode_attn_head_fp8q(int dtype, int Hkv, int Hq, const uint8_t *k_cache,
+                               const uint8_t *v_cache, const float *k_scale, const float *v_scale,
+                               float kv_scale, const uint16_t *q, float sm_scale,
+                               const int32_t *block_tables, int max_blocks_per_seq,
+                               const int32_t *context_lens, int b, int h, double *out)
+{
+    uint8_t codes[KVQO_DIM];
+    float s;
+    double qd[KVQO_DIM];
+    kvqo_quantize_q_fp8_row(q + ((size_t)b * Hq + h) * KVQO_DIM, codes, &s);
+    for (int d = 0; d < KVQO_DIM; ++d)
+        qd[d] = kvqo_fp8_decode(KVQO_E4M3, codes[d]) * (double)s;   /* exact: 4 + 24 bits */
+    return decode_attn_row(dtype, Hkv, Hq, k_cache, v_cache, k_scale, v_scale, kv_scale, qd, sm_scale,
+                           block_tables, max_blocks_per_seq, context_lens, b, h, out);
+}
+
+static int decode_attn_row(int dtype, int Hkv, int Hq, const uint8_t *k_cache, const uint8_t *v_cache,
+                           const float *k_scale, const float *v_scale, float kv_scale,
+                           const double *qd, float sm_scale, const int32_t *block_tables,
+                           int max_blocks_per_seq, const int32_t *context_lens, int b, int h,
+                           double *out)
 {
     if (dtype != KVQO_E4M3 && dtype != KVQO_E5M2 && dtype != KVQO_INT8 && dtype != KVQO_E4M3FNUZ &&
         dtype != KVQO_INT4)
@@ -437,9 +493,6 @@ int kvqo_decode_attn_head(int dtype, int Hkv, int Hq, const uint8_t *k_cache, co
         out[d] = 0.0;
     if (n <= 0)
         return 0;
-    double qd[KVQO_DIM];
-    for (int d = 0; d < KVQO_DIM; ++d)
-        qd[d] = kvqo_fp16_to_double(q[((size_t)b * Hq + h) * KVQO_DIM + d]);
     double *z = (double *)malloc(sizeof(double) * (size_t)n);
     if (!z)
         return -1;
@@ -538,4 +591,10 @@ void kvqo_int4_quantize_rows(const uint16_t *x, int rows, int n, uint8_t *q, flo
 {
     for (int r = 0; r < rows; ++r)
         kvqo_int4_quantize_row(x + (size_t)r * n, n, q + (size_t)r * n, s + r, zp + r);
+}
+
+void kvqo_quantize_q_fp8_rows(const uint16_t *q, int rows, uint8_t *codes, float *s)
+{
+    for (int r = 0; r < rows; ++r)
+        kvqo_quantize_q_fp8_row(q + (size_t)r * KVQO_DIM, codes + (size_t)r * KVQO_DIM, s + r);
 }

@@ -16,6 +16,7 @@ from oracle import build as obuild
 
 import test_oracle_attention as TA
 import test_oracle_codec as TC
+import test_oracle_fp8q as TQ
 import test_oracle_int4 as T4
 import test_oracle_int8 as TI
 
@@ -92,6 +93,18 @@ MUTATIONS = {
     "int4-dequant-drops-zero-point": (
         "return (double)get_nibble(codes, off, hi) * (double)sz[2 * so] + (double)sz[2 * so + 1];",
         "return (double)get_nibble(codes, off, hi) * (double)sz[2 * so];"),
+    "fp8q-scale-240": (
+        "float s = amax > 0.0f ? amax / 448.0f : 1.0f;",
+        "float s = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    "fp8q-encodes-e5m2": (
+        "codes[d] = kvqo_fp8_encode(KVQO_E4M3, (float)kvqo_fp16_to_double(q[d]) / s);",
+        "codes[d] = kvqo_fp8_encode(KVQO_E5M2, (float)kvqo_fp16_to_double(q[d]) / s);"),
+    "fp8q-dequant-drops-scale": (
+        "qd[d] = kvqo_fp8_decode(KVQO_E4M3, codes[d]) * (double)s;",
+        "qd[d] = kvqo_fp8_decode(KVQO_E4M3, codes[d]);"),
+    "fp8q-signed-max": (
+        "        float v = fabsf((float)kvqo_fp16_to_double(q[d]));",
+        "        float v = (float)kvqo_fp16_to_double(q[d]);"),
     "append-position-reversed": (
         "int p = context_lens[b] - n_b + j;",
         "int p = context_lens[b] - 1 - j;"),
@@ -132,6 +145,9 @@ def _pins():
         lambda: T4.test_int4_matches_numpy(o, "normal"),
         lambda: T4.test_int4_append_layout_and_poison(o),
         lambda: TA.test_dequant_matches_independent_decode(o, TA.INT4),
+        lambda: TQ.test_q_scale_matches_float32(o, "outliers"),
+        lambda: TQ.test_q_error_within_half_step(o, "wide"),
+        lambda: TQ.test_fp8_attention_matches_independent_softmax(o, 1, 8, 2),
     ]
 
 
