@@ -38,6 +38,8 @@ def log(*a):
 def partition_kernel(w) -> tuple[str, str]:
     """(kernel name, source file) of the partition kernel that serves the workload."""
     mha = w.num_q_heads == w.num_kv_heads
+    if w.fp8_math:  # every grouping runs on the grouped-head kernel
+        return f"attn_partition_mfma<{w.dtype}, fp8 math>", "kvq_attn_gqa.hip"
     if w.dtype == "int4":
         return (("attn_partition_valu4", "kvq_attn_mha4.hip") if mha
                 else ("attn_partition_mfma4", "kvq_attn_gqa4.hip"))
@@ -48,8 +50,11 @@ def partition_kernel(w) -> tuple[str, str]:
 
 def kernel_source_files(w) -> tuple:
     """The partition kernel's file and the headers it includes."""
+    src = partition_kernel(w)[1]
     extra = ("kvq_int4.h", "kvq_attn4.h") if w.dtype == "int4" else ()
-    return (partition_kernel(w)[1], "kvq_attn.h", "kvq_device.h") + extra
+    if src == "kvq_attn_gqa.hip":
+        extra += ("kvq_mfma.h", "kvq_fp8m.h")
+    return (src, "kvq_attn.h", "kvq_device.h") + extra
 
 
 def kernel_source_digest(w) -> str:
@@ -127,7 +132,7 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
     reps = 0
     while True:
         oracle.append(cache, k[last], v[last], bt, ctx)
-        oracle.decode_attn(cache, q, bt, ctx, threads=threads)
+        oracle.decode_attn(cache, q, bt, ctx, threads=threads, fp8_math=w.fp8_math)
         reps += 1
         if time.perf_counter() - t1 >= budget_s:
             break
@@ -148,6 +153,9 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
 
 PREFILL_METRIC = "prefill attention over the 8-bit paged cache: achieved TFLOP/s (% of fp16 MFMA peak)"
 PEAK_MFMA_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+PEAK_MFMA_F8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak
+# FP8 math: QK^T (half the flops) on the fp8 peak, PV on the fp16 one -> the peak of the mix
+PEAK_MFMA_F8F16_TFLOPS = 2.0 / (1.0 / PEAK_MFMA_F8_TFLOPS + 1.0 / PEAK_MFMA_F16_TFLOPS)
 
 
 def run_prefill(args, w):
@@ -171,9 +179,11 @@ def run_prefill(args, w):
     out = torch.empty_like(q_d)
     stream = torch.cuda.current_stream()
 
+    attn = kvq.paged_prefill_attn_fp8math if w.fp8_math else kvq.paged_prefill_attn
+    peak = PEAK_MFMA_F8F16_TFLOPS if w.fp8_math else PEAK_MFMA_F16_TFLOPS
+
     def call():
-        kvq.paged_prefill_attn(case.cache, q_d, cu_d, case.bt_d, case.ctx_d, case.max_ctx, m, out=out,
-                               stream=stream)
+        attn(case.cache, q_d, cu_d, case.bt_d, case.ctx_d, case.max_ctx, m, out=out, stream=stream)
 
     for _ in range(args.warmup):
         call()
@@ -210,7 +220,8 @@ def run_prefill(args, w):
         T = int(cu_q[-1])
         rows = sorted(set(np.linspace(0, T - 1, 8).astype(int).tolist()))
         t0 = time.perf_counter()
-        ref = oracle.prefill_attn(oc, q, case.bt, case.ctx, cu_q, rows=rows, threads=threads)
+        ref = oracle.prefill_attn(oc, q, case.bt, case.ctx, cu_q, rows=rows, threads=threads,
+                                  fp8_math=w.fp8_math)
         sec = time.perf_counter() - t0
         fl = sum(4 * 128 * w.num_q_heads * (n - m + (r % m) + 1) for r in rows)
         cpu = {"value": fl / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -225,18 +236,21 @@ def run_prefill(args, w):
         "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f8+f16" if w.fp8_math else "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": 128, "block_size": 16,
                    "context": n, "query_rows_per_sequence": m, "kv_cache_dtype": w.dtype,
-                   "entry_points": "kvq_paged_prefill_attn"},
+                   "entry_points": ("kvq_paged_prefill_attn_fp8math" if w.fp8_math
+                                    else "kvq_paged_prefill_attn")},
         "flops": flops,
         "kv_code_bytes": code_bytes,
-        "roofline": {"kernel": ("attn_prefill_mfma4" if w.dtype == "int4" else f"attn_prefill_mfma<{w.dtype}>"),
+        "roofline": {"kernel": ("attn_prefill_mfma4" if w.dtype == "int4" else
+                                f"attn_prefill_mfma<{w.dtype}{', fp8 math' if w.fp8_math else ''}>"),
                      "bound": "mfma",
-                     "achieved": round(flops / (kms * 1e-3) / 1e12, 2), "peak": PEAK_MFMA_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(flops / (kms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+                     "achieved": round(flops / (kms * 1e-3) / 1e12, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(flops / (kms * 1e-3) / 1e12 / peak, 4),
                      "traffic": None, "kernel_ms": round(kms, 5)},
         "parity_sampled_rows": parity,
         "cpu_baseline": cpu,
@@ -384,7 +398,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f8+f16" if w.fp8_math else "f16",
         "data": "synthetic",
         "config": {
             "workload": w.name,
@@ -401,7 +415,7 @@ def main():
             "partition_size": w.partition_size,
             "layers_rotated": args.layers,
             "entry_points": ("kvq_append+kvq_paged_decode_attn" if args.separate_calls
-                             else "kvq_decode_step"),
+                             else "kvq_decode_step") + ("_fp8math" if w.fp8_math else ""),
         },
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),

@@ -16,6 +16,9 @@
  *     the online INT8 KV cache, read here as symmetric INT8 with one fp32 scale per (token, head);
  *     INT4, named beside it, read as asymmetric 4-bit codes with an fp32 (scale, zero point) pair
  *     per (token, head).
+ *     FP8 attention (FP8 in the arithmetic, not only in storage), to which the thread points, with
+ *     E4M3 as its format: the *_fp8math calls, read as query rows quantized to E4M3 with one
+ *     dynamic fp32 scale per row and QK^T on the FP8 matrix cores.
  *   "[QST] Scale factors and benchmarks" (QQQ issue thread):
  *     the cache lives in a paged-attention serving stack: fixed-size blocks of tokens reached
  *     through a per-sequence block table.
@@ -188,6 +191,40 @@ int kvq_paged_prefill_attn(const kvq_cache *cache, const void *q, void *out, int
                            const int32_t *context_lens, int32_t batch, int32_t max_context_len,
                            void *stream);
 
+/* FP8 math ("[Feature] TurboMind support W8A8 or FP8 KV Cache": the FP8 attention it points to,
+ * whose format is E4M3).  Each 128-wide fp16 query row q is quantized to OCP E4M3 with its own
+ * scale,
+ *   s_q = fl32(max_d |q_d| / 448)  (1 for an all-zero row),   c_d = enc_E4M3(fl32(q_d / s_q))
+ * (the cache encoder: nearest, ties to even, saturating), and the attention is that of the row
+ * dec(c) * s_q: QK^T multiplies the E4M3 codes with the cache's K codes as stored, on the FP8
+ * matrix cores with fp32 accumulation (exact products), and everything after the logits is as in
+ * the fp16 calls.  The result differs from the fp16-query attention by the query's quantization.
+ *   kvq_paged_decode_attn_fp8math, kvq_decode_step_fp8math, kvq_paged_prefill_attn_fp8math take the
+ *   arguments of kvq_paged_decode_attn, kvq_decode_step and kvq_paged_prefill_attn (the same
+ *   workspace sizes) and need an fp8_e4m3 or fp8_e5m2 cache (else KVQ_ERR_DTYPE); every grouping
+ *   Hq / Hkv <= 16 runs on the grouped-head matrix-core kernel.  Inputs are assumed finite. */
+int kvq_paged_decode_attn_fp8math(const kvq_cache *cache, const void *q, void *out,
+                                  int32_t num_q_heads, float sm_scale, const int32_t *block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                  int32_t batch, int32_t max_context_len, int32_t partition_size,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+int kvq_decode_step_fp8math(const kvq_cache *cache, const void *k_new, const void *v_new,
+                            const void *q, void *out, int32_t num_q_heads, float sm_scale,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, int32_t batch, int32_t max_context_len,
+                            int32_t partition_size, void *workspace, size_t workspace_bytes,
+                            void *stream);
+int kvq_paged_prefill_attn_fp8math(const kvq_cache *cache, const void *q, void *out,
+                                   int32_t num_q_heads, float sm_scale, const int32_t *cu_q_lens,
+                                   int32_t num_q_rows, int32_t max_q_len, const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                   int32_t batch, int32_t max_context_len, void *stream);
+
+/* The query quantization of the FP8-math calls on its own: q fp16 [num_rows][128] (device) ->
+ * codes uint8 [num_rows][128] (E4M3) and scales fp32 [num_rows] (device, caller-owned), bit-exact
+ * as defined above.  For inspection and tests. */
+int kvq_quantize_q_fp8(const void *q, int32_t num_rows, void *codes, float *scales, void *stream);
+
 /* Dequantize the cache into dense fp32 [batch][Hkv][max_context_len][128] arrays for K and V:
  * each element is fl32(dec(code) * kv_scale) (FP8), fl32(q * s) (INT8) or fl32(q * s + zp)
  * (INT4), one rounding.  Slots t >= context_lens[b] are left untouched.  For inspection and tests;
@@ -209,11 +246,11 @@ const char *kvq_status_string(int status);
 const char *kvq_last_error(void);
 
 /* Kernel-timing hook for benchmarks: after kvq_timing_begin(capacity), each kvq_paged_decode_attn,
- * kvq_decode_step or kvq_paged_prefill_attn call times its main (attention) kernel with a HIP event
- * pair recorded in that kernel's own dispatch (hipExtLaunchKernel), on the call's stream, for up to
- * `capacity` calls.  kvq_timing_end() waits for the events, returns the summed milliseconds and the
- * number of timed launches, and releases the events.  Events are created in kvq_timing_begin,
- * outside any timed region.  Not thread-safe: one timing session at a time.  Returns KVQ_OK or
+ * kvq_decode_step or kvq_paged_prefill_attn call (or its FP8-math variant) times its main
+ * (attention) kernel with a HIP event pair recorded in that kernel's own dispatch
+ * (hipExtLaunchKernel), on the call's stream, for up to `capacity` calls.  kvq_timing_end() waits
+ * for the events, returns the summed milliseconds and the number of timed launches, and releases
+ * the events.  Events are created in kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a time.  Returns KVQ_OK or
  * KVQ_ERR_ARG / KVQ_ERR_HIP. */
 int kvq_timing_begin(int32_t capacity);
 int kvq_timing_end(double *main_ms_total, int32_t *main_count);

@@ -68,6 +68,14 @@ int check_common(const int32_t* block_tables, int32_t max_blocks_per_seq, const 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// FP8 math multiplies the E4M3 query codes with the cache's own codes on the OCP FP8 matrix cores.
+int check_fp8_math(const kvq_cache* c) {
+    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2)
+        return fail(KVQ_ERR_DTYPE, "FP8 math needs an fp8_e4m3 or fp8_e5m2 cache (dtype %d given)",
+                    (int)c->dtype);
+    return KVQ_OK;
+}
+
 // Work split of the decode attention.  Fixed partitions: P partitions of PS tokens (P == 1: one
 // pass, no workspace).  Balanced split: NW waves per head row (query heads for MHA, KV heads for
 // grouped heads), about kBalancedWaves waves in all -- two per SIMD of the 1024 on the chip, enough
@@ -202,14 +210,16 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
 
 namespace {
 
-// Shared body of kvq_paged_decode_attn and kvq_decode_step (k_new / v_new set for the latter).
-int decode_common(const char* where, const kvq_cache* cache, const void* k_new, const void* v_new,
-                  const void* q, void* out, int32_t num_q_heads, float sm_scale,
+// Shared body of kvq_paged_decode_attn and kvq_decode_step (k_new / v_new set for the latter) and
+// of their FP8-math variants.
+int decode_common(const char* where, bool fp8_math, const kvq_cache* cache, const void* k_new,
+                  const void* v_new, const void* q, void* out, int32_t num_q_heads, float sm_scale,
                   const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, int32_t batch, int32_t max_context_len,
                   int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_cache(cache);
     if (st) return st;
+    if (fp8_math && (st = check_fp8_math(cache))) return st;
     st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
     if (st) return st;
     if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
@@ -258,6 +268,7 @@ int decode_common(const char* where, const kvq_cache* cache, const void* k_new, 
     a.part_o = a.part_m = a.part_l = nullptr;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
+    a.fp8_math = fp8_math;
     if (need > 0) {
         char* w = static_cast<char*>(workspace);
         if (p.plan_bytes) a.plan = reinterpret_cast<int32_t*>(w);
@@ -289,8 +300,18 @@ int kvq_paged_decode_attn(const kvq_cache* cache, const void* q, void* out, int3
                           const int32_t* context_lens, int32_t batch, int32_t max_context_len,
                           int32_t partition_size, void* workspace, size_t workspace_bytes,
                           void* stream) {
-    return decode_common("kvq_paged_decode_attn", cache, nullptr, nullptr, q, out, num_q_heads,
+    return decode_common("kvq_paged_decode_attn", false, cache, nullptr, nullptr, q, out, num_q_heads,
                          sm_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                         max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+int kvq_paged_decode_attn_fp8math(const kvq_cache* cache, const void* q, void* out,
+                                  int32_t num_q_heads, float sm_scale, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t batch, int32_t max_context_len, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_common("kvq_paged_decode_attn_fp8math", true, cache, nullptr, nullptr, q, out,
+                         num_q_heads, sm_scale, block_tables, max_blocks_per_seq, context_lens, batch,
                          max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
 
@@ -300,18 +321,34 @@ int kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new
                     int32_t max_context_len, int32_t partition_size, void* workspace,
                     size_t workspace_bytes, void* stream) {
     if (batch > 0 && (!k_new || !v_new)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
-    return decode_common("kvq_decode_step", cache, k_new, v_new, q, out, num_q_heads, sm_scale,
+    return decode_common("kvq_decode_step", false, cache, k_new, v_new, q, out, num_q_heads, sm_scale,
                          block_tables, max_blocks_per_seq, context_lens, batch, max_context_len,
                          partition_size, workspace, workspace_bytes, stream);
 }
 
-int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int32_t num_q_heads,
-                           float sm_scale, const int32_t* cu_q_lens, int32_t num_q_rows,
-                           int32_t max_q_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           const int32_t* context_lens, int32_t batch, int32_t max_context_len,
-                           void* stream) {
+int kvq_decode_step_fp8math(const kvq_cache* cache, const void* k_new, const void* v_new,
+                            const void* q, void* out, int32_t num_q_heads, float sm_scale,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                            int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    if (batch > 0 && (!k_new || !v_new)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
+    return decode_common("kvq_decode_step_fp8math", true, cache, k_new, v_new, q, out, num_q_heads,
+                         sm_scale, block_tables, max_blocks_per_seq, context_lens, batch,
+                         max_context_len, partition_size, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_common(const char* where, bool fp8_math, const kvq_cache* cache, const void* q, void* out,
+                   int32_t num_q_heads, float sm_scale, const int32_t* cu_q_lens, int32_t num_q_rows,
+                   int32_t max_q_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, int32_t batch, int32_t max_context_len, void* stream) {
     int st = check_cache(cache);
     if (st) return st;
+    if (fp8_math && (st = check_fp8_math(cache))) return st;
     st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
     if (st) return st;
     if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
@@ -350,6 +387,7 @@ int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.context_lens = context_lens;
     a.batch = batch;
+    a.fp8_math = fp8_math;
     hipEvent_t ev[2] = {nullptr, nullptr};
     if (g_timing.active && g_timing.used < g_timing.capacity) {
         const int slot = g_timing.used++;
@@ -357,7 +395,42 @@ int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int
         ev[1] = g_timing.ev[2 * slot + 1];
     }
     hipError_t e = kvq::launch_prefill(a, static_cast<hipStream_t>(stream), ev[0], ev[1]);
-    if (e != hipSuccess) return hip_fail(e, "kvq_paged_prefill_attn");
+    if (e != hipSuccess) return hip_fail(e, where);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_paged_prefill_attn(const kvq_cache* cache, const void* q, void* out, int32_t num_q_heads,
+                           float sm_scale, const int32_t* cu_q_lens, int32_t num_q_rows,
+                           int32_t max_q_len, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t batch, int32_t max_context_len,
+                           void* stream) {
+    return prefill_common("kvq_paged_prefill_attn", false, cache, q, out, num_q_heads, sm_scale,
+                          cu_q_lens, num_q_rows, max_q_len, block_tables, max_blocks_per_seq,
+                          context_lens, batch, max_context_len, stream);
+}
+
+int kvq_paged_prefill_attn_fp8math(const kvq_cache* cache, const void* q, void* out,
+                                   int32_t num_q_heads, float sm_scale, const int32_t* cu_q_lens,
+                                   int32_t num_q_rows, int32_t max_q_len, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t batch, int32_t max_context_len, void* stream) {
+    return prefill_common("kvq_paged_prefill_attn_fp8math", true, cache, q, out, num_q_heads, sm_scale,
+                          cu_q_lens, num_q_rows, max_q_len, block_tables, max_blocks_per_seq,
+                          context_lens, batch, max_context_len, stream);
+}
+
+int kvq_quantize_q_fp8(const void* q, int32_t num_rows, void* codes, float* scales, void* stream) {
+    if (num_rows < 0) return fail(KVQ_ERR_ARG, "num_rows %d is negative", num_rows);
+    if (num_rows == 0) return ok();
+    if (!q || !codes || !scales) return fail(KVQ_ERR_ARG, "q / codes / scales is NULL");
+    hipError_t e = kvq::launch_quantize_q_fp8(static_cast<const uint16_t*>(q), num_rows,
+                                              static_cast<uint8_t*>(codes), scales,
+                                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kvq_quantize_q_fp8");
     return ok();
 }
 

@@ -1,6 +1,6 @@
 // kvq_attn_gqa.hip -- decode attention for grouped query heads (the MFMA kernel).
 #include "kvq_attn.h"
-#include "kvq_mfma.h"
+#include "kvq_fp8m.h"
 
 namespace kvq {
 
@@ -16,6 +16,10 @@ namespace kvq {
 //                 B = P^T in exactly the layout the S^T accumulator left it (lane: head, the same
 //                 tokens), so no transposition is needed.  P is split into fp16 hi + lo parts.
 // The online softmax keeps one running max per head (all lanes of a column agree).
+// F8Q (FP8 math, OCP E4M3 / E5M2 caches): the wave quantizes its query rows to E4M3 (one scale per
+// head, kvq_fp8m.h) and S^T runs on v_mfma_f32_16x16x32_{fp8,bf8}_fp8 with the K codes as loaded --
+// the same lane layout, 8 one-byte k-slots per lane -- so K needs no decode; the head's s_q joins
+// its logit scale.  P V^T is unchanged.  With F8Q the kernel also serves one query head per KV head.
 
 // Replace the appended token's slot in the MFMA operand registers of its tile by the codes in LDS
 // (K: lane (token, k-group) takes chunks q4 and q4 + 4 of the token; V: the lanes of k-group
@@ -85,7 +89,7 @@ __device__ __forceinline__ void flush_append_g(const KernelParams& a, PendingApp
 // APPEND: the decode step's new token is quantized by the wave whose segment holds the sequence's
 // last tile and patched into its registers; its stores are left pending until the wave's end (one
 // wave per (KV head, tile) reads it, so the wave is the tile's only reader and writer).
-template <int DT, int TW, bool APPEND>
+template <int DT, int TW, bool APPEND, bool F8Q>
 __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g, int n, int nt, int lo,
                                             int hi, int64_t rmul, int64_t radd, int lane,
                                             u32x4* lds_knew, uint8_t* lds_vnew, PendingAppendG& pend) {
@@ -119,6 +123,9 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
         for (int m = 0; m < 4; ++m)
             qB[m] = *reinterpret_cast<const half8_v*>(qrow + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
     }
+    [[maybe_unused]] fp8x8_t q8[4];  // F8Q: the E4M3 codes of qB
+    float qk_f = a.qk_scale;         // logit scale of this lane's head
+    if constexpr (F8Q) qk_f *= quantize_q_row_fp8(qB, q8);
 
     float m_run = kNegInf;  // running max of this lane's head (base-2 logits)
     float l_lane = 0.0f;    // sum of this lane's weights (tokens 4 q4 .. +3 of every tile)
@@ -188,14 +195,22 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
 #pragma unroll
             for (int i = 0; i < TW; ++i) {
                 float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].x, ka[i].y), qB[0], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].z, ka[i].w), qB[1], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].x, kb[i].y), qB[2], sacc, 0, 0, 0);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].z, kb[i].w), qB[3], sacc, 0, 0, 0);
+                if constexpr (F8Q) {
+                    const uint32_t kw[8] = {ka[i].x, ka[i].y, ka[i].z, ka[i].w,
+                                            kb[i].x, kb[i].y, kb[i].z, kb[i].w};
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        sacc = mfma_qk_fp8<DT>(k_fp8x8(kw[2 * m], kw[2 * m + 1]), q8[m], sacc);
+                } else {
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].x, ka[i].y), qB[0], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].z, ka[i].w), qB[1], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].x, kb[i].y), qB[2], sacc, 0, 0, 0);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(kb[i].z, kb[i].w), qB[3], sacc, 0, 0, 0);
+                }
                 const int pos0 = (tb + c0 + i) * kBlock + 4 * q4;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    float f = a.qk_scale;
+                    float f = qk_f;
                     if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
                     z[i][t] = (pos0 + t < t_end) ? sacc[t] * f : kNegInf;
                     cmax = fmaxf(cmax, z[i][t]);
@@ -275,8 +290,8 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
 }
 
 // BAL: grid (KV head, wave of the balanced split), else (KV head, partition, sequence).
-template <int DT, int TW, bool APPEND, bool BAL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((DT == KVQ_INT8 && APPEND) ? 3 : 4), 8))) void attn_partition_mfma(
+template <int DT, int TW, bool APPEND, bool BAL, bool F8Q>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((DT == KVQ_INT8 || DT == KVQ_FP8_E4M3FNUZ) && APPEND ? 3 : 4), 8))) void attn_partition_mfma(
     KernelParams a) {
     __shared__ u32x4 lds_knew[APPEND ? 8 : 1];
     __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
@@ -288,7 +303,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
     if constexpr (BAL) {
         const int w = blockIdx.y;
         for_each_segment(a, w, g == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
-            gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, lds_knew, lds_vnew, pend);
+            gqa_segment<DT, TW, APPEND, F8Q>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, lds_knew, lds_vnew, pend);
         });
         if constexpr (APPEND) flush_append_g<DT>(a, pend, lds_knew, g, lane, v_off);
     } else {
@@ -310,8 +325,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
         const int lo = p * (a.PS / kBlock);
         if (lo >= nt) return;
         const int hi = min(nt, lo + a.PS / kBlock);
-        gqa_segment<DT, TW, APPEND>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane,
-                                    lds_knew, lds_vnew, pend);
+        gqa_segment<DT, TW, APPEND, F8Q>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane,
+                                         lds_knew, lds_vnew, pend);
         if constexpr (APPEND) flush_append_g<DT>(a, pend, lds_knew, g, lane, v_off);
     }
 }
@@ -321,23 +336,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : ((
 #define KVQ_GQA_TILES 2
 #endif
 
-template <int DT, bool BAL>
+template <int DT, bool BAL, bool F8Q>
 static void launch_gqa(const KernelParams& kp, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     // one wave per KV head; the KV head is the fastest grid dimension
     const dim3 grid = BAL ? dim3((unsigned)kp.Hkv, (unsigned)kp.NW)
                           : dim3((unsigned)kp.Hkv, (unsigned)kp.P, (unsigned)kp.B);
     if (kp.k_new)
-        launch_timed(attn_partition_mfma<DT, KVQ_GQA_TILES, true, BAL>, grid, kp, stream, t0, t1);
+        launch_timed(attn_partition_mfma<DT, KVQ_GQA_TILES, true, BAL, F8Q>, grid, kp, stream, t0, t1);
     else
-        launch_timed(attn_partition_mfma<DT, KVQ_GQA_TILES, false, BAL>, grid, kp, stream, t0, t1);
+        launch_timed(attn_partition_mfma<DT, KVQ_GQA_TILES, false, BAL, F8Q>, grid, kp, stream, t0, t1);
 }
 
-template <int DT>
+template <int DT, bool F8Q = false>
 static void launch_gqa(const KernelParams& kp, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
     if (kp.NW > 0)
-        launch_gqa<DT, true>(kp, stream, t0, t1);
+        launch_gqa<DT, true, F8Q>(kp, stream, t0, t1);
     else
-        launch_gqa<DT, false>(kp, stream, t0, t1);
+        launch_gqa<DT, false, F8Q>(kp, stream, t0, t1);
 }
 
 void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream, hipEvent_t start,
@@ -348,6 +363,12 @@ void launch_partition_gqa(const KernelParams& kp, int dtype, hipStream_t stream,
         case KVQ_FP8_E4M3FNUZ: launch_gqa<KVQ_FP8_E4M3FNUZ>(kp, stream, start, stop); break;
         default: launch_gqa<KVQ_INT8>(kp, stream, start, stop); break;
     }
+}
+
+void launch_partition_fp8math(const KernelParams& kp, int dtype, hipStream_t stream, hipEvent_t start,
+                              hipEvent_t stop) {
+    if (dtype == KVQ_FP8_E5M2) launch_gqa<KVQ_FP8_E5M2, true>(kp, stream, start, stop);
+    else launch_gqa<KVQ_FP8_E4M3, true>(kp, stream, start, stop);
 }
 
 }  // namespace kvq

@@ -8,6 +8,7 @@
 // second kernel merges the partials with the log-sum-exp rule (flash-decoding split-K).  A fused
 // decode step appends the new token inside the partition kernel (see the two kernel files).
 #include "kvq_attn.h"
+#include "kvq_fp8m.h"
 #include "kvq_int4.h"
 
 namespace kvq {
@@ -109,7 +110,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
     kp.k_new = a.k_new;
     kp.v_new = a.v_new;
 
-    if (c.dtype == KVQ_INT4 && kp.Hq == kp.Hkv)
+    if (a.fp8_math)
+        launch_partition_fp8math(kp, c.dtype, stream, main_begin, main_end);
+    else if (c.dtype == KVQ_INT4 && kp.Hq == kp.Hkv)
         launch_partition_mha4(kp, stream, main_begin, main_end);
     else if (c.dtype == KVQ_INT4)
         launch_partition_gqa4(kp, stream, main_begin, main_end);
@@ -124,6 +127,27 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
         e = hipGetLastError();
     }
     return e;
+}
+
+// ------------------------------------------------------------------------------------------------
+// FP8 math query quantization, standalone: one wave per row, lane l holding dims 2l, 2l + 1.
+__global__ __launch_bounds__(64) void quantize_q_fp8_kernel(const uint16_t* q, uint8_t* codes,
+                                                            float* scales) {
+    const int lane = threadIdx.x;
+    const size_t row = blockIdx.x;
+    const half2_t x = *reinterpret_cast<const half2_t*>(q + row * kDim + 2 * lane);
+    const float s = q_fp8_scale(wave_max(fmaxf(fabsf((float)x.x), fabsf((float)x.y))));
+    const uint32_t c = encode_fp8<KVQ_FP8_E4M3>((float)x.x / s) |
+                       (encode_fp8<KVQ_FP8_E4M3>((float)x.y / s) << 8);
+    *reinterpret_cast<uint16_t*>(codes + row * kDim + 2 * lane) = (uint16_t)c;
+    if (lane == 0) scales[row] = s;
+}
+
+hipError_t launch_quantize_q_fp8(const uint16_t* q, int32_t num_rows, uint8_t* codes, float* scales,
+                                 hipStream_t stream) {
+    if (num_rows == 0) return hipSuccess;
+    quantize_q_fp8_kernel<<<dim3((unsigned)num_rows), 64, 0, stream>>>(q, codes, scales);
+    return hipGetLastError();
 }
 
 }  // namespace kvq

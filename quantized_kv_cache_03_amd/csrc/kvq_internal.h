@@ -34,6 +34,7 @@ struct DecodeArgs {
     float* part_l;            // one float per partial row
     const uint16_t* k_new;    // fused decode step: fp16 [B][Hkv][128] rows to append, else NULL
     const uint16_t* v_new;
+    bool fp8_math;            // query rows quantized to E4M3, QK^T on the FP8 matrix cores
 };
 
 // Launch parameters of the prefill attention, resolved by the ABI layer.
@@ -50,6 +51,7 @@ struct PrefillArgs {
     int32_t max_blocks_per_seq;
     const int32_t* context_lens;
     int32_t batch;
+    bool fp8_math;            // query rows quantized to E4M3, QK^T on the FP8 matrix cores
 };
 
 hipError_t launch_append(const kvq_cache& c, const uint16_t* k_new, const uint16_t* v_new,
@@ -69,5 +71,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t mai
 
 // Prefill attention kernel; the optional events time its own dispatch (kernel-timing hook).
 hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+// FP8 math: each 128-wide fp16 query row -> E4M3 codes and its fp32 scale (the quantization the
+// FP8-math attention kernels apply to their query rows).
+hipError_t launch_quantize_q_fp8(const uint16_t* q, int32_t num_rows, uint8_t* codes, float* scales,
+                                 hipStream_t stream);
 
 }  // namespace kvq

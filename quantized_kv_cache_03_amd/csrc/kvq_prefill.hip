@@ -18,9 +18,11 @@
 // Each column masks the tokens past its own position; the wave reads the tiles up to the position
 // of its last row.  The tiles of a head stay in its XCD's L2 for the other row tiles of the head
 // (the KV head is the fastest grid dimension, and workgroup ids go round-robin to the 8 XCDs).
+// F8Q (FP8 math, OCP E4M3 / E5M2 caches): each column's query row is quantized to E4M3 with its own
+// scale (kvq_fp8m.h) and S^T runs on v_mfma_f32_16x16x32_{fp8,bf8}_fp8 with the K codes as loaded.
 #include "kvq_attn.h"
+#include "kvq_fp8m.h"
 #include "kvq_int4.h"
-#include "kvq_mfma.h"
 
 namespace kvq {
 
@@ -46,7 +48,7 @@ struct PrefillParams {
 
 // NB column blocks of 16 per wave (NB R consecutive rows): the K and V^T operands of a tile are
 // decoded once and feed the MFMAs of every block, which is what keeps the VALU from limiting.
-template <int DT, int NB>
+template <int DT, int NB, bool F8Q>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 : (NB > 1 ? 2 : (DT == KVQ_INT8 ? 3 : 4)), 8))) void attn_prefill_mfma(
     PrefillParams a) {
     constexpr int TW = 2;  // tiles per chunk, paired for the PV products
@@ -101,6 +103,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
             for (int m = 0; m < 4; ++m)
                 qB[nb][m] = *reinterpret_cast<const half8_v*>(a.q + orow[nb] + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
         }
+    }
+    [[maybe_unused]] fp8x8_t q8[NB][4];  // F8Q: the E4M3 codes of qB
+    float qk_f[NB];                      // logit scale of each block's column
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        qk_f[nb] = a.qk_scale;
+        if constexpr (F8Q) qk_f[nb] *= quantize_q_row_fp8(qB[nb], q8[nb]);
     }
 
     float m_run[NB], l_lane[NB];  // per block: running max (base-2 logits) and this lane's weights
@@ -184,21 +193,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
             const bool all_visible = tok_base + TW * kBlock - 1 <= pos_min;  // wave-uniform
 #pragma unroll
             for (int i = 0; i < TW; ++i) {
-                const half8_v k0 = codes8<DT>(ka[i].x, ka[i].y), k1 = codes8<DT>(ka[i].z, ka[i].w);
-                const half8_v k2 = codes8<DT>(kb[i].x, kb[i].y), k3 = codes8<DT>(kb[i].z, kb[i].w);
                 const int tok0 = tok_base + i * kBlock + 4 * q4;
+                float4_t sacc[NB];
+                if constexpr (F8Q) {
+                    const uint32_t kw[8] = {ka[i].x, ka[i].y, ka[i].z, ka[i].w,
+                                            kb[i].x, kb[i].y, kb[i].z, kb[i].w};
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        sacc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            sacc[nb] = mfma_qk_fp8<DT>(k_fp8x8(kw[2 * m], kw[2 * m + 1]), q8[nb][m], sacc[nb]);
+                    }
+                } else {
+                    const half8_v k0 = codes8<DT>(ka[i].x, ka[i].y), k1 = codes8<DT>(ka[i].z, ka[i].w);
+                    const half8_v k2 = codes8<DT>(kb[i].x, kb[i].y), k3 = codes8<DT>(kb[i].z, kb[i].w);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        sacc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qB[nb][0], sacc[nb], 0, 0, 0);
+                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qB[nb][1], sacc[nb], 0, 0, 0);
+                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k2, qB[nb][2], sacc[nb], 0, 0, 0);
+                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k3, qB[nb][3], sacc[nb], 0, 0, 0);
+                    }
+                }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qB[nb][0], sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qB[nb][1], sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k2, qB[nb][2], sacc, 0, 0, 0);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k3, qB[nb][3], sacc, 0, 0, 0);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        float f = a.qk_scale;
+                        float f = qk_f[nb];
                         if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
-                        z[nb][i][t] = sacc[t] * f;
+                        z[nb][i][t] = sacc[nb][t] * f;
                         // a token past the column's own position is masked
                         if (!all_visible && tok0 + t > pos[nb]) z[nb][i][t] = kNegInf;
                     }
@@ -355,11 +380,16 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
         else
             hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a);
     };
+    if (p.fp8_math) {
+        if (c.dtype == KVQ_FP8_E5M2) go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, true>);
+        else go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, true>);
+        return hipGetLastError();
+    }
     switch (c.dtype) {
-        case KVQ_FP8_E4M3: go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS>); break;
-        case KVQ_FP8_E5M2: go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS>); break;
-        case KVQ_FP8_E4M3FNUZ: go(attn_prefill_mfma<KVQ_FP8_E4M3FNUZ, KVQ_PREFILL_BLOCKS>); break;
-        default: go(attn_prefill_mfma<KVQ_INT8, KVQ_PREFILL_BLOCKS>); break;
+        case KVQ_FP8_E4M3: go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, false>); break;
+        case KVQ_FP8_E5M2: go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, false>); break;
+        case KVQ_FP8_E4M3FNUZ: go(attn_prefill_mfma<KVQ_FP8_E4M3FNUZ, KVQ_PREFILL_BLOCKS, false>); break;
+        default: go(attn_prefill_mfma<KVQ_INT8, KVQ_PREFILL_BLOCKS, false>); break;
     }
     return hipGetLastError();
 }

@@ -114,21 +114,23 @@ class DeviceCase:
         K.append(self.cache, self.step_k_d, self.step_v_d, self.bt_d, self.ctx_d, stream=stream)
 
     def attention(self, partition_size: int | None = None, stream=None, out=None):
+        """kvq_paged_decode_attn (kvq_paged_decode_attn_fp8math for an FP8-math workload)."""
         ps = self.partition_size if partition_size is None else partition_size
         ws = self.workspace if ps == self.partition_size else None
-        return K.paged_decode_attn(self.cache, self.q_d, self.bt_d, self.ctx_d, self.max_ctx,
-                                   partition_size=ps, workspace=ws,
-                                   out=self.out_d if out is None else out, stream=stream)
+        fn = K.paged_decode_attn_fp8math if self.w.fp8_math else K.paged_decode_attn
+        return fn(self.cache, self.q_d, self.bt_d, self.ctx_d, self.max_ctx, partition_size=ps,
+                  workspace=ws, out=self.out_d if out is None else out, stream=stream)
 
     def step(self, stream=None, fused: bool = True):
         """One decode step: append one token per sequence, then attention (one fused call, or
-        kvq_append followed by kvq_paged_decode_attn)."""
+        kvq_append followed by the attention call); FP8 math for an FP8-math workload."""
         if not fused:
             self.append_step(stream)
             return self.attention(stream=stream)
-        return K.decode_step(self.cache, self.step_k_d, self.step_v_d, self.q_d, self.bt_d, self.ctx_d,
-                             self.max_ctx, partition_size=self.partition_size,
-                             workspace=self.workspace, out=self.out_d, stream=stream)
+        fn = K.decode_step_fp8math if self.w.fp8_math else K.decode_step
+        return fn(self.cache, self.step_k_d, self.step_v_d, self.q_d, self.bt_d, self.ctx_d,
+                  self.max_ctx, partition_size=self.partition_size, workspace=self.workspace,
+                  out=self.out_d, stream=stream)
 
     # host views of the sequences' own rows (regenerated from the seeds)
     def rows_of(self, b: int):

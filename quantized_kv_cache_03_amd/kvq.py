@@ -57,6 +57,14 @@ lib.kvq_decode_step.restype = ctypes.c_int
 lib.kvq_paged_prefill_attn.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _i32, _f32, _vp, _i32, _i32,
                                        _vp, _i32, _vp, _i32, _i32, _vp]
 lib.kvq_paged_prefill_attn.restype = ctypes.c_int
+lib.kvq_paged_decode_attn_fp8math.argtypes = lib.kvq_paged_decode_attn.argtypes
+lib.kvq_paged_decode_attn_fp8math.restype = ctypes.c_int
+lib.kvq_decode_step_fp8math.argtypes = lib.kvq_decode_step.argtypes
+lib.kvq_decode_step_fp8math.restype = ctypes.c_int
+lib.kvq_paged_prefill_attn_fp8math.argtypes = lib.kvq_paged_prefill_attn.argtypes
+lib.kvq_paged_prefill_attn_fp8math.restype = ctypes.c_int
+lib.kvq_quantize_q_fp8.argtypes = [_vp, _i32, _vp, _vp, _vp]
+lib.kvq_quantize_q_fp8.restype = ctypes.c_int
 lib.kvq_dequant.argtypes = [ctypes.POINTER(KvqCache), _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp]
 lib.kvq_dequant.restype = ctypes.c_int
 lib.kvq_dtype_from_string.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]
@@ -73,7 +81,8 @@ lib.kvq_version.argtypes = []
 lib.kvq_version.restype = ctypes.c_char_p
 
 EXPORTS = ["kvq_append", "kvq_decode_workspace_size", "kvq_paged_decode_attn", "kvq_decode_step",
-           "kvq_paged_prefill_attn", "kvq_dequant",
+           "kvq_paged_prefill_attn", "kvq_dequant", "kvq_paged_decode_attn_fp8math",
+           "kvq_decode_step_fp8math", "kvq_paged_prefill_attn_fp8math", "kvq_quantize_q_fp8",
            "kvq_dtype_from_string", "kvq_status_string", "kvq_last_error", "kvq_timing_begin",
            "kvq_timing_end", "kvq_version"]
 
@@ -189,6 +198,23 @@ def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.
                       partition_size: int = PARTITION_BALANCED, workspace: torch.Tensor | None = None,
                       out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """kvq_paged_decode_attn: q fp16 [B][Hq][128] -> out fp16 [B][Hq][128]."""
+    return _decode_attn("kvq_paged_decode_attn", cache, q, block_tables, context_lens, max_context_len,
+                        sm_scale, partition_size, workspace, out, stream)
+
+
+def paged_decode_attn_fp8math(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, max_context_len: int,
+                              sm_scale: float | None = None, partition_size: int = PARTITION_BALANCED,
+                              workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """kvq_paged_decode_attn_fp8math: as paged_decode_attn, the query rows quantized to E4M3 and
+    QK^T on the FP8 matrix cores (E4M3 / E5M2 caches)."""
+    return _decode_attn("kvq_paged_decode_attn_fp8math", cache, q, block_tables, context_lens,
+                        max_context_len, sm_scale, partition_size, workspace, out, stream)
+
+
+def _decode_attn(name, cache, q, block_tables, context_lens, max_context_len, sm_scale, partition_size,
+                 workspace, out, stream):
     assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
     B, Hq, _ = q.shape
     if sm_scale is None:
@@ -200,10 +226,10 @@ def paged_decode_attn(cache: PagedKVCache, q: torch.Tensor, block_tables: torch.
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = cache.descriptor()
-    _check(lib.kvq_paged_decode_attn(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
-                                     _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
-                                     int(max_context_len), int(partition_size), _ptr(workspace),
-                                     ws_bytes, _stream(stream)), "kvq_paged_decode_attn")
+    _check(getattr(lib, name)(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
+                              _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+                              int(max_context_len), int(partition_size), _ptr(workspace), ws_bytes,
+                              _stream(stream)), name)
     return out
 
 
@@ -213,6 +239,22 @@ def decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q
                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 stream=None) -> torch.Tensor:
     """kvq_decode_step: append one row per sequence (fp16 [B][Hkv][128]) and attend, fused."""
+    return _decode_step("kvq_decode_step", cache, k_new, v_new, q, block_tables, context_lens,
+                        max_context_len, sm_scale, partition_size, workspace, out, stream)
+
+
+def decode_step_fp8math(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                        sm_scale: float | None = None, partition_size: int = PARTITION_BALANCED,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """kvq_decode_step_fp8math: decode_step with FP8 math for QK^T."""
+    return _decode_step("kvq_decode_step_fp8math", cache, k_new, v_new, q, block_tables, context_lens,
+                        max_context_len, sm_scale, partition_size, workspace, out, stream)
+
+
+def _decode_step(name, cache, k_new, v_new, q, block_tables, context_lens, max_context_len, sm_scale,
+                 partition_size, workspace, out, stream):
     assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
     assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
     B, Hq, _ = q.shape
@@ -226,10 +268,10 @@ def decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     d = cache.descriptor()
-    _check(lib.kvq_decode_step(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), Hq,
-                               float(sm_scale), _ptr(block_tables), block_tables.shape[1],
-                               _ptr(context_lens), B, int(max_context_len), int(partition_size),
-                               _ptr(workspace), ws_bytes, _stream(stream)), "kvq_decode_step")
+    _check(getattr(lib, name)(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), Hq,
+                              float(sm_scale), _ptr(block_tables), block_tables.shape[1],
+                              _ptr(context_lens), B, int(max_context_len), int(partition_size),
+                              _ptr(workspace), ws_bytes, _stream(stream)), name)
     return out
 
 
@@ -239,6 +281,21 @@ def paged_prefill_attn(cache: PagedKVCache, q: torch.Tensor, cu_q_lens: torch.Te
                        stream=None) -> torch.Tensor:
     """kvq_paged_prefill_attn: q fp16 [T][Hq][128] (rows of sequence b at cu_q_lens[b] ..
     cu_q_lens[b+1]-1, the last rows of its context) -> out fp16 [T][Hq][128], causal."""
+    return _prefill("kvq_paged_prefill_attn", cache, q, cu_q_lens, block_tables, context_lens,
+                    max_context_len, max_q_len, sm_scale, out, stream)
+
+
+def paged_prefill_attn_fp8math(cache: PagedKVCache, q: torch.Tensor, cu_q_lens: torch.Tensor,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               max_context_len: int, max_q_len: int, sm_scale: float | None = None,
+                               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_paged_prefill_attn_fp8math: paged_prefill_attn with FP8 math for QK^T."""
+    return _prefill("kvq_paged_prefill_attn_fp8math", cache, q, cu_q_lens, block_tables, context_lens,
+                    max_context_len, max_q_len, sm_scale, out, stream)
+
+
+def _prefill(name, cache, q, cu_q_lens, block_tables, context_lens, max_context_len, max_q_len,
+             sm_scale, out, stream):
     assert q.dtype == torch.float16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM
     T, Hq, _ = q.shape
     B = context_lens.shape[0]
@@ -247,11 +304,22 @@ def paged_prefill_attn(cache: PagedKVCache, q: torch.Tensor, cu_q_lens: torch.Te
     if out is None:
         out = torch.empty_like(q)
     d = cache.descriptor()
-    _check(lib.kvq_paged_prefill_attn(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
-                                      _ptr(cu_q_lens), T, int(max_q_len), _ptr(block_tables),
-                                      block_tables.shape[1], _ptr(context_lens), B,
-                                      int(max_context_len), _stream(stream)), "kvq_paged_prefill_attn")
+    _check(getattr(lib, name)(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
+                              _ptr(cu_q_lens), T, int(max_q_len), _ptr(block_tables),
+                              block_tables.shape[1], _ptr(context_lens), B, int(max_context_len),
+                              _stream(stream)), name)
     return out
+
+
+def quantize_q_fp8(q: torch.Tensor, stream=None):
+    """kvq_quantize_q_fp8: fp16 rows [..., 128] -> (E4M3 codes uint8 [..., 128], fp32 scales [...])."""
+    assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM and q.is_contiguous()
+    codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    scales = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    rows = q.numel() // HEAD_DIM
+    _check(lib.kvq_quantize_q_fp8(_ptr(q), rows, _ptr(codes), _ptr(scales), _stream(stream)),
+           "kvq_quantize_q_fp8")
+    return codes, scales
 
 
 def dequant(cache: PagedKVCache, block_tables: torch.Tensor, context_lens: torch.Tensor,

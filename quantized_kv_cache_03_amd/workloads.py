@@ -45,6 +45,7 @@ class Workload:
     outliers: int = 0
     outlier_gain: float = 20.0
     partition_size: int = -1  # the balanced split (KVQ_PARTITION_BALANCED)
+    fp8_math: bool = False    # query rows quantized to E4M3, QK^T on the FP8 matrix cores
 
     @property
     def group(self) -> int:
@@ -78,6 +79,15 @@ WORKLOADS = {
     "llama2-7b-mha-int4": Workload("llama2-7b-mha-int4", 2, 32, 32, 32, "int4",
                                    ("uniform", 512, 4096), table="shuffled"),
     "llama3-8b-gqa-int4": Workload("llama3-8b-gqa-int4", 3, 64, 32, 8, "int4", ("fixed", 8192)),
+    # FP8 math (same caches and queries as the fp16-math workloads of the same shapes)
+    "llama2-7b-mha-e4m3-fp8math": Workload("llama2-7b-mha-e4m3-fp8math", 2, 32, 32, 32, "fp8_e4m3",
+                                           ("uniform", 512, 4096), table="shuffled",
+                                           scale_rule="amax/448", fp8_math=True),
+    "llama3-8b-gqa-e5m2-fp8math": Workload("llama3-8b-gqa-e5m2-fp8math", 3, 64, 32, 8, "fp8_e5m2",
+                                           ("fixed", 8192), scale_rule="one", fp8_math=True),
+    "llama3-70b-gqa-e4m3-32k-fp8math": Workload("llama3-70b-gqa-e4m3-32k-fp8math", 5, 16, 64, 8,
+                                                "fp8_e4m3", ("fixed", 32768), scale_rule="amax/448",
+                                                fp8_math=True),
 }
 ORDER = list(WORKLOADS)
 

@@ -45,8 +45,9 @@ class OracleTwin:
         oracle.append(self.cache, k, v, self.bt, self.ctx, cu)
         self.q = case.q[self.seqs]
 
-    def attention(self, heads=None, threads=8):
-        return oracle.decode_attn(self.cache, self.q, self.bt, self.ctx, heads=heads, threads=threads)
+    def attention(self, heads=None, threads=8, fp8_math=False):
+        return oracle.decode_attn(self.cache, self.q, self.bt, self.ctx, heads=heads, threads=threads,
+                                  fp8_math=fp8_math)
 
 
 def device_blocks(case, blocks):

@@ -173,3 +173,42 @@ def test_decode_step_argument_errors(K):
     assert L.kvq_decode_step(ctypes.byref(c), 0x50, 0x60, 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1, 64, 16,
                              None, 0, None) == K.ERR_WORKSPACE
     del args
+
+
+@pytest.mark.parametrize("dtype", [3, 4, 5])
+def test_fp8math_rejects_non_ocp_caches(K, dtype):
+    """FP8 math needs OCP E4M3 / E5M2 K codes: INT8, E4M3FNUZ and INT4 caches are KVQ_ERR_DTYPE
+    (before any pointer is touched)."""
+    c = _cache(K, dtype=dtype, k_scale=0x70, v_scale=0x80)
+    L = K.lib
+    assert L.kvq_paged_decode_attn_fp8math(ctypes.byref(c), 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1, 64, 0,
+                                           None, 0, None) == K.ERR_DTYPE
+    assert b"FP8 math" in L.kvq_last_error()
+    assert L.kvq_decode_step_fp8math(ctypes.byref(c), 0x50, 0x60, 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1,
+                                     64, 0, None, 0, None) == K.ERR_DTYPE
+    assert L.kvq_paged_prefill_attn_fp8math(ctypes.byref(c), 0x30, 0x40, 2, 0.1, 0x90, 4, 4, 0x10, 4,
+                                            0x20, 1, 64, None) == K.ERR_DTYPE
+
+
+def test_fp8math_shares_the_validation(K):
+    c = _cache(K)
+    L = K.lib
+    assert L.kvq_paged_decode_attn_fp8math(ctypes.byref(c), 0x30, 0x40, 3, 0.1, 0x10, 4, 0x20, 1, 64, 0,
+                                           None, 0, None) == K.ERR_SHAPE
+    assert L.kvq_paged_decode_attn_fp8math(ctypes.byref(c), 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1, 64, 16,
+                                           None, 0, None) == K.ERR_WORKSPACE
+    assert L.kvq_decode_step_fp8math(ctypes.byref(c), None, 0x60, 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1,
+                                     64, 0, None, 0, None) == K.ERR_ARG
+    assert L.kvq_paged_prefill_attn_fp8math(ctypes.byref(c), 0x30, 0x40, 2, 0.1, 0x90, 4, 65, 0x10, 4,
+                                            0x20, 1, 64, None) == K.ERR_ARG   # max_q_len > max_context
+    # nothing to do: no launch
+    assert L.kvq_paged_decode_attn_fp8math(ctypes.byref(c), None, None, 2, 0.1, None, 0, None, 0, 0, 0,
+                                           None, 0, None) == K.OK
+
+
+def test_quantize_q_fp8_argument_errors(K):
+    L = K.lib
+    assert L.kvq_quantize_q_fp8(0x10, -1, 0x20, 0x30, None) == K.ERR_ARG
+    assert L.kvq_quantize_q_fp8(None, 4, 0x20, 0x30, None) == K.ERR_ARG
+    assert L.kvq_quantize_q_fp8(0x10, 4, 0x20, None, None) == K.ERR_ARG
+    assert L.kvq_quantize_q_fp8(None, 0, None, None, None) == K.OK

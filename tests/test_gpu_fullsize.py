@@ -1,5 +1,5 @@
-"""The five decode workloads (and the E4M3FNUZ and INT4 variants) at full size, in the launch
-configuration the benchmark times.
+"""The five decode workloads (and the E4M3FNUZ, INT4 and FP8-math variants) at full size, in the
+launch configuration the benchmark times.
 
 Each case fills the cache through kvq_append with all but each sequence's last token, runs one
 fused decode step (kvq_decode_step: append that token, then split-K attention with the workload's
@@ -17,7 +17,8 @@ pytestmark = pytest.mark.gpu
 
 NAMES = ["tiny-e4m3", "llama2-7b-mha-e4m3", "llama3-8b-gqa-e5m2", "llama2-13b-mha-int8",
          "llama3-70b-gqa-e4m3-32k", "llama2-7b-mha-e4m3fnuz", "llama3-70b-gqa-e4m3fnuz-32k",
-         "llama2-7b-mha-int4", "llama3-8b-gqa-int4"]
+         "llama2-7b-mha-int4", "llama3-8b-gqa-int4", "llama2-7b-mha-e4m3-fp8math",
+         "llama3-8b-gqa-e5m2-fp8math", "llama3-70b-gqa-e4m3-32k-fp8math"]
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -41,7 +42,7 @@ def test_full_size_decode_step(name):
     say(f"  oracle on sequences {seqs} (ctx {case.ctx[seqs].tolist()})")
     twin = OracleTwin(case, seqs)
     assert_cache_bytes_equal(case, twin, name)
-    ref = twin.attention(threads=16)
+    ref = twin.attention(threads=16, fp8_math=w.fp8_math)
     st = assert_attn_close(o1[seqs], ref, name)
     say(f"  ok {st}")
     del case
