@@ -17,9 +17,9 @@ namespace kvq {
 //                 tokens), so no transposition is needed.  P is split into fp16 hi + lo parts.
 // The online softmax keeps one running max per head (all lanes of a column agree).
 // F8Q (FP8 math, OCP E4M3 / E5M2 caches): the wave quantizes its query rows to E4M3 (one scale per
-// head, kvq_fp8m.h) and S^T runs on v_mfma_f32_16x16x32_{fp8,bf8}_fp8 with the K codes as loaded --
-// the same lane layout, 8 one-byte k-slots per lane -- so K needs no decode; the head's s_q joins
-// its logit scale.  P V^T is unchanged.  With F8Q the kernel also serves one query head per KV head.
+// head, kvq_fp8m.h) and S^T of a tile is one v_mfma_scale_f32_16x16x128_f8f6f4 with the lane's K
+// codes as loaded (32 one-byte k-slots per lane), so K needs no decode; the head's s_q joins its
+// logit scale.  P V^T is unchanged.  With F8Q the kernel also serves one query head per KV head.
 
 // Replace the appended token's slot in the MFMA operand registers of its tile by the codes in LDS
 // (K: lane (token, k-group) takes chunks q4 and q4 + 4 of the token; V: the lanes of k-group
@@ -123,7 +123,7 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
         for (int m = 0; m < 4; ++m)
             qB[m] = *reinterpret_cast<const half8_v*>(qrow + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
     }
-    [[maybe_unused]] fp8x8_t q8[4];  // F8Q: the E4M3 codes of qB
+    [[maybe_unused]] i32x8 q8;       // F8Q: the E4M3 codes of qB
     float qk_f = a.qk_scale;         // logit scale of this lane's head
     if constexpr (F8Q) qk_f *= quantize_q_row_fp8(qB, q8);
 
@@ -196,11 +196,7 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
             for (int i = 0; i < TW; ++i) {
                 float4_t sacc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 if constexpr (F8Q) {
-                    const uint32_t kw[8] = {ka[i].x, ka[i].y, ka[i].z, ka[i].w,
-                                            kb[i].x, kb[i].y, kb[i].z, kb[i].w};
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        sacc = mfma_qk_fp8<DT>(k_fp8x8(kw[2 * m], kw[2 * m + 1]), q8[m], sacc);
+                    sacc = mfma_qk_fp8<DT>(k_fp8x32(ka[i], kb[i]), q8, sacc);
                 } else {
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].x, ka[i].y), qB[0], sacc, 0, 0, 0);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes8<DT>(ka[i].z, ka[i].w), qB[1], sacc, 0, 0, 0);

@@ -1,5 +1,5 @@
 // kvq_fp8m.h -- FP8 math: the query rows quantized to E4M3 for the QK^T product on the FP8 matrix
-// cores (v_mfma_f32_16x16x32_fp8_fp8 / _bf8_fp8), the cache's K codes used as they are stored.
+// cores (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales), the cache's K codes used as stored.
 //
 // "[Feature] TurboMind support W8A8 or FP8 KV Cache" points beyond FP8 storage to FP8 attention,
 // where E4M3 is the format used; it fixes no scale.  Here each 128-wide query row gets its own
@@ -13,7 +13,12 @@
 
 namespace kvq {
 
-typedef long fp8x8_t;  // one lane's 8 FP8 k-slots of a v_mfma_f32_16x16x32_{fp8,bf8}_fp8 operand
+// One lane's 32 FP8 k-slots of a 16x16x128 operand (byte i = k-slot i of the lane's group).  In A
+// (16 rows x 128) and B (128 x 16 columns) lane l holds row / column l % 16 and k-slots
+// 32 (l / 16) .. +31 alike, so any assignment of the 128 dims to a lane group's 32 bytes works as
+// long as K and Q agree: K's two 16-byte loads of the lane (dims 16 q4 .. +15 and 64 + 16 q4 .. +15)
+// and the query codes of the same dims, in the same byte order.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kE4M3Max = 448.0f;
 
@@ -21,13 +26,14 @@ __device__ __forceinline__ float q_fp8_scale(float amax) {
     return amax > 0.0f ? amax / kE4M3Max : 1.0f;  // one correctly rounded fp32 division
 }
 
-// 8 fp16 query values -> their 8 E4M3 codes under scale s, byte i = value i
-__device__ __forceinline__ fp8x8_t q_fp8_codes8(half8_v x, float s) {
+// 8 fp16 query values -> their 8 E4M3 codes under scale s, byte i = value i, in two dwords
+__device__ __forceinline__ void q_fp8_codes8(half8_v x, float s, uint32_t& lo, uint32_t& hi) {
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         w[i >> 2] |= encode_fp8<KVQ_FP8_E4M3>((float)x[i] / s) << (8 * (i & 3));
-    return (fp8x8_t)(((uint64_t)w[1] << 32) | w[0]);
+    lo = w[0];
+    hi = w[1];
 }
 
 __device__ __forceinline__ float abs_max8(half8_v x, float m) {
@@ -37,29 +43,34 @@ __device__ __forceinline__ float abs_max8(half8_v x, float m) {
 }
 
 // One query row held by the four lanes col, col + 16, col + 32, col + 48 (32 values each, in the
-// four half8 operands x[0..3]): its scale and this lane's codes.  Every lane of the wave calls it.
-__device__ __forceinline__ float quantize_q_row_fp8(const half8_v (&x)[4], fp8x8_t (&c)[4]) {
+// four half8 operands x[0..3], dims 64 (m/2) + 16 q4 + 8 (m%2) .. +7 of x[m]): its scale and this
+// lane's 32 codes in that order.  Every lane of the wave calls it.
+__device__ __forceinline__ float quantize_q_row_fp8(const half8_v (&x)[4], i32x8& c) {
     float m = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) m = abs_max8(x[k], m);
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     const float s = q_fp8_scale(m);
+    uint32_t w[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c[k] = q_fp8_codes8(x[k], s);
+    for (int k = 0; k < 4; ++k) q_fp8_codes8(x[k], s, w[2 * k], w[2 * k + 1]);
+    c = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
     return s;
 }
 
-// Two dwords of K codes (8 consecutive dims of one token) as an MFMA operand.
-__device__ __forceinline__ fp8x8_t k_fp8x8(uint32_t lo, uint32_t hi) {
-    return (fp8x8_t)(((uint64_t)hi << 32) | lo);
+// The lane's K codes (its 16-byte loads from the two 1 KiB halves of the tile) as the A operand.
+__device__ __forceinline__ i32x8 k_fp8x32(const u32x4& ka, const u32x4& kb) {
+    const uint32_t w[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
+    return i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
 }
 
-// S^T accumulation of one 32-dim slice: A = K codes (E4M3 or E5M2), B = E4M3 query codes.
+// S^T of one tile, all 128 dims in one instruction: A = K codes (format 0 = E4M3, 1 = E5M2),
+// B = E4M3 query codes; unit scales (the scale operands 0 select the unscaled form).
 template <int DT>
-__device__ __forceinline__ float4_t mfma_qk_fp8(fp8x8_t k, fp8x8_t q, float4_t acc) {
-    if constexpr (DT == KVQ_FP8_E5M2) return __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(k, q, acc, 0, 0, 0);
-    else return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(k, q, acc, 0, 0, 0);
+__device__ __forceinline__ float4_t mfma_qk_fp8(const i32x8& k, const i32x8& q, float4_t acc) {
+    constexpr int FMT_A = DT == KVQ_FP8_E5M2 ? 1 : 0;
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, q, acc, FMT_A, 0, 0, 0, 0, 0);
 }
 
 struct KernelParams;

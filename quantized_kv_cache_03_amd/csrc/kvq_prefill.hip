@@ -19,7 +19,8 @@
 // of its last row.  The tiles of a head stay in its XCD's L2 for the other row tiles of the head
 // (the KV head is the fastest grid dimension, and workgroup ids go round-robin to the 8 XCDs).
 // F8Q (FP8 math, OCP E4M3 / E5M2 caches): each column's query row is quantized to E4M3 with its own
-// scale (kvq_fp8m.h) and S^T runs on v_mfma_f32_16x16x32_{fp8,bf8}_fp8 with the K codes as loaded.
+// scale (kvq_fp8m.h) and S^T of a tile is one v_mfma_scale_f32_16x16x128_f8f6f4 per block with the
+// K codes as loaded.
 #include "kvq_attn.h"
 #include "kvq_fp8m.h"
 #include "kvq_int4.h"
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
                 qB[nb][m] = *reinterpret_cast<const half8_v*>(a.q + orow[nb] + 64 * (m >> 1) + 16 * q4 + 8 * (m & 1));
         }
     }
-    [[maybe_unused]] fp8x8_t q8[NB][4];  // F8Q: the E4M3 codes of qB
+    [[maybe_unused]] i32x8 q8[NB];       // F8Q: the E4M3 codes of qB
     float qk_f[NB];                      // logit scale of each block's column
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -196,15 +197,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
                 const int tok0 = tok_base + i * kBlock + 4 * q4;
                 float4_t sacc[NB];
                 if constexpr (F8Q) {
-                    const uint32_t kw[8] = {ka[i].x, ka[i].y, ka[i].z, ka[i].w,
-                                            kb[i].x, kb[i].y, kb[i].z, kb[i].w};
+                    const i32x8 k8 = k_fp8x32(ka[i], kb[i]);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        sacc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            sacc[nb] = mfma_qk_fp8<DT>(k_fp8x8(kw[2 * m], kw[2 * m + 1]), q8[nb][m], sacc[nb]);
-                    }
+                    for (int nb = 0; nb < NB; ++nb)
+                        sacc[nb] = mfma_qk_fp8<DT>(k8, q8[nb], float4_t{0.0f, 0.0f, 0.0f, 0.0f});
                 } else {
                     const half8_v k0 = codes8<DT>(ka[i].x, ka[i].y), k1 = codes8<DT>(ka[i].z, ka[i].w);
                     const half8_v k2 = codes8<DT>(kb[i].x, kb[i].y), k3 = codes8<DT>(kb[i].z, kb[i].w);
