@@ -1,4 +1,6 @@
-// kvq_mfma.h -- fp16 operands of v_mfma_f32_16x16x32_f16 built from 8-bit codes.
+// kvq_mfma.h -- fp16 operands of v_mfma_f32_16x16x32_f16 built from 8-bit codes, and the
+// column-wise helpers of kernels that keep a 16x16 accumulator (lane l: column l % 16, rows
+// 4 (l / 16) .. +3).
 #pragma once
 
 #include "kvq_device.h"
@@ -17,6 +19,44 @@ template <int DT>
 __device__ __forceinline__ half8_v codes8(uint32_t w0, uint32_t w1) {
     return join8(codes_to_f16<DT, 0>(w0), codes_to_f16<DT, 1>(w0), codes_to_f16<DT, 0>(w1),
                  codes_to_f16<DT, 1>(w1));
+}
+
+// Max and sum over the four lanes of a column (l, l ^ 16, l ^ 32, l ^ 48), every lane getting the
+// result.  v_permlane16_swap / v_permlane32_swap of (x, x) leave the two rows (halves) of each pair
+// in the two results, so one VALU operation per step replaces an LDS permute; each lane of a pair
+// combines the same two values in the same order, so the results agree bitwise.  The max is one
+// v_max_f32 (the callers' logits are never NaN, so no operand needs quieting first).
+__device__ __forceinline__ float max_f32(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float col_max4(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    u = __float_as_uint(x);
+    auto r2 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return max_f32(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    u = __float_as_uint(x);
+    auto r2 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+
+// Two fp32 weights -> fp16 hi parts (round to nearest even, one v_cvt_pk_f16_f32) and lo parts
+// f16(w - f32(hi)), each one mixed-precision FMA (v_fma_mix{lo,hi}_f16: w * 1 - hi in fp32, rounded
+// once to fp16; w - hi is exact in fp32, so this equals the plain conversion sequence bit for bit).
+__device__ __forceinline__ void split_hi_lo(float w0, float w1, uint32_t& hi, uint32_t& lo) {
+    const half2_t h = {(_Float16)w0, (_Float16)w1};
+    hi = __builtin_bit_cast(uint32_t, h);
+    // mixlo leaves the high half as it was; mixhi then writes it
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(lo) : "v"(w0), "v"(hi));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo) : "v"(w1), "v"(hi));
 }
 
 }  // namespace kvq

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         if constexpr (F8Q) qk_f[nb] *= quantize_q_row_fp8(qB[nb], q8[nb]);
     }
 
-    float m_run[NB], l_lane[NB];  // per block: running max (base-2 logits) and this lane's weights
+    float m_run[NB], l_lane[NB];  // per block: reference max (base-2 logits) and this lane's weights
     float4_t acc[NB][8];          // O^T row blocks: dims 16 r + 4 q4 .. +3 of the block's column
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -127,52 +127,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
     const uint32_t v_off = (uint32_t)col * kBlock + 4u * (uint32_t)q4;  // dim col (+16 r), tokens 4 q4
 
     // Block ids in groups of 64 tiles, one per lane: ids_cur for group grp, ids_nxt for grp + 1 (loaded
-    // a group ahead, so a prefetch never waits for the table).
+    // a group ahead, so a load never waits for the table).  Every tile a load touches lies in one of
+    // the two groups: K runs two chunks ahead of the softmax, V one.
     auto load_ids = [&](int group) {
         const int t = group * 64 + lane;
         return t < tile_end ? bt[t] : 0;
     };
     int grp = 0;
     int ids_cur = load_ids(0), ids_nxt = load_ids(1);
-    // Codes of a chunk (two tiles); tiles at or past tile_end are zeros.
-    struct Chunk {
-        u32x4 ka[TW], kb[TW];
-        uint32_t vd[TW][8];
-        float4_t ks4[TW], vs4[TW];
+    auto block_of = [&](int t) {
+        return (t >> 6) == grp ? __builtin_amdgcn_readlane(ids_cur, t & 63)
+                               : __builtin_amdgcn_readlane(ids_nxt, t & 63);
     };
-    auto load_chunk = [&](Chunk& ch, int t0) {
-#pragma unroll
-        for (int i = 0; i < TW; ++i) {
-            const int t = t0 + i;
-            if (t < tile_end) {
-                const int blk = (t >> 6) == grp ? __builtin_amdgcn_readlane(ids_cur, t & 63)
-                                                : __builtin_amdgcn_readlane(ids_nxt, t & 63);
-                const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
-                const uint8_t* kt = a.kc + tile;
-                const uint8_t* vt = a.vc + tile;
-                ch.ka[i] = ldg16(kt + k_off);
-                ch.kb[i] = ldg16(kt + k_off + 1024u);
-#pragma unroll
-                for (int r = 0; r < 8; ++r) ch.vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
-                if constexpr (DT == KVQ_INT8) {
-                    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
-                    ch.ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
-                    ch.vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-                }
-            } else {
-                ch.ka[i] = u32x4{0u, 0u, 0u, 0u};
-                ch.kb[i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int r = 0; r < 8; ++r) ch.vd[i][r] = 0u;
-                if constexpr (DT == KVQ_INT8) {
-                    ch.ks4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                    ch.vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                }
-            }
-        }
-    };
-
-    // the next prefetch reads tile t: keep its group in the two id registers
+    // the next K load reads tile t: keep its group in the two id registers
     auto ids_for = [&](int t) {
         if ((t >> 6) > grp + 1) {
             ++grp;
@@ -181,152 +148,223 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         }
     };
 
-    auto compute_chunk = [&](Chunk& ch, int t0) {
-        {
-            const int tok_base = t0 * kBlock;  // first token of the chunk
-            u32x4 (&ka)[TW] = ch.ka;
-            u32x4 (&kb)[TW] = ch.kb;
-            uint32_t (&vd)[TW][8] = ch.vd;
-            float4_t (&ks4)[TW] = ch.ks4;
-            float4_t (&vs4)[TW] = ch.vs4;
-            // logits S^T for every block from the K operands decoded once
-            float z[NB][TW][4];
-            const bool all_visible = tok_base + TW * kBlock - 1 <= pos_min;  // wave-uniform
+    // Software pipeline over chunks of TW tiles, three stages kept in flight: the K codes of chunk
+    // c + 2 are loading, the S^T MFMAs of chunk c + 1 are issued, and chunk c's softmax and P V^T run
+    // -- so the VALU work of one chunk overlaps the matrix cores' work on the next.  Two buffers of
+    // each kind, swapped by unrolling the loop by two.  Tiles at or past tile_end are zeros.
+    struct KBuf { u32x4 ka[TW], kb[TW]; };
+    struct VBuf { uint32_t vd[TW][8]; float4_t ks4[TW], vs4[TW]; };
+    struct SBuf { float4_t s[NB][TW]; };
+    auto load_k = [&](KBuf& kb_, int t0) {
 #pragma unroll
-            for (int i = 0; i < TW; ++i) {
-                const int tok0 = tok_base + i * kBlock + 4 * q4;
-                float4_t sacc[NB];
-                if constexpr (F8Q) {
-                    const i32x8 k8 = k_fp8x32(ka[i], kb[i]);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        sacc[nb] = mfma_qk_fp8<DT>(k8, q8[nb], float4_t{0.0f, 0.0f, 0.0f, 0.0f});
-                } else {
-                    const half8_v k0 = codes8<DT>(ka[i].x, ka[i].y), k1 = codes8<DT>(ka[i].z, ka[i].w);
-                    const half8_v k2 = codes8<DT>(kb[i].x, kb[i].y), k3 = codes8<DT>(kb[i].z, kb[i].w);
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        sacc[nb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qB[nb][0], sacc[nb], 0, 0, 0);
-                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qB[nb][1], sacc[nb], 0, 0, 0);
-                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k2, qB[nb][2], sacc[nb], 0, 0, 0);
-                        sacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k3, qB[nb][3], sacc[nb], 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        float f = qk_f[nb];
-                        if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
-                        z[nb][i][t] = sacc[nb][t] * f;
-                        // a token past the column's own position is masked
-                        if (!all_visible && tok0 + t > pos[nb]) z[nb][i][t] = kNegInf;
-                    }
-                }
+        for (int i = 0; i < TW; ++i) {
+            const int t = t0 + i;
+            if (t < tile_end) {
+                const uint8_t* kt = a.kc + ((size_t)block_of(t) * a.Hkv + g) * kTileBytes;
+                kb_.ka[i] = ldg16(kt + k_off);
+                kb_.kb[i] = ldg16(kt + k_off + 1024u);
+            } else {
+                kb_.ka[i] = u32x4{0u, 0u, 0u, 0u};
+                kb_.kb[i] = u32x4{0u, 0u, 0u, 0u};
             }
-            // per block: max over the column's tokens (the four row groups of the column).  Every
-            // column sees token 0, which the first chunk holds, so the running max is finite from
-            // then on.
-            float m_new[NB];
-            bool moved = false;
+        }
+    };
+    auto load_v = [&](VBuf& vb, int t0) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                float cmax = kNegInf;
+        for (int i = 0; i < TW; ++i) {
+            const int t = t0 + i;
+            if (t < tile_end) {
+                const int blk = block_of(t);
+                const uint8_t* vt = a.vc + ((size_t)blk * a.Hkv + g) * kTileBytes;
 #pragma unroll
-                for (int i = 0; i < TW; ++i)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) cmax = fmaxf(cmax, z[nb][i][t]);
-                cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-                cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-                m_new[nb] = fmaxf(m_run[nb], cmax);
-                moved |= m_new[nb] > m_run[nb];
-            }
-            if (__builtin_amdgcn_ballot_w64(moved)) {  // rescale only when some running max moved
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_new[nb]);
-                    l_lane[nb] *= alpha;
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) acc[nb][r] *= alpha;
+                for (int r = 0; r < 8; ++r) vb.vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
+                if constexpr (DT == KVQ_INT8) {
+                    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
+                    vb.ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+                    vb.vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
                 }
-            }
+            } else {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) m_run[nb] = m_new[nb];
-
-            // weights of the tile pair, hi and lo fp16 parts, in the B layout, per block
-            half8_v whi[NB], wlo[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float pw = __builtin_amdgcn_exp2f(z[nb][u][t] - m_new[nb]);
-                        l_lane[nb] += pw;
-                        float w = pw;
-                        if constexpr (DT == KVQ_INT8) w = (pw > 0.0f) ? pw * vs4[u][t] : 0.0f;
-                        const _Float16 hi = (_Float16)w;
-                        whi[nb][4 * u + t] = hi;
-                        wlo[nb][4 * u + t] = (_Float16)(w - (float)hi);
-                    }
-                }
-            }
-            // V codes of the slots at and past t_end are zeroed (past the context they may hold NaN
-            // codes; a zero weight alone would still give 0 * NaN); chunks inside it need nothing
-            if (tok_base + TW * kBlock > t_end) {
-                const int valid0 = t_end - tok_base - 4 * q4;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    vd[0][r] = keep_bytes(vd[0][r], valid0);
-                    vd[1][r] = keep_bytes(vd[1][r], valid0 - kBlock);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const half8_v va8 = join8(codes_to_f16<DT, 0>(vd[0][r]), codes_to_f16<DT, 1>(vd[0][r]),
-                                          codes_to_f16<DT, 0>(vd[1][r]), codes_to_f16<DT, 1>(vd[1][r]));
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi[nb], acc[nb][r], 0, 0, 0);
-                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, wlo[nb], acc[nb][r], 0, 0, 0);
+                for (int r = 0; r < 8; ++r) vb.vd[i][r] = 0u;
+                if constexpr (DT == KVQ_INT8) {
+                    vb.ks4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    vb.vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 }
             }
         }
     };
 
+    // S^T of a chunk for every block, from the K operands decoded once (FP8 math: used as loaded)
+    auto scores = [&](const KBuf& kb_, SBuf& sb) {
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            if constexpr (F8Q) {
+                const i32x8 k8 = k_fp8x32(kb_.ka[i], kb_.kb[i]);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    sb.s[nb][i] = mfma_qk_fp8<DT>(k8, q8[nb], float4_t{0.0f, 0.0f, 0.0f, 0.0f});
+            } else {
+                const half8_v k0 = codes8<DT>(kb_.ka[i].x, kb_.ka[i].y), k1 = codes8<DT>(kb_.ka[i].z, kb_.ka[i].w);
+                const half8_v k2 = codes8<DT>(kb_.kb[i].x, kb_.kb[i].y), k3 = codes8<DT>(kb_.kb[i].z, kb_.kb[i].w);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    float4_t c = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qB[nb][0], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qB[nb][1], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(k2, qB[nb][2], c, 0, 0, 0);
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(k3, qB[nb][3], c, 0, 0, 0);
+                    sb.s[nb][i] = c;
+                }
+            }
+        }
+    };
+
+    // Softmax of a chunk and its P V^T.  The reference max of a column moves only when a logit
+    // exceeds it by more than kSlack (base 2): weights stay below 2^kSlack, and the rescale of the
+    // accumulators (a branch every lane skips together) becomes rare after the first chunks.
+    constexpr float kSlack = 8.0f;
+    auto softmax_pv = [&](VBuf& vb, const SBuf& sb, int t0) {
+        const int tok_base = t0 * kBlock;  // first token of the chunk
+        float z[NB][TW][4];
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    float f = qk_f[nb];
+                    if constexpr (DT == KVQ_INT8) f *= vb.ks4[i][t];
+                    z[nb][i][t] = sb.s[nb][i][t] * f;
+                }
+        // The causal mask: a token past the column's own position gets -inf.  Only the chunks that
+        // reach past the wave's first row need it (wave-uniform test).
+        if (tok_base + TW * kBlock - 1 > pos_min) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int lim = pos[nb] - (tok_base + 4 * q4);  // last visible offset in the chunk
+#pragma unroll
+                for (int i = 0; i < TW; ++i)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (i * kBlock + t > lim) z[nb][i][t] = kNegInf;
+            }
+        }
+        // Every column sees token 0, which the first chunk holds, so the reference max is finite
+        // from then on.
+        bool moved = false;
+        bool up[NB];
+        float cmax[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float m = kNegInf;
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) m = fmaxf(m, z[nb][i][t]);
+            cmax[nb] = col_max4(m);
+            up[nb] = cmax[nb] > m_run[nb] + kSlack;  // m_run = -inf: any finite max
+            moved |= up[nb];
+        }
+        if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const float alpha = up[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - cmax[nb]) : 1.0f;
+                l_lane[nb] *= alpha;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[nb][r] *= alpha;
+                if (up[nb]) m_run[nb] = cmax[nb];
+            }
+        }
+
+        // weights of the tile pair, hi and lo fp16 parts, in the B layout, per block
+        half8_v whi[NB], wlo[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float w[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float pw = __builtin_amdgcn_exp2f(z[nb][u][t] - m_run[nb]);
+                    l_lane[nb] += pw;
+                    w[t] = pw;
+                    if constexpr (DT == KVQ_INT8) w[t] = (pw > 0.0f) ? pw * vb.vs4[u][t] : 0.0f;
+                }
+                split_hi_lo(w[0], w[1], h[2 * u], l[2 * u]);
+                split_hi_lo(w[2], w[3], h[2 * u + 1], l[2 * u + 1]);
+            }
+            whi[nb] = __builtin_bit_cast(half8_v, u32x4{h[0], h[1], h[2], h[3]});
+            wlo[nb] = __builtin_bit_cast(half8_v, u32x4{l[0], l[1], l[2], l[3]});
+        }
+        // V codes of the slots at and past t_end are zeroed (past the context they may hold NaN
+        // codes; a zero weight alone would still give 0 * NaN); chunks inside it need nothing
+        if (tok_base + TW * kBlock > t_end) {
+            const int valid0 = t_end - tok_base - 4 * q4;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                vb.vd[0][r] = keep_bytes(vb.vd[0][r], valid0);
+                vb.vd[1][r] = keep_bytes(vb.vd[1][r], valid0 - kBlock);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const half8_v va8 = join8(codes_to_f16<DT, 0>(vb.vd[0][r]), codes_to_f16<DT, 1>(vb.vd[0][r]),
+                                      codes_to_f16<DT, 0>(vb.vd[1][r]), codes_to_f16<DT, 1>(vb.vd[1][r]));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi[nb], acc[nb][r], 0, 0, 0);
+                acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, wlo[nb], acc[nb][r], 0, 0, 0);
+            }
+        }
+    };
+
+    // One pipeline step for chunk c = t0 / TW: K loads of chunk c + 2 into kc_ (free: its chunk's
+    // S^T was issued one step ago), V loads of chunk c + 1 into vn, S^T of chunk c + 1 from kn into
+    // sn, then chunk c's softmax and P V^T from vc_ and sc.
+    auto step = [&](KBuf& kc_, KBuf& kn, VBuf& vc_, VBuf& vn, SBuf& sc, SBuf& sn, int t0) {
+        if (t0 + 2 * TW < tile_end) {
+            ids_for(t0 + 3 * TW - 1);
+            load_k(kc_, t0 + 2 * TW);
+        }
+        if (t0 + TW < tile_end) {
+            load_v(vn, t0 + TW);
+            scores(kn, sn);
+        }
+        softmax_pv(vc_, sc, t0);
+    };
+
     if constexpr (DT == KVQ_INT8) {
         // the per-token scales do not fit in registers twice: one chunk at a time
-        Chunk A;
+        KBuf K;
+        VBuf V;
+        SBuf S;
         for (int t0 = 0; t0 < tile_end; t0 += TW) {
-            load_chunk(A, t0);
-            ids_for(t0 + TW);
-            compute_chunk(A, t0);
+            ids_for(t0 + TW - 1);
+            load_k(K, t0);
+            load_v(V, t0);
+            scores(K, S);
+            softmax_pv(V, S, t0);
         }
     } else {
-        // Software pipeline, unrolled by two so the buffers swap roles without a register copy:
-        // the loads of the next chunk are in flight while the current one is computed.
-        Chunk A, B;
-        load_chunk(A, 0);
+        KBuf KA, KB;
+        VBuf VA, VB;
+        SBuf SA, SB;
+        ids_for(2 * TW - 1);
+        load_k(KA, 0);
+        load_v(VA, 0);
+        if (TW < tile_end) load_k(KB, TW);
+        scores(KA, SA);
         for (int t0 = 0; t0 < tile_end; t0 += 2 * TW) {
-            if (t0 + TW < tile_end) {
-                load_chunk(B, t0 + TW);
-                ids_for(t0 + 2 * TW);
-            }
-            compute_chunk(A, t0);
+            step(KA, KB, VA, VB, SA, SB, t0);
             if (t0 + TW >= tile_end) break;
-            if (t0 + 2 * TW < tile_end) {
-                load_chunk(A, t0 + 2 * TW);
-                ids_for(t0 + 3 * TW);
-            }
-            compute_chunk(B, t0 + TW);
+            step(KB, KA, VB, VA, SB, SA, t0 + TW);
         }
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         // sum of the column's weights over the four row groups
-        float l_sum = l_lane[nb] + __shfl_xor(l_lane[nb], 16);
-        l_sum += __shfl_xor(l_sum, 32);
+        const float l_sum = col_sum4(l_lane[nb]);
         if (live[nb]) {
             const float inv = a.v_scale / l_sum;
 #pragma unroll
