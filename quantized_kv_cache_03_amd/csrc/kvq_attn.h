@@ -19,6 +19,13 @@ namespace kvq {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// Lazy rescale of the online softmax: a running (reference) max moves only when a logit exceeds it
+// by more than this many binades, so the weights exp2(z - m) stay below 2^kRescaleSlack and the
+// rescale of the accumulators becomes rare after the first chunks.  Every sum (weights, outputs,
+// and the split-K partials with their m) shares the reference, so the result is unchanged up to
+// rounding.
+constexpr float kRescaleSlack = 8.0f;
+
 // Keep the low `nbytes` (0..4) bytes of w.
 __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int nbytes) {
     return nbytes >= 4 ? w : (nbytes <= 0 ? 0u : (w & ((1u << (8 * nbytes)) - 1u)));

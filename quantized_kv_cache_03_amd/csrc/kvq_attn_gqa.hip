@@ -212,33 +212,38 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
                     cmax = fmaxf(cmax, z[i][t]);
                 }
             }
-            // max over the head's tokens: the four row groups of the column
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-            const float m_new = fmaxf(m_run, cmax);  // finite: every chunk holds a valid token
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_lane *= alpha;
+            // max over the head's tokens (the four row groups of the column); finite: every chunk
+            // holds a valid token.  Lazy rescale (kRescaleSlack), a branch every lane takes or
+            // skips together.
+            cmax = col_max4(cmax);
+            const bool up = cmax > m_run + kRescaleSlack;  // m_run = -inf: any finite max
+            if (__builtin_amdgcn_ballot_w64(up)) {
+                const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
+                if (up) m_run = cmax;
+                l_lane *= alpha;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+                for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+            }
 
 #pragma unroll
             for (int i = 0; i < TW; i += 2) {
                 // weights of the tile pair (i, i+1), hi and lo fp16 parts, in the B layout
-                half8_v whi, wlo;
+                uint32_t h[4], l[4];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
+                    float w[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
-                        const float pw = __builtin_amdgcn_exp2f(z[i + u][t] - m_new);
+                        const float pw = __builtin_amdgcn_exp2f(z[i + u][t] - m_run);
                         l_lane += pw;
-                        float w = pw;
-                        if constexpr (DT == KVQ_INT8) w = (pw > 0.0f) ? pw * vs4[i + u][t] : 0.0f;
-                        const _Float16 hi = (_Float16)w;
-                        whi[4 * u + t] = hi;
-                        wlo[4 * u + t] = (_Float16)(w - (float)hi);
+                        w[t] = pw;
+                        if constexpr (DT == KVQ_INT8) w[t] = (pw > 0.0f) ? pw * vs4[i + u][t] : 0.0f;
                     }
+                    split_hi_lo(w[0], w[1], h[2 * u], l[2 * u]);
+                    split_hi_lo(w[2], w[3], h[2 * u + 1], l[2 * u + 1]);
                 }
+                const half8_v whi = __builtin_bit_cast(half8_v, u32x4{h[0], h[1], h[2], h[3]});
+                const half8_v wlo = __builtin_bit_cast(half8_v, u32x4{l[0], l[1], l[2], l[3]});
                 // V codes of the slots past the end are zeroed (they may hold NaN codes)
                 uint32_t v0[8], v1[8];
                 const int valid0 = t_end - (tb + c0 + i) * kBlock - 4 * q4;
@@ -259,8 +264,7 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
         }
     }
     // sum of the head's weights over the four row groups
-    float l_sum = l_lane + __shfl_xor(l_lane, 16);
-    l_sum += __shfl_xor(l_sum, 32);
+    const float l_sum = col_sum4(l_lane);
 
     if (col < G) {
         if (lo == 0 && hi == nt) {

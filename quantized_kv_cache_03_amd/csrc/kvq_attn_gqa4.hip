@@ -108,42 +108,56 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTil
             cmax = fmaxf(cmax, z[i][u]);
         }
     }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);  // finite: every chunk holds a valid token
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_lane *= alpha;
-    z_lane *= alpha;
+    // Lazy rescale (kRescaleSlack), a branch every lane takes or skips together.  Every chunk holds
+    // a valid token, so cmax is finite.
+    cmax = col_max4(cmax);
+    const bool up = cmax > m_run + kRescaleSlack;  // m_run = -inf: any finite max
+    if (__builtin_amdgcn_ballot_w64(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
+        if (up) m_run = cmax;
+        l_lane *= alpha;
+        z_lane *= alpha;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        acc_e[r] *= alpha;
-        acc_o[r] *= alpha;
-    }
-    // P^T operands: the even tokens (0, 2) and the odd tokens (1, 3) of this lane's quad of each
-    // tile, as fp16 hi and lo parts of w = p s_v
-    half8_v we_hi, we_lo, wo_hi, wo_lo;
-#pragma unroll
-    for (int i = 0; i < kTiles4; ++i) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_new);
-            l_lane += pw;
-            const bool live = pw > 0.0f;  // masked slots may hold NaN scales
-            const float w = live ? pw * t[i].vs[u] : 0.0f;
-            z_lane += live ? pw * t[i].vz[u] : 0.0f;
-            const _Float16 hi = (_Float16)w;
-            const _Float16 lo = (_Float16)(w - (float)hi);
-            const int k = 2 * i + (u >> 1);  // slot: tile i, token u of the pair (0, 2) or (1, 3)
-            if (u & 1) {
-                wo_hi[k] = hi;
-                wo_lo[k] = lo;
-            } else {
-                we_hi[k] = hi;
-                we_lo[k] = lo;
-            }
+        for (int r = 0; r < 8; ++r) {
+            acc_e[r] *= alpha;
+            acc_o[r] *= alpha;
         }
     }
+    // The V parameters of the slots at and past t_end are zeroed (past the context they may be
+    // NaN, and a zero weight alone would still give 0 * NaN); only a tile that reaches past the
+    // end has such slots (wave-uniform test).
+#pragma unroll
+    for (int i = 0; i < kTiles4; ++i) {
+        if ((tile0 + i + 1) * kBlock > t_end) {
+            const int pos0 = (tile0 + i) * kBlock + 4 * q4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (pos0 + u >= t_end) {
+                    t[i].vs[u] = 0.0f;
+                    t[i].vz[u] = 0.0f;
+                }
+        }
+    }
+    // P^T operands: the even tokens (0, 2) and the odd tokens (1, 3) of this lane's quad of each
+    // tile, as fp16 hi and lo parts of w = p s_v (dword i of an operand: tile i's pair)
+    uint32_t ehi[kTiles4], elo[kTiles4], ohi[kTiles4], olo[kTiles4];
+#pragma unroll
+    for (int i = 0; i < kTiles4; ++i) {
+        float w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_run);
+            l_lane += pw;
+            w[u] = pw * t[i].vs[u];
+            z_lane = __builtin_fmaf(pw, t[i].vz[u], z_lane);
+        }
+        split_hi_lo(w[0], w[2], ehi[i], elo[i]);
+        split_hi_lo(w[1], w[3], ohi[i], olo[i]);
+    }
+    const half8_v we_hi = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
+    const half8_v we_lo = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
+    const half8_v wo_hi = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
+    const half8_v wo_lo = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
     // O^T += V^T P^T, row block r = dims 16 r .. +15
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -267,10 +281,8 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
         }
     }
     // the head's weight sum and zero-point sum over the four row groups
-    float l_sum = l_lane + __shfl_xor(l_lane, 16);
-    l_sum += __shfl_xor(l_sum, 32);
-    float z_sum = z_lane + __shfl_xor(z_lane, 16);
-    z_sum += __shfl_xor(z_sum, 32);
+    const float l_sum = col_sum4(l_lane);
+    const float z_sum = col_sum4(z_lane);
 
     if (col < G) {
         float4_t o[8];

@@ -111,27 +111,30 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
         cmax = fmaxf(cmax, z[i]);
     }
     cmax = max_across_quads(cmax);  // a chunk always holds at least one valid token
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    if (cmax > m_run + kRescaleSlack) {  // lazy rescale; one head per wave, so wave-uniform
+        const float alpha = __builtin_amdgcn_exp2f(m_run - cmax);
+        m_run = cmax;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        acc[r].e *= alpha;
-        acc[r].o *= alpha;
+        for (int r = 0; r < 8; ++r) {
+            acc[r].e *= alpha;
+            acc[r].o *= alpha;
+        }
+        l_lane *= alpha;
+        z_lane *= alpha;
     }
-    l_lane *= alpha;
-    z_lane *= alpha;
 
     // half index of token tk: quad tk / 4, then (t0, t2, t1, t3) for hi and again for lo
     const int slot = 8 * (tk >> 2) + (((tk & 1) << 1) | ((tk >> 1) & 1));
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const float pw = __builtin_amdgcn_exp2f(z[i] - m_new);
+        const float pw = __builtin_amdgcn_exp2f(z[i] - m_run);
         l_lane += pw;
-        // masked slots may hold NaN scales: keep their weight exactly 0
-        const bool live = pw > 0.0f;
-        const float w = live ? pw * t[i].vs.x : 0.0f;
-        z_lane += live ? pw * t[i].vs.y : 0.0f;
+        float vs = t[i].vs.x, vz = t[i].vs.y;
+        if constexpr (MASKED) {  // slots past the end may hold NaN scales: their weight is exactly 0
+            if ((tile0 + i) * kBlock + tk >= t_end) vs = vz = 0.0f;
+        }
+        const float w = pw * vs;
+        z_lane = __builtin_fmaf(pw, vz, z_lane);
         if ((lane & 3) == 0) {
             const _Float16 h = (_Float16)w;
             lds[i * 32 + slot] = __builtin_bit_cast(uint16_t, h);

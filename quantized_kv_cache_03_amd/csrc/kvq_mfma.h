@@ -24,20 +24,16 @@ __device__ __forceinline__ half8_v codes8(uint32_t w0, uint32_t w1) {
 // Max and sum over the four lanes of a column (l, l ^ 16, l ^ 32, l ^ 48), every lane getting the
 // result.  v_permlane16_swap / v_permlane32_swap of (x, x) leave the two rows (halves) of each pair
 // in the two results, so one VALU operation per step replaces an LDS permute; each lane of a pair
-// combines the same two values in the same order, so the results agree bitwise.  The max is one
-// v_max_f32 (the callers' logits are never NaN, so no operand needs quieting first).
-__device__ __forceinline__ float max_f32(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
+// combines the same two values in the same order, so the results agree bitwise.  (No inline
+// assembly here or below: the compiler's hazard recognizer does not see the registers an asm
+// statement writes, and a matrix instruction reading them too early takes stale values.)
 __device__ __forceinline__ float col_max4(float x) {
     uint32_t u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
     u = __float_as_uint(x);
     auto r2 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return max_f32(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+    return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
 }
 __device__ __forceinline__ float col_sum4(float x) {
     uint32_t u = __float_as_uint(x);
@@ -48,15 +44,13 @@ __device__ __forceinline__ float col_sum4(float x) {
     return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
-// Two fp32 weights -> fp16 hi parts (round to nearest even, one v_cvt_pk_f16_f32) and lo parts
-// f16(w - f32(hi)), each one mixed-precision FMA (v_fma_mix{lo,hi}_f16: w * 1 - hi in fp32, rounded
-// once to fp16; w - hi is exact in fp32, so this equals the plain conversion sequence bit for bit).
+// Two fp32 weights -> packed fp16 hi parts (round to nearest even) and lo parts f16(w - f32(hi))
+// (w - hi is exact in fp32): one packed conversion each, the pair's values side by side.
 __device__ __forceinline__ void split_hi_lo(float w0, float w1, uint32_t& hi, uint32_t& lo) {
     const half2_t h = {(_Float16)w0, (_Float16)w1};
+    const half2_t l = {(_Float16)(w0 - (float)h.x), (_Float16)(w1 - (float)h.y)};
     hi = __builtin_bit_cast(uint32_t, h);
-    // mixlo leaves the high half as it was; mixhi then writes it
-    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(lo) : "v"(w0), "v"(hi));
-    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(lo) : "v"(w1), "v"(hi));
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 }  // namespace kvq

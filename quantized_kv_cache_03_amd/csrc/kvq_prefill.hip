@@ -219,10 +219,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         }
     };
 
-    // Softmax of a chunk and its P V^T.  The reference max of a column moves only when a logit
-    // exceeds it by more than kSlack (base 2): weights stay below 2^kSlack, and the rescale of the
-    // accumulators (a branch every lane skips together) becomes rare after the first chunks.
-    constexpr float kSlack = 8.0f;
+    // Softmax of a chunk and its P V^T, with the lazy rescale (kRescaleSlack; a branch every lane
+    // takes or skips together).
     auto softmax_pv = [&](VBuf& vb, const SBuf& sb, int t0) {
         const int tok_base = t0 * kBlock;  // first token of the chunk
         float z[NB][TW][4];
@@ -262,7 +260,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
 #pragma unroll
                 for (int t = 0; t < 4; ++t) m = fmaxf(m, z[nb][i][t]);
             cmax[nb] = col_max4(m);
-            up[nb] = cmax[nb] > m_run[nb] + kSlack;  // m_run = -inf: any finite max
+            up[nb] = cmax[nb] > m_run[nb] + kRescaleSlack;  // m_run = -inf: any finite max
             moved |= up[nb];
         }
         if (__builtin_amdgcn_ballot_w64(moved)) {
