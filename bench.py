@@ -80,6 +80,53 @@ def load_traffic(workload: str, digest: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def read_ceiling(mib: int = 2048, waves: int = 2048, iters: int = 10):
+    """The HBM read rate a plain read kernel reaches on this GPU (libkvq_probe.so): 2 KiB tiles
+    streamed by `waves` waves in sequential order and in a shuffled order (as a shuffled block
+    table lays the tiles out), over `mib` MiB, far past the last-level cache.  None if the probe
+    library is missing."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "quantized_kv_cache_03_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.kvq_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvq_probe_read_tiles.restype = ctypes.c_int
+    n = (mib << 20) // 2048
+    buf = torch.empty(n * 2048, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {"kernel": "kvq_probe_read_tiles (quantized_kv_cache_03_amd/probe/read_probe.hip)",
+           "bytes_per_pass": n * 2048, "waves": waves, "tile_bytes": 2048}
+    orders = {"sequential": np.arange(n, dtype=np.int32),
+              "shuffled": np.random.default_rng(0).permutation(n).astype(np.int32)}
+    for name, order in orders.items():
+        o = torch.from_numpy(order).cuda()
+
+        def call():
+            rc = lib.kvq_probe_read_tiles(buf.data_ptr(), o.data_ptr(), n, waves, sink.data_ptr(),
+                                          stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"kvq_probe_read_tiles failed ({rc})")
+        for _ in range(2):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[f"{name}_gbs"] = round(n * 2048 * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -379,6 +426,7 @@ def main():
     achieved = attn_bytes / (main_avg_ms * 1e-3) / 1e9
     digest = kernel_source_digest(w)
     traffic = load_traffic(w.name, digest)
+    ceiling = read_ceiling()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -441,6 +489,11 @@ def main():
             "algorithmic_bytes_per_launch": attn_bytes,
             "kernel_source_digest": digest,
         },
+        # a plain read kernel's rate on this GPU, beside the nominal peak (the kernel's achieved
+        # rate as a fraction of it: the table order matching the workload's)
+        "read_ceiling": ceiling,
+        "frac_of_read_ceiling": (None if not ceiling else round(
+            achieved / ceiling["shuffled_gbs" if w.table == "shuffled" else "sequential_gbs"], 4)),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -8,6 +8,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
+# the HBM read-rate probe the benchmark reports beside the roofline (not part of the cache's ABI)
+PROBE_SRC = os.path.join(HERE, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only.  Packed fp32 instructions are switched off for every kernel; fp32 division stays
@@ -22,11 +25,12 @@ def sources():
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra_flags, *sources(), "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    for srcs, out in ((sources(), LIB), ([PROBE_SRC], PROBE_LIB)):
+        cmd = [HIPCC, *FLAGS, *extra_flags, *srcs, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(out + ".tmp", out)
     return LIB
 
 

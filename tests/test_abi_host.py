@@ -212,3 +212,20 @@ def test_quantize_q_fp8_argument_errors(K):
     assert L.kvq_quantize_q_fp8(None, 4, 0x20, 0x30, None) == K.ERR_ARG
     assert L.kvq_quantize_q_fp8(0x10, 4, 0x20, None, None) == K.ERR_ARG
     assert L.kvq_quantize_q_fp8(None, 0, None, None, None) == K.OK
+
+
+def test_read_probe_library_rejects_bad_arguments():
+    """The benchmark's read-rate probe (libkvq_probe.so, built beside libkvq.so) validates its
+    arguments on the host before any launch."""
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "quantized_kv_cache_03_amd", "libkvq_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.kvq_probe_read_tiles
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 0x10, 4, 8, 0x20, None) == -1
+    assert f(0x10, 0x10, 0, 8, 0x20, None) == -1
+    assert f(0x10, 0x10, 4, 0, 0x20, None) == -1
+    assert f(0x10, None, 4, 8, 0x20, None) == -1
