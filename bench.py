@@ -189,13 +189,23 @@ def cpu_baseline(w, threads: int, budget_s: float, scale: float):
     bytes_ = (int(ctx.sum()) * w.num_kv_heads * per_tok + 2 * len(seqs) * w.num_q_heads * 128 * 2
               + 4 * int(((ctx + 15) // 16).sum()) + 4 * len(seqs))
     step_s = (t2 - t1) / reps
+    # the same step on one thread, for the first sequence alone (a few seconds at most)
+    b0 = cu[1] - 1
+    t3 = time.perf_counter()
+    oracle.append(cache, k[b0:b0 + 1], v[b0:b0 + 1], bt[:1], ctx[:1])
+    oracle.decode_attn(cache, q[:1], bt[:1], ctx[:1], threads=1, fp8_math=w.fp8_math)
+    one_s = time.perf_counter() - t3
+    one_bytes = (int(ctx[0]) * w.num_kv_heads * per_tok + 2 * w.num_q_heads * 128 * 2
+                 + 4 * int((ctx[0] + 15) // 16) + 4)
     return {"value": bytes_ / step_s / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": f"first {len(seqs)} of {len(ctx_all)} sequences (sum ctx {int(ctx.sum())}), "
                       f"all {w.num_q_heads} heads: one append + fp64 attention, {reps} repetitions "
                       f"in {t2 - t1:.1f} s ({step_s:.3f} s each); prefill of the sample not timed "
                       f"({t1 - t0:.1f} s)",
-            "tokens_per_s": len(seqs) / step_s}
+            "tokens_per_s": len(seqs) / step_s,
+            "single_thread": {"value": one_bytes / one_s / 1e9, "unit": "GB/s",
+                              "sample": f"sequence 0 ({int(ctx[0])} tokens), all heads, one step"}}
 
 
 PREFILL_METRIC = "prefill attention over the 8-bit paged cache: achieved TFLOP/s (% of fp16 MFMA peak)"
