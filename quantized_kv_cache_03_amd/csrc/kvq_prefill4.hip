@@ -163,9 +163,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 }
             }
             const int tok_base = (tb + c0) * kBlock;
-            const bool all_visible = tok_base + kTilesP4 * kBlock - 1 <= pos_min;  // wave-uniform
             float z[kTilesP4][4];
-            float cmax = kNegInf;
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
                 half8_v kop[4];
@@ -173,46 +171,66 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int m = 0; m < 4; ++m) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[m], qB[m], s, 0, 0, 0);
-                const int tok0 = tok_base + i * kBlock + 4 * q4;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float zz = qk24 * (s[u] * t[i].ks[u]) + a.qk_scale * (t[i].kz[u] * qsum);
-                    z[i][u] = (all_visible || tok0 + u <= pos) ? zz : kNegInf;
-                    cmax = fmaxf(cmax, z[i][u]);
-                }
+                for (int u = 0; u < 4; ++u)
+                    z[i][u] = qk24 * (s[u] * t[i].ks[u]) + a.qk_scale * (t[i].kz[u] * qsum);
             }
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-            const float m_new = fmaxf(m_run, cmax);  // finite: the first chunk holds token 0
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_lane *= alpha;
-            z_lane *= alpha;
+            // The causal mask, only for the chunks that reach past the wave's first row
+            // (wave-uniform test); and the V parameters of slots past the context are zeroed (they
+            // may be NaN, and a zero weight alone would still give 0 * NaN), only in the chunk
+            // that reaches past it.
+            if (tok_base + kTilesP4 * kBlock - 1 > pos_min) {
+                const int lim = pos - (tok_base + 4 * q4);  // last visible offset in the chunk
 #pragma unroll
-            for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+                for (int i = 0; i < kTilesP4; ++i)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (i * kBlock + u > lim) z[i][u] = kNegInf;
+            }
+            if (tok_base + kTilesP4 * kBlock > n) {
+#pragma unroll
+                for (int i = 0; i < kTilesP4; ++i)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (tok_base + i * kBlock + 4 * q4 + u >= n) t[i].vs[u] = t[i].vz[u] = 0.0f;
+            }
+            float cmax = kNegInf;
+#pragma unroll
+            for (int i = 0; i < kTilesP4; ++i)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) cmax = fmaxf(cmax, z[i][u]);
+            // finite: the first chunk holds token 0.  Lazy rescale (kRescaleSlack), a branch every
+            // lane takes or skips together.
+            cmax = col_max4(cmax);
+            const bool up = cmax > m_run + kRescaleSlack;  // m_run = -inf: any finite max
+            if (__builtin_amdgcn_ballot_w64(up)) {
+                const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
+                if (up) m_run = cmax;
+                l_lane *= alpha;
+                z_lane *= alpha;
+#pragma unroll
+                for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+            }
             // P^T operands: tokens (0, 2) and (1, 3) of this lane's quad of each tile, w = p s_v
-            half8_v we_hi, we_lo, wo_hi, wo_lo;
+            // (dword i of an operand: tile i's pair)
+            uint32_t ehi[kTilesP4], elo[kTilesP4], ohi[kTilesP4], olo[kTilesP4];
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
+                float w[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_new);
+                    const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_run);
                     l_lane += pw;
-                    const bool on = pw > 0.0f;  // masked slots may hold NaN scales
-                    const float w = on ? pw * t[i].vs[u] : 0.0f;
-                    z_lane += on ? pw * t[i].vz[u] : 0.0f;
-                    const _Float16 hi = (_Float16)w;
-                    const _Float16 lo = (_Float16)(w - (float)hi);
-                    const int k = 2 * i + (u >> 1);
-                    if (u & 1) {
-                        wo_hi[k] = hi;
-                        wo_lo[k] = lo;
-                    } else {
-                        we_hi[k] = hi;
-                        we_lo[k] = lo;
-                    }
+                    w[u] = pw * t[i].vs[u];
+                    z_lane = __builtin_fmaf(pw, t[i].vz[u], z_lane);
                 }
+                split_hi_lo(w[0], w[2], ehi[i], elo[i]);
+                split_hi_lo(w[1], w[3], ohi[i], olo[i]);
             }
+            const half8_v we_hi = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
+            const half8_v we_lo = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
+            const half8_v wo_hi = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
+            const half8_v wo_lo = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 half2_t ve[kTilesP4], vo[kTilesP4];
@@ -233,10 +251,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             }
         }
     }
-    float l_sum = l_lane + __shfl_xor(l_lane, 16);
-    l_sum += __shfl_xor(l_sum, 32);
-    float z_sum = z_lane + __shfl_xor(z_lane, 16);
-    z_sum += __shfl_xor(z_sum, 32);
+    const float l_sum = col_sum4(l_lane);
+    const float z_sum = col_sum4(z_lane);
     if (live) {
         const float inv = 1.0f / l_sum;
 #pragma unroll
