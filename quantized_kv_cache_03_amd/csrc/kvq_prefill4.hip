@@ -5,11 +5,12 @@
 // cache (asymmetric 4-bit codes, an fp32 (scale, zero point) pair per (token, KV head)), with the
 // logits and the output factored as in the INT4 decode kernels:
 //     z_t = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d),  out = (sum_t p_t s_t c_t + sum_t p_t zp_t) / sum_t p_t.
-// One wave per (KV head, tile of 16 / G query rows, sequence) on v_mfma_f32_16x16x32_f16; the 16
-// columns are (query row, query head) pairs as in the 8-bit prefill kernel, and the operands are
-// those of the grouped INT4 decode kernel (kvq_attn_gqa4.hip): one 16-byte load per lane for each
-// of the K and V tiles, P^T left in the lanes by the S^T accumulator, chunks of four tiles.  Every
-// decoded code is in 2^-24 units (odd nibbles shifted down), so each product keeps one accumulator.
+// One wave per (KV head, tile of query rows, sequence) on v_mfma_f32_16x16x32_f16, serving two
+// blocks of 16 columns -- (query row, query head) pairs as in the 8-bit prefill kernel -- with the
+// operands of the grouped INT4 decode kernel (kvq_attn_gqa4.hip): one 16-byte load per lane for
+// each of the K and V tiles, decoded once for both blocks, P^T left in the lanes by the S^T
+// accumulator, chunks of four tiles.  Every decoded code is in 2^-24 units (odd nibbles shifted
+// down), so each product keeps one accumulator.
 #include "kvq_attn4.h"
 #include "kvq_mfma.h"
 
@@ -33,7 +34,7 @@ struct Prefill4Params {
     int32_t Hq;
     int32_t Hkv;
     int32_t G;                // query heads per KV head
-    int32_t R;                // query rows per wave (16 / G)
+    int32_t R;                // query rows per column block (16 / G)
     int32_t row_tiles;        // grid extent over row tiles
     float qk_scale;           // sm_scale * log2(e)
 };
@@ -81,70 +82,90 @@ __device__ __forceinline__ int kslot_dim(int m, int slot) {
     return 8 * dw + i + 4 * (slot % 2);
 }
 
+// NB column blocks of 16 per wave (NB R consecutive rows): the K and V operands of a tile are
+// decoded once and feed the MFMAs of every block.
+template <int NB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_prefill_mfma4(
     Prefill4Params a) {
     const int g = blockIdx.x;
     const int rt = a.row_tiles - 1 - (int)blockIdx.y;  // later rows read more tiles: run them first
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
-    const int col = lane & 15;  // column: (row jr, head hg)
+    const int col = lane & 15;  // column of each block: (row jr, head hg)
     const int q4 = lane >> 4;   // MFMA k-group / C row group
 
     const int r0 = a.cu_q[b];
     const int nq = a.cu_q[b + 1] - r0;
-    const int j0 = rt * a.R;
+    const int j0 = rt * (NB * a.R);
     if (j0 >= nq) return;
     const int n = a.ctx[b];
     const int jr = col / a.G, hg = col % a.G;
-    const int j = j0 + jr;
-    const bool live = jr < a.R && j < nq;  // the column holds a real (row, head)
-    const size_t orow = ((size_t)(r0 + j) * a.Hq + (size_t)g * a.G + hg) * kDim;
-    if (n < nq) {  // more query rows than tokens: outside the contract; the rows get zeros
-        if (live) {
+    bool live[NB];  // the column of block nb holds a real (row, head)
+    size_t orow[NB];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                *reinterpret_cast<half4_t*>(a.out + orow + 16 * r + 4 * q4) = half4_t{0, 0, 0, 0};
-        }
+    for (int nb = 0; nb < NB; ++nb) {
+        const int j = j0 + nb * a.R + jr;
+        live[nb] = jr < a.R && j < nq;
+        orow[nb] = ((size_t)(r0 + j) * a.Hq + (size_t)g * a.G + hg) * kDim;
+    }
+    if (n < nq) {  // more query rows than tokens: outside the contract; the rows get zeros
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            if (live[nb]) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    *reinterpret_cast<half4_t*>(a.out + orow[nb] + 16 * r + 4 * q4) = half4_t{0, 0, 0, 0};
+            }
         return;
     }
-    const int pos_min = n - nq + j0;                   // every column sees tokens 0 .. pos_min
-    const int t_end = n - nq + min(nq, j0 + a.R);      // tokens the wave reads
+    const int pos_min = n - nq + j0;                       // every column sees tokens 0 .. pos_min
+    const int t_end = n - nq + min(nq, j0 + NB * a.R);     // tokens the wave reads
     const int tile_end = (t_end + kBlock - 1) / kBlock;
-    const int pos = live ? n - nq + j : pos_min;       // the column's last visible token
+    int pos[NB];  // last visible token of each block's column (padding columns: pos_min)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pos[nb] = live[nb] ? n - nq + j0 + nb * a.R + jr : pos_min;
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
-    // Q^T operands of the column over chunk q4's dims, and the sum of its 128 q elements
-    half8_v qB[4];
-    float qsum = 0.0f;
+    // Q^T operands of each block's column over chunk q4's dims, and the sum of its 128 q elements
+    half8_v qB[NB][4];
+    float qsum[NB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) qB[m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
-    if (live) {
-        const uint16_t* qrow = a.q + orow + 32 * q4;
-        uint16_t qv[32];
+    for (int nb = 0; nb < NB; ++nb) {
+        qsum[nb] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 w = reinterpret_cast<const u32x4*>(qrow)[c];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        for (int m = 0; m < 4; ++m) qB[nb][m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
+        if (live[nb]) {
+            const uint16_t* qrow = a.q + orow[nb] + 32 * q4;
+            uint16_t qv[32];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                qv[8 * c + 2 * k] = (uint16_t)(ww[k] & 0xFFFFu);
-                qv[8 * c + 2 * k + 1] = (uint16_t)(ww[k] >> 16);
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 w = reinterpret_cast<const u32x4*>(qrow)[c];
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    qv[8 * c + 2 * k] = (uint16_t)(ww[k] & 0xFFFFu);
+                    qv[8 * c + 2 * k + 1] = (uint16_t)(ww[k] >> 16);
+                }
             }
+#pragma unroll
+            for (int d = 0; d < 32; ++d) qsum[nb] += (float)__builtin_bit_cast(_Float16, qv[d]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int s = 0; s < 8; ++s) qB[nb][m][s] = __builtin_bit_cast(_Float16, qv[kslot_dim(m, s)]);
         }
-#pragma unroll
-        for (int d = 0; d < 32; ++d) qsum += (float)__builtin_bit_cast(_Float16, qv[d]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int s = 0; s < 8; ++s) qB[m][s] = __builtin_bit_cast(_Float16, qv[kslot_dim(m, s)]);
+        qsum[nb] = col_sum4(qsum[nb]);
     }
-    qsum += __shfl_xor(qsum, 16);
-    qsum += __shfl_xor(qsum, 32);
 
-    float m_run = kNegInf, l_lane = 0.0f, z_lane = 0.0f;
-    float4_t acc[8];  // O^T row blocks in 2^-24 units: dims 16 r + 4 q4 .. +3 of the column
+    float m_run[NB], l_lane[NB], z_lane[NB];
+    float4_t acc[NB][8];  // O^T row blocks in 2^-24 units: dims 16 r + 4 q4 .. +3 of the column
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nb = 0; nb < NB; ++nb) {
+        m_run[nb] = kNegInf;
+        l_lane[nb] = z_lane[nb] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[nb][r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     const uint32_t off = 256u * (uint32_t)q4 + 16u * (uint32_t)col;
     const float qk24 = a.qk_scale * kInt4Even;
 
@@ -163,29 +184,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 }
             }
             const int tok_base = (tb + c0) * kBlock;
-            float z[kTilesP4][4];
+            float z[NB][kTilesP4][4];
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
                 half8_v kop[4];
                 k_operands_p4(t[i].k, kop);
-                float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int m = 0; m < 4; ++m) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[m], qB[m], s, 0, 0, 0);
+                for (int nb = 0; nb < NB; ++nb) {
+                    float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    z[i][u] = qk24 * (s[u] * t[i].ks[u]) + a.qk_scale * (t[i].kz[u] * qsum);
+                    for (int m = 0; m < 4; ++m) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[m], qB[nb][m], s, 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        z[nb][i][u] = qk24 * (s[u] * t[i].ks[u]) + a.qk_scale * (t[i].kz[u] * qsum[nb]);
+                }
             }
             // The causal mask, only for the chunks that reach past the wave's first row
             // (wave-uniform test); and the V parameters of slots past the context are zeroed (they
             // may be NaN, and a zero weight alone would still give 0 * NaN), only in the chunk
             // that reaches past it.
             if (tok_base + kTilesP4 * kBlock - 1 > pos_min) {
-                const int lim = pos - (tok_base + 4 * q4);  // last visible offset in the chunk
 #pragma unroll
-                for (int i = 0; i < kTilesP4; ++i)
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int lim = pos[nb] - (tok_base + 4 * q4);  // last visible offset in the chunk
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (i * kBlock + u > lim) z[i][u] = kNegInf;
+                    for (int i = 0; i < kTilesP4; ++i)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (i * kBlock + u > lim) z[nb][i][u] = kNegInf;
+                }
             }
             if (tok_base + kTilesP4 * kBlock > n) {
 #pragma unroll
@@ -194,43 +221,57 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                     for (int u = 0; u < 4; ++u)
                         if (tok_base + i * kBlock + 4 * q4 + u >= n) t[i].vs[u] = t[i].vz[u] = 0.0f;
             }
-            float cmax = kNegInf;
-#pragma unroll
-            for (int i = 0; i < kTilesP4; ++i)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) cmax = fmaxf(cmax, z[i][u]);
             // finite: the first chunk holds token 0.  Lazy rescale (kRescaleSlack), a branch every
             // lane takes or skips together.
-            cmax = col_max4(cmax);
-            const bool up = cmax > m_run + kRescaleSlack;  // m_run = -inf: any finite max
-            if (__builtin_amdgcn_ballot_w64(up)) {
-                const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
-                if (up) m_run = cmax;
-                l_lane *= alpha;
-                z_lane *= alpha;
+            bool moved = false;
+            bool up[NB];
+            float cmax[NB];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) acc[r] *= alpha;
+            for (int nb = 0; nb < NB; ++nb) {
+                float m = kNegInf;
+#pragma unroll
+                for (int i = 0; i < kTilesP4; ++i)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) m = fmaxf(m, z[nb][i][u]);
+                cmax[nb] = col_max4(m);
+                up[nb] = cmax[nb] > m_run[nb] + kRescaleSlack;  // m_run = -inf: any finite max
+                moved |= up[nb];
             }
-            // P^T operands: tokens (0, 2) and (1, 3) of this lane's quad of each tile, w = p s_v
-            // (dword i of an operand: tile i's pair)
-            uint32_t ehi[kTilesP4], elo[kTilesP4], ohi[kTilesP4], olo[kTilesP4];
+            if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-            for (int i = 0; i < kTilesP4; ++i) {
-                float w[4];
+                for (int nb = 0; nb < NB; ++nb) {
+                    const float alpha = up[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - cmax[nb]) : 1.0f;
+                    if (up[nb]) m_run[nb] = cmax[nb];
+                    l_lane[nb] *= alpha;
+                    z_lane[nb] *= alpha;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_run);
-                    l_lane += pw;
-                    w[u] = pw * t[i].vs[u];
-                    z_lane = __builtin_fmaf(pw, t[i].vz[u], z_lane);
+                    for (int r = 0; r < 8; ++r) acc[nb][r] *= alpha;
                 }
-                split_hi_lo(w[0], w[2], ehi[i], elo[i]);
-                split_hi_lo(w[1], w[3], ohi[i], olo[i]);
             }
-            const half8_v we_hi = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
-            const half8_v we_lo = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
-            const half8_v wo_hi = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
-            const half8_v wo_lo = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
+            // P^T operands per block: tokens (0, 2) and (1, 3) of this lane's quad of each tile,
+            // w = p s_v (dword i of an operand: tile i's pair)
+            half8_v we_hi[NB], we_lo[NB], wo_hi[NB], wo_lo[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                uint32_t ehi[kTilesP4], elo[kTilesP4], ohi[kTilesP4], olo[kTilesP4];
+#pragma unroll
+                for (int i = 0; i < kTilesP4; ++i) {
+                    float w[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float pw = __builtin_amdgcn_exp2f(z[nb][i][u] - m_run[nb]);
+                        l_lane[nb] += pw;
+                        w[u] = pw * t[i].vs[u];
+                        z_lane[nb] = __builtin_fmaf(pw, t[i].vz[u], z_lane[nb]);
+                    }
+                    split_hi_lo(w[0], w[2], ehi[i], elo[i]);
+                    split_hi_lo(w[1], w[3], ohi[i], olo[i]);
+                }
+                we_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
+                we_lo[nb] = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
+                wo_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
+                wo_lo[nb] = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
+            }
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 half2_t ve[kTilesP4], vo[kTilesP4];
@@ -244,26 +285,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 }
                 const half8_v ae = join8(ve[0], ve[1], ve[2], ve[3]);
                 const half8_v ao = join8(vo[0], vo[1], vo[2], vo[3]);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc[r], 0, 0, 0);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc[r], 0, 0, 0);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc[r], 0, 0, 0);
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc[r], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi[nb], acc[nb][r], 0, 0, 0);
+                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo[nb], acc[nb][r], 0, 0, 0);
+                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi[nb], acc[nb][r], 0, 0, 0);
+                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo[nb], acc[nb][r], 0, 0, 0);
+                }
             }
         }
     }
-    const float l_sum = col_sum4(l_lane);
-    const float z_sum = col_sum4(z_lane);
-    if (live) {
-        const float inv = 1.0f / l_sum;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float4_t o = acc[r] * kInt4Even + z_sum;
-            const half4_t v = {(_Float16)(o[0] * inv), (_Float16)(o[1] * inv), (_Float16)(o[2] * inv),
-                               (_Float16)(o[3] * inv)};
-            *reinterpret_cast<half4_t*>(a.out + orow + 16 * r + 4 * q4) = v;
+    for (int nb = 0; nb < NB; ++nb) {
+        const float l_sum = col_sum4(l_lane[nb]);
+        const float z_sum = col_sum4(z_lane[nb]);
+        if (live[nb]) {
+            const float inv = 1.0f / l_sum;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const float4_t o = acc[nb][r] * kInt4Even + z_sum;
+                const half4_t v = {(_Float16)(o[0] * inv), (_Float16)(o[1] * inv), (_Float16)(o[2] * inv),
+                                   (_Float16)(o[3] * inv)};
+                *reinterpret_cast<half4_t*>(a.out + orow[nb] + 16 * r + 4 * q4) = v;
+            }
         }
     }
 }
+
+#ifndef KVQ_PREFILL4_BLOCKS
+#define KVQ_PREFILL4_BLOCKS 2
+#endif
 
 }  // namespace
 
@@ -285,13 +336,15 @@ hipError_t launch_prefill4(const PrefillArgs& p, hipStream_t stream, hipEvent_t 
     a.Hkv = c.num_kv_heads;
     a.G = p.num_q_heads / c.num_kv_heads;
     a.R = 16 / a.G;
-    a.row_tiles = (p.max_q_len + a.R - 1) / a.R;
+    const int rows_per_wave = KVQ_PREFILL4_BLOCKS * a.R;
+    a.row_tiles = (p.max_q_len + rows_per_wave - 1) / rows_per_wave;
     a.qk_scale = p.sm_scale * kLog2e;
     const dim3 grid((unsigned)a.Hkv, (unsigned)a.row_tiles, (unsigned)p.batch);
     if (start)
-        hipExtLaunchKernelGGL(attn_prefill_mfma4, grid, dim3(64), 0, stream, start, stop, 0, a);
+        hipExtLaunchKernelGGL(attn_prefill_mfma4<KVQ_PREFILL4_BLOCKS>, grid, dim3(64), 0, stream, start,
+                              stop, 0, a);
     else
-        hipLaunchKernelGGL(attn_prefill_mfma4, grid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(attn_prefill_mfma4<KVQ_PREFILL4_BLOCKS>, grid, dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
