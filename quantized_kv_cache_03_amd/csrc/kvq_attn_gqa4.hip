@@ -26,35 +26,6 @@ namespace {
 
 constexpr int kTiles4 = 4;  // tiles per chunk: the P^T operand spans four tiles
 
-// This lane's share of one tile.
-struct TileG4 {
-    u32x4 k, v;      // K: token l % 16, chunk l / 16; V: quad l / 16, dims l % 16 + 16 r
-    float4_t ks, kz;  // K (scale, zero point) of tokens 4 (l / 16) .. +3
-    float4_t vs, vz;  // V (scale, zero point) of the same tokens
-};
-
-__device__ __forceinline__ void load_tile_g4(const KernelParams& a, TileG4& t, int blk, int g,
-                                             uint32_t off, int q4) {
-    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes4;
-    t.k = ldg16(a.kc + tile + off);
-    t.v = ldg16(a.vc + tile + off);
-    // (scale, zero point) pairs of four tokens: two 16-byte loads each for K and V
-    const size_t so = (((size_t)blk * a.Hkv + g) * kBlock + 4 * q4) * 2;
-    const float4_t k0 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
-    const float4_t k1 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so + 4));
-    const float4_t v0 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-    const float4_t v1 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so + 4));
-    t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
-    t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
-    t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};
-    t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
-}
-
-__device__ __forceinline__ void zero_tile_g4(TileG4& t) {
-    t.k = t.v = u32x4{0u, 0u, 0u, 0u};
-    t.ks = t.kz = t.vs = t.vz = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-}
-
 __device__ __forceinline__ half8_v join4(half2_t a, half2_t b, half2_t c, half2_t d) {
     return join8(a, b, c, d);
 }
@@ -84,7 +55,7 @@ __device__ __forceinline__ int k_slot_dim(int dw0, int odd, int slot) {
 
 // One chunk of kTiles4 tiles (tiles past the segment's end are zero, their tokens masked).
 template <bool APPEND>
-__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTiles4], int tile0, int t_end,
+__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[kTiles4], int tile0, int t_end,
                                          const half8_v (&qe)[2], const half8_v (&qo)[2], float qsum,
                                          int q4, float& m_run, float& l_lane, float& z_lane,
                                          float4_t (&acc_e)[8], float4_t (&acc_o)[8]) {
@@ -181,7 +152,7 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTil
 
 // Replace the new token's codes and scales in the registers of its tile: K in the four lanes whose
 // operand row is the token, V and the scale pairs in the 16 lanes of its quad.
-__device__ __forceinline__ void patch_tile_g4(TileG4& t, const NewToken4& nt, const uint8_t* lds_k,
+__device__ __forceinline__ void patch_tile_g4(TileMfma4& t, const NewToken4& nt, const uint8_t* lds_k,
                                               const uint8_t* lds_v, int lane) {
     const int col = lane & 15, q4 = lane >> 4;
     if (col == nt.slot) t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
@@ -255,13 +226,13 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
         const int nt_grp = min(64, hi - tb);
         const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
         for (int c0 = 0; c0 < nt_grp; c0 += kTiles4) {
-            TileG4 t[kTiles4];
+            TileMfma4 t[kTiles4];
 #pragma unroll
             for (int i = 0; i < kTiles4; ++i) {
                 if (c0 + i < nt_grp)
-                    load_tile_g4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                    load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
                 else
-                    zero_tile_g4(t[i]);
+                    zero_tile_mfma4(t[i]);
             }
             if constexpr (APPEND) {
                 const int inew = tile_new - (tb + c0);  // wave-uniform

@@ -67,6 +67,40 @@ __device__ __forceinline__ uint32_t v_byte4(int t, int d) {
            (uint32_t)((t % 4) / 2);
 }
 
+// One lane's share of one tile in the matrix-core lane layout (the grouped decode kernel and the
+// prefill kernel): K of token l % 16 in chunk l / 16, V of quad l / 16 for the dims l % 16 + 16 r
+// (one 16-byte load each), and the (scale, zero point) pairs of the quad's tokens 4 (l / 16) .. +3.
+struct TileMfma4 {
+    u32x4 k, v;
+    float4_t ks, kz;  // K (scale, zero point) of the four tokens
+    float4_t vs, vz;  // V (scale, zero point) of the same tokens
+};
+
+// Load tile (blk, g) for this lane (off = 256 q4 + 16 col); ks / vs are the [blocks][Hkv][16][2]
+// pair arrays.
+__device__ __forceinline__ void load_tile_mfma4(const uint8_t* kc, const uint8_t* vc, const float* ks,
+                                                const float* vs, int Hkv, TileMfma4& t, int blk, int g,
+                                                uint32_t off, int q4) {
+    const size_t tile = ((size_t)blk * Hkv + g) * kTileBytes4;
+    t.k = ldg16(kc + tile + off);
+    t.v = ldg16(vc + tile + off);
+    // (scale, zero point) pairs of four tokens: two 16-byte loads each for K and V
+    const size_t so = (((size_t)blk * Hkv + g) * kBlock + 4 * q4) * 2;
+    const float4_t k0 = ldg_nt(reinterpret_cast<const float4_t*>(ks + so));
+    const float4_t k1 = ldg_nt(reinterpret_cast<const float4_t*>(ks + so + 4));
+    const float4_t v0 = ldg_nt(reinterpret_cast<const float4_t*>(vs + so));
+    const float4_t v1 = ldg_nt(reinterpret_cast<const float4_t*>(vs + so + 4));
+    t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
+    t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
+    t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};
+    t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
+}
+
+__device__ __forceinline__ void zero_tile_mfma4(TileMfma4& t) {
+    t.k = t.v = u32x4{0u, 0u, 0u, 0u};
+    t.ks = t.kz = t.vs = t.vz = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
 // The 16-bit unit of a V dword (SEL 0: bits 0-15, 1: bits 16-31: four tokens of one dim) as two
 // binary16 pairs (see int4x8_to_f16): e = tokens (0, 2) * 2^-24, o = tokens (1, 3) * 2^-20.
 template <int SEL>

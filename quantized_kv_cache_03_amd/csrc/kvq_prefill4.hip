@@ -39,28 +39,6 @@ struct Prefill4Params {
     float qk_scale;           // sm_scale * log2(e)
 };
 
-// This lane's share of one tile (as in the grouped INT4 decode kernel).
-struct TileP4 {
-    u32x4 k, v;       // K: token l % 16, chunk l / 16; V: quad l / 16, dims l % 16 + 16 r
-    float4_t ks, kz;  // K (scale, zero point) of tokens 4 (l / 16) .. +3
-    float4_t vs, vz;  // V (scale, zero point) of the same tokens
-};
-
-__device__ __forceinline__ void load_tile_p4(const Prefill4Params& a, TileP4& t, int blk, int g,
-                                             uint32_t off, int q4) {
-    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes4;
-    t.k = ldg16(a.kc + tile + off);
-    t.v = ldg16(a.vc + tile + off);
-    const size_t so = (((size_t)blk * a.Hkv + g) * kBlock + 4 * q4) * 2;
-    const float4_t k0 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
-    const float4_t k1 = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so + 4));
-    const float4_t v0 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-    const float4_t v1 = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so + 4));
-    t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
-    t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
-    t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};
-    t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
-}
 
 // The K operands of one tile in the k-slot order of kslot_dim: the four MFMAs take the (0, 4),
 // (2, 6) nibble pairs and then the (1, 5), (3, 7) pairs of dwords (0, 1) and of dwords (2, 3).
@@ -173,15 +151,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         const int nt_grp = min(64, tile_end - tb);
         const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
         for (int c0 = 0; c0 < nt_grp; c0 += kTilesP4) {
-            TileP4 t[kTilesP4];
+            TileMfma4 t[kTilesP4];  // this lane's share of each tile (kvq_int4.h)
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
-                if (c0 + i < nt_grp) {
-                    load_tile_p4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
-                } else {
-                    t[i].k = t[i].v = u32x4{0u, 0u, 0u, 0u};
-                    t[i].ks = t[i].kz = t[i].vs = t[i].vz = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                }
+                if (c0 + i < nt_grp)
+                    load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
+                                    __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                else
+                    zero_tile_mfma4(t[i]);
             }
             const int tok_base = (tb + c0) * kBlock;
             float z[NB][kTilesP4][4];
