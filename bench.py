@@ -339,8 +339,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decode kernels run on a single MI355X and this build "
-              "has no multi-GPU path (see the design notes on how it would shard). Run with --gpus 1.",
+        print("bench.py measures one GPU: the decode kernels run on a single MI355X and the library "
+              "has no multi-GPU path (the design notes describe how it would shard). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
