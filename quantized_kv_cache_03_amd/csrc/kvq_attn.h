@@ -26,6 +26,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // rounding.
 constexpr float kRescaleSlack = 8.0f;
 
+// With per-token V scales (INT8, INT4) the P V products take w = p s_v as fp16 hi + lo parts, and
+// p may reach 2^slack, so the slack keeps 2^slack times the largest scale a finite fp16 row can
+// have inside the fp16 range: INT8 s_v <= 65504 / 127, and 2^6.5 * 515.8 < 46,700; INT4
+// s_v <= 131008 / 15, and 2^2.5 * 8733.9 < 49,400.  (Per-tensor formats: w = p <= 2^8.)
+constexpr float kRescaleSlackInt8 = 6.5f;
+constexpr float kRescaleSlackInt4 = 2.5f;
+
 // Keep the low `nbytes` (0..4) bytes of w.
 __device__ __forceinline__ uint32_t keep_bytes(uint32_t w, int nbytes) {
     return nbytes >= 4 ? w : (nbytes <= 0 ? 0u : (w & ((1u << (8 * nbytes)) - 1u)));

@@ -138,32 +138,30 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
 
     for (int tb = tile_begin; tb < tile_end; tb += 64) {
         const int nt_grp = min(64, tile_end - tb);
-        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        // Lanes past the group's tiles repeat its last block, so a chunk's loads are issued together
+        // with no branch between them; the extra tiles' tokens lie past the segment: their logits
+        // are masked and their V codes zeroed below.
+        const int blk_lane = bt[tb + min(lane, nt_grp - 1)];
         for (int c0 = 0; c0 < nt_grp; c0 += TW) {
             u32x4 ka[TW], kb[TW];
             uint32_t vd[TW][8];
             float4_t ks4[TW], vs4[TW];
 #pragma unroll
             for (int i = 0; i < TW; ++i) {
-                if (c0 + i < nt_grp) {
-                    const int blk = __builtin_amdgcn_readlane(blk_lane, c0 + i);
-                    const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
-                    const uint8_t* kt = a.kc + tile;
-                    const uint8_t* vt = a.vc + tile;
-                    ka[i] = ldg16(kt + k_off);
-                    kb[i] = ldg16(kt + k_off + 1024u);
+                const int blk = __builtin_amdgcn_readlane(blk_lane, c0 + i);
+                const size_t tile = ((size_t)blk * a.Hkv + g) * kTileBytes;
+                const uint8_t* kt = a.kc + tile;
+                const uint8_t* vt = a.vc + tile;
+                ka[i] = ldg16(kt + k_off);
+                kb[i] = ldg16(kt + k_off + 1024u);
 #pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
-                    if constexpr (DT == KVQ_INT8) {
-                        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
-                        ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
-                        vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-                    }
+                for (int r = 0; r < 8; ++r)
+                    vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
+                if constexpr (DT == KVQ_INT8) {
+                    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
+                    ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
+                    vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
                 } else {
-                    ka[i] = kb[i] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) vd[i][r] = 0u;
                     ks4[i] = vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 }
             }
@@ -213,10 +211,11 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
                 }
             }
             // max over the head's tokens (the four row groups of the column); finite: every chunk
-            // holds a valid token.  Lazy rescale (kRescaleSlack), a branch every lane takes or
-            // skips together.
+            // holds a valid token.  Lazy rescale (kRescaleSlack, kRescaleSlackInt8), a branch every
+            // lane takes or skips together.
             cmax = col_max4(cmax);
-            const bool up = cmax > m_run + kRescaleSlack;  // m_run = -inf: any finite max
+            constexpr float slack = DT == KVQ_INT8 ? kRescaleSlackInt8 : kRescaleSlack;
+            const bool up = cmax > m_run + slack;  // m_run = -inf: any finite max
             if (__builtin_amdgcn_ballot_w64(up)) {
                 const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
                 if (up) m_run = cmax;

@@ -7,8 +7,9 @@
 // One wave per (KV head, share of the work) serves the G <= 16 query heads of the group, as the
 // 8-bit grouped kernel (kvq_attn_gqa.hip) does, with both products on v_mfma_f32_16x16x32_f16
 // (query heads padded to 16 columns).  Codes decode to exact binary16 subnormals by masking
-// (int4x8_to_f16 / int4_unit_to_f16): the even nibble pairs are worth 2^-24 per unit, the odd ones
-// 2^-20, so every operand holds only one of the two kinds and each product keeps two accumulators.
+// (int4x8_to_f16): K's even nibble pairs are worth 2^-24 per unit and its odd ones 2^-20, so each
+// K operand holds one of the two kinds and S^T keeps two accumulators; V's odd nibbles are shifted
+// down before the masking (int4_unit_to_f16_unit), so O^T keeps one, in 2^-24 units.
 //   S^T = K Q^T per tile: A = K (lane: token l % 16, the 32 dims of chunk l / 16 -- one 16-byte
 //       load per lane reads the tile), B = Q^T (lane: head l % 16, the same dims); two MFMAs for
 //       the even nibble pairs of the chunk's dims, two for the odd ones.  C: lane (head l % 16,
@@ -53,12 +54,12 @@ __device__ __forceinline__ int k_slot_dim(int dw0, int odd, int slot) {
     return 8 * dw + i + 4 * (slot % 2);
 }
 
-// One chunk of kTiles4 tiles (tiles past the segment's end are zero, their tokens masked).
+// One chunk of kTiles4 tiles (tiles past the segment's end repeat its last one; their tokens are masked).
 template <bool APPEND>
 __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[kTiles4], int tile0, int t_end,
                                          const half8_v (&qe)[2], const half8_v (&qo)[2], float qsum,
                                          int q4, float& m_run, float& l_lane, float& z_lane,
-                                         float4_t (&acc_e)[8], float4_t (&acc_o)[8]) {
+                                         float4_t (&acc)[8]) {
     float z[kTiles4][4];
     float cmax = kNegInf;
 #pragma unroll
@@ -79,21 +80,6 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
             cmax = fmaxf(cmax, z[i][u]);
         }
     }
-    // Lazy rescale (kRescaleSlack), a branch every lane takes or skips together.  Every chunk holds
-    // a valid token, so cmax is finite.
-    cmax = col_max4(cmax);
-    const bool up = cmax > m_run + kRescaleSlack;  // m_run = -inf: any finite max
-    if (__builtin_amdgcn_ballot_w64(up)) {
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
-        if (up) m_run = cmax;
-        l_lane *= alpha;
-        z_lane *= alpha;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            acc_e[r] *= alpha;
-            acc_o[r] *= alpha;
-        }
-    }
     // The V parameters of the slots at and past t_end are zeroed (past the context they may be
     // NaN, and a zero weight alone would still give 0 * NaN); only a tile that reaches past the
     // end has such slots (wave-uniform test).
@@ -108,6 +94,18 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
                     t[i].vz[u] = 0.0f;
                 }
         }
+    }
+    // Lazy rescale (kRescaleSlackInt4), a branch every lane takes or skips together.  Every chunk
+    // holds a valid token, so cmax is finite.
+    cmax = col_max4(cmax);
+    const bool up = cmax > m_run + kRescaleSlackInt4;  // m_run = -inf: any finite max
+    if (__builtin_amdgcn_ballot_w64(up)) {
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
+        if (up) m_run = cmax;
+        l_lane *= alpha;
+        z_lane *= alpha;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc[r] *= alpha;
     }
     // P^T operands: the even tokens (0, 2) and the odd tokens (1, 3) of this lane's quad of each
     // tile, as fp16 hi and lo parts of w = p s_v (dword i of an operand: tile i's pair)
@@ -137,16 +135,16 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
         for (int i = 0; i < kTiles4; ++i) {
             const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
             if (r & 1)
-                int4_unit_to_f16<1>(w[r / 2], ve[i], vo[i]);
+                int4_unit_to_f16_unit<1>(w[r / 2], ve[i], vo[i]);
             else
-                int4_unit_to_f16<0>(w[r / 2], ve[i], vo[i]);
+                int4_unit_to_f16_unit<0>(w[r / 2], ve[i], vo[i]);
         }
         const half8_v ae = join4(ve[0], ve[1], ve[2], ve[3]);
         const half8_v ao = join4(vo[0], vo[1], vo[2], vo[3]);
-        acc_e[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc_e[r], 0, 0, 0);
-        acc_e[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc_e[r], 0, 0, 0);
-        acc_o[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc_o[r], 0, 0, 0);
-        acc_o[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc_o[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc[r], 0, 0, 0);
     }
 }
 
@@ -216,24 +214,22 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
 
     float m_run = kNegInf;
     float l_lane = 0.0f, z_lane = 0.0f;
-    float4_t acc_e[8], acc_o[8];  // O^T row blocks: dims 16 r + 4 q4 .. +3 of head col
+    float4_t acc[8];  // O^T row blocks in 2^-24 units: dims 16 r + 4 q4 .. +3 of head col
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc_e[r] = acc_o[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint32_t off = 256u * (uint32_t)q4 + 16u * (uint32_t)col;
 
     for (int tb = lo; tb < hi; tb += 64) {
         const int nt_grp = min(64, hi - tb);
-        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        // Lanes past the group's tiles repeat its last block, so a chunk's loads are issued together
+        // with no branch between them; the extra tiles' tokens lie past the segment and are masked.
+        const int blk_lane = bt[tb + min(lane, nt_grp - 1)];
         for (int c0 = 0; c0 < nt_grp; c0 += kTiles4) {
             TileMfma4 t[kTiles4];
 #pragma unroll
-            for (int i = 0; i < kTiles4; ++i) {
-                if (c0 + i < nt_grp)
-                    load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
-                else
-                    zero_tile_mfma4(t[i]);
-            }
+            for (int i = 0; i < kTiles4; ++i)
+                load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
             if constexpr (APPEND) {
                 const int inew = tile_new - (tb + c0);  // wave-uniform
                 if (inew >= 0 && inew < kTiles4) {
@@ -248,7 +244,7 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
                         }
                 }
             }
-            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, qsum, q4, m_run, l_lane, z_lane, acc_e, acc_o);
+            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, qsum, q4, m_run, l_lane, z_lane, acc);
         }
     }
     // the head's weight sum and zero-point sum over the four row groups
@@ -258,7 +254,7 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
     if (col < G) {
         float4_t o[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) o[r] = acc_e[r] * kInt4Even + acc_o[r] * kInt4Odd + z_sum;
+        for (int r = 0; r < 8; ++r) o[r] = acc[r] * kInt4Even + z_sum;
         if (lo == 0 && hi == nt) {
             const float inv = a.v_scale / l_sum;
             uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * kDim;

@@ -111,7 +111,7 @@ __device__ __forceinline__ void chunk_step4(const KernelParams& a, const Tile4 (
         cmax = fmaxf(cmax, z[i]);
     }
     cmax = max_across_quads(cmax);  // a chunk always holds at least one valid token
-    if (cmax > m_run + kRescaleSlack) {  // lazy rescale; one head per wave, so wave-uniform
+    if (cmax > m_run + kRescaleSlackInt4) {  // lazy rescale; one head per wave, so wave-uniform
         const float alpha = __builtin_amdgcn_exp2f(m_run - cmax);
         m_run = cmax;
 #pragma unroll

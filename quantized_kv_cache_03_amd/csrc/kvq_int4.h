@@ -96,11 +96,6 @@ __device__ __forceinline__ void load_tile_mfma4(const uint8_t* kc, const uint8_t
     t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
 }
 
-__device__ __forceinline__ void zero_tile_mfma4(TileMfma4& t) {
-    t.k = t.v = u32x4{0u, 0u, 0u, 0u};
-    t.ks = t.kz = t.vs = t.vz = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-}
-
 // The 16-bit unit of a V dword (SEL 0: bits 0-15, 1: bits 16-31: four tokens of one dim) as two
 // binary16 pairs (see int4x8_to_f16): e = tokens (0, 2) * 2^-24, o = tokens (1, 3) * 2^-20.
 template <int SEL>

@@ -151,30 +151,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
     // Software pipeline over chunks of TW tiles, three stages kept in flight: the K codes of chunk
     // c + 2 are loading, the S^T MFMAs of chunk c + 1 are issued, and chunk c's softmax and P V^T run
     // -- so the VALU work of one chunk overlaps the matrix cores' work on the next.  Two buffers of
-    // each kind, swapped by unrolling the loop by two.  Tiles at or past tile_end are zeros.
+    // each kind, swapped by unrolling the loop by two.
     struct KBuf { u32x4 ka[TW], kb[TW]; };
     struct VBuf { uint32_t vd[TW][8]; float4_t ks4[TW], vs4[TW]; };
     struct SBuf { float4_t s[NB][TW]; };
+    // A chunk's tiles at or past tile_end repeat tile tile_end - 1 (its first tile is always valid,
+    // and the repeat lies between it and the loaded tile, so its id is in the two id registers):
+    // the loads are unconditional, so no zero-filled registers make the wave wait for loads still
+    // in flight.  The repeats' tokens lie past every column's causal limit and past t_end: their
+    // logits are masked and their V codes zeroed.  INT8 runs one chunk at a time with nothing in
+    // flight across chunks, and zero-fills those tiles instead (measured faster there).
     auto load_k = [&](KBuf& kb_, int t0) {
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
-            const int t = t0 + i;
-            if (t < tile_end) {
+            if (DT == KVQ_INT8 && t0 + i >= tile_end) {
+                kb_.ka[i] = u32x4{0u, 0u, 0u, 0u};
+                kb_.kb[i] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                const int t = min(t0 + i, tile_end - 1);
                 const uint8_t* kt = a.kc + ((size_t)block_of(t) * a.Hkv + g) * kTileBytes;
                 kb_.ka[i] = ldg16(kt + k_off);
                 kb_.kb[i] = ldg16(kt + k_off + 1024u);
-            } else {
-                kb_.ka[i] = u32x4{0u, 0u, 0u, 0u};
-                kb_.kb[i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
     auto load_v = [&](VBuf& vb, int t0) {
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
-            const int t = t0 + i;
-            if (t < tile_end) {
-                const int blk = block_of(t);
+            if (DT == KVQ_INT8 && t0 + i >= tile_end) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) vb.vd[i][r] = 0u;
+                vb.ks4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                vb.vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            } else {
+                const int blk = block_of(min(t0 + i, tile_end - 1));
                 const uint8_t* vt = a.vc + ((size_t)blk * a.Hkv + g) * kTileBytes;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) vb.vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
@@ -182,13 +192,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
                     const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
                     vb.ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
                     vb.vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) vb.vd[i][r] = 0u;
-                if constexpr (DT == KVQ_INT8) {
-                    vb.ks4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                    vb.vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
                 }
             }
         }
@@ -219,8 +222,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         }
     };
 
-    // Softmax of a chunk and its P V^T, with the lazy rescale (kRescaleSlack; a branch every lane
-    // takes or skips together).
+    // Softmax of a chunk and its P V^T, with the lazy rescale (kRescaleSlack, kRescaleSlackInt8; a
+    // branch every lane takes or skips together).
     auto softmax_pv = [&](VBuf& vb, const SBuf& sb, int t0) {
         const int tok_base = t0 * kBlock;  // first token of the chunk
         float z[NB][TW][4];
@@ -249,6 +252,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         }
         // Every column sees token 0, which the first chunk holds, so the reference max is finite
         // from then on.
+        constexpr float slack = DT == KVQ_INT8 ? kRescaleSlackInt8 : kRescaleSlack;
         bool moved = false;
         bool up[NB];
         float cmax[NB];
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
 #pragma unroll
                 for (int t = 0; t < 4; ++t) m = fmaxf(m, z[nb][i][t]);
             cmax[nb] = col_max4(m);
-            up[nb] = cmax[nb] > m_run[nb] + kRescaleSlack;  // m_run = -inf: any finite max
+            up[nb] = cmax[nb] > m_run[nb] + slack;  // m_run = -inf: any finite max
             moved |= up[nb];
         }
         if (__builtin_amdgcn_ballot_w64(moved)) {

@@ -149,17 +149,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 
     for (int tb = 0; tb < tile_end; tb += 64) {
         const int nt_grp = min(64, tile_end - tb);
-        const int blk_lane = (lane < nt_grp) ? bt[tb + lane] : 0;
+        // Lanes past the group's tiles repeat its last block, so a chunk's loads are issued together
+        // with no branch between them; the extra tiles' tokens lie past every column's causal limit.
+        const int blk_lane = bt[tb + min(lane, nt_grp - 1)];
         for (int c0 = 0; c0 < nt_grp; c0 += kTilesP4) {
             TileMfma4 t[kTilesP4];  // this lane's share of each tile (kvq_int4.h)
 #pragma unroll
-            for (int i = 0; i < kTilesP4; ++i) {
-                if (c0 + i < nt_grp)
-                    load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
-                                    __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
-                else
-                    zero_tile_mfma4(t[i]);
-            }
+            for (int i = 0; i < kTilesP4; ++i)
+                load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
+                                __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
             const int tok_base = (tb + c0) * kBlock;
             float z[NB][kTilesP4][4];
 #pragma unroll
@@ -198,8 +196,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                     for (int u = 0; u < 4; ++u)
                         if (tok_base + i * kBlock + 4 * q4 + u >= n) t[i].vs[u] = t[i].vz[u] = 0.0f;
             }
-            // finite: the first chunk holds token 0.  Lazy rescale (kRescaleSlack), a branch every
-            // lane takes or skips together.
+            // finite: the first chunk holds token 0.  Lazy rescale (kRescaleSlackInt4), a branch
+            // every lane takes or skips together.
             bool moved = false;
             bool up[NB];
             float cmax[NB];
@@ -211,7 +209,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 #pragma unroll
                     for (int u = 0; u < 4; ++u) m = fmaxf(m, z[nb][i][u]);
                 cmax[nb] = col_max4(m);
-                up[nb] = cmax[nb] > m_run[nb] + kRescaleSlack;  // m_run = -inf: any finite max
+                up[nb] = cmax[nb] > m_run[nb] + kRescaleSlackInt4;  // m_run = -inf: any finite max
                 moved |= up[nb];
             }
             if (__builtin_amdgcn_ballot_w64(moved)) {
