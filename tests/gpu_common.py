@@ -91,3 +91,62 @@ def assert_attn_close(gpu: np.ndarray, ref: np.ndarray, tag=""):
     st = attn_stats(gpu, ref)
     assert not bad.any(), f"attention outside the gate {tag}: {int(bad.sum())} elements, {st}"
     return st
+
+
+# FP8 math: the matrix cores accumulate the FP8 products with an error of up to 8e-5 of the sum of
+# their magnitudes (measured on the instruction); the bound below takes twice that.
+FP8_ACCUMULATION = 1.6e-4
+
+
+def fp8_math_slack(cache, q, block_tables, context_lens, cu_q_lens=None, sm_scale=None):
+    """Extra tolerance per output element for FP8 math, on top of the gate.  Logit errors of at
+    most e_t = FP8_ACCUMULATION * sm_scale * sum_d |q^_d k^_td| (q^ the query as FP8 math quantizes
+    it, k^ the dequantized K row) move softmax output d by at most
+    sum_t p_t (e_t + sum_s p_s e_s) |v_td - o_d| (decode: this form, from the exact softmax), which
+    is at most 2 max_t(e_t) (max_t v_td - min_t v_td) over the tokens the row sees (prefill: this
+    cheaper form).  q: fp16 [B][Hq][128] (decode) or [T][Hq][128] with cu_q_lens (prefill)."""
+    sm = 1.0 / np.sqrt(128.0) if sm_scale is None else sm_scale
+    codes, scales = oracle.quantize_q_fp8_rows(q)
+    qh = oracle.fp8_decode(oracle.E4M3, codes) * scales[..., None].astype(np.float64)
+    ctx = np.asarray(context_lens)
+    kd, vd = oracle.dequant(cache, block_tables, ctx, max(1, int(ctx.max(initial=0))))
+    Hkv = kd.shape[1]
+    G = q.shape[1] // Hkv
+    slack = np.zeros(q.shape, np.float64)
+    for b, n in enumerate(ctx):
+        n = int(n)
+        if n == 0:
+            continue
+        if cu_q_lens is None:
+            rows, lims = [b], np.array([n])
+        else:
+            r0, r1 = int(cu_q_lens[b]), int(cu_q_lens[b + 1])
+            rows, lims = list(range(r0, r1)), n - (r1 - r0) + 1 + np.arange(r1 - r0)
+        if len(rows) == 0:
+            continue
+        for g in range(Hkv):
+            k = np.abs(kd[b, g, :n].astype(np.float64))
+            v = vd[b, g, :n].astype(np.float64)
+            vrange = np.maximum.accumulate(v, axis=0) - np.minimum.accumulate(v, axis=0)  # [n][128]
+            for hg in range(G):
+                h = g * G + hg
+                e = FP8_ACCUMULATION * sm * (np.abs(qh[rows, h]) @ k.T)  # [rows][n]
+                if cu_q_lens is None:
+                    z = sm * (kd[b, g, :n].astype(np.float64) @ qh[b, h])
+                    p = np.exp(z - z.max())
+                    p /= p.sum()
+                    o = p @ v
+                    et = e[0] + p @ e[0]
+                    slack[b, h] = (p * et) @ np.abs(v - o)
+                else:
+                    emax = np.maximum.accumulate(e, axis=1)[np.arange(len(rows)), lims - 1]
+                    slack[rows, h] = 2.0 * emax[:, None] * vrange[lims - 1]
+    return slack
+
+
+def assert_attn_close_fp8_math(gpu: np.ndarray, ref: np.ndarray, slack: np.ndarray, tag=""):
+    """The gate widened by fp8_math_slack."""
+    g = gpu.astype(np.float64)
+    assert not np.isnan(g).any(), f"NaN in GPU attention output {tag}"
+    bad = np.abs(g - ref) > ATOL + RTOL * np.abs(ref) + slack
+    assert not bad.any(), f"FP8-math attention outside the widened gate {tag}: {int(bad.sum())} elements, {attn_stats(gpu, ref)}"
