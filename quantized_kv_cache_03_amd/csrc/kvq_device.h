@@ -122,13 +122,15 @@ __device__ __forceinline__ half2_t e4m3fnuz_x2_to_f16(uint32_t w) {
     return __builtin_bit_cast(half2_t, __builtin_bit_cast(uint32_t, sh) & 0xBF80BF80u);
 }
 
-// INT8 -> fp16: put each signed byte in the low byte of a half with high byte 0x64 and its sign
-// bit flipped, which is the binary16 number 1024 + (q + 128); subtracting 1152 leaves q exactly
-// (all integers below 2048 are exact in binary16).
+// INT8 -> fp16: put each signed byte, its sign bit flipped, in the low byte of a half with high
+// byte 0x64, which is the binary16 number 1024 + (q + 128); subtracting 1152 leaves q exactly
+// (all integers below 2048 are exact in binary16).  The sign flip is one XOR of the whole dword,
+// which the two pairs of a dword share; the byte permute then takes the 0x64 bytes from its other
+// operand.
 template <int SEL>
 __device__ __forceinline__ half2_t int8x2_to_f16(uint32_t w) {
-    constexpr uint32_t sel = (SEL == 0) ? 0x0C010C00u : 0x0C030C02u;
-    const uint32_t x = __builtin_amdgcn_perm(0u, w, sel) ^ 0x64806480u;
+    constexpr uint32_t sel = (SEL == 0) ? 0x04010400u : 0x04030402u;
+    const uint32_t x = __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, sel);
     return __builtin_bit_cast(half2_t, x) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
 }
 
