@@ -98,6 +98,9 @@ enum {
 #define KVQ_HEAD_DIM 128
 #define KVQ_BLOCK_SIZE 16
 #define KVQ_MAX_GROUP 16
+/* Largest max_context_len the attention calls accept (2^30 tokens: 256 GiB of codes per KV head,
+ * beyond one GPU's memory); token positions then stay within 32-bit integers everywhere. */
+#define KVQ_MAX_CONTEXT_LEN (1 << 30)
 
 /* Cache descriptor: a host struct read at call time; the pointers are device pointers. */
 typedef struct {
@@ -140,7 +143,8 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
  *   out[b][h] = sum_t softmax_t(sm_scale * q[b][h] . k^[t]) v^[t] over t < context_lens[b],
  *   with k^, v^ the dequantized rows of KV head h / (Hq / Hkv).  context_lens[b] == 0 gives zeros.
  *   sm_scale       : finite; 1/sqrt(128) is the usual value.
- *   max_context_len: host-side upper bound of context_lens (sizes the grid without a device read).
+ *   max_context_len: host-side upper bound of context_lens (sizes the grid without a device read),
+ *                    at most KVQ_MAX_CONTEXT_LEN.
  *   partition_size : how the work is split (flash-decoding split-K: each piece writes fp32 (max,
  *                    sum, unnormalized output) partials into `workspace`, and a second kernel merges
  *                    them with the log-sum-exp rule):
@@ -182,7 +186,8 @@ int kvq_decode_step(const kvq_cache *cache, const void *k_new, const void *v_new
  *   Decode is the case n_b = 1; a whole prompt is n_b = context_lens[b].
  *   q, out      : fp16 [num_q_rows][num_q_heads][128], device; num_q_rows = cu_q_lens[batch].
  *   cu_q_lens   : int32 [batch + 1] device row offsets.
- *   max_q_len   : host-side upper bound of n_b (sizes the grid), at most max_context_len.
+ *   max_q_len   : host-side upper bound of n_b (sizes the grid), at most max_context_len
+ *                 (itself at most KVQ_MAX_CONTEXT_LEN).
  *   Device-side contract: n_b <= context_lens[b] (rows of a sequence breaking it get zeros),
  *   n_b <= max_q_len.  No workspace; the result is bitwise deterministic. */
 int kvq_paged_prefill_attn(const kvq_cache *cache, const void *q, void *out, int32_t num_q_heads,
@@ -227,8 +232,8 @@ int kvq_quantize_q_fp8(const void *q, int32_t num_rows, void *codes, float *scal
 
 /* Dequantize the cache into dense fp32 [batch][Hkv][max_context_len][128] arrays for K and V:
  * each element is fl32(dec(code) * kv_scale) (FP8), fl32(q * s) (INT8) or fl32(q * s + zp)
- * (INT4), one rounding.  Slots t >= context_lens[b] are left untouched.  For inspection and tests;
- * not on the decode path. */
+ * (INT4), one rounding.  Slots t >= context_lens[b] are left untouched; max_context_len is at
+ * most KVQ_MAX_CONTEXT_LEN.  For inspection and tests; not on the decode path. */
 int kvq_dequant(const kvq_cache *cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
                 const int32_t *context_lens, int32_t batch, int32_t max_context_len, float *k_out,
                 float *v_out, void *stream);

@@ -99,7 +99,7 @@ Plan plan(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_context_len, int32
     Plan p;
     if (partition_size == KVQ_PARTITION_BALANCED) {
         const int64_t hw = Hq == Hkv ? Hq : Hkv;
-        const int64_t max_tiles = (int64_t)batch * ((max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE);
+        const int64_t max_tiles = (int64_t)batch * (((int64_t)max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE);
         int64_t nw = (kBalancedWaves + hw - 1) / hw;
         nw = std::min(nw, std::max<int64_t>(1, (max_tiles + kMinTiles - 1) / kMinTiles));
         nw = std::min<int64_t>(nw, 65535);
@@ -107,11 +107,13 @@ Plan plan(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_context_len, int32
         p.rows = (size_t)Hq * (size_t)(nw + batch);
         p.plan_bytes = (size_t)(batch + 2) * sizeof(int32_t);
     } else if (partition_size == 0) {
-        const int32_t whole = ((max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE) * KVQ_BLOCK_SIZE;
-        p.PS = whole > 0 ? whole : KVQ_BLOCK_SIZE;
+        const int64_t whole = (((int64_t)max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE) * KVQ_BLOCK_SIZE;
+        p.PS = whole > 0 ? (int32_t)whole : KVQ_BLOCK_SIZE;  // max_context_len <= KVQ_MAX_CONTEXT_LEN
     } else {
         p.PS = partition_size;
-        p.P = max_context_len > 0 ? (max_context_len + partition_size - 1) / partition_size : 1;
+        p.P = max_context_len > 0
+                  ? (int32_t)(((int64_t)max_context_len + partition_size - 1) / partition_size)
+                  : 1;
         if (p.P > 1) p.rows = (size_t)batch * (size_t)Hq * (size_t)p.P;
     }
     return p;
@@ -199,7 +201,7 @@ int kvq_append(const kvq_cache* cache, const void* k_new, const void* v_new,
 size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size) {
     if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-        max_context_len < 0)
+        max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
         return 0;
     if (partition_size != KVQ_PARTITION_BALANCED && (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE))
         return 0;
@@ -229,7 +231,8 @@ int decode_common(const char* where, bool fp8_math, const kvq_cache* cache, cons
         return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
-    if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
+    if (max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
+        return fail(KVQ_ERR_ARG, "max_context_len %d is outside [0, %d]", max_context_len, KVQ_MAX_CONTEXT_LEN);
     if (partition_size != KVQ_PARTITION_BALANCED &&
         (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0))
         return fail(KVQ_ERR_ARG,
@@ -358,7 +361,8 @@ int prefill_common(const char* where, bool fp8_math, const kvq_cache* cache, con
         return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
                     num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
-    if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
+    if (max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
+        return fail(KVQ_ERR_ARG, "max_context_len %d is outside [0, %d]", max_context_len, KVQ_MAX_CONTEXT_LEN);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
         return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",
                     max_context_len, max_blocks_per_seq, KVQ_BLOCK_SIZE);
@@ -441,7 +445,8 @@ int kvq_dequant(const kvq_cache* cache, const int32_t* block_tables, int32_t max
     if (st) return st;
     st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
     if (st) return st;
-    if (max_context_len < 0) return fail(KVQ_ERR_ARG, "max_context_len %d is negative", max_context_len);
+    if (max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
+        return fail(KVQ_ERR_ARG, "max_context_len %d is outside [0, %d]", max_context_len, KVQ_MAX_CONTEXT_LEN);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
         return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table", max_context_len);
     if (batch == 0 || max_context_len == 0) return ok();

@@ -93,6 +93,7 @@ CASES = [
     ("null table", {}, dict(bt=None), -1),
     ("null ctx", {}, dict(ctx=None), -1),
     ("ctx beyond table", {}, dict(L=65), -1),
+    ("ctx above the maximum", {}, dict(L=(1 << 30) + 16, mb=(1 << 26) + 1), -1),
     ("null q", {}, dict(q=None), -1),
     ("workspace missing", {}, dict(ps=16, L=64), -4),
     ("workspace small", {}, dict(ps=16, L=64, ws=0x50, wsb=100), -4),
@@ -116,6 +117,10 @@ def test_workspace_size(K):
     assert K.lib.kvq_decode_workspace_size(1, 3, 2, 100, 16) == 0    # Hq not a multiple of Hkv
     assert K.lib.kvq_decode_workspace_size(1, 2, 2, 100, 24) == 0    # not a multiple of 16
     assert K.lib.kvq_decode_workspace_size(1, 2, 2, 100, -2) == 0    # negative, not the balanced value
+    # the largest context the attention accepts, and one tile more (rejected)
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 1 << 30, 512) > 0
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, (1 << 30) + 16, 512) == 0
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 2**31 - 1, 0) == 0
 
 
 def test_workspace_size_balanced(K):
@@ -229,3 +234,18 @@ def test_read_probe_library_rejects_bad_arguments():
     assert f(0x10, 0x10, 0, 8, 0x20, None) == -1
     assert f(0x10, 0x10, 4, 0, 0x20, None) == -1
     assert f(0x10, None, 4, 8, 0x20, None) == -1
+
+
+def test_context_length_limit(K):
+    """max_context_len above KVQ_MAX_CONTEXT_LEN (2^30) is rejected before any device work, by the
+    decode, prefill and dequant calls alike; exactly the limit passes that check."""
+    c = _cache(K)
+    L = K.lib
+    big, mb = (1 << 30) + 16, (1 << 26) + 1
+    assert _attn(K, c, L=big, mb=mb, ps=0) == K.ERR_ARG
+    assert b"outside" in L.kvq_last_error()
+    assert L.kvq_paged_prefill_attn(ctypes.byref(c), 0x30, 0x40, 2, 0.1, 0x90, 4, 4, 0x10, mb, 0x20, 1, big,
+                                    None) == K.ERR_ARG
+    assert L.kvq_dequant(ctypes.byref(c), 0x10, mb, 0x20, 1, big, 0x50, 0x60, None) == K.ERR_ARG
+    # at the limit the call gets past the length checks and stops at the missing workspace
+    assert _attn(K, c, L=1 << 30, mb=1 << 26, ps=-1) == K.ERR_WORKSPACE
