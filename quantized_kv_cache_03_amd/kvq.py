@@ -99,10 +99,19 @@ def _check(status: int, where: str):
         raise KvqError(status, where)
 
 
+def _device_tensor(t: torch.Tensor, what: str) -> None:
+    """The library reads and writes device memory in the documented layouts: a host tensor, or a
+    strided view, would send a kernel to the wrong addresses."""
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be in GPU memory (got a tensor on {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
 def _ptr(t: torch.Tensor | None):
     if t is None:
         return None
-    assert t.is_contiguous(), "tensors passed to the library must be contiguous"
+    _device_tensor(t, "tensors passed to the library")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -156,6 +165,22 @@ class PagedKVCache:
         return PagedKVCache(dtype, k, v, ks, vs, float(kv_scale))
 
     def descriptor(self) -> KvqCache:
+        per = 2 if self.dtype == INT4 else 1
+        nb, hkv = self.k_cache.shape[0], self.k_cache.shape[1]
+        layout = {"k_cache": (self.k_cache, torch.uint8, (nb, hkv, HEAD_DIM // (16 * per), BLOCK_SIZE, 16)),
+                  "v_cache": (self.v_cache, torch.uint8, (nb, hkv, HEAD_DIM, BLOCK_SIZE // per))}
+        if self.dtype in (INT8, INT4):
+            sshape = (nb, hkv, BLOCK_SIZE) + ((2,) if self.dtype == INT4 else ())
+            for name, t in (("k_scale", self.k_scale), ("v_scale", self.v_scale)):
+                if t is None:
+                    raise ValueError(f"{name} is required for this cache dtype")
+                layout[name] = (t, torch.float32, sshape)
+        for name, (t, dt, shape) in layout.items():
+            _device_tensor(t, f"cache.{name}")
+            if t.dtype != dt or tuple(t.shape) != shape:
+                raise ValueError(f"cache.{name} must be {dt} {list(shape)} (got {t.dtype} {list(t.shape)})")
+            if t.device != self.k_cache.device:
+                raise ValueError("the cache tensors must be on one device")
         return KvqCache(self.dtype, self.k_cache.shape[0], BLOCK_SIZE, self.k_cache.shape[1], HEAD_DIM,
                         self.k_cache.data_ptr(), self.v_cache.data_ptr(),
                         self.k_scale.data_ptr() if self.k_scale is not None else None,
