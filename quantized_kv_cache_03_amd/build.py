@@ -1,21 +1,28 @@
-"""Build the HIP library ``libkvq.so`` for gfx950 with hipcc (in-tree, next to this file)."""
+"""Build the HIP library ``libkvq.so`` for gfx950 with hipcc (in-tree, next to this file).
+
+Each source is compiled to an object of its own, in parallel (the kernels of one file call no
+device code of another), and the objects are linked into the shared library.
+"""
 import glob
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvq.so")
-# the HBM read-rate probe the benchmark reports beside the roofline (not part of the cache's ABI)
-PROBE_SRC = os.path.join(HERE, "probe", "read_probe.hip")
+OBJ = os.path.join(HERE, "_build")
+# the HBM read-rate probe the benchmark reports beside the roofline, and the matrix-instruction
+# accumulation probe of the FP8-math tests (neither is part of the cache's ABI)
+PROBE_SRCS = [os.path.join(HERE, "probe", "read_probe.hip"), os.path.join(HERE, "probe", "mfma_probe.hip")]
 PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only.  Packed fp32 instructions are switched off for every kernel; fp32 division stays
 # correctly rounded (hipcc's default) and denormals are not flushed (the append path relies on both).
-FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
@@ -24,13 +31,27 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    for srcs, out in ((sources(), LIB), ([PROBE_SRC], PROBE_LIB)):
-        cmd = [HIPCC, *FLAGS, *extra_flags, *srcs, "-o", out + ".tmp"]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        os.replace(out + ".tmp", out)
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def _link(srcs, out, verbose, extra_flags, jobs):
+    os.makedirs(OBJ, exist_ok=True)
+    stem = os.path.splitext(os.path.basename(out))[0]
+    objs = [os.path.join(OBJ, f"{stem}.{os.path.splitext(os.path.basename(s))[0]}.o") for s in srcs]
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda so: _run([HIPCC, *FLAGS, *extra_flags, "-c", so[0], "-o", so[1]], verbose),
+                    zip(srcs, objs)))
+    _run([HIPCC, *FLAGS, *extra_flags, "-shared", *objs, "-o", out + ".tmp"], verbose)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False, extra_flags=(), jobs: int | None = None) -> str:
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    _link(sources(), LIB, verbose, list(extra_flags), jobs)
+    _link(PROBE_SRCS, PROBE_LIB, verbose, list(extra_flags), jobs)
     return LIB
 
 
