@@ -64,8 +64,8 @@
  *   - Device-side contract, not checked (violations are undefined behaviour): block ids are in
  *     [0, num_blocks); 0 <= context_lens[b] <= min(max_context_len, 16 * max_blocks_per_seq);
  *     every pointer addresses memory of the documented size on the current device.
- *   - Functions hold no state across calls (apart from the optional kernel-timing hook) and may be
- *     called concurrently on different streams for disjoint outputs.
+ *   - Functions hold no state across calls (apart from the calling thread's optional kernel-timing
+ *     session) and may be called concurrently on different streams for disjoint outputs.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -134,7 +134,10 @@ int kvq_append(const kvq_cache *cache, const void *k_new, const void *v_new,
 #define KVQ_PARTITION_BALANCED (-1)
 
 /* Bytes of split-K workspace kvq_paged_decode_attn needs for these sizes and partition_size
- * (0 when none is needed; also 0 for arguments the attention call would reject). */
+ * (0 when none is needed, and 0 for every combination of these arguments that the attention calls
+ * reject: the two share one validator).  Takes num_kv_heads, not head_dim (fixed at 128): the
+ * balanced split plans its waves per head row, whose count depends on the grouping Hq / Hkv.
+ * Does not change kvq_last_error(). */
 size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size);
 
@@ -255,8 +258,10 @@ const char *kvq_last_error(void);
  * (attention) kernel with a HIP event pair recorded in that kernel's own dispatch
  * (hipExtLaunchKernel), on the call's stream, for up to `capacity` calls.  kvq_timing_end() waits
  * for the events, returns the summed milliseconds and the number of timed launches, and releases
- * the events.  Events are created in kvq_timing_begin, outside any timed region.  Not thread-safe: one timing session at a time.  Returns KVQ_OK or
- * KVQ_ERR_ARG / KVQ_ERR_HIP. */
+ * the events.  Events are created in kvq_timing_begin, outside any timed region.  A session belongs
+ * to the thread that began it: only that thread's calls are timed, and threads may hold sessions
+ * of their own at the same time (a thread that exits with a session open leaks its events).
+ * Returns KVQ_OK or KVQ_ERR_ARG / KVQ_ERR_HIP. */
 int kvq_timing_begin(int32_t capacity);
 int kvq_timing_end(double *main_ms_total, int32_t *main_count);
 

@@ -68,6 +68,36 @@ int check_common(const int32_t* block_tables, int32_t max_blocks_per_seq, const 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The checks of the decode calls that depend only on the sizes kvq_decode_workspace_size also
+// takes (one validator, so that the size query is 0 exactly for sizes the calls reject).
+int check_decode_sizes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                       int32_t partition_size) {
+    if (batch < 0) return fail(KVQ_ERR_ARG, "batch %d is negative", batch);
+    if (num_kv_heads <= 0) return fail(KVQ_ERR_SHAPE, "num_kv_heads %d must be positive", num_kv_heads);
+    if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+        return fail(KVQ_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    if (num_q_heads / num_kv_heads > KVQ_MAX_GROUP)
+        return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d", num_q_heads / num_kv_heads,
+                    KVQ_MAX_GROUP);
+    if (max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
+        return fail(KVQ_ERR_ARG, "max_context_len %d is outside [0, %d]", max_context_len, KVQ_MAX_CONTEXT_LEN);
+    if (partition_size != KVQ_PARTITION_BALANCED &&
+        (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0))
+        return fail(KVQ_ERR_ARG,
+                    "partition_size %d must be KVQ_PARTITION_BALANCED (-1), 0 or a positive multiple of %d",
+                    partition_size, KVQ_BLOCK_SIZE);
+    if (batch > 65535 || num_q_heads > 65535)
+        return fail(KVQ_ERR_SHAPE, "batch and num_q_heads must be at most 65535");
+    if (partition_size > 0) {
+        const int64_t P = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+        if (P > 65535)
+            return fail(KVQ_ERR_SHAPE, "%lld partitions of %d tokens exceed the grid limit 65535",
+                        (long long)P, partition_size);
+    }
+    return KVQ_OK;
+}
+
 // FP8 math multiplies the E4M3 query codes with the cache's own codes on the OCP FP8 matrix cores.
 int check_fp8_math(const kvq_cache* c) {
     if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2)
@@ -127,14 +157,15 @@ size_t plan_workspace_bytes(const Plan& p) {
            2 * align256(p.rows * sizeof(float));
 }
 
-// kernel-timing hook state
+// Kernel-timing hook state: one session per calling thread (only that thread's calls are timed,
+// and sessions on different threads never touch each other's events).
 struct Timing {
     bool active = false;
     int32_t capacity = 0;
     int32_t used = 0;
     std::vector<hipEvent_t> ev;  // 2 per call: before and after the partition kernel
 };
-Timing g_timing;
+thread_local Timing g_timing;
 
 void timing_release() {
     for (hipEvent_t e : g_timing.ev)
@@ -200,11 +231,13 @@ int kvq_append(const kvq_cache* cache, const void* k_new, const void* v_new,
 
 size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size) {
-    if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
-        max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
-        return 0;
-    if (partition_size != KVQ_PARTITION_BALANCED && (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE))
-        return 0;
+    if (batch <= 0) return 0;
+    // a size query is not a failed call: the thread's last error stays as it was
+    char saved[sizeof(g_err)];
+    memcpy(saved, g_err, sizeof(g_err));
+    const int st = check_decode_sizes(batch, num_q_heads, num_kv_heads, max_context_len, partition_size);
+    memcpy(g_err, saved, sizeof(g_err));
+    if (st != KVQ_OK) return 0;
     return plan_workspace_bytes(plan(batch, num_q_heads, num_kv_heads, max_context_len, partition_size));
 }
 
@@ -224,31 +257,17 @@ int decode_common(const char* where, bool fp8_math, const kvq_cache* cache, cons
     if (fp8_math && (st = check_fp8_math(cache))) return st;
     st = check_common(block_tables, max_blocks_per_seq, context_lens, batch);
     if (st) return st;
-    if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads != 0)
-        return fail(KVQ_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
-                    num_q_heads, cache->num_kv_heads);
-    if (num_q_heads / cache->num_kv_heads > KVQ_MAX_GROUP)
-        return fail(KVQ_ERR_SHAPE, "query heads per KV head (%d) above %d",
-                    num_q_heads / cache->num_kv_heads, KVQ_MAX_GROUP);
+    st = check_decode_sizes(batch, num_q_heads, cache->num_kv_heads, max_context_len, partition_size);
+    if (st) return st;
     if (!isfinite(sm_scale)) return fail(KVQ_ERR_ARG, "sm_scale must be finite");
-    if (max_context_len < 0 || max_context_len > KVQ_MAX_CONTEXT_LEN)
-        return fail(KVQ_ERR_ARG, "max_context_len %d is outside [0, %d]", max_context_len, KVQ_MAX_CONTEXT_LEN);
-    if (partition_size != KVQ_PARTITION_BALANCED &&
-        (partition_size < 0 || partition_size % KVQ_BLOCK_SIZE != 0))
-        return fail(KVQ_ERR_ARG,
-                    "partition_size %d must be KVQ_PARTITION_BALANCED (-1), 0 or a positive multiple of %d",
-                    partition_size, KVQ_BLOCK_SIZE);
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * KVQ_BLOCK_SIZE)
         return fail(KVQ_ERR_ARG, "max_context_len %d exceeds the block table (%d blocks of %d)",
                     max_context_len, max_blocks_per_seq, KVQ_BLOCK_SIZE);
     if (batch == 0) return ok();
     if (!q || !out) return fail(KVQ_ERR_ARG, "q / out is NULL");
     if ((k_new == nullptr) != (v_new == nullptr)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
-    if (batch > 65535 || num_q_heads > 65535)
-        return fail(KVQ_ERR_SHAPE, "batch and num_q_heads must be at most 65535");
 
     const Plan p = plan(batch, num_q_heads, cache->num_kv_heads, max_context_len, partition_size);
-    if (p.P > 65535) return fail(KVQ_ERR_SHAPE, "%d partitions exceed the grid limit 65535", p.P);
     const size_t need = plan_workspace_bytes(p);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVQ_ERR_WORKSPACE, "split-K workspace of %zu bytes needed, %zu given%s", need,
@@ -340,6 +359,7 @@ int kvq_decode_step_fp8math(const kvq_cache* cache, const void* k_new, const voi
                          sm_scale, block_tables, max_blocks_per_seq, context_lens, batch,
                          max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
+
 
 }  // extern "C"
 

@@ -108,6 +108,32 @@ def _device_tensor(t: torch.Tensor, what: str) -> None:
         raise ValueError(f"{what} must be contiguous")
 
 
+def _tensor(t: torch.Tensor, what: str, dtype: torch.dtype, shape=None, device=None) -> None:
+    """Check a caller tensor against the layout the library will read or write: GPU memory,
+    contiguous, the dtype, the shape (None entries match any extent) and the cache's device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    _device_tensor(t, what)
+    if t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype} (got {t.dtype})")
+    if shape is not None and (t.dim() != len(shape) or
+                              any(e is not None and t.shape[i] != e for i, e in enumerate(shape))):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{what} must have shape {want} (got {list(t.shape)})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, the cache on {device}")
+
+
+def _tables(block_tables, context_lens, device, batch=None):
+    """block_tables int32 [batch][max_blocks], context_lens int32 [batch]; returns batch."""
+    _tensor(context_lens, "context_lens", torch.int32, (batch,), device)
+    b = context_lens.shape[0]
+    _tensor(block_tables, "block_tables", torch.int32, (b, None), device)
+    if block_tables.shape[1] < 1:
+        raise ValueError("block_tables needs at least one column")
+    return b
+
+
 def _ptr(t: torch.Tensor | None):
     if t is None:
         return None
@@ -191,14 +217,21 @@ class PagedKVCache:
 def append(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, block_tables: torch.Tensor,
            context_lens: torch.Tensor, cu_new_lens: torch.Tensor | None = None,
            num_new_rows: int | None = None, stream=None) -> None:
-    """kvq_append: fp16 rows [T][Hkv][128] -> their paged slots (post-append context_lens)."""
-    assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
-    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
-    batch = context_lens.shape[0]
-    T = k_new.shape[0] if num_new_rows is None else num_new_rows
-    if cu_new_lens is not None:
-        assert cu_new_lens.dtype == torch.int32
+    """kvq_append: fp16 rows [T][Hkv][128] -> their paged slots (post-append context_lens).
+    With cu_new_lens (int32 [B+1], device), num_new_rows must equal cu_new_lens[B] (default: all of
+    k_new's rows); without it there is one row per sequence."""
     d = cache.descriptor()
+    dev = cache.k_cache.device
+    batch = _tables(block_tables, context_lens, dev)
+    _tensor(k_new, "k_new", torch.float16, (None, cache.num_kv_heads, HEAD_DIM), dev)
+    _tensor(v_new, "v_new", torch.float16, tuple(k_new.shape), dev)
+    T = k_new.shape[0] if num_new_rows is None else int(num_new_rows)
+    if not 0 <= T <= k_new.shape[0]:
+        raise ValueError(f"num_new_rows {T} outside [0, {k_new.shape[0]}] (the rows of k_new)")
+    if cu_new_lens is not None:
+        _tensor(cu_new_lens, "cu_new_lens", torch.int32, (batch + 1,), dev)
+    elif T != batch:
+        raise ValueError(f"without cu_new_lens there is one new row per sequence ({batch}), not {T}")
     _check(lib.kvq_append(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(cu_new_lens), T,
                           _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), batch,
                           _stream(stream)), "kvq_append")
@@ -238,19 +271,32 @@ def paged_decode_attn_fp8math(cache: PagedKVCache, q: torch.Tensor, block_tables
                         max_context_len, sm_scale, partition_size, workspace, out, stream)
 
 
+def _decode_args(cache, q, block_tables, context_lens, max_context_len, partition_size, workspace, out):
+    """Checks shared by the decode calls -> (descriptor, out, workspace, workspace bytes)."""
+    d = cache.descriptor()
+    dev = cache.k_cache.device
+    B = _tables(block_tables, context_lens, dev)
+    _tensor(q, "q", torch.float16, (B, None, HEAD_DIM), dev)
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _tensor(out, "out", torch.float16, tuple(q.shape), dev)
+    need = workspace_size(B, Hq, cache.num_kv_heads, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _tensor(workspace, "workspace", torch.uint8, (None,), dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    return d, out, workspace, ws_bytes
+
+
 def _decode_attn(name, cache, q, block_tables, context_lens, max_context_len, sm_scale, partition_size,
                  workspace, out, stream):
-    assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
+    d, out, workspace, ws_bytes = _decode_args(cache, q, block_tables, context_lens, max_context_len,
+                                               partition_size, workspace, out)
     B, Hq, _ = q.shape
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
-    if out is None:
-        out = torch.empty_like(q)
-    need = workspace_size(B, Hq, cache.num_kv_heads, max_context_len, partition_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    d = cache.descriptor()
     _check(getattr(lib, name)(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
                               _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
                               int(max_context_len), int(partition_size), _ptr(workspace), ws_bytes,
@@ -280,19 +326,14 @@ def decode_step_fp8math(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.T
 
 def _decode_step(name, cache, k_new, v_new, q, block_tables, context_lens, max_context_len, sm_scale,
                  partition_size, workspace, out, stream):
-    assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM
-    assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
+    d, out, workspace, ws_bytes = _decode_args(cache, q, block_tables, context_lens, max_context_len,
+                                               partition_size, workspace, out)
     B, Hq, _ = q.shape
-    assert k_new.shape == (B, cache.num_kv_heads, HEAD_DIM) and v_new.shape == k_new.shape
+    dev = cache.k_cache.device
+    _tensor(k_new, "k_new", torch.float16, (B, cache.num_kv_heads, HEAD_DIM), dev)
+    _tensor(v_new, "v_new", torch.float16, (B, cache.num_kv_heads, HEAD_DIM), dev)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
-    if out is None:
-        out = torch.empty_like(q)
-    need = workspace_size(B, Hq, cache.num_kv_heads, max_context_len, partition_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    d = cache.descriptor()
     _check(getattr(lib, name)(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), Hq,
                               float(sm_scale), _ptr(block_tables), block_tables.shape[1],
                               _ptr(context_lens), B, int(max_context_len), int(partition_size),
@@ -321,14 +362,17 @@ def paged_prefill_attn_fp8math(cache: PagedKVCache, q: torch.Tensor, cu_q_lens: 
 
 def _prefill(name, cache, q, cu_q_lens, block_tables, context_lens, max_context_len, max_q_len,
              sm_scale, out, stream):
-    assert q.dtype == torch.float16 and q.dim() == 3 and q.shape[-1] == HEAD_DIM
+    d = cache.descriptor()
+    dev = cache.k_cache.device
+    B = _tables(block_tables, context_lens, dev)
+    _tensor(q, "q", torch.float16, (None, None, HEAD_DIM), dev)
+    _tensor(cu_q_lens, "cu_q_lens", torch.int32, (B + 1,), dev)
     T, Hq, _ = q.shape
-    B = context_lens.shape[0]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty_like(q)
-    d = cache.descriptor()
+    _tensor(out, "out", torch.float16, tuple(q.shape), dev)
     _check(getattr(lib, name)(ctypes.byref(d), _ptr(q), _ptr(out), Hq, float(sm_scale),
                               _ptr(cu_q_lens), T, int(max_q_len), _ptr(block_tables),
                               block_tables.shape[1], _ptr(context_lens), B, int(max_context_len),
@@ -338,7 +382,9 @@ def _prefill(name, cache, q, cu_q_lens, block_tables, context_lens, max_context_
 
 def quantize_q_fp8(q: torch.Tensor, stream=None):
     """kvq_quantize_q_fp8: fp16 rows [..., 128] -> (E4M3 codes uint8 [..., 128], fp32 scales [...])."""
-    assert q.dtype == torch.float16 and q.shape[-1] == HEAD_DIM and q.is_contiguous()
+    _tensor(q, "q", torch.float16)
+    if q.dim() < 1 or q.shape[-1] != HEAD_DIM:
+        raise ValueError(f"q must have rows of {HEAD_DIM} (got {list(q.shape)})")
     codes = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
     scales = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     rows = q.numel() // HEAD_DIM
@@ -351,14 +397,16 @@ def dequant(cache: PagedKVCache, block_tables: torch.Tensor, context_lens: torch
             max_context_len: int, k_out: torch.Tensor | None = None, v_out: torch.Tensor | None = None,
             stream=None):
     """kvq_dequant -> (k, v) fp32 [B][Hkv][max_context_len][128] (slots past a context untouched)."""
-    B = context_lens.shape[0]
-    shape = (B, cache.num_kv_heads, max_context_len, HEAD_DIM)
+    d = cache.descriptor()
     dev = cache.k_cache.device
+    B = _tables(block_tables, context_lens, dev)
+    shape = (B, cache.num_kv_heads, max_context_len, HEAD_DIM)
     if k_out is None:
         k_out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
     if v_out is None:
         v_out = torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
-    d = cache.descriptor()
+    _tensor(k_out, "k_out", torch.float32, shape, dev)
+    _tensor(v_out, "v_out", torch.float32, shape, dev)
     _check(lib.kvq_dequant(ctypes.byref(d), _ptr(block_tables), block_tables.shape[1],
                            _ptr(context_lens), B, int(max_context_len), _ptr(k_out), _ptr(v_out),
                            _stream(stream)), "kvq_dequant")

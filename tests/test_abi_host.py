@@ -118,9 +118,44 @@ def test_workspace_size(K):
     assert K.lib.kvq_decode_workspace_size(1, 2, 2, 100, 24) == 0    # not a multiple of 16
     assert K.lib.kvq_decode_workspace_size(1, 2, 2, 100, -2) == 0    # negative, not the balanced value
     # the largest context the attention accepts, and one tile more (rejected)
-    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 1 << 30, 512) > 0
-    assert K.lib.kvq_decode_workspace_size(1, 2, 2, (1 << 30) + 16, 512) == 0
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 1 << 30, -1) > 0
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, (1 << 30) + 16, -1) == 0
     assert K.lib.kvq_decode_workspace_size(1, 2, 2, 2**31 - 1, 0) == 0
+    # 0 exactly where the attention call rejects the sizes: at most 65535 partitions ...
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 65535 * 512, 512) > 0
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 65535 * 512 + 1, 512) == 0
+    assert K.lib.kvq_decode_workspace_size(1, 2, 2, 1 << 30, 512) == 0
+    # ... at most 16 query heads per KV head, and batch / query heads within the grid
+    assert K.lib.kvq_decode_workspace_size(4, 32, 2, 4096, 512) > 0
+    assert K.lib.kvq_decode_workspace_size(4, 34, 2, 4096, 512) == 0
+    assert K.lib.kvq_decode_workspace_size(65535, 2, 2, 4096, -1) > 0
+    assert K.lib.kvq_decode_workspace_size(65536, 2, 2, 4096, -1) == 0
+    assert K.lib.kvq_decode_workspace_size(1, 65536, 65536, 4096, 512) == 0
+
+
+def test_workspace_size_agrees_with_the_call(K):
+    """For every size combination, the workspace query is 0 for the sizes the attention call rejects,
+    and positive for the accepted ones that need a workspace (a balanced split, or more than one
+    fixed partition).  q and out are NULL, so an accepted call stops at that check: no launch."""
+    L = K.lib
+    c = _cache(K)
+    for B in (1, 3, 65535, 65536):
+        for Hq, Hkv in ((2, 2), (32, 2), (34, 2), (2, 1), (17, 1), (16, 1)):
+            c.num_kv_heads = Hkv
+            for ctx in (0, 16, 4096, 65535 * 64, 65535 * 64 + 1, 1 << 30, (1 << 30) + 1):
+                mb = (ctx + 15) // 16 + 1
+                for ps in (-1, -2, 0, 16, 24, 64, 512):
+                    n = L.kvq_decode_workspace_size(B, Hq, Hkv, ctx, ps)
+                    rc = L.kvq_paged_decode_attn(ctypes.byref(c), None, None, Hq, 0.1, 0x10, mb, 0x20, B, ctx,
+                                                 ps, None, 0, None)
+                    accepted = rc == K.ERR_ARG and L.kvq_last_error() == b"q / out is NULL"
+                    case = (B, Hq, Hkv, ctx, ps, rc, L.kvq_last_error())
+                    if not accepted:
+                        assert rc in (K.ERR_ARG, K.ERR_SHAPE) and n == 0, case
+                    elif ps == -1 or (ps > 0 and ctx > ps):
+                        assert n > 0, case
+                    else:
+                        assert n == 0, case
 
 
 def test_workspace_size_balanced(K):

@@ -27,3 +27,84 @@ def test_int_caches_need_their_scales():
     c2 = K.PagedKVCache(c.dtype, c.k_cache, c.v_cache, None, c.v_scale, 1.0)
     with pytest.raises(ValueError, match="k_scale is required"):
         c2.descriptor()
+
+
+@pytest.fixture
+def host_binding(monkeypatch):
+    """The binding with its GPU-memory test lifted (host tensors stand in for device ones) and a
+    library stub that fails the test if any entry point but the workspace-size query is reached:
+    every case below must be refused by the binding's own checks."""
+    real = K.lib
+
+    class Stub:
+        def __getattr__(self, name):
+            if name in ("kvq_decode_workspace_size", "kvq_dtype_from_string", "kvq_last_error",
+                        "kvq_status_string"):
+                return getattr(real, name)
+            raise AssertionError(f"the library was called ({name}) with arguments the binding should refuse")
+
+    def contiguous_only(t, what):
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous")
+
+    monkeypatch.setattr(K, "lib", Stub())
+    monkeypatch.setattr(K, "_device_tensor", contiguous_only)
+    return K
+
+
+def _t(shape, dtype=torch.float16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_checks_every_caller_tensor(host_binding):
+    K = host_binding
+    c = K.PagedKVCache.allocate("fp8_e4m3", 8, 2, 1.0, device="cpu")
+    bt, ctx = _t((3, 4), torch.int32), _t((3,), torch.int32)
+    q = _t((3, 4, 128))
+    bad_decode = [
+        dict(out=_t((3, 4, 64))),                       # out too small
+        dict(out=_t((3, 4, 128), torch.float32)),       # out of the wrong dtype
+        dict(q=_t((3, 4, 64))),                         # rows of 64
+        dict(q=_t((2, 4, 128))),                        # q rows != batch
+        dict(block_tables=_t((2, 4), torch.int32)),     # table rows != batch
+        dict(block_tables=_t((3, 4), torch.int64)),
+        dict(context_lens=_t((3,), torch.int64)),
+        dict(workspace=_t((1024,), torch.float32), partition_size=16),
+        dict(q=_t((3, 4, 128))[:, ::2]),                # strided view
+    ]
+    for over in bad_decode:
+        args = dict(q=q, block_tables=bt, context_lens=ctx, max_context_len=64, partition_size=16,
+                    workspace=None, out=None)
+        args.update(over)
+        with pytest.raises(ValueError):
+            K.paged_decode_attn(c, args["q"], args["block_tables"], args["context_lens"],
+                                args["max_context_len"], partition_size=args["partition_size"],
+                                workspace=args["workspace"], out=args["out"])
+    kn = _t((3, 2, 128))
+    for kbad in (_t((3, 1, 128)), _t((2, 2, 128)), _t((3, 2, 128), torch.float32)):
+        with pytest.raises(ValueError):
+            K.decode_step(c, kbad, kn, q, bt, ctx, 64)
+        with pytest.raises(ValueError):
+            K.decode_step(c, kn, kbad, q, bt, ctx, 64)
+    # prefill: cu_q_lens of batch + 1 entries, out of q's shape
+    cu = _t((4,), torch.int32)
+    with pytest.raises(ValueError):
+        K.paged_prefill_attn(c, _t((10, 4, 128)), _t((3,), torch.int32), bt, ctx, 64, 5)
+    with pytest.raises(ValueError):
+        K.paged_prefill_attn(c, _t((10, 4, 128)), cu, bt, ctx, 64, 5, out=_t((9, 4, 128)))
+    # dequant outputs of [batch][Hkv][max_context_len][128] fp32
+    with pytest.raises(ValueError):
+        K.dequant(c, bt, ctx, 64, k_out=_t((3, 2, 63, 128), torch.float32))
+    with pytest.raises(ValueError):
+        K.dequant(c, bt, ctx, 64, v_out=_t((3, 2, 64, 128), torch.float16))
+    # append: rows of [T][Hkv][128], num_new_rows within them, cu of batch + 1
+    with pytest.raises(ValueError):
+        K.append(c, _t((3, 1, 128)), _t((3, 1, 128)), bt, ctx)
+    with pytest.raises(ValueError):
+        K.append(c, _t((5, 2, 128)), _t((5, 2, 128)), bt, ctx, cu_new_lens=cu, num_new_rows=6)
+    with pytest.raises(ValueError):
+        K.append(c, _t((5, 2, 128)), _t((5, 2, 128)), bt, ctx, cu_new_lens=_t((3,), torch.int32))
+    with pytest.raises(ValueError):
+        K.append(c, _t((5, 2, 128)), _t((5, 2, 128)), bt, ctx)  # one row per sequence without cu
+    with pytest.raises(ValueError):
+        K.quantize_q_fp8(_t((4, 64)))
