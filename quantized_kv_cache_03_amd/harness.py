@@ -27,9 +27,11 @@ def kv_bytes_per_token(dtype: str) -> int:
 class DeviceCase:
     def __init__(self, w: W.Workload, device: str = "cuda", spare_blocks: int = 0,
                  keep_host_rows: bool = False, poison: bool = True, verbose: bool = False,
-                 prefill_last: bool = True):
+                 prefill_last: bool = True, threads: int = 1, rows=None):
         """prefill_last=False leaves each sequence's last slot unwritten (poisoned), so the first
-        decode step is the only writer of the appended token."""
+        decode step is the only writer of the appended token.  threads: host threads drawing the
+        rows (the same rows for any count).  rows: the (k, v, cu) that W.all_kv_rows gives for
+        this workload's recipe, drawn once and shared by several cases (kept as the host rows)."""
         self.w = w
         self.device = device
         self.ctx = W.context_lens(w)
@@ -38,10 +40,13 @@ class DeviceCase:
         self.max_ctx = int(self.ctx.max()) if self.B else 0
         self.channels = W.outlier_channels(w)
         total_vals = int(self.ctx.sum()) * w.num_kv_heads * W.HEAD_DIM * 2
-        in_memory = keep_host_rows or total_vals <= (1 << 31)
+        in_memory = keep_host_rows or rows is not None or total_vals <= (1 << 31)
         self.k_host = self.v_host = None
+        if rows is not None:
+            keep_host_rows = True
         if in_memory:
-            k, v, cu = W.all_kv_rows(w, self.ctx)
+            k, v, cu = rows if rows is not None else W.all_kv_rows(w, self.ctx, threads=threads)
+            assert k.shape[0] == int(self.ctx.sum()) and v.shape == k.shape
             self.kv_scale = W.kv_scale(w, k, v)
             if keep_host_rows:
                 self.k_host, self.v_host, self.cu = k, v, cu

@@ -68,6 +68,9 @@ WORKLOADS = {
                                     ("lognormal", 2048, 1.0, 16384), outliers=4),
     "llama3-70b-gqa-e4m3-32k": Workload("llama3-70b-gqa-e4m3-32k", 5, 16, 64, 8, "fp8_e4m3",
                                         ("fixed", 32768), scale_rule="amax/448"),
+    # the 32k GQA-8 batch at its own work split: fixed 512-token partitions, then the merge kernel
+    "llama3-70b-gqa-e4m3-32k-p512": Workload("llama3-70b-gqa-e4m3-32k-p512", 5, 16, 64, 8, "fp8_e4m3",
+                                             ("fixed", 32768), scale_rule="amax/448", partition_size=512),
     # the AMD E4M3 flavour (FNUZ) on the Llama-2-7B and Llama-3-70B shapes
     "llama2-7b-mha-e4m3fnuz": Workload("llama2-7b-mha-e4m3fnuz", 2, 32, 32, 32, "fp8_e4m3fnuz",
                                        ("uniform", 512, 4096), table="shuffled",
@@ -157,18 +160,28 @@ def kv_rows(w: Workload, b: int, n: int, channels: np.ndarray | None = None):
     return k.astype(np.float16), v.astype(np.float16)
 
 
-def all_kv_rows(w: Workload, ctx: np.ndarray):
-    """All sequences' rows concatenated: (k [T][Hkv][128], v [T][Hkv][128], cu [B+1])."""
+def all_kv_rows(w: Workload, ctx: np.ndarray, threads: int = 1):
+    """All sequences' rows concatenated: (k [T][Hkv][128], v [T][Hkv][128], cu [B+1]).  Each
+    sequence has its own stream, so `threads` > 1 draws them concurrently with the same result."""
     ch = outlier_channels(w)
     cu = np.zeros(len(ctx) + 1, np.int32)
     cu[1:] = np.cumsum(ctx)
     T = int(cu[-1])
     k = np.empty((T, w.num_kv_heads, HEAD_DIM), np.float16)
     v = np.empty((T, w.num_kv_heads, HEAD_DIM), np.float16)
-    for b, n in enumerate(ctx):
-        kb, vb = kv_rows(w, b, int(n), ch)
+
+    def one(b):
+        kb, vb = kv_rows(w, b, int(ctx[b]), ch)
         k[cu[b]:cu[b + 1]] = kb
         v[cu[b]:cu[b + 1]] = vb
+
+    if threads <= 1:
+        for b in range(len(ctx)):
+            one(b)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(len(ctx))))
     return k, v, cu
 
 

@@ -1,0 +1,221 @@
+"""The accumulation of the two matrix instructions the attention kernels use, held on the GPU to the
+error models stated in gpu_common (mfma_fp8_bound, mfma_f16_bound), against exact products.
+
+libkvq_probe.so issues one instruction per 16x16 problem in the kernels' operand layout:
+- v_mfma_scale_f32_16x16x128_f8f6f4 (FP8 math, unit scales).  Its model: within each group of 8
+  consecutive k-slots, products aligned to the group's largest exponent and cut to 2^(E_g - 13).
+  The FP8-math tolerance (gpu_common.fp8_math_slack) is that bound carried through the softmax.
+  Adversarial operands (one large product and many same-sign small ones) reach the bound, and a
+  model one bit wider (2^(E_g - 14)) is violated by them: the 13 bits are the instruction's width.
+- v_mfma_f32_16x16x32_f16 (fp16 math): within groups of 8, 2^(E_g - 24); group sums and
+  accumulator to 2^(E - 23).  Exponents come from the operands' exponent fields, so a subnormal
+  fp16 operand (n * 2^-24) keeps only about 14 bits of its products: the reason the INT4 kernels
+  give the matrix cores their codes as normal fp16 integers.
+
+Inputs: seeded normal rows under the cache's calibrations, outlier channels of gain 200, every
+finite code, rows built to cancel, subnormal code operands, and the adversarial sets.  Each case
+prints its worst error as a share of the model's bound.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import pytest
+
+import gpu_common as GC
+import oracle
+from gpu_common import mfma_f16_bound, mfma_fp8_bound, say
+
+pytestmark = pytest.mark.gpu
+
+N = 256  # problems per random case
+
+
+@pytest.fixture(scope="module")
+def P():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "quantized_kv_cache_03_amd", "libkvq_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.kvq_probe_mfma_f16.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p]
+    lib.kvq_probe_mfma_f16.restype = ctypes.c_int
+    lib.kvq_probe_mfma_fp8.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.kvq_probe_mfma_fp8.restype = ctypes.c_int
+    return lib
+
+
+def _run(fn, a, b, c_in, *fmts):
+    import torch
+    ad, bd = torch.from_numpy(np.ascontiguousarray(a)).cuda(), torch.from_numpy(np.ascontiguousarray(b)).cuda()
+    cd = torch.from_numpy(np.ascontiguousarray(c_in)).cuda()
+    out = torch.empty_like(cd)
+    n = a.shape[0]
+    assert a.shape[:2] == (n, 16) and b.shape[:2] == (n, 16) and c_in.shape == (n, 16, 16)
+    rc = fn(ad.data_ptr(), bd.data_ptr(), *fmts, cd.data_ptr(), out.data_ptr(), n,
+            torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _exact(av, bv, c_in):
+    """C_in + A B per problem [n][16 i][16 j], each the fp64 rounding of the exact sum."""
+    n = av.shape[0]
+    out = np.empty((n, 16, 16), np.float64)
+    for p in range(n):
+        prod = av[p][:, None, :] * bv[p][None, :, :]  # exact in fp64
+        for i in range(16):
+            for j in range(16):
+                out[p, i, j] = math.fsum([float(c_in[p, i, j]), *prod[i, j]])
+    return out
+
+
+E4 = oracle.fp8_decode(oracle.E4M3, np.arange(256, dtype=np.uint8))
+
+
+def _fp8_codes(r, fmt, kind, n):
+    """[n][16][128] codes of one distribution."""
+    if kind == "uniform":
+        c = r.integers(0, 256, size=(n, 16, 128)).astype(np.uint8)
+        c[~np.isfinite(oracle.fp8_decode(fmt, c))] = 0  # NaN / inf codes
+        return c
+    x = r.standard_normal((n, 16, 128)).astype(np.float32)
+    if kind == "outliers":
+        for p in range(n):
+            for i in range(16):
+                x[p, i, r.choice(128, size=int(r.integers(1, 9)), replace=False)] *= 200.0
+    if kind == "cancel":
+        x[..., 64:] = -x[..., :64] * np.float32(1.0 + 2.0 ** -3)
+    x16 = x.astype(np.float16)
+    if fmt == oracle.E5M2:
+        return oracle.fp8_quantize(oracle.E5M2, x16, 1.0)
+    amax = float(np.abs(x16).max())
+    return oracle.fp8_quantize(oracle.E4M3, x16, float(np.float32(amax) / np.float32(448.0)))
+
+
+def _fp8_adversarial():
+    """Problem p, row i: one product 2^8 in slot p's big slot and 127 same-sign products
+    m * 2^(6 - i) (m in {1, 1.875, 1.5}; 0 where not an E4M3 value); column j keeps all slots (j = 0),
+    one group of 16 (j = 1..8) or one group of 8 (j = 9..15), plus the big slot."""
+    n = 24
+    a = np.zeros((n, 16, 128), np.uint8)
+    b = np.zeros((n, 16, 128), np.uint8)
+    code = {float(v): c for c, v in enumerate(E4) if np.isfinite(v)}
+    for p in range(n):
+        big = [0, 1, 7, 8, 31, 32, 64, 127][p % 8]
+        m = [1.0, 1.875, 1.5][p // 8]
+        for i in range(16):
+            a[p, i, :] = code.get(m * 2.0 ** (6 - i), 0)
+            a[p, i, big] = code[256.0]
+        for j in range(16):
+            keep = np.zeros(128, bool)
+            if j == 0:
+                keep[:] = True
+            elif j <= 8:
+                keep[16 * (j - 1):16 * j] = True
+            else:
+                keep[8 * (j - 9):8 * (j - 9) + 8] = True
+            keep[big] = True
+            b[p, j, keep] = code[1.0]
+    return a, b
+
+
+FP8_CASES = [(f, k) for f in ("e4m3", "e5m2") for k in ("normal", "outliers", "uniform", "cancel")] + \
+            [("e4m3", "adversarial")]
+
+
+@pytest.mark.parametrize("fmt_a,kind", FP8_CASES, ids=[f"{f}-{k}" for f, k in FP8_CASES])
+def test_fp8_instruction_model(P, fmt_a, kind):
+    """A = K codes (E4M3 or E5M2), B = E4M3 query codes, zero accumulator (one instruction per tile,
+    as the FP8-math kernels issue it)."""
+    fa = oracle.E4M3 if fmt_a == "e4m3" else oracle.E5M2
+    if kind == "adversarial":
+        a, b = _fp8_adversarial()
+    else:
+        r = np.random.default_rng([7, fa, ["normal", "outliers", "uniform", "cancel"].index(kind)])
+        a = _fp8_codes(r, fa, kind, N)
+        b = _fp8_codes(r, oracle.E4M3, "uniform" if kind == "uniform" else "normal", N)
+    c_in = np.zeros((a.shape[0], 16, 16), np.float32)
+    got = _run(P.kvq_probe_mfma_fp8, a, b, c_in, 0 if fa == oracle.E4M3 else 1, 0)
+    av, bv = oracle.fp8_decode(fa, a), oracle.fp8_decode(oracle.E4M3, b)
+    ref = _exact(av, bv, c_in)
+    emin_a = -6 if fa == oracle.E4M3 else -14
+    bound = mfma_fp8_bound(av[:, :, None, :], bv[:, None, :, :], emin_a, -6, ref)
+    err = np.abs(got - ref)
+    share = float((err / np.maximum(bound, 1e-300)).max())
+    say(f"  FP8 {fmt_a} x E4M3 {kind}: worst error / model bound = {share:.3f}")
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= bound), f"worst share of the model bound {share:.3f}"
+    if kind == "adversarial":
+        # the model's width is the instruction's: one more bit would be violated
+        old = GC.FP8_GROUP_BITS
+        try:
+            GC.FP8_GROUP_BITS = old + 1
+            tighter = mfma_fp8_bound(av[:, :, None, :], bv[:, None, :, :], emin_a, -6, ref)
+        finally:
+            GC.FP8_GROUP_BITS = old
+        assert np.any(err > tighter)
+
+
+def _f16_operands(r, kind, n):
+    if kind == "normal":
+        a = r.standard_normal((n, 16, 32))
+        b = r.standard_normal((n, 16, 32))
+    elif kind == "wide":  # magnitudes over the whole normal fp16 range
+        a = r.standard_normal((n, 16, 32)) * np.exp2(r.integers(-14, 15, size=(n, 16, 32)))
+        b = r.standard_normal((n, 16, 32)) * np.exp2(r.integers(-14, 15, size=(n, 16, 32)))
+    elif kind == "subnormal-codes":  # 4-bit codes as fp16 subnormals (n * 2^-24) times queries
+        a = r.integers(0, 16, size=(n, 16, 32)) * 2.0 ** -24
+        b = r.standard_normal((n, 16, 32))
+    elif kind == "integer-codes":  # centred 4-bit codes as normal fp16 integers, as the kernels give them
+        a = r.integers(-15, 16, size=(n, 16, 32)).astype(np.float64)
+        b = r.standard_normal((n, 16, 32))
+    else:  # cancel
+        a = r.standard_normal((n, 16, 32))
+        a[..., 16:] = -a[..., :16]
+        b = np.ones((n, 16, 32)) + r.standard_normal((n, 16, 32)) * 2.0 ** -8
+    return np.clip(a, -65504, 65504).astype(np.float16), np.clip(b, -65504, 65504).astype(np.float16)
+
+
+def _f16_adversarial():
+    """One product 2^10 and 31 same-sign products m * 2^(-8 - i), accumulator 0 or 2^10."""
+    n = 24
+    a = np.zeros((n, 16, 32), np.float16)
+    b = np.ones((n, 16, 32), np.float16)
+    c = np.zeros((n, 16, 16), np.float32)
+    for p in range(n):
+        big = [0, 1, 7, 8, 15, 16, 24, 31][p % 8]
+        m = [1.0, 1.9990234375, 1.5][p // 8]
+        for i in range(16):
+            a[p, i, :] = np.float16(m * 2.0 ** (-8 - i))
+            a[p, i, big] = np.float16(1024.0)
+        c[p, :, 8:] = np.float32(1024.0)
+    return a, b, c
+
+
+F16_CASES = ["normal", "wide", "subnormal-codes", "integer-codes", "cancel", "adversarial"]
+
+
+@pytest.mark.parametrize("kind", F16_CASES)
+def test_f16_instruction_model(P, kind):
+    if kind == "adversarial":
+        a, b, c_in = _f16_adversarial()
+    else:
+        r = np.random.default_rng([8, F16_CASES.index(kind)])
+        a, b = _f16_operands(r, kind, N)
+        c_in = (r.standard_normal((N, 16, 16)) * (1e-5 if kind == "subnormal-codes" else 4.0)).astype(np.float32)
+    got = _run(P.kvq_probe_mfma_f16, a.view(np.uint16), b.view(np.uint16), c_in)
+    av, bv = a.astype(np.float64), b.astype(np.float64)
+    ref = _exact(av, bv, c_in)
+    bound = mfma_f16_bound(av[:, :, None, :], bv[:, None, :, :], c_in.astype(np.float64), ref)
+    err = np.abs(got - ref)
+    mag = np.abs(av[:, :, None, :] * bv[:, None, :, :]).sum(-1) + np.abs(c_in)
+    share = float((err / np.maximum(bound, 1e-300)).max())
+    say(f"  f16 {kind}: worst error / model bound = {share:.3f}; worst error / (u (|c| + sum |p|)) = "
+        f"{float((err / np.maximum(GC.U32 * mag, 1e-300)).max()):.1f}")
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= bound), f"worst share of the model bound {share:.3f}"
