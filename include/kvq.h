@@ -179,6 +179,26 @@ int kvq_decode_step(const kvq_cache *cache, const void *k_new, const void *v_new
                     int32_t max_context_len, int32_t partition_size, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* Size of the device scratch array kvq_decode_step_noalloc uses as its split-K workspace (64 MiB
+ * per GPU the library runs on, held until the process ends). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kvq_decode_step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments without workspace /
+ * workspace_bytes, the same kernels, and bitwise the same cache bytes and output as kvq_decode_step
+ * with a workspace.  The split-K workspace is a file-scope device array of
+ * KVQ_NOALLOC_SCRATCH_BYTES; sizes whose workspace (kvq_decode_workspace_size) exceeds it return
+ * KVQ_ERR_WORKSPACE before any device work.  The array's device address is looked up once per
+ * device, on that device's first call (the call then takes a lock; later calls only read the
+ * stored address).  The call allocates nothing.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (on different streams, or from different threads) race
+ * and may return wrong results; calls ordered on one stream are safe.  The array needs no
+ * clearing: each call writes every partial it reads. */
+int kvq_decode_step_noalloc(const kvq_cache *cache, const void *k_new, const void *v_new, const void *q,
+                            void *out, int32_t num_q_heads, float sm_scale, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t batch,
+                            int32_t max_context_len, int32_t partition_size, void *stream);
+
 /* Prefill / chunked-prefill attention over the paged 8-bit cache (the same formats and arithmetic
  * as kvq_paged_decode_attn: stored as FP8 or INT8, computed at higher precision):
  *   sequence b brings n_b = cu_q_lens[b+1] - cu_q_lens[b] query rows, the last n_b of its

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "kvq.h"
@@ -360,6 +361,62 @@ int kvq_decode_step_fp8math(const kvq_cache* cache, const void* k_new, const voi
                          max_context_len, partition_size, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The split-K workspace of kvq_decode_step_noalloc: one array per device, held until the process
+// ends.  Host code uses only the device address hipGetSymbolAddress gives for it (the array's
+// name is a host-side stand-in), taken once per device on that device's first call.
+__device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "kvq_decode_step_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(KVQ_ERR_ARG, "kvq_decode_step_noalloc: device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "kvq_decode_step_noalloc: hipGetSymbolAddress");
+        if (!p) return fail(KVQ_ERR_HIP, "kvq_decode_step_noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_decode_step_noalloc(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                            void* out, int32_t num_q_heads, float sm_scale, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t batch,
+                            int32_t max_context_len, int32_t partition_size, void* stream) {
+    int st = check_cache(cache);
+    if (st) return st;
+    if (batch > 0 && (!k_new || !v_new)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
+    // 0 for sizes the call rejects: decode_common then reports them
+    const size_t need = kvq_decode_workspace_size(batch, num_q_heads, cache->num_kv_heads, max_context_len,
+                                                  partition_size);
+    if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES)
+        return fail(KVQ_ERR_WORKSPACE,
+                    "kvq_decode_step_noalloc: these sizes need %zu bytes of split-K workspace, more than "
+                    "its %zu-byte scratch (pass a workspace to kvq_decode_step instead)",
+                    need, (size_t)KVQ_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws))) return st;
+    return decode_common("kvq_decode_step_noalloc", false, cache, k_new, v_new, q, out, num_q_heads,
+                         sm_scale, block_tables, max_blocks_per_seq, context_lens, batch, max_context_len,
+                         partition_size, ws, need > 0 ? (size_t)KVQ_NOALLOC_SCRATCH_BYTES : 0, stream);
+}
 
 }  // extern "C"
 

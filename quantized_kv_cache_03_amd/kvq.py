@@ -54,6 +54,9 @@ lib.kvq_paged_decode_attn.restype = ctypes.c_int
 lib.kvq_decode_step.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32,
                                 _vp, _i32, _i32, _i32, _vp, _sz, _vp]
 lib.kvq_decode_step.restype = ctypes.c_int
+lib.kvq_decode_step_noalloc.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32,
+                                        _vp, _i32, _i32, _i32, _vp]
+lib.kvq_decode_step_noalloc.restype = ctypes.c_int
 lib.kvq_paged_prefill_attn.argtypes = [ctypes.POINTER(KvqCache), _vp, _vp, _i32, _f32, _vp, _i32, _i32,
                                        _vp, _i32, _vp, _i32, _i32, _vp]
 lib.kvq_paged_prefill_attn.restype = ctypes.c_int
@@ -84,7 +87,8 @@ EXPORTS = ["kvq_append", "kvq_decode_workspace_size", "kvq_paged_decode_attn", "
            "kvq_paged_prefill_attn", "kvq_dequant", "kvq_paged_decode_attn_fp8math",
            "kvq_decode_step_fp8math", "kvq_paged_prefill_attn_fp8math", "kvq_quantize_q_fp8",
            "kvq_dtype_from_string", "kvq_status_string", "kvq_last_error", "kvq_timing_begin",
-           "kvq_timing_end", "kvq_version"]
+           "kvq_timing_end", "kvq_version", "kvq_decode_step_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 
 
 class KvqError(RuntimeError):
@@ -271,6 +275,9 @@ def paged_decode_attn_fp8math(cache: PagedKVCache, q: torch.Tensor, block_tables
                         max_context_len, sm_scale, partition_size, workspace, out, stream)
 
 
+_NO_WORKSPACE = object()  # _decode_args: the call brings its own workspace
+
+
 def _decode_args(cache, q, block_tables, context_lens, max_context_len, partition_size, workspace, out):
     """Checks shared by the decode calls -> (descriptor, out, workspace, workspace bytes)."""
     d = cache.descriptor()
@@ -281,6 +288,8 @@ def _decode_args(cache, q, block_tables, context_lens, max_context_len, partitio
     if out is None:
         out = torch.empty_like(q)
     _tensor(out, "out", torch.float16, tuple(q.shape), dev)
+    if workspace is _NO_WORKSPACE:
+        return d, out, None, 0
     need = workspace_size(B, Hq, cache.num_kv_heads, max_context_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -338,6 +347,27 @@ def _decode_step(name, cache, k_new, v_new, q, block_tables, context_lens, max_c
                               float(sm_scale), _ptr(block_tables), block_tables.shape[1],
                               _ptr(context_lens), B, int(max_context_len), int(partition_size),
                               _ptr(workspace), ws_bytes, _stream(stream)), name)
+    return out
+
+
+def decode_step_noalloc(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                        sm_scale: float | None = None, partition_size: int = PARTITION_BALANCED,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_decode_step_noalloc: decode_step with the library's own device scratch as the split-K
+    workspace (no allocation in the call when `out` is given; calls that overlap on one GPU race)."""
+    d, out, _, _ = _decode_args(cache, q, block_tables, context_lens, max_context_len, PARTITION_BALANCED
+                                if partition_size is None else partition_size, _NO_WORKSPACE, out)
+    B, Hq, _ = q.shape
+    dev = cache.k_cache.device
+    _tensor(k_new, "k_new", torch.float16, (B, cache.num_kv_heads, HEAD_DIM), dev)
+    _tensor(v_new, "v_new", torch.float16, (B, cache.num_kv_heads, HEAD_DIM), dev)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _check(lib.kvq_decode_step_noalloc(ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), Hq,
+                                       float(sm_scale), _ptr(block_tables), block_tables.shape[1],
+                                       _ptr(context_lens), B, int(max_context_len), int(partition_size),
+                                       _stream(stream)), "kvq_decode_step_noalloc")
     return out
 
 
