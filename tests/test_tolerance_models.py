@@ -191,3 +191,21 @@ def test_fp32_slack_weights(fmt):
     r, cache, bt, ctx = _one_token_cache(fmt)
     q = r.standard_normal((1, 2, 128)).astype(np.float16)
     assert np.all(fp32_slack(cache, q[:, :1], bt, ctx) == 0.0)
+
+
+def test_fp8_math_slack_prefill_form_bounds_the_model():
+    """The prefill rows' FP8 slack takes each product's loss at its group's quantum
+    2^(Eq_g + Ek_g - 13): never below the model's bound, on random codes of every magnitude."""
+    from gpu_common import _exp_field
+    r = np.random.default_rng(1)
+    for fk, emin in ((oracle.E4M3, -6), (oracle.E5M2, -14)):
+        for _ in range(10):
+            qc = oracle.fp8_decode(oracle.E4M3, r.integers(0, 0x7E, size=(7, 128)).astype(np.uint8))
+            qc *= r.choice([-1.0, 1.0], size=qc.shape)
+            kc = oracle.fp8_decode(fk, r.integers(0, 0x7B, size=(11, 128)).astype(np.uint8))
+            kc *= r.choice([-1.0, 1.0], size=kc.shape)
+            exact = mfma_fp8_bound(kc[None, :, :], qc[:, None, :], emin, -6)
+            eq = _exp_field(qc, -6).reshape(7, 16, 8).max(-1)
+            ek = _exp_field(kc, emin).reshape(11, 16, 8).max(-1)
+            fac = 8.0 * np.exp2(eq - FP8_GROUP_BITS) @ np.exp2(ek).T + 2 * U32 * (np.abs(qc) @ np.abs(kc).T)
+            assert np.all(fac >= exact * (1 - 1e-12))
