@@ -2,14 +2,16 @@
 //
 // The INT4 cache (asymmetric 4-bit codes, an fp32 (scale, zero point) pair per (token, KV head);
 // the online INT4 cache named beside INT8 in "[Feature] TurboMind support W8A8 or FP8 KV Cache"):
-//     z_t   = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d)
-//     out_d = (sum_t p_t s_t c_td + sum_t p_t zp_t) / sum_t p_t.
+//     z_t   = sm_scale * (s_t (q . (c_t - c0_t)) + zp'_t sum_d q_d),   zp'_t = zp_t + s_t c0_t,
+//     out_d = (sum_t p_t s_t c_td + sum_t p_t zp_t) / sum_t p_t,
+// c0_t the code of the token's row nearest zero (int4_zero_code): centred, the logit sums terms
+// no larger than q . k^ itself.
 // One wave per (KV head, share of the work) serves the G <= 16 query heads of the group, as the
 // 8-bit grouped kernel (kvq_attn_gqa.hip) does, with both products on v_mfma_f32_16x16x32_f16
-// (query heads padded to 16 columns).  Codes decode to exact binary16 subnormals by masking
-// (int4x8_to_f16): K's even nibble pairs are worth 2^-24 per unit and its odd ones 2^-20, so each
-// K operand holds one of the two kinds and S^T keeps two accumulators; V's odd nibbles are shifted
-// down before the masking (int4_unit_to_f16_unit), so O^T keeps one, in 2^-24 units.
+// (query heads padded to 16 columns).  The matrix cores get exact binary16 integers (they align a
+// group's products by exponent fields, which would cost subnormal codes their low bits): K codes as
+// c - c0 and 16 (c - c0) (int4x8_centred), V codes as c and 16 c with the odd tokens' weights
+// divided by 16 (int4_unit_to_f16_int).
 //   S^T = K Q^T per tile: A = K (lane: token l % 16, the 32 dims of chunk l / 16 -- one 16-byte
 //       load per lane reads the tile), B = Q^T (lane: head l % 16, the same dims); two MFMAs for
 //       the even nibble pairs of the chunk's dims, two for the odd ones.  C: lane (head l % 16,
@@ -31,14 +33,16 @@ __device__ __forceinline__ half8_v join4(half2_t a, half2_t b, half2_t c, half2_
     return join8(a, b, c, d);
 }
 
-// The K operands of one tile: (even, odd) nibble pairs of dwords (0, 1) and (2, 3).
-__device__ __forceinline__ void k_operands(const u32x4& k, half8_v (&e)[2], half8_v (&o)[2]) {
+// The K operands of one tile: (even, odd) nibble pairs of dwords (0, 1) and (2, 3), every code
+// minus its token's zero code (ne, no): c - c0 in the even operands, 16 (c - c0) in the odd ones.
+__device__ __forceinline__ void k_operands(const u32x4& k, half2_t ne, half2_t no, half8_v (&e)[2],
+                                           half8_v (&o)[2]) {
     const uint32_t w[4] = {k.x, k.y, k.z, k.w};
     half2_t h0[4], h1[4], h2[4], h3[4];
-    int4x8_to_f16(w[0], h0);
-    int4x8_to_f16(w[1], h1);
-    int4x8_to_f16(w[2], h2);
-    int4x8_to_f16(w[3], h3);
+    int4x8_centred(w[0], ne, no, h0);
+    int4x8_centred(w[1], ne, no, h1);
+    int4x8_centred(w[2], ne, no, h2);
+    int4x8_centred(w[3], ne, no, h3);
     e[0] = join4(h0[0], h0[2], h1[0], h1[2]);
     o[0] = join4(h0[1], h0[3], h1[1], h1[3]);
     e[1] = join4(h2[0], h2[2], h3[0], h3[2]);
@@ -64,9 +68,19 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
     float cmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i) {
+        // every token centred at its own zero code c0 (int4_zero_code), computed once, by the
+        // lanes whose K operand row it is (l % 16, from its pair kp); the accumulator's tokens
+        // 4 q4 + u take their zp' = zp + s c0 from those lanes
+        const float zc = int4_zero_code(t[i].kp.x, t[i].kp.y);
+        const float zpa = __builtin_fmaf(t[i].kp.x, zc, t[i].kp.y);
+        float zps[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) zps[u] = __shfl(zpa, 4 * q4 + u);
+        half2_t ne, no;
+        int4_centre_pairs(zc, ne, no);
         half8_v e[2], o[2];
-        k_operands(t[i].k, e, o);
-        float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};
+        k_operands(t[i].k, ne, no, e, o);
+        float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};  // q . (c - c0), x16 for so
         se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[0], qe[0], se, 0, 0, 0);
         so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[0], qo[0], so, 0, 0, 0);
         se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[1], qe[1], se, 0, 0, 0);
@@ -74,8 +88,8 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
         const int pos0 = (tile0 + i) * kBlock + 4 * q4;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float s = se[u] + so[u] * (kInt4Odd / kInt4Even);  // q . c in 2^-24 units
-            const float zz = a.qk_scale * (s * (t[i].ks[u] * kInt4Even) + t[i].kz[u] * qsum);
+            const float sc = se[u] + so[u] * 0.0625f;
+            const float zz = a.qk_scale * (sc * t[i].ks[u]) + a.qk_scale * (zps[u] * qsum);
             z[i][u] = (pos0 + u < t_end) ? zz : kNegInf;
             cmax = fmaxf(cmax, z[i][u]);
         }
@@ -121,7 +135,7 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
             z_lane = __builtin_fmaf(pw, t[i].vz[u], z_lane);
         }
         split_hi_lo(w[0], w[2], ehi[i], elo[i]);
-        split_hi_lo(w[1], w[3], ohi[i], olo[i]);
+        split_hi_lo(w[1] * kInt4OddWeight, w[3] * kInt4OddWeight, ohi[i], olo[i]);
     }
     const half8_v we_hi = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
     const half8_v we_lo = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
@@ -135,9 +149,9 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
         for (int i = 0; i < kTiles4; ++i) {
             const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
             if (r & 1)
-                int4_unit_to_f16_unit<1>(w[r / 2], ve[i], vo[i]);
+                int4_unit_to_f16_int<1>(w[r / 2], ve[i], vo[i]);
             else
-                int4_unit_to_f16_unit<0>(w[r / 2], ve[i], vo[i]);
+                int4_unit_to_f16_int<0>(w[r / 2], ve[i], vo[i]);
         }
         const half8_v ae = join4(ve[0], ve[1], ve[2], ve[3]);
         const half8_v ao = join4(vo[0], vo[1], vo[2], vo[3]);
@@ -153,7 +167,10 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
 __device__ __forceinline__ void patch_tile_g4(TileMfma4& t, const NewToken4& nt, const uint8_t* lds_k,
                                               const uint8_t* lds_v, int lane) {
     const int col = lane & 15, q4 = lane >> 4;
-    if (col == nt.slot) t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
+    if (col == nt.slot) {
+        t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
+        t.kp = nt.ks;
+    }
     patch_v_quad(t.v, nt.slot, lds_v, lane);
     if (q4 == (nt.slot >> 2)) {
 #pragma unroll
@@ -214,7 +231,7 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
 
     float m_run = kNegInf;
     float l_lane = 0.0f, z_lane = 0.0f;
-    float4_t acc[8];  // O^T row blocks in 2^-24 units: dims 16 r + 4 q4 .. +3 of head col
+    float4_t acc[8];  // O^T row blocks, sum of w c: dims 16 r + 4 q4 .. +3 of head col
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -254,7 +271,7 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
     if (col < G) {
         float4_t o[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) o[r] = acc[r] * kInt4Even + z_sum;
+        for (int r = 0; r < 8; ++r) o[r] = acc[r] + z_sum;
         if (lo == 0 && hi == nt) {
             const float inv = a.v_scale / l_sum;
             uint16_t* orow = a.out + ((size_t)b * a.Hq + h) * kDim;

@@ -3,14 +3,17 @@
 // The same causal attention as kvq_prefill.hip (sequence b's n_b query rows are its last n_b
 // tokens; row j at position p = context_lens[b] - n_b + j sees the tokens 0 .. p) over the INT4
 // cache (asymmetric 4-bit codes, an fp32 (scale, zero point) pair per (token, KV head)), with the
-// logits and the output factored as in the INT4 decode kernels:
-//     z_t = sm_scale * (s_t (q . c_t) + zp_t sum_d q_d),  out = (sum_t p_t s_t c_t + sum_t p_t zp_t) / sum_t p_t.
+// logits and the output factored as in the grouped INT4 decode kernel (kvq_attn_gqa4.hip):
+//     z_t = sm_scale * (s_t (q . (c_t - c0_t)) + zp'_t sum_d q_d),   zp'_t = zp_t + s_t c0_t,
+//     out = (sum_t p_t s_t c_t + sum_t p_t zp_t) / sum_t p_t,
+// c0_t the code of the token's row nearest zero (int4_zero_code).
 // One wave per (KV head, tile of query rows, sequence) on v_mfma_f32_16x16x32_f16, serving two
 // blocks of 16 columns -- (query row, query head) pairs as in the 8-bit prefill kernel -- with the
-// operands of the grouped INT4 decode kernel (kvq_attn_gqa4.hip): one 16-byte load per lane for
-// each of the K and V tiles, decoded once for both blocks, P^T left in the lanes by the S^T
-// accumulator, chunks of four tiles.  Every decoded code is in 2^-24 units (odd nibbles shifted
-// down), so each product keeps one accumulator.
+// operands of the grouped INT4 decode kernel: one 16-byte load per lane for each of the K and V
+// tiles, decoded once for both blocks, P^T left in the lanes by the S^T accumulator, chunks of four
+// tiles.  The matrix cores get exact binary16 integers: K codes as c - c0 and 16 (c - c0)
+// (int4x8_centred), V codes as c and 16 c with the odd tokens' weights divided by 16
+// (int4_unit_to_f16_int).
 #include "kvq_attn4.h"
 #include "kvq_mfma.h"
 
@@ -41,12 +44,13 @@ struct Prefill4Params {
 
 
 // The K operands of one tile in the k-slot order of kslot_dim: the four MFMAs take the (0, 4),
-// (2, 6) nibble pairs and then the (1, 5), (3, 7) pairs of dwords (0, 1) and of dwords (2, 3).
-__device__ __forceinline__ void k_operands_p4(const u32x4& k, half8_v (&op)[4]) {
+// (2, 6) nibble pairs and then the (1, 5), (3, 7) pairs of dwords (0, 1) and of dwords (2, 3); every
+// code minus its token's zero code (ne, no): c - c0 in operands 0 and 2, 16 (c - c0) in operands 1 and 3.
+__device__ __forceinline__ void k_operands_p4(const u32x4& k, half2_t ne, half2_t no, half8_v (&op)[4]) {
     const uint32_t w[4] = {k.x, k.y, k.z, k.w};
     half2_t h[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) int4x8_to_f16_unit(w[j], h[j]);
+    for (int j = 0; j < 4; ++j) int4x8_centred(w[j], ne, no, h[j]);
     op[0] = join8(h[0][0], h[0][2], h[1][0], h[1][2]);
     op[1] = join8(h[0][1], h[0][3], h[1][1], h[1][3]);
     op[2] = join8(h[2][0], h[2][2], h[3][0], h[3][2]);
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     }
 
     float m_run[NB], l_lane[NB], z_lane[NB];
-    float4_t acc[NB][8];  // O^T row blocks in 2^-24 units: dims 16 r + 4 q4 .. +3 of the column
+    float4_t acc[NB][8];  // O^T row blocks, sum of w c: dims 16 r + 4 q4 .. +3 of the column
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         m_run[nb] = kNegInf;
@@ -145,7 +149,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         for (int r = 0; r < 8; ++r) acc[nb][r] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
     const uint32_t off = 256u * (uint32_t)q4 + 16u * (uint32_t)col;
-    const float qk24 = a.qk_scale * kInt4Even;
 
     for (int tb = 0; tb < tile_end; tb += 64) {
         const int nt_grp = min(64, tile_end - tb);
@@ -162,16 +165,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             float z[NB][kTilesP4][4];
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
+                // every token centred at its own zero code (int4_zero_code): the K operand row's
+                // token (col) from its pair kp, the accumulator's tokens 4 q4 + u from theirs
+                half2_t ne, no;
+                int4_centre_pairs(int4_zero_code(t[i].kp.x, t[i].kp.y), ne, no);
                 half8_v kop[4];
-                k_operands_p4(t[i].k, kop);
+                k_operands_p4(t[i].k, ne, no, kop);
+                float zp[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    zp[u] = __builtin_fmaf(t[i].ks[u], int4_zero_code(t[i].ks[u], t[i].kz[u]), t[i].kz[u]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    float4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[m], qB[nb][m], s, 0, 0, 0);
+                    float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};  // so: x16
+                    se = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[0], qB[nb][0], se, 0, 0, 0);
+                    so = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[1], qB[nb][1], so, 0, 0, 0);
+                    se = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[2], qB[nb][2], se, 0, 0, 0);
+                    so = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[3], qB[nb][3], so, 0, 0, 0);
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        z[nb][i][u] = qk24 * (s[u] * t[i].ks[u]) + a.qk_scale * (t[i].kz[u] * qsum[nb]);
+                        z[nb][i][u] = a.qk_scale * ((se[u] + so[u] * 0.0625f) * t[i].ks[u]) +
+                                      a.qk_scale * (zp[u] * qsum[nb]);
                 }
             }
             // The causal mask, only for the chunks that reach past the wave's first row
@@ -240,7 +254,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                         z_lane[nb] = __builtin_fmaf(pw, t[i].vz[u], z_lane[nb]);
                     }
                     split_hi_lo(w[0], w[2], ehi[i], elo[i]);
-                    split_hi_lo(w[1], w[3], ohi[i], olo[i]);
+                    split_hi_lo(w[1] * kInt4OddWeight, w[3] * kInt4OddWeight, ohi[i], olo[i]);
                 }
                 we_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
                 we_lo[nb] = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
@@ -254,9 +268,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 for (int i = 0; i < kTilesP4; ++i) {
                     const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
                     if (r & 1)
-                        int4_unit_to_f16_unit<1>(w[r / 2], ve[i], vo[i]);
+                        int4_unit_to_f16_int<1>(w[r / 2], ve[i], vo[i]);
                     else
-                        int4_unit_to_f16_unit<0>(w[r / 2], ve[i], vo[i]);
+                        int4_unit_to_f16_int<0>(w[r / 2], ve[i], vo[i]);
                 }
                 const half8_v ae = join8(ve[0], ve[1], ve[2], ve[3]);
                 const half8_v ao = join8(vo[0], vo[1], vo[2], vo[3]);
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             const float inv = 1.0f / l_sum;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const float4_t o = acc[nb][r] * kInt4Even + z_sum;
+                const float4_t o = acc[nb][r] + z_sum;
                 const half4_t v = {(_Float16)(o[0] * inv), (_Float16)(o[1] * inv), (_Float16)(o[2] * inv),
                                    (_Float16)(o[3] * inv)};
                 *reinterpret_cast<half4_t*>(a.out + orow[nb] + 16 * r + 4 * q4) = v;

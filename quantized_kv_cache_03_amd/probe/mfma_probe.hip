@@ -84,3 +84,53 @@ extern "C" int kvq_probe_mfma_fp8(const void* a, const void* b, int32_t fmt_a, i
     else mfma_fp8<1, 1><<<grid, block, 0, s>>>(pa, pb, c_in, c_out);
     return (int)hipGetLastError();
 }
+
+// The INT4 kernels' K operand path on its own: for problem p, lane l takes the 16 bytes
+// codes[p][l] (32 nibbles), decodes them with int4x8_centred around the zero code c0[p] (the even
+// pairs as c - c0, the odd ones as 16 (c - c0)), writes the four decoded dwords of each of its
+// 4 code dwords to dec[p][l][16], and issues the kernels' four matrix instructions against the
+// fp16 query operands qop[p][l][4][8] (the even operands into one accumulator, the odd into
+// another), writing S = se + so / 16 to s_out[p][l][4].
+#include "kvq_int4.h"
+namespace {
+__global__ __launch_bounds__(64) void int4_centred(const uint32_t* codes, const float* c0s,
+                                                   const uint16_t* qop, uint32_t* dec, float* s_out) {
+    const int p = blockIdx.x, l = threadIdx.x;
+    const uint32_t* w = codes + ((size_t)p * 64 + l) * 4;
+    kvq::half2_t ne, no;
+    kvq::int4_centre_pairs(c0s[p], ne, no);
+    kvq::half2_t h[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kvq::int4x8_centred(w[j], ne, no, h[j]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dec[((size_t)p * 64 + l) * 16 + 4 * j + k] = __builtin_bit_cast(uint32_t, h[j][k]);
+    }
+    const half8_v e0 = {h[0][0].x, h[0][0].y, h[0][2].x, h[0][2].y, h[1][0].x, h[1][0].y, h[1][2].x, h[1][2].y};
+    const half8_v o0 = {h[0][1].x, h[0][1].y, h[0][3].x, h[0][3].y, h[1][1].x, h[1][1].y, h[1][3].x, h[1][3].y};
+    const half8_v e1 = {h[2][0].x, h[2][0].y, h[2][2].x, h[2][2].y, h[3][0].x, h[3][0].y, h[3][2].x, h[3][2].y};
+    const half8_v o1 = {h[2][1].x, h[2][1].y, h[2][3].x, h[2][3].y, h[3][1].x, h[3][1].y, h[3][3].x, h[3][3].y};
+    half8_v q[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[m][e] = __builtin_bit_cast(_Float16, qop[(((size_t)p * 64 + l) * 4 + m) * 8 + e]);
+    float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};
+    se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e0, q[0], se, 0, 0, 0);
+    so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o0, q[1], so, 0, 0, 0);
+    se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e1, q[2], se, 0, 0, 0);
+    so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o1, q[3], so, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s_out[((size_t)p * 64 + l) * 4 + u] = se[u] + so[u] * 0.0625f;
+}
+}  // namespace
+
+// n problems: codes uint32 [n][64][4], c0 float [n], qop fp16 [n][64][4][8], dec uint32 [n][64][16],
+// s_out float [n][64][4]; device memory.  Returns 0, -1 for bad arguments, or the HIP error code.
+extern "C" int kvq_probe_int4_centred(const uint32_t* codes, const float* c0, const void* qop, uint32_t* dec,
+                                      float* s_out, int32_t n, void* stream) {
+    if (!codes || !c0 || !qop || !dec || !s_out || n <= 0 || n > 65535) return -1;
+    int4_centred<<<dim3((unsigned)n), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(
+        codes, c0, static_cast<const uint16_t*>(qop), dec, s_out);
+    return (int)hipGetLastError();
+}

@@ -219,3 +219,54 @@ def test_f16_instruction_model(P, kind):
         f"{float((err / np.maximum(GC.U32 * mag, 1e-300)).max()):.1f}")
     assert np.all(np.isfinite(got))
     assert np.all(err <= bound), f"worst share of the model bound {share:.3f}"
+
+
+def test_int4_centred_operands(P):
+    """The INT4 kernels' K operand path (int4x8_centred and the four matrix instructions of a tile,
+    run by kvq_probe_int4_centred): every decoded pair bit for bit c - c0 (even pairs) and 16 (c - c0)
+    (odd pairs) for every zero code c0, and the sums q . (c - c0) within the f16 instruction's model
+    chained over its four instructions."""
+    import torch
+    f = P.kvq_probe_int4_centred
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    r = np.random.default_rng(9)
+    n = 256
+    codes = r.integers(0, 2 ** 32, size=(n, 64, 4), dtype=np.uint64).astype(np.uint32)
+    c0 = np.repeat(np.arange(16, dtype=np.float32), n // 16)
+    qop = r.standard_normal((n, 64, 4, 8)).astype(np.float16)
+    d = [torch.from_numpy(x).cuda() for x in (codes, c0, qop.view(np.uint16))]
+    dec = torch.zeros((n, 64, 16), dtype=torch.int32, device="cuda")
+    s_out = torch.zeros((n, 64, 4), dtype=torch.float32, device="cuda")
+    assert f(d[0].data_ptr(), d[1].data_ptr(), d[2].data_ptr(), dec.data_ptr(), s_out.data_ptr(), n, None) == 0
+    torch.cuda.synchronize()
+    dec = dec.cpu().numpy().view(np.uint32)
+    s_out = s_out.cpu().numpy().astype(np.float64)
+    nib = np.stack([(codes >> (4 * i)) & 0xF for i in range(8)], -1).astype(np.int64)  # [n][64][dword][nibble]
+    cc = c0[:, None, None].astype(np.int64)
+    want = np.zeros((n, 64, 4, 4, 2))
+    for k in range(4):  # pair (k, k + 4); odd pairs in units of 16
+        sc = 16 if k % 2 else 1
+        want[..., k, 0] = sc * (nib[..., k] - cc)
+        want[..., k, 1] = sc * (nib[..., k + 4] - cc)
+    got = np.stack([dec & 0xFFFF, dec >> 16], -1).astype(np.uint16).view(np.float16).astype(np.float64)
+    np.testing.assert_array_equal(got.reshape(want.shape), want)
+    # the operands as the kernels join them, and the exact sums
+    ops = [np.concatenate([want[:, :, j, k], want[:, :, j, k + 2], want[:, :, j + 1, k], want[:, :, j + 1, k + 2]], -1)
+           for j, k in ((0, 0), (0, 1), (2, 0), (2, 1))]
+    qv = qop.astype(np.float64)
+    exact = np.zeros((n, 16, 16))
+    bound = np.zeros((n, 16, 16))
+    for m in range(4):
+        sc = 1.0 if m % 2 == 0 else 1.0 / 16
+        for kg in range(4):
+            a, b = ops[m][:, 16 * kg:16 * kg + 16], qv[:, 16 * kg:16 * kg + 16, m]
+            exact += sc * np.einsum("pie,pje->pij", a, b)
+            bound += sc * np.einsum("pie,pje->pij", np.abs(a), np.abs(b))
+    want_s = np.stack([exact[:, 4 * (l // 16):4 * (l // 16) + 4, l % 16] for l in range(64)], 1)
+    mag = np.stack([bound[:, 4 * (l // 16):4 * (l // 16) + 4, l % 16] for l in range(64)], 1)
+    err = np.abs(s_out - want_s)
+    # four chained instructions of 32 products, each within 19 u of its magnitudes (the f16 model), and
+    # the final fp32 sum se + so / 16
+    say(f"  INT4 centred operands: worst error / (u sum |products|) = {float((err / (GC.U32 * mag)).max()):.1f}")
+    assert np.all(err <= (4 * 19 + 1) * GC.U32 * mag + 1e-30)

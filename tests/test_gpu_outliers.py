@@ -11,13 +11,18 @@ is widened by a derived bound of that rounding carried through the softmax (gpu_
 2^-16 sm_scale sum_d |q_d| w_td per logit), and for FP8 math by the FP8 instruction's accumulation
 bound (gpu_common.fp8_math_slack) instead.  Every cache byte is compared bit for bit as everywhere.
 
+The INT4 cases are also held to the plain gate.  Their kernels give the matrix cores each token's
+codes centred at its own zero code, as exact binary16 integers (kvq_int4.h); with the codes as
+fp16 subnormals and the logit factored as s (q . c) + zp sum q, rows like these once missed the
+plain gate by up to 29 times while a float32 evaluation of the same codes met it.
+
 Each case prints the worst element's share of the widened gate and of the plain gate.
 """
 import numpy as np
 import pytest
 
 import oracle
-from gpu_common import (ATOL, RTOL, OracleTwin, assert_attn_close_slack, assert_cache_bytes_equal,
+from gpu_common import (ATOL, RTOL, OracleTwin, assert_attn_close, assert_attn_close_slack, assert_cache_bytes_equal,
                         attn_stats, fp32_attention, fp32_slack, fp8_math_slack, say)
 
 pytestmark = pytest.mark.gpu
@@ -48,9 +53,11 @@ def _plain(x, ref):
     return float((np.abs(x.astype(np.float64) - ref) / (ATOL + RTOL * np.abs(ref))).max(initial=0))
 
 
-def _report(tag, gpu, ref, slack, f32):
-    """Assert the widened gate; print the plain gate's share for the kernel and for a plain float32
-    evaluation of the same codes (the data's conditioning)."""
+def _report(tag, gpu, ref, slack, f32, plain=False):
+    """Assert the widened gate (and the plain one when `plain`); print the plain gate's share for the
+    kernel and for a plain float32 evaluation of the same codes (the data's conditioning)."""
+    if plain:
+        assert_attn_close(gpu, ref, tag)
     share = assert_attn_close_slack(gpu, ref, slack, tag)
     say(f"    widened gate share {share:.3f}; plain gate share: kernel {_plain(gpu, ref):.3f}, float32 "
         f"evaluation {_plain(f32, ref):.3f}; {attn_stats(gpu, ref)}")
@@ -80,7 +87,8 @@ def test_outlier_decode(H, dtype, G, outliers, partition, fp8_math):
         qe = oracle.fp8_decode(oracle.E4M3, codes) * sc[..., None]
     else:
         slack = fp32_slack(twin.cache, twin.q, twin.bt, twin.ctx)
-    _report(w.name, out, ref, slack, fp32_attention(twin.cache, twin.q, twin.bt, twin.ctx, q_eff=qe))
+    _report(w.name, out, ref, slack, fp32_attention(twin.cache, twin.q, twin.bt, twin.ctx, q_eff=qe),
+            plain=dtype == "int4")
 
 
 PREFILL = [(dt, G, o, f8) for dt in BASES for G in (1, 4, 10) for o in (2, 8)
@@ -114,4 +122,5 @@ def test_outlier_prefill(H, dtype, G, outliers, fp8_math):
         qe = oracle.fp8_decode(oracle.E4M3, codes) * sc[..., None]
     else:
         slack = fp32_slack(twin.cache, q, twin.bt, twin.ctx, cu_q)
-    _report(w.name, out, ref, slack, fp32_attention(twin.cache, q, twin.bt, twin.ctx, cu_q, q_eff=qe))
+    _report(w.name, out, ref, slack, fp32_attention(twin.cache, q, twin.bt, twin.ctx, cu_q, q_eff=qe),
+            plain=dtype == "int4")
