@@ -225,8 +225,11 @@ int kvq_paged_prefill_attn(const kvq_cache *cache, const void *q, void *out, int
  *   s_q = fl32(max_d |q_d| / 448)  (1 for an all-zero row),   c_d = enc_E4M3(fl32(q_d / s_q))
  * (the cache encoder: nearest, ties to even, saturating), and the attention is that of the row
  * dec(c) * s_q: QK^T multiplies the E4M3 codes with the cache's K codes as stored, on the FP8
- * matrix cores with fp32 accumulation (exact products), and everything after the logits is as in
- * the fp16 calls.  The result differs from the fp16-query attention by the query's quantization.
+ * matrix cores, and everything after the logits is as in the fp16 calls.  The matrix instruction
+ * does not sum exactly in fp32: within each group of 8 consecutive products it aligns the products
+ * to the group's largest exponent and keeps 13 bits below it, so a logit may be off by up to about
+ * 2^-13 of each group's largest product (more than fp32 rounding where one product dominates many
+ * small ones).  The result differs from the fp16-query attention by the query's quantization.
  *   kvq_paged_decode_attn_fp8math, kvq_decode_step_fp8math, kvq_paged_prefill_attn_fp8math take the
  *   arguments of kvq_paged_decode_attn, kvq_decode_step and kvq_paged_prefill_attn (the same
  *   workspace sizes) and need an fp8_e4m3 or fp8_e5m2 cache (else KVQ_ERR_DTYPE); every grouping

@@ -3,7 +3,8 @@
 //
 // The cache is stored as 8-bit codes and the attention arithmetic runs at higher precision
 // ("Accelerating Inference with FP8 KV Cache", opening section): codes are decoded exactly to
-// fp16, the dot products use fp16 inputs with fp32 accumulation, softmax statistics are fp32.
+// fp16, the dot products take fp16 inputs and sum in fp32 (the matrix instruction aligns each group
+// of 8 products to its largest and keeps 24 bits below it), softmax statistics are fp32.
 // Scales are factored out of the sums: logits are  sm_scale * kv_scale * (q . dec(k))  and the
 // output is  kv_scale * sum_t p_t dec(v_t) / sum_t p_t  (FP8);  INT8 applies the per-token K
 // scale to each logit and folds the per-token V scale into the weight p_t * s_t.  Softmax runs in

@@ -5,7 +5,8 @@
 // cache tokens at positions 0 .. p (causal).  Decode is the case n_b = 1.  The cache is stored as
 // 8-bit codes and the arithmetic runs at higher precision ("Accelerating Inference with FP8 KV
 // Cache", opening section), exactly as in the decode kernels: codes decoded exactly to fp16, fp16
-// products with fp32 accumulation, base-2 online softmax in fp32, scales factored out of the sums.
+// products summed in fp32 on the matrix cores, base-2 online softmax in fp32, scales factored out
+// of the sums.
 //
 // One wave per (KV head, tile of query rows, sequence) on the matrix cores
 // (v_mfma_f32_16x16x32_f16).  The 16 MFMA columns are (query row, query head) pairs: R = 16 / G
