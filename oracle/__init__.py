@@ -35,7 +35,8 @@ BLOCK = 16
 DIM = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkvq_oracle.so")
+# KVQ_ORACLE_LIBRARY may name another build of the same source (the sanitizer build)
+_LIB_PATH = os.environ.get("KVQ_ORACLE_LIBRARY") or os.path.join(_HERE, "libkvq_oracle.so")
 _lib = None
 
 _u8p = ctypes.POINTER(ctypes.c_uint8)

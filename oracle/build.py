@@ -25,5 +25,25 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# The same source under clang's AddressSanitizer and UndefinedBehaviorSanitizer (the shared
+# runtime, so that one runtime serves this library and the HIP library's sanitized build in one
+# process).  Loaded in place of libkvq_oracle.so when KVQ_ORACLE_LIBRARY names it.
+CLANG = os.environ.get("KVQ_SAN_CC", "/opt/rocm/llvm/bin/clang")
+SAN_LIB = os.path.join(HERE, "_san", "libkvq_oracle.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g", "-shared-libsan"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    flags = [f for f in CFLAGS if f != "-O2"] + ["-O1"]
+    cmd = [CLANG, *flags, *SAN_FLAGS, SRC, "-o", SAN_LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -55,5 +55,28 @@ def build(verbose: bool = False, extra_flags=(), jobs: int | None = None) -> str
     return LIB
 
 
+# The host code (argument validation, sizing, the planning arithmetic) under clang's
+# AddressSanitizer and UndefinedBehaviorSanitizer, linked to the shared sanitizer runtime; the
+# device code is built as always.  The library goes to its own directory and is loaded in place of
+# libkvq.so when KVQ_LIBRARY names it (tests/sanitize.py).
+SAN_DIR = os.path.join(HERE, "_san")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g", "-shared-libsan"]
+
+
+def build_sanitized(verbose: bool = False, jobs: int | None = None) -> str:
+    global OBJ
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    os.makedirs(SAN_DIR, exist_ok=True)
+    out = os.path.join(SAN_DIR, "libkvq.so")
+    saved, OBJ = OBJ, os.path.join(SAN_DIR, "obj")
+    try:
+        _link(sources(), out, verbose, SAN_FLAGS, jobs)
+    finally:
+        OBJ = saved
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -21,7 +21,8 @@ DTYPE_NAMES = {"fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3, "fp8_e5m2": FP8_E5M2, "int
 
 OK, ERR_ARG, ERR_DTYPE, ERR_SHAPE, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIBRARY may name another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
                       f"g.build()' or python quantized_kv_cache_03_amd/build.py)")
