@@ -365,10 +365,7 @@ def main():
     # layer copies: same codes, distinct memory
     layers = [case.cache]
     for _ in range(args.layers - 1):
-        c = case.cache
-        layers.append(kvq.PagedKVCache(c.dtype, c.k_cache.clone(), c.v_cache.clone(),
-                                       None if c.k_scale is None else c.k_scale.clone(),
-                                       None if c.v_scale is None else c.v_scale.clone(), c.kv_scale))
+        layers.append(case.cache.clone())
     stream = torch.cuda.current_stream()
     if args.calibration_copy_mib > 0:
         nbytes = args.calibration_copy_mib << 20

@@ -41,7 +41,9 @@
  *   K codes  uint8 [num_blocks][num_kv_heads][8][16 tokens][16 dims] (2 KiB tile of eight 256-byte
  *            chunks: dim d of token t is byte (d / 16) * 256 + t * 16 + d % 16 of the tile)
  *   V codes  uint8 [num_blocks][num_kv_heads][128 dims][16 tokens]   (dim-major tile, 2 KiB)
- *   INT8 scales  float [num_blocks][num_kv_heads][16 tokens], one array for K and one for V
+ *   INT8 scales  float [num_blocks][num_kv_heads][2][16 tokens]: one 128-byte row per tile, its
+ *                16 K scales and then its 16 V scales, so that a tile's scales are one whole
+ *                line; k_scale points at the array and v_scale must be k_scale + 16
  *   INT4 (two codes per byte, the even element in the low nibble; tiles of 1 KiB):
  *     K codes  uint8 [num_blocks][num_kv_heads][4][16 tokens][16 bytes]: dim d of token t is in
  *              byte (d / 32) * 256 + t * 16 + (d % 32) / 2 of the tile, nibble d % 2
@@ -111,8 +113,10 @@ typedef struct {
     int32_t head_dim;     /* must be 128 */
     uint8_t *k_cache;     /* K codes, layout above */
     uint8_t *v_cache;     /* V codes, layout above */
-    float *k_scale;       /* INT8: [num_blocks][Hkv][16]; INT4: [num_blocks][Hkv][16][2]; NULL for FP8 */
-    float *v_scale;       /* INT8: [num_blocks][Hkv][16]; INT4: [num_blocks][Hkv][16][2]; NULL for FP8 */
+    float *k_scale;       /* INT8: the [num_blocks][Hkv][2][16] scale rows; INT4: [num_blocks][Hkv][16][2];
+                             NULL for FP8 */
+    float *v_scale;       /* INT8: k_scale + 16 (else KVQ_ERR_SHAPE); INT4: [num_blocks][Hkv][16][2];
+                             NULL for FP8 */
     float kv_scale;       /* FP8 only: per-tensor scale shared by K and V, finite and > 0;
                              1.0 is the default ("FP8 E4M3 KV Cache" section) */
 } kvq_cache;

@@ -19,7 +19,8 @@ step is written from its definition in fp64:
 * Paged cache: "[QST] Scale factors and benchmarks" (paged attention in the serving stack).
 
 Layouts are those the C file documents: K codes ``[num_blocks][Hkv][8][16][16]`` (16-dim chunks),
-V codes ``[num_blocks][Hkv][128][16]``, INT8 scales ``[num_blocks][Hkv][16]``; INT4 tiles are half
+V codes ``[num_blocks][Hkv][128][16]``, INT8 scales ``[num_blocks][Hkv][2][16]`` (a tile's K scales,
+then its V scales; ``Cache.ks`` / ``Cache.vs`` are the two halves as views); INT4 tiles are half
 the size (two codes per byte) and its (scale, zero point) pairs are ``[num_blocks][Hkv][16][2]``.
 """
 from __future__ import annotations
@@ -205,8 +206,18 @@ class Cache:
         fill = 0x7F if poison else 0
         self.k = np.full(shape, fill, np.uint8) if k_codes is None else np.ascontiguousarray(k_codes, np.uint8).reshape(shape)
         self.v = np.full(shape, fill, np.uint8) if v_codes is None else np.ascontiguousarray(v_codes, np.uint8).reshape(shape)
-        if dtype in (INT8, INT4):
-            sshape = (num_blocks, num_kv_heads, BLOCK) + ((2,) if dtype == INT4 else ())
+        self.rows = None
+        if dtype == INT8:
+            # one row per tile: [..][0][t] the K scale of token t, [..][1][t] its V scale
+            self.rows = np.full((num_blocks, num_kv_heads, 2, BLOCK), np.nan, np.float32)
+            self.ks, self.vs = self.rows[:, :, 0], self.rows[:, :, 1]
+            sshape = (num_blocks, num_kv_heads, BLOCK)
+            if k_scale is not None:
+                self.ks[...] = np.asarray(k_scale, np.float32).reshape(sshape)
+            if v_scale is not None:
+                self.vs[...] = np.asarray(v_scale, np.float32).reshape(sshape)
+        elif dtype == INT4:
+            sshape = (num_blocks, num_kv_heads, BLOCK, 2)
             self.ks = np.full(sshape, np.nan, np.float32) if k_scale is None else np.ascontiguousarray(k_scale, np.float32).reshape(sshape)
             self.vs = np.full(sshape, np.nan, np.float32) if v_scale is None else np.ascontiguousarray(v_scale, np.float32).reshape(sshape)
         else:
@@ -214,8 +225,12 @@ class Cache:
             self.vs = None
 
     def args(self):
-        return (self.dtype, self.Hkv, _ptr(self.k, _u8p), _ptr(self.v, _u8p),
-                _ptr(self.ks, _f32p), _ptr(self.vs, _f32p), self.kv_scale)
+        if self.rows is not None:  # INT8: k_scale at the rows, v_scale 16 floats on
+            ks = _ptr(self.rows, _f32p)
+            vs = ctypes.cast(ctypes.addressof(ks.contents) + 4 * BLOCK, _f32p)
+        else:
+            ks, vs = _ptr(self.ks, _f32p), _ptr(self.vs, _f32p)
+        return (self.dtype, self.Hkv, _ptr(self.k, _u8p), _ptr(self.v, _u8p), ks, vs, self.kv_scale)
 
 
 def append(cache: Cache, k_new, v_new, block_tables, context_lens, cu_new_lens=None) -> None:

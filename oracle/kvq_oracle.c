@@ -44,7 +44,9 @@
  *     NaN encodes as sign | 0x7F; signed zero and subnormals are kept.
  *   - Cache layout (both formats and INT8): K codes [num_blocks][Hkv][8][16 tokens][16 dims], i.e.
  *     dim d of token t sits at byte (d / 16) * 256 + t * 16 + d % 16 of its 2048-byte tile;
- *     V codes [num_blocks][Hkv][128 dims][16 tokens]; INT8 scales [num_blocks][Hkv][16 tokens].
+ *     V codes [num_blocks][Hkv][128 dims][16 tokens]; INT8 scales [num_blocks][Hkv][2][16 tokens]:
+ *     per (block, head) tile one row of the 16 K scales and then the 16 V scales; k_scale points at
+ *     the rows and v_scale at k_scale + 16, so both are indexed alike.
  *   - INT4 layout (two 4-bit codes per byte, the even one in the low nibble): K [num_blocks][Hkv]
  *     [4][16 tokens][16 bytes], dim d of token t in byte (d / 32) * 256 + t * 16 + (d % 32) / 2
  *     of its 1024-byte tile, nibble d % 2; V [num_blocks][Hkv][4 token quads][16][8][2 bytes],
@@ -275,6 +277,11 @@ static size_t s_off(int Hkv, int blk, int g, int t)
 {
     return ((size_t)blk * Hkv + g) * KVQO_BLOCK + t;
 }
+/* INT8: token t's scale in the tile's row of 2 * 16 scales, from k_scale or from v_scale */
+static size_t s_off8(int Hkv, int blk, int g, int t)
+{
+    return ((size_t)blk * Hkv + g) * (2 * KVQO_BLOCK) + t;
+}
 /* INT4: byte offsets; the code is nibble (d % 2) of the K byte and nibble (t % 2) of the V byte */
 static size_t k_off4(int Hkv, int blk, int g, int t, int d)
 {
@@ -343,8 +350,8 @@ int kvqo_append(int dtype, int Hkv, uint8_t *k_cache, uint8_t *v_cache, float *k
                         k_cache[k_off(Hkv, blk, g, t, d)] = (uint8_t)qk[d];
                         v_cache[v_off(Hkv, blk, g, t, d)] = (uint8_t)qv[d];
                     }
-                    k_scale[s_off(Hkv, blk, g, t)] = sk;
-                    v_scale[s_off(Hkv, blk, g, t)] = sv;
+                    k_scale[s_off8(Hkv, blk, g, t)] = sk;
+                    v_scale[s_off8(Hkv, blk, g, t)] = sv;
                 } else {
                     for (int d = 0; d < KVQO_DIM; ++d) {
                         k_cache[k_off(Hkv, blk, g, t, d)] = kvqo_fp8_quantize(dtype, xk[d], kv_scale);
@@ -373,7 +380,7 @@ static double dq_k(int dtype, int Hkv, const uint8_t *kc, const float *ks, float
         return dq4(kc, k_off4(Hkv, blk, g, t, d), d % 2, ks, s_off(Hkv, blk, g, t));
     uint8_t c = kc[k_off(Hkv, blk, g, t, d)];
     if (dtype == KVQO_INT8)
-        return (double)(int8_t)c * (double)ks[s_off(Hkv, blk, g, t)];
+        return (double)(int8_t)c * (double)ks[s_off8(Hkv, blk, g, t)];
     return kvqo_fp8_decode(dtype, c) * (double)kv_scale;
 }
 static double dq_v(int dtype, int Hkv, const uint8_t *vc, const float *vs, float kv_scale, int blk,
@@ -383,7 +390,7 @@ static double dq_v(int dtype, int Hkv, const uint8_t *vc, const float *vs, float
         return dq4(vc, v_off4(Hkv, blk, g, t, d), t % 2, vs, s_off(Hkv, blk, g, t));
     uint8_t c = vc[v_off(Hkv, blk, g, t, d)];
     if (dtype == KVQO_INT8)
-        return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, t)];
+        return (double)(int8_t)c * (double)vs[s_off8(Hkv, blk, g, t)];
     return kvqo_fp8_decode(dtype, c) * (double)kv_scale;
 }
 

@@ -50,6 +50,9 @@ int check_cache(const kvq_cache* c) {
         if (!c->k_scale || !c->v_scale)
             return fail(KVQ_ERR_ARG, "%s cache needs k_scale and v_scale arrays",
                         c->dtype == KVQ_INT8 ? "INT8" : "INT4");
+        if (c->dtype == KVQ_INT8 && c->v_scale != c->k_scale + KVQ_BLOCK_SIZE)
+            return fail(KVQ_ERR_SHAPE, "an INT8 cache keeps each tile's K and V scales in one row "
+                        "[num_blocks][Hkv][2][16]: v_scale must be k_scale + 16");
     } else {
         if (!(isfinite(c->kv_scale) && c->kv_scale > 0.0f))
             return fail(KVQ_ERR_ARG, "kv_scale %g must be finite and positive", (double)c->kv_scale);

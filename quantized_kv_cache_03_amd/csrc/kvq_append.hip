@@ -75,7 +75,7 @@ __global__ __launch_bounds__(64) void append_kernel(
         vc0 = encode_int8(v0, sv);
         vc1 = encode_int8(v1, sv);
         if (lane == 0) {
-            const size_t so = ((size_t)blk * Hkv + g) * kBlock + t;
+            const size_t so = int8_scale_index(blk, Hkv, g, t);
             ks[so] = sk;
             vs[so] = sv;
         }

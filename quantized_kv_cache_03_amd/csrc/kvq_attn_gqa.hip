@@ -78,7 +78,7 @@ __device__ __forceinline__ void flush_append_g(const KernelParams& a, PendingApp
         __builtin_nontemporal_store(pa.vd[r], reinterpret_cast<uint32_t*>(vt + v_off + (uint32_t)r * 256u));
     if constexpr (DT == KVQ_INT8) {
         if (lane == 0) {
-            const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
+            const size_t so = int8_scale_index(pa.blk, a.Hkv, g, pa.slot);
             const_cast<float*>(a.ks)[so] = pa.ks;
             const_cast<float*>(a.vs)[so] = pa.vs;
         }
@@ -158,7 +158,7 @@ __device__ __forceinline__ void gqa_segment(const KernelParams& a, int b, int g,
                 for (int r = 0; r < 8; ++r)
                     vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
                 if constexpr (DT == KVQ_INT8) {
-                    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
+                    const size_t so = int8_scale_index(blk, a.Hkv, g, 4 * q4);
                     ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
                     vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
                 } else {

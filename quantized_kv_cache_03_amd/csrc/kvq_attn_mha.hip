@@ -79,7 +79,7 @@ __device__ __forceinline__ void load_tile(const KernelParams& a, Tile& t, int bl
     t.va = ldg16(vt + v_off);
     t.vb = ldg16(vt + 1024u + v_off);
     if constexpr (DT == KVQ_INT8) {
-        const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + tk;
+        const size_t so = int8_scale_index(blk, a.Hkv, g, tk);
         t.ks = ldg_nt(a.ks + so);
         t.vs = ldg_nt(a.vs + so);
     }
@@ -205,7 +205,7 @@ __device__ __forceinline__ void flush_append(const KernelParams& a, PendingAppen
     __builtin_nontemporal_store(pa.vb, reinterpret_cast<u32x4*>(vt + 1024u + 16u * (uint32_t)lane));
     if constexpr (DT == KVQ_INT8) {
         if (lane == 0) {
-            const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
+            const size_t so = int8_scale_index(pa.blk, a.Hkv, g, pa.slot);
             const_cast<float*>(a.ks)[so] = pa.ks;
             const_cast<float*>(a.vs)[so] = pa.vs;
         }

@@ -39,7 +39,7 @@ __global__ __launch_bounds__(64) void dequant_kernel(
     if (tile_idx * kBlock >= n) return;
     const int blk = block_tables[(size_t)b * max_blocks + tile_idx];
     const size_t tile = ((size_t)blk * Hkv + g) * kTileBytes;
-    const size_t sbase = ((size_t)blk * Hkv + g) * kBlock;
+    const size_t sbase = int8_scale_index(blk, Hkv, g, 0);
     const size_t obase = ((size_t)b * Hkv + g) * (size_t)max_ctx * kDim;
 
     // K: chunked tile; in each 1 KiB half lane l reads the 16 codes of token l % 16 in chunk

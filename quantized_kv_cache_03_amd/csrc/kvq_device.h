@@ -32,6 +32,13 @@ __device__ __forceinline__ uint32_t k_byte(int t, int d) {
     return (uint32_t)(d / kChunk) * kChunkBytes + (uint32_t)t * kChunk + (uint32_t)(d % kChunk);
 }
 constexpr float kLog2e = 1.4426950408889634f;
+// INT8 scales: one 128-byte row per (block, KV head) tile, its 16 K scales and then its 16 V scales
+// (the cache's k_scale points at the rows, v_scale = k_scale + 16), so a wave reading a tile's
+// scales reads one whole line.  Index of token t's scale from either pointer:
+constexpr int kScaleRow8 = 2 * kBlock;
+__device__ __forceinline__ size_t int8_scale_index(int blk, int Hkv, int g, int t) {
+    return ((size_t)blk * Hkv + g) * kScaleRow8 + t;
+}
 
 // ------------------------------------------------------------------------------------------------
 // encode (append path).  y is the fp32 quotient x / kv_scale.

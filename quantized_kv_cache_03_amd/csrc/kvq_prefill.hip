@@ -190,7 +190,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
 #pragma unroll
                 for (int r = 0; r < 8; ++r) vb.vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
                 if constexpr (DT == KVQ_INT8) {
-                    const size_t so = ((size_t)blk * a.Hkv + g) * kBlock + 4 * q4;
+                    const size_t so = int8_scale_index(blk, a.Hkv, g, 4 * q4);
                     vb.ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
                     vb.vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
                 }

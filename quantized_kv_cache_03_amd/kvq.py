@@ -104,11 +104,15 @@ def _check(status: int, where: str):
         raise KvqError(status, where)
 
 
+def _device_memory(t: torch.Tensor, what: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be in GPU memory (got a tensor on {t.device})")
+
+
 def _device_tensor(t: torch.Tensor, what: str) -> None:
     """The library reads and writes device memory in the documented layouts: a host tensor, or a
     strided view, would send a kernel to the wrong addresses."""
-    if not t.is_cuda:
-        raise ValueError(f"{what} must be in GPU memory (got a tensor on {t.device})")
+    _device_memory(t, what)
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
 
@@ -166,7 +170,9 @@ class PagedKVCache:
                                     # (INT4: [num_blocks][Hkv][4][16][16], 32-dim chunks)
     v_cache: torch.Tensor           # uint8 [num_blocks][Hkv][128][16] (INT4: [..][128][8])
     k_scale: torch.Tensor | None    # float32 [num_blocks][Hkv][16] (INT8), [..][16][2] (INT4)
-    v_scale: torch.Tensor | None
+    v_scale: torch.Tensor | None    # INT8: k_scale and v_scale are the two halves of one
+                                    # [num_blocks][Hkv][2][16] tensor (a tile's scales in one
+                                    # 128-byte row), as allocate() makes them
     kv_scale: float = 1.0
 
     @property
@@ -189,11 +195,25 @@ class PagedKVCache:
         v = torch.full((num_blocks, num_kv_heads, HEAD_DIM, BLOCK_SIZE // per), fill, dtype=torch.uint8,
                        device=device)
         ks = vs = None
-        if dtype in (INT8, INT4):
-            shape = (num_blocks, num_kv_heads, BLOCK_SIZE) + ((2,) if dtype == INT4 else ())
-            ks = torch.full(shape, float("nan") if poison else 0.0, dtype=torch.float32, device=device)
-            vs = torch.full_like(ks, float("nan") if poison else 0.0)
+        sfill = float("nan") if poison else 0.0
+        if dtype == INT8:
+            rows = torch.full((num_blocks, num_kv_heads, 2, BLOCK_SIZE), sfill, dtype=torch.float32, device=device)
+            ks, vs = rows[:, :, 0], rows[:, :, 1]
+        elif dtype == INT4:
+            ks = torch.full((num_blocks, num_kv_heads, BLOCK_SIZE, 2), sfill, dtype=torch.float32, device=device)
+            vs = torch.full_like(ks, sfill)
         return PagedKVCache(dtype, k, v, ks, vs, float(kv_scale))
+
+    def clone(self) -> "PagedKVCache":
+        """A copy in new device memory, with the same layout (INT8 scales interleaved again)."""
+        c = PagedKVCache.allocate(self.dtype, self.num_blocks, self.num_kv_heads, self.kv_scale,
+                                  device=self.k_cache.device, poison=False)
+        c.k_cache.copy_(self.k_cache)
+        c.v_cache.copy_(self.v_cache)
+        if self.k_scale is not None:
+            c.k_scale.copy_(self.k_scale)
+            c.v_scale.copy_(self.v_scale)
+        return c
 
     def descriptor(self) -> KvqCache:
         per = 2 if self.dtype == INT4 else 1
@@ -207,11 +227,22 @@ class PagedKVCache:
                     raise ValueError(f"{name} is required for this cache dtype")
                 layout[name] = (t, torch.float32, sshape)
         for name, (t, dt, shape) in layout.items():
-            _device_tensor(t, f"cache.{name}")
+            if self.dtype == INT8 and name in ("k_scale", "v_scale"):
+                # the halves of one [nb][Hkv][2][16] tensor: strided views, checked below
+                _device_memory(t, f"cache.{name}")
+            else:
+                _device_tensor(t, f"cache.{name}")
             if t.dtype != dt or tuple(t.shape) != shape:
                 raise ValueError(f"cache.{name} must be {dt} {list(shape)} (got {t.dtype} {list(t.shape)})")
             if t.device != self.k_cache.device:
                 raise ValueError("the cache tensors must be on one device")
+        if self.dtype == INT8:
+            rows = (hkv * 2 * BLOCK_SIZE, 2 * BLOCK_SIZE, 1)
+            if (self.k_scale.stride() != rows or self.v_scale.stride() != rows or
+                    self.v_scale.data_ptr() != self.k_scale.data_ptr() + 4 * BLOCK_SIZE):
+                raise ValueError("INT8 scales must be the two halves of one [num_blocks][Hkv][2][16] float32 "
+                                 "tensor (k_scale = rows[:, :, 0], v_scale = rows[:, :, 1]; "
+                                 "PagedKVCache.allocate makes them so)")
         return KvqCache(self.dtype, self.k_cache.shape[0], BLOCK_SIZE, self.k_cache.shape[1], HEAD_DIM,
                         self.k_cache.data_ptr(), self.v_cache.data_ptr(),
                         self.k_scale.data_ptr() if self.k_scale is not None else None,

@@ -84,6 +84,9 @@ CASES = [
     ("zero scale", dict(kv_scale=0.0), {}, -1),
     ("neg scale", dict(kv_scale=-1.0), {}, -1),
     ("int8 without scales", dict(dtype=3), {}, -1),
+    # INT8 scales are one row per tile: v_scale must be k_scale + 16 floats
+    ("int8 scales apart", dict(dtype=3, k_scale=0x1000, v_scale=0x2000), {}, -3),
+    ("int8 scales 16 B apart", dict(dtype=3, k_scale=0x1000, v_scale=0x1010), {}, -3),
     ("hq not multiple", {}, dict(Hq=3), -3),
     ("group above 16", dict(num_kv_heads=1), dict(Hq=32), -3),
     ("nan sm", {}, dict(sm=float("inf")), -1),
@@ -219,7 +222,7 @@ def test_decode_step_argument_errors(K):
 def test_fp8math_rejects_non_ocp_caches(K, dtype):
     """FP8 math needs OCP E4M3 / E5M2 K codes: INT8, E4M3FNUZ and INT4 caches are KVQ_ERR_DTYPE
     (before any pointer is touched)."""
-    c = _cache(K, dtype=dtype, k_scale=0x70, v_scale=0x80)
+    c = _cache(K, dtype=dtype, k_scale=0x1000, v_scale=0x1040 if dtype == 3 else 0x2000)
     L = K.lib
     assert L.kvq_paged_decode_attn_fp8math(ctypes.byref(c), 0x30, 0x40, 2, 0.1, 0x10, 4, 0x20, 1, 64, 0,
                                            None, 0, None) == K.ERR_DTYPE

@@ -49,6 +49,7 @@ def host_binding(monkeypatch):
 
     monkeypatch.setattr(K, "lib", Stub())
     monkeypatch.setattr(K, "_device_tensor", contiguous_only)
+    monkeypatch.setattr(K, "_device_memory", lambda t, what: None)
     return K
 
 
@@ -108,3 +109,27 @@ def test_binding_checks_every_caller_tensor(host_binding):
         K.append(c, _t((5, 2, 128)), _t((5, 2, 128)), bt, ctx)  # one row per sequence without cu
     with pytest.raises(ValueError):
         K.quantize_q_fp8(_t((4, 64)))
+
+
+def test_int8_scales_are_one_row_per_tile(host_binding):
+    """An INT8 cache's K and V scales are the halves of one [num_blocks][Hkv][2][16] tensor (a tile's
+    scales in one 128-byte row): allocate() and clone() make them so, and separate arrays are
+    refused."""
+    K = host_binding
+    c = K.PagedKVCache.allocate("int8", 3, 2, 1.0, device="cpu")
+    assert c.k_scale.shape == (3, 2, 16) and c.k_scale.stride() == (64, 32, 1)
+    assert c.v_scale.data_ptr() == c.k_scale.data_ptr() + 64
+    d = c.descriptor()
+    assert d.v_scale == d.k_scale + 64
+    c.k_scale.copy_(torch.arange(96, dtype=torch.float32).reshape(3, 2, 16))
+    c.v_scale.fill_(-1.0)
+    c2 = c.clone()
+    assert c2.v_scale.data_ptr() == c2.k_scale.data_ptr() + 64
+    assert torch.equal(c2.k_scale, c.k_scale) and torch.equal(c2.v_scale, c.v_scale)
+    c2.descriptor()
+    apart = K.PagedKVCache(c.dtype, c.k_cache, c.v_cache, c.k_scale.contiguous(), c.v_scale.contiguous(), 1.0)
+    with pytest.raises(ValueError, match="two halves"):
+        apart.descriptor()
+    swapped = K.PagedKVCache(c.dtype, c.k_cache, c.v_cache, c.v_scale, c.k_scale, 1.0)
+    with pytest.raises(ValueError, match="two halves"):
+        swapped.descriptor()

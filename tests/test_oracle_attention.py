@@ -88,6 +88,11 @@ def test_append_layout_and_poison(oracle_mod, dtype):
                     sc = np.abs(xf).max() / np.float32(127)
                     qq = np.clip(np.rint(xf / sc), -127, 127).astype(np.int8)
                     np.testing.assert_array_equal(kc[blk, g, t].view(np.int8), qq)
+                    # one row of 32 floats per (block, head) tile: K scales at 0..15, V at 16..31
+                    flat = cache.rows.reshape(-1)
+                    assert flat[(blk * cache.Hkv + g) * 32 + t] == sc
+                    xv = rv[p, g].astype(np.float32)
+                    assert flat[(blk * cache.Hkv + g) * 32 + 16 + t] == np.abs(xv).max() / np.float32(127)
                     assert cache.ks[blk, g, t] == sc
             else:
                 yk = torch.from_numpy(rk[p].astype(np.float32)) / torch.tensor(np.float32(s))

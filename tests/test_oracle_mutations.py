@@ -46,8 +46,11 @@ MUTATIONS = {
         "float s = amax / 127.0f;",
         "float s = amax / 128.0f;"),
     "int8-v-uses-k-scale": (
-        "return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, t)];",
-        "return (double)(int8_t)c * (double)vs[s_off(Hkv, blk, g, 0)];"),
+        "return (double)(int8_t)c * (double)vs[s_off8(Hkv, blk, g, t)];",
+        "return (double)(int8_t)c * (double)vs[s_off8(Hkv, blk, g, 0)];"),
+    "int8-scale-rows-of-16": (
+        "return ((size_t)blk * Hkv + g) * (2 * KVQO_BLOCK) + t;",
+        "return ((size_t)blk * Hkv + g) * KVQO_BLOCK + t;"),
     "attn-drops-sm-scale": (
         "z[t] = (double)sm_scale * acc;\n        if (z[t] > zmax)\n            zmax = z[t];\n    }\n    double denom = 0.0;\n    for (int t = 0; t < n; ++t) {\n        double w = exp(z[t] - zmax);\n        int blk",
         "z[t] = acc;\n        if (z[t] > zmax)\n            zmax = z[t];\n    }\n    double denom = 0.0;\n    for (int t = 0; t < n; ++t) {\n        double w = exp(z[t] - zmax);\n        int blk"),
