@@ -35,14 +35,14 @@ __device__ __forceinline__ half8_v join4(half2_t a, half2_t b, half2_t c, half2_
 
 // The K operands of one tile: (even, odd) nibble pairs of dwords (0, 1) and (2, 3), every code
 // minus its token's zero code (ne, no): c - c0 in the even operands, 16 (c - c0) in the odd ones.
-__device__ __forceinline__ void k_operands(const u32x4& k, half2_t ne, half2_t no, half8_v (&e)[2],
-                                           half8_v (&o)[2]) {
+__device__ __forceinline__ void k_operands(const u32x4& k, half2_t ne, half2_t no, const Int4Bits& b,
+                                           half8_v (&e)[2], half8_v (&o)[2]) {
     const uint32_t w[4] = {k.x, k.y, k.z, k.w};
     half2_t h0[4], h1[4], h2[4], h3[4];
-    int4x8_centred(w[0], ne, no, h0);
-    int4x8_centred(w[1], ne, no, h1);
-    int4x8_centred(w[2], ne, no, h2);
-    int4x8_centred(w[3], ne, no, h3);
+    int4x8_centred(w[0], ne, no, b, h0);
+    int4x8_centred(w[1], ne, no, b, h1);
+    int4x8_centred(w[2], ne, no, b, h2);
+    int4x8_centred(w[3], ne, no, b, h3);
     e[0] = join4(h0[0], h0[2], h1[0], h1[2]);
     o[0] = join4(h0[1], h0[3], h1[1], h1[3]);
     e[1] = join4(h2[0], h2[2], h3[0], h3[2]);
@@ -61,11 +61,11 @@ __device__ __forceinline__ int k_slot_dim(int dw0, int odd, int slot) {
 // One chunk of kTiles4 tiles (tiles past the segment's end repeat its last one; their tokens are masked).
 template <bool APPEND>
 __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[kTiles4], int tile0, int t_end,
-                                         const half8_v (&qe)[2], const half8_v (&qo)[2], float qsum,
+                                         const half8_v (&qe)[2], const half8_v (&qo)[2], float zq,
                                          int q4, float& m_run, float& l_lane, float& z_lane,
                                          float4_t (&acc)[8]) {
     float z[kTiles4][4];
-    float cmax = kNegInf;
+    const Int4Bits bits = int4_bits();
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i) {
         // every token centred at its own zero code c0 (int4_zero_code), computed once, by the
@@ -79,21 +79,31 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
         half2_t ne, no;
         int4_centre_pairs(zc, ne, no);
         half8_v e[2], o[2];
-        k_operands(t[i].k, ne, no, e, o);
-        float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};  // q . (c - c0), x16 for so
-        se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[0], qe[0], se, 0, 0, 0);
-        so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[0], qo[0], so, 0, 0, 0);
-        se = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[1], qe[1], se, 0, 0, 0);
-        so = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[1], qo[1], so, 0, 0, 0);
-        const int pos0 = (tile0 + i) * kBlock + 4 * q4;
+        k_operands(t[i].k, ne, no, bits, e, o);
+        // q . (c - c0): the odd operands hold 16 (c - c0) and meet q / 16 (qo), so all four
+        // products share one accumulator
+        float4_t s = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[0], qe[0], float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[0], qo[0], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[1], qe[1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[1], qo[1], s, 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float sc = se[u] + so[u] * 0.0625f;
-            const float zz = a.qk_scale * (sc * t[i].ks[u]) + a.qk_scale * (zps[u] * qsum);
-            z[i][u] = (pos0 + u < t_end) ? zz : kNegInf;
-            cmax = fmaxf(cmax, z[i][u]);
+        for (int u = 0; u < 4; ++u) z[i][u] = __builtin_fmaf(s[u], a.qk_scale * t[i].ks[u], zq * zps[u]);
+    }
+    // Tokens at and past t_end are masked; only a chunk that reaches past it has such tokens
+    // (wave-uniform test).
+    if ((tile0 + kTiles4) * kBlock > t_end) {
+#pragma unroll
+        for (int i = 0; i < kTiles4; ++i) {
+            const int pos0 = (tile0 + i) * kBlock + 4 * q4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (pos0 + u >= t_end) z[i][u] = kNegInf;
         }
     }
+    float cmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kTiles4; ++i)
+        cmax = fmaxf(cmax, fmaxf(fmaxf(z[i][0], z[i][1]), fmaxf(z[i][2], z[i][3])));
     // The V parameters of the slots at and past t_end are zeroed (past the context they may be
     // NaN, and a zero weight alone would still give 0 * NaN); only a tile that reaches past the
     // end has such slots (wave-uniform test).
@@ -149,9 +159,9 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
         for (int i = 0; i < kTiles4; ++i) {
             const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
             if (r & 1)
-                int4_unit_to_f16_int<1>(w[r / 2], ve[i], vo[i]);
+                int4_unit_to_f16_int<1>(w[r / 2], bits, ve[i], vo[i]);
             else
-                int4_unit_to_f16_int<0>(w[r / 2], ve[i], vo[i]);
+                int4_unit_to_f16_int<0>(w[r / 2], bits, ve[i], vo[i]);
         }
         const half8_v ae = join4(ve[0], ve[1], ve[2], ve[3]);
         const half8_v ao = join4(vo[0], vo[1], vo[2], vo[3]);
@@ -218,16 +228,19 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
         }
 #pragma unroll
         for (int d = 0; d < 32; ++d) qsum += (float)__builtin_bit_cast(_Float16, qv[d]);
+        // the odd operands take q 16 times smaller: exact for |q| >= 2^-10, and below that off
+        // by at most 2^-25 (negligible beside the sums' own rounding)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 qe[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 0, s)]);
-                qo[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 1, s)]);
+                qo[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 1, s)]) * (_Float16)0.0625f;
             }
     }
     qsum += __shfl_xor(qsum, 16);
     qsum += __shfl_xor(qsum, 32);
+    const float zq = a.qk_scale * qsum;  // the logit term of the zero points is zq * (zp + s c0)
 
     float m_run = kNegInf;
     float l_lane = 0.0f, z_lane = 0.0f;
@@ -261,7 +274,7 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
                         }
                 }
             }
-            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, qsum, q4, m_run, l_lane, z_lane, acc);
+            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, zq, q4, m_run, l_lane, z_lane, acc);
         }
     }
     // the head's weight sum and zero-point sum over the four row groups

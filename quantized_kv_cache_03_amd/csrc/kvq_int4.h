@@ -47,14 +47,30 @@ __device__ __forceinline__ void int4x8_to_f16(uint32_t w, half2_t (&h)[4]) {
 // as above keep only about 14 bits of each product there.  The matrix-core kernels therefore give the K codes as
 // exact small binary16 integers, centred: in the pairs (i, i + 4) of int4x8_to_f16, the even pairs as
 // n - c0 = (1024 + n) - (1024 + c0) and the odd ones as 16 (n - c0) = (1024 + 16 n) - (1024 + 16 c0),
-// each the code placed under the exponent of 1024 (one AND-OR) and one packed fp16 addition of
-// ne = -(1024 + c0) or no = -(1024 + 16 c0).
-__device__ __forceinline__ void int4x8_centred(uint32_t w, half2_t ne, half2_t no, half2_t (&h)[4]) {
+// each the code placed under the exponent of 1024 (one v_and_or_b32, Int4Bits) and one packed fp16
+// addition of ne = -(1024 + c0) or no = -(1024 + 16 c0).
+//
+// Int4Bits holds the two nibble masks (in SGPRs) and the exponent pattern 0x6400 of 1024 (in a
+// VGPR).  With literal operands the compiler issues an AND and an OR for every mask-and-insert; with
+// the operands in registers, one v_and_or_b32.  The identity DPP move only hides the constants from
+// constant folding.
+struct Int4Bits {
+    uint32_t even, odd, magic;
+};
+__device__ __forceinline__ uint32_t int4_opaque(uint32_t c) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xE4, 0xF, 0xF, false);
+}
+__device__ __forceinline__ Int4Bits int4_bits() {
+    return {(uint32_t)__builtin_amdgcn_readfirstlane(int4_opaque(0x000F000Fu)),
+            (uint32_t)__builtin_amdgcn_readfirstlane(int4_opaque(0x00F000F0u)), int4_opaque(0x64006400u)};
+}
+__device__ __forceinline__ void int4x8_centred(uint32_t w, half2_t ne, half2_t no, const Int4Bits& b,
+                                               half2_t (&h)[4]) {
     const uint32_t w8 = w >> 8;
-    h[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | 0x64006400u) + ne;
-    h[1] = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | 0x64006400u) + no;
-    h[2] = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | 0x64006400u) + ne;
-    h[3] = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | 0x64006400u) + no;
+    h[0] = __builtin_bit_cast(half2_t, (w & b.even) | b.magic) + ne;
+    h[1] = __builtin_bit_cast(half2_t, (w & b.odd) | b.magic) + no;
+    h[2] = __builtin_bit_cast(half2_t, (w8 & b.even) | b.magic) + ne;
+    h[3] = __builtin_bit_cast(half2_t, (w8 & b.odd) | b.magic) + no;
 }
 
 // The code of a row (scale s, zero point zp) whose value s c + zp is nearest zero, clamped to
@@ -146,15 +162,16 @@ __device__ __forceinline__ float wave_min(float v) {
 
 // The 16-bit unit of a V dword (as int4_unit_to_f16: e = tokens (0, 2), o = tokens (1, 3)) as exact
 // binary16 integers for the matrix cores: e = c and o = 16 c, each the code placed under the exponent
-// of 1024 (one AND-OR) less 1024 (one packed fp16 addition).  The odd tokens' weights are taken
-// sixteen times smaller (exact), so both products land in one accumulator in units of c.
+// of 1024 (one v_and_or_b32, Int4Bits) less 1024 (one packed fp16 addition).  The odd tokens'
+// weights are taken sixteen times smaller (exact), so both products land in one accumulator in
+// units of c.
 template <int SEL>
-__device__ __forceinline__ void int4_unit_to_f16_int(uint32_t w, half2_t& e, half2_t& o) {
+__device__ __forceinline__ void int4_unit_to_f16_int(uint32_t w, const Int4Bits& b, half2_t& e, half2_t& o) {
     constexpr uint32_t sel = (SEL == 0) ? 0x0C010C00u : 0x0C030C02u;
     const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
     const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    e = __builtin_bit_cast(half2_t, (x & 0x000F000Fu) | 0x64006400u) + m1024;
-    o = __builtin_bit_cast(half2_t, (x & 0x00F000F0u) | 0x64006400u) + m1024;
+    e = __builtin_bit_cast(half2_t, (x & b.even) | b.magic) + m1024;
+    o = __builtin_bit_cast(half2_t, (x & b.odd) | b.magic) + m1024;
 }
 constexpr float kInt4OddWeight = 0.0625f;  // 1 / 16
 

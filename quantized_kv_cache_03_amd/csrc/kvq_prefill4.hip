@@ -46,11 +46,12 @@ struct Prefill4Params {
 // The K operands of one tile in the k-slot order of kslot_dim: the four MFMAs take the (0, 4),
 // (2, 6) nibble pairs and then the (1, 5), (3, 7) pairs of dwords (0, 1) and of dwords (2, 3); every
 // code minus its token's zero code (ne, no): c - c0 in operands 0 and 2, 16 (c - c0) in operands 1 and 3.
-__device__ __forceinline__ void k_operands_p4(const u32x4& k, half2_t ne, half2_t no, half8_v (&op)[4]) {
+__device__ __forceinline__ void k_operands_p4(const u32x4& k, half2_t ne, half2_t no, const Int4Bits& b,
+                                              half8_v (&op)[4]) {
     const uint32_t w[4] = {k.x, k.y, k.z, k.w};
     half2_t h[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) int4x8_centred(w[j], ne, no, h[j]);
+    for (int j = 0; j < 4; ++j) int4x8_centred(w[j], ne, no, b, h[j]);
     op[0] = join8(h[0][0], h[0][2], h[1][0], h[1][2]);
     op[1] = join8(h[0][1], h[0][3], h[1][1], h[1][3]);
     op[2] = join8(h[2][0], h[2][2], h[3][0], h[3][2]);
@@ -131,12 +132,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             }
 #pragma unroll
             for (int d = 0; d < 32; ++d) qsum[nb] += (float)__builtin_bit_cast(_Float16, qv[d]);
+            // the odd operands (1, 3) take q 16 times smaller, so that all four K products share
+            // one accumulator: exact for |q| >= 2^-10, and below that off by at most 2^-25
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int s = 0; s < 8; ++s) qB[nb][m][s] = __builtin_bit_cast(_Float16, qv[kslot_dim(m, s)]);
+                for (int s = 0; s < 8; ++s)
+                    qB[nb][m][s] = __builtin_bit_cast(_Float16, qv[kslot_dim(m, s)]) *
+                                   (_Float16)((m & 1) ? 0.0625f : 1.0f);
         }
-        qsum[nb] = col_sum4(qsum[nb]);
+        qsum[nb] = a.qk_scale * col_sum4(qsum[nb]);  // the logit term of the zero points: qsum * zp'
     }
 
     float m_run[NB], l_lane[NB], z_lane[NB];
@@ -162,6 +167,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
                                 __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
             const int tok_base = (tb + c0) * kBlock;
+            const Int4Bits bits = int4_bits();
             float z[NB][kTilesP4][4];
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
@@ -170,22 +176,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 half2_t ne, no;
                 int4_centre_pairs(int4_zero_code(t[i].kp.x, t[i].kp.y), ne, no);
                 half8_v kop[4];
-                k_operands_p4(t[i].k, ne, no, kop);
+                k_operands_p4(t[i].k, ne, no, bits, kop);
                 float zp[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     zp[u] = __builtin_fmaf(t[i].ks[u], int4_zero_code(t[i].ks[u], t[i].kz[u]), t[i].kz[u]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    float4_t se = {0.0f, 0.0f, 0.0f, 0.0f}, so = {0.0f, 0.0f, 0.0f, 0.0f};  // so: x16
-                    se = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[0], qB[nb][0], se, 0, 0, 0);
-                    so = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[1], qB[nb][1], so, 0, 0, 0);
-                    se = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[2], qB[nb][2], se, 0, 0, 0);
-                    so = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[3], qB[nb][3], so, 0, 0, 0);
+                    float4_t s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[0], qB[nb][0],
+                                                                        float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[1], qB[nb][1], s, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[2], qB[nb][2], s, 0, 0, 0);
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[3], qB[nb][3], s, 0, 0, 0);
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        z[nb][i][u] = a.qk_scale * ((se[u] + so[u] * 0.0625f) * t[i].ks[u]) +
-                                      a.qk_scale * (zp[u] * qsum[nb]);
+                        z[nb][i][u] = __builtin_fmaf(s[u], a.qk_scale * t[i].ks[u], qsum[nb] * zp[u]);
                 }
             }
             // The causal mask, only for the chunks that reach past the wave's first row
@@ -268,9 +273,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 for (int i = 0; i < kTilesP4; ++i) {
                     const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
                     if (r & 1)
-                        int4_unit_to_f16_int<1>(w[r / 2], ve[i], vo[i]);
+                        int4_unit_to_f16_int<1>(w[r / 2], bits, ve[i], vo[i]);
                     else
-                        int4_unit_to_f16_int<0>(w[r / 2], ve[i], vo[i]);
+                        int4_unit_to_f16_int<0>(w[r / 2], bits, ve[i], vo[i]);
                 }
                 const half8_v ae = join8(ve[0], ve[1], ve[2], ve[3]);
                 const half8_v ao = join8(vo[0], vo[1], vo[2], vo[3]);

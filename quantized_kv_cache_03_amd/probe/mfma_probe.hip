@@ -99,10 +99,11 @@ __global__ __launch_bounds__(64) void int4_centred(const uint32_t* codes, const 
     const uint32_t* w = codes + ((size_t)p * 64 + l) * 4;
     kvq::half2_t ne, no;
     kvq::int4_centre_pairs(c0s[p], ne, no);
+    const kvq::Int4Bits bits = kvq::int4_bits();
     kvq::half2_t h[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        kvq::int4x8_centred(w[j], ne, no, h[j]);
+        kvq::int4x8_centred(w[j], ne, no, bits, h[j]);
 #pragma unroll
         for (int k = 0; k < 4; ++k) dec[((size_t)p * 64 + l) * 16 + 4 * j + k] = __builtin_bit_cast(uint32_t, h[j][k]);
     }
