@@ -259,7 +259,7 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
             TileMfma4 t[kTiles4];
 #pragma unroll
             for (int i = 0; i < kTiles4; ++i)
-                load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                load_tile_mfma4<true>(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
             if constexpr (APPEND) {
                 const int inew = tile_new - (tb + c0);  // wave-uniform
                 if (inew >= 0 && inew < kTiles4) {

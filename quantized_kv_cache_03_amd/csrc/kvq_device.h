@@ -225,5 +225,15 @@ template <typename T>
 __device__ __forceinline__ T ldg_nt(const T* p) {
     return __builtin_nontemporal_load(p);
 }
+// Prefill reads each tile once per row tile of its sequence, so its loads keep the ordinary
+// caching: the streaming hint would evict the lines the sequence's other row tiles are about to
+// read (measured: twice the kernel time).
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
 
 }  // namespace kvq

@@ -120,20 +120,22 @@ struct TileMfma4 {
 };
 
 // Load tile (blk, g) for this lane (off = 256 q4 + 16 col); ks / vs are the [blocks][Hkv][16][2]
-// pair arrays.
+// pair arrays.  NT: the streaming hint (decode reads each tile once; prefill re-reads it for every
+// row tile of the sequence and keeps the ordinary caching).
+template <bool NT>
 __device__ __forceinline__ void load_tile_mfma4(const uint8_t* kc, const uint8_t* vc, const float* ks,
                                                 const float* vs, int Hkv, TileMfma4& t, int blk, int g,
                                                 uint32_t off, int q4) {
     const size_t tile = ((size_t)blk * Hkv + g) * kTileBytes4;
-    t.k = ldg16(kc + tile + off);
-    t.v = ldg16(vc + tile + off);
-    t.kp = ldg_nt(reinterpret_cast<const f32x2*>(ks) + ((size_t)blk * Hkv + g) * kBlock + ((off >> 4) & 15u));
+    t.k = ld<NT>(reinterpret_cast<const u32x4*>(kc + tile + off));
+    t.v = ld<NT>(reinterpret_cast<const u32x4*>(vc + tile + off));
+    t.kp = ld<NT>(reinterpret_cast<const f32x2*>(ks) + ((size_t)blk * Hkv + g) * kBlock + ((off >> 4) & 15u));
     // (scale, zero point) pairs of four tokens: two 16-byte loads each for K and V
     const size_t so = (((size_t)blk * Hkv + g) * kBlock + 4 * q4) * 2;
-    const float4_t k0 = ldg_nt(reinterpret_cast<const float4_t*>(ks + so));
-    const float4_t k1 = ldg_nt(reinterpret_cast<const float4_t*>(ks + so + 4));
-    const float4_t v0 = ldg_nt(reinterpret_cast<const float4_t*>(vs + so));
-    const float4_t v1 = ldg_nt(reinterpret_cast<const float4_t*>(vs + so + 4));
+    const float4_t k0 = ld<NT>(reinterpret_cast<const float4_t*>(ks + so));
+    const float4_t k1 = ld<NT>(reinterpret_cast<const float4_t*>(ks + so + 4));
+    const float4_t v0 = ld<NT>(reinterpret_cast<const float4_t*>(vs + so));
+    const float4_t v1 = ld<NT>(reinterpret_cast<const float4_t*>(vs + so + 4));
     t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
     t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
     t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};

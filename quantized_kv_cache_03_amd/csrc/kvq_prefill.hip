@@ -43,30 +43,52 @@ struct PrefillParams {
     int32_t Hkv;
     int32_t G;              // query heads per KV head
     int32_t R;              // query rows per column block (16 / G)
-    int32_t row_tiles;      // grid extent over row tiles (NB R rows each)
+    int32_t row_tiles;      // grid extent over groups of kPfWaves row tiles (NB R rows each)
     float qk_scale;         // sm_scale * log2(e) (* kv_scale * code_unit for FP8)
     float v_scale;          // kv_scale * code_unit for FP8, 1 for INT8
 };
 
 // NB column blocks of 16 per wave (NB R consecutive rows): the K and V^T operands of a tile are
-// decoded once and feed the MFMAs of every block, which is what keeps the VALU from limiting.
+// decoded once and feed the MFMAs of every block.  A workgroup is kPfWaves waves holding
+// consecutive row tiles of one (KV head, sequence); they read the same K/V tiles (each up to its own
+// causal limit), so each chunk of TW tiles is loaded from memory once per workgroup into LDS and
+// every wave reads its operands from there.  Loading every chunk once per wave left the kernel
+// waiting on memory: a timing copy with the loads removed ran 1.9 times faster.
+#ifndef KVQ_PREFILL_WAVES
+#define KVQ_PREFILL_WAVES 4
+#endif
+constexpr int kPfWaves = KVQ_PREFILL_WAVES;
+constexpr int kPfTW = 2;  // tiles per chunk, paired for the PV products
+
+// One staged chunk: the tiles' codes as stored, and for INT8 the tiles' scale rows (K then V).
+struct alignas(16) PfStage {
+    uint8_t k[kPfTW][kTileBytes];
+    uint8_t v[kPfTW][kTileBytes];
+    float s[kPfTW][2 * kBlock];
+};
+
 template <int DT, int NB, bool F8Q>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 : (NB > 1 ? 2 : (DT == KVQ_INT8 ? 3 : 4)), 8))) void attn_prefill_mfma(
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_prefill_mfma(
     PrefillParams a) {
-    constexpr int TW = 2;  // tiles per chunk, paired for the PV products
+    constexpr int TW = kPfTW;
+    __shared__ PfStage stage[3];  // three chunks: one read by the softmax, one by S^T, one filling
     const int g = blockIdx.x;
-    // the row tiles of a sequence run last-first: later rows read more tiles (longest work first)
-    const int rt = a.row_tiles - 1 - (int)blockIdx.y;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // the row-tile groups of a sequence run last-first: later rows read more tiles (longest first)
+    const int rt = kPfWaves * (a.row_tiles - 1 - (int)blockIdx.y) + wave;
     const int b = blockIdx.z;
-    const int lane = threadIdx.x;
     const int col = lane & 15;  // column of each block: (row jr, head hg)
     const int q4 = lane >> 4;   // MFMA k-group / C row group
 
     const int r0 = a.cu_q[b];
     const int nq = a.cu_q[b + 1] - r0;
-    const int j0 = rt * (NB * a.R);
-    if (j0 >= nq) return;
+    const int rows_wave = NB * a.R;
+    const int j0 = rt * rows_wave;
+    const int j0_first = (rt - wave) * rows_wave;  // the workgroup's first row
+    if (j0_first >= nq) return;                    // (workgroup-uniform)
     const int n = a.ctx[b];
+    const bool rows = j0 < nq;  // this wave holds query rows (the others only help load)
     const int jr = col / a.G, hg = col % a.G;
     bool live[NB];        // the column of block nb holds a real (row, head)
     size_t orow[NB];
@@ -84,11 +106,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
                 for (int r = 0; r < 8; ++r)
                     *reinterpret_cast<half4_t*>(a.out + orow[nb] + 16 * r + 4 * q4) = half4_t{0, 0, 0, 0};
             }
-        return;
+        return;  // (workgroup-uniform)
     }
-    const int pos_min = n - nq + j0;                 // the wave's first row: every column sees 0..pos_min
-    const int t_end = n - nq + min(nq, j0 + NB * a.R);  // tokens the wave reads: up to its last row
-    const int tile_end = (t_end + kBlock - 1) / kBlock;
+    const int pos_min = n - nq + j0;                    // the wave's first row: every column sees 0..pos_min
+    const int t_end = n - nq + min(nq, j0 + rows_wave);  // tokens the wave reads: up to its last row
+    const int tile_end = rows ? (t_end + kBlock - 1) / kBlock : 0;
+    // the workgroup's tiles: those of its last wave with rows
+    const int wg_t_end = n - nq + min(nq, j0_first + kPfWaves * rows_wave);
+    const int wg_tile_end = (wg_t_end + kBlock - 1) / kBlock;
     int pos[NB];  // last visible position of each block's column (padding columns: pos_min)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) pos[nb] = live[nb] ? n - nq + j0 + nb * a.R + jr : pos_min;
@@ -127,12 +152,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
     const uint32_t k_off = 16u * (uint32_t)lane;  // chunk q4 (+4): token col, dims 16 q4 (+64)
     const uint32_t v_off = (uint32_t)col * kBlock + 4u * (uint32_t)q4;  // dim col (+16 r), tokens 4 q4
 
-    // Block ids in groups of 64 tiles, one per lane: ids_cur for group grp, ids_nxt for grp + 1 (loaded
-    // a group ahead, so a load never waits for the table).  Every tile a load touches lies in one of
-    // the two groups: K runs two chunks ahead of the softmax, V one.
+    // Block ids in groups of 64 tiles, one per lane (the same in every wave): ids_cur for group grp,
+    // ids_nxt for grp + 1 (loaded a group ahead).  The staging loads run two chunks ahead.
     auto load_ids = [&](int group) {
         const int t = group * 64 + lane;
-        return t < tile_end ? bt[t] : 0;
+        return t < wg_tile_end ? bt[t] : 0;
     };
     int grp = 0;
     int ids_cur = load_ids(0), ids_nxt = load_ids(1);
@@ -140,7 +164,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         return (t >> 6) == grp ? __builtin_amdgcn_readlane(ids_cur, t & 63)
                                : __builtin_amdgcn_readlane(ids_nxt, t & 63);
     };
-    // the next K load reads tile t: keep its group in the two id registers
     auto ids_for = [&](int t) {
         if ((t >> 6) > grp + 1) {
             ++grp;
@@ -149,67 +172,53 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         }
     };
 
-    // Software pipeline over chunks of TW tiles, three stages kept in flight: the K codes of chunk
-    // c + 2 are loading, the S^T MFMAs of chunk c + 1 are issued, and chunk c's softmax and P V^T run
-    // -- so the VALU work of one chunk overlaps the matrix cores' work on the next.  Two buffers of
-    // each kind, swapped by unrolling the loop by two.
-    struct KBuf { u32x4 ka[TW], kb[TW]; };
-    struct VBuf { uint32_t vd[TW][8]; float4_t ks4[TW], vs4[TW]; };
-    struct SBuf { float4_t s[NB][TW]; };
-    // A chunk's tiles at or past tile_end repeat tile tile_end - 1 (its first tile is always valid,
-    // and the repeat lies between it and the loaded tile, so its id is in the two id registers):
-    // the loads are unconditional, so no zero-filled registers make the wave wait for loads still
-    // in flight.  The repeats' tokens lie past every column's causal limit and past t_end: their
-    // logits are masked and their V codes zeroed.  INT8 runs one chunk at a time with nothing in
-    // flight across chunks, and zero-fills those tiles instead (measured faster there).
-    auto load_k = [&](KBuf& kb_, int t0) {
-#pragma unroll
-        for (int i = 0; i < TW; ++i) {
-            if (DT == KVQ_INT8 && t0 + i >= tile_end) {
-                kb_.ka[i] = u32x4{0u, 0u, 0u, 0u};
-                kb_.kb[i] = u32x4{0u, 0u, 0u, 0u};
-            } else {
-                const int t = min(t0 + i, tile_end - 1);
-                const uint8_t* kt = a.kc + ((size_t)block_of(t) * a.Hkv + g) * kTileBytes;
-                kb_.ka[i] = ldg16(kt + k_off);
-                kb_.kb[i] = ldg16(kt + k_off + 1024u);
-            }
+    // Staging: wave w loads tile t0 + w / 2 of the chunk, its K codes (w even, with the INT8 scale
+    // row in lanes 0..7) or its V codes (w odd): 32 bytes per lane.  Tiles at or past the
+    // workgroup's last repeat that tile; their tokens are masked by every wave.
+    const int st_tile = (wave >> 1) & 1;
+    const bool st_k = (wave & 1) == 0;
+    const bool stager = wave < 2 * kPfTW;  // the first four waves stage; any others only compute
+    struct Staged { u32x4 x0, x1; float4_t sc; };
+    auto stage_load = [&](int t0) {
+        Staged r{};
+        if (!stager) return r;
+        const int blk = block_of(min(t0 + st_tile, wg_tile_end - 1));
+        const uint8_t* src = (st_k ? a.kc : a.vc) + ((size_t)blk * a.Hkv + g) * kTileBytes;
+        r.x0 = ld16(src + 32u * (uint32_t)lane);
+        r.x1 = ld16(src + 32u * (uint32_t)lane + 16u);
+        r.sc = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (DT == KVQ_INT8) {
+            if (st_k && lane < 8)
+                r.sc = *reinterpret_cast<const float4_t*>(a.ks + int8_scale_index(blk, a.Hkv, g, 0) + 4 * lane);
         }
+        return r;
     };
-    auto load_v = [&](VBuf& vb, int t0) {
-#pragma unroll
-        for (int i = 0; i < TW; ++i) {
-            if (DT == KVQ_INT8 && t0 + i >= tile_end) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) vb.vd[i][r] = 0u;
-                vb.ks4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                vb.vs4[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            } else {
-                const int blk = block_of(min(t0 + i, tile_end - 1));
-                const uint8_t* vt = a.vc + ((size_t)blk * a.Hkv + g) * kTileBytes;
-#pragma unroll
-                for (int r = 0; r < 8; ++r) vb.vd[i][r] = ldg4(vt + v_off + (uint32_t)r * 256u);
-                if constexpr (DT == KVQ_INT8) {
-                    const size_t so = int8_scale_index(blk, a.Hkv, g, 4 * q4);
-                    vb.ks4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.ks + so));
-                    vb.vs4[i] = ldg_nt(reinterpret_cast<const float4_t*>(a.vs + so));
-                }
-            }
+    auto stage_store = [&](PfStage& st, const Staged& r) {
+        if (!stager) return;
+        uint8_t* dst = (st_k ? st.k[st_tile] : st.v[st_tile]) + 32u * (uint32_t)lane;
+        *reinterpret_cast<u32x4*>(dst) = r.x0;
+        *reinterpret_cast<u32x4*>(dst + 16) = r.x1;
+        if constexpr (DT == KVQ_INT8) {
+            if (st_k && lane < 8) *reinterpret_cast<float4_t*>(&st.s[st_tile][4 * lane]) = r.sc;
         }
     };
 
+    struct SBuf { float4_t s[NB][TW]; };
+
     // S^T of a chunk for every block, from the K operands decoded once (FP8 math: used as loaded)
-    auto scores = [&](const KBuf& kb_, SBuf& sb) {
+    auto scores = [&](const PfStage& st, SBuf& sb) {
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(st.k[i] + k_off);
+            const u32x4 kb = *reinterpret_cast<const u32x4*>(st.k[i] + 1024u + k_off);
             if constexpr (F8Q) {
-                const i32x8 k8 = k_fp8x32(kb_.ka[i], kb_.kb[i]);
+                const i32x8 k8 = k_fp8x32(ka, kb);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
                     sb.s[nb][i] = mfma_qk_fp8<DT>(k8, q8[nb], float4_t{0.0f, 0.0f, 0.0f, 0.0f});
             } else {
-                const half8_v k0 = codes8<DT>(kb_.ka[i].x, kb_.ka[i].y), k1 = codes8<DT>(kb_.ka[i].z, kb_.ka[i].w);
-                const half8_v k2 = codes8<DT>(kb_.kb[i].x, kb_.kb[i].y), k3 = codes8<DT>(kb_.kb[i].z, kb_.kb[i].w);
+                const half8_v k0 = codes8<DT>(ka.x, ka.y), k1 = codes8<DT>(ka.z, ka.w);
+                const half8_v k2 = codes8<DT>(kb.x, kb.y), k3 = codes8<DT>(kb.z, kb.w);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     float4_t c = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -225,8 +234,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
 
     // Softmax of a chunk and its P V^T, with the lazy rescale (kRescaleSlack, kRescaleSlackInt8; a
     // branch every lane takes or skips together).
-    auto softmax_pv = [&](VBuf& vb, const SBuf& sb, int t0) {
+    auto softmax_pv = [&](const PfStage& st, const SBuf& sb, int t0) {
         const int tok_base = t0 * kBlock;  // first token of the chunk
+        float4_t ks4[TW], vs4[TW];         // INT8: the scales of this lane's four tokens of each tile
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            ks4[i] = vs4[i] = float4_t{1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (DT == KVQ_INT8) {
+                ks4[i] = *reinterpret_cast<const float4_t*>(&st.s[i][4 * q4]);
+                vs4[i] = *reinterpret_cast<const float4_t*>(&st.s[i][kBlock + 4 * q4]);
+            }
+        }
         float z[NB][TW][4];
 #pragma unroll
         for (int i = 0; i < TW; ++i)
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     float f = qk_f[nb];
-                    if constexpr (DT == KVQ_INT8) f *= vb.ks4[i][t];
+                    if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
                     z[nb][i][t] = sb.s[nb][i][t] * f;
                 }
         // The causal mask: a token past the column's own position gets -inf.  Only the chunks that
@@ -292,7 +310,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
                     const float pw = __builtin_amdgcn_exp2f(z[nb][u][t] - m_run[nb]);
                     l_lane[nb] += pw;
                     w[t] = pw;
-                    if constexpr (DT == KVQ_INT8) w[t] = (pw > 0.0f) ? pw * vb.vs4[u][t] : 0.0f;
+                    if constexpr (DT == KVQ_INT8) w[t] = (pw > 0.0f) ? pw * vs4[u][t] : 0.0f;
                 }
                 split_hi_lo(w[0], w[1], h[2 * u], l[2 * u]);
                 split_hi_lo(w[2], w[3], h[2 * u + 1], l[2 * u + 1]);
@@ -300,20 +318,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
             whi[nb] = __builtin_bit_cast(half8_v, u32x4{h[0], h[1], h[2], h[3]});
             wlo[nb] = __builtin_bit_cast(half8_v, u32x4{l[0], l[1], l[2], l[3]});
         }
+        uint32_t vd[TW][8];
+#pragma unroll
+        for (int i = 0; i < TW; ++i)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                vd[i][r] = *reinterpret_cast<const uint32_t*>(st.v[i] + v_off + (uint32_t)r * 256u);
         // V codes of the slots at and past t_end are zeroed (past the context they may hold NaN
         // codes; a zero weight alone would still give 0 * NaN); chunks inside it need nothing
         if (tok_base + TW * kBlock > t_end) {
             const int valid0 = t_end - tok_base - 4 * q4;
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                vb.vd[0][r] = keep_bytes(vb.vd[0][r], valid0);
-                vb.vd[1][r] = keep_bytes(vb.vd[1][r], valid0 - kBlock);
+                vd[0][r] = keep_bytes(vd[0][r], valid0);
+                vd[1][r] = keep_bytes(vd[1][r], valid0 - kBlock);
             }
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const half8_v va8 = join8(codes_to_f16<DT, 0>(vb.vd[0][r]), codes_to_f16<DT, 1>(vb.vd[0][r]),
-                                      codes_to_f16<DT, 0>(vb.vd[1][r]), codes_to_f16<DT, 1>(vb.vd[1][r]));
+            const half8_v va8 = join8(codes_to_f16<DT, 0>(vd[0][r]), codes_to_f16<DT, 1>(vd[0][r]),
+                                      codes_to_f16<DT, 0>(vd[1][r]), codes_to_f16<DT, 1>(vd[1][r]));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi[nb], acc[nb][r], 0, 0, 0);
@@ -322,47 +346,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NB >= 4 ? 1 
         }
     };
 
-    // One pipeline step for chunk c = t0 / TW: K loads of chunk c + 2 into kc_ (free: its chunk's
-    // S^T was issued one step ago), V loads of chunk c + 1 into vn, S^T of chunk c + 1 from kn into
-    // sn, then chunk c's softmax and P V^T from vc_ and sc.
-    auto step = [&](KBuf& kc_, KBuf& kn, VBuf& vc_, VBuf& vn, SBuf& sc, SBuf& sn, int t0) {
-        if (t0 + 2 * TW < tile_end) {
-            ids_for(t0 + 3 * TW - 1);
-            load_k(kc_, t0 + 2 * TW);
+    // Pipeline over the workgroup's chunks, three LDS buffers: at step c the staging loads of chunk
+    // c + 2 are in flight, S^T of chunk c + 1 is issued from its buffer, chunk c's softmax and
+    // P V^T read theirs, and then chunk c + 2 is stored into the buffer chunk c - 1 used; one
+    // barrier per step.  A wave computes only the chunks up to its own last tile.
+    const int nch = (wg_tile_end + TW - 1) / TW;
+    {
+        ids_for(min(2 * TW - 1, wg_tile_end - 1));
+        const Staged s0 = stage_load(0);
+        stage_store(stage[0], s0);
+        if (nch > 1) {
+            const Staged s1 = stage_load(TW);
+            stage_store(stage[1], s1);
         }
-        if (t0 + TW < tile_end) {
-            load_v(vn, t0 + TW);
-            scores(kn, sn);
+        __syncthreads();
+    }
+    SBuf SA, SB;
+    if (0 < tile_end) scores(stage[0], SA);
+    auto step = [&](SBuf& sc, SBuf& sn, int c) {
+        const int t0 = c * TW;
+        Staged nx;
+        const bool more = c + 2 < nch;  // (workgroup-uniform)
+        if (more) {
+            ids_for(min(t0 + 3 * TW - 1, wg_tile_end - 1));
+            nx = stage_load(t0 + 2 * TW);
         }
-        softmax_pv(vc_, sc, t0);
+        if (t0 + TW < tile_end) scores(stage[(c + 1) % 3], sn);
+        if (t0 < tile_end) softmax_pv(stage[c % 3], sc, t0);
+        if (more) stage_store(stage[(c + 2) % 3], nx);
+        __syncthreads();
     };
-
-    if constexpr (DT == KVQ_INT8) {
-        // the per-token scales do not fit in registers twice: one chunk at a time
-        KBuf K;
-        VBuf V;
-        SBuf S;
-        for (int t0 = 0; t0 < tile_end; t0 += TW) {
-            ids_for(t0 + TW - 1);
-            load_k(K, t0);
-            load_v(V, t0);
-            scores(K, S);
-            softmax_pv(V, S, t0);
-        }
-    } else {
-        KBuf KA, KB;
-        VBuf VA, VB;
-        SBuf SA, SB;
-        ids_for(2 * TW - 1);
-        load_k(KA, 0);
-        load_v(VA, 0);
-        if (TW < tile_end) load_k(KB, TW);
-        scores(KA, SA);
-        for (int t0 = 0; t0 < tile_end; t0 += 2 * TW) {
-            step(KA, KB, VA, VB, SA, SB, t0);
-            if (t0 + TW >= tile_end) break;
-            step(KB, KA, VB, VA, SB, SA, t0 + TW);
-        }
+    for (int c = 0; c < nch; c += 2) {
+        step(SA, SB, c);
+        if (c + 1 >= nch) break;
+        step(SB, SA, c + 1);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -403,8 +420,9 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
     a.Hkv = c.num_kv_heads;
     a.G = p.num_q_heads / c.num_kv_heads;
     a.R = 16 / a.G;
-    const int rows_per_wave = KVQ_PREFILL_BLOCKS * a.R;
-    a.row_tiles = (p.max_q_len + rows_per_wave - 1) / rows_per_wave;
+    // row_tiles counts groups of kPfWaves row tiles (one workgroup each)
+    const int rows_per_group = kPfWaves * KVQ_PREFILL_BLOCKS * a.R;
+    a.row_tiles = (p.max_q_len + rows_per_group - 1) / rows_per_group;
     const bool fp8 = is_fp8(c.dtype);
     // the decoders give code values divided by code_unit (a power of two): fold it into the scales
     const float unit_scale = fp8 ? c.kv_scale * code_unit(c.dtype) : 1.0f;
@@ -413,9 +431,9 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
     const dim3 grid((unsigned)a.Hkv, (unsigned)a.row_tiles, (unsigned)p.batch);
     auto go = [&](auto kernel) {
         if (start)
-            hipExtLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, start, stop, 0, a);
+            hipExtLaunchKernelGGL(kernel, grid, dim3(64 * kPfWaves), 0, stream, start, stop, 0, a);
         else
-            hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, a);
+            hipLaunchKernelGGL(kernel, grid, dim3(64 * kPfWaves), 0, stream, a);
     };
     if (p.fp8_math) {
         if (c.dtype == KVQ_FP8_E5M2) go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, true>);

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             TileMfma4 t[kTilesP4];  // this lane's share of each tile (kvq_int4.h)
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i)
-                load_tile_mfma4(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
+                load_tile_mfma4<false>(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
                                 __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
             const int tok_base = (tb + c0) * kBlock;
             const Int4Bits bits = int4_bits();
