@@ -137,6 +137,13 @@ class DeviceCase:
                   self.max_ctx, partition_size=self.partition_size, workspace=self.workspace,
                   out=self.out_d, stream=stream)
 
+    def prepared_step(self, cache=None, stream=None) -> K.PreparedCall:
+        """The fused step of step() on `cache` (default: this case's), checked and marshalled once."""
+        return K.prepare_decode_step(self.cache if cache is None else cache, self.step_k_d, self.step_v_d,
+                                     self.q_d, self.bt_d, self.ctx_d, self.max_ctx,
+                                     partition_size=self.partition_size, workspace=self.workspace,
+                                     out=self.out_d, stream=stream, fp8_math=self.w.fp8_math)
+
     # host views of the sequences' own rows (regenerated from the seeds)
     def rows_of(self, b: int):
         if self.k_host is not None:

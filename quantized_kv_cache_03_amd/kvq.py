@@ -382,6 +382,48 @@ def _decode_step(name, cache, k_new, v_new, q, block_tables, context_lens, max_c
     return out
 
 
+class PreparedCall:
+    """One library call whose arguments were checked and marshalled once: calling it only invokes
+    the entry point again, with the same device buffers, sizes and stream.  For a loop that issues
+    the same call step after step (a serving loop, a benchmark), where the binding's per-call
+    checks would otherwise cost more host time than a small step's kernels take."""
+
+    def __init__(self, name: str, args: tuple, keep: tuple, result: torch.Tensor):
+        self._name = name
+        self._fn = getattr(lib, name)
+        self._args = args
+        self._keep = keep  # the tensors and the descriptor the marshalled pointers refer to
+        self.result = result
+
+    def __call__(self) -> torch.Tensor:
+        _check(self._fn(*self._args), self._name)
+        return self.result
+
+
+def prepare_decode_step(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                        block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                        sm_scale: float | None = None, partition_size: int = PARTITION_BALANCED,
+                        workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        stream=None, fp8_math: bool = False) -> PreparedCall:
+    """decode_step (decode_step_fp8math with fp8_math) checked and marshalled once; the returned
+    PreparedCall launches it on every call.  The caller keeps the tensors' contents current (new
+    rows in k_new / v_new, the lengths in context_lens) and must not reallocate them."""
+    name = "kvq_decode_step_fp8math" if fp8_math else "kvq_decode_step"
+    d, out, workspace, ws_bytes = _decode_args(cache, q, block_tables, context_lens, max_context_len,
+                                               partition_size, workspace, out)
+    B, Hq, _ = q.shape
+    dev = cache.k_cache.device
+    _tensor(k_new, "k_new", torch.float16, (B, cache.num_kv_heads, HEAD_DIM), dev)
+    _tensor(v_new, "v_new", torch.float16, (B, cache.num_kv_heads, HEAD_DIM), dev)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    args = (ctypes.byref(d), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), Hq, float(sm_scale),
+            _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, int(max_context_len),
+            int(partition_size), _ptr(workspace), ws_bytes, _stream(stream))
+    keep = (d, cache, k_new, v_new, q, out, block_tables, context_lens, workspace)
+    return PreparedCall(name, args, keep, out)
+
+
 def decode_step_noalloc(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
                         block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
                         sm_scale: float | None = None, partition_size: int = PARTITION_BALANCED,

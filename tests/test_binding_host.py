@@ -133,3 +133,17 @@ def test_int8_scales_are_one_row_per_tile(host_binding):
     swapped = K.PagedKVCache(c.dtype, c.k_cache, c.v_cache, c.v_scale, c.k_scale, 1.0)
     with pytest.raises(ValueError, match="two halves"):
         swapped.descriptor()
+
+
+def test_prepared_step_checks_its_arguments(host_binding):
+    """prepare_decode_step runs decode_step's checks once, at preparation: bad arguments are
+    refused there, before any library call (the stub would fail the test)."""
+    K = host_binding
+    c = K.PagedKVCache.allocate("fp8_e4m3", 8, 2, 1.0, device="cpu")
+    bt, ctx = _t((3, 4), torch.int32), _t((3,), torch.int32)
+    q, kn = _t((3, 4, 128)), _t((3, 2, 128))
+    for args in ((_t((3, 1, 128)), kn, q, bt, ctx), (kn, _t((2, 2, 128)), q, bt, ctx),
+                 (kn, kn, _t((3, 4, 64)), bt, ctx), (kn, kn, q, _t((3, 4), torch.int64), ctx),
+                 (kn, kn, q, bt, _t((2,), torch.int32))):
+        with pytest.raises(ValueError):
+            K.prepare_decode_step(c, *args, 64)
