@@ -67,9 +67,13 @@ struct alignas(16) PfStage {
     float s[kPfTW][2 * kBlock];
 };
 
-template <int DT, int NB, bool F8Q>
+// FOLD (FP8 formats with a positive logit scale): the logit scale f is applied inside the exponent,
+// exp2(fma(s, f, -m)) with the raw products s and the chunk max taken on s (f > 0 keeps the order),
+// one FMA per weight instead of a multiply and a subtraction.
+template <int DT, int NB, bool F8Q, bool FOLD>
 __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_prefill_mfma(
     PrefillParams a) {
+    static_assert(!(FOLD && DT == KVQ_INT8), "the INT8 logit scale is per token");
     constexpr int TW = kPfTW;
     __shared__ PfStage stage[3];  // three chunks: one read by the softmax, one by S^T, one filling
     const int g = blockIdx.x;
@@ -137,6 +141,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     for (int nb = 0; nb < NB; ++nb) {
         qk_f[nb] = a.qk_scale;
         if constexpr (F8Q) qk_f[nb] *= quantize_q_row_fp8(qB[nb], q8[nb]);
+        if constexpr (FOLD) qk_f[nb] = fmaxf(qk_f[nb], 1.17549435e-38f);  // -inf * f must stay -inf
     }
 
     float m_run[NB], l_lane[NB];  // per block: reference max (base-2 logits) and this lane's weights
@@ -252,9 +257,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    float f = qk_f[nb];
-                    if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
-                    z[nb][i][t] = sb.s[nb][i][t] * f;
+                    if constexpr (FOLD) {
+                        z[nb][i][t] = sb.s[nb][i][t];  // scaled inside the exponent below
+                    } else {
+                        float f = qk_f[nb];
+                        if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
+                        z[nb][i][t] = sb.s[nb][i][t] * f;
+                    }
                 }
         // The causal mask: a token past the column's own position gets -inf.  Only the chunks that
         // reach past the wave's first row need it (wave-uniform test).
@@ -283,6 +292,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
                 for (int t = 0; t < 4; ++t) m = fmaxf(m, z[nb][i][t]);
             cmax[nb] = col_max4(m);
+            if constexpr (FOLD) cmax[nb] *= qk_f[nb];  // the max of s f, as f > 0
             up[nb] = cmax[nb] > m_run[nb] + slack;  // m_run = -inf: any finite max
             moved |= up[nb];
         }
@@ -307,9 +317,11 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                 float w[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const float pw = __builtin_amdgcn_exp2f(z[nb][u][t] - m_run[nb]);
+                    const float pw = FOLD ? __builtin_amdgcn_exp2f(__builtin_fmaf(z[nb][u][t], qk_f[nb], -m_run[nb]))
+                                          : __builtin_amdgcn_exp2f(z[nb][u][t] - m_run[nb]);
                     l_lane[nb] += pw;
                     w[t] = pw;
+                    // INT8: slots past the context may hold NaN scales; their weight is zero
                     if constexpr (DT == KVQ_INT8) w[t] = (pw > 0.0f) ? pw * vs4[u][t] : 0.0f;
                 }
                 split_hi_lo(w[0], w[1], h[2 * u], l[2 * u]);
@@ -435,16 +447,31 @@ hipError_t launch_prefill(const PrefillArgs& p, hipStream_t stream, hipEvent_t s
         else
             hipLaunchKernelGGL(kernel, grid, dim3(64 * kPfWaves), 0, stream, a);
     };
+    const bool fold = a.qk_scale > 0.0f;  // FOLD needs a positive logit scale
     if (p.fp8_math) {
-        if (c.dtype == KVQ_FP8_E5M2) go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, true>);
-        else go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, true>);
+        if (c.dtype == KVQ_FP8_E5M2) {
+            if (fold) go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, true, true>);
+            else go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, true, false>);
+        } else {
+            if (fold) go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, true, true>);
+            else go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, true, false>);
+        }
         return hipGetLastError();
     }
     switch (c.dtype) {
-        case KVQ_FP8_E4M3: go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, false>); break;
-        case KVQ_FP8_E5M2: go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, false>); break;
-        case KVQ_FP8_E4M3FNUZ: go(attn_prefill_mfma<KVQ_FP8_E4M3FNUZ, KVQ_PREFILL_BLOCKS, false>); break;
-        default: go(attn_prefill_mfma<KVQ_INT8, KVQ_PREFILL_BLOCKS, false>); break;
+        case KVQ_FP8_E4M3:
+            if (fold) go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, false, true>);
+            else go(attn_prefill_mfma<KVQ_FP8_E4M3, KVQ_PREFILL_BLOCKS, false, false>);
+            break;
+        case KVQ_FP8_E5M2:
+            if (fold) go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, false, true>);
+            else go(attn_prefill_mfma<KVQ_FP8_E5M2, KVQ_PREFILL_BLOCKS, false, false>);
+            break;
+        case KVQ_FP8_E4M3FNUZ:
+            if (fold) go(attn_prefill_mfma<KVQ_FP8_E4M3FNUZ, KVQ_PREFILL_BLOCKS, false, true>);
+            else go(attn_prefill_mfma<KVQ_FP8_E4M3FNUZ, KVQ_PREFILL_BLOCKS, false, false>);
+            break;
+        default: go(attn_prefill_mfma<KVQ_INT8, KVQ_PREFILL_BLOCKS, false, false>); break;
     }
     return hipGetLastError();
 }
