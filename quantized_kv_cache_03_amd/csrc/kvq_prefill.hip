@@ -183,11 +183,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     const int st_tile = (wave >> 1) & 1;
     const bool st_k = (wave & 1) == 0;
     const bool stager = wave < 2 * kPfTW;  // the first four waves stage; any others only compute
-    struct Staged { u32x4 x0, x1; float4_t sc; };
+    struct Staged { u32x4 x0, x1; float4_t sc; int valid; };
     auto stage_load = [&](int t0) {
         Staged r{};
         if (!stager) return r;
-        const int blk = block_of(min(t0 + st_tile, wg_tile_end - 1));
+        const int tile = min(t0 + st_tile, wg_tile_end - 1);
+        const int blk = block_of(tile);
+        r.valid = n - tile * kBlock;  // the tile's tokens inside the context
         const uint8_t* src = (st_k ? a.kc : a.vc) + ((size_t)blk * a.Hkv + g) * kTileBytes;
         r.x0 = ld16(src + 32u * (uint32_t)lane);
         r.x1 = ld16(src + 32u * (uint32_t)lane + 16u);
@@ -201,8 +203,19 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     auto stage_store = [&](PfStage& st, const Staged& r) {
         if (!stager) return;
         uint8_t* dst = (st_k ? st.k[st_tile] : st.v[st_tile]) + 32u * (uint32_t)lane;
-        *reinterpret_cast<u32x4*>(dst) = r.x0;
-        *reinterpret_cast<u32x4*>(dst + 16) = r.x1;
+        u32x4 x0 = r.x0, x1 = r.x1;
+        // V codes of the slots past the context (only in its last tile) are zeroed: they may hold
+        // NaN codes, and their zero weights alone would still give 0 * NaN.  The lane's 32 bytes are
+        // dims 2 lane and 2 lane + 1, tokens 0..15 each.  (K codes there only reach logits that the
+        // causal mask replaces.)
+        if (!st_k && r.valid < kBlock) {
+            x0 = u32x4{keep_bytes(x0.x, r.valid), keep_bytes(x0.y, r.valid - 4), keep_bytes(x0.z, r.valid - 8),
+                       keep_bytes(x0.w, r.valid - 12)};
+            x1 = u32x4{keep_bytes(x1.x, r.valid), keep_bytes(x1.y, r.valid - 4), keep_bytes(x1.z, r.valid - 8),
+                       keep_bytes(x1.w, r.valid - 12)};
+        }
+        *reinterpret_cast<u32x4*>(dst) = x0;
+        *reinterpret_cast<u32x4*>(dst + 16) = x1;
         if constexpr (DT == KVQ_INT8) {
             if (st_k && lane < 8) *reinterpret_cast<float4_t*>(&st.s[st_tile][4 * lane]) = r.sc;
         }
@@ -239,7 +252,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 
     // Softmax of a chunk and its P V^T, with the lazy rescale (kRescaleSlack, kRescaleSlackInt8; a
     // branch every lane takes or skips together).
-    auto softmax_pv = [&](const PfStage& st, const SBuf& sb, int t0) {
+    auto softmax_pv = [&](const PfStage& st, const SBuf& sb, int t0, auto&& mid) {
         const int tok_base = t0 * kBlock;  // first token of the chunk
         float4_t ks4[TW], vs4[TW];         // INT8: the scales of this lane's four tokens of each tile
 #pragma unroll
@@ -306,6 +319,9 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                 if (up[nb]) m_run[nb] = cmax[nb];
             }
         }
+        // the next chunk's S^T products, in the same basic block as the weights and P V^T below, so
+        // that the scheduler can interleave their matrix instructions with this chunk's VALU work
+        mid();
 
         // weights of the tile pair, hi and lo fp16 parts, in the B layout, per block
         half8_v whi[NB], wlo[NB];
@@ -336,16 +352,8 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 vd[i][r] = *reinterpret_cast<const uint32_t*>(st.v[i] + v_off + (uint32_t)r * 256u);
-        // V codes of the slots at and past t_end are zeroed (past the context they may hold NaN
-        // codes; a zero weight alone would still give 0 * NaN); chunks inside it need nothing
-        if (tok_base + TW * kBlock > t_end) {
-            const int valid0 = t_end - tok_base - 4 * q4;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                vd[0][r] = keep_bytes(vd[0][r], valid0);
-                vd[1][r] = keep_bytes(vd[1][r], valid0 - kBlock);
-            }
-        }
+        // (slots past the context were zeroed when staged; those in it past the column's own
+        // position have zero weights)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const half8_v va8 = join8(codes_to_f16<DT, 0>(vd[0][r]), codes_to_f16<DT, 1>(vd[0][r]),
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     };
 
     // Pipeline over the workgroup's chunks, three LDS buffers: at step c the staging loads of chunk
-    // c + 2 are in flight, S^T of chunk c + 1 is issued from its buffer, chunk c's softmax and
+    // c + 2 are in flight, S^T of chunk c + 1 is computed from its buffer, chunk c's softmax and
     // P V^T read theirs, and then chunk c + 2 is stored into the buffer chunk c - 1 used; one
     // barrier per step.  A wave computes only the chunks up to its own last tile.
     const int nch = (wg_tile_end + TW - 1) / TW;
@@ -383,8 +391,9 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
             ids_for(min(t0 + 3 * TW - 1, wg_tile_end - 1));
             nx = stage_load(t0 + 2 * TW);
         }
-        if (t0 + TW < tile_end) scores(stage[(c + 1) % 3], sn);
-        if (t0 < tile_end) softmax_pv(stage[c % 3], sc, t0);
+        // S^T of chunk c + 1 is computed by every wave that computes chunk c (on a wave's last chunk,
+        // or past the workgroup's last, it reads a buffer of no use and its result is never read)
+        if (t0 < tile_end) softmax_pv(stage[c % 3], sc, t0, [&] { scores(stage[(c + 1) % 3], sn); });
         if (more) stage_store(stage[(c + 2) % 3], nx);
         __syncthreads();
     };
