@@ -48,11 +48,11 @@ __device__ __forceinline__ uint32_t set_nibble(uint32_t w, int i, uint32_t q) {
 }
 
 // The appended token's stores, held back until the wave has read all its tiles (as in the 8-bit
-// kernel): its K bytes wait in LDS, this lane's patched V rows in registers.
+// kernel): its K bytes and this lane's patched 16 V bytes wait in LDS (lds_k, lds_vrow[lane]), so
+// that no registers are held for them across the attention loop.
 struct PendingAppend4 {
     int blk;       // -1 when nothing is pending (wave-uniform)
     int slot;
-    u32x4 v;       // this lane's V codes (its quad's units), patched
     f32x2 ks, vs;
 };
 
@@ -61,7 +61,7 @@ struct PendingAppend4 {
 // other tokens' nibbles are written back unchanged -- this wave is the tile's only reader and
 // writer), and the (scale, zero point) pairs.
 __device__ __forceinline__ void flush_append4(const KernelParams& a, PendingAppend4& pa,
-                                              const uint8_t* lds_k, int g, int lane) {
+                                              const uint8_t* lds_k, const u32x4* lds_vrow, int g, int lane) {
     if (pa.blk < 0) return;
     const size_t tile = ((size_t)pa.blk * a.Hkv + g) * kTileBytes4;
     uint8_t* kt = const_cast<uint8_t*>(a.kc) + tile;
@@ -70,7 +70,7 @@ __device__ __forceinline__ void flush_append4(const KernelParams& a, PendingAppe
         __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(lds_k)[lane],
                                     reinterpret_cast<u32x4*>(kt + k_byte4(pa.slot, 32 * lane)));
     if ((lane >> 4) == (pa.slot >> 2))
-        __builtin_nontemporal_store(pa.v, reinterpret_cast<u32x4*>(vt + v_byte4(pa.slot & ~3, lane & 15)));
+        __builtin_nontemporal_store(lds_vrow[lane], reinterpret_cast<u32x4*>(vt + v_byte4(pa.slot & ~3, lane & 15)));
     if (lane == 0) {
         const size_t so = ((size_t)pa.blk * a.Hkv + g) * kBlock + pa.slot;
         reinterpret_cast<f32x2*>(const_cast<float*>(a.ks))[so] = pa.ks;

@@ -10,8 +10,7 @@
 // 8-bit grouped kernel (kvq_attn_gqa.hip) does, with both products on v_mfma_f32_16x16x32_f16
 // (query heads padded to 16 columns).  The matrix cores get exact binary16 integers (they align a
 // group's products by exponent fields, which would cost subnormal codes their low bits): K codes as
-// c - c0 and 16 (c - c0) (int4x8_centred), V codes as c and 16 c with the odd tokens' weights
-// divided by 16 (int4_unit_to_f16_int).
+// c - c0 and 16 (c - c0) (int4x8_centred), V codes as c through the FP8 converter (int4x8_exact).
 //   S^T = K Q^T per tile: A = K (lane: token l % 16, the 32 dims of chunk l / 16 -- one 16-byte
 //       load per lane reads the tile), B = Q^T (lane: head l % 16, the same dims); two MFMAs for
 //       the even nibble pairs of the chunk's dims, two for the odd ones.  C: lane (head l % 16,
@@ -58,24 +57,58 @@ __device__ __forceinline__ int k_slot_dim(int dw0, int odd, int slot) {
     return 8 * dw + i + 4 * (slot % 2);
 }
 
+// One lane's share of one tile: K of token l % 16 in chunk l / 16 and V of quad l / 16 for the dims
+// l % 16 + 16 r (one 16-byte load each), and the K and V (scale, zero point) pairs of the lane's own
+// token 4 (l / 16) + l % 4 -- one of the four tokens 4 q4 + u of the lane's accumulator, so each
+// quad of lanes holds all four and hands them round with quad broadcasts (no LDS round trip), and a
+// tile costs 12 registers while its loads are in flight.
+struct TileG4 {
+    u32x4 k, v;
+    f32x2 kp, vp;
+};
+__device__ __forceinline__ void load_tile_g4(const KernelParams& a, TileG4& t, int blk, int g, uint32_t off,
+                                             int own) {
+    const size_t pair = (size_t)blk * a.Hkv + g;
+    t.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.kc + pair * kTileBytes4 + off));
+    t.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vc + pair * kTileBytes4 + off));
+    t.kp = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(a.ks) + pair * kBlock + own);
+    t.vp = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(a.vs) + pair * kBlock + own);
+}
+
+// Value of lane 4 (l / 4) + U of the lane's quad (DPP quad_perm [U, U, U, U]).
+template <int U>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return dpp<U * 0x55>(v);
+}
+
 // One chunk of kTiles4 tiles (tiles past the segment's end repeat its last one; their tokens are masked).
 template <bool APPEND>
-__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[kTiles4], int tile0, int t_end,
-                                         const half8_v (&qe)[2], const half8_v (&qo)[2], float zq,
+__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTiles4], int tile0, int t_end,
+                                         const half8_v (&qe)[2], const half8_v (&qo)[2], float qsum, float qf,
                                          int q4, float& m_run, float& l_lane, float& z_lane,
                                          float4_t (&acc)[8]) {
     float z[kTiles4][4];
     const Int4Bits bits = int4_bits();
+    const int col = (int)(threadIdx.x & 15u);  // the token of the lane's K operand row
+    const int own = 4 * q4 + (col & 3);        // the token of the lane's pairs
+    const int src = 16 * (col >> 2) + (col & 3);  // a lane whose pairs are those of token col
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i) {
-        // every token centred at its own zero code c0 (int4_zero_code), computed once, by the
-        // lanes whose K operand row it is (l % 16, from its pair kp); the accumulator's tokens
-        // 4 q4 + u take their zp' = zp + s c0 from those lanes
-        const float zc = int4_zero_code(t[i].kp.x, t[i].kp.y);
-        const float zpa = __builtin_fmaf(t[i].kp.x, zc, t[i].kp.y);
-        float zps[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) zps[u] = __shfl(zpa, 4 * q4 + u);
+        // every token centred at its own zero code c0 (int4_zero_code), computed once per token by
+        // the lanes holding its pairs; the K operand rows (token col) take it by shuffle, and the
+        // accumulator's tokens 4 q4 + u take their K scale and zp' = zp + s c0 by quad broadcast.
+        // The V pairs of slots at and past t_end are zeroed first (past the context they may be
+        // NaN, and a zero weight alone would still give 0 * NaN); only a tile that reaches past
+        // the end has such slots (wave-uniform test).
+        const float zo = int4_zero_code(t[i].kp.x, t[i].kp.y);
+        const float zpa = __builtin_fmaf(t[i].kp.x, zo, t[i].kp.y);
+        if ((tile0 + i + 1) * kBlock > t_end && (tile0 + i) * kBlock + own >= t_end) t[i].vp = f32x2{0.0f, 0.0f};
+        const float zc = __shfl(zo, src);
+        float ks[4], zps[4];  // K scale and zp' of the tokens 4 q4 + u
+        ks[0] = quad_bcast<0>(t[i].kp.x), zps[0] = quad_bcast<0>(zpa);
+        ks[1] = quad_bcast<1>(t[i].kp.x), zps[1] = quad_bcast<1>(zpa);
+        ks[2] = quad_bcast<2>(t[i].kp.x), zps[2] = quad_bcast<2>(zpa);
+        ks[3] = quad_bcast<3>(t[i].kp.x), zps[3] = quad_bcast<3>(zpa);
         half2_t ne, no;
         int4_centre_pairs(zc, ne, no);
         half8_v e[2], o[2];
@@ -87,7 +120,7 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(e[1], qe[1], s, 0, 0, 0);
         s = __builtin_amdgcn_mfma_f32_16x16x32_f16(o[1], qo[1], s, 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) z[i][u] = __builtin_fmaf(s[u], a.qk_scale * t[i].ks[u], zq * zps[u]);
+        for (int u = 0; u < 4; ++u) z[i][u] = __builtin_fmaf(s[u], ks[u], qsum * zps[u]);  // z / qf
     }
     // Tokens at and past t_end are masked; only a chunk that reaches past it has such tokens
     // (wave-uniform test).
@@ -104,24 +137,9 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i)
         cmax = fmaxf(cmax, fmaxf(fmaxf(z[i][0], z[i][1]), fmaxf(z[i][2], z[i][3])));
-    // The V parameters of the slots at and past t_end are zeroed (past the context they may be
-    // NaN, and a zero weight alone would still give 0 * NaN); only a tile that reaches past the
-    // end has such slots (wave-uniform test).
-#pragma unroll
-    for (int i = 0; i < kTiles4; ++i) {
-        if ((tile0 + i + 1) * kBlock > t_end) {
-            const int pos0 = (tile0 + i) * kBlock + 4 * q4;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (pos0 + u >= t_end) {
-                    t[i].vs[u] = 0.0f;
-                    t[i].vz[u] = 0.0f;
-                }
-        }
-    }
     // Lazy rescale (kRescaleSlackInt4), a branch every lane takes or skips together.  Every chunk
     // holds a valid token, so cmax is finite.
-    cmax = col_max4(cmax);
+    cmax = col_max4(cmax) * qf;
     const bool up = cmax > m_run + kRescaleSlackInt4;  // m_run = -inf: any finite max
     if (__builtin_amdgcn_ballot_w64(up)) {
         const float alpha = up ? __builtin_amdgcn_exp2f(m_run - cmax) : 1.0f;
@@ -137,61 +155,57 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileMfma4 (&t)[k
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i) {
         float w[4];
+        const float vs[4] = {quad_bcast<0>(t[i].vp.x), quad_bcast<1>(t[i].vp.x), quad_bcast<2>(t[i].vp.x),
+                             quad_bcast<3>(t[i].vp.x)};  // the V pairs of the tokens 4 q4 + u
+        const float vz[4] = {quad_bcast<0>(t[i].vp.y), quad_bcast<1>(t[i].vp.y), quad_bcast<2>(t[i].vp.y),
+                             quad_bcast<3>(t[i].vp.y)};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float pw = __builtin_amdgcn_exp2f(z[i][u] - m_run);
+            const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i][u], qf, -m_run));
             l_lane += pw;
-            w[u] = pw * t[i].vs[u];
-            z_lane = __builtin_fmaf(pw, t[i].vz[u], z_lane);
+            w[u] = pw * vs[u];
+            z_lane = __builtin_fmaf(pw, vz[u], z_lane);
         }
         split_hi_lo(w[0], w[2], ehi[i], elo[i]);
-        split_hi_lo(w[1] * kInt4OddWeight, w[3] * kInt4OddWeight, ohi[i], olo[i]);
+        split_hi_lo(w[1], w[3], ohi[i], olo[i]);
     }
     const half8_v we_hi = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
     const half8_v we_lo = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
     const half8_v wo_hi = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
     const half8_v wo_lo = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
-    // O^T += V^T P^T, row block r = dims 16 r .. +15
+    // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 (dims 16 r .. +15) from dword d of every tile's V
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        half2_t ve[kTiles4], vo[kTiles4];
+    for (int d = 0; d < 4; ++d) {
+        half2_t hv[kTiles4][4];
 #pragma unroll
         for (int i = 0; i < kTiles4; ++i) {
             const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
-            if (r & 1)
-                int4_unit_to_f16_int<1>(w[r / 2], bits, ve[i], vo[i]);
-            else
-                int4_unit_to_f16_int<0>(w[r / 2], bits, ve[i], vo[i]);
+            int4x8_exact(w[d], hv[i]);  // unit 0: tokens (0, 2) in hv[0], (1, 3) in hv[2]; unit 1: hv[1], hv[3]
         }
-        const half8_v ae = join4(ve[0], ve[1], ve[2], ve[3]);
-        const half8_v ao = join4(vo[0], vo[1], vo[2], vo[3]);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc[r], 0, 0, 0);
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc[r], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = 2 * d + e;
+            const half8_v ae = join4(hv[0][e], hv[1][e], hv[2][e], hv[3][e]);
+            const half8_v ao = join4(hv[0][2 + e], hv[1][2 + e], hv[2][2 + e], hv[3][2 + e]);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi, acc[r], 0, 0, 0);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo, acc[r], 0, 0, 0);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi, acc[r], 0, 0, 0);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc[r], 0, 0, 0);
+        }
     }
 }
 
-// Replace the new token's codes and scales in the registers of its tile: K in the four lanes whose
-// operand row is the token, V and the scale pairs in the 16 lanes of its quad.
-__device__ __forceinline__ void patch_tile_g4(TileMfma4& t, const NewToken4& nt, const uint8_t* lds_k,
+// Replace the new token's codes and pairs in the registers of its tile: K in the four lanes whose
+// operand row is the token, both pairs in the four lanes that own them, V in the 16 lanes of its quad.
+__device__ __forceinline__ void patch_tile_g4(TileG4& t, const NewToken4& nt, const uint8_t* lds_k,
                                               const uint8_t* lds_v, int lane) {
     const int col = lane & 15, q4 = lane >> 4;
-    if (col == nt.slot) {
-        t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
+    if (col == nt.slot) t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
+    if (4 * q4 + (col & 3) == nt.slot) {
         t.kp = nt.ks;
+        t.vp = nt.vs;
     }
     patch_v_quad(t.v, nt.slot, lds_v, lane);
-    if (q4 == (nt.slot >> 2)) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)  // (a constant element index keeps the vectors in registers)
-            if (u == (nt.slot & 3)) {
-                t.ks[u] = nt.ks.x;
-                t.kz[u] = nt.ks.y;
-                t.vs[u] = nt.vs.x;
-                t.vz[u] = nt.vs.y;
-            }
-    }
 }
 
 // The work of one segment -- tiles [lo, hi) of sequence b (n tokens, nt tiles): the final output
@@ -199,7 +213,8 @@ __device__ __forceinline__ void patch_tile_g4(TileMfma4& t, const NewToken4& nt,
 template <bool APPEND>
 __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g, int n, int nt, int lo,
                                              int hi, int64_t rmul, int64_t radd, int lane,
-                                             uint8_t* lds_knew, uint8_t* lds_vnew, PendingAppend4& pend) {
+                                             uint8_t* lds_knew, uint8_t* lds_vnew, u32x4* lds_vrow,
+                                             PendingAppend4& pend) {
     const int col = lane & 15;  // query head within the group (B / C column), or A row
     const int q4 = lane >> 4;   // k-group / C row group
     const int G = a.Hq / a.Hkv;
@@ -207,12 +222,27 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
     const int t_end = min(n, hi * kBlock);
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
     const int tile_new = (APPEND && hi == nt) ? nt - 1 : -1;
+    // The appended token (the segment holding the sequence's last tile): an earlier sequence's
+    // pending token is stored first (its segment is done; the LDS buffers are reused), then the new
+    // one is encoded into LDS, before the loop, so that none of its registers are live there.
+    [[maybe_unused]] NewToken4 ntok{};
+    if constexpr (APPEND) {
+        if (tile_new >= 0) {  // (wave-uniform)
+            flush_append4(a, pend, lds_knew, lds_vrow, g, lane);
+            ntok = new_token4(a, b, g, n, lane, lds_knew, lds_vnew);
+        }
+    }
 
     // Q^T operands over chunk q4's dims in the K operands' slot order, and sum(q) of the head
     half8_v qe[2], qo[2];
     float qsum = 0.0f;
 #pragma unroll
     for (int m = 0; m < 2; ++m) qe[m] = qo[m] = half8_v{0, 0, 0, 0, 0, 0, 0, 0};
+    // The logit scale f = sm_scale log2(e) is applied in the exponent as |f| (exp2(fma(z, |f|, -m))
+    // with the chunk max taken on the unscaled z and scaled once); a negative f negates q instead.
+    const bool neg = a.qk_scale < 0.0f;
+    const _Float16 qsign = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+    const float qf = fmaxf(fabsf(a.qk_scale), 1.17549435e-38f);  // -inf * qf must stay -inf
     if (col < G) {
         const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h) * kDim + 32 * q4;
         uint16_t qv[32];
@@ -234,13 +264,13 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                qe[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 0, s)]);
-                qo[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 1, s)]) * (_Float16)0.0625f;
+                qe[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 0, s)]) * qsign;
+                qo[m][s] = __builtin_bit_cast(_Float16, qv[k_slot_dim(2 * m, 1, s)]) * (qsign * (_Float16)0.0625f);
             }
     }
     qsum += __shfl_xor(qsum, 16);
     qsum += __shfl_xor(qsum, 32);
-    const float zq = a.qk_scale * qsum;  // the logit term of the zero points is zq * (zp + s c0)
+    if (neg) qsum = -qsum;  // the logit term of the zero points is qsum * (zp + s c0)
 
     float m_run = kNegInf;
     float l_lane = 0.0f, z_lane = 0.0f;
@@ -256,25 +286,24 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
         // with no branch between them; the extra tiles' tokens lie past the segment and are masked.
         const int blk_lane = bt[tb + min(lane, nt_grp - 1)];
         for (int c0 = 0; c0 < nt_grp; c0 += kTiles4) {
-            TileMfma4 t[kTiles4];
+            TileG4 t[kTiles4];
 #pragma unroll
             for (int i = 0; i < kTiles4; ++i)
-                load_tile_mfma4<true>(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                load_tile_g4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, 4 * q4 + (col & 3));
             if constexpr (APPEND) {
                 const int inew = tile_new - (tb + c0);  // wave-uniform
                 if (inew >= 0 && inew < kTiles4) {
-                    flush_append4(a, pend, lds_knew, g, lane);  // an earlier sequence's token, if any
-                    const NewToken4 ntok = new_token4(a, b, g, n, lane, lds_knew, lds_vnew);
 #pragma unroll
                     for (int i = 0; i < kTiles4; ++i)
                         if (i == inew) {
                             patch_tile_g4(t[i], ntok, lds_knew, lds_vnew, lane);
-                            pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0 + i), ntok.slot,
-                                                  t[i].v, ntok.ks, ntok.vs};
+                            lds_vrow[lane] = t[i].v;
+                            pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0 + i), ntok.slot, ntok.ks,
+                                                  ntok.vs};
                         }
                 }
             }
-            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, zq, q4, m_run, l_lane, z_lane, acc);
+            chunk_g4<APPEND>(a, t, tb + c0, t_end, qe, qo, qsum, qf, q4, m_run, l_lane, z_lane, acc);
         }
     }
     // the head's weight sum and zero-point sum over the four row groups
@@ -309,20 +338,21 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
 
 // BAL: grid (KV head, wave of the balanced split), else (KV head, partition, sequence).
 template <bool APPEND, bool BAL>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_partition_mfma4(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void attn_partition_mfma4(
     KernelParams a) {
     __shared__ u32x4 lds_knew[APPEND ? 4 : 1];
     __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
+    __shared__ u32x4 lds_vrow[APPEND ? 64 : 1];  // the pending token's patched V rows, one per lane
     const int lane = threadIdx.x;
     const int g = blockIdx.x;
     uint8_t* knew = reinterpret_cast<uint8_t*>(lds_knew);
-    PendingAppend4 pend{-1, 0, u32x4{0u, 0u, 0u, 0u}, f32x2{0.0f, 0.0f}, f32x2{0.0f, 0.0f}};
+    PendingAppend4 pend{-1, 0, f32x2{0.0f, 0.0f}, f32x2{0.0f, 0.0f}};
     if constexpr (BAL) {
         const int w = blockIdx.y;
         for_each_segment(a, w, g == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
-            gqa4_segment<APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, knew, lds_vnew, pend);
+            gqa4_segment<APPEND>(a, b, g, n, nt, lo, hi, a.S, w + b, lane, knew, lds_vnew, lds_vrow, pend);
         });
-        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+        if constexpr (APPEND) flush_append4(a, pend, knew, lds_vrow, g, lane);
     } else {
         const int p = blockIdx.y;
         const int b = blockIdx.z;
@@ -343,8 +373,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         if (lo >= nt) return;
         const int hi = min(nt, lo + a.PS / kBlock);
         gqa4_segment<APPEND>(a, b, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane, knew, lds_vnew,
-                             pend);
-        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+                             lds_vrow, pend);
+        if constexpr (APPEND) flush_append4(a, pend, knew, lds_vrow, g, lane);
     }
 }
 

@@ -182,7 +182,7 @@ template <int TW, bool APPEND>
 __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h, int g, int n, int nt,
                                              int lo, int hi, int64_t rmul, int64_t radd, int lane,
                                              uint16_t* lds, uint8_t* lds_knew, uint8_t* lds_vnew,
-                                             PendingAppend4& pend) {
+                                             u32x4* lds_vrow, PendingAppend4& pend) {
     const int tk = lane >> 2;
     const size_t orow = ((size_t)b * a.Hq + h) * kDim;
     const bool has_last = hi == nt;
@@ -241,11 +241,11 @@ __device__ __forceinline__ void mha4_segment(const KernelParams& a, int b, int h
             load_tile4(a, t[0], __builtin_amdgcn_readlane(blk_lane, c0), g, k_off, v_off, tk);
             if constexpr (APPEND) {
                 if (tb + c0 == tile_new) {
-                    flush_append4(a, pend, lds_knew, g, lane);  // an earlier sequence's token, if any
+                    flush_append4(a, pend, lds_knew, lds_vrow, g, lane);  // an earlier sequence's token, if any
                     const NewToken4 ntok = new_token4(a, b, g, n, lane, lds_knew, lds_vnew);
                     patch_tile4(t[0], ntok, lds_knew, lds_vnew, lane);
-                    pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0), ntok.slot, t[0].v,
-                                          ntok.ks, ntok.vs};
+                    lds_vrow[lane] = t[0].v;
+                    pend = PendingAppend4{__builtin_amdgcn_readlane(blk_lane, c0), ntok.slot, ntok.ks, ntok.vs};
                 }
             }
             chunk_step4<1, true>(a, t, tb + c0, t_end, qv, qsum, lane, lds, m_run, l_lane, z_lane, acc);
@@ -290,17 +290,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 3,
     __shared__ __attribute__((aligned(16))) uint16_t lds[TW * 32];
     __shared__ u32x4 lds_knew[APPEND ? 4 : 1];
     __shared__ uint8_t lds_vnew[APPEND ? 128 : 1];
+    __shared__ u32x4 lds_vrow[APPEND ? 64 : 1];  // the pending token's patched V rows, one per lane
     const int lane = threadIdx.x;
     const int h = blockIdx.x;
     const int g = h / (a.Hq / a.Hkv);
     uint8_t* knew = reinterpret_cast<uint8_t*>(lds_knew);
-    PendingAppend4 pend{-1, 0, u32x4{0u, 0u, 0u, 0u}, f32x2{0.0f, 0.0f}, f32x2{0.0f, 0.0f}};
+    PendingAppend4 pend{-1, 0, f32x2{0.0f, 0.0f}, f32x2{0.0f, 0.0f}};
     if constexpr (BAL) {
         const int w = blockIdx.y;
         for_each_segment(a, w, h == 0 && w == 0, lane, [&](int b, int n, int nt, int lo, int hi) {
-            mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, knew, lds_vnew, pend);
+            mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.S, w + b, lane, lds, knew, lds_vnew, lds_vrow,
+                                     pend);
         });
-        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+        if constexpr (APPEND) flush_append4(a, pend, knew, lds_vrow, g, lane);
     } else {
         const int p = blockIdx.y;
         const int b = blockIdx.z;
@@ -314,8 +316,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BAL ? 2 : 3,
         if (lo >= nt) return;
         const int hi = min(nt, lo + a.PS / kBlock);
         mha4_segment<TW, APPEND>(a, b, h, g, n, nt, lo, hi, a.P, (int64_t)b * a.Hq * a.P + p, lane, lds,
-                                 knew, lds_vnew, pend);
-        if constexpr (APPEND) flush_append4(a, pend, knew, g, lane);
+                                 knew, lds_vnew, lds_vrow, pend);
+        if constexpr (APPEND) flush_append4(a, pend, knew, lds_vrow, g, lane);
     }
 }
 

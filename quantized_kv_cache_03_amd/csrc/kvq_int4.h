@@ -91,6 +91,24 @@ __device__ __forceinline__ void int4_centre_pairs(float c0, half2_t& ne, half2_t
     no = half2_t{o, o};
 }
 
+// Eight 4-bit codes as exact binary16 integers through the FP8 converter.  A byte holding one
+// nibble n alone is the E4M3 code of n 2^-9: codes 0..7 are the subnormals n 2^-9 and codes 8..15
+// the first normal binade, (1 + (n - 8) / 8) 2^-6 = n 2^-9, so the scaled conversion with scale 2^9
+// gives n exactly, two codes per instruction:
+//   h[0] = nibbles (0, 2),  h[1] = nibbles (4, 6),  h[2] = nibbles (1, 3),  h[3] = nibbles (5, 7).
+// The matrix cores keep products of such operands whole (normal binary16 integers of 4 bits).
+constexpr float kNibbleScale = 512.0f;  // 2^9
+__device__ __forceinline__ void int4x8_exact(uint32_t w, half2_t (&h)[4]) {
+    const uint32_t lo = w & 0x0F0F0F0Fu;         // nibbles 0, 2, 4, 6, one per byte
+    const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 1, 3, 5, 7
+    h[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, kNibbleScale, false);
+    h[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, kNibbleScale, true);
+    h[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, kNibbleScale, false);
+    h[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, kNibbleScale, true);
+}
+// The nibble of a dword that k-slot s of its operand join8(h[0], h[1], h[2], h[3]) holds.
+__device__ __forceinline__ constexpr int int4_slot_nibble(int s) { return s < 4 ? 2 * s : 2 * (s - 4) + 1; }
+
 // Tile geometry (1 KiB per tile).
 //   K: four 256-byte chunks of 32 dims x 16 tokens; the byte of dim d of token t holds dims
 //      d & ~1 (low nibble) and d | 1.
@@ -162,20 +180,6 @@ __device__ __forceinline__ float wave_min(float v) {
     return v;
 }
 
-// The 16-bit unit of a V dword (as int4_unit_to_f16: e = tokens (0, 2), o = tokens (1, 3)) as exact
-// binary16 integers for the matrix cores: e = c and o = 16 c, each the code placed under the exponent
-// of 1024 (one v_and_or_b32, Int4Bits) less 1024 (one packed fp16 addition).  The odd tokens'
-// weights are taken sixteen times smaller (exact), so both products land in one accumulator in
-// units of c.
-template <int SEL>
-__device__ __forceinline__ void int4_unit_to_f16_int(uint32_t w, const Int4Bits& b, half2_t& e, half2_t& o) {
-    constexpr uint32_t sel = (SEL == 0) ? 0x0C010C00u : 0x0C030C02u;
-    const uint32_t x = __builtin_amdgcn_perm(0u, w, sel);
-    const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-    e = __builtin_bit_cast(half2_t, (x & b.even) | b.magic) + m1024;
-    o = __builtin_bit_cast(half2_t, (x & b.odd) | b.magic) + m1024;
-}
-constexpr float kInt4OddWeight = 0.0625f;  // 1 / 16
 
 // Partition kernels of the INT4 cache: one query head per KV head (kvq_attn_mha4.hip) and grouped
 // query heads (kvq_attn_gqa4.hip).

@@ -12,8 +12,7 @@
 // operands of the grouped INT4 decode kernel: one 16-byte load per lane for each of the K and V
 // tiles, decoded once for both blocks, P^T left in the lanes by the S^T accumulator, chunks of four
 // tiles.  The matrix cores get exact binary16 integers: K codes as c - c0 and 16 (c - c0)
-// (int4x8_centred), V codes as c and 16 c with the odd tokens' weights divided by 16
-// (int4_unit_to_f16_int).
+// (int4x8_centred), V codes as c through the FP8 converter (int4x8_exact).
 #include "kvq_attn4.h"
 #include "kvq_mfma.h"
 
@@ -259,32 +258,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                         z_lane[nb] = __builtin_fmaf(pw, t[i].vz[u], z_lane[nb]);
                     }
                     split_hi_lo(w[0], w[2], ehi[i], elo[i]);
-                    split_hi_lo(w[1] * kInt4OddWeight, w[3] * kInt4OddWeight, ohi[i], olo[i]);
+                    split_hi_lo(w[1], w[3], ohi[i], olo[i]);
                 }
                 we_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
                 we_lo[nb] = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
                 wo_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
                 wo_lo[nb] = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
             }
+            // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 from dword d of every tile's V
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                half2_t ve[kTilesP4], vo[kTilesP4];
+            for (int d = 0; d < 4; ++d) {
+                half2_t hv[kTilesP4][4];
 #pragma unroll
                 for (int i = 0; i < kTilesP4; ++i) {
                     const uint32_t w[4] = {t[i].v.x, t[i].v.y, t[i].v.z, t[i].v.w};
-                    if (r & 1)
-                        int4_unit_to_f16_int<1>(w[r / 2], bits, ve[i], vo[i]);
-                    else
-                        int4_unit_to_f16_int<0>(w[r / 2], bits, ve[i], vo[i]);
+                    int4x8_exact(w[d], hv[i]);  // unit 0: tokens (0, 2) in hv[0], (1, 3) in hv[2]; unit 1: hv[1], hv[3]
                 }
-                const half8_v ae = join8(ve[0], ve[1], ve[2], ve[3]);
-                const half8_v ao = join8(vo[0], vo[1], vo[2], vo[3]);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi[nb], acc[nb][r], 0, 0, 0);
-                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo[nb], acc[nb][r], 0, 0, 0);
-                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi[nb], acc[nb][r], 0, 0, 0);
-                    acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo[nb], acc[nb][r], 0, 0, 0);
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * d + e;
+                    const half8_v ae = join8(hv[0][e], hv[1][e], hv[2][e], hv[3][e]);
+                    const half8_v ao = join8(hv[0][2 + e], hv[1][2 + e], hv[2][2 + e], hv[3][2 + e]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_hi[nb], acc[nb][r], 0, 0, 0);
+                        acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, we_lo[nb], acc[nb][r], 0, 0, 0);
+                        acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_hi[nb], acc[nb][r], 0, 0, 0);
+                        acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo[nb], acc[nb][r], 0, 0, 0);
+                    }
                 }
             }
         }

@@ -135,3 +135,28 @@ extern "C" int kvq_probe_int4_centred(const uint32_t* codes, const float* c0, co
         codes, c0, static_cast<const uint16_t*>(qop), dec, s_out);
     return (int)hipGetLastError();
 }
+
+// The INT4 kernels' V operand decode on its own (int4x8_exact, the FP8 converter with scale 2^9):
+// for problem p, lane l decodes its four code dwords codes[p][l][4] and writes each one's four
+// binary16 pairs -- nibbles (0, 2), (4, 6), (1, 3), (5, 7) -- to dec[p][l][16].
+namespace {
+__global__ __launch_bounds__(64) void int4_exact(const uint32_t* codes, uint32_t* dec) {
+    const int p = blockIdx.x, l = threadIdx.x;
+    const uint32_t* w = codes + ((size_t)p * 64 + l) * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kvq::half2_t h[4];
+        kvq::int4x8_exact(w[j], h);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dec[((size_t)p * 64 + l) * 16 + 4 * j + k] = __builtin_bit_cast(uint32_t, h[k]);
+    }
+}
+}  // namespace
+
+// n problems: codes uint32 [n][64][4], dec uint32 [n][64][16]; device memory.  Returns 0, -1 for bad
+// arguments, or the HIP error code.
+extern "C" int kvq_probe_int4_exact(const uint32_t* codes, uint32_t* dec, int32_t n, void* stream) {
+    if (!codes || !dec || n <= 0 || n > 65535) return -1;
+    int4_exact<<<dim3((unsigned)n), dim3(64), 0, static_cast<hipStream_t>(stream)>>>(codes, dec);
+    return (int)hipGetLastError();
+}

@@ -270,3 +270,33 @@ def test_int4_centred_operands(P):
     # the final fp32 sum se + so / 16
     say(f"  INT4 centred operands: worst error / (u sum |products|) = {float((err / (GC.U32 * mag)).max()):.1f}")
     assert np.all(err <= (4 * 19 + 1) * GC.U32 * mag + 1e-30)
+
+
+def test_int4_exact_nibbles(P):
+    """The INT4 kernels' V operand decode (int4x8_exact, run by kvq_probe_int4_exact): a byte holding
+    one nibble n is the E4M3 code of n 2^-9 (subnormal below 8, first binade from 8), so the FP8
+    converter with scale 2^9 gives n exactly -- every nibble value in every position of a dword, bit
+    for bit, in the pairs (0, 2), (4, 6), (1, 3), (5, 7)."""
+    import torch
+    f = P.kvq_probe_int4_exact
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    r = np.random.default_rng(11)
+    n = 64
+    codes = r.integers(0, 2 ** 32, size=(n, 64, 4), dtype=np.uint64).astype(np.uint32)
+    # exhaustive: problem 0 holds every value 0..15 in every nibble position (dword j, lane l)
+    for l in range(64):
+        for j in range(4):
+            v = (16 * j + l) % 16
+            codes[0, l, j] = np.uint32(sum(((v + i) % 16) << (4 * i) for i in range(8)))
+    dc = torch.from_numpy(codes).cuda()
+    dec = torch.zeros((n, 64, 16), dtype=torch.int32, device="cuda")
+    assert f(dc.data_ptr(), dec.data_ptr(), n, None) == 0
+    torch.cuda.synchronize()
+    dec = dec.cpu().numpy().view(np.uint32)
+    got = np.stack([dec & 0xFFFF, dec >> 16], -1).astype(np.uint16).view(np.float16).astype(np.float64)
+    nib = np.stack([(codes >> (4 * i)) & 0xF for i in range(8)], -1).astype(np.float64)  # [n][64][4][8]
+    order = [(0, 2), (4, 6), (1, 3), (5, 7)]
+    want = np.stack([np.stack([nib[..., a], nib[..., b]], -1) for a, b in order], -2)  # [n][64][4][4][2]
+    np.testing.assert_array_equal(got.reshape(want.shape), want)
+    assert {int(x) for x in np.unique(nib[0])} == set(range(16))
