@@ -44,17 +44,19 @@ __device__ __forceinline__ float col_sum4(float x) {
     return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
-// Two fp32 weights -> packed fp16 hi parts (round to nearest even) and lo parts f16(w - f32(hi))
-// (w - hi is exact in fp32): one packed conversion for the hi parts, and the lo parts as fused
-// multiply-adds of the hi half with -1, issued as one mixed-precision v_fma_mix per value (a plain
-// subtraction takes an unpack, a subtraction and a conversion each).  The -1 comes from an identity
-// DPP move: as a literal the compiler folds the multiply-add back into a subtraction.
+// Two fp32 weights -> packed fp16 hi parts and lo parts f16(w - f32(hi)) (w - hi is exact in fp32):
+// one packed round-toward-zero conversion for the hi parts (v_cvt_pkrtz_f16_f32), and the lo parts
+// as fused multiply-adds of each hi half with -1, one mixed-precision v_fma_mix per value reading its
+// half of the packed register.  Three instructions per pair: with round-to-nearest hi parts the
+// compiler converts each weight a second time for the v_fma_mix inputs (five).  hi + lo keeps
+// ~21 significant bits of w (|w - hi| < one fp16 ulp, lo rounded to nearest).  The -1 comes from an
+// identity DPP move: as a literal the compiler folds the multiply-add back into a subtraction.
 __device__ __forceinline__ float opaque_neg_one() {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                          __builtin_amdgcn_mov_dpp((int)0xBF800000u, 0xE4, 0xF, 0xF, false)));
 }
 __device__ __forceinline__ void split_hi_lo(float w0, float w1, uint32_t& hi, uint32_t& lo) {
-    const half2_t h = {(_Float16)w0, (_Float16)w1};
+    const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(w0, w1));
     const float m1 = opaque_neg_one();
     const half2_t l = {(_Float16)__builtin_fmaf(m1, (float)h.x, w0), (_Float16)__builtin_fmaf(m1, (float)h.y, w1)};
     hi = __builtin_bit_cast(uint32_t, h);
