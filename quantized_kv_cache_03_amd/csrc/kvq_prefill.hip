@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     // workgroup's last repeat that tile; their tokens are masked by every wave.
     const int st_tile = (wave >> 1) & 1;
     const bool st_k = (wave & 1) == 0;
-    const bool stager = wave < 2 * kPfTW;  // the first four waves stage; any others only compute
+    const bool stager = kPfWaves <= 2 * kPfTW || wave < 2 * kPfTW;  // the first four waves stage; any others only compute
     struct Staged { u32x4 x0, x1; float4_t sc; int valid; };
     auto stage_load = [&](int t0) {
         Staged r{};
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 
     // Softmax of a chunk and its P V^T, with the lazy rescale (kRescaleSlack, kRescaleSlackInt8; a
     // branch every lane takes or skips together).
-    auto softmax_pv = [&](const PfStage& st, const SBuf& sb, int t0, auto&& mid) {
+    auto softmax_pv = [&](const PfStage& st, SBuf& sb, int t0, auto&& mid) {
         const int tok_base = t0 * kBlock;  // first token of the chunk
         float4_t ks4[TW], vs4[TW];         // INT8: the scales of this lane's four tokens of each tile
 #pragma unroll
@@ -262,6 +262,25 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                 ks4[i] = *reinterpret_cast<const float4_t*>(&st.s[i][4 * q4]);
                 vs4[i] = *reinterpret_cast<const float4_t*>(&st.s[i][kBlock + 4 * q4]);
             }
+        }
+        // The causal mask: a token past the column's own position gets -inf.  Only the chunks that
+        // reach past the wave's first row need it (wave-uniform test).  FOLD masks the products
+        // in place (they are the logits, scaled in the exponent; in place, the registers need no
+        // copies where the branch joins); otherwise the scaled logits are masked.
+        const bool diag = tok_base + TW * kBlock - 1 > pos_min;
+        auto mask = [&](auto& v) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int lim = pos[nb] - (tok_base + 4 * q4);  // last visible offset in the chunk
+#pragma unroll
+                for (int i = 0; i < TW; ++i)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (i * kBlock + t > lim) v[nb][i][t] = kNegInf;
+            }
+        };
+        if constexpr (FOLD) {
+            if (diag) mask(sb.s);
         }
         float z[NB][TW][4];
 #pragma unroll
@@ -278,18 +297,8 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                         z[nb][i][t] = sb.s[nb][i][t] * f;
                     }
                 }
-        // The causal mask: a token past the column's own position gets -inf.  Only the chunks that
-        // reach past the wave's first row need it (wave-uniform test).
-        if (tok_base + TW * kBlock - 1 > pos_min) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int lim = pos[nb] - (tok_base + 4 * q4);  // last visible offset in the chunk
-#pragma unroll
-                for (int i = 0; i < TW; ++i)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        if (i * kBlock + t > lim) z[nb][i][t] = kNegInf;
-            }
+        if constexpr (!FOLD) {
+            if (diag) mask(z);
         }
         // Every column sees token 0, which the first chunk holds, so the reference max is finite
         // from then on.
