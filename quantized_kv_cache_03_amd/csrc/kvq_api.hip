@@ -113,13 +113,21 @@ int check_fp8_math(const kvq_cache* c) {
 // Work split of the decode attention.  Fixed partitions: P partitions of PS tokens (P == 1: one
 // pass, no workspace).  Balanced split: NW waves per head row (query heads for MHA, KV heads for
 // grouped heads), about kBalancedWaves waves in all -- two per SIMD of the 1024 on the chip, enough
-// to keep HBM busy while each wave streams a long, equal share.  A wave gets at least kMinTiles
-// tiles (the device caps the waves it uses by the same rule on the actual tile count).
+// to keep HBM busy while each wave streams a long, equal share -- and four per SIMD for the one-head
+// INT8 kernel, which holds four waves per SIMD and measured faster with them.  A wave gets at least
+// kMinTiles tiles (the device caps the waves it uses by the same rule on the actual tile count).
+// The workspace is sized for the largest target of the shape (any cache dtype fits it).
 #ifndef KVQ_BALANCED_WAVES
 #define KVQ_BALANCED_WAVES 2048
 #endif
 constexpr int64_t kBalancedWaves = KVQ_BALANCED_WAVES;
+constexpr int64_t kBalancedWavesInt8Mha = 2 * kBalancedWaves;
 constexpr int64_t kMinTiles = 8;
+
+// Waves in all for the balanced split of a cache dtype (dtype < 0: the largest over the dtypes).
+int64_t balanced_wave_target(int dtype, int32_t Hq, int32_t Hkv) {
+    return (Hq == Hkv && (dtype < 0 || dtype == KVQ_INT8)) ? kBalancedWavesInt8Mha : kBalancedWaves;
+}
 
 struct Plan {
     int32_t P = 1;
@@ -129,12 +137,13 @@ struct Plan {
     size_t plan_bytes = 0;   // balanced split: int32 [batch + 2]
 };
 
-Plan plan(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_context_len, int32_t partition_size) {
+Plan plan(int32_t batch, int32_t Hq, int32_t Hkv, int32_t max_context_len, int32_t partition_size,
+          int64_t waves) {
     Plan p;
     if (partition_size == KVQ_PARTITION_BALANCED) {
         const int64_t hw = Hq == Hkv ? Hq : Hkv;
         const int64_t max_tiles = (int64_t)batch * (((int64_t)max_context_len + KVQ_BLOCK_SIZE - 1) / KVQ_BLOCK_SIZE);
-        int64_t nw = (kBalancedWaves + hw - 1) / hw;
+        int64_t nw = (waves + hw - 1) / hw;
         nw = std::min(nw, std::max<int64_t>(1, (max_tiles + kMinTiles - 1) / kMinTiles));
         nw = std::min<int64_t>(nw, 65535);
         p.NW = (int32_t)nw;
@@ -242,7 +251,8 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
     const int st = check_decode_sizes(batch, num_q_heads, num_kv_heads, max_context_len, partition_size);
     memcpy(g_err, saved, sizeof(g_err));
     if (st != KVQ_OK) return 0;
-    return plan_workspace_bytes(plan(batch, num_q_heads, num_kv_heads, max_context_len, partition_size));
+    return plan_workspace_bytes(plan(batch, num_q_heads, num_kv_heads, max_context_len, partition_size,
+                                     balanced_wave_target(-1, num_q_heads, num_kv_heads)));
 }
 
 }  // extern "C"
@@ -271,7 +281,8 @@ int decode_common(const char* where, bool fp8_math, const kvq_cache* cache, cons
     if (!q || !out) return fail(KVQ_ERR_ARG, "q / out is NULL");
     if ((k_new == nullptr) != (v_new == nullptr)) return fail(KVQ_ERR_ARG, "k_new / v_new is NULL");
 
-    const Plan p = plan(batch, num_q_heads, cache->num_kv_heads, max_context_len, partition_size);
+    const Plan p = plan(batch, num_q_heads, cache->num_kv_heads, max_context_len, partition_size,
+                        balanced_wave_target(cache->dtype, num_q_heads, cache->num_kv_heads));
     const size_t need = plan_workspace_bytes(p);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVQ_ERR_WORKSPACE, "split-K workspace of %zu bytes needed, %zu given%s", need,

@@ -15,10 +15,14 @@ MIN_TILES = 8
 BALANCED_WAVES = 2048
 
 
-def host_nw(batch, hq, hkv, max_ctx):
+def host_nw(batch, hq, hkv, max_ctx, waves=None):
+    """NW of the host plan.  The workspace is sized for the largest wave target of the shape: twice
+    BALANCED_WAVES with one query head per KV head (the INT8 one-head kernel's target)."""
+    if waves is None:
+        waves = 2 * BALANCED_WAVES if hq == hkv else BALANCED_WAVES
     hw = hq if hq == hkv else hkv
     max_tiles = batch * ((max_ctx + 15) // 16)
-    nw = (BALANCED_WAVES + hw - 1) // hw
+    nw = (waves + hw - 1) // hw
     nw = min(nw, max(1, (max_tiles + MIN_TILES - 1) // MIN_TILES))
     return min(nw, 65535)
 
