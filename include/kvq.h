@@ -158,8 +158,9 @@ size_t kvq_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num
  *                      0                      one pass per sequence, no workspace;
  *                      a positive multiple of 16: fixed partitions of that many tokens;
  *                      KVQ_PARTITION_BALANCED the tiles of all sequences, laid end to end, are cut
- *                                             into equal shares, about 2048 waves in all (4096 for
- *                                             an INT8 cache with one query head per KV head),
+ *                                             into equal shares, about 2048 waves in all (with one
+ *                                             query head per KV head: 4096 for an INT8 cache, 3072
+ *                                             for INT4),
  *                                             whatever the mix of context lengths (a share may hold
  *                                             the end of one sequence and the start of the next).
  *                    For given arguments the result is bitwise deterministic.

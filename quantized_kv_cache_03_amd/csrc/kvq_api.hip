@@ -113,8 +113,9 @@ int check_fp8_math(const kvq_cache* c) {
 // Work split of the decode attention.  Fixed partitions: P partitions of PS tokens (P == 1: one
 // pass, no workspace).  Balanced split: NW waves per head row (query heads for MHA, KV heads for
 // grouped heads), about kBalancedWaves waves in all -- two per SIMD of the 1024 on the chip, enough
-// to keep HBM busy while each wave streams a long, equal share -- and four per SIMD for the one-head
-// INT8 kernel, which holds four waves per SIMD and measured faster with them.  A wave gets at least
+// to keep HBM busy while each wave streams a long, equal share -- four per SIMD for the one-head
+// INT8 kernel and three for the one-head INT4 kernel, which hold that many waves per SIMD and
+// measured faster with them.  A wave gets at least
 // kMinTiles tiles (the device caps the waves it uses by the same rule on the actual tile count).
 // The workspace is sized for the largest target of the shape (any cache dtype fits it).
 #ifndef KVQ_BALANCED_WAVES
@@ -122,11 +123,15 @@ int check_fp8_math(const kvq_cache* c) {
 #endif
 constexpr int64_t kBalancedWaves = KVQ_BALANCED_WAVES;
 constexpr int64_t kBalancedWavesInt8Mha = 2 * kBalancedWaves;
+constexpr int64_t kBalancedWavesInt4Mha = 3 * kBalancedWaves / 2;
 constexpr int64_t kMinTiles = 8;
 
 // Waves in all for the balanced split of a cache dtype (dtype < 0: the largest over the dtypes).
 int64_t balanced_wave_target(int dtype, int32_t Hq, int32_t Hkv) {
-    return (Hq == Hkv && (dtype < 0 || dtype == KVQ_INT8)) ? kBalancedWavesInt8Mha : kBalancedWaves;
+    if (Hq != Hkv) return kBalancedWaves;
+    if (dtype < 0 || dtype == KVQ_INT8) return kBalancedWavesInt8Mha;
+    if (dtype == KVQ_INT4) return kBalancedWavesInt4Mha;
+    return kBalancedWaves;
 }
 
 struct Plan {
