@@ -57,33 +57,9 @@ __device__ __forceinline__ int k_slot_dim(int dw0, int odd, int slot) {
     return 8 * dw + i + 4 * (slot % 2);
 }
 
-// One lane's share of one tile: K of token l % 16 in chunk l / 16 and V of quad l / 16 for the dims
-// l % 16 + 16 r (one 16-byte load each), and the K and V (scale, zero point) pairs of the lane's own
-// token 4 (l / 16) + l % 4 -- one of the four tokens 4 q4 + u of the lane's accumulator, so each
-// quad of lanes holds all four and hands them round with quad broadcasts (no LDS round trip), and a
-// tile costs 12 registers while its loads are in flight.
-struct TileG4 {
-    u32x4 k, v;
-    f32x2 kp, vp;
-};
-__device__ __forceinline__ void load_tile_g4(const KernelParams& a, TileG4& t, int blk, int g, uint32_t off,
-                                             int own) {
-    const size_t pair = (size_t)blk * a.Hkv + g;
-    t.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.kc + pair * kTileBytes4 + off));
-    t.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vc + pair * kTileBytes4 + off));
-    t.kp = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(a.ks) + pair * kBlock + own);
-    t.vp = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(a.vs) + pair * kBlock + own);
-}
-
-// Value of lane 4 (l / 4) + U of the lane's quad (DPP quad_perm [U, U, U, U]).
-template <int U>
-__device__ __forceinline__ float quad_bcast(float v) {
-    return dpp<U * 0x55>(v);
-}
-
 // One chunk of kTiles4 tiles (tiles past the segment's end repeat its last one; their tokens are masked).
 template <bool APPEND>
-__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTiles4], int tile0, int t_end,
+__device__ __forceinline__ void chunk_g4(const KernelParams& a, TileQ4 (&t)[kTiles4], int tile0, int t_end,
                                          const half8_v (&qe)[2], const half8_v (&qo)[2], float qsum, float qf,
                                          int q4, float& m_run, float& l_lane, float& z_lane,
                                          float4_t (&acc)[8]) {
@@ -96,7 +72,8 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTil
     for (int i = 0; i < kTiles4; ++i) {
         // every token centred at its own zero code c0 (int4_zero_code), computed once per token by
         // the lanes holding its pairs; the K operand rows (token col) take it by shuffle, and the
-        // accumulator's tokens 4 q4 + u take their K scale and zp' = zp + s c0 by quad broadcast.
+        // accumulator's tokens 4 q4 + u take their K scale and zp' = zp + s c0 by quad broadcast
+        // (fenced: quad_bcast).
         // The V pairs of slots at and past t_end are zeroed first (past the context they may be
         // NaN, and a zero weight alone would still give 0 * NaN); only a tile that reaches past
         // the end has such slots (wave-uniform test).
@@ -105,10 +82,12 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTil
         if ((tile0 + i + 1) * kBlock > t_end && (tile0 + i) * kBlock + own >= t_end) t[i].vp = f32x2{0.0f, 0.0f};
         const float zc = __shfl(zo, src);
         float ks[4], zps[4];  // K scale and zp' of the tokens 4 q4 + u
+        __builtin_amdgcn_sched_barrier(0);
         ks[0] = quad_bcast<0>(t[i].kp.x), zps[0] = quad_bcast<0>(zpa);
         ks[1] = quad_bcast<1>(t[i].kp.x), zps[1] = quad_bcast<1>(zpa);
         ks[2] = quad_bcast<2>(t[i].kp.x), zps[2] = quad_bcast<2>(zpa);
         ks[3] = quad_bcast<3>(t[i].kp.x), zps[3] = quad_bcast<3>(zpa);
+        __builtin_amdgcn_sched_barrier(0);
         half2_t ne, no;
         int4_centre_pairs(zc, ne, no);
         half8_v e[2], o[2];
@@ -155,10 +134,12 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTil
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i) {
         float w[4];
+        __builtin_amdgcn_sched_barrier(0);
         const float vs[4] = {quad_bcast<0>(t[i].vp.x), quad_bcast<1>(t[i].vp.x), quad_bcast<2>(t[i].vp.x),
                              quad_bcast<3>(t[i].vp.x)};  // the V pairs of the tokens 4 q4 + u
         const float vz[4] = {quad_bcast<0>(t[i].vp.y), quad_bcast<1>(t[i].vp.y), quad_bcast<2>(t[i].vp.y),
                              quad_bcast<3>(t[i].vp.y)};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(z[i][u], qf, -m_run));
@@ -197,7 +178,7 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileG4 (&t)[kTil
 
 // Replace the new token's codes and pairs in the registers of its tile: K in the four lanes whose
 // operand row is the token, both pairs in the four lanes that own them, V in the 16 lanes of its quad.
-__device__ __forceinline__ void patch_tile_g4(TileG4& t, const NewToken4& nt, const uint8_t* lds_k,
+__device__ __forceinline__ void patch_tile_g4(TileQ4& t, const NewToken4& nt, const uint8_t* lds_k,
                                               const uint8_t* lds_v, int lane) {
     const int col = lane & 15, q4 = lane >> 4;
     if (col == nt.slot) t.k = reinterpret_cast<const u32x4*>(lds_k)[q4];
@@ -286,10 +267,11 @@ __device__ __forceinline__ void gqa4_segment(const KernelParams& a, int b, int g
         // with no branch between them; the extra tiles' tokens lie past the segment and are masked.
         const int blk_lane = bt[tb + min(lane, nt_grp - 1)];
         for (int c0 = 0; c0 < nt_grp; c0 += kTiles4) {
-            TileG4 t[kTiles4];
+            TileQ4 t[kTiles4];
 #pragma unroll
             for (int i = 0; i < kTiles4; ++i)
-                load_tile_g4(a, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, 4 * q4 + (col & 3));
+                load_tile_q4<true>(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g,
+                                   off, int4_own_token(lane));
             if constexpr (APPEND) {
                 const int inew = tile_new - (tb + c0);  // wave-uniform
                 if (inew >= 0 && inew < kTiles4) {

@@ -127,37 +127,40 @@ __device__ __forceinline__ uint32_t v_byte4(int t, int d) {
 }
 
 // One lane's share of one tile in the matrix-core lane layout (the grouped decode kernel and the
-// prefill kernel): K of token l % 16 in chunk l / 16 and that token's K (scale, zero point), V of
-// quad l / 16 for the dims l % 16 + 16 r (one 16-byte load each), and the (scale, zero point)
-// pairs of the quad's tokens 4 (l / 16) .. +3.
-struct TileMfma4 {
+// prefill kernel): K of token l % 16 in chunk l / 16 and V of quad l / 16 for the dims l % 16 + 16 r
+// (one 16-byte load each), and the K and V (scale, zero point) pairs of the lane's own token
+// 4 (l / 16) + l % 4 -- one of the four tokens 4 q4 + u of the lane's accumulator, so each quad of
+// lanes holds all four and hands them round with quad broadcasts (quad_bcast), and a tile costs 12
+// registers while its loads are in flight.
+struct TileQ4 {
     u32x4 k, v;
-    f32x2 kp;         // K (scale, zero point) of the K operand's token l % 16
-    float4_t ks, kz;  // K (scale, zero point) of the four tokens
-    float4_t vs, vz;  // V (scale, zero point) of the same tokens
+    f32x2 kp, vp;
 };
+__device__ __forceinline__ int int4_own_token(int lane) { return 4 * (lane >> 4) + (lane & 3); }
 
-// Load tile (blk, g) for this lane (off = 256 q4 + 16 col); ks / vs are the [blocks][Hkv][16][2]
-// pair arrays.  NT: the streaming hint (decode reads each tile once; prefill re-reads it for every
-// row tile of the sequence and keeps the ordinary caching).
+// NT: the streaming hint (decode reads each tile once; prefill re-reads it for every row tile of
+// the sequence and keeps the ordinary caching).  ks / vs are the [blocks][Hkv][16][2] pair arrays.
 template <bool NT>
-__device__ __forceinline__ void load_tile_mfma4(const uint8_t* kc, const uint8_t* vc, const float* ks,
-                                                const float* vs, int Hkv, TileMfma4& t, int blk, int g,
-                                                uint32_t off, int q4) {
-    const size_t tile = ((size_t)blk * Hkv + g) * kTileBytes4;
-    t.k = ld<NT>(reinterpret_cast<const u32x4*>(kc + tile + off));
-    t.v = ld<NT>(reinterpret_cast<const u32x4*>(vc + tile + off));
-    t.kp = ld<NT>(reinterpret_cast<const f32x2*>(ks) + ((size_t)blk * Hkv + g) * kBlock + ((off >> 4) & 15u));
-    // (scale, zero point) pairs of four tokens: two 16-byte loads each for K and V
-    const size_t so = (((size_t)blk * Hkv + g) * kBlock + 4 * q4) * 2;
-    const float4_t k0 = ld<NT>(reinterpret_cast<const float4_t*>(ks + so));
-    const float4_t k1 = ld<NT>(reinterpret_cast<const float4_t*>(ks + so + 4));
-    const float4_t v0 = ld<NT>(reinterpret_cast<const float4_t*>(vs + so));
-    const float4_t v1 = ld<NT>(reinterpret_cast<const float4_t*>(vs + so + 4));
-    t.ks = float4_t{k0[0], k0[2], k1[0], k1[2]};
-    t.kz = float4_t{k0[1], k0[3], k1[1], k1[3]};
-    t.vs = float4_t{v0[0], v0[2], v1[0], v1[2]};
-    t.vz = float4_t{v0[1], v0[3], v1[1], v1[3]};
+__device__ __forceinline__ void load_tile_q4(const uint8_t* kc, const uint8_t* vc, const float* ks,
+                                             const float* vs, int Hkv, TileQ4& t, int blk, int g, uint32_t off,
+                                             int own) {
+    const size_t pair = (size_t)blk * Hkv + g;
+    t.k = ld<NT>(reinterpret_cast<const u32x4*>(kc + pair * kTileBytes4 + off));
+    t.v = ld<NT>(reinterpret_cast<const u32x4*>(vc + pair * kTileBytes4 + off));
+    t.kp = ld<NT>(reinterpret_cast<const f32x2*>(ks) + pair * kBlock + own);
+    t.vp = ld<NT>(reinterpret_cast<const f32x2*>(vs) + pair * kBlock + own);
+}
+
+// Value of lane 4 (l / 4) + U of the lane's quad (DPP quad_perm [U, U, U, U]).  In the matrix-core
+// kernels every group of these broadcasts is fenced off from the scheduler
+// (__builtin_amdgcn_sched_barrier on both sides): interleaved with the surrounding matrix and VALU
+// instructions, the K-pair broadcasts of the INT4 prefill kernel gave NaN outputs on the
+// low-binade codes test, and with the fences (or with LDS shuffles instead) the same kernel is
+// correct.  The cause was not established, so the fences stay wherever these broadcasts meet
+// matrix-core code.
+template <int U>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return dpp<U * 0x55>(v);
 }
 
 // The 16-bit unit of a V dword (SEL 0: bits 0-15, 1: bits 16-31: four tokens of one dim) as two

@@ -75,6 +75,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int lane = threadIdx.x;
     const int col = lane & 15;  // column of each block: (row jr, head hg)
     const int q4 = lane >> 4;   // MFMA k-group / C row group
+    const int own = int4_own_token(lane);         // the token of the lane's K and V pairs
+    const int src = 16 * (col >> 2) + (col & 3);  // a lane whose pairs are those of token col
 
     const int r0 = a.cu_q[b];
     const int nq = a.cu_q[b + 1] - r0;
@@ -108,7 +110,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     for (int nb = 0; nb < NB; ++nb) pos[nb] = live[nb] ? n - nq + j0 + nb * a.R + jr : pos_min;
     const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks;
 
-    // Q^T operands of each block's column over chunk q4's dims, and the sum of its 128 q elements
+    // Q^T operands of each block's column over chunk q4's dims, and the sum of its 128 q elements.
+    // The logit scale f = sm_scale log2(e) is applied in the exponent as |f| (exp2(fma(z, |f|, -m))
+    // with the chunk max taken on the unscaled z and scaled once); a negative f negates q instead.
+    const bool neg = a.qk_scale < 0.0f;
+    const _Float16 qsign = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+    const float qf = fmaxf(fabsf(a.qk_scale), 1.17549435e-38f);  // -inf * qf must stay -inf
     half8_v qB[NB][4];
     float qsum[NB];
 #pragma unroll
@@ -138,9 +145,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 #pragma unroll
                 for (int s = 0; s < 8; ++s)
                     qB[nb][m][s] = __builtin_bit_cast(_Float16, qv[kslot_dim(m, s)]) *
-                                   (_Float16)((m & 1) ? 0.0625f : 1.0f);
+                                   (qsign * (_Float16)((m & 1) ? 0.0625f : 1.0f));
         }
-        qsum[nb] = a.qk_scale * col_sum4(qsum[nb]);  // the logit term of the zero points: qsum * zp'
+        qsum[nb] = col_sum4(qsum[nb]);  // the logit term of the zero points: qsum * zp'
+        if (neg) qsum[nb] = -qsum[nb];
     }
 
     float m_run[NB], l_lane[NB], z_lane[NB];
@@ -160,26 +168,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         // with no branch between them; the extra tiles' tokens lie past every column's causal limit.
         const int blk_lane = bt[tb + min(lane, nt_grp - 1)];
         for (int c0 = 0; c0 < nt_grp; c0 += kTilesP4) {
-            TileMfma4 t[kTilesP4];  // this lane's share of each tile (kvq_int4.h)
+            TileQ4 t[kTilesP4];  // this lane's share of each tile (kvq_int4.h)
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i)
-                load_tile_mfma4<false>(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i],
-                                __builtin_amdgcn_readlane(blk_lane, c0 + i), g, off, q4);
+                load_tile_q4<false>(a.kc, a.vc, a.ks, a.vs, a.Hkv, t[i], __builtin_amdgcn_readlane(blk_lane, c0 + i), g,
+                                    off, own);
             const int tok_base = (tb + c0) * kBlock;
             const Int4Bits bits = int4_bits();
             float z[NB][kTilesP4][4];
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
-                // every token centred at its own zero code (int4_zero_code): the K operand row's
-                // token (col) from its pair kp, the accumulator's tokens 4 q4 + u from theirs
+                // every token centred at its own zero code (int4_zero_code), computed once per token
+                // by the lanes holding its pairs; the K operand rows (token col) take it by shuffle,
+                // the accumulator's tokens 4 q4 + u take their K scale and zp' = zp + s c0 by quad
+                // broadcast.  The V pairs of slots past the context are zeroed first (they may be
+                // NaN, and a zero weight alone would still give 0 * NaN); only the chunk reaching
+                // past the context has such slots (wave-uniform test).
+                const float zo = int4_zero_code(t[i].kp.x, t[i].kp.y);
+                const float zpa = __builtin_fmaf(t[i].kp.x, zo, t[i].kp.y);
+                if (tok_base + kTilesP4 * kBlock > n && tok_base + i * kBlock + own >= n) t[i].vp = f32x2{0.0f, 0.0f};
                 half2_t ne, no;
-                int4_centre_pairs(int4_zero_code(t[i].kp.x, t[i].kp.y), ne, no);
+                int4_centre_pairs(__shfl(zo, src), ne, no);
                 half8_v kop[4];
                 k_operands_p4(t[i].k, ne, no, bits, kop);
-                float zp[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    zp[u] = __builtin_fmaf(t[i].ks[u], int4_zero_code(t[i].ks[u], t[i].kz[u]), t[i].kz[u]);
+                float ks[4], zp[4];
+                __builtin_amdgcn_sched_barrier(0);
+                ks[0] = quad_bcast<0>(t[i].kp.x), zp[0] = quad_bcast<0>(zpa);
+                ks[1] = quad_bcast<1>(t[i].kp.x), zp[1] = quad_bcast<1>(zpa);
+                ks[2] = quad_bcast<2>(t[i].kp.x), zp[2] = quad_bcast<2>(zpa);
+                ks[3] = quad_bcast<3>(t[i].kp.x), zp[3] = quad_bcast<3>(zpa);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     float4_t s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[0], qB[nb][0],
@@ -189,7 +207,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                     s = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[3], qB[nb][3], s, 0, 0, 0);
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        z[nb][i][u] = __builtin_fmaf(s[u], a.qk_scale * t[i].ks[u], qsum[nb] * zp[u]);
+                        z[nb][i][u] = __builtin_fmaf(s[u], ks[u], qsum[nb] * zp[u]);  // z / |f|
                 }
             }
             // The causal mask, only for the chunks that reach past the wave's first row
@@ -207,13 +225,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                             if (i * kBlock + u > lim) z[nb][i][u] = kNegInf;
                 }
             }
-            if (tok_base + kTilesP4 * kBlock > n) {
-#pragma unroll
-                for (int i = 0; i < kTilesP4; ++i)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (tok_base + i * kBlock + 4 * q4 + u >= n) t[i].vs[u] = t[i].vz[u] = 0.0f;
-            }
             // finite: the first chunk holds token 0.  Lazy rescale (kRescaleSlackInt4), a branch
             // every lane takes or skips together.
             bool moved = false;
@@ -226,7 +237,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 for (int i = 0; i < kTilesP4; ++i)
 #pragma unroll
                     for (int u = 0; u < 4; ++u) m = fmaxf(m, z[nb][i][u]);
-                cmax[nb] = col_max4(m);
+                cmax[nb] = col_max4(m) * qf;  // the max of z |f|
                 up[nb] = cmax[nb] > m_run[nb] + kRescaleSlackInt4;  // m_run = -inf: any finite max
                 moved |= up[nb];
             }
@@ -244,26 +255,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             // P^T operands per block: tokens (0, 2) and (1, 3) of this lane's quad of each tile,
             // w = p s_v (dword i of an operand: tile i's pair)
             half8_v we_hi[NB], we_lo[NB], wo_hi[NB], wo_lo[NB];
+            uint32_t ehi[NB][kTilesP4], elo[NB][kTilesP4], ohi[NB][kTilesP4], olo[NB][kTilesP4];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                uint32_t ehi[kTilesP4], elo[kTilesP4], ohi[kTilesP4], olo[kTilesP4];
+            for (int i = 0; i < kTilesP4; ++i) {
+                // the V pairs of the tokens 4 q4 + u, shared by both blocks
+                __builtin_amdgcn_sched_barrier(0);
+                const float vs[4] = {quad_bcast<0>(t[i].vp.x), quad_bcast<1>(t[i].vp.x), quad_bcast<2>(t[i].vp.x),
+                                     quad_bcast<3>(t[i].vp.x)};
+                const float vz[4] = {quad_bcast<0>(t[i].vp.y), quad_bcast<1>(t[i].vp.y), quad_bcast<2>(t[i].vp.y),
+                                     quad_bcast<3>(t[i].vp.y)};
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < kTilesP4; ++i) {
+                for (int nb = 0; nb < NB; ++nb) {
                     float w[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const float pw = __builtin_amdgcn_exp2f(z[nb][i][u] - m_run[nb]);
+                        const float pw = __builtin_amdgcn_exp2f(__builtin_fmaf(z[nb][i][u], qf, -m_run[nb]));
                         l_lane[nb] += pw;
-                        w[u] = pw * t[i].vs[u];
-                        z_lane[nb] = __builtin_fmaf(pw, t[i].vz[u], z_lane[nb]);
+                        w[u] = pw * vs[u];
+                        z_lane[nb] = __builtin_fmaf(pw, vz[u], z_lane[nb]);
                     }
-                    split_hi_lo(w[0], w[2], ehi[i], elo[i]);
-                    split_hi_lo(w[1], w[3], ohi[i], olo[i]);
+                    split_hi_lo(w[0], w[2], ehi[nb][i], elo[nb][i]);
+                    split_hi_lo(w[1], w[3], ohi[nb][i], olo[nb][i]);
                 }
-                we_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ehi[0], ehi[1], ehi[2], ehi[3]});
-                we_lo[nb] = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
-                wo_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
-                wo_lo[nb] = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                we_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ehi[nb][0], ehi[nb][1], ehi[nb][2], ehi[nb][3]});
+                we_lo[nb] = __builtin_bit_cast(half8_v, u32x4{elo[nb][0], elo[nb][1], elo[nb][2], elo[nb][3]});
+                wo_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ohi[nb][0], ohi[nb][1], ohi[nb][2], ohi[nb][3]});
+                wo_lo[nb] = __builtin_bit_cast(half8_v, u32x4{olo[nb][0], olo[nb][1], olo[nb][2], olo[nb][3]});
             }
             // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 from dword d of every tile's V
 #pragma unroll
