@@ -120,6 +120,9 @@ def test_prefill_rows_beyond_context_get_zeros(H):
     ("llama2-7b-mha-e4m3", {}, [4096, 2500], [4096, 1200]),
     ("llama3-70b-gqa-e4m3-32k", {}, [8192], [2048]),
     ("llama3-8b-gqa-int4", {}, [4096, 1500], [4096, 700]),
+    ("llama2-13b-mha-int8", {}, [4096, 1500], [4096, 700]),
+    ("llama2-7b-mha-e4m3fnuz", {}, [4096, 1500], [4096, 700]),
+    ("llama3-8b-gqa-e5m2", {}, [4096, 1500], [4096, 700]),
 ])
 def test_prefill_full_size_sampled_rows(H, name, kw, ctx, nq):
     """Prompts at model size (all heads of the workload's layer); sampled rows against the oracle,
