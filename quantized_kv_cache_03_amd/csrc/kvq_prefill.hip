@@ -60,12 +60,35 @@ struct PrefillParams {
 constexpr int kPfWaves = KVQ_PREFILL_WAVES;
 constexpr int kPfTW = 2;  // tiles per chunk, paired for the PV products
 
-// One staged chunk: the tiles' codes as stored, and for INT8 the tiles' scale rows (K then V).
+// One staged chunk: the tiles' codes as stored (INT8: with their sign bits flipped), and for INT8 the
+// tiles' scale rows (K then V; the K scales times the logit scale, the V scales of the slots past
+// the context zero).
 struct alignas(16) PfStage {
     uint8_t k[kPfTW][kTileBytes];
     uint8_t v[kPfTW][kTileBytes];
     float s[kPfTW][2 * kBlock];
 };
+
+// Staged codes as fp16.  INT8 codes are staged with their sign bits flipped (q + 128 as unsigned
+// bytes), one XOR per staged dword instead of one per decoded dword in every wave: each byte goes
+// to the low byte of a half with high byte 0x64, the binary16 number 1024 + (q + 128), and
+// subtracting 1152 leaves q exactly (as int8x2_to_f16, without its XOR).
+template <int DT, int SEL>
+__device__ __forceinline__ half2_t staged_to_f16(uint32_t w) {
+    if constexpr (DT == KVQ_INT8) {
+        constexpr uint32_t sel = (SEL == 0) ? 0x04010400u : 0x04030402u;
+        const uint32_t x = __builtin_amdgcn_perm(0x64646464u, w, sel);
+        return __builtin_bit_cast(half2_t, x) - half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+    } else {
+        return codes_to_f16<DT, SEL>(w);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ half8_v staged8(uint32_t w0, uint32_t w1) {
+    return join8(staged_to_f16<DT, 0>(w0), staged_to_f16<DT, 1>(w0), staged_to_f16<DT, 0>(w1),
+                 staged_to_f16<DT, 1>(w1));
+}
 
 // FOLD (FP8 formats with a positive logit scale): the logit scale f is applied inside the exponent,
 // exp2(fma(s, f, -m)) with the raw products s and the chunk max taken on s (f > 0 keeps the order),
@@ -214,10 +237,27 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
             x1 = u32x4{keep_bytes(x1.x, r.valid), keep_bytes(x1.y, r.valid - 4), keep_bytes(x1.z, r.valid - 8),
                        keep_bytes(x1.w, r.valid - 12)};
         }
+        if constexpr (DT == KVQ_INT8) {  // (after the zeroing: a zeroed code reads as 0)
+            x0 ^= 0x80808080u;
+            x1 ^= 0x80808080u;
+        }
         *reinterpret_cast<u32x4*>(dst) = x0;
         *reinterpret_cast<u32x4*>(dst + 16) = x1;
         if constexpr (DT == KVQ_INT8) {
-            if (st_k && lane < 8) *reinterpret_cast<float4_t*>(&st.s[st_tile][4 * lane]) = r.sc;
+            // lanes 0..3: K scales of tokens 4 lane .. +3, times the logit scale (the product each
+            // logit takes); lanes 4..7: V scales of tokens 4 (lane - 4) .. +3, those past the context
+            // zeroed (they may be NaN, and a zero weight times NaN is NaN)
+            if (st_k && lane < 8) {
+                float4_t sc = r.sc;
+                if (lane < 4) {
+                    sc *= a.qk_scale;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * (lane - 4) + j >= r.valid) sc[j] = 0.0f;
+                }
+                *reinterpret_cast<float4_t*>(&st.s[st_tile][4 * lane]) = sc;
+            }
         }
     };
 
@@ -235,8 +275,8 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                 for (int nb = 0; nb < NB; ++nb)
                     sb.s[nb][i] = mfma_qk_fp8<DT>(k8, q8[nb], float4_t{0.0f, 0.0f, 0.0f, 0.0f});
             } else {
-                const half8_v k0 = codes8<DT>(ka.x, ka.y), k1 = codes8<DT>(ka.z, ka.w);
-                const half8_v k2 = codes8<DT>(kb.x, kb.y), k3 = codes8<DT>(kb.z, kb.w);
+                const half8_v k0 = staged8<DT>(ka.x, ka.y), k1 = staged8<DT>(ka.z, ka.w);
+                const half8_v k2 = staged8<DT>(kb.x, kb.y), k3 = staged8<DT>(kb.z, kb.w);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     float4_t c = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -254,7 +294,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     // branch every lane takes or skips together).
     auto softmax_pv = [&](const PfStage& st, SBuf& sb, int t0, auto&& mid) {
         const int tok_base = t0 * kBlock;  // first token of the chunk
-        float4_t ks4[TW], vs4[TW];         // INT8: the scales of this lane's four tokens of each tile
+        float4_t ks4[TW], vs4[TW];         // INT8: the (staged) scales of this lane's four tokens of each tile
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
             ks4[i] = vs4[i] = float4_t{1.0f, 1.0f, 1.0f, 1.0f};
@@ -291,21 +331,23 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                 for (int t = 0; t < 4; ++t) {
                     if constexpr (FOLD) {
                         z[nb][i][t] = sb.s[nb][i][t];  // scaled inside the exponent below
+                    } else if constexpr (DT == KVQ_INT8) {
+                        z[nb][i][t] = sb.s[nb][i][t] * ks4[i][t];  // (K scale times the logit scale)
                     } else {
-                        float f = qk_f[nb];
-                        if constexpr (DT == KVQ_INT8) f *= ks4[i][t];
-                        z[nb][i][t] = sb.s[nb][i][t] * f;
+                        z[nb][i][t] = sb.s[nb][i][t] * qk_f[nb];
                     }
                 }
         if constexpr (!FOLD) {
             if (diag) mask(z);
         }
         // Every column sees token 0, which the first chunk holds, so the reference max is finite
-        // from then on.
+        // from then on.  The column max (over the column's four lanes) is taken only when some
+        // lane's own max passes the reference max plus the slack: the column max passes it exactly
+        // when one of its lanes' maxima does (scaling by f > 0 is monotone), so the rescale
+        // decisions are those of the column max, without its cross-lane reduction on every chunk.
         constexpr float slack = DT == KVQ_INT8 ? kRescaleSlackInt8 : kRescaleSlack;
         bool moved = false;
-        bool up[NB];
-        float cmax[NB];
+        float lmax[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             float m = kNegInf;
@@ -313,19 +355,21 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
             for (int i = 0; i < TW; ++i)
 #pragma unroll
                 for (int t = 0; t < 4; ++t) m = fmaxf(m, z[nb][i][t]);
-            cmax[nb] = col_max4(m);
-            if constexpr (FOLD) cmax[nb] *= qk_f[nb];  // the max of s f, as f > 0
-            up[nb] = cmax[nb] > m_run[nb] + slack;  // m_run = -inf: any finite max
-            moved |= up[nb];
+            lmax[nb] = m;
+            if constexpr (FOLD) m *= qk_f[nb];  // the max of s f, as f > 0
+            moved |= m > m_run[nb] + slack;     // m_run = -inf: any finite max
         }
         if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const float alpha = up[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - cmax[nb]) : 1.0f;
+                float cmax = col_max4(lmax[nb]);
+                if constexpr (FOLD) cmax *= qk_f[nb];
+                const bool up = cmax > m_run[nb] + slack;
+                const float alpha = up ? __builtin_amdgcn_exp2f(m_run[nb] - cmax) : 1.0f;
                 l_lane[nb] *= alpha;
 #pragma unroll
                 for (int r = 0; r < 8; ++r) acc[nb][r] *= alpha;
-                if (up[nb]) m_run[nb] = cmax[nb];
+                if (up) m_run[nb] = cmax;
             }
         }
         // the next chunk's S^T products, in the same basic block as the weights and P V^T below, so
@@ -346,8 +390,8 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                                           : __builtin_amdgcn_exp2f(z[nb][u][t] - m_run[nb]);
                     l_lane[nb] += pw;
                     w[t] = pw;
-                    // INT8: slots past the context may hold NaN scales; their weight is zero
-                    if constexpr (DT == KVQ_INT8) w[t] = (pw > 0.0f) ? pw * vs4[u][t] : 0.0f;
+                    // INT8: the slots past the context have zero weights and (staged) zero scales
+                    if constexpr (DT == KVQ_INT8) w[t] = pw * vs4[u][t];
                 }
                 split_hi_lo(w[0], w[1], h[2 * u], l[2 * u]);
                 split_hi_lo(w[2], w[3], h[2 * u + 1], l[2 * u + 1]);
@@ -365,8 +409,8 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
         // position have zero weights)
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const half8_v va8 = join8(codes_to_f16<DT, 0>(vd[0][r]), codes_to_f16<DT, 1>(vd[0][r]),
-                                      codes_to_f16<DT, 0>(vd[1][r]), codes_to_f16<DT, 1>(vd[1][r]));
+            const half8_v va8 = join8(staged_to_f16<DT, 0>(vd[0][r]), staged_to_f16<DT, 1>(vd[0][r]),
+                                      staged_to_f16<DT, 0>(vd[1][r]), staged_to_f16<DT, 1>(vd[1][r]));
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, whi[nb], acc[nb][r], 0, 0, 0);

@@ -226,10 +226,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 }
             }
             // finite: the first chunk holds token 0.  Lazy rescale (kRescaleSlackInt4), a branch
-            // every lane takes or skips together.
+            // every lane takes or skips together.  The column max (over the column's four lanes)
+            // is taken only when some lane's own max passes the reference max plus the slack: the
+            // column max passes it exactly when one of its lanes' maxima does (scaling by |f| > 0
+            // is monotone).
             bool moved = false;
-            bool up[NB];
-            float cmax[NB];
+            float lmax[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float m = kNegInf;
@@ -237,15 +239,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 for (int i = 0; i < kTilesP4; ++i)
 #pragma unroll
                     for (int u = 0; u < 4; ++u) m = fmaxf(m, z[nb][i][u]);
-                cmax[nb] = col_max4(m) * qf;  // the max of z |f|
-                up[nb] = cmax[nb] > m_run[nb] + kRescaleSlackInt4;  // m_run = -inf: any finite max
-                moved |= up[nb];
+                lmax[nb] = m;
+                moved |= m * qf > m_run[nb] + kRescaleSlackInt4;  // m_run = -inf: any finite max
             }
             if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const float alpha = up[nb] ? __builtin_amdgcn_exp2f(m_run[nb] - cmax[nb]) : 1.0f;
-                    if (up[nb]) m_run[nb] = cmax[nb];
+                    const float cmax = col_max4(lmax[nb]) * qf;  // the max of z |f|
+                    const bool up = cmax > m_run[nb] + kRescaleSlackInt4;
+                    const float alpha = up ? __builtin_amdgcn_exp2f(m_run[nb] - cmax) : 1.0f;
+                    if (up) m_run[nb] = cmax;
                     l_lane[nb] *= alpha;
                     z_lane[nb] *= alpha;
 #pragma unroll
