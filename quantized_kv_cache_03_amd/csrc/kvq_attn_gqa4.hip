@@ -154,7 +154,10 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileQ4 (&t)[kTil
     const half8_v we_lo = __builtin_bit_cast(half8_v, u32x4{elo[0], elo[1], elo[2], elo[3]});
     const half8_v wo_hi = __builtin_bit_cast(half8_v, u32x4{ohi[0], ohi[1], ohi[2], ohi[3]});
     const half8_v wo_lo = __builtin_bit_cast(half8_v, u32x4{olo[0], olo[1], olo[2], olo[3]});
-    // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 (dims 16 r .. +15) from dword d of every tile's V
+    // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 (dims 16 r .. +15) from dword d of every tile's V,
+    // at raised wave priority (s_setprio 1): when waves of a SIMD compete, the one feeding the
+    // matrix cores issues first
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         half2_t hv[kTiles4][4];
@@ -174,6 +177,7 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileQ4 (&t)[kTil
             acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, wo_lo, acc[r], 0, 0, 0);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // Replace the new token's codes and pairs in the registers of its tile: K in the four lanes whose

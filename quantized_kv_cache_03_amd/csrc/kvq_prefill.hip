@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
     constexpr int TW = kPfTW;
     __shared__ PfStage stage[3];  // three chunks: one read by the softmax, one by S^T, one filling
     const int g = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (wave-uniform: scalar registers)
     const int lane = threadIdx.x & 63;
     // the row-tile groups of a sequence run last-first: later rows read more tiles (longest first)
     const int rt = kPfWaves * (a.row_tiles - 1 - (int)blockIdx.y) + wave;
@@ -373,7 +373,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
             }
         }
         // the next chunk's S^T products, in the same basic block as the weights and P V^T below, so
-        // that the scheduler can interleave their matrix instructions with this chunk's VALU work
+        // that the scheduler can interleave their matrix instructions with this chunk's VALU work.
+        // The wave runs this matrix-core block at raised priority (s_setprio 1, back to 0 after
+        // P V^T): when both waves of a SIMD have an instruction ready, the one feeding the matrix
+        // cores issues first, and the other's softmax front, staging and barrier fill its gaps.
+        // (Not under FP8 math, whose S^T is one matrix instruction per block and tile: there it
+        // measured slower.)
+        if constexpr (!F8Q) __builtin_amdgcn_s_setprio(1);
         mid();
 
         // weights of the tile pair, hi and lo fp16 parts, in the B layout, per block
@@ -417,6 +423,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
                 acc[nb][r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va8, wlo[nb], acc[nb][r], 0, 0, 0);
             }
         }
+        if constexpr (!F8Q) __builtin_amdgcn_s_setprio(0);
     };
 
     // Pipeline over the workgroup's chunks, three LDS buffers: at step c the staging loads of chunk

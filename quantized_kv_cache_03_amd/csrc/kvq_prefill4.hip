@@ -289,7 +289,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                 wo_hi[nb] = __builtin_bit_cast(half8_v, u32x4{ohi[nb][0], ohi[nb][1], ohi[nb][2], ohi[nb][3]});
                 wo_lo[nb] = __builtin_bit_cast(half8_v, u32x4{olo[nb][0], olo[nb][1], olo[nb][2], olo[nb][3]});
             }
-            // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 from dword d of every tile's V
+            // O^T += V^T P^T, row blocks r = 2 d, 2 d + 1 from dword d of every tile's V, at raised
+            // wave priority (s_setprio 1): when waves of a SIMD compete, the one feeding the matrix
+            // cores issues first
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 half2_t hv[kTilesP4][4];
@@ -312,6 +315,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                     }
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     }
 #pragma unroll
