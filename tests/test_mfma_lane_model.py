@@ -136,3 +136,50 @@ def test_output_rows_cover_every_dim_once():
     dim is written exactly once."""
     covered = sorted(16 * r + 4 * q4 + e for q4 in range(4) for r in range(8) for e in range(4))
     assert covered == list(range(DIM))
+
+
+def perm_b32(hi_src, lo_src, sel):
+    """v_perm_b32: byte i of the result is byte sel_i of the 8-byte value (hi_src:lo_src), for the
+    selector values 0..7 used here."""
+    pool = list(int(lo_src).to_bytes(4, "little")) + list(int(hi_src).to_bytes(4, "little"))
+    return int.from_bytes(bytes(pool[(sel >> (8 * i)) & 0xFF] for i in range(4)), "little")
+
+
+def test_staged_int8_decode_is_exact():
+    """The prefill kernel stages INT8 codes with their sign bits flipped and decodes a pair by
+    placing each byte under a 0x64 high byte (the binary16 number 1024 + byte) and subtracting
+    1152 in binary16: every signed code comes back exactly, in its slot."""
+    rng = np.random.default_rng(5)
+    codes = np.arange(-128, 128, dtype=np.int64)
+    for _ in range(4):
+        quads = np.stack([codes, rng.permutation(codes), rng.permutation(codes), rng.permutation(codes)], 1)
+        for c in quads:
+            w = sum((int(c[i]) & 0xFF) << (8 * i) for i in range(4)) ^ 0x80808080  # the staging flip
+            for pair, sel in ((0, 0x04010400), (1, 0x04030402)):
+                x = perm_b32(0x64646464, w, sel)
+                halves = np.array([x & 0xFFFF, x >> 16], np.uint16).view(np.float16)
+                got = (halves - np.float16(1152)).astype(np.float64)
+                assert list(got) == [c[2 * pair], c[2 * pair + 1]]
+
+
+def test_int8_scale_row_lanes():
+    """INT8 staging: lanes 0..7 of the K-staging wave carry a tile's scale row as four floats each
+    (the oracle's row: the 16 K scales, then the 16 V scales of the tile's tokens), and the softmax
+    of lane l reads the K and V scales of its accumulator rows 4 (l / 16) + t at 4 q4 + t and
+    16 + 4 q4 + t of the staged row."""
+    rng = np.random.default_rng(11)
+    k = (rng.standard_normal((BLOCK, 1, DIM)) * np.arange(1, BLOCK + 1)[:, None, None]).astype(np.float16)
+    v = (rng.standard_normal((BLOCK, 1, DIM)) * np.arange(BLOCK, 0, -1)[:, None, None]).astype(np.float16)
+    c = oracle.Cache(oracle.INT8, num_blocks=2, num_kv_heads=1)
+    oracle.append(c, k, v, np.array([[1]], np.int32), np.array([BLOCK], np.int32), np.array([0, BLOCK], np.int32))
+    _, ks = oracle.int8_quantize_rows(k[:, 0])
+    _, vs = oracle.int8_quantize_rows(v[:, 0])
+    flat = c.rows[1, 0].reshape(-1)  # the 128-byte row as stored
+    staged = np.empty(2 * BLOCK, np.float32)
+    for lane in range(8):  # lane's float4 at 4 lane
+        staged[4 * lane:4 * lane + 4] = flat[4 * lane:4 * lane + 4]
+    for l in range(LANES):
+        q4 = l // 16
+        for t in range(4):
+            assert staged[4 * q4 + t] == ks[4 * q4 + t]
+            assert staged[BLOCK + 4 * q4 + t] == vs[4 * q4 + t]
