@@ -68,6 +68,10 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileQ4 (&t)[kTil
     const int col = (int)(threadIdx.x & 15u);  // the token of the lane's K operand row
     const int own = 4 * q4 + (col & 3);        // the token of the lane's pairs
     const int src = 16 * (col >> 2) + (col & 3);  // a lane whose pairs are those of token col
+    // The K operands and S^T products run at raised wave priority, like P V^T below (s_setprio 1;
+    // back to 0 for the softmax): when waves of a SIMD compete, the one feeding the matrix cores
+    // issues first.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < kTiles4; ++i) {
         // every token centred at its own zero code c0 (int4_zero_code), computed once per token by
@@ -101,6 +105,7 @@ __device__ __forceinline__ void chunk_g4(const KernelParams& a, TileQ4 (&t)[kTil
 #pragma unroll
         for (int u = 0; u < 4; ++u) z[i][u] = __builtin_fmaf(s[u], ks[u], qsum * zps[u]);  // z / qf
     }
+    __builtin_amdgcn_s_setprio(0);
     // Tokens at and past t_end are masked; only a chunk that reaches past it has such tokens
     // (wave-uniform test).
     if ((tile0 + kTiles4) * kBlock > t_end) {

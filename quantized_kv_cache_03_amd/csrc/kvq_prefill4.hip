@@ -176,6 +176,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
             const int tok_base = (tb + c0) * kBlock;
             const Int4Bits bits = int4_bits();
             float z[NB][kTilesP4][4];
+            // The K operands and S^T products run at raised wave priority, like P V^T below
+            // (s_setprio 1; back to 0 for the softmax).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int i = 0; i < kTilesP4; ++i) {
                 // every token centred at its own zero code (int4_zero_code), computed once per token
@@ -210,6 +213,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
                         z[nb][i][u] = __builtin_fmaf(s[u], ks[u], qsum[nb] * zp[u]);  // z / |f|
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             // The causal mask, only for the chunks that reach past the wave's first row
             // (wave-uniform test); and the V parameters of slots past the context are zeroed (they
             // may be NaN, and a zero weight alone would still give 0 * NaN), only in the chunk
